@@ -1,0 +1,246 @@
+"""CPU oracle for the MobileMoE MoE-FFN layer (eq. (*) of the MobileMoE close
+reading, paper-archivist.com).
+
+TEST INFRASTRUCTURE ONLY.  The tests, the smoke check and the benchmark's
+CPU-baseline leg are the only callers.  The HIP library never imports this
+package and this package never imports the HIP library; they share no code.
+
+The arithmetic lives in ``mobmoe_oracle.cpp`` (plain C++, no fast-math, FMAs
+written out); this module builds it with g++ and wraps it with ctypes/numpy.
+Every wrapper names the oracle function it calls; the passage each follows is
+cited in the C++ source.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mobmoe_oracle.cpp")
+_LIB = os.path.join(_HERE, "libmobmoe_oracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle shared library with g++ (host code only)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        cmd = ["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fno-fast-math",
+               "-fPIC", "-shared", "-fopenmp", _SRC, "-o", tmp]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        _lib = ctypes.CDLL(_LIB)
+        _lib.ora_version.restype = ctypes.c_char_p
+    return _lib
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _i8(a):
+    return np.ascontiguousarray(a, dtype=np.int8)
+
+
+def _i64(v):
+    return ctypes.c_int64(int(v))
+
+
+def version() -> str:
+    return _load().ora_version().decode()
+
+
+def quant_w4g32(w: np.ndarray):
+    """eq. (6), b=4, group 32 -> (q int8 [rows, cols], s float32 [rows, cols/32])."""
+    w = _f32(w)
+    rows, cols = w.reshape(-1, w.shape[-1]).shape
+    q = np.empty((rows, cols), np.int8)
+    s = np.empty((rows, cols // 32), np.float32)
+    rc = _load().ora_quant_w4g32(_i64(rows), _i64(cols), _p(w), _p(q), _p(s))
+    if rc:
+        raise ValueError("ora_quant_w4g32: cols must be a multiple of 32")
+    return q.reshape(w.shape), s.reshape(w.shape[:-1] + (cols // 32,))
+
+
+def quant_act_i8(x: np.ndarray):
+    """Per-row INT8 (eq. (6) with b=8, one group per row) -> (q int8, s float32 [rows])."""
+    x = _f32(x)
+    rows, cols = x.reshape(-1, x.shape[-1]).shape
+    q = np.empty((rows, cols), np.int8)
+    s = np.empty((rows,), np.float32)
+    _load().ora_quant_act_i8(_i64(rows), _i64(cols), _p(x), _p(q), _p(s))
+    return q.reshape(x.shape), s.reshape(x.shape[:-1])
+
+
+def router(x, wr, bias, k: int, gating: int = 0):
+    """FP32 router -> (idx int32 [T,k], w float64 [T,k], logits float32 [T,E])."""
+    x, wr = _f32(x), _f32(wr)
+    T, d = x.shape
+    E = wr.shape[0]
+    b = None if bias is None else _f32(bias)
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    lib = _load()
+    if gating == 0:
+        logits = np.empty((T, E), np.float32)
+        rc = lib.ora_router(_i64(T), d, E, k, _p(x), _p(wr), _p(b), _p(logits), _p(idx), _p(w))
+    else:
+        logits = None
+        rc = lib.ora_router_sigmoid(_i64(T), d, E, k, _p(x), _p(wr), _p(b), _p(idx), _p(w))
+    if rc:
+        raise ValueError("ora_router: bad shapes")
+    return idx, w, logits
+
+
+def route(idx: np.ndarray, E: int):
+    """Stable count sort -> (offsets [E+1], perm [T*k], inv_perm [T*k]) int32."""
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    T, k = idx.shape
+    offsets = np.empty(E + 1, np.int32)
+    perm = np.empty(T * k, np.int32)
+    inv = np.empty(T * k, np.int32)
+    rc = _load().ora_route(_i64(T), E, k, _p(idx), _p(offsets), _p(perm), _p(inv))
+    if rc:
+        raise ValueError("ora_route: expert id out of range")
+    return offsets, perm, inv
+
+
+def linear_w4a8(aq, sa, wq, ws, want_isum: bool = False):
+    """out[r,o] = sa[r] * sum_g ws[o,g] * isum[r,o,g]  (double), isum optional."""
+    aq, wq = _i8(aq), _i8(wq)
+    sa, ws = _f32(sa), _f32(ws)
+    rows, K = aq.shape
+    N = wq.shape[0]
+    out = np.empty((rows, N), np.float64)
+    isum = np.empty((rows, N, K // 32), np.int32) if want_isum else None
+    _load().ora_linear_w4a8(_i64(rows), N, K, _p(aq), _p(sa), _p(wq), _p(ws), _p(out), _p(isum))
+    return (out, isum) if want_isum else out
+
+
+def ffn_w4a8(xq, sx, wgu_q, wgu_s, wd_q, wd_s, want_isum: bool = False):
+    """SwiGLU expert on INT8 rows -> (hq, hs, f[, isum_gu, isum_d])."""
+    xq, wgu_q, wd_q = _i8(xq), _i8(wgu_q), _i8(wd_q)
+    sx, wgu_s, wd_s = _f32(sx), _f32(wgu_s), _f32(wd_s)
+    rows, d = xq.shape
+    h = wd_q.shape[1]
+    hq = np.empty((rows, h), np.int8)
+    hs = np.empty((rows,), np.float32)
+    f = np.empty((rows, d), np.float64)
+    igu = np.empty((rows, 2 * h, d // 32), np.int32) if want_isum else None
+    idn = np.empty((rows, d, h // 32), np.int32) if want_isum else None
+    _load().ora_ffn_w4a8(_i64(rows), d, h, _p(xq), _p(sx), _p(wgu_q), _p(wgu_s), _p(wd_q),
+                         _p(wd_s), _p(hq), _p(hs), _p(f), _p(igu), _p(idn))
+    return (hq, hs, f, igu, idn) if want_isum else (hq, hs, f)
+
+
+def ffn_float(x, wgu, wd, bf16: bool = False):
+    x, wgu, wd = _f32(x), _f32(wgu), _f32(wd)
+    rows, d = x.shape
+    h = wd.shape[1]
+    f = np.empty((rows, d), np.float64)
+    _load().ora_ffn_float(_i64(rows), d, h, _p(x), _p(wgu), _p(wd), 1 if bf16 else 0, _p(f))
+    return f
+
+
+def combine(f, w, ys):
+    """f [T,k,d], w [T,k], ys [T,d] or None (all float64) -> y [T,d] float64."""
+    f = np.ascontiguousarray(f, dtype=np.float64)
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    ys = None if ys is None else np.ascontiguousarray(ys, dtype=np.float64)
+    T, k, d = f.shape
+    y = np.empty((T, d), np.float64)
+    _load().ora_combine(_i64(T), k, d, _p(f), _p(w), _p(ys), _p(y))
+    return y
+
+
+def rmsnorm(x, eps: float = 1e-5):
+    x = _f32(x)
+    rows, cols = x.shape
+    y = np.empty((rows, cols), np.float64)
+    _load().ora_rmsnorm(_i64(rows), cols, ctypes.c_double(eps), _p(x), _p(y))
+    return y
+
+
+def round_bf16(x):
+    x = _f32(x)
+    y = np.empty_like(x)
+    _load().ora_round_bf16(_i64(x.size), _p(x), _p(y))
+    return y
+
+
+class _Out(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("y", "idx", "w", "logits", "xq", "sx", "hq", "hs", "f", "ys", "hq_s", "hs_s")]
+
+
+@dataclass
+class LayerResult:
+    y: np.ndarray
+    idx: np.ndarray
+    w: np.ndarray
+    logits: Optional[np.ndarray]
+    f: np.ndarray
+    ys: Optional[np.ndarray]
+    xq: Optional[np.ndarray] = None
+    sx: Optional[np.ndarray] = None
+    hq: Optional[np.ndarray] = None
+    hs: Optional[np.ndarray] = None
+    hq_s: Optional[np.ndarray] = None
+    hs_s: Optional[np.ndarray] = None
+
+
+WFMT = {"f32": 0, "int4g32": 1, "bf16": 2}
+
+
+def forward(x, wr, bias, w_gu, w_d, ws_gu, ws_d, *, k: int, wfmt: str = "int4g32",
+            gating: int = 0, nthreads: int = 1) -> LayerResult:
+    """Whole layer, eq. (*), with every intermediate returned.
+
+    x [T,d]; wr [E,d]; bias [E] or None; w_gu [E,2h,d]; w_d [E,d,h];
+    ws_gu [2hs,d] / ws_d [d,hs] or None for no shared expert.
+    """
+    x, wr, w_gu, w_d = _f32(x), _f32(wr), _f32(w_gu), _f32(w_d)
+    b = None if bias is None else _f32(bias)
+    T, d = x.shape
+    E, h2, _ = w_gu.shape
+    h = h2 // 2
+    hs = 0 if ws_gu is None else ws_gu.shape[0] // 2
+    ws_gu = None if ws_gu is None else _f32(ws_gu)
+    ws_d = None if ws_d is None else _f32(ws_d)
+    fm = WFMT[wfmt]
+    r = LayerResult(
+        y=np.empty((T, d), np.float64), idx=np.empty((T, k), np.int32),
+        w=np.empty((T, k), np.float64),
+        logits=np.empty((T, E), np.float32) if gating == 0 else None,
+        f=np.empty((T, k, d), np.float64), ys=np.empty((T, d), np.float64) if hs else None)
+    if fm == 1:
+        r.xq, r.sx = np.empty((T, d), np.int8), np.empty((T,), np.float32)
+        r.hq, r.hs = np.empty((T, k, h), np.int8), np.empty((T, k), np.float32)
+        if hs:
+            r.hq_s, r.hs_s = np.empty((T, hs), np.int8), np.empty((T,), np.float32)
+    o = _Out(*[None if a is None else a.ctypes.data for a in
+               (r.y, r.idx, r.w, r.logits, r.xq, r.sx, r.hq, r.hs, r.f, r.ys, r.hq_s, r.hs_s)])
+    rc = _load().ora_forward(d, E, h, hs, k, fm, gating, _i64(T), _p(x), _p(wr), _p(b),
+                             _p(w_gu), _p(w_d), _p(ws_gu), _p(ws_d), int(nthreads),
+                             ctypes.byref(o))
+    if rc:
+        raise ValueError("ora_forward: bad shapes or formats")
+    return r

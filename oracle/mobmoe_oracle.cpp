@@ -1,0 +1,464 @@
+// MobileMoE MoE-FFN layer: CPU oracle.
+//
+// TEST INFRASTRUCTURE ONLY.  This file is the slow, plain reference that the
+// HIP library is checked against.  Only the tests, the smoke check and the
+// benchmark's CPU-baseline leg may load it.  It shares no code, header, table
+// or helper with the HIP library under sparse_moe_ffn_amd/, and it includes
+// nothing from there.
+//
+// Sources (page titles as published; sections named on those pages):
+//   [P1] "MobileMoE: Scaling On-Device Mixture of Experts" close reading,
+//        paper-archivist.com.
+//        - section "MoE preliminaries and three design factors", eq. (*):
+//          y = sum over the top-k routed experts of router_i(x) * FFN_i(x),
+//          plus the always-on shared expert FFN^(s)(x).
+//        - section "Pre-training", MoE stability list: the router runs in FP32.
+//        - section "Quantisation-aware training", eq. (6): symmetric group
+//          quantiser, group size 32, b = 4 for weights; activations are
+//          quantised to INT8 on the fly; router stays FP32.
+//        - section "Custom MoE kernel": count-sort of tokens by expert id,
+//          one fused gate/up product per expert, SwiGLU, down product,
+//          weighted scatter back through the inverse permutation.
+//
+// Precision policy.  Where a floating-point result decides an integer (the
+// top-k choice, a quantised code, a quantisation scale) the oracle works in
+// FP32 with the operation order stated at each function, because the device
+// must reproduce those bits.  Everything else (scale application, SwiGLU,
+// softmax weights, combine, RMSNorm) is evaluated in double precision, the
+// plain definition, and the device result is compared within a tolerance.
+//
+// Build: g++ -O2 -std=c++17 -ffp-contract=off -fPIC -shared -fopenmp
+// (no fast-math: every FMA below is written out as std::fma).
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+namespace {
+
+constexpr int kGroup = 32;  // eq. (6) group size
+
+int8_t clamp_i(float v, int lo, int hi) {
+  if (v < (float)lo) return (int8_t)lo;
+  if (v > (float)hi) return (int8_t)hi;
+  return (int8_t)(int)v;
+}
+
+// Round-to-nearest-even of an FP32 value to BF16, returned as FP32.
+float round_bf16(float v) {
+  uint32_t u;
+  std::memcpy(&u, &v, 4);
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7FFFu + lsb;
+  u &= 0xFFFF0000u;
+  float r;
+  std::memcpy(&r, &u, 4);
+  return r;
+}
+
+double silu(double z) { return z / (1.0 + std::exp(-z)); }
+
+}  // namespace
+
+extern "C" {
+
+const char* ora_version() { return "mobmoe-oracle 1"; }
+
+// ---------------------------------------------------------------------------
+// eq. (6) with b = 4, group 32 along the input (reduction) dimension.
+//   s_g = (2 * max|W_g|) / 15                      (FP32, IEEE division)
+//   q   = clamp(round_half_even(W / s_g), -8, 7)   (FP32 division)
+//   an all-zero group gives s_g = 0 and q = 0.
+// w: [rows][cols] FP32, q: [rows][cols] int8 (one value per element),
+// s: [rows][cols/32] FP32.  Returns 0, or -1 if cols is not a multiple of 32.
+int ora_quant_w4g32(int64_t rows, int64_t cols, const float* w, int8_t* q, float* s) {
+  if (cols % kGroup) return -1;
+  const int64_t G = cols / kGroup;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t g = 0; g < G; ++g) {
+      const float* wg = w + r * cols + g * kGroup;
+      float amax = 0.0f;
+      for (int c = 0; c < kGroup; ++c) amax = std::max(amax, std::fabs(wg[c]));
+      float sg = (2.0f * amax) / 15.0f;
+      s[r * G + g] = sg;
+      for (int c = 0; c < kGroup; ++c) {
+        int8_t v = 0;
+        if (sg != 0.0f) v = clamp_i(std::nearbyint(wg[c] / sg), -8, 7);
+        q[r * cols + g * kGroup + c] = v;
+      }
+    }
+  }
+  return 0;
+}
+
+// Dynamic INT8 quantisation of activations, one scale per row: eq. (6) read
+// with b = 8 and the whole row as the group.
+//   s = (2 * max|v|) / 255,  q = clamp(round_half_even(v / s), -128, 127)
+//   an all-zero row gives s = 0 and q = 0.
+int ora_quant_act_i8(int64_t rows, int64_t cols, const float* x, int8_t* q, float* s) {
+  for (int64_t r = 0; r < rows; ++r) {
+    const float* xr = x + r * cols;
+    float amax = 0.0f;
+    for (int64_t c = 0; c < cols; ++c) amax = std::max(amax, std::fabs(xr[c]));
+    float sr = (2.0f * amax) / 255.0f;
+    s[r] = sr;
+    for (int64_t c = 0; c < cols; ++c) {
+      int8_t v = 0;
+      if (sr != 0.0f) v = clamp_i(std::nearbyint(xr[c] / sr), -128, 127);
+      q[r * cols + c] = v;
+    }
+  }
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
+// FP32 router logit for one (token, expert), in the fixed order the device
+// uses (needed because the top-k choice must agree bit for bit):
+//   64 partial sums p[l], l = 0..63; p[l] = 0, then for j = l, l+64, l+128, ...
+//   in ascending order p[l] = fma(x[j], w[j], p[l]);
+//   then a balanced pairwise tree: for s = 1, 2, 4, 8, 16, 32 in turn, every
+//   p[l] with l a multiple of 2s becomes p[l] + p[l+s];  logit = p[0] + bias.
+// Requires d % 64 == 0.
+static float router_logit(const float* x, const float* w, int d, float bias) {
+  float p[64];
+  for (int l = 0; l < 64; ++l) p[l] = 0.0f;
+  for (int j = 0; j < d; ++j) p[j % 64] = std::fma(x[j], w[j], p[j % 64]);
+  for (int s = 1; s < 64; s *= 2)
+    for (int l = 0; l < 64; l += 2 * s) p[l] = p[l] + p[l + s];
+  return p[0] + bias;
+}
+
+// Router: FP32 logits (plus an optional per-expert bias added to every
+// logit), top-k selection, softmax gate weights.
+//   selection: experts ordered by (logit descending, index ascending); the
+//     first k are idx[t][0..k-1].  Selecting on the logits is the same as
+//     selecting on the softmax, which is monotone in the logit.
+//   gate weights: softmax over ALL E logits, not renormalised over the k:
+//     w[t][j] = exp(l_idx - m) / sum_e exp(l_e - m), m = max_e l_e  (double).
+// logits_out [T][E] FP32 is optional.  Returns -1 on bad shapes.
+int ora_router(int64_t T, int d, int E, int k, const float* x, const float* wr,
+               const float* bias, float* logits_out, int32_t* idx, double* w) {
+  if (d % 64 || E < 1 || k < 1 || k > E) return -1;
+  std::vector<float> lg(E);
+  std::vector<int> order(E);
+  for (int64_t t = 0; t < T; ++t) {
+    for (int e = 0; e < E; ++e)
+      lg[e] = router_logit(x + t * d, wr + (int64_t)e * d, d, bias ? bias[e] : 0.0f);
+    if (logits_out)
+      for (int e = 0; e < E; ++e) logits_out[t * E + e] = lg[e];
+    for (int e = 0; e < E; ++e) order[e] = e;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int a, int b) { return lg[a] > lg[b]; });
+    float m = lg[order[0]];
+    double S = 0.0;
+    for (int e = 0; e < E; ++e) S += std::exp((double)lg[e] - (double)m);
+    for (int j = 0; j < k; ++j) {
+      int e = order[j];
+      idx[t * k + j] = e;
+      w[t * k + j] = std::exp((double)lg[e] - (double)m) / S;
+    }
+  }
+  return 0;
+}
+
+// Sigmoid gating with per-token renormalisation over the selected k
+// (the training-time gate of the "Pre-training" section): selection as above
+// on the (biased) logits, w_j = sig(l_j) / sum_{i in top-k} sig(l_i).
+int ora_router_sigmoid(int64_t T, int d, int E, int k, const float* x, const float* wr,
+                       const float* bias, int32_t* idx, double* w) {
+  if (d % 64 || E < 1 || k < 1 || k > E) return -1;
+  std::vector<float> lg(E);
+  std::vector<int> order(E);
+  for (int64_t t = 0; t < T; ++t) {
+    for (int e = 0; e < E; ++e)
+      lg[e] = router_logit(x + t * d, wr + (int64_t)e * d, d, bias ? bias[e] : 0.0f);
+    for (int e = 0; e < E; ++e) order[e] = e;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int a, int b) { return lg[a] > lg[b]; });
+    double S = 0.0;
+    for (int j = 0; j < k; ++j) S += 1.0 / (1.0 + std::exp(-(double)lg[order[j]]));
+    for (int j = 0; j < k; ++j) {
+      idx[t * k + j] = order[j];
+      w[t * k + j] = (1.0 / (1.0 + std::exp(-(double)lg[order[j]]))) / S;
+    }
+  }
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
+// Count sort of the T*k (token, slot) assignments by expert id ("Custom MoE
+// kernel" section): tokens routed to one expert become one contiguous run.
+//   count[e]   = number of (t, j) with idx[t][j] == e
+//   offsets    = exclusive prefix sum of count, offsets[E] = T*k
+//   walking t ascending, then j ascending: p = cursor[e]++,
+//   perm[p] = t*k + j, inv_perm[t*k + j] = p.
+// Returns -1 if an id is out of range.
+int ora_route(int64_t T, int E, int k, const int32_t* idx, int32_t* offsets,
+              int32_t* perm, int32_t* inv_perm) {
+  std::vector<int64_t> count(E, 0);
+  for (int64_t i = 0; i < T * k; ++i) {
+    if (idx[i] < 0 || idx[i] >= E) return -1;
+    count[idx[i]]++;
+  }
+  int64_t run = 0;
+  std::vector<int64_t> cursor(E);
+  for (int e = 0; e < E; ++e) {
+    offsets[e] = (int32_t)run;
+    cursor[e] = run;
+    run += count[e];
+  }
+  offsets[E] = (int32_t)run;
+  for (int64_t t = 0; t < T; ++t)
+    for (int j = 0; j < k; ++j) {
+      int64_t slot = t * k + j;
+      int64_t p = cursor[idx[slot]]++;
+      perm[p] = (int32_t)slot;
+      inv_perm[slot] = (int32_t)p;
+    }
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
+// W4A8 linear on one row: out[o] = s_a * sum_g s_w[o][g] * isum[o][g], with
+//   isum[o][g] = sum_{c in group g} (int32) q_w[o][c] * (int32) q_a[c]
+// (exact in int32).  Scale application in double.  isum_out [N][K/32] optional.
+static void linear_w4a8_row(int N, int K, const int8_t* aq, float sa, const int8_t* wq,
+                            const float* ws, double* out, int32_t* isum_out) {
+  const int G = K / kGroup;
+  for (int o = 0; o < N; ++o) {
+    double acc = 0.0;
+    for (int g = 0; g < G; ++g) {
+      int32_t is = 0;
+      for (int c = g * kGroup; c < (g + 1) * kGroup; ++c)
+        is += (int32_t)wq[(int64_t)o * K + c] * (int32_t)aq[c];
+      if (isum_out) isum_out[(int64_t)o * G + g] = is;
+      acc += (double)ws[(int64_t)o * G + g] * (double)is;
+    }
+    out[o] = acc * (double)sa;
+  }
+}
+
+int ora_linear_w4a8(int64_t rows, int N, int K, const int8_t* aq, const float* sa,
+                    const int8_t* wq, const float* ws, double* out, int32_t* isum) {
+  if (K % kGroup) return -1;
+  const int G = K / kGroup;
+  for (int64_t r = 0; r < rows; ++r)
+    linear_w4a8_row(N, K, aq + r * K, sa[r], wq, ws, out + r * N,
+                    isum ? isum + r * (int64_t)N * G : nullptr);
+  return 0;
+}
+
+// One SwiGLU expert FFN on one INT8 row (NC: gate rows 0..h-1 and up rows
+// h..2h-1 of the stacked gate/up weight, SiLU(g) * u, INT8 re-quantisation of
+// that hidden row, then the down product).
+//   wgu_q [2h][d] / wgu_s [2h][d/32], wd_q [d][h] / wd_s [d][h/32].
+//   The hidden row is rounded to FP32 before its INT8 quantisation, since the
+//   quantiser's decisions are defined in FP32.
+static void ffn_w4a8_row(int d, int h, const int8_t* xq, float sx, const int8_t* wgu_q,
+                         const float* wgu_s, const int8_t* wd_q, const float* wd_s,
+                         int8_t* hq, float* hs, double* f, int32_t* isum_gu,
+                         int32_t* isum_d) {
+  std::vector<double> gu(2 * h);
+  linear_w4a8_row(2 * h, d, xq, sx, wgu_q, wgu_s, gu.data(), isum_gu);
+  std::vector<float> a(h);
+  for (int o = 0; o < h; ++o) a[o] = (float)(silu(gu[o]) * gu[h + o]);
+  ora_quant_act_i8(1, h, a.data(), hq, hs);
+  linear_w4a8_row(d, h, hq, *hs, wd_q, wd_s, f, isum_d);
+}
+
+int ora_ffn_w4a8(int64_t rows, int d, int h, const int8_t* xq, const float* sx,
+                 const int8_t* wgu_q, const float* wgu_s, const int8_t* wd_q,
+                 const float* wd_s, int8_t* hq, float* hs, double* f, int32_t* isum_gu,
+                 int32_t* isum_d) {
+  if (d % kGroup || h % kGroup) return -1;
+  for (int64_t r = 0; r < rows; ++r)
+    ffn_w4a8_row(d, h, xq + r * d, sx[r], wgu_q, wgu_s, wd_q, wd_s, hq + r * h, hs + r,
+                 f + r * d, isum_gu ? isum_gu + r * (int64_t)2 * h * (d / kGroup) : nullptr,
+                 isum_d ? isum_d + r * (int64_t)d * (h / kGroup) : nullptr);
+  return 0;
+}
+
+// Plain floating-point SwiGLU FFN on one row.  mode 0: FP32 operands,
+// evaluated in double.  mode 1: operands rounded to BF16 first (x, both
+// weights), the hidden row rounded to BF16 before the down product.
+static void ffn_float_row(int d, int h, const float* x, const float* wgu, const float* wd,
+                          int mode, double* f) {
+  std::vector<double> xv(d);
+  for (int c = 0; c < d; ++c) xv[c] = mode ? round_bf16(x[c]) : x[c];
+  std::vector<double> gu(2 * h);
+  for (int o = 0; o < 2 * h; ++o) {
+    double acc = 0.0;
+    for (int c = 0; c < d; ++c) {
+      float wv = wgu[(int64_t)o * d + c];
+      acc += xv[c] * (double)(mode ? round_bf16(wv) : wv);
+    }
+    gu[o] = acc;
+  }
+  std::vector<double> a(h);
+  for (int o = 0; o < h; ++o) {
+    a[o] = silu(gu[o]) * gu[h + o];
+    if (mode) a[o] = round_bf16((float)a[o]);
+  }
+  for (int o = 0; o < d; ++o) {
+    double acc = 0.0;
+    for (int c = 0; c < h; ++c) {
+      float wv = wd[(int64_t)o * h + c];
+      acc += a[c] * (double)(mode ? round_bf16(wv) : wv);
+    }
+    f[o] = acc;
+  }
+}
+
+int ora_ffn_float(int64_t rows, int d, int h, const float* x, const float* wgu,
+                  const float* wd, int mode, double* f) {
+  for (int64_t r = 0; r < rows; ++r) ffn_float_row(d, h, x + r * d, wgu, wd, mode, f + r * d);
+  return 0;
+}
+
+// Combine (eq. (*) with the "weighted scatter through the inverse
+// permutation" of the custom-kernel section): y[t] = sum_j w[t][j] f[t][j] +
+// ys[t], slots summed in j order, in double.  f is in token-slot order
+// [T][k][d].  ys may be null (no shared expert).
+int ora_combine(int64_t T, int k, int d, const double* f, const double* w, const double* ys,
+                double* y) {
+  for (int64_t t = 0; t < T; ++t)
+    for (int c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int j = 0; j < k; ++j) acc += w[t * k + j] * f[(t * k + j) * d + c];
+      y[t * d + c] = acc + (ys ? ys[t * d + c] : 0.0);
+    }
+  return 0;
+}
+
+// RMSNorm used between stacked layers in the decode workload (not part of
+// eq. (*)): y = x / sqrt(mean(x^2) + eps), unit gain, in double.
+int ora_rmsnorm(int64_t rows, int cols, double eps, const float* x, double* y) {
+  for (int64_t r = 0; r < rows; ++r) {
+    double ss = 0.0;
+    for (int c = 0; c < cols; ++c) ss += (double)x[r * cols + c] * (double)x[r * cols + c];
+    double inv = 1.0 / std::sqrt(ss / cols + eps);
+    for (int c = 0; c < cols; ++c) y[r * cols + c] = (double)x[r * cols + c] * inv;
+  }
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
+// Whole layer, eq. (*).
+//   wfmt 0: FP32 weights and activations, no quantisation.
+//   wfmt 1: INT4 group-32 weights (eq. (6)), per-token INT8 activations.
+//   wfmt 2: BF16 weights and activations, output rounded to BF16.
+//   gating 0: softmax over all E, no renormalisation; 1: sigmoid + top-k norm.
+// Inputs (FP32, row-major): x [T][d]; wr [E][d]; bias [E] (nullable);
+//   w_gu [E][2h][d] (gate rows first, then up rows); w_d [E][d][h];
+//   ws_gu [2hs][d]; ws_d [d][hs] (both ignored when hs == 0).
+// Outputs: y [T][d] double; every other pointer in ora_out is optional.
+struct ora_out {
+  double* y;         // [T][d]
+  int32_t* idx;      // [T][k]
+  double* w;         // [T][k]
+  float* logits;     // [T][E]
+  int8_t* xq;        // [T][d]        (wfmt 1)
+  float* sx;         // [T]           (wfmt 1)
+  int8_t* hq;        // [T][k][h]     (wfmt 1)
+  float* hs;         // [T][k]        (wfmt 1)
+  double* f;         // [T][k][d]     routed expert outputs, before gating
+  double* ys;        // [T][d]        shared expert output
+  int8_t* hq_s;      // [T][hs]       (wfmt 1)
+  float* hs_s;       // [T]           (wfmt 1)
+};
+
+int ora_forward(int d, int E, int h, int hs, int k, int wfmt, int gating, int64_t T,
+                const float* x, const float* wr, const float* bias, const float* w_gu,
+                const float* w_d, const float* ws_gu, const float* ws_d, int nthreads,
+                ora_out* out) {
+  if (d % 64 || h % kGroup || hs % kGroup || k < 1 || k > E || !out || !out->y) return -1;
+  if (wfmt < 0 || wfmt > 2 || gating < 0 || gating > 1) return -1;
+  std::vector<int32_t> idx(T * k);
+  std::vector<double> w(T * k);
+  int rc = gating == 0 ? ora_router(T, d, E, k, x, wr, bias, out->logits, idx.data(), w.data())
+                       : ora_router_sigmoid(T, d, E, k, x, wr, bias, idx.data(), w.data());
+  if (rc) return rc;
+  if (out->idx) std::copy(idx.begin(), idx.end(), out->idx);
+  if (out->w) std::copy(w.begin(), w.end(), out->w);
+
+  // Weights quantised once per call (eq. (6)); only for the INT4 format.
+  std::vector<int8_t> gu_q, d_q, sgu_q, sd_q, xq;
+  std::vector<float> gu_s, d_s, sgu_s, sd_s, sx;
+  if (wfmt == 1) {
+    gu_q.resize((int64_t)E * 2 * h * d);  gu_s.resize((int64_t)E * 2 * h * d / kGroup);
+    d_q.resize((int64_t)E * d * h);       d_s.resize((int64_t)E * d * h / kGroup);
+    ora_quant_w4g32((int64_t)E * 2 * h, d, w_gu, gu_q.data(), gu_s.data());
+    ora_quant_w4g32((int64_t)E * d, h, w_d, d_q.data(), d_s.data());
+    if (hs) {
+      sgu_q.resize((int64_t)2 * hs * d);  sgu_s.resize((int64_t)2 * hs * d / kGroup);
+      sd_q.resize((int64_t)d * hs);       sd_s.resize((int64_t)d * hs / kGroup);
+      ora_quant_w4g32(2 * hs, d, ws_gu, sgu_q.data(), sgu_s.data());
+      ora_quant_w4g32(d, hs, ws_d, sd_q.data(), sd_s.data());
+    }
+    xq.resize(T * d);
+    sx.resize(T);
+    ora_quant_act_i8(T, d, x, xq.data(), sx.data());
+    if (out->xq) std::copy(xq.begin(), xq.end(), out->xq);
+    if (out->sx) std::copy(sx.begin(), sx.end(), out->sx);
+  }
+
+  std::vector<double> f((int64_t)T * k * d);
+  std::vector<double> ys(hs ? (int64_t)T * d : 0);
+  const int64_t gu_q_stride = (int64_t)2 * h * d, gu_s_stride = gu_q_stride / kGroup;
+  const int64_t d_q_stride = (int64_t)d * h, d_s_stride = d_q_stride / kGroup;
+
+#ifdef _OPENMP
+  int nt = nthreads > 0 ? nthreads : 1;
+#pragma omp parallel for num_threads(nt) schedule(static)
+#endif
+  for (int64_t t = 0; t < T; ++t) {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[t * k + j];
+      double* fr = f.data() + (t * k + j) * d;
+      if (wfmt == 1) {
+        std::vector<int8_t> hq(h);
+        float hsc = 0.0f;
+        ffn_w4a8_row(d, h, xq.data() + t * d, sx[t], gu_q.data() + e * gu_q_stride,
+                     gu_s.data() + e * gu_s_stride, d_q.data() + e * d_q_stride,
+                     d_s.data() + e * d_s_stride, hq.data(), &hsc, fr, nullptr, nullptr);
+        if (out->hq) std::copy(hq.begin(), hq.end(), out->hq + (t * k + j) * h);
+        if (out->hs) out->hs[t * k + j] = hsc;
+      } else {
+        ffn_float_row(d, h, x + t * d, w_gu + e * gu_q_stride, w_d + e * d_q_stride,
+                      wfmt == 2 ? 1 : 0, fr);
+      }
+    }
+    if (hs) {
+      double* yr = ys.data() + t * d;
+      if (wfmt == 1) {
+        std::vector<int8_t> hq(hs);
+        float hsc = 0.0f;
+        ffn_w4a8_row(d, hs, xq.data() + t * d, sx[t], sgu_q.data(), sgu_s.data(),
+                     sd_q.data(), sd_s.data(), hq.data(), &hsc, yr, nullptr, nullptr);
+        if (out->hq_s) std::copy(hq.begin(), hq.end(), out->hq_s + t * hs);
+        if (out->hs_s) out->hs_s[t] = hsc;
+      } else {
+        ffn_float_row(d, hs, x + t * d, ws_gu, ws_d, wfmt == 2 ? 1 : 0, yr);
+      }
+    }
+  }
+  if (out->f) std::copy(f.begin(), f.end(), out->f);
+  if (out->ys && hs) std::copy(ys.begin(), ys.end(), out->ys);
+  ora_combine(T, k, d, f.data(), w.data(), hs ? ys.data() : nullptr, out->y);
+  if (wfmt == 2)
+    for (int64_t i = 0; i < T * d; ++i) out->y[i] = round_bf16((float)out->y[i]);
+  return 0;
+}
+
+// BF16 rounding exposed for the pins.
+void ora_round_bf16(int64_t n, const float* x, float* y) {
+  for (int64_t i = 0; i < n; ++i) y[i] = round_bf16(x[i]);
+}
+
+}  // extern "C"

@@ -1,0 +1,469 @@
+"""Pins for the CPU oracle: each check ties an oracle function to something
+other than itself -- closed forms, brute force on tiny inputs, double-precision
+explicit dequantisation, library routines, invariants the method fixes, and
+the sizes the MobileMoE close reading prints.  CPU only."""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+from sparse_moe_ffn_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+# ----------------------------------------------------------------- eq. (6), b=4
+def _crafted_weights():
+    g = rng(1)
+    w = (g.standard_normal((24, 128)) * 0.02).astype(np.float32)
+    w[0, :32] = 0.0                      # all-zero group
+    w[1, :32] = 0.0
+    w[1, 5] = 0.3                        # single non-zero element
+    w[2, 32:64] = np.linspace(-1, 1, 32, dtype=np.float32)   # exact +-max
+    w[3, :32] = -w[3, :32]
+    w[4, 64:96] = 1e-30                  # tiny values
+    return w
+
+
+def test_quant_w4_range_and_error_bound(ora):
+    w = _crafted_weights()
+    q, s = ora.quant_w4g32(w)
+    assert q.min() >= -8 and q.max() <= 7
+    wq = w.reshape(24, 4, 32).astype(np.float64)
+    qq = q.reshape(24, 4, 32).astype(np.float64)
+    ss = s.astype(np.float64)[..., None]
+    amax = np.abs(wq).max(-1, keepdims=True)
+    # scale is 2*max/15 up to one FP32 rounding
+    np.testing.assert_allclose(ss, 2 * amax / 15, rtol=2 ** -23, atol=0)
+    err = np.abs(wq - ss * qq)
+    # every element is within half a step, except +max which clips from 7.5 to 7
+    is_pmax = (wq == amax) & (amax > 0)
+    assert np.all(err[~is_pmax] <= ss.repeat(32, -1)[~is_pmax] * (0.5 + 1e-5))
+    assert np.all(qq[is_pmax] == 7)
+    # -max lands on -7.5 up to the rounding of s, so -8 (half-even) or -7
+    is_nmax = (wq == -amax) & (amax > 0)
+    assert np.all(np.isin(qq[is_nmax], (-8, -7)))
+    # all-zero group -> zero scale and codes
+    assert s[0, 0] == 0 and np.all(q[0, :32] == 0)
+    # single non-zero element -> it is the max, code 7; the rest 0
+    assert q[1, 5] == 7 and np.count_nonzero(q[1, :32]) == 1
+
+
+def test_quant_w4_dequant_error_is_small(ora):
+    """Group-32 symmetric INT4 reconstruction error is bounded by s/2 per element,
+    i.e. relative RMS error well under the 4-bit step."""
+    w = (rng(2).standard_normal((64, 256)) * 0.02).astype(np.float32)
+    q, s = ora.quant_w4g32(w)
+    wd = q.reshape(64, 8, 32) * s[..., None].astype(np.float64)
+    rel = np.sqrt(((wd.reshape(64, 256) - w) ** 2).mean()) / np.sqrt((w.astype(np.float64) ** 2).mean())
+    assert 0.02 < rel < 0.2
+
+
+def test_quant_w4_grouping_axis(ora):
+    """Groups run along the reduction (column) axis: scaling one 32-column block
+    by 2 doubles only that block's scale and leaves codes unchanged."""
+    w = (rng(3).standard_normal((8, 96)) * 0.02).astype(np.float32)
+    q1, s1 = ora.quant_w4g32(w)
+    w2 = w.copy()
+    w2[:, 32:64] *= 2
+    q2, s2 = ora.quant_w4g32(w2)
+    assert np.array_equal(q1, q2)
+    assert np.array_equal(s2[:, 1], s1[:, 1] * 2)
+    assert np.array_equal(s2[:, [0, 2]], s1[:, [0, 2]])
+
+
+# ----------------------------------------------------------------- INT8 activations
+def test_quant_act_invariants(ora):
+    g = rng(4)
+    x = g.standard_normal((50, 768)).astype(np.float32)
+    x[3] = 0.0
+    q, s = ora.quant_act_i8(x)
+    assert s[3] == 0 and np.all(q[3] == 0)
+    xd = q.astype(np.float64) * s[:, None]
+    amax = np.abs(x).max(1)
+    nz = amax > 0
+    np.testing.assert_allclose(s[nz], 2 * amax[nz].astype(np.float64) / 255, rtol=2 ** -23)
+    err = np.abs(xd - x)
+    pmax = (x == amax[:, None]) & nz[:, None]
+    assert np.all(q[pmax] == 127)                      # +max maps to 127 (from 127.5)
+    nmax = (x == -amax[:, None]) & nz[:, None]
+    assert np.all(np.isin(q[nmax], (-128, -127)))
+    assert np.all(err[~pmax] <= s[:, None].repeat(768, 1)[~pmax] * (0.5 + 1e-5))
+    # power-of-two scaling of a row scales s exactly and keeps q
+    q2, s2 = ora.quant_act_i8(x * np.float32(4))
+    assert np.array_equal(q2, q) and np.array_equal(s2, s * 4)
+
+
+# ----------------------------------------------------------------- W4A8 linear
+def test_linear_isum_bruteforce_and_dequant(ora):
+    """int32 group sums equal an int64 brute-force product; the scaled output
+    equals the explicitly dequantised product computed in double."""
+    g = rng(5)
+    rows, N, K = 7, 40, 192
+    x = g.standard_normal((rows, K)).astype(np.float32)
+    w = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    wq, ws = ora.quant_w4g32(w)
+    aq, sa = ora.quant_act_i8(x)
+    out, isum = ora.linear_w4a8(aq, sa, wq, ws, want_isum=True)
+    brute = np.einsum("rgc,ogc->rog", aq.reshape(rows, K // 32, 32).astype(np.int64),
+                      wq.reshape(N, K // 32, 32).astype(np.int64))
+    assert np.array_equal(isum.astype(np.int64), brute)
+    assert np.abs(brute).max() <= 32 * 8 * 128
+    wdq = (wq.reshape(N, K // 32, 32) * ws[..., None].astype(np.float64)).reshape(N, K)
+    xdq = aq.astype(np.float64) * sa[:, None].astype(np.float64)
+    ref = xdq @ wdq.T
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-15)
+
+
+# ----------------------------------------------------------------- router
+def _f32_round(fr: Fraction) -> Fraction:
+    """Round an exact rational to the nearest FP32 value, ties to even (normal range)."""
+    if fr == 0:
+        return Fraction(0)
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** (e - 23)
+    n = a / ulp
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * fl * ulp
+
+
+def test_router_logit_exact_rational_emulation(ora):
+    """Brute force: every fma and every tree addition of the router's fixed order
+    evaluated in exact rational arithmetic with one FP32 rounding each."""
+    g = rng(6)
+    T, d, E = 3, 128, 5
+    x = g.standard_normal((T, d)).astype(np.float32)
+    wr = (g.standard_normal((E, d)) * 0.02).astype(np.float32)
+    bias = g.standard_normal(E).astype(np.float32)
+    _, _, logits = ora.router(x, wr, bias, k=2)
+    for t in range(T):
+        for e in range(E):
+            p = [Fraction(0)] * 64
+            for j in range(d):
+                p[j % 64] = _f32_round(Fraction(float(x[t, j])) * Fraction(float(wr[e, j])) + p[j % 64])
+            s = 1
+            while s < 64:
+                for l in range(0, 64, 2 * s):
+                    p[l] = _f32_round(p[l] + p[l + s])
+                s *= 2
+            ref = _f32_round(p[0] + Fraction(float(bias[e])))
+            assert Fraction(float(logits[t, e])) == ref
+
+
+def test_router_against_double(ora):
+    g = rng(7)
+    T, d, E, k = 256, 768, 60, 4
+    x = g.standard_normal((T, d)).astype(np.float32)
+    wr = (g.standard_normal((E, d)) * 0.02).astype(np.float32)
+    idx, w, logits = ora.router(x, wr, None, k=k)
+    l64 = x.astype(np.float64) @ wr.astype(np.float64).T
+    bound = d * 2.0 ** -23 * (np.abs(x).astype(np.float64) @ np.abs(wr).astype(np.float64).T)
+    assert np.all(np.abs(logits - l64) <= bound)
+    # selection equals the double-precision ranking wherever the margin is clear
+    srt = np.argsort(-l64, axis=1, kind="stable")
+    clear = (np.take_along_axis(l64, srt[:, k - 1:k], 1) - np.take_along_axis(l64, srt[:, k:k + 1], 1))[:, 0] \
+        > 4 * bound.max()
+    for t in np.nonzero(clear)[0]:
+        assert set(idx[t]) == set(srt[t, :k])
+    assert clear.mean() > 0.9
+    # idx listed by descending logit, distinct
+    assert np.all(np.diff(np.take_along_axis(logits, idx, 1), axis=1) <= 0)
+    assert all(len(set(r)) == k for r in idx)
+    # gate weights: softmax over all E (library routine), not renormalised
+    lg = logits.astype(np.float64)
+    p = np.exp(lg - lg.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    np.testing.assert_allclose(w, np.take_along_axis(p, idx, 1), rtol=1e-12)
+    assert np.all(w.sum(1) < 1.0)
+
+
+def test_router_full_k_sums_to_one(ora):
+    g = rng(8)
+    x = g.standard_normal((16, 64)).astype(np.float32)
+    wr = g.standard_normal((8, 64)).astype(np.float32)
+    idx, w, logits = ora.router(x, wr, None, k=8)
+    np.testing.assert_allclose(w.sum(1), 1.0, atol=1e-12)
+    assert np.all(np.sort(idx, 1) == np.arange(8))
+
+
+def test_router_ties_and_forced_bias(ora):
+    g = rng(9)
+    x = g.standard_normal((10, 128)).astype(np.float32)
+    row = (g.standard_normal(128) * 0.02).astype(np.float32)
+    wr = np.tile(row, (60, 1))
+    idx, w, _ = ora.router(x, wr, None, k=4)
+    assert np.all(idx == np.arange(4))             # equal logits: lowest index first
+    np.testing.assert_allclose(w, 1 / 60, rtol=1e-12)
+    wr2 = (g.standard_normal((60, 128)) * 0.02).astype(np.float32)
+    bias = np.zeros(60, np.float32)
+    bias[[7, 19, 33, 58]] = [100, 101, 102, 103]
+    idx2, _, _ = ora.router(x, wr2, bias, k=4)
+    assert np.all(idx2 == [58, 33, 19, 7])
+
+
+def test_router_sigmoid_gate(ora):
+    g = rng(10)
+    x = g.standard_normal((32, 128)).astype(np.float32)
+    wr = (g.standard_normal((60, 128)) * 0.1).astype(np.float32)
+    i_s, w_s, lg = ora.router(x, wr, None, k=4, gating=0)
+    i_g, w_g, _ = ora.router(x, wr, None, k=4, gating=1)
+    assert np.array_equal(i_s, i_g)                # both gates are monotone in the logit
+    sel = np.take_along_axis(lg.astype(np.float64), i_g, 1)
+    ref = expit(sel) / expit(sel).sum(1, keepdims=True)
+    np.testing.assert_allclose(w_g, ref, rtol=1e-12)
+
+
+# ----------------------------------------------------------------- routing
+def test_route_invariants_and_stable_sort(ora):
+    g = rng(11)
+    T, E, k = 300, 60, 4
+    idx = np.stack([g.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    off, perm, inv = ora.route(idx, E)
+    flat = idx.reshape(-1)
+    assert off[0] == 0 and off[E] == T * k
+    assert np.array_equal(np.diff(off), np.bincount(flat, minlength=E))
+    assert np.array_equal(np.sort(perm), np.arange(T * k))
+    assert np.array_equal(inv[perm], np.arange(T * k))
+    assert np.array_equal(perm, np.argsort(flat, kind="stable"))  # library stable sort
+    for e in range(E):
+        seg = perm[off[e]:off[e + 1]]
+        assert np.all(flat[seg] == e) and np.all(np.diff(seg) > 0)
+
+
+def test_route_rejects_bad_ids(ora):
+    with pytest.raises(ValueError):
+        ora.route(np.array([[0, 61]], np.int32), 60)
+
+
+# ----------------------------------------------------------------- FFN and layer
+def _dense_swiglu(x, wgu, wd):
+    h = wd.shape[1]
+    gu = x @ wgu.T
+    a = gu[:, :h] * expit(gu[:, :h]) * gu[:, h:]
+    return a @ wd.T
+
+
+def _mk(E, d, h, hs, seed, std=0.02):
+    g = rng(seed)
+    wr = (g.standard_normal((E, d)) * std).astype(np.float32)
+    wgu = (g.standard_normal((E, 2 * h, d)) * std).astype(np.float32)
+    wd = (g.standard_normal((E, d, h)) * std).astype(np.float32)
+    sgu = (g.standard_normal((2 * hs, d)) * std).astype(np.float32) if hs else None
+    sd = (g.standard_normal((d, hs)) * std).astype(np.float32) if hs else None
+    return wr, wgu, wd, sgu, sd
+
+
+def test_ffn_w4a8_against_dequantised_double(ora):
+    g = rng(12)
+    d, h, rows = 256, 128, 24
+    x = g.standard_normal((rows, d)).astype(np.float32)
+    wgu = (g.standard_normal((2 * h, d)) * 0.02).astype(np.float32)
+    wd = (g.standard_normal((d, h)) * 0.02).astype(np.float32)
+    guq, gus = ora.quant_w4g32(wgu)
+    dq, ds = ora.quant_w4g32(wd)
+    xq, sx = ora.quant_act_i8(x)
+    hq, hs, f = ora.ffn_w4a8(xq, sx, guq, gus, dq, ds)
+    W = lambda q, s: (q.reshape(q.shape[0], -1, 32) * s[..., None].astype(np.float64)).reshape(q.shape)
+    xd = xq * sx[:, None].astype(np.float64)
+    gu = xd @ W(guq, gus).T
+    a = gu[:, :h] * expit(gu[:, :h]) * gu[:, h:]
+    # hidden row re-quantised per row, then the down product on the dequantised row
+    hd = hq * hs[:, None].astype(np.float64)
+    amax = np.abs(a).max(1)
+    np.testing.assert_allclose(hs, 2 * amax / 255, rtol=1e-6)
+    assert np.all(np.abs(hd - a) <= hs[:, None] * 0.5 * (1 + 1e-4))
+    np.testing.assert_allclose(f, hd @ W(dq, ds).T, rtol=1e-12, atol=1e-14)
+    # and the whole thing is close to the unquantised FP32 FFN
+    ref = _dense_swiglu(x.astype(np.float64), wgu.astype(np.float64), wd.astype(np.float64))
+    assert np.abs(f - ref).max() / np.abs(ref).max() < 0.3
+
+
+def test_degenerate_single_expert_is_dense_swiglu(ora):
+    """E = 1, k = 1, no shared expert: the gate is exp(0)/1 = 1 and the layer is
+    a plain dense SwiGLU FFN."""
+    g = rng(13)
+    d, h, T = 128, 64, 20
+    x = g.standard_normal((T, d)).astype(np.float32)
+    wr, wgu, wd, _, _ = _mk(1, d, h, 0, 14)
+    r = ora.forward(x, wr, None, wgu, wd, None, None, k=1, wfmt="f32")
+    assert np.all(r.w == 1.0) and np.all(r.idx == 0)
+    ref = _dense_swiglu(x.astype(np.float64), wgu[0].astype(np.float64), wd[0].astype(np.float64))
+    np.testing.assert_allclose(r.y, ref, rtol=1e-12, atol=1e-15)
+    ri = ora.forward(x, wr, None, wgu, wd, None, None, k=1, wfmt="int4g32")
+    assert np.abs(ri.y - ref).max() / np.abs(ref).max() < 0.3
+
+
+def test_k_equals_E_is_dense_softmax_mixture(ora):
+    g = rng(15)
+    E, d, h, hs, T = 6, 64, 64, 64, 12
+    x = g.standard_normal((T, d)).astype(np.float32)
+    wr, wgu, wd, sgu, sd = _mk(E, d, h, hs, 16, std=0.2)
+    r = ora.forward(x, wr, None, wgu, wd, sgu, sd, k=E, wfmt="f32")
+    lg = r.logits.astype(np.float64)
+    p = np.exp(lg - lg.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    X = x.astype(np.float64)
+    ref = sum(p[:, e:e + 1] * _dense_swiglu(X, wgu[e].astype(np.float64), wd[e].astype(np.float64))
+              for e in range(E))
+    ref += _dense_swiglu(X, sgu.astype(np.float64), sd.astype(np.float64))
+    np.testing.assert_allclose(r.y, ref, rtol=1e-10, atol=1e-13)
+
+
+@pytest.mark.parametrize("wfmt", ["f32", "int4g32"])
+def test_dense_masked_bruteforce(ora, wfmt):
+    """Every expert evaluated on every token, then masked by the top-k choice,
+    equals the sparse layer."""
+    g = rng(17)
+    E, d, h, hs, T, k = 8, 64, 64, 64, 16, 3
+    x = g.standard_normal((T, d)).astype(np.float32)
+    wr, wgu, wd, sgu, sd = _mk(E, d, h, hs, 18, std=0.1)
+    r = ora.forward(x, wr, None, wgu, wd, sgu, sd, k=k, wfmt=wfmt)
+    lg = r.logits.astype(np.float64)
+    p = np.exp(lg - lg.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    mask = np.zeros((T, E))
+    np.put_along_axis(mask, r.idx, 1.0, 1)
+    if wfmt == "f32":
+        X = x.astype(np.float64)
+        allf = np.stack([_dense_swiglu(X, wgu[e].astype(np.float64), wd[e].astype(np.float64))
+                         for e in range(E)], 1)
+        ys = _dense_swiglu(X, sgu.astype(np.float64), sd.astype(np.float64))
+        tol = 1e-12
+    else:
+        xq, sx = ora.quant_act_i8(x)
+        allf = np.stack([ora.ffn_w4a8(xq, sx, *ora.quant_w4g32(wgu[e]), *ora.quant_w4g32(wd[e]))[2]
+                         for e in range(E)], 1)
+        ys = ora.ffn_w4a8(xq, sx, *ora.quant_w4g32(sgu), *ora.quant_w4g32(sd))[2]
+        tol = 1e-12
+    ref = np.einsum("te,ted->td", mask * p, allf) + ys
+    np.testing.assert_allclose(r.y, ref, rtol=tol, atol=1e-14)
+    np.testing.assert_allclose(r.ys, ys, rtol=tol, atol=1e-15)
+    np.testing.assert_allclose(r.f, np.take_along_axis(allf, r.idx[..., None], 1), rtol=tol, atol=1e-15)
+
+
+def test_shared_expert_reaches_every_token(ora):
+    g = rng(19)
+    E, d, h, hs, T = 60, 128, 64, 256, 40
+    x = g.standard_normal((T, d)).astype(np.float32)
+    wr, wgu, wd, sgu, sd = _mk(E, d, h, hs, 20)
+    for wfmt in ("f32", "int4g32"):
+        r = ora.forward(x, wr, None, wgu, np.zeros_like(wd), sgu, sd, k=4, wfmt=wfmt)
+        assert np.array_equal(r.y, r.ys) and np.all(np.abs(r.ys).max(1) > 0)
+        r0 = ora.forward(x, wr, None, wgu, wd, np.zeros_like(sgu), np.zeros_like(sd), k=4, wfmt=wfmt)
+        assert np.all(r0.ys == 0)
+
+
+def test_token_permutation_equivariance(ora):
+    g = rng(21)
+    E, d, h, hs, T = 60, 128, 64, 256, 33
+    x = g.standard_normal((T, d)).astype(np.float32)
+    wr, wgu, wd, sgu, sd = _mk(E, d, h, hs, 22)
+    pi = g.permutation(T)
+    a = ora.forward(x, wr, None, wgu, wd, sgu, sd, k=4)
+    b = ora.forward(x[pi], wr, None, wgu, wd, sgu, sd, k=4)
+    assert np.array_equal(a.y[pi], b.y) and np.array_equal(a.idx[pi], b.idx)
+
+
+def test_expert_relabelling(ora):
+    g = rng(23)
+    E, d, h, hs, T = 60, 128, 64, 128, 25
+    x = g.standard_normal((T, d)).astype(np.float32)
+    wr, wgu, wd, sgu, sd = _mk(E, d, h, hs, 24)
+    sigma = g.permutation(E)              # new label i holds old expert sigma[i]
+    a = ora.forward(x, wr, None, wgu, wd, sgu, sd, k=4)
+    b = ora.forward(x, wr[sigma], None, wgu[sigma], wd[sigma], sgu, sd, k=4)
+    assert np.array_equal(sigma[b.idx], a.idx)
+    np.testing.assert_allclose(b.y, a.y, rtol=1e-12, atol=1e-15)
+
+
+def test_layer_routing_properties(ora):
+    g = rng(25)
+    E, d, h, hs, T, k = 60, 256, 64, 256, 64, 4
+    x = g.standard_normal((T, d)).astype(np.float32)
+    wr, wgu, wd, sgu, sd = _mk(E, d, h, hs, 26)
+    r = ora.forward(x, wr, None, wgu, wd, sgu, sd, k=k)
+    assert all(len(set(row)) == k for row in r.idx)      # k distinct experts per token
+    off, perm, inv = ora.route(r.idx, E)
+    assert off[E] == T * k and np.bincount(r.idx.reshape(-1), minlength=E).sum() == T * k
+
+
+def test_bf16_rounding_matches_torch(ora):
+    torch = pytest.importorskip("torch")
+    x = (rng(27).standard_normal(100_000) * 10).astype(np.float32)
+    x[:4] = [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 0.0]   # exact ties
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(ora.round_bf16(x), ref)
+
+
+def test_bf16_layer_close_to_f32(ora):
+    g = rng(28)
+    E, d, h, hs, T = 60, 128, 64, 256, 16
+    x = g.standard_normal((T, d)).astype(np.float32)
+    wr, wgu, wd, sgu, sd = _mk(E, d, h, hs, 29)
+    a = ora.forward(x, wr, None, wgu, wd, sgu, sd, k=4, wfmt="f32")
+    b = ora.forward(x, wr, None, wgu, wd, sgu, sd, k=4, wfmt="bf16")
+    assert np.array_equal(a.idx, b.idx)
+    assert np.all(ora.round_bf16(b.y.astype(np.float32)) == b.y)
+    assert np.abs(a.y - b.y).max() / np.abs(a.y).max() < 2e-2
+
+
+def test_combine_closed_form(ora):
+    g = rng(30)
+    f = g.standard_normal((5, 4, 16))
+    w = g.random((5, 4))
+    ys = g.standard_normal((5, 16))
+    np.testing.assert_allclose(ora.combine(f, w, ys), np.einsum("tj,tjd->td", w, f) + ys, rtol=1e-14)
+    np.testing.assert_allclose(ora.combine(f, w, None), np.einsum("tj,tjd->td", w, f), rtol=1e-14)
+
+
+def test_rmsnorm_closed_form(ora):
+    x = np.full((2, 64), 3.0, np.float32)
+    x[1] = -3.0
+    y = ora.rmsnorm(x, eps=0.0)
+    np.testing.assert_allclose(y, np.sign(x), rtol=1e-15)
+    z = rng(31).standard_normal((4, 96)).astype(np.float32)
+    yz = ora.rmsnorm(z, eps=0.0)
+    np.testing.assert_allclose((yz ** 2).mean(1), 1.0, rtol=1e-12)
+
+
+def test_oracle_rejects_bad_shapes(ora):
+    with pytest.raises(ValueError):
+        ora.quant_w4g32(np.zeros((2, 40), np.float32))
+    with pytest.raises(ValueError):
+        ora.router(np.zeros((2, 100), np.float32), np.zeros((4, 100), np.float32), None, k=2)
+
+
+# ----------------------------------------------------------------- printed sizes
+def test_layer_shapes_reproduce_printed_parameter_counts():
+    """Routed hidden d/2 (d_ff = 4d split g = 8 ways), shared hidden 4x that,
+    60 experts, top-4, FP32 router [E, d], GQA with 4 KV heads of 64, and a
+    128K tied vocabulary reproduce the printed active and total counts of
+    MobileMoE-S/M/L, with 20/26/32 layers (d/n_l close to 40)."""
+    g = {e["key"]: e for e in json.load(open(os.path.join(GOLDEN, "mobilemoe_printed_shapes.json")))["entries"]}
+    s = wl.WORKLOADS["s_prefill"]
+    assert (s.d, s.h) == tuple(g["s_expert_shape"]["value"])
+    assert s.E == g["routed_experts"]["value"] and s.k == g["top_k"]["value"]
+    for name, key, n_l in (("s_prefill", "S", 20), ("m_prefill", "M", 26), ("l_prefill", "L", 32)):
+        w = wl.WORKLOADS[name]
+        assert w.h * g["granularity"]["value"] == g["ffn_expansion_ratio"]["value"] * w.d
+        assert w.hs == g["shared_expert_size_ratio"]["value"] * w.h
+        act, tot = wl.param_counts(w.d, n_l, n_kv=g["kv_heads"]["value"], d_head=g["head_dim"]["value"])
+        assert abs(act - g[f"active_params_{key}"]["value"]) <= g[f"active_params_{key}"]["tol"]
+        assert abs(tot - g[f"total_params_{key}"]["value"]) <= g[f"total_params_{key}"]["tol"]
+        assert abs(w.d / n_l - g["aspect_ratio_d_over_layers"]["value"]) <= g["aspect_ratio_d_over_layers"]["tol"]
