@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Throughput of the MobileMoE MoE-FFN layer forward (eq. (*)) on one MI355X.
+
+Default workload: the MobileMoE-S-shaped layer, prefill of 2048 tokens, INT4
+group-32 weights with FP32 scales, per-token INT8 activations, 60 routed
+experts (top-4) plus the shared expert.  One step = the seven library calls
+(router/top-k, route/permute, activation quantisation, routed gate/up+SwiGLU,
+routed down, shared expert, combine) over one batch of tokens already resident
+in HBM.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--batch B]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+INT8_MFMA_PEAK_TOPS = 5000.0    # MI355X dense int8 MFMA
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+FP32_VALU_PEAK_TFLOPS = 157.3
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="s_prefill")
+    ap.add_argument("--batch", type=int, default=None, help="tokens per step (decode batch) override")
+    ap.add_argument("--layers", type=int, default=None, help="decode stack depth override")
+    ap.add_argument("--instances", type=int, default=0,
+                    help="distinct weight sets rotated across steps (0: enough to exceed the 256 MB MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
+    return ap.parse_args()
+
+
+def layer_work(w, T, counts=None):
+    """Algorithmic work of one layer call: int8 ops per expert product and
+    bytes the decode path must stream."""
+    ops = {
+        "router": 2 * T * w.E * w.d,
+        "gateup": 2 * T * w.k * 2 * w.h * w.d,
+        "down": 2 * T * w.k * w.d * w.h,
+        "shared": 2 * T * 3 * w.d * w.hs,
+    }
+    wb = {"int4g32": 0.5 + 4 / 32, "bf16": 2.0, "f32": 4.0}[w.wfmt]
+    B_r = 3 * w.d * w.h * wb
+    B_s = 3 * w.d * w.hs * wb
+    return ops, B_r, B_s
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the layer shards by tokens with replicated weights; see DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_moe_ffn_amd import binding as B
+    from sparse_moe_ffn_amd import workloads as wl
+    from sparse_moe_ffn_amd.layer import MoELayer
+
+    B.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = wl.WORKLOADS[args.workload]
+    if args.batch is not None:
+        w = w.with_(T=args.batch)
+    if args.layers is not None:
+        w = w.with_(layers=args.layers)
+    decode = w.mode == "decode"
+    T = w.T
+
+    # ---- weights: distinct layers (decode stack) or rotated instances (single layer)
+    t0 = time.time()
+    wb = {"int4g32": 0.625, "bf16": 2.0, "f32": 4.0}[w.wfmt]
+    layer_bytes = (w.E * 3 * w.d * w.h + 3 * w.d * w.hs) * wb + w.E * w.d * 4
+    if w.layers > 1:
+        n_inst = w.layers
+    elif args.instances > 0:
+        n_inst = args.instances
+    else:
+        n_inst = int(min(16, max(1, math.ceil(1.15 * MALL_BYTES / layer_bytes))))
+    layers = []
+    for i in range(n_inst):
+        lw = wl.layer_weights(w, layer=i)
+        layers.append(MoELayer.from_workload(w, lw, device=dev))
+        del lw
+    for L in layers:
+        L.buffers(T)
+    print(f"[bench] {w.name}: T={T} layers/instances={n_inst} weights {n_inst * layer_bytes / 1e6:.0f} MB "
+          f"setup {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    n_inputs = args.warmup + args.steps if decode else 1
+    xs = [torch.from_numpy(wl.tokens(w, step=s)).to(dev) for s in range(n_inputs)]
+    nxt = torch.empty((T, w.d), dtype=torch.float32, device=dev)
+
+    def step(s: int):
+        if decode:
+            cur = xs[s % n_inputs]
+            for L in layers:
+                y = L.forward(cur)
+                B.rmsnorm_f32(T, w.d, 1e-5, y, nxt)
+                cur = nxt
+        else:
+            layers[s % n_inst].forward(xs[0])
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for s in range(args.steps):
+        step(args.warmup + s)
+    e1.record(st)
+    e1.synchronize()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tok_s = T / (ms / 1e3)
+
+    # ---- per-call durations with HIP events on the launch stream
+    calls = ["router", "route", "act_quant", "gateup", "down", "shared", "combine"]
+    if w.wfmt != "int4g32":
+        calls.remove("act_quant")
+    if not w.hs:
+        calls.remove("shared")
+    n_time = max(5, min(args.steps, 20))
+    acc = {c: 0.0 for c in calls}
+    x0 = xs[0]
+    for s in range(n_time):
+        L = layers[s % len(layers)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+        ev[0].record(st)
+        for i, c in enumerate(calls):
+            if c == "router":
+                L.router(x0, T)
+            elif c == "route":
+                L.route(T)
+            elif c == "act_quant":
+                L.act_quant(x0, T)
+            elif c == "gateup":
+                L.gateup(x0, T)
+            elif c == "down":
+                L.down(T)
+            elif c == "shared":
+                L.shared(x0, T)
+            elif c == "combine":
+                L.combine(T)
+            ev[i + 1].record(st)
+        ev[-1].synchronize()
+        for i, c in enumerate(calls):
+            acc[c] += ev[i].elapsed_time(ev[i + 1])
+    per_call_us = {c: 1e3 * v / n_time for c, v in acc.items()}
+
+    ops, B_r, B_s = layer_work(w, T)
+    # decode: bytes of the selected experts' weights (distinct experts counted
+    # from the ids of the last step) + shared + router + activations
+    L0 = layers[0]
+    n_distinct = int(np.unique(L0.idx.cpu().numpy()).size)
+    if decode:
+        dom = max(("gateup", "down", "shared"), key=lambda c: per_call_us.get(c, 0.0))
+        by_call = {
+            "gateup": n_distinct * (2 * w.h * w.d) * wb,
+            "down": n_distinct * (w.d * w.h) * wb,
+            "shared": B_s,
+        }
+        achieved = by_call[dom] / (per_call_us[dom] * 1e-6) / 1e9
+        roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None,
+                "algorithmic_bytes_per_launch": by_call[dom], "launch_us": round(per_call_us[dom], 3)}
+    else:
+        dom = max(("gateup", "down", "shared"), key=lambda c: per_call_us.get(c, 0.0))
+        peak = INT8_MFMA_PEAK_TOPS if w.wfmt == "int4g32" else (
+            BF16_MFMA_PEAK_TFLOPS if w.wfmt == "bf16" else FP32_VALU_PEAK_TFLOPS)
+        achieved = ops[dom] / (per_call_us[dom] * 1e-6) / 1e12
+        roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 3), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 5), "traffic": None,
+                "algorithmic_ops_per_launch": ops[dom], "launch_us": round(per_call_us[dom], 3)}
+
+    # ---- CPU oracle on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        cores = max(1, min(16, os.cpu_count() or 1))
+        lw = wl.layer_weights(w, layer=0)
+        xall = wl.tokens(w, step=0)
+        n = min(T, 16)
+        t1 = time.time()
+        oracle.forward(xall[:n], lw.wr, lw.bias, lw.w_gu, lw.w_d, lw.ws_gu, lw.ws_d, k=w.k,
+                       wfmt=w.wfmt, nthreads=cores)
+        dt = time.time() - t1
+        if dt < args.cpu_seconds / 4 and n < T:
+            n = int(min(T, max(n, n * args.cpu_seconds / max(dt, 1e-3))))
+            t1 = time.time()
+            oracle.forward(xall[:n], lw.wr, lw.bias, lw.w_gu, lw.w_d, lw.ws_gu, lw.ws_d, k=w.k,
+                           wfmt=w.wfmt, nthreads=cores)
+            dt = time.time() - t1
+        layers_per_step = w.layers if decode else 1
+        cpu = {"value": round(n / dt / layers_per_step, 2), "unit": "tokens/s", "cores": cores,
+               "kind": "oracle",
+               "sample": f"{n} of the {T} tokens of {w.name}, one layer, oracle.forward (includes its "
+                         f"per-call weight quantisation), {dt:.1f}s"
+                         + (f"; per-step rate = per-layer rate / {layers_per_step} layers" if decode else "")}
+
+    total_ops = (ops["gateup"] + ops["down"] + ops["shared"]) * (w.layers if decode else 1)
+    out = {
+        "metric": "MoE-layer tokens/s (prefill T=2048/8192, decode B=1-64) + % HBM/MFMA peak",
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"int4g32": "int8", "bf16": "bf16", "f32": "f32"}[w.wfmt],
+        "data": "synthetic",
+        "config": {"workload": w.name, "mode": w.mode, "tokens_per_step": T, "d_model": w.d,
+                   "experts": w.E, "top_k": w.k, "hidden": w.h, "shared_hidden": w.hs,
+                   "weights": w.wfmt, "layers": w.layers, "router_bias": w.bias,
+                   "weight_sets_rotated": n_inst, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "layer_int8_frac": round(total_ops / (ms * 1e-3) / 1e12 / INT8_MFMA_PEAK_TOPS, 5)
+        if w.wfmt == "int4g32" else None,
+        "per_call_us": {c: round(v, 3) for c, v in per_call_us.items()},
+        "distinct_experts_last_step": n_distinct,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

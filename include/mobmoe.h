@@ -1,0 +1,286 @@
+/*
+ * libmobmoe -- MobileMoE MoE-FFN layer forward on AMD Instinct MI355X (gfx950).
+ *
+ * The layer (eq. (*) of "MobileMoE: Scaling On-Device Mixture of Experts",
+ * close reading on paper-archivist.com, section "MoE preliminaries and three
+ * design factors"):
+ *
+ *     y = sum_{i in top-k(x)} router_i(x) * FFN_i(x)  +  FFN_s(x)
+ *
+ * with E routed SwiGLU experts of hidden size h, top-k selection by an FP32
+ * router, one always-on shared SwiGLU expert of hidden size h_s, INT4
+ * symmetric group-32 weights with FP32 scales (eq. (6), section
+ * "Quantisation-aware training") and per-token dynamic INT8 activations.
+ * The split into calls follows the custom MoE operator of the section
+ * "Custom MoE kernel": top-k selection, count-sort of tokens by expert,
+ * one fused gate/up product per expert, SwiGLU, down product, and a weighted
+ * scatter back through the inverse permutation.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every call returns an mm_status and never throws or aborts.
+ *  - All pointers named "device" point to device memory (hipMalloc or a torch
+ *    CUDA tensor); "host" pointers point to host memory.  Device pointers must
+ *    be 16-byte aligned (MM_ERR_ALIGN otherwise).
+ *  - The caller owns every buffer, including workspace.  The library keeps no
+ *    pointer past the call and allocates no device memory.
+ *  - Work is queued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    default stream).  No call synchronises or reads device memory back.
+ *    Buffers must stay alive until the queued work has finished.
+ *  - All argument checks happen on the host before anything is queued; a
+ *    rejected call queues nothing.  A HIP launch failure returns MM_ERR_HIP;
+ *    mm_last_error_string() then describes it (per host thread).
+ *  - T == 0 (no tokens) is a valid no-op returning MM_OK.
+ *  - Inputs and outputs must not alias.
+ *  - Results are deterministic: identical inputs give identical bits for any
+ *    stream.  No floating-point atomics are used.
+ *
+ * Shape limits of this version: 1 <= E <= 64, 1 <= k <= min(8, E),
+ * d_model, hidden and shared_hidden multiples of 64 (shared_hidden may be 0:
+ * no shared expert), T*k <= 2^24.
+ *
+ * "Sorted order" below means expert-contiguous order: position p in
+ * [expert_offsets[e], expert_offsets[e+1]) holds one (token, slot) routed to
+ * expert e, and perm[p] = token*k + slot.
+ */
+#ifndef MOBMOE_H
+#define MOBMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mm_status {
+  MM_OK = 0,
+  MM_ERR_NULL = 1,       /* a required pointer is NULL                      */
+  MM_ERR_SHAPE = 2,      /* a size is out of range or inconsistent          */
+  MM_ERR_ALIGN = 3,      /* a device pointer is not 16-byte aligned         */
+  MM_ERR_FORMAT = 4,     /* unknown weight format, gating rule or dtype     */
+  MM_ERR_WORKSPACE = 5,  /* workspace smaller than mm_workspace_bytes()     */
+  MM_ERR_HIP = 6         /* a HIP runtime call or kernel launch failed      */
+} mm_status;
+
+/* Weight formats (mm_layer_desc.wfmt). */
+enum {
+  MM_W_F32 = 0,      /* FP32 weights, FP32 activations, no quantisation         */
+  MM_W_INT4G32 = 1,  /* INT4 group-32 weights (prepacked), INT8 activations     */
+  MM_W_BF16 = 2      /* BF16 weights and activations, FP32 accumulation         */
+};
+
+/* Gating rules (mm_layer_desc.gating). */
+enum {
+  MM_GATE_SOFTMAX = 0,      /* softmax over all E logits, no renormalisation    */
+  MM_GATE_SIGMOID_NORM = 1  /* sigmoid of each selected logit, divided by their
+                               sum over the k selected (training-time gate of the
+                               "Pre-training" section)                           */
+};
+
+/* Output dtypes (mm_layer_desc.out_dtype): y of mm_combine. */
+enum { MM_OUT_F32 = 0, MM_OUT_BF16 = 1 };
+
+/* Workspace queries (mm_workspace_bytes `which`). */
+enum {
+  MM_WS_ROUTE = 0,
+  MM_WS_GATEUP = 1,
+  MM_WS_DOWN = 2,
+  MM_WS_SHARED = 3,
+  MM_WS_MAX = 4      /* the largest of the above: one buffer serves every call */
+};
+
+typedef struct mm_layer_desc {
+  int32_t d_model;        /* d: token width                                   */
+  int32_t n_experts;      /* E: routed experts                                */
+  int32_t hidden;         /* h: routed expert hidden size                     */
+  int32_t shared_hidden;  /* h_s: shared expert hidden size, 0 = none         */
+  int32_t top_k;          /* k: experts per token                             */
+  int32_t wfmt;           /* MM_W_*                                           */
+  int32_t gating;         /* MM_GATE_*                                        */
+  int32_t out_dtype;      /* MM_OUT_*                                         */
+} mm_layer_desc;
+
+/*
+ * A weight tensor.  For MM_W_INT4G32 `data` is the prepacked nibble buffer and
+ * `scales` its prepacked FP32 scales, both written by mm_prepack_int4g32().
+ * For MM_W_F32 `data` is FP32 row-major and for MM_W_BF16 it is BF16
+ * (uint16) row-major; `scales` must then be NULL.  Expert tensors are stacked
+ * [E][rows][cols].  Gate/up tensors have 2*h rows: rows 0..h-1 are the gate
+ * projection and rows h..2h-1 the up projection.
+ */
+typedef struct mm_weight {
+  const void* data;     /* device */
+  const float* scales;  /* device, INT4 only */
+} mm_weight;
+
+/* ---------------------------------------------------------------- helpers */
+
+const char* mm_version(void);
+const char* mm_status_string(mm_status s);
+/* Description of the last failure on the calling host thread ("" if none). */
+const char* mm_last_error_string(void);
+
+/* Bytes of caller workspace the named call needs for T tokens (0 if none).
+ * Returns 0 for an invalid descriptor. */
+size_t mm_workspace_bytes(const mm_layer_desc* desc, int64_t T, int32_t which);
+
+/*
+ * Offline weight quantisation, eq. (6) with b = 4 and groups of 32 along the
+ * input (column) dimension:  s_g = (2 * max|W_g|) / 15 in FP32 with IEEE
+ * division, q = clamp(round_half_even(W / s_g), -8, 7); an all-zero group has
+ * s_g = 0 and q = 0.
+ *   w       device FP32 [rows][cols], cols % 32 == 0
+ *   q       device uint8 [rows][cols/2], canonical nibble layout: column c is
+ *           in byte c/2, low nibble for even c, 4-bit two's complement
+ *   scales  device FP32 [rows][cols/32]
+ */
+mm_status mm_quantize_int4g32(int64_t rows, int64_t cols, const float* w, uint8_t* q,
+                              float* scales, void* stream);
+
+/* Size in bytes of the prepacked nibble buffer and of the prepacked scale
+ * buffer for a [rows][cols] INT4 matrix (rows % 32 == 0, cols % 32 == 0). */
+size_t mm_prepacked_bytes(int64_t rows, int64_t cols);
+size_t mm_prepacked_scale_bytes(int64_t rows, int64_t cols);
+
+/*
+ * Rearranges `n_mat` stacked canonical INT4 matrices [n_mat][rows][cols]
+ * (layout of mm_quantize_int4g32) into the kernels' layout.  The prepacked
+ * layout is private to this library version: pass it only to the calls below.
+ *   q_canon, s_canon   device, canonical nibbles and scales
+ *   q_out, s_out       device, n_mat * mm_prepacked_bytes / _scale_bytes
+ */
+mm_status mm_prepack_int4g32(int64_t n_mat, int64_t rows, int64_t cols, const uint8_t* q_canon,
+                             const float* s_canon, uint8_t* q_out, float* s_out, void* stream);
+
+/* FP32 -> BF16 (round to nearest even) conversion of n values (device). */
+mm_status mm_convert_bf16(int64_t n, const float* x, uint16_t* y, void* stream);
+
+/* ------------------------------------------------------- the seven calls */
+
+/*
+ * S1+S2.  FP32 router, top-k selection and gate weights (the section
+ * "Pre-training" keeps the router in FP32; eq. (*) weights each selected
+ * expert by router_i(x)).
+ *   x          device FP32 [T][d]
+ *   w_router   device FP32 [E][d]
+ *   bias       device FP32 [E] or NULL; added to every logit before selection
+ *   topk_idx   device int32 [T][k]   out: selected experts, best first
+ *   topk_w     device FP32 [T][k]    out: gate weights
+ * Logit of (t, e): 64 partial sums, partial l accumulating x[t][j]*w[e][j]
+ * with fused multiply-adds for j = l, l+64, ... ascending; then a balanced
+ * pairwise tree (pairs at distance 1, 2, 4, ..., 32); then + bias[e].  Experts
+ * are ranked by (logit descending, index ascending).  MM_GATE_SOFTMAX gives
+ * w = exp(l_i - max l) / sum over all E of exp(l_e - max l).
+ */
+mm_status mm_router_topk(const mm_layer_desc* desc, int64_t T, const float* x,
+                         const float* w_router, const float* bias, int32_t* topk_idx,
+                         float* topk_w, void* stream);
+
+/*
+ * S3.  Stable count sort of the T*k (token, slot) assignments by expert id
+ * (section "Custom MoE kernel": tokens of one expert become contiguous).
+ *   topk_idx        device int32 [T*k]
+ *   expert_offsets  device int32 [E+1]  out: start of each expert's run,
+ *                                        expert_offsets[E] = T*k
+ *   perm            device int32 [T*k]  out: sorted position -> token*k+slot
+ *   inv_perm        device int32 [T*k]  out: token*k+slot -> sorted position
+ *   ws / ws_bytes   device workspace, mm_workspace_bytes(desc, T, MM_WS_ROUTE)
+ * Within one expert's run, entries are in ascending token*k+slot order.
+ * Ids outside [0, E) are skipped (not counted, not placed); the outputs are then
+ * incomplete, but no memory outside the buffers above is touched.
+ */
+mm_status mm_route_permute(const mm_layer_desc* desc, int64_t T, const int32_t* topk_idx,
+                           int32_t* expert_offsets, int32_t* perm, int32_t* inv_perm, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/*
+ * S4.  Per-row dynamic INT8 quantisation (eq. (6) read with b = 8 and one
+ * group per row): s = (2 * max|v|) / 255, q = clamp(round_half_even(v / s),
+ * -128, 127), FP32 with IEEE division; an all-zero row has s = 0, q = 0.
+ *   x      device FP32 [rows][cols]
+ *   q      device int8 [rows][cols]    out
+ *   scale  device FP32 [rows]          out
+ */
+mm_status mm_act_quant_i8(int64_t rows, int64_t cols, const float* x, int8_t* q, float* scale,
+                          void* stream);
+
+/*
+ * S5.  Routed experts' fused gate/up product with SwiGLU (section "Custom MoE
+ * kernel"), for every sorted position p of every expert e:
+ *   g = x[t] W_gate[e]^T, u = x[t] W_up[e]^T, a = SiLU(g) * u, t = perm[p]/k.
+ * MM_W_INT4G32:  act is x_q (int8 [T][d]) with act_scale (FP32 [T]); each
+ *   output is s_x * sum_g s_w[g] * isum_g with exact int32 group sums; the row
+ *   a is re-quantised per row like mm_act_quant_i8 into h (int8 [T*k][h],
+ *   sorted order) and h_scale (FP32 [T*k]).
+ * MM_W_F32 / MM_W_BF16: act is x (FP32 [T][d]), act_scale and h_scale NULL;
+ *   h is FP32 (MM_W_F32) or BF16 (MM_W_BF16) [T*k][h], sorted order.
+ *   w_gateup        stacked [E][2h][d] (see mm_weight)
+ *   perm, expert_offsets  from mm_route_permute
+ *   ws / ws_bytes   mm_workspace_bytes(desc, T, MM_WS_GATEUP)
+ */
+mm_status mm_expert_gateup_swiglu(const mm_layer_desc* desc, int64_t T, const void* act,
+                                  const float* act_scale, const int32_t* perm,
+                                  const int32_t* expert_offsets, mm_weight w_gateup, void* h,
+                                  float* h_scale, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * S6.  Routed experts' down product: f[p] = h[p] W_down[e]^T for every sorted
+ * position p of expert e, FP32 [T*k][d] in sorted order (gate weight not yet
+ * applied).  INT4: h int8 with h_scale, exact int32 group sums then FP32
+ * scales.  F32 / BF16: h as written by mm_expert_gateup_swiglu, h_scale NULL.
+ *   w_down  stacked [E][d][h]
+ */
+mm_status mm_expert_down(const mm_layer_desc* desc, int64_t T, const void* h,
+                         const float* h_scale, const int32_t* expert_offsets, mm_weight w_down,
+                         float* f, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * S7.  The always-on shared expert (section "Divide-and-conquer architecture
+ * search", Finding 3): a dense SwiGLU FFN of hidden h_s on every token with
+ * weight 1, using the same activation input and arithmetic as the routed
+ * experts: ys [T][d] FP32.  w_gateup [2h_s][d], w_down [d][h_s].
+ *   ws / ws_bytes  mm_workspace_bytes(desc, T, MM_WS_SHARED)
+ * Returns MM_ERR_SHAPE if desc->shared_hidden == 0.
+ */
+mm_status mm_shared_expert(const mm_layer_desc* desc, int64_t T, const void* act,
+                           const float* act_scale, mm_weight w_gateup, mm_weight w_down,
+                           float* ys, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * S8.  Weighted combine through the inverse permutation (section "Custom MoE
+ * kernel"): y[t][c] = fma-chain over j = 0..k-1 of topk_w[t][j] *
+ * f[inv_perm[t*k+j]][c], then + ys[t][c] (ys may be NULL).  No atomics.
+ *   y  device [T][d], FP32 (MM_OUT_F32) or BF16 (MM_OUT_BF16)
+ */
+mm_status mm_combine(const mm_layer_desc* desc, int64_t T, const float* f,
+                     const int32_t* inv_perm, const float* topk_w, const float* ys, void* y,
+                     void* stream);
+
+/* --------------------------------------------------- around the layer */
+
+/* Row RMSNorm with unit gain used between stacked layers of the decode
+ * workload (not part of eq. (*)): y = x / sqrt(mean(x^2) + eps), FP32. */
+mm_status mm_rmsnorm_f32(int64_t rows, int64_t cols, float eps, const float* x, float* y,
+                         void* stream);
+
+/*
+ * Test-only twins of the INT4 gate/up and down calls that also write the
+ * exact int32 group sums of the same kernels:
+ *   gate/up: isum [T*k][2h][d/32] (sorted order), down: isum [T*k][d][h/32].
+ */
+mm_status mm_expert_gateup_swiglu_dbg(const mm_layer_desc* desc, int64_t T, const void* act,
+                                      const float* act_scale, const int32_t* perm,
+                                      const int32_t* expert_offsets, mm_weight w_gateup,
+                                      void* h, float* h_scale, void* ws, size_t ws_bytes,
+                                      int32_t* isum, void* stream);
+mm_status mm_expert_down_dbg(const mm_layer_desc* desc, int64_t T, const void* h,
+                             const float* h_scale, const int32_t* expert_offsets,
+                             mm_weight w_down, float* f, void* ws, size_t ws_bytes,
+                             int32_t* isum, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOBMOE_H */

@@ -1,0 +1,216 @@
+"""Thin ctypes binding of libmobmoe (include/mobmoe.h).
+
+Every function here only marshals arguments: torch device tensors become raw
+device pointers, the current torch stream becomes the HIP stream, and a
+non-OK status becomes an MMError carrying the library's message.  All
+computation happens in the library's HIP kernels.  If libmobmoe.so is missing
+the import fails loudly; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmobmoe.so")
+
+MM_OK, MM_ERR_NULL, MM_ERR_SHAPE, MM_ERR_ALIGN, MM_ERR_FORMAT, MM_ERR_WORKSPACE, MM_ERR_HIP = range(7)
+MM_W_F32, MM_W_INT4G32, MM_W_BF16 = range(3)
+MM_GATE_SOFTMAX, MM_GATE_SIGMOID_NORM = range(2)
+MM_OUT_F32, MM_OUT_BF16 = range(2)
+MM_WS_ROUTE, MM_WS_GATEUP, MM_WS_DOWN, MM_WS_SHARED, MM_WS_MAX = range(5)
+
+WFMT = {"f32": MM_W_F32, "int4g32": MM_W_INT4G32, "bf16": MM_W_BF16}
+
+# Every symbol include/mobmoe.h declares.
+EXPORTS = (
+    "mm_version", "mm_status_string", "mm_last_error_string", "mm_workspace_bytes",
+    "mm_quantize_int4g32", "mm_prepacked_bytes", "mm_prepacked_scale_bytes", "mm_prepack_int4g32",
+    "mm_convert_bf16", "mm_router_topk", "mm_route_permute", "mm_act_quant_i8",
+    "mm_expert_gateup_swiglu", "mm_expert_down", "mm_shared_expert", "mm_combine",
+    "mm_rmsnorm_f32", "mm_expert_gateup_swiglu_dbg", "mm_expert_down_dbg",
+)
+
+
+class MMError(RuntimeError):
+    def __init__(self, status: int, func: str, msg: str):
+        super().__init__(f"{func}: {STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+STATUS_NAMES = {0: "MM_OK", 1: "MM_ERR_NULL", 2: "MM_ERR_SHAPE", 3: "MM_ERR_ALIGN",
+                4: "MM_ERR_FORMAT", 5: "MM_ERR_WORKSPACE", 6: "MM_ERR_HIP"}
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("shared_hidden", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("wfmt", ctypes.c_int32),
+                ("gating", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+
+
+class Weight(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+_VP, _I64, _I32, _SZ, _F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+_DESC = ctypes.POINTER(LayerDesc)
+
+_SIGS = {
+    "mm_version": ([], ctypes.c_char_p),
+    "mm_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "mm_last_error_string": ([], ctypes.c_char_p),
+    "mm_workspace_bytes": ([_DESC, _I64, _I32], _SZ),
+    "mm_quantize_int4g32": ([_I64, _I64, _VP, _VP, _VP, _VP], ctypes.c_int),
+    "mm_prepacked_bytes": ([_I64, _I64], _SZ),
+    "mm_prepacked_scale_bytes": ([_I64, _I64], _SZ),
+    "mm_prepack_int4g32": ([_I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP], ctypes.c_int),
+    "mm_convert_bf16": ([_I64, _VP, _VP, _VP], ctypes.c_int),
+    "mm_router_topk": ([_DESC, _I64, _VP, _VP, _VP, _VP, _VP, _VP], ctypes.c_int),
+    "mm_route_permute": ([_DESC, _I64, _VP, _VP, _VP, _VP, _VP, _SZ, _VP], ctypes.c_int),
+    "mm_act_quant_i8": ([_I64, _I64, _VP, _VP, _VP, _VP], ctypes.c_int),
+    "mm_expert_gateup_swiglu": ([_DESC, _I64, _VP, _VP, _VP, _VP, Weight, _VP, _VP, _VP, _SZ, _VP],
+                                ctypes.c_int),
+    "mm_expert_gateup_swiglu_dbg": ([_DESC, _I64, _VP, _VP, _VP, _VP, Weight, _VP, _VP, _VP, _SZ,
+                                     _VP, _VP], ctypes.c_int),
+    "mm_expert_down": ([_DESC, _I64, _VP, _VP, _VP, Weight, _VP, _VP, _SZ, _VP], ctypes.c_int),
+    "mm_expert_down_dbg": ([_DESC, _I64, _VP, _VP, _VP, Weight, _VP, _VP, _SZ, _VP, _VP],
+                           ctypes.c_int),
+    "mm_shared_expert": ([_DESC, _I64, _VP, _VP, Weight, Weight, _VP, _VP, _SZ, _VP], ctypes.c_int),
+    "mm_combine": ([_DESC, _I64, _VP, _VP, _VP, _VP, _VP, _VP], ctypes.c_int),
+    "mm_rmsnorm_f32": ([_I64, _I64, _F, _VP, _VP, _VP], ctypes.c_int),
+}
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Loads libmobmoe.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m sparse_moe_ffn_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = lib
+    return _lib
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(rc: int, name: str):
+    if rc != MM_OK:
+        raise MMError(rc, name, load().mm_last_error_string().decode())
+
+
+def desc(d: int, E: int, h: int, hs: int, k: int, wfmt="int4g32", gating: int = 0,
+         out_dtype: int = MM_OUT_F32) -> LayerDesc:
+    return LayerDesc(d, E, h, hs, k, WFMT[wfmt] if isinstance(wfmt, str) else wfmt, gating, out_dtype)
+
+
+def weight(data, scales=None) -> Weight:
+    return Weight(_ptr(data), _ptr(scales))
+
+
+def version() -> str:
+    return load().mm_version().decode()
+
+
+def workspace_bytes(ds: LayerDesc, T: int, which: int = MM_WS_MAX) -> int:
+    return load().mm_workspace_bytes(ctypes.byref(ds), T, which)
+
+
+def prepacked_bytes(rows: int, cols: int) -> int:
+    return load().mm_prepacked_bytes(rows, cols)
+
+
+def prepacked_scale_bytes(rows: int, cols: int) -> int:
+    return load().mm_prepacked_scale_bytes(rows, cols)
+
+
+def quantize_int4g32(rows, cols, w, q, scales, stream=None):
+    _check(load().mm_quantize_int4g32(rows, cols, _ptr(w), _ptr(q), _ptr(scales), _stream(stream)),
+           "mm_quantize_int4g32")
+
+
+def prepack_int4g32(n_mat, rows, cols, q_canon, s_canon, q_out, s_out, stream=None):
+    _check(load().mm_prepack_int4g32(n_mat, rows, cols, _ptr(q_canon), _ptr(s_canon), _ptr(q_out),
+                                     _ptr(s_out), _stream(stream)), "mm_prepack_int4g32")
+
+
+def convert_bf16(n, x, y, stream=None):
+    _check(load().mm_convert_bf16(n, _ptr(x), _ptr(y), _stream(stream)), "mm_convert_bf16")
+
+
+def router_topk(ds, T, x, w_router, bias, topk_idx, topk_w, stream=None):
+    _check(load().mm_router_topk(ctypes.byref(ds), T, _ptr(x), _ptr(w_router), _ptr(bias),
+                                 _ptr(topk_idx), _ptr(topk_w), _stream(stream)), "mm_router_topk")
+
+
+def route_permute(ds, T, topk_idx, offsets, perm, inv_perm, ws, ws_bytes, stream=None):
+    _check(load().mm_route_permute(ctypes.byref(ds), T, _ptr(topk_idx), _ptr(offsets), _ptr(perm),
+                                   _ptr(inv_perm), _ptr(ws), ws_bytes, _stream(stream)),
+           "mm_route_permute")
+
+
+def act_quant_i8(rows, cols, x, q, scale, stream=None):
+    _check(load().mm_act_quant_i8(rows, cols, _ptr(x), _ptr(q), _ptr(scale), _stream(stream)),
+           "mm_act_quant_i8")
+
+
+def expert_gateup_swiglu(ds, T, act, act_scale, perm, offsets, w, h, h_scale, ws, ws_bytes,
+                         stream=None, isum=None):
+    lib = load()
+    if isum is None:
+        rc = lib.mm_expert_gateup_swiglu(ctypes.byref(ds), T, _ptr(act), _ptr(act_scale), _ptr(perm),
+                                         _ptr(offsets), w, _ptr(h), _ptr(h_scale), _ptr(ws), ws_bytes,
+                                         _stream(stream))
+        _check(rc, "mm_expert_gateup_swiglu")
+    else:
+        rc = lib.mm_expert_gateup_swiglu_dbg(ctypes.byref(ds), T, _ptr(act), _ptr(act_scale),
+                                             _ptr(perm), _ptr(offsets), w, _ptr(h), _ptr(h_scale),
+                                             _ptr(ws), ws_bytes, _ptr(isum), _stream(stream))
+        _check(rc, "mm_expert_gateup_swiglu_dbg")
+
+
+def expert_down(ds, T, h, h_scale, offsets, w, f, ws, ws_bytes, stream=None, isum=None):
+    lib = load()
+    if isum is None:
+        _check(lib.mm_expert_down(ctypes.byref(ds), T, _ptr(h), _ptr(h_scale), _ptr(offsets), w,
+                                  _ptr(f), _ptr(ws), ws_bytes, _stream(stream)), "mm_expert_down")
+    else:
+        _check(lib.mm_expert_down_dbg(ctypes.byref(ds), T, _ptr(h), _ptr(h_scale), _ptr(offsets), w,
+                                      _ptr(f), _ptr(ws), ws_bytes, _ptr(isum), _stream(stream)),
+               "mm_expert_down_dbg")
+
+
+def shared_expert(ds, T, act, act_scale, w_gateup, w_down, ys, ws, ws_bytes, stream=None):
+    _check(load().mm_shared_expert(ctypes.byref(ds), T, _ptr(act), _ptr(act_scale), w_gateup, w_down,
+                                   _ptr(ys), _ptr(ws), ws_bytes, _stream(stream)), "mm_shared_expert")
+
+
+def combine(ds, T, f, inv_perm, topk_w, ys, y, stream=None):
+    _check(load().mm_combine(ctypes.byref(ds), T, _ptr(f), _ptr(inv_perm), _ptr(topk_w), _ptr(ys),
+                             _ptr(y), _stream(stream)), "mm_combine")
+
+
+def rmsnorm_f32(rows, cols, eps, x, y, stream=None):
+    _check(load().mm_rmsnorm_f32(rows, cols, eps, _ptr(x), _ptr(y), _stream(stream)),
+           "mm_rmsnorm_f32")

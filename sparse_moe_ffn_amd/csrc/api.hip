@@ -1,0 +1,410 @@
+// libmobmoe C ABI: argument checks on the host, then kernel launches on the
+// caller's stream.  See include/mobmoe.h for the contract of every call.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/mobmoe.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mm_status fail(mm_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+mm_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return MM_OK;
+  snprintf(g_err, sizeof(g_err), "%s: %s", where, hipGetErrorString(e));
+  return MM_ERR_HIP;
+}
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define MM_REQUIRE(p)                                                          \
+  do {                                                                         \
+    if (!(p)) return fail(MM_ERR_NULL, "%s is NULL", #p);                \
+    if (!aligned(p)) return fail(MM_ERR_ALIGN, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+#define MM_OPTIONAL(p)                                                         \
+  do {                                                                         \
+    if ((p) && !aligned(p)) return fail(MM_ERR_ALIGN, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+constexpr int64_t kMaxSlots = int64_t(1) << 24;
+
+mm_status check_desc(const mm_layer_desc* d) {
+  if (!d) return fail(MM_ERR_NULL, "desc is NULL");
+  if (d->d_model < 64 || d->d_model % 64)
+    return fail(MM_ERR_SHAPE, "d_model %lld must be a positive multiple of 64", (long long)(d->d_model));
+  if (d->n_experts < 1 || d->n_experts > 64)
+    return fail(MM_ERR_SHAPE, "n_experts %lld must be in [1, 64]", (long long)(d->n_experts));
+  if (d->hidden < 64 || d->hidden % 64)
+    return fail(MM_ERR_SHAPE, "hidden %lld must be a positive multiple of 64", (long long)(d->hidden));
+  if (d->shared_hidden < 0 || d->shared_hidden % 64)
+    return fail(MM_ERR_SHAPE, "shared_hidden %lld must be 0 or a multiple of 64",
+                (long long)d->shared_hidden);
+  if (d->top_k < 1 || d->top_k > 8 || d->top_k > d->n_experts)
+    return fail(MM_ERR_SHAPE, "top_k %lld must be in [1, min(8, n_experts)]", (long long)(d->top_k));
+  if (d->wfmt < MM_W_F32 || d->wfmt > MM_W_BF16)
+    return fail(MM_ERR_FORMAT, "unknown weight format %lld", (long long)(d->wfmt));
+  if (d->gating < MM_GATE_SOFTMAX || d->gating > MM_GATE_SIGMOID_NORM)
+    return fail(MM_ERR_FORMAT, "unknown gating rule %lld", (long long)(d->gating));
+  if (d->out_dtype < MM_OUT_F32 || d->out_dtype > MM_OUT_BF16)
+    return fail(MM_ERR_FORMAT, "unknown output dtype %lld", (long long)(d->out_dtype));
+  return MM_OK;
+}
+
+mm_status check_T(const mm_layer_desc* d, int64_t T) {
+  if (T < 0) return fail(MM_ERR_SHAPE, "T %lld is negative", (long long)(T));
+  if (T * d->top_k > kMaxSlots) return fail(MM_ERR_SHAPE, "T*k %lld exceeds 2^24", (long long)(T * d->top_k));
+  return MM_OK;
+}
+
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// Shared-expert workspace carve-up.
+struct SharedWs {
+  size_t a_off, q_off, s_off, total;
+};
+SharedWs shared_ws(const mm_layer_desc* d, int64_t T) {
+  SharedWs w{};
+  const int64_t hs = d->shared_hidden;
+  if (d->wfmt == MM_W_INT4G32) {
+    w.a_off = 0;
+    w.q_off = align256(T * hs * 4);
+    w.s_off = w.q_off + align256(T * hs);
+    w.total = w.s_off + align256(T * 4);
+  } else {
+    w.a_off = 0;
+    w.total = align256(T * hs * (d->wfmt == MM_W_BF16 ? 2 : 4));
+  }
+  return w;
+}
+
+size_t ws_bytes(const mm_layer_desc* d, int64_t T, int32_t which) {
+  const int64_t Tk = T * d->top_k;
+  switch (which) {
+    case MM_WS_ROUTE:
+      return align256((size_t)mm::route_blocks(Tk) * d->n_experts * 4);
+    case MM_WS_GATEUP:
+      return d->wfmt == MM_W_INT4G32 ? align256((size_t)Tk * d->hidden * 4) : 0;
+    case MM_WS_DOWN:
+      return 0;
+    case MM_WS_SHARED:
+      return d->shared_hidden ? shared_ws(d, T).total : 0;
+    case MM_WS_MAX: {
+      size_t m = 0;
+      for (int i = 0; i < MM_WS_MAX; ++i) m = std::max(m, ws_bytes(d, T, i));
+      return m;
+    }
+    default:
+      return 0;
+  }
+}
+
+mm_status check_weight(const mm_layer_desc* d, const mm_weight& w, const char* name) {
+  if (!w.data) return fail(MM_ERR_NULL, "%s.data is NULL", name);
+  if (!aligned(w.data)) return fail(MM_ERR_ALIGN, "%s.data is not 16-byte aligned", name);
+  if (d->wfmt == MM_W_INT4G32) {
+    if (!w.scales) return fail(MM_ERR_NULL, "%s.scales is NULL for INT4 weights", name);
+    if (!aligned(w.scales)) return fail(MM_ERR_ALIGN, "%s.scales is not 16-byte aligned", name);
+  } else if (w.scales) {
+    return fail(MM_ERR_FORMAT, "%s.scales must be NULL for non-INT4 weights", name);
+  }
+  return MM_OK;
+}
+
+#define MM_TRY(expr)                 \
+  do {                               \
+    mm_status _s = (expr);           \
+    if (_s != MM_OK) return _s;      \
+  } while (0)
+
+hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* mm_version(void) { return "libmobmoe 0.1 (gfx950)"; }
+
+const char* mm_status_string(mm_status s) {
+  switch (s) {
+    case MM_OK: return "MM_OK";
+    case MM_ERR_NULL: return "MM_ERR_NULL";
+    case MM_ERR_SHAPE: return "MM_ERR_SHAPE";
+    case MM_ERR_ALIGN: return "MM_ERR_ALIGN";
+    case MM_ERR_FORMAT: return "MM_ERR_FORMAT";
+    case MM_ERR_WORKSPACE: return "MM_ERR_WORKSPACE";
+    case MM_ERR_HIP: return "MM_ERR_HIP";
+  }
+  return "MM_ERR_UNKNOWN";
+}
+
+const char* mm_last_error_string(void) { return g_err; }
+
+size_t mm_workspace_bytes(const mm_layer_desc* desc, int64_t T, int32_t which) {
+  if (check_desc(desc) != MM_OK || T < 0) return 0;
+  return ws_bytes(desc, T, which);
+}
+
+mm_status mm_quantize_int4g32(int64_t rows, int64_t cols, const float* w, uint8_t* q,
+                              float* scales, void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 32) return fail(MM_ERR_SHAPE, "cols %lld must be a positive multiple of 32", (long long)(cols));
+  if (rows == 0) return MM_OK;
+  MM_REQUIRE(w);
+  MM_REQUIRE(q);
+  MM_REQUIRE(scales);
+  return hip_status(mm::launch_quantize_int4g32(rows, cols, w, q, scales, S(stream)),
+                    "mm_quantize_int4g32");
+}
+
+size_t mm_prepacked_bytes(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols <= 0 || rows % 32 || cols % 32) return 0;
+  return (size_t)rows * cols / 2;
+}
+
+size_t mm_prepacked_scale_bytes(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols <= 0 || rows % 32 || cols % 32) return 0;
+  return (size_t)rows * (cols / 32) * 4;
+}
+
+mm_status mm_prepack_int4g32(int64_t n_mat, int64_t rows, int64_t cols, const uint8_t* q_canon,
+                             const float* s_canon, uint8_t* q_out, float* s_out, void* stream) {
+  if (n_mat < 0 || rows <= 0 || cols <= 0 || rows % 32 || cols % 32)
+    return fail(MM_ERR_SHAPE, "prepack needs rows and cols multiples of 32");
+  if (n_mat == 0) return MM_OK;
+  MM_REQUIRE(q_canon);
+  MM_REQUIRE(s_canon);
+  MM_REQUIRE(q_out);
+  MM_REQUIRE(s_out);
+  return hip_status(mm::launch_prepack_int4g32(n_mat, rows, cols, q_canon, s_canon, q_out, s_out,
+                                               S(stream)),
+                    "mm_prepack_int4g32");
+}
+
+mm_status mm_convert_bf16(int64_t n, const float* x, uint16_t* y, void* stream) {
+  if (n < 0) return fail(MM_ERR_SHAPE, "n %lld is negative", (long long)(n));
+  if (n == 0) return MM_OK;
+  MM_REQUIRE(x);
+  MM_REQUIRE(y);
+  return hip_status(mm::launch_convert_bf16(n, x, y, S(stream)), "mm_convert_bf16");
+}
+
+mm_status mm_router_topk(const mm_layer_desc* desc, int64_t T, const float* x,
+                         const float* w_router, const float* bias, int32_t* topk_idx,
+                         float* topk_w, void* stream) {
+  MM_TRY(check_desc(desc));
+  MM_TRY(check_T(desc, T));
+  if (T == 0) return MM_OK;
+  MM_REQUIRE(x);
+  MM_REQUIRE(w_router);
+  MM_OPTIONAL(bias);
+  MM_REQUIRE(topk_idx);
+  MM_REQUIRE(topk_w);
+  return hip_status(mm::launch_router(T, desc->d_model, desc->n_experts, desc->top_k, desc->gating,
+                                      x, w_router, bias, topk_idx, topk_w, S(stream)),
+                    "mm_router_topk");
+}
+
+mm_status mm_route_permute(const mm_layer_desc* desc, int64_t T, const int32_t* topk_idx,
+                           int32_t* expert_offsets, int32_t* perm, int32_t* inv_perm, void* ws,
+                           size_t ws_size, void* stream) {
+  MM_TRY(check_desc(desc));
+  MM_TRY(check_T(desc, T));
+  if (T == 0) return MM_OK;
+  MM_REQUIRE(topk_idx);
+  MM_REQUIRE(expert_offsets);
+  MM_REQUIRE(perm);
+  MM_REQUIRE(inv_perm);
+  MM_REQUIRE(ws);
+  if (ws_size < ws_bytes(desc, T, MM_WS_ROUTE))
+    return fail(MM_ERR_WORKSPACE, "route workspace too small (need %lld bytes)", (long long)ws_bytes(desc, T, MM_WS_ROUTE));
+  return hip_status(mm::launch_route(T * desc->top_k, desc->n_experts, topk_idx, expert_offsets,
+                                     perm, inv_perm, static_cast<int32_t*>(ws), S(stream)),
+                    "mm_route_permute");
+}
+
+mm_status mm_act_quant_i8(int64_t rows, int64_t cols, const float* x, int8_t* q, float* scale,
+                          void* stream) {
+  if (rows < 0 || cols <= 0) return fail(MM_ERR_SHAPE, "bad shape");
+  if (rows == 0) return MM_OK;
+  MM_REQUIRE(x);
+  MM_REQUIRE(q);
+  MM_REQUIRE(scale);
+  return hip_status(mm::launch_act_quant_i8(rows, cols, x, q, scale, S(stream)), "mm_act_quant_i8");
+}
+
+static mm_status gateup_impl(const mm_layer_desc* desc, int64_t T, const void* act,
+                             const float* act_scale, const int32_t* perm,
+                             const int32_t* expert_offsets, mm_weight w, void* h, float* h_scale,
+                             void* ws, size_t ws_size, int32_t* isum, void* stream) {
+  MM_TRY(check_desc(desc));
+  MM_TRY(check_T(desc, T));
+  if (T == 0) return MM_OK;
+  MM_REQUIRE(act);
+  MM_REQUIRE(perm);
+  MM_REQUIRE(expert_offsets);
+  MM_REQUIRE(h);
+  MM_TRY(check_weight(desc, w, "w_gateup"));
+  mm::ExpertArgs a{T * desc->top_k, T, desc->d_model, desc->hidden, desc->n_experts, desc->top_k,
+                   perm, expert_offsets};
+  hipStream_t st = S(stream);
+  if (desc->wfmt == MM_W_INT4G32) {
+    MM_REQUIRE(act_scale);
+    MM_REQUIRE(h_scale);
+    MM_REQUIRE(ws);
+    if (ws_size < ws_bytes(desc, T, MM_WS_GATEUP))
+      return fail(MM_ERR_WORKSPACE, "gate/up workspace too small (need %lld bytes)", (long long)ws_bytes(desc, T, MM_WS_GATEUP));
+    float* abuf = static_cast<float*>(ws);
+    return hip_status(mm::launch_gateup_i4(a, static_cast<const int8_t*>(act), act_scale,
+                                           static_cast<const uint8_t*>(w.data), w.scales, abuf,
+                                           static_cast<int8_t*>(h), h_scale, isum, st),
+                      "mm_expert_gateup_swiglu");
+  }
+  if (act_scale || h_scale)
+    return fail(MM_ERR_FORMAT, "act_scale and h_scale must be NULL for FP32/BF16 weights");
+  return hip_status(mm::launch_gateup_fp(a, desc->wfmt == MM_W_BF16, act, w.data, h, st),
+                    "mm_expert_gateup_swiglu");
+}
+
+mm_status mm_expert_gateup_swiglu(const mm_layer_desc* desc, int64_t T, const void* act,
+                                  const float* act_scale, const int32_t* perm,
+                                  const int32_t* expert_offsets, mm_weight w_gateup, void* h,
+                                  float* h_scale, void* ws, size_t ws_size, void* stream) {
+  return gateup_impl(desc, T, act, act_scale, perm, expert_offsets, w_gateup, h, h_scale, ws,
+                     ws_size, nullptr, stream);
+}
+
+mm_status mm_expert_gateup_swiglu_dbg(const mm_layer_desc* desc, int64_t T, const void* act,
+                                      const float* act_scale, const int32_t* perm,
+                                      const int32_t* expert_offsets, mm_weight w_gateup,
+                                      void* h, float* h_scale, void* ws, size_t ws_size,
+                                      int32_t* isum, void* stream) {
+  if (desc && desc->wfmt != MM_W_INT4G32)
+    return fail(MM_ERR_FORMAT, "group sums exist only for INT4 weights");
+  MM_REQUIRE(isum);
+  return gateup_impl(desc, T, act, act_scale, perm, expert_offsets, w_gateup, h, h_scale, ws,
+                     ws_size, isum, stream);
+}
+
+static mm_status down_impl(const mm_layer_desc* desc, int64_t T, const void* h,
+                           const float* h_scale, const int32_t* expert_offsets, mm_weight w,
+                           float* f, int32_t* isum, void* stream) {
+  MM_TRY(check_desc(desc));
+  MM_TRY(check_T(desc, T));
+  if (T == 0) return MM_OK;
+  MM_REQUIRE(h);
+  MM_REQUIRE(expert_offsets);
+  MM_REQUIRE(f);
+  MM_TRY(check_weight(desc, w, "w_down"));
+  mm::ExpertArgs a{T * desc->top_k, T, desc->d_model, desc->hidden, desc->n_experts, desc->top_k,
+                   nullptr, expert_offsets};
+  hipStream_t st = S(stream);
+  if (desc->wfmt == MM_W_INT4G32) {
+    MM_REQUIRE(h_scale);
+    return hip_status(mm::launch_down_i4(a, static_cast<const int8_t*>(h), h_scale,
+                                         static_cast<const uint8_t*>(w.data), w.scales, f, isum,
+                                         st),
+                      "mm_expert_down");
+  }
+  if (h_scale) return fail(MM_ERR_FORMAT, "h_scale must be NULL for FP32/BF16 weights");
+  return hip_status(mm::launch_down_fp(a, desc->wfmt == MM_W_BF16, h, w.data, f, st),
+                    "mm_expert_down");
+}
+
+mm_status mm_expert_down(const mm_layer_desc* desc, int64_t T, const void* h,
+                         const float* h_scale, const int32_t* expert_offsets, mm_weight w_down,
+                         float* f, void* ws, size_t ws_size, void* stream) {
+  (void)ws;
+  (void)ws_size;
+  return down_impl(desc, T, h, h_scale, expert_offsets, w_down, f, nullptr, stream);
+}
+
+mm_status mm_expert_down_dbg(const mm_layer_desc* desc, int64_t T, const void* h,
+                             const float* h_scale, const int32_t* expert_offsets,
+                             mm_weight w_down, float* f, void* ws, size_t ws_size,
+                             int32_t* isum, void* stream) {
+  (void)ws;
+  (void)ws_size;
+  if (desc && desc->wfmt != MM_W_INT4G32)
+    return fail(MM_ERR_FORMAT, "group sums exist only for INT4 weights");
+  MM_REQUIRE(isum);
+  return down_impl(desc, T, h, h_scale, expert_offsets, w_down, f, isum, stream);
+}
+
+mm_status mm_shared_expert(const mm_layer_desc* desc, int64_t T, const void* act,
+                           const float* act_scale, mm_weight w_gateup, mm_weight w_down,
+                           float* ys, void* ws, size_t ws_size, void* stream) {
+  MM_TRY(check_desc(desc));
+  MM_TRY(check_T(desc, T));
+  if (desc->shared_hidden == 0) return fail(MM_ERR_SHAPE, "no shared expert (shared_hidden == 0)");
+  if (T == 0) return MM_OK;
+  MM_REQUIRE(act);
+  MM_REQUIRE(ys);
+  MM_REQUIRE(ws);
+  MM_TRY(check_weight(desc, w_gateup, "w_gateup"));
+  MM_TRY(check_weight(desc, w_down, "w_down"));
+  const SharedWs sw = shared_ws(desc, T);
+  if (ws_size < sw.total)
+    return fail(MM_ERR_WORKSPACE, "shared workspace too small (need %lld bytes)", (long long)sw.total);
+  mm::ExpertArgs a{T, T, desc->d_model, desc->shared_hidden, 1, 1, nullptr, nullptr};
+  hipStream_t st = S(stream);
+  char* base = static_cast<char*>(ws);
+  if (desc->wfmt == MM_W_INT4G32) {
+    MM_REQUIRE(act_scale);
+    float* abuf = reinterpret_cast<float*>(base + sw.a_off);
+    int8_t* hq = reinterpret_cast<int8_t*>(base + sw.q_off);
+    float* hsc = reinterpret_cast<float*>(base + sw.s_off);
+    MM_TRY(hip_status(mm::launch_gateup_i4(a, static_cast<const int8_t*>(act), act_scale,
+                                           static_cast<const uint8_t*>(w_gateup.data),
+                                           w_gateup.scales, abuf, hq, hsc, nullptr, st),
+                      "mm_shared_expert (gate/up)"));
+    return hip_status(mm::launch_down_i4(a, hq, hsc, static_cast<const uint8_t*>(w_down.data),
+                                         w_down.scales, ys, nullptr, st),
+                      "mm_shared_expert (down)");
+  }
+  if (act_scale) return fail(MM_ERR_FORMAT, "act_scale must be NULL for FP32/BF16 weights");
+  const bool bf = desc->wfmt == MM_W_BF16;
+  void* hbuf = base + sw.a_off;
+  MM_TRY(hip_status(mm::launch_gateup_fp(a, bf, act, w_gateup.data, hbuf, st),
+                    "mm_shared_expert (gate/up)"));
+  return hip_status(mm::launch_down_fp(a, bf, hbuf, w_down.data, ys, st), "mm_shared_expert (down)");
+}
+
+mm_status mm_combine(const mm_layer_desc* desc, int64_t T, const float* f,
+                     const int32_t* inv_perm, const float* topk_w, const float* ys, void* y,
+                     void* stream) {
+  MM_TRY(check_desc(desc));
+  MM_TRY(check_T(desc, T));
+  if (T == 0) return MM_OK;
+  MM_REQUIRE(f);
+  MM_REQUIRE(inv_perm);
+  MM_REQUIRE(topk_w);
+  MM_OPTIONAL(ys);
+  MM_REQUIRE(y);
+  return hip_status(mm::launch_combine(T, desc->d_model, desc->top_k, f, inv_perm, topk_w, ys, y,
+                                       desc->out_dtype == MM_OUT_BF16, S(stream)),
+                    "mm_combine");
+}
+
+mm_status mm_rmsnorm_f32(int64_t rows, int64_t cols, float eps, const float* x, float* y,
+                         void* stream) {
+  if (rows < 0 || cols <= 0) return fail(MM_ERR_SHAPE, "bad shape");
+  if (rows == 0) return MM_OK;
+  MM_REQUIRE(x);
+  MM_REQUIRE(y);
+  return hip_status(mm::launch_rmsnorm(rows, cols, eps, x, y, S(stream)), "mm_rmsnorm_f32");
+}
+
+}  // extern "C"

@@ -1,0 +1,156 @@
+// Weight quantisation (eq. (6), b = 4, group 32), prepacking, per-row INT8
+// activation quantisation, BF16 conversion and RMSNorm.
+//
+// eq. (6) and the INT8 activation rule are from the section "Quantisation-
+// aware training" of the MobileMoE close reading (paper-archivist.com).
+#include "common.h"
+#include "launch.h"
+
+namespace mm {
+namespace {
+
+// One thread per (row, group of 32 columns).
+__global__ __launch_bounds__(256) void k_quantize_int4g32(int64_t rows, int64_t cols,
+                                                          const float* __restrict__ w,
+                                                          uint8_t* __restrict__ q,
+                                                          float* __restrict__ s) {
+  const int64_t G = cols / kGroup;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * G) return;
+  const int64_t r = i / G, g = i % G;
+  const float* wg = w + r * cols + g * kGroup;
+  float v[kGroup];
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kGroup; ++c) {
+    v[c] = wg[c];
+    amax = fmaxf(amax, fabsf(v[c]));
+  }
+  const float sg = (2.0f * amax) / 15.0f;
+  s[i] = sg;
+  uint8_t* qg = q + r * (cols / 2) + g * (kGroup / 2);
+#pragma unroll
+  for (int b = 0; b < kGroup / 2; ++b) {
+    int lo = 0, hi = 0;
+    if (sg != 0.0f) {
+      lo = (int)fminf(fmaxf(rintf(v[2 * b] / sg), -8.0f), 7.0f);
+      hi = (int)fminf(fmaxf(rintf(v[2 * b + 1] / sg), -8.0f), 7.0f);
+    }
+    qg[b] = (uint8_t)((lo & 0xF) | ((hi & 0xF) << 4));
+  }
+}
+
+// One thread per (matrix, 32-row block, group, lane of the chunk): writes the
+// 8 bytes of that lane (layout in common.h) and, for lanes 0..31, the scale.
+__global__ __launch_bounds__(256) void k_prepack_int4g32(int64_t n_mat, int64_t rows,
+                                                         int64_t cols,
+                                                         const uint8_t* __restrict__ qc,
+                                                         const float* __restrict__ sc,
+                                                         uint8_t* __restrict__ qo,
+                                                         float* __restrict__ so) {
+  const int64_t G = cols / kGroup, RB = rows / 32;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_mat * RB * G * 64) return;
+  const int L = (int)(i % 64);
+  const int64_t chunk = i / 64;  // ((m * RB + rb) * G + g)
+  const int64_t g = chunk % G;
+  const int64_t mrb = chunk / G;  // m * RB + rb
+  const int64_t row = mrb * 32 + (L % 32);  // global row over all matrices
+  const uint8_t* src = qc + row * (cols / 2);
+  const int64_t base = g * kGroup + 16 * (L / 32);
+  auto nib = [&](int64_t c) -> uint32_t { return (src[c / 2] >> (4 * (c & 1))) & 0xFu; };
+  uint32_t word[2];
+#pragma unroll
+  for (int wi = 0; wi < 2; ++wi) {
+    uint32_t acc = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      uint32_t lo = nib(base + 8 * wi + b), hi = nib(base + 8 * wi + b + 4);
+      acc |= (lo | (hi << 4)) << (8 * b);
+    }
+    word[wi] = acc;
+  }
+  uint32_t* dst = reinterpret_cast<uint32_t*>(qo + chunk * kChunkBytes + L * 8);
+  dst[0] = word[0];
+  dst[1] = word[1];
+  if (L < 32) so[chunk * 32 + L] = sc[row * G + g] * 0.0625f;
+}
+
+// One wave per row: exact max|v|, s = 2*amax/255, q = clamp(rint(v/s)).
+__global__ __launch_bounds__(256) void k_act_quant_i8(int64_t rows, int64_t cols,
+                                                      const float* __restrict__ x,
+                                                      int8_t* __restrict__ q,
+                                                      float* __restrict__ s) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const float* xr = x + r * cols;
+  float amax = 0.0f;
+  for (int64_t c = lane; c < cols; c += kWave) amax = fmaxf(amax, fabsf(xr[c]));
+  amax = wave_max(amax);
+  const float sr = (2.0f * amax) / 255.0f;
+  if (lane == 0) s[r] = sr;
+  int8_t* qr = q + r * cols;
+  for (int64_t c = lane; c < cols; c += kWave) qr[c] = sr != 0.0f ? quant_i8(xr[c], sr) : (int8_t)0;
+}
+
+__global__ __launch_bounds__(256) void k_convert_bf16(int64_t n, const float* __restrict__ x,
+                                                      uint16_t* __restrict__ y) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) y[i] = f32_to_bf16(x[i]);
+}
+
+__global__ __launch_bounds__(256) void k_rmsnorm(int64_t rows, int64_t cols, float eps,
+                                                 const float* __restrict__ x,
+                                                 float* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const float* xr = x + r * cols;
+  float ss = 0.0f;
+  for (int64_t c = lane; c < cols; c += kWave) ss = fmaf(xr[c], xr[c], ss);
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)cols + eps);
+  for (int64_t c = lane; c < cols; c += kWave) y[r * cols + c] = xr[c] * inv;
+}
+
+inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+}  // namespace
+
+hipError_t launch_quantize_int4g32(int64_t rows, int64_t cols, const float* w, uint8_t* q,
+                                   float* s, hipStream_t st) {
+  const int64_t n = rows * (cols / kGroup);
+  hipLaunchKernelGGL(k_quantize_int4g32, dim3(blocks_for(n, 256)), dim3(256), 0, st, rows, cols,
+                     w, q, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_prepack_int4g32(int64_t n_mat, int64_t rows, int64_t cols, const uint8_t* qc,
+                                  const float* sc, uint8_t* qo, float* so, hipStream_t st) {
+  const int64_t n = n_mat * (rows / 32) * (cols / kGroup) * 64;
+  hipLaunchKernelGGL(k_prepack_int4g32, dim3(blocks_for(n, 256)), dim3(256), 0, st, n_mat, rows,
+                     cols, qc, sc, qo, so);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_quant_i8(int64_t rows, int64_t cols, const float* x, int8_t* q, float* s,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(k_act_quant_i8, dim3(blocks_for(rows, 4)), dim3(256), 0, st, rows, cols, x,
+                     q, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_convert_bf16(int64_t n, const float* x, uint16_t* y, hipStream_t st) {
+  hipLaunchKernelGGL(k_convert_bf16, dim3(blocks_for(n, 256)), dim3(256), 0, st, n, x, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(int64_t rows, int64_t cols, float eps, const float* x, float* y,
+                          hipStream_t st) {
+  hipLaunchKernelGGL(k_rmsnorm, dim3(blocks_for(rows, 4)), dim3(256), 0, st, rows, cols, eps, x,
+                     y);
+  return hipGetLastError();
+}
+
+}  // namespace mm

@@ -1,0 +1,118 @@
+// Stable count sort of the T*k (token, slot) assignments by expert id.
+//
+// MobileMoE close reading, section "Custom MoE kernel": tokens are reordered
+// by their assigned expert with a counting sort so that each expert's tokens
+// are contiguous and each expert runs one batched product on its slice.
+// Inference routing is dropless (section "Supervised fine-tuning").
+//
+// Two kernels, no host synchronisation and no order-dependent atomics:
+//   k_route_count    one workgroup per block of 256 slots: per-expert counts
+//                    of the block (integer LDS atomics; the result does not
+//                    depend on their order) -> ws[block][E].
+//   k_route_scatter  one workgroup per block: sums the counts of all earlier
+//                    blocks per expert and of all blocks (for the offsets),
+//                    then ranks each slot among the equal ids of its block in
+//                    slot order and writes perm / inv_perm.  Block 0 also
+//                    writes expert_offsets.
+#include "common.h"
+#include "launch.h"
+
+namespace mm {
+namespace {
+
+constexpr int kBlockSlots = 256;
+
+__global__ __launch_bounds__(kBlockSlots) void k_route_count(int64_t Tk, int E,
+                                                             const int32_t* __restrict__ idx,
+                                                             int32_t* __restrict__ counts) {
+  __shared__ int cnt[64];
+  const int tid = threadIdx.x;
+  if (tid < 64) cnt[tid] = 0;
+  __syncthreads();
+  const int64_t slot = (int64_t)blockIdx.x * kBlockSlots + tid;
+  if (slot < Tk) {
+    const int e = idx[slot];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  if (tid < E) counts[(int64_t)blockIdx.x * E + tid] = cnt[tid];
+}
+
+__global__ __launch_bounds__(kBlockSlots) void k_route_scatter(
+    int64_t Tk, int E, int64_t nblk, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
+  __shared__ int part_before[4][64];
+  __shared__ int part_total[4][64];
+  __shared__ int base[64];    // offsets[e] + count of e in earlier blocks
+  __shared__ int wcnt[4][64];  // count of e in each wave of this block
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t blk = blockIdx.x;
+
+  // Per-expert sums over blocks: 4 threads per expert, interleaved blocks.
+  {
+    int before = 0, total = 0;
+    if (lane < E) {
+      for (int64_t b = wv; b < nblk; b += 4) {
+        const int c = counts[b * E + lane];
+        total += c;
+        if (b < blk) before += c;
+      }
+    }
+    part_before[wv][lane] = before;
+    part_total[wv][lane] = total;
+    wcnt[wv][lane] = 0;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int e = 0; e < E; ++e) {
+      const int tot = part_total[0][e] + part_total[1][e] + part_total[2][e] + part_total[3][e];
+      const int bef = part_before[0][e] + part_before[1][e] + part_before[2][e] + part_before[3][e];
+      if (blk == 0) offsets[e] = run;
+      base[e] = run + bef;
+      run += tot;
+    }
+    if (blk == 0) offsets[E] = run;
+  }
+
+  // Rank inside the wave: the lanes holding the same id are found with one
+  // ballot per id bit (ids < 64).
+  const int64_t slot = blk * kBlockSlots + tid;
+  const int eraw = slot < Tk ? idx[slot] : -1;
+  const bool valid = (unsigned)eraw < (unsigned)E;  // out-of-range ids are skipped
+  const int e = valid ? eraw : 0;
+  uint64_t same = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < 6; ++b) {
+    const uint64_t ones = __ballot(valid && ((e >> b) & 1));
+    same &= ((e >> b) & 1) ? ones : ~ones;
+  }
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int rank = __popcll(same & below);
+  if (valid && rank == 0) wcnt[wv][e] = __popcll(same);
+  __syncthreads();
+  if (valid) {
+    int pos = base[e] + rank;
+    for (int w2 = 0; w2 < wv; ++w2) pos += wcnt[w2][e];
+    perm[pos] = (int32_t)slot;
+    inv_perm[slot] = pos;
+  }
+}
+
+}  // namespace
+
+int64_t route_blocks(int64_t Tk) { return (Tk + kBlockSlots - 1) / kBlockSlots; }
+
+hipError_t launch_route(int64_t Tk, int E, const int32_t* idx, int32_t* offsets, int32_t* perm,
+                        int32_t* inv_perm, int32_t* ws, hipStream_t st) {
+  const int64_t nblk = route_blocks(Tk);
+  hipLaunchKernelGGL(k_route_count, dim3((unsigned)nblk), dim3(kBlockSlots), 0, st, Tk, E, idx, ws);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_route_scatter, dim3((unsigned)nblk), dim3(kBlockSlots), 0, st, Tk, E, nblk,
+                     idx, ws, offsets, perm, inv_perm);
+  return hipGetLastError();
+}
+
+}  // namespace mm

@@ -1,0 +1,60 @@
+// Host-side launchers of the libmobmoe kernels.  Each returns the result of
+// hipGetLastError() after queueing its kernels on `st`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mm {
+
+// Quantisation, packing, conversions (k_quant.hip)
+hipError_t launch_quantize_int4g32(int64_t rows, int64_t cols, const float* w, uint8_t* q,
+                                   float* s, hipStream_t st);
+hipError_t launch_prepack_int4g32(int64_t n_mat, int64_t rows, int64_t cols, const uint8_t* qc,
+                                  const float* sc, uint8_t* qo, float* so, hipStream_t st);
+hipError_t launch_act_quant_i8(int64_t rows, int64_t cols, const float* x, int8_t* q, float* s,
+                               hipStream_t st);
+hipError_t launch_convert_bf16(int64_t n, const float* x, uint16_t* y, hipStream_t st);
+hipError_t launch_rmsnorm(int64_t rows, int64_t cols, float eps, const float* x, float* y,
+                          hipStream_t st);
+
+// Router (k_router.hip)
+hipError_t launch_router(int64_t T, int d, int E, int k, int gating, const float* x,
+                         const float* wr, const float* bias, int32_t* idx, float* w,
+                         hipStream_t st);
+
+// Route / permute (k_route.hip).  ws holds ceil(T*k/256) * E int32 counts.
+int64_t route_blocks(int64_t Tk);
+hipError_t launch_route(int64_t Tk, int E, const int32_t* idx, int32_t* offsets, int32_t* perm,
+                        int32_t* inv_perm, int32_t* ws, hipStream_t st);
+
+// Expert products (k_expert.hip).  `perm`/`offsets` are null for the dense
+// (shared-expert) form, where the rows are the T tokens in order.
+struct ExpertArgs {
+  int64_t rows;        // routed: T*k sorted positions; dense: T
+  int64_t T;           // tokens
+  int d, h, E, k;      // h = hidden of this expert kind
+  const int32_t* perm;
+  const int32_t* offsets;
+};
+// INT4 gate/up + SwiGLU + per-row INT8 re-quantisation: hq [rows][h], hs [rows].
+// a_buf [rows][h] FP32 is staging space for the unquantised hidden rows.
+hipError_t launch_gateup_i4(const ExpertArgs& a, const int8_t* xq, const float* sx,
+                            const uint8_t* wq, const float* ws, float* a_buf, int8_t* hq,
+                            float* hs, int32_t* isum, hipStream_t st);
+// INT4 down: f [rows][d] = s_h * sum_g s_w * isum_g
+hipError_t launch_down_i4(const ExpertArgs& a, const int8_t* hq, const float* hs,
+                          const uint8_t* wq, const float* ws, float* f, int32_t* isum,
+                          hipStream_t st);
+// Floating-point forms: bf16 = false uses FP32 operands, true uses BF16.
+hipError_t launch_gateup_fp(const ExpertArgs& a, bool bf16, const void* x, const void* w,
+                            void* h_out, hipStream_t st);
+hipError_t launch_down_fp(const ExpertArgs& a, bool bf16, const void* hrow, const void* w,
+                          float* f, hipStream_t st);
+
+// Combine (k_combine.hip)
+hipError_t launch_combine(int64_t T, int d, int k, const float* f, const int32_t* inv_perm,
+                          const float* w, const float* ys, void* y, bool bf16_out,
+                          hipStream_t st);
+
+}  // namespace mm

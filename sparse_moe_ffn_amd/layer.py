@@ -1,0 +1,154 @@
+"""A MoE-FFN layer object on top of the C ABI: owns the device weights and the
+per-call buffers, and issues the seven calls in order on the current stream.
+
+Weight preparation runs on the device through the library (eq. (6)
+quantisation with mm_quantize_int4g32, then mm_prepack_int4g32; or BF16
+conversion).  torch is used only to allocate device memory and to provide the
+stream.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+def _dev(a: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def _empty(shape, dtype, device) -> torch.Tensor:
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
+@dataclass
+class DevWeight:
+    data: torch.Tensor
+    scales: Optional[torch.Tensor]
+    canon: Optional[torch.Tensor] = None        # INT4 canonical nibbles (kept for tests)
+    canon_scales: Optional[torch.Tensor] = None
+
+    def c(self) -> B.Weight:
+        return B.weight(self.data, self.scales)
+
+
+def prepare_weight(w: np.ndarray, wfmt: str, device, keep_canonical: bool = False) -> DevWeight:
+    """w: FP32 [n_mat, rows, cols] (or [rows, cols]) -> device weight in `wfmt`."""
+    a = w if w.ndim == 3 else w[None]
+    n, rows, cols = a.shape
+    src = _dev(a.astype(np.float32, copy=False), device)
+    if wfmt == "f32":
+        return DevWeight(src, None)
+    if wfmt == "bf16":
+        out = _empty((n, rows, cols), torch.int16, device)
+        B.convert_bf16(src.numel(), src, out)
+        return DevWeight(out, None)
+    qc = _empty((n * rows, cols // 2), torch.uint8, device)
+    sc = _empty((n * rows, cols // 32), torch.float32, device)
+    B.quantize_int4g32(n * rows, cols, src, qc, sc)
+    qp = _empty((n * B.prepacked_bytes(rows, cols),), torch.uint8, device)
+    sp = _empty((n * B.prepacked_scale_bytes(rows, cols) // 4,), torch.float32, device)
+    B.prepack_int4g32(n, rows, cols, qc, sc, qp, sp)
+    del src
+    if keep_canonical:
+        return DevWeight(qp, sp, qc, sc)
+    return DevWeight(qp, sp)
+
+
+class MoELayer:
+    """One MoE-FFN layer (eq. (*)) with device-resident weights."""
+
+    def __init__(self, d, E, h, hs, k, wr, bias, w_gu, w_d, ws_gu=None, ws_d=None, *,
+                 wfmt="int4g32", gating=0, out_dtype=B.MM_OUT_F32, device="cuda",
+                 keep_canonical=False):
+        self.d, self.E, self.h, self.hs, self.k = d, E, h, hs, k
+        self.wfmt = wfmt
+        self.device = torch.device(device)
+        self.desc = B.desc(d, E, h, hs, k, wfmt, gating, out_dtype)
+        self.wr = _dev(wr.astype(np.float32), self.device)
+        self.bias = None if bias is None else _dev(bias.astype(np.float32), self.device)
+        self.w_gu = prepare_weight(w_gu, wfmt, self.device, keep_canonical)
+        self.w_d = prepare_weight(w_d, wfmt, self.device, keep_canonical)
+        self.ws_gu = prepare_weight(ws_gu, wfmt, self.device, keep_canonical) if hs else None
+        self.ws_d = prepare_weight(ws_d, wfmt, self.device, keep_canonical) if hs else None
+        self._T = -1
+
+    @classmethod
+    def from_workload(cls, w, lw, device="cuda", **kw):
+        return cls(w.d, w.E, w.h, w.hs, w.k, lw.wr, lw.bias, lw.w_gu, lw.w_d, lw.ws_gu, lw.ws_d,
+                   wfmt=w.wfmt, device=device,
+                   out_dtype=B.MM_OUT_BF16 if w.wfmt == "bf16" else B.MM_OUT_F32, **kw)
+
+    def buffers(self, T: int):
+        """(Re)allocates the per-call buffers for T tokens."""
+        if T == self._T:
+            return
+        dv, k, d, h = self.device, self.k, self.d, self.h
+        self.idx = _empty((T, k), torch.int32, dv)
+        self.topw = _empty((T, k), torch.float32, dv)
+        self.offsets = _empty((self.E + 1,), torch.int32, dv)
+        self.perm = _empty((T * k,), torch.int32, dv)
+        self.inv = _empty((T * k,), torch.int32, dv)
+        if self.wfmt == "int4g32":
+            self.xq = _empty((T, d), torch.int8, dv)
+            self.sx = _empty((T,), torch.float32, dv)
+            self.hbuf = _empty((T * k, h), torch.int8, dv)
+            self.hscale = _empty((T * k,), torch.float32, dv)
+        else:
+            self.xq, self.sx, self.hscale = None, None, None
+            self.hbuf = _empty((T * k, h), torch.float32 if self.wfmt == "f32" else torch.int16, dv)
+        self.f = _empty((T * k, d), torch.float32, dv)
+        self.ys = _empty((T, d), torch.float32, dv) if self.hs else None
+        self.y = _empty((T, d), torch.float32 if self.desc.out_dtype == B.MM_OUT_F32 else torch.int16, dv)
+        self.ws_bytes = max(B.workspace_bytes(self.desc, T, B.MM_WS_MAX), 256)
+        self.ws = _empty((self.ws_bytes,), torch.uint8, dv)
+        self._T = T
+
+    # The seven calls, in order.  Each uses the current torch stream.
+    def router(self, x, T):
+        B.router_topk(self.desc, T, x, self.wr, self.bias, self.idx, self.topw)
+
+    def route(self, T):
+        B.route_permute(self.desc, T, self.idx, self.offsets, self.perm, self.inv, self.ws, self.ws_bytes)
+
+    def act_quant(self, x, T):
+        B.act_quant_i8(T, self.d, x, self.xq, self.sx)
+
+    def act(self, x):
+        return (self.xq, self.sx) if self.wfmt == "int4g32" else (x, None)
+
+    def gateup(self, x, T, isum=None):
+        a, s = self.act(x)
+        B.expert_gateup_swiglu(self.desc, T, a, s, self.perm, self.offsets, self.w_gu.c(), self.hbuf,
+                               self.hscale, self.ws, self.ws_bytes, isum=isum)
+
+    def down(self, T, isum=None):
+        B.expert_down(self.desc, T, self.hbuf, self.hscale, self.offsets, self.w_d.c(), self.f,
+                      self.ws, self.ws_bytes, isum=isum)
+
+    def shared(self, x, T):
+        a, s = self.act(x)
+        B.shared_expert(self.desc, T, a, s, self.ws_gu.c(), self.ws_d.c(), self.ys, self.ws,
+                        self.ws_bytes)
+
+    def combine(self, T):
+        B.combine(self.desc, T, self.f, self.inv, self.topw, self.ys, self.y)
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        """y = eq. (*) of x [T, d] FP32 (device).  Returns the layer's y buffer."""
+        T = x.shape[0]
+        self.buffers(T)
+        self.router(x, T)
+        self.route(T)
+        if self.wfmt == "int4g32":
+            self.act_quant(x, T)
+        self.gateup(x, T)
+        self.down(T)
+        if self.hs:
+            self.shared(x, T)
+        self.combine(T)
+        return self.y

@@ -1,0 +1,135 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch.
+No GPU is touched: every call here fails validation (or is a size query)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_moe_ffn_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from sparse_moe_ffn_amd import build
+        build.build()
+    return B.load()
+
+
+def header_symbols():
+    src = open(os.path.join(ROOT, "include", "mobmoe.h")).read()
+    return set(re.findall(r"^(?:mm_status|const char\*|size_t)\s+(mm_\w+)\(", src, re.M))
+
+
+def test_header_and_binding_agree():
+    assert header_symbols() == set(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_symbols():
+        assert hasattr(lib, name), name
+    assert "gfx950" in B.version()
+
+
+def test_status_strings(lib):
+    assert lib.mm_status_string(0) == b"MM_OK"
+    assert lib.mm_status_string(5) == b"MM_ERR_WORKSPACE"
+
+
+FAKE = 1 << 20           # aligned, never dereferenced (validation fails first)
+MISALIGNED = FAKE + 4
+
+
+def S():
+    return B.desc(768, 60, 384, 1536, 4, "int4g32")
+
+
+def rc_of(fn, *args):
+    return fn(*args)
+
+
+def test_desc_validation(lib):
+    bad = [B.desc(100, 60, 384, 1536, 4), B.desc(768, 65, 384, 1536, 4), B.desc(768, 60, 96, 1536, 4),
+           B.desc(768, 60, 384, 100, 4), B.desc(768, 4, 384, 0, 5), B.desc(768, 60, 384, 0, 9)]
+    for ds in bad:
+        assert lib.mm_router_topk(ctypes.byref(ds), 4, FAKE, FAKE, None, FAKE, FAKE, None) == B.MM_ERR_SHAPE
+        assert B.workspace_bytes(ds, 4) == 0
+    for ds in (B.desc(768, 60, 384, 0, 4, wfmt=7), B.desc(768, 60, 384, 0, 4, gating=3),
+               B.desc(768, 60, 384, 0, 4, out_dtype=2)):
+        assert lib.mm_router_topk(ctypes.byref(ds), 4, FAKE, FAKE, None, FAKE, FAKE, None) == B.MM_ERR_FORMAT
+    assert lib.mm_router_topk(None, 4, FAKE, FAKE, None, FAKE, FAKE, None) == B.MM_ERR_NULL
+    assert b"desc" in lib.mm_last_error_string()
+
+
+def test_null_and_alignment(lib):
+    ds = S()
+    assert lib.mm_router_topk(ctypes.byref(ds), 4, None, FAKE, None, FAKE, FAKE, None) == B.MM_ERR_NULL
+    assert b"x is NULL" in lib.mm_last_error_string()
+    assert lib.mm_router_topk(ctypes.byref(ds), 4, MISALIGNED, FAKE, None, FAKE, FAKE, None) == B.MM_ERR_ALIGN
+    assert lib.mm_router_topk(ctypes.byref(ds), 4, FAKE, FAKE, MISALIGNED, FAKE, FAKE, None) == B.MM_ERR_ALIGN
+    assert lib.mm_combine(ctypes.byref(ds), 4, FAKE, FAKE, FAKE, None, None, None) == B.MM_ERR_NULL
+    assert lib.mm_act_quant_i8(3, 768, FAKE, None, FAKE, None) == B.MM_ERR_NULL
+    w = B.Weight(FAKE, None)
+    assert lib.mm_expert_down(ctypes.byref(ds), 4, FAKE, FAKE, FAKE, w, FAKE, None, 0, None) == B.MM_ERR_NULL
+    assert b"w_down.scales" in lib.mm_last_error_string()
+
+
+def test_zero_tokens_is_a_noop(lib):
+    ds = S()
+    assert lib.mm_router_topk(ctypes.byref(ds), 0, None, None, None, None, None, None) == B.MM_OK
+    assert lib.mm_route_permute(ctypes.byref(ds), 0, None, None, None, None, None, 0, None) == B.MM_OK
+    assert lib.mm_act_quant_i8(0, 768, None, None, None, None) == B.MM_OK
+    assert lib.mm_combine(ctypes.byref(ds), 0, None, None, None, None, None, None) == B.MM_OK
+    w = B.Weight(None, None)
+    assert lib.mm_expert_gateup_swiglu(ctypes.byref(ds), 0, None, None, None, None, w, None, None,
+                                       None, 0, None) == B.MM_OK
+
+
+def test_shape_limits(lib):
+    ds = S()
+    assert lib.mm_router_topk(ctypes.byref(ds), -1, FAKE, FAKE, None, FAKE, FAKE, None) == B.MM_ERR_SHAPE
+    assert lib.mm_router_topk(ctypes.byref(ds), (1 << 22) + 1, FAKE, FAKE, None, FAKE, FAKE, None) == B.MM_ERR_SHAPE
+    noshared = B.desc(768, 60, 384, 0, 4)
+    w = B.Weight(FAKE, FAKE)
+    assert lib.mm_shared_expert(ctypes.byref(noshared), 4, FAKE, FAKE, w, w, FAKE, FAKE, 1 << 20,
+                                None) == B.MM_ERR_SHAPE
+    assert lib.mm_quantize_int4g32(4, 40, FAKE, FAKE, FAKE, None) == B.MM_ERR_SHAPE
+    assert lib.mm_prepack_int4g32(1, 48, 64, FAKE, FAKE, FAKE, FAKE, None) == B.MM_ERR_SHAPE
+
+
+def test_format_rules(lib):
+    f32 = B.desc(256, 60, 64, 256, 4, "f32")
+    w_with_scales = B.Weight(FAKE, FAKE)
+    assert lib.mm_expert_down(ctypes.byref(f32), 4, FAKE, None, FAKE, w_with_scales, FAKE, None, 0,
+                              None) == B.MM_ERR_FORMAT
+    w = B.Weight(FAKE, None)
+    assert lib.mm_expert_down_dbg(ctypes.byref(f32), 4, FAKE, None, FAKE, w, FAKE, None, 0, FAKE,
+                                  None) == B.MM_ERR_FORMAT
+
+
+def test_workspace_checks(lib):
+    ds = S()
+    need = B.workspace_bytes(ds, 2048, B.MM_WS_ROUTE)
+    assert need == ((2048 * 4 + 255) // 256) * 60 * 4
+    assert lib.mm_route_permute(ctypes.byref(ds), 2048, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1,
+                                None) == B.MM_ERR_WORKSPACE
+    gu = B.workspace_bytes(ds, 2048, B.MM_WS_GATEUP)
+    assert gu >= 2048 * 4 * 384 * 4
+    w = B.Weight(FAKE, FAKE)
+    assert lib.mm_expert_gateup_swiglu(ctypes.byref(ds), 2048, FAKE, FAKE, FAKE, FAKE, w, FAKE, FAKE,
+                                       FAKE, gu - 1, None) == B.MM_ERR_WORKSPACE
+    sh = B.workspace_bytes(ds, 2048, B.MM_WS_SHARED)
+    assert lib.mm_shared_expert(ctypes.byref(ds), 2048, FAKE, FAKE, w, w, FAKE, FAKE, sh - 1,
+                                None) == B.MM_ERR_WORKSPACE
+    assert B.workspace_bytes(ds, 2048, B.MM_WS_MAX) == max(
+        B.workspace_bytes(ds, 2048, i) for i in range(4))
+
+
+def test_prepacked_sizes(lib):
+    assert B.prepacked_bytes(768, 768) == 768 * 384
+    assert B.prepacked_scale_bytes(768, 768) == 768 * 24 * 4
+    assert B.prepacked_bytes(48, 64) == 0

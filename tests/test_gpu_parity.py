@@ -1,0 +1,292 @@
+"""GPU parity of the HIP path (called through the C ABI) against the CPU
+oracle, stage by stage and end to end, on seeded synthetic inputs.
+
+Bars: bit-exact for integer work (weight codes and scales, activation codes
+and scales, top-k ids, routing offsets / permutation, int32 group sums); for
+floating point, per token row max|gpu - oracle| / max|oracle| <= 1e-3 (FP32
+output) or 2e-2 (BF16 output)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_moe_ffn_amd import binding as B
+from sparse_moe_ffn_amd import workloads as wl
+from gpu_util import (DEV, bf16_bits_to_f32, decode_prepacked, layer_output, make_layer, np_,
+                            oracle_forward, row_rel_err, unpack_canonical)
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32, TOL_BF16 = 1e-3, 2e-2
+
+
+def rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+# ------------------------------------------------------------ weights: eq. (6)
+@pytest.mark.parametrize("n,rows,cols", [(1, 32, 32), (3, 64, 128), (2, 768, 384)])
+def test_quantize_and_prepack_bitexact(n, rows, cols):
+    g = rng(100 + rows)
+    w = (g.standard_normal((n, rows, cols)) * 0.02).astype(np.float32)
+    w[0, 0, :32] = 0.0                                      # all-zero group
+    w[0, 1, :32] = np.linspace(-1, 1, 32, dtype=np.float32)  # exact +-max
+    qc = torch.empty((n * rows, cols // 2), dtype=torch.uint8, device=DEV)
+    sc = torch.empty((n * rows, cols // 32), dtype=torch.float32, device=DEV)
+    B.quantize_int4g32(n * rows, cols, dev(w), qc, sc)
+    q_ref, s_ref = oracle.quant_w4g32(w.reshape(n * rows, cols))
+    assert np.array_equal(unpack_canonical(np_(qc)), q_ref)
+    assert np.array_equal(np_(sc), s_ref)
+    qp = torch.empty((n * B.prepacked_bytes(rows, cols),), dtype=torch.uint8, device=DEV)
+    sp = torch.empty((n * B.prepacked_scale_bytes(rows, cols) // 4,), dtype=torch.float32, device=DEV)
+    B.prepack_int4g32(n, rows, cols, qc, sc, qp, sp)
+    q2, s2 = decode_prepacked(np_(qp), np_(sp), n, rows, cols)
+    assert np.array_equal(q2.reshape(n * rows, cols), q_ref)
+    assert np.array_equal(s2.reshape(n * rows, -1), s_ref)
+
+
+# ------------------------------------------------------------ activations
+@pytest.mark.parametrize("rows,cols", [(1, 64), (333, 768), (64, 1280), (5, 2560)])
+def test_act_quant_bitexact(rows, cols):
+    x = rng(rows).standard_normal((rows, cols)).astype(np.float32)
+    x[0, :] = 0.0
+    if rows > 2:
+        x[2] *= 1e-20
+    q = torch.empty((rows, cols), dtype=torch.int8, device=DEV)
+    s = torch.empty((rows,), dtype=torch.float32, device=DEV)
+    B.act_quant_i8(rows, cols, dev(x), q, s)
+    q_ref, s_ref = oracle.quant_act_i8(x)
+    assert np.array_equal(np_(q), q_ref)
+    assert np.array_equal(np_(s), s_ref)
+
+
+# ------------------------------------------------------------ router
+@pytest.mark.parametrize("T,d,E,k,use_bias,gating", [
+    (1000, 768, 60, 4, False, 0), (257, 1280, 60, 4, True, 0), (33, 64, 8, 2, False, 0),
+    (130, 256, 60, 4, False, 0), (64, 1024, 64, 8, True, 0), (77, 768, 60, 4, True, 1),
+    (5, 3072, 60, 4, False, 0)])
+def test_router_bitexact(T, d, E, k, use_bias, gating):
+    g = rng(T + d)
+    x = g.standard_normal((T, d)).astype(np.float32)
+    wr = (g.standard_normal((E, d)) * 0.02).astype(np.float32)
+    bias = wl.zipf_bias(wl.WORKLOADS["l_prefill"].with_(E=E)) if use_bias else None
+    ds = B.desc(d, E, 64, 0, k, "int4g32", gating)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    wt = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    B.router_topk(ds, T, dev(x), dev(wr), None if bias is None else dev(bias), idx, wt)
+    i_ref, w_ref, _ = oracle.router(x, wr, bias, k=k, gating=gating)
+    assert np.array_equal(np_(idx), i_ref)
+    np.testing.assert_allclose(np_(wt), w_ref, rtol=1e-5, atol=1e-9)
+
+
+def test_router_ties_pick_lowest_index():
+    g = rng(7)
+    T, d, E, k = 50, 256, 60, 4
+    x = g.standard_normal((T, d)).astype(np.float32)
+    wr = np.tile((g.standard_normal(d) * 0.02).astype(np.float32), (E, 1))
+    ds = B.desc(d, E, 64, 0, k)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    wt = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    B.router_topk(ds, T, dev(x), dev(wr), None, idx, wt)
+    assert np.all(np_(idx) == np.arange(k))
+    np.testing.assert_allclose(np_(wt), 1 / E, rtol=1e-6)
+
+
+# ------------------------------------------------------------ routing
+@pytest.mark.parametrize("T,E,k,skew", [(3000, 60, 4, False), (2048, 60, 4, True), (1, 60, 4, False),
+                                         (513, 1, 1, False), (100, 64, 8, True), (8192, 60, 4, True)])
+def test_route_permute_bitexact(T, E, k, skew):
+    g = rng(T * 7 + E)
+    if skew:
+        p = np.arange(1, E + 1, dtype=np.float64) ** -1.2
+        p /= p.sum()
+        idx = np.stack([g.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    else:
+        idx = np.stack([g.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    ds = B.desc(64, E, 64, 0, k)
+    off = torch.empty((E + 1,), dtype=torch.int32, device=DEV)
+    perm = torch.empty((T * k,), dtype=torch.int32, device=DEV)
+    inv = torch.empty((T * k,), dtype=torch.int32, device=DEV)
+    nb = B.workspace_bytes(ds, T, B.MM_WS_ROUTE)
+    ws = torch.empty((nb,), dtype=torch.uint8, device=DEV)
+    B.route_permute(ds, T, dev(idx), off, perm, inv, ws, nb)
+    o_ref, p_ref, i_ref = oracle.route(idx, E)
+    assert np.array_equal(np_(off), o_ref)
+    assert np.array_equal(np_(perm), p_ref)
+    assert np.array_equal(np_(inv), i_ref)
+
+
+# ------------------------------------------------------------ expert stages
+def _sorted_reference(layer, w, lw, x):
+    """Oracle per-sorted-row gate/up and down results for the layer's routing."""
+    perm = np_(layer.perm)
+    off = np_(layer.offsets)
+    xq, sx = oracle.quant_act_i8(x)
+    rows = w.T * w.k
+    hq = np.zeros((rows, w.h), np.int8)
+    hs = np.zeros((rows,), np.float32)
+    f = np.zeros((rows, w.d))
+    igu = np.zeros((rows, 2 * w.h, w.d // 32), np.int32)
+    idn = np.zeros((rows, w.d, w.h // 32), np.int32)
+    for e in range(w.E):
+        p = np.arange(off[e], off[e + 1])
+        if len(p) == 0:
+            continue
+        tok = perm[p] // w.k
+        gq, gs = oracle.quant_w4g32(lw.w_gu[e])
+        dq, dsc = oracle.quant_w4g32(lw.w_d[e])
+        hq[p], hs[p], f[p], igu[p], idn[p] = oracle.ffn_w4a8(xq[tok], sx[tok], gq, gs, dq, dsc,
+                                                               want_isum=True)
+    return hq, hs, f, igu, idn
+
+
+@pytest.mark.parametrize("name,T", [("s_prefill", 200), ("m_prefill", 70), ("l_prefill", 45)])
+def test_expert_stages_int4(name, T):
+    w = wl.WORKLOADS[name].with_(T=T)
+    lw = wl.layer_weights(w)
+    x = wl.tokens(w)
+    layer = make_layer(w, lw)
+    xd = dev(x)
+    layer.buffers(T)
+    layer.router(xd, T)
+    layer.route(T)
+    layer.act_quant(xd, T)
+    rows = T * w.k
+    isum_gu = torch.zeros((rows, 2 * w.h, w.d // 32), dtype=torch.int32, device=DEV)
+    layer.gateup(xd, T, isum=isum_gu)
+    hq_ref, hs_ref, f_ref, igu_ref, idn_ref = _sorted_reference(layer, w, lw, x)
+    # exact int32 group sums of the fused gate/up product
+    assert np.array_equal(np_(isum_gu), igu_ref)
+    # re-quantised hidden rows: FP32 (device) vs double (oracle) SwiGLU may move
+    # a code by one step where a value sits on a rounding boundary
+    hq = np_(layer.hbuf).astype(np.int16)
+    diff = np.abs(hq - hq_ref)
+    assert diff.max() <= 1 and (diff > 0).mean() < 1e-3
+    np.testing.assert_allclose(np_(layer.hscale), hs_ref, rtol=1e-5)
+    # down product, stage-isolated: feed the oracle's hidden rows
+    layer.hbuf.copy_(dev(hq_ref))
+    layer.hscale.copy_(dev(hs_ref))
+    isum_d = torch.zeros((rows, w.d, w.h // 32), dtype=torch.int32, device=DEV)
+    layer.down(T, isum=isum_d)
+    assert np.array_equal(np_(isum_d), idn_ref)
+    assert row_rel_err(np_(layer.f), f_ref) < 1e-5
+
+
+# ------------------------------------------------------------ whole layer
+CASES = [
+    ("tiny_f32", 128, {}),
+    ("tiny_f32", 37, {}),
+    ("s_prefill", 256, {}),
+    ("s_prefill", 100, {"hs": 0}),
+    ("s_prefill", 1, {}),
+    ("m_prefill", 200, {}),
+    ("l_prefill", 130, {}),
+    ("l_prefill_bf16", 64, {}),
+    ("s_prefill", 64, {"E": 8, "k": 2, "d": 128, "h": 64, "hs": 64}),
+    ("s_prefill", 16, {"E": 1, "k": 1, "hs": 0}),
+]
+
+
+@pytest.mark.parametrize("name,T,over", CASES)
+def test_layer_end_to_end(name, T, over):
+    w = wl.WORKLOADS[name].with_(T=T, **over)
+    lw = wl.layer_weights(w)
+    x = wl.tokens(w)
+    layer = make_layer(w, lw)
+    layer.forward(dev(x))
+    ref = oracle_forward(w, lw, x)
+    assert np.array_equal(np_(layer.idx), ref.idx)
+    np.testing.assert_allclose(np_(layer.topw), ref.w, rtol=1e-5, atol=1e-9)
+    y = layer_output(layer)
+    tol = TOL_BF16 if w.wfmt == "bf16" else TOL_F32
+    assert row_rel_err(y, ref.y) <= tol
+    # routed outputs per slot, and the shared expert on its own (the routed
+    # term is only a few percent of y)
+    inv = np_(layer.inv)
+    f = np_(layer.f)[inv].reshape(T, w.k, w.d)
+    assert row_rel_err(f.reshape(T * w.k, w.d), ref.f.reshape(T * w.k, w.d)) <= (
+        TOL_BF16 if w.wfmt == "bf16" else 5e-3)
+    if w.hs:
+        assert row_rel_err(np_(layer.ys), ref.ys) <= tol
+
+
+def test_layer_deterministic_and_no_shared_equals_routed_only():
+    w = wl.WORKLOADS["s_prefill"].with_(T=300)
+    lw = wl.layer_weights(w)
+    x = dev(wl.tokens(w))
+    layer = make_layer(w, lw)
+    y1 = np_(layer.forward(x)).copy()
+    y2 = np_(layer.forward(x)).copy()
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    # zero routed down weights: y equals the shared expert bit for bit
+    lw0 = wl.LayerWeights(lw.wr, lw.bias, lw.w_gu, np.zeros_like(lw.w_d), lw.ws_gu, lw.ws_d)
+    l0 = make_layer(w, lw0)
+    y0 = np_(l0.forward(x))
+    assert np.array_equal(y0, np_(l0.ys))
+
+
+def test_token_permutation_equivariance_gpu():
+    w = wl.WORKLOADS["s_prefill"].with_(T=257)
+    lw = wl.layer_weights(w)
+    x = wl.tokens(w)
+    pi = rng(3).permutation(w.T)
+    layer = make_layer(w, lw)
+    y = np_(layer.forward(dev(x))).copy()
+    yp = np_(layer.forward(dev(x[pi]))).copy()
+    assert np.array_equal(y[pi], yp)
+
+
+def test_rmsnorm():
+    x = rng(5).standard_normal((67, 768)).astype(np.float32)
+    y = torch.empty((67, 768), dtype=torch.float32, device=DEV)
+    B.rmsnorm_f32(67, 768, 1e-5, dev(x), y)
+    assert row_rel_err(np_(y), oracle.rmsnorm(x, 1e-5)) < 1e-5
+
+
+# ------------------------------------------------------------ full sizes
+@pytest.mark.parametrize("name", ["s_prefill", "m_prefill", "l_prefill"])
+def test_full_size_sampled(name):
+    """The prefill workload at its full token count, in the configuration the
+    benchmark times: routing checked in full, y on a sample of tokens (every
+    token's output depends only on that token)."""
+    w = wl.WORKLOADS[name]
+    lw = wl.layer_weights(w)
+    x = wl.tokens(w)
+    layer = make_layer(w, lw)
+    layer.forward(dev(x))
+    i_ref, w_ref, _ = oracle.router(x, lw.wr, lw.bias, k=w.k)
+    assert np.array_equal(np_(layer.idx), i_ref)
+    o_ref, p_ref, v_ref = oracle.route(i_ref, w.E)
+    assert np.array_equal(np_(layer.offsets), o_ref)
+    assert np.array_equal(np_(layer.perm), p_ref)
+    xq_ref, sx_ref = oracle.quant_act_i8(x)
+    assert np.array_equal(np_(layer.xq), xq_ref)
+    sample = np.unique(np.concatenate([[0, w.T - 1], rng(11).choice(w.T, 62, replace=False)]))
+    ref = oracle_forward(w, lw, x[sample])
+    assert row_rel_err(np_(layer.y)[sample], ref.y) <= TOL_F32
+
+
+# ------------------------------------------------------------ decode stack
+@pytest.mark.parametrize("B_", [1, 8, 64])
+def test_decode_stack_teacher_forced(B_):
+    """S-shaped stack, 3 layers, RMSNorm between layers.  Each layer is checked
+    on the same input the device layer received (teacher forcing)."""
+    w = wl.WORKLOADS["s_decode"].with_(T=B_)
+    x = wl.tokens(w, step=0)
+    cur = dev(x)
+    for l in range(3):
+        lw = wl.layer_weights(w, layer=l)
+        layer = make_layer(w, lw)
+        xin = np_(cur).copy()
+        y = layer.forward(cur)
+        ref = oracle_forward(w, lw, xin)
+        assert np.array_equal(np_(layer.idx), ref.idx)
+        assert row_rel_err(np_(y), ref.y) <= TOL_F32
+        nxt = torch.empty_like(y)
+        B.rmsnorm_f32(B_, w.d, 1e-5, y, nxt)
+        assert row_rel_err(np_(nxt), oracle.rmsnorm(np_(y), 1e-5)) < 1e-5
+        cur = nxt
