@@ -124,12 +124,12 @@ def route(idx: np.ndarray, E: int):
 
 
 def linear_w4a8(aq, sa, wq, ws, want_isum: bool = False):
-    """out[r,o] = sa[r] * sum_g ws[o,g] * isum[r,o,g]  (double), isum optional."""
+    """out[r,o] = sa[r] * (fma chain over g of ws[o,g] * isum[r,o,g]) in FP32; isum optional."""
     aq, wq = _i8(aq), _i8(wq)
     sa, ws = _f32(sa), _f32(ws)
     rows, K = aq.shape
     N = wq.shape[0]
-    out = np.empty((rows, N), np.float64)
+    out = np.empty((rows, N), np.float32)
     isum = np.empty((rows, N, K // 32), np.int32) if want_isum else None
     _load().ora_linear_w4a8(_i64(rows), N, K, _p(aq), _p(sa), _p(wq), _p(ws), _p(out), _p(isum))
     return (out, isum) if want_isum else out
@@ -143,7 +143,7 @@ def ffn_w4a8(xq, sx, wgu_q, wgu_s, wd_q, wd_s, want_isum: bool = False):
     h = wd_q.shape[1]
     hq = np.empty((rows, h), np.int8)
     hs = np.empty((rows,), np.float32)
-    f = np.empty((rows, d), np.float64)
+    f = np.empty((rows, d), np.float32)
     igu = np.empty((rows, 2 * h, d // 32), np.int32) if want_isum else None
     idn = np.empty((rows, d, h // 32), np.int32) if want_isum else None
     _load().ora_ffn_w4a8(_i64(rows), d, h, _p(xq), _p(sx), _p(wgu_q), _p(wgu_s), _p(wd_q),
@@ -168,6 +168,25 @@ def combine(f, w, ys):
     T, k, d = f.shape
     y = np.empty((T, d), np.float64)
     _load().ora_combine(_i64(T), k, d, _p(f), _p(w), _p(ys), _p(y))
+    return y
+
+
+def combine_f32(f, w, ys):
+    """FP32 combine of the INT4 path: fma chain over slots, then + ys."""
+    f = _f32(f)
+    w = _f32(w)
+    ys = None if ys is None else _f32(ys)
+    T, k, d = f.shape
+    y = np.empty((T, d), np.float32)
+    _load().ora_combine_f32(_i64(T), k, d, _p(f), _p(w), _p(ys), _p(y))
+    return y
+
+
+def exp_ref(x):
+    """The FP32 exponential the INT4 path uses (Cody-Waite + Taylor)."""
+    x = _f32(x)
+    y = np.empty_like(x)
+    _load().ora_exp_ref(_i64(x.size), _p(x), _p(y))
     return y
 
 

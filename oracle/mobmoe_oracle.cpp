@@ -20,12 +20,15 @@
 //          one fused gate/up product per expert, SwiGLU, down product,
 //          weighted scatter back through the inverse permutation.
 //
-// Precision policy.  Where a floating-point result decides an integer (the
-// top-k choice, a quantised code, a quantisation scale) the oracle works in
-// FP32 with the operation order stated at each function, because the device
-// must reproduce those bits.  Everything else (scale application, SwiGLU,
-// softmax weights, combine, RMSNorm) is evaluated in double precision, the
-// plain definition, and the device result is compared within a tolerance.
+// Precision policy.  In the INT4/INT8 path every floating-point result can
+// decide an integer downstream (the top-k choice, the INT8 code of the hidden
+// row), so that path is evaluated in FP32 with the operation order stated at
+// each function: scale application as an fma chain over groups, SwiGLU with
+// the exponential exp_ref below, softmax with a fixed summation tree, combine
+// as an fma chain over slots.  The device follows the same order and must
+// match bit for bit.  The FP32-weight and BF16-weight paths and RMSNorm have
+// no such decisions and are evaluated in double precision (the plain
+// definition); the device is compared to them within a tolerance.
 //
 // Build: g++ -O2 -std=c++17 -ffp-contract=off -fPIC -shared -fopenmp
 // (no fast-math: every FMA below is written out as std::fma).
@@ -63,6 +66,43 @@ float round_bf16(float v) {
 }
 
 double silu(double z) { return z / (1.0 + std::exp(-z)); }
+
+// e^x in FP32 by Cody-Waite range reduction and a Taylor polynomial (a
+// textbook method; constants are the exact values of ln 2 and 1/n!):
+//   n = round_half_even(x * log2(e)),  r = x - n*ln2 with ln2 split in a part
+//   whose product with n is exact (ln2_hi, 15 significant bits) and the rest;
+//   p(r) = sum_{i=0..7} r^i / i! in Horner form with fused multiply-adds;
+//   e^x = p(r) * 2^n.  x >= 88.72 gives +inf, x <= -87.33 gives 0.
+constexpr double kLn2 = 0.69314718055994530942;
+constexpr float kLn2Hi = 0.693145751953125f;                 // 11357 / 2^14
+constexpr float kLn2Lo = (float)(kLn2 - 0.693145751953125);
+constexpr float kLog2e = (float)(1.0 / kLn2);
+
+float exp_ref(float x) {
+  if (x >= 88.72f) return INFINITY;
+  if (x <= -87.33f) return 0.0f;
+  const float n = std::nearbyint(x * kLog2e);
+  float r = std::fma(n, -kLn2Hi, x);
+  r = std::fma(n, -kLn2Lo, r);
+  float p = 1.0f / 5040.0f;
+  p = std::fma(p, r, 1.0f / 720.0f);
+  p = std::fma(p, r, 1.0f / 120.0f);
+  p = std::fma(p, r, 1.0f / 24.0f);
+  p = std::fma(p, r, 1.0f / 6.0f);
+  p = std::fma(p, r, 0.5f);
+  p = std::fma(p, r, 1.0f);
+  p = std::fma(p, r, 1.0f);
+  return std::ldexp(p, (int)n);
+}
+
+float silu32(float z) { return z / (1.0f + exp_ref(-z)); }
+
+// Balanced pairwise sum of 64 values: pairs at distance 1, then 2, 4, ..., 32.
+float tree64(float* p) {
+  for (int s = 1; s < 64; s *= 2)
+    for (int l = 0; l < 64; l += 2 * s) p[l] = p[l] + p[l + s];
+  return p[0];
+}
 
 }  // namespace
 
@@ -129,9 +169,7 @@ static float router_logit(const float* x, const float* w, int d, float bias) {
   float p[64];
   for (int l = 0; l < 64; ++l) p[l] = 0.0f;
   for (int j = 0; j < d; ++j) p[j % 64] = std::fma(x[j], w[j], p[j % 64]);
-  for (int s = 1; s < 64; s *= 2)
-    for (int l = 0; l < 64; l += 2 * s) p[l] = p[l] + p[l + s];
-  return p[0] + bias;
+  return tree64(p) + bias;
 }
 
 // Router: FP32 logits (plus an optional per-expert bias added to every
@@ -139,8 +177,9 @@ static float router_logit(const float* x, const float* w, int d, float bias) {
 //   selection: experts ordered by (logit descending, index ascending); the
 //     first k are idx[t][0..k-1].  Selecting on the logits is the same as
 //     selecting on the softmax, which is monotone in the logit.
-//   gate weights: softmax over ALL E logits, not renormalised over the k:
-//     w[t][j] = exp(l_idx - m) / sum_e exp(l_e - m), m = max_e l_e  (double).
+//   gate weights: softmax over ALL E logits, not renormalised over the k, in
+//     FP32: m = max_e l_e, z_e = exp_ref(l_e - m), S = tree64 of z_0..z_{E-1}
+//     padded with zeros to 64 entries, w[t][j] = z_idx / S.
 // logits_out [T][E] FP32 is optional.  Returns -1 on bad shapes.
 int ora_router(int64_t T, int d, int E, int k, const float* x, const float* wr,
                const float* bias, float* logits_out, int32_t* idx, double* w) {
@@ -155,13 +194,15 @@ int ora_router(int64_t T, int d, int E, int k, const float* x, const float* wr,
     for (int e = 0; e < E; ++e) order[e] = e;
     std::stable_sort(order.begin(), order.end(),
                      [&](int a, int b) { return lg[a] > lg[b]; });
-    float m = lg[order[0]];
-    double S = 0.0;
-    for (int e = 0; e < E; ++e) S += std::exp((double)lg[e] - (double)m);
+    const float m = lg[order[0]];
+    float z[64], zs[64];
+    for (int e = 0; e < 64; ++e) z[e] = e < E ? exp_ref(lg[e] - m) : 0.0f;
+    std::copy(z, z + 64, zs);
+    const float S = tree64(zs);
     for (int j = 0; j < k; ++j) {
       int e = order[j];
       idx[t * k + j] = e;
-      w[t * k + j] = std::exp((double)lg[e] - (double)m) / S;
+      w[t * k + j] = z[e] / S;
     }
   }
   return 0;
@@ -169,7 +210,8 @@ int ora_router(int64_t T, int d, int E, int k, const float* x, const float* wr,
 
 // Sigmoid gating with per-token renormalisation over the selected k
 // (the training-time gate of the "Pre-training" section): selection as above
-// on the (biased) logits, w_j = sig(l_j) / sum_{i in top-k} sig(l_i).
+// on the (biased) logits, FP32: g_j = 1 / (1 + exp_ref(-l_j)) for the k
+// selected, S = tree64 of g_0..g_{k-1} padded with zeros, w_j = g_j / S.
 int ora_router_sigmoid(int64_t T, int d, int E, int k, const float* x, const float* wr,
                        const float* bias, int32_t* idx, double* w) {
   if (d % 64 || E < 1 || k < 1 || k > E) return -1;
@@ -181,11 +223,13 @@ int ora_router_sigmoid(int64_t T, int d, int E, int k, const float* x, const flo
     for (int e = 0; e < E; ++e) order[e] = e;
     std::stable_sort(order.begin(), order.end(),
                      [&](int a, int b) { return lg[a] > lg[b]; });
-    double S = 0.0;
-    for (int j = 0; j < k; ++j) S += 1.0 / (1.0 + std::exp(-(double)lg[order[j]]));
+    float g[64], gs[64];
+    for (int j = 0; j < 64; ++j) g[j] = j < k ? 1.0f / (1.0f + exp_ref(-lg[order[j]])) : 0.0f;
+    std::copy(g, g + 64, gs);
+    const float S = tree64(gs);
     for (int j = 0; j < k; ++j) {
       idx[t * k + j] = order[j];
-      w[t * k + j] = (1.0 / (1.0 + std::exp(-(double)lg[order[j]]))) / S;
+      w[t * k + j] = g[j] / S;
     }
   }
   return 0;
@@ -227,25 +271,27 @@ int ora_route(int64_t T, int E, int k, const int32_t* idx, int32_t* offsets,
 // ---------------------------------------------------------------------------
 // W4A8 linear on one row: out[o] = s_a * sum_g s_w[o][g] * isum[o][g], with
 //   isum[o][g] = sum_{c in group g} (int32) q_w[o][c] * (int32) q_a[c]
-// (exact in int32).  Scale application in double.  isum_out [N][K/32] optional.
+// (exact in int32; (float)isum is exact too, |isum| <= 32*8*128).  Scale
+// application in FP32: acc = 0; acc = fma(s_w[o][g], isum, acc) for g
+// ascending; out = acc * s_a.  isum_out [N][K/32] optional.
 static void linear_w4a8_row(int N, int K, const int8_t* aq, float sa, const int8_t* wq,
-                            const float* ws, double* out, int32_t* isum_out) {
+                            const float* ws, float* out, int32_t* isum_out) {
   const int G = K / kGroup;
   for (int o = 0; o < N; ++o) {
-    double acc = 0.0;
+    float acc = 0.0f;
     for (int g = 0; g < G; ++g) {
       int32_t is = 0;
       for (int c = g * kGroup; c < (g + 1) * kGroup; ++c)
         is += (int32_t)wq[(int64_t)o * K + c] * (int32_t)aq[c];
       if (isum_out) isum_out[(int64_t)o * G + g] = is;
-      acc += (double)ws[(int64_t)o * G + g] * (double)is;
+      acc = std::fma(ws[(int64_t)o * G + g], (float)is, acc);
     }
-    out[o] = acc * (double)sa;
+    out[o] = acc * sa;
   }
 }
 
 int ora_linear_w4a8(int64_t rows, int N, int K, const int8_t* aq, const float* sa,
-                    const int8_t* wq, const float* ws, double* out, int32_t* isum) {
+                    const int8_t* wq, const float* ws, float* out, int32_t* isum) {
   if (K % kGroup) return -1;
   const int G = K / kGroup;
   for (int64_t r = 0; r < rows; ++r)
@@ -254,27 +300,26 @@ int ora_linear_w4a8(int64_t rows, int N, int K, const int8_t* aq, const float* s
   return 0;
 }
 
-// One SwiGLU expert FFN on one INT8 row (NC: gate rows 0..h-1 and up rows
-// h..2h-1 of the stacked gate/up weight, SiLU(g) * u, INT8 re-quantisation of
-// that hidden row, then the down product).
+// One SwiGLU expert FFN on one INT8 row: gate rows 0..h-1 and up rows h..2h-1
+// of the stacked gate/up weight, a = SiLU(g) * u in FP32 with
+// SiLU(z) = z / (1 + exp_ref(-z)), INT8 re-quantisation of that hidden row,
+// then the down product.
 //   wgu_q [2h][d] / wgu_s [2h][d/32], wd_q [d][h] / wd_s [d][h/32].
-//   The hidden row is rounded to FP32 before its INT8 quantisation, since the
-//   quantiser's decisions are defined in FP32.
 static void ffn_w4a8_row(int d, int h, const int8_t* xq, float sx, const int8_t* wgu_q,
                          const float* wgu_s, const int8_t* wd_q, const float* wd_s,
-                         int8_t* hq, float* hs, double* f, int32_t* isum_gu,
+                         int8_t* hq, float* hs, float* f, int32_t* isum_gu,
                          int32_t* isum_d) {
-  std::vector<double> gu(2 * h);
+  std::vector<float> gu(2 * h);
   linear_w4a8_row(2 * h, d, xq, sx, wgu_q, wgu_s, gu.data(), isum_gu);
   std::vector<float> a(h);
-  for (int o = 0; o < h; ++o) a[o] = (float)(silu(gu[o]) * gu[h + o]);
+  for (int o = 0; o < h; ++o) a[o] = silu32(gu[o]) * gu[h + o];
   ora_quant_act_i8(1, h, a.data(), hq, hs);
   linear_w4a8_row(d, h, hq, *hs, wd_q, wd_s, f, isum_d);
 }
 
 int ora_ffn_w4a8(int64_t rows, int d, int h, const int8_t* xq, const float* sx,
                  const int8_t* wgu_q, const float* wgu_s, const int8_t* wd_q,
-                 const float* wd_s, int8_t* hq, float* hs, double* f, int32_t* isum_gu,
+                 const float* wd_s, int8_t* hq, float* hs, float* f, int32_t* isum_gu,
                  int32_t* isum_d) {
   if (d % kGroup || h % kGroup) return -1;
   for (int64_t r = 0; r < rows; ++r)
@@ -332,6 +377,19 @@ int ora_combine(int64_t T, int k, int d, const double* f, const double* w, const
       double acc = 0.0;
       for (int j = 0; j < k; ++j) acc += w[t * k + j] * f[(t * k + j) * d + c];
       y[t * d + c] = acc + (ys ? ys[t * d + c] : 0.0);
+    }
+  return 0;
+}
+
+// FP32 combine of the INT4/INT8 path: acc = 0; acc = fma(w[t][j], f[t][j][c],
+// acc) for j ascending; y = acc + ys (ys may be null).
+int ora_combine_f32(int64_t T, int k, int d, const float* f, const float* w, const float* ys,
+                    float* y) {
+  for (int64_t t = 0; t < T; ++t)
+    for (int c = 0; c < d; ++c) {
+      float acc = 0.0f;
+      for (int j = 0; j < k; ++j) acc = std::fma(w[t * k + j], f[(t * k + j) * d + c], acc);
+      y[t * d + c] = ys ? acc + ys[t * d + c] : acc;
     }
   return 0;
 }
@@ -408,8 +466,12 @@ int ora_forward(int d, int E, int h, int hs, int k, int wfmt, int gating, int64_
     if (out->sx) std::copy(sx.begin(), sx.end(), out->sx);
   }
 
+  // INT4 path: FP32 throughout (see the precision policy at the top);
+  // FP32/BF16 weight paths: double.
   std::vector<double> f((int64_t)T * k * d);
   std::vector<double> ys(hs ? (int64_t)T * d : 0);
+  std::vector<float> f32(wfmt == 1 ? (int64_t)T * k * d : 0);
+  std::vector<float> ys32(wfmt == 1 && hs ? (int64_t)T * d : 0);
   const int64_t gu_q_stride = (int64_t)2 * h * d, gu_s_stride = gu_q_stride / kGroup;
   const int64_t d_q_stride = (int64_t)d * h, d_s_stride = d_q_stride / kGroup;
 
@@ -420,40 +482,53 @@ int ora_forward(int d, int E, int h, int hs, int k, int wfmt, int gating, int64_
   for (int64_t t = 0; t < T; ++t) {
     for (int j = 0; j < k; ++j) {
       const int e = idx[t * k + j];
-      double* fr = f.data() + (t * k + j) * d;
       if (wfmt == 1) {
         std::vector<int8_t> hq(h);
         float hsc = 0.0f;
         ffn_w4a8_row(d, h, xq.data() + t * d, sx[t], gu_q.data() + e * gu_q_stride,
                      gu_s.data() + e * gu_s_stride, d_q.data() + e * d_q_stride,
-                     d_s.data() + e * d_s_stride, hq.data(), &hsc, fr, nullptr, nullptr);
+                     d_s.data() + e * d_s_stride, hq.data(), &hsc,
+                     f32.data() + (t * k + j) * d, nullptr, nullptr);
         if (out->hq) std::copy(hq.begin(), hq.end(), out->hq + (t * k + j) * h);
         if (out->hs) out->hs[t * k + j] = hsc;
       } else {
         ffn_float_row(d, h, x + t * d, w_gu + e * gu_q_stride, w_d + e * d_q_stride,
-                      wfmt == 2 ? 1 : 0, fr);
+                      wfmt == 2 ? 1 : 0, f.data() + (t * k + j) * d);
       }
     }
     if (hs) {
-      double* yr = ys.data() + t * d;
       if (wfmt == 1) {
         std::vector<int8_t> hq(hs);
         float hsc = 0.0f;
         ffn_w4a8_row(d, hs, xq.data() + t * d, sx[t], sgu_q.data(), sgu_s.data(),
-                     sd_q.data(), sd_s.data(), hq.data(), &hsc, yr, nullptr, nullptr);
+                     sd_q.data(), sd_s.data(), hq.data(), &hsc, ys32.data() + t * d, nullptr,
+                     nullptr);
         if (out->hq_s) std::copy(hq.begin(), hq.end(), out->hq_s + t * hs);
         if (out->hs_s) out->hs_s[t] = hsc;
       } else {
-        ffn_float_row(d, hs, x + t * d, ws_gu, ws_d, wfmt == 2 ? 1 : 0, yr);
+        ffn_float_row(d, hs, x + t * d, ws_gu, ws_d, wfmt == 2 ? 1 : 0, ys.data() + t * d);
       }
     }
   }
+  if (wfmt == 1) {
+    std::copy(f32.begin(), f32.end(), f.begin());
+    if (hs) std::copy(ys32.begin(), ys32.end(), ys.begin());
+    std::vector<float> w32(w.begin(), w.end()), y32((int64_t)T * d);
+    ora_combine_f32(T, k, d, f32.data(), w32.data(), hs ? ys32.data() : nullptr, y32.data());
+    std::copy(y32.begin(), y32.end(), out->y);
+  } else {
+    ora_combine(T, k, d, f.data(), w.data(), hs ? ys.data() : nullptr, out->y);
+  }
   if (out->f) std::copy(f.begin(), f.end(), out->f);
   if (out->ys && hs) std::copy(ys.begin(), ys.end(), out->ys);
-  ora_combine(T, k, d, f.data(), w.data(), hs ? ys.data() : nullptr, out->y);
   if (wfmt == 2)
     for (int64_t i = 0; i < T * d; ++i) out->y[i] = round_bf16((float)out->y[i]);
   return 0;
+}
+
+// FP32 exponential of the INT4 path, exposed for its pin.
+void ora_exp_ref(int64_t n, const float* x, float* y) {
+  for (int64_t i = 0; i < n; ++i) y[i] = exp_ref(x[i]);
 }
 
 // BF16 rounding exposed for the pins.

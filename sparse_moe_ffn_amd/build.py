@@ -24,6 +24,8 @@ CFLAGS = [
     # packed FP32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # matrix-core results in VGPRs (no accumulation-register copies in the epilogue)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -132,6 +132,26 @@ mm_status check_weight(const mm_layer_desc* d, const mm_weight& w, const char* n
 
 hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// INT4 gate/up + SwiGLU + per-row re-quantisation: matrix-core GEMM then the
+// row quantiser for larger row counts, the fused row-tile kernel otherwise.
+hipError_t gateup_i4(const mm::ExpertArgs& a, const int8_t* xq, const float* sx,
+                     const uint8_t* wq, const float* ws, float* abuf, int8_t* hq, float* hs,
+                     int32_t* isum, hipStream_t st) {
+  if (a.rows >= mm::kMfmaMinRows && a.d % mm::kMfmaK == 0) {
+    hipError_t e = mm::launch_gateup_i4_mfma(a, xq, sx, wq, ws, abuf, isum, st);
+    if (e != hipSuccess) return e;
+    return mm::launch_act_quant_i8(a.rows, a.h, abuf, hq, hs, st);
+  }
+  return mm::launch_gateup_i4(a, xq, sx, wq, ws, abuf, hq, hs, isum, st);
+}
+
+hipError_t down_i4(const mm::ExpertArgs& a, const int8_t* hq, const float* hs,
+                   const uint8_t* wq, const float* ws, float* f, int32_t* isum, hipStream_t st) {
+  if (a.rows >= mm::kMfmaMinRows && a.h % mm::kMfmaK == 0)
+    return mm::launch_down_i4_mfma(a, hq, hs, wq, ws, f, isum, st);
+  return mm::launch_down_i4(a, hq, hs, wq, ws, f, isum, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -267,9 +287,9 @@ static mm_status gateup_impl(const mm_layer_desc* desc, int64_t T, const void* a
     if (ws_size < ws_bytes(desc, T, MM_WS_GATEUP))
       return fail(MM_ERR_WORKSPACE, "gate/up workspace too small (need %lld bytes)", (long long)ws_bytes(desc, T, MM_WS_GATEUP));
     float* abuf = static_cast<float*>(ws);
-    return hip_status(mm::launch_gateup_i4(a, static_cast<const int8_t*>(act), act_scale,
-                                           static_cast<const uint8_t*>(w.data), w.scales, abuf,
-                                           static_cast<int8_t*>(h), h_scale, isum, st),
+    return hip_status(gateup_i4(a, static_cast<const int8_t*>(act), act_scale,
+                                static_cast<const uint8_t*>(w.data), w.scales, abuf,
+                                static_cast<int8_t*>(h), h_scale, isum, st),
                       "mm_expert_gateup_swiglu");
   }
   if (act_scale || h_scale)
@@ -313,9 +333,8 @@ static mm_status down_impl(const mm_layer_desc* desc, int64_t T, const void* h,
   hipStream_t st = S(stream);
   if (desc->wfmt == MM_W_INT4G32) {
     MM_REQUIRE(h_scale);
-    return hip_status(mm::launch_down_i4(a, static_cast<const int8_t*>(h), h_scale,
-                                         static_cast<const uint8_t*>(w.data), w.scales, f, isum,
-                                         st),
+    return hip_status(down_i4(a, static_cast<const int8_t*>(h), h_scale,
+                              static_cast<const uint8_t*>(w.data), w.scales, f, isum, st),
                       "mm_expert_down");
   }
   if (h_scale) return fail(MM_ERR_FORMAT, "h_scale must be NULL for FP32/BF16 weights");
@@ -366,12 +385,12 @@ mm_status mm_shared_expert(const mm_layer_desc* desc, int64_t T, const void* act
     float* abuf = reinterpret_cast<float*>(base + sw.a_off);
     int8_t* hq = reinterpret_cast<int8_t*>(base + sw.q_off);
     float* hsc = reinterpret_cast<float*>(base + sw.s_off);
-    MM_TRY(hip_status(mm::launch_gateup_i4(a, static_cast<const int8_t*>(act), act_scale,
-                                           static_cast<const uint8_t*>(w_gateup.data),
-                                           w_gateup.scales, abuf, hq, hsc, nullptr, st),
+    MM_TRY(hip_status(gateup_i4(a, static_cast<const int8_t*>(act), act_scale,
+                                static_cast<const uint8_t*>(w_gateup.data), w_gateup.scales,
+                                abuf, hq, hsc, nullptr, st),
                       "mm_shared_expert (gate/up)"));
-    return hip_status(mm::launch_down_i4(a, hq, hsc, static_cast<const uint8_t*>(w_down.data),
-                                         w_down.scales, ys, nullptr, st),
+    return hip_status(down_i4(a, hq, hsc, static_cast<const uint8_t*>(w_down.data),
+                              w_down.scales, ys, nullptr, st),
                       "mm_shared_expert (down)");
   }
   if (act_scale) return fail(MM_ERR_FORMAT, "act_scale must be NULL for FP32/BF16 weights");

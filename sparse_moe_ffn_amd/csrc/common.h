@@ -42,7 +42,82 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// DPP lane moves within rows of 16 lanes (gfx9 encodings).
+enum : int {
+  kDppXor1 = 0xB1,          // quad_perm [1,0,3,2]
+  kDppXor2 = 0x4E,          // quad_perm [2,3,0,1]
+  kDppHalfMirror = 0x141,   // lane i of each 8 <- lane 7-i
+  kDppMirror = 0x140        // lane i of each 16 <- lane 15-i
+};
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
+// Sum of the 64 lanes as a balanced pairwise tree over lane indices: pairs at
+// distance 1, 2, 4, 8 (inside each 16-lane row, with DPP moves; after each
+// step all lanes of a group hold the same value, so a mirror partner is as
+// good as the xor partner), then rows (0+1) and (2+3), then their sum.  Every
+// lane returns the same value.  IEEE addition is commutative, so the result
+// equals the tree evaluated in any lane order.
+__device__ __forceinline__ float tree_sum64(float v) {
+  v = v + dpp<kDppXor1>(v);
+  v = v + dpp<kDppXor2>(v);
+  v = v + dpp<kDppHalfMirror>(v);
+  v = v + dpp<kDppMirror>(v);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (a + b) + (c + d);
+}
+
+// Maximum over the 64 lanes (exact; order does not matter).
+__device__ __forceinline__ float max64(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppMirror>(v));
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+// e^x, FP32: Cody-Waite reduction x = n*ln2 + r (ln 2 split into a 15-bit head,
+// whose product with any |n| <= 128 is exact, and the remainder), then the
+// degree-7 Taylor polynomial of e^r in Horner form with fused multiply-adds,
+// then scaling by 2^n.  Every step is an IEEE-defined FP32 operation, so any
+// implementation of the same steps returns the same bits.  Accurate to about
+// 1.3 ulp on [-87.33, 88.72]; +inf above, 0 below.
+namespace expc {
+constexpr double kLn2 = 0.69314718055994530942;
+constexpr float kHi = 0.693145751953125f;  // 11357 / 2^14
+constexpr float kLo = (float)(kLn2 - 0.693145751953125);
+constexpr float kLog2e = (float)(1.0 / kLn2);
+}  // namespace expc
+
+__device__ __forceinline__ float exp_fp32(float x) {
+  if (x >= 88.72f) return __builtin_huge_valf();
+  if (x <= -87.33f) return 0.0f;
+  const float n = rintf(x * expc::kLog2e);
+  float r = fmaf(n, -expc::kHi, x);
+  r = fmaf(n, -expc::kLo, r);
+  float p = 1.0f / 5040.0f;
+  p = fmaf(p, r, 1.0f / 720.0f);
+  p = fmaf(p, r, 1.0f / 120.0f);
+  p = fmaf(p, r, 1.0f / 24.0f);
+  p = fmaf(p, r, 1.0f / 6.0f);
+  p = fmaf(p, r, 0.5f);
+  p = fmaf(p, r, 1.0f);
+  p = fmaf(p, r, 1.0f);
+  return ldexpf(p, (int)n);
+}
+
+// SiLU(z) = z * sigmoid(z), written z / (1 + e^-z) with IEEE division.
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + exp_fp32(-z)); }
 
 // FP32 -> BF16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
@@ -52,6 +127,44 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Tile lookup for the routed (expert-sorted) layout: expert e owns rows
+// [offsets[e], offsets[e+1]) cut into ceil(n_e / rows_per_tile) tiles,
+// numbered expert by expert.  Called by all 64 lanes of one wave: lane e
+// computes its expert's tile count, an inclusive scan over the lanes gives
+// each expert's first tile, and the lane whose range holds tile `mt` writes
+// (first row, rows, expert) to *p0, *n, *e; if none does, lane 0 writes n = 0.
+// Offsets are clamped to [0, rows] so a corrupt table cannot move a tile out
+// of bounds.  E <= 64.
+__device__ __forceinline__ void routed_tile(const int32_t* __restrict__ offsets, int E, int rows,
+                                            int rows_per_tile, int mt, int* p0, int* n, int* e) {
+  const int lane = threadIdx.x & 63;
+  int beg = 0, end = 0;
+  if (lane < E) {
+    beg = min(max(offsets[lane], 0), rows);
+    end = min(max(offsets[lane + 1], beg), rows);
+  }
+  const int nt = (end - beg + rows_per_tile - 1) / rows_per_tile;
+  int inc = nt;
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) {
+    const int v = __shfl_up(inc, s);
+    if (lane >= s) inc += v;
+  }
+  const int first = inc - nt;
+  const bool mine = lane < E && mt >= first && mt < inc;
+  const uint64_t owners = __ballot(mine);  // all 64 lanes take part
+  if (mine) {
+    *p0 = beg + (mt - first) * rows_per_tile;
+    *n = min(rows_per_tile, end - *p0);
+    *e = lane;
+  }
+  if (lane == 0 && owners == 0ull) {
+    *p0 = 0;
+    *n = 0;
+    *e = 0;
+  }
+}
 
 // Per-row INT8 code of v given the row scale s (s > 0): clamp(rint(v / s)).
 __device__ __forceinline__ int8_t quant_i8(float v, float s) {

@@ -30,27 +30,8 @@ __device__ void find_tile(const ExpertArgs& a, int& p0, int& n, int& e) {
     e = 0;
     return;
   }
-  if (threadIdx.x == 0) {
-    int tile0 = 0;
-    s_n = 0;
-    s_p0 = 0;
-    s_e = 0;
-    const int rows = (int)a.rows;
-    for (int ex = 0; ex < a.E; ++ex) {
-      // clamped so that a corrupt offsets table cannot move a tile outside [0, rows)
-      const int beg = min(max(a.offsets[ex], 0), rows);
-      const int end = min(max(a.offsets[ex + 1], beg), rows);
-      const int nt = (end - beg + kRows - 1) / kRows;
-      if ((int)blockIdx.x < tile0 + nt) {
-        const int ti = (int)blockIdx.x - tile0;
-        s_p0 = beg + ti * kRows;
-        s_n = min(kRows, end - s_p0);
-        s_e = ex;
-        break;
-      }
-      tile0 += nt;
-    }
-  }
+  if (threadIdx.x < 64)
+    routed_tile(a.offsets, a.E, (int)a.rows, kRows, (int)blockIdx.x, &s_p0, &s_n, &s_e);
   __syncthreads();
   p0 = s_p0;
   n = s_n;

@@ -87,11 +87,47 @@ __global__ __launch_bounds__(256) void k_act_quant_i8(int64_t rows, int64_t cols
   const float* xr = x + r * cols;
   float amax = 0.0f;
   for (int64_t c = lane; c < cols; c += kWave) amax = fmaxf(amax, fabsf(xr[c]));
-  amax = wave_max(amax);
+  amax = max64(amax);
   const float sr = (2.0f * amax) / 255.0f;
   if (lane == 0) s[r] = sr;
   int8_t* qr = q + r * cols;
   for (int64_t c = lane; c < cols; c += kWave) qr[c] = sr != 0.0f ? quant_i8(xr[c], sr) : (int8_t)0;
+}
+
+// Same quantiser, rows with cols % 128 == 0: the row is read once as float2
+// per lane, kept in registers, and written as 2 codes per lane.
+template <int kMaxV>
+__global__ __launch_bounds__(256) void k_act_quant_i8_v2(int64_t rows, int64_t cols,
+                                                         const float* __restrict__ x,
+                                                         int8_t* __restrict__ q,
+                                                         float* __restrict__ s) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int nv = (int)(cols / 128);
+  const float2* xr = reinterpret_cast<const float2*>(x + r * cols);
+  float2 v[kMaxV];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kMaxV; ++i)
+    if (i < nv) {
+      v[i] = xr[lane + 64 * i];
+      amax = fmaxf(amax, fmaxf(fabsf(v[i].x), fabsf(v[i].y)));
+    }
+  amax = max64(amax);
+  const float sr = (2.0f * amax) / 255.0f;
+  if (lane == 0) s[r] = sr;
+  uint16_t* qr = reinterpret_cast<uint16_t*>(q + r * cols);
+#pragma unroll
+  for (int i = 0; i < kMaxV; ++i)
+    if (i < nv) {
+      int8_t a = 0, b = 0;
+      if (sr != 0.0f) {
+        a = quant_i8(v[i].x, sr);
+        b = quant_i8(v[i].y, sr);
+      }
+      qr[lane + 64 * i] = (uint16_t)((uint8_t)a | ((uint16_t)(uint8_t)b << 8));
+    }
 }
 
 __global__ __launch_bounds__(256) void k_convert_bf16(int64_t n, const float* __restrict__ x,
@@ -136,8 +172,12 @@ hipError_t launch_prepack_int4g32(int64_t n_mat, int64_t rows, int64_t cols, con
 
 hipError_t launch_act_quant_i8(int64_t rows, int64_t cols, const float* x, int8_t* q, float* s,
                                hipStream_t st) {
-  hipLaunchKernelGGL(k_act_quant_i8, dim3(blocks_for(rows, 4)), dim3(256), 0, st, rows, cols, x,
-                     q, s);
+  if (cols % 128 == 0 && cols <= 128 * 24)
+    hipLaunchKernelGGL(k_act_quant_i8_v2<24>, dim3(blocks_for(rows, 4)), dim3(256), 0, st, rows,
+                       cols, x, q, s);
+  else
+    hipLaunchKernelGGL(k_act_quant_i8, dim3(blocks_for(rows, 4)), dim3(256), 0, st, rows, cols, x,
+                       q, s);
   return hipGetLastError();
 }
 

@@ -46,6 +46,19 @@ hipError_t launch_gateup_i4(const ExpertArgs& a, const int8_t* xq, const float* 
 hipError_t launch_down_i4(const ExpertArgs& a, const int8_t* hq, const float* hs,
                           const uint8_t* wq, const float* ws, float* f, int32_t* isum,
                           hipStream_t st);
+// Matrix-core forms (k_mfma.hip) for larger row counts.  Gate/up writes the
+// FP32 hidden rows a = SiLU(g) * u to a_buf [rows][h]; re-quantise them with
+// launch_act_quant_i8.  Down writes f [rows][d].
+hipError_t launch_gateup_i4_mfma(const ExpertArgs& a, const int8_t* xq, const float* sx,
+                                 const uint8_t* wq, const float* ws, float* a_buf, int32_t* isum,
+                                 hipStream_t st);
+hipError_t launch_down_i4_mfma(const ExpertArgs& a, const int8_t* hq, const float* hs,
+                               const uint8_t* wq, const float* ws, float* f, int32_t* isum,
+                               hipStream_t st);
+// The matrix-core forms are used from this many rows on, when the reduction
+// dimension is a multiple of 128.
+constexpr int64_t kMfmaMinRows = 256;
+constexpr int kMfmaK = 128;
 // Floating-point forms: bf16 = false uses FP32 operands, true uses BF16.
 hipError_t launch_gateup_fp(const ExpertArgs& a, bool bf16, const void* x, const void* w,
                             void* h_out, hipStream_t st);

@@ -64,7 +64,7 @@ class MoELayer:
 
     def __init__(self, d, E, h, hs, k, wr, bias, w_gu, w_d, ws_gu=None, ws_d=None, *,
                  wfmt="int4g32", gating=0, out_dtype=B.MM_OUT_F32, device="cuda",
-                 keep_canonical=False):
+                 keep_canonical=False, overlap_shared=True):
         self.d, self.E, self.h, self.hs, self.k = d, E, h, hs, k
         self.wfmt = wfmt
         self.device = torch.device(device)
@@ -76,6 +76,10 @@ class MoELayer:
         self.ws_gu = prepare_weight(ws_gu, wfmt, self.device, keep_canonical) if hs else None
         self.ws_d = prepare_weight(ws_d, wfmt, self.device, keep_canonical) if hs else None
         self._T = -1
+        # The shared expert depends only on the (quantised) input, so it can run
+        # on a second stream (default priority) beside the routed experts.
+        self.overlap_shared = overlap_shared and bool(hs)
+        self.side = torch.cuda.Stream(device=self.device) if self.overlap_shared else None
 
     @classmethod
     def from_workload(cls, w, lw, device="cuda", **kw):
@@ -106,6 +110,9 @@ class MoELayer:
         self.y = _empty((T, d), torch.float32 if self.desc.out_dtype == B.MM_OUT_F32 else torch.int16, dv)
         self.ws_bytes = max(B.workspace_bytes(self.desc, T, B.MM_WS_MAX), 256)
         self.ws = _empty((self.ws_bytes,), torch.uint8, dv)
+        # separate workspace for the shared expert so it can run concurrently
+        self.ws2_bytes = max(B.workspace_bytes(self.desc, T, B.MM_WS_SHARED), 256)
+        self.ws2 = _empty((self.ws2_bytes,), torch.uint8, dv)
         self._T = T
 
     # The seven calls, in order.  Each uses the current torch stream.
@@ -132,8 +139,8 @@ class MoELayer:
 
     def shared(self, x, T):
         a, s = self.act(x)
-        B.shared_expert(self.desc, T, a, s, self.ws_gu.c(), self.ws_d.c(), self.ys, self.ws,
-                        self.ws_bytes)
+        B.shared_expert(self.desc, T, a, s, self.ws_gu.c(), self.ws_d.c(), self.ys, self.ws2,
+                        self.ws2_bytes)
 
     def combine(self, T):
         B.combine(self.desc, T, self.f, self.inv, self.topw, self.ys, self.y)
@@ -142,13 +149,20 @@ class MoELayer:
         """y = eq. (*) of x [T, d] FP32 (device).  Returns the layer's y buffer."""
         T = x.shape[0]
         self.buffers(T)
-        self.router(x, T)
-        self.route(T)
         if self.wfmt == "int4g32":
             self.act_quant(x, T)
+        main = torch.cuda.current_stream(self.device)
+        if self.overlap_shared:
+            self.side.wait_stream(main)
+            with torch.cuda.stream(self.side):
+                self.shared(x, T)
+        self.router(x, T)
+        self.route(T)
         self.gateup(x, T)
         self.down(T)
-        if self.hs:
+        if self.hs and not self.overlap_shared:
             self.shared(x, T)
+        if self.overlap_shared:
+            main.wait_stream(self.side)
         self.combine(T)
         return self.y

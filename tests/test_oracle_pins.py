@@ -119,7 +119,9 @@ def test_linear_isum_bruteforce_and_dequant(ora):
     wdq = (wq.reshape(N, K // 32, 32) * ws[..., None].astype(np.float64)).reshape(N, K)
     xdq = aq.astype(np.float64) * sa[:, None].astype(np.float64)
     ref = xdq @ wdq.T
-    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-15)
+    # FP32 scale application (fma chain over 6 groups, then one product)
+    bound = 8 * 2.0 ** -24 * (np.abs(isum) * ws[None].astype(np.float64)).sum(-1) * sa[:, None]
+    assert np.all(np.abs(out - ref) <= bound + 1e-30)
 
 
 # ----------------------------------------------------------------- router
@@ -189,7 +191,7 @@ def test_router_against_double(ora):
     lg = logits.astype(np.float64)
     p = np.exp(lg - lg.max(1, keepdims=True))
     p /= p.sum(1, keepdims=True)
-    np.testing.assert_allclose(w, np.take_along_axis(p, idx, 1), rtol=1e-12)
+    np.testing.assert_allclose(w, np.take_along_axis(p, idx, 1), rtol=1e-6)
     assert np.all(w.sum(1) < 1.0)
 
 
@@ -198,7 +200,7 @@ def test_router_full_k_sums_to_one(ora):
     x = g.standard_normal((16, 64)).astype(np.float32)
     wr = g.standard_normal((8, 64)).astype(np.float32)
     idx, w, logits = ora.router(x, wr, None, k=8)
-    np.testing.assert_allclose(w.sum(1), 1.0, atol=1e-12)
+    np.testing.assert_allclose(w.sum(1), 1.0, atol=1e-6)
     assert np.all(np.sort(idx, 1) == np.arange(8))
 
 
@@ -209,7 +211,7 @@ def test_router_ties_and_forced_bias(ora):
     wr = np.tile(row, (60, 1))
     idx, w, _ = ora.router(x, wr, None, k=4)
     assert np.all(idx == np.arange(4))             # equal logits: lowest index first
-    np.testing.assert_allclose(w, 1 / 60, rtol=1e-12)
+    np.testing.assert_allclose(w, 1 / 60, rtol=1e-6)
     wr2 = (g.standard_normal((60, 128)) * 0.02).astype(np.float32)
     bias = np.zeros(60, np.float32)
     bias[[7, 19, 33, 58]] = [100, 101, 102, 103]
@@ -226,7 +228,7 @@ def test_router_sigmoid_gate(ora):
     assert np.array_equal(i_s, i_g)                # both gates are monotone in the logit
     sel = np.take_along_axis(lg.astype(np.float64), i_g, 1)
     ref = expit(sel) / expit(sel).sum(1, keepdims=True)
-    np.testing.assert_allclose(w_g, ref, rtol=1e-12)
+    np.testing.assert_allclose(w_g, ref, rtol=1e-6)
 
 
 # ----------------------------------------------------------------- routing
@@ -288,7 +290,8 @@ def test_ffn_w4a8_against_dequantised_double(ora):
     amax = np.abs(a).max(1)
     np.testing.assert_allclose(hs, 2 * amax / 255, rtol=1e-6)
     assert np.all(np.abs(hd - a) <= hs[:, None] * 0.5 * (1 + 1e-4))
-    np.testing.assert_allclose(f, hd @ W(dq, ds).T, rtol=1e-12, atol=1e-14)
+    fd = hd @ W(dq, ds).T
+    assert (np.abs(f - fd).max(1) / np.abs(fd).max(1)).max() < 1e-5
     # and the whole thing is close to the unquantised FP32 FFN
     ref = _dense_swiglu(x.astype(np.float64), wgu.astype(np.float64), wd.astype(np.float64))
     assert np.abs(f - ref).max() / np.abs(ref).max() < 0.3
@@ -322,7 +325,7 @@ def test_k_equals_E_is_dense_softmax_mixture(ora):
     ref = sum(p[:, e:e + 1] * _dense_swiglu(X, wgu[e].astype(np.float64), wd[e].astype(np.float64))
               for e in range(E))
     ref += _dense_swiglu(X, sgu.astype(np.float64), sd.astype(np.float64))
-    np.testing.assert_allclose(r.y, ref, rtol=1e-10, atol=1e-13)
+    assert (np.abs(r.y - ref).max(1) / np.abs(ref).max(1)).max() < 1e-6
 
 
 @pytest.mark.parametrize("wfmt", ["f32", "int4g32"])
@@ -344,17 +347,22 @@ def test_dense_masked_bruteforce(ora, wfmt):
         allf = np.stack([_dense_swiglu(X, wgu[e].astype(np.float64), wd[e].astype(np.float64))
                          for e in range(E)], 1)
         ys = _dense_swiglu(X, sgu.astype(np.float64), sd.astype(np.float64))
-        tol = 1e-12
+        exact_parts = False
     else:
         xq, sx = ora.quant_act_i8(x)
         allf = np.stack([ora.ffn_w4a8(xq, sx, *ora.quant_w4g32(wgu[e]), *ora.quant_w4g32(wd[e]))[2]
-                         for e in range(E)], 1)
-        ys = ora.ffn_w4a8(xq, sx, *ora.quant_w4g32(sgu), *ora.quant_w4g32(sd))[2]
-        tol = 1e-12
+                         for e in range(E)], 1).astype(np.float64)
+        ys = ora.ffn_w4a8(xq, sx, *ora.quant_w4g32(sgu), *ora.quant_w4g32(sd))[2].astype(np.float64)
+        exact_parts = True
     ref = np.einsum("te,ted->td", mask * p, allf) + ys
-    np.testing.assert_allclose(r.y, ref, rtol=tol, atol=1e-14)
-    np.testing.assert_allclose(r.ys, ys, rtol=tol, atol=1e-15)
-    np.testing.assert_allclose(r.f, np.take_along_axis(allf, r.idx[..., None], 1), rtol=tol, atol=1e-15)
+    # gate weights and the combine are FP32 in the INT4 path
+    assert (np.abs(r.y - ref).max(1) / np.abs(ref).max(1)).max() < 1e-6
+    sel = np.take_along_axis(allf, r.idx[..., None], 1)
+    if exact_parts:          # same FP32 arithmetic, evaluated expert by expert
+        assert np.array_equal(r.ys, ys) and np.array_equal(r.f, sel)
+    else:
+        np.testing.assert_allclose(r.ys, ys, rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(r.f, sel, rtol=1e-12, atol=1e-15)
 
 
 def test_shared_expert_reaches_every_token(ora):
@@ -389,7 +397,9 @@ def test_expert_relabelling(ora):
     a = ora.forward(x, wr, None, wgu, wd, sgu, sd, k=4)
     b = ora.forward(x, wr[sigma], None, wgu[sigma], wd[sigma], sgu, sd, k=4)
     assert np.array_equal(sigma[b.idx], a.idx)
-    np.testing.assert_allclose(b.y, a.y, rtol=1e-12, atol=1e-15)
+    # the softmax denominator's summation tree follows expert labels, so only
+    # rounding may differ
+    assert (np.abs(b.y - a.y).max(1) / np.abs(a.y).max(1)).max() < 1e-6
 
 
 def test_layer_routing_properties(ora):
@@ -421,6 +431,28 @@ def test_bf16_layer_close_to_f32(ora):
     assert np.array_equal(a.idx, b.idx)
     assert np.all(ora.round_bf16(b.y.astype(np.float32)) == b.y)
     assert np.abs(a.y - b.y).max() / np.abs(a.y).max() < 2e-2
+
+
+def test_exp_ref_accuracy(ora):
+    x = np.linspace(-87.3, 88.7, 3_000_001, dtype=np.float32)
+    y = ora.exp_ref(x).astype(np.float64)
+    r = np.exp(x.astype(np.float64))
+    assert (np.abs(y - r) / r).max() < 2.5 * 2.0 ** -24      # within ~2 ulp
+    sp = ora.exp_ref(np.array([0.0, 1.0, -1.0, 89.0, -88.0, 1e-8], np.float32))
+    assert sp[0] == 1.0 and sp[3] == np.inf and sp[4] == 0.0 and sp[5] == 1.0
+    assert abs(sp[1] - np.e) <= 2.5e-7 * np.e and abs(sp[2] - 1 / np.e) <= 2.5e-7 / np.e
+
+
+def test_combine_f32_against_double(ora):
+    g = rng(32)
+    f = g.standard_normal((7, 4, 64)).astype(np.float32)
+    w = g.random((7, 4)).astype(np.float32)
+    ys = g.standard_normal((7, 64)).astype(np.float32)
+    ref = np.einsum("tj,tjd->td", w.astype(np.float64), f.astype(np.float64)) + ys
+    got = ora.combine_f32(f, w, ys)
+    assert np.abs(got - ref).max() < 1e-5
+    assert np.array_equal(ora.combine_f32(f, w, None) + ys, got) or np.abs(
+        ora.combine_f32(f, w, None) + ys - got).max() == 0
 
 
 def test_combine_closed_form(ora):
