@@ -40,6 +40,7 @@ def parse():
     ap.add_argument("--instances", type=int, default=0,
                     help="distinct weight sets rotated across steps (0: enough to exceed the 256 MB MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="issue the calls eagerly instead of replaying graphs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
     return ap.parse_args()
 
@@ -109,7 +110,7 @@ def main():
     xs = [torch.from_numpy(wl.tokens(w, step=s)).to(dev) for s in range(n_inputs)]
     nxt = torch.empty((T, w.d), dtype=torch.float32, device=dev)
 
-    def step(s: int):
+    def eager_step(s: int):
         if decode:
             cur = xs[s % n_inputs]
             for L in layers:
@@ -118,6 +119,47 @@ def main():
                 cur = nxt
         else:
             layers[s % n_inst].forward(xs[0])
+
+    # The step is replayed from HIP graphs (one per weight set; for the decode
+    # stack one graph for all layers): launches are recorded once.  The decode
+    # input is copied into the graph's static input buffer before each replay.
+    graphs = []
+    if args.eager:
+        step = eager_step
+    else:
+        if decode:
+            xin = torch.empty((T, w.d), dtype=torch.float32, device=dev)
+            for L in layers:
+                L.buffers(T)
+            warm = torch.cuda.Stream(device=dev)
+            warm.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(warm):
+                xin.copy_(xs[0])
+            torch.cuda.current_stream().wait_stream(warm)
+
+            def stack(src):
+                cur = src
+                for L in layers:
+                    y = L.forward(cur)
+                    B.rmsnorm_f32(T, w.d, 1e-5, y, nxt)
+                    cur = nxt
+
+            stack(xin)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                stack(xin)
+            graphs.append(g)
+
+            def step(s: int):
+                xin.copy_(xs[s % n_inputs])
+                graphs[0].replay()
+        else:
+            for L in layers:
+                graphs.append(L.capture(xs[0]))
+
+            def step(s: int):
+                graphs[s % n_inst].replay()
 
     for s in range(args.warmup):
         step(s)

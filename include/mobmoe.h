@@ -159,7 +159,7 @@ mm_status mm_convert_bf16(int64_t n, const float* x, uint16_t* y, void* stream);
 /* ------------------------------------------------------- the seven calls */
 
 /*
- * S1+S2.  FP32 router, top-k selection and gate weights (the section
+ * FP32 router, top-k selection and gate weights (the section
  * "Pre-training" keeps the router in FP32; eq. (*) weights each selected
  * expert by router_i(x)).
  *   x          device FP32 [T][d]
@@ -178,7 +178,7 @@ mm_status mm_router_topk(const mm_layer_desc* desc, int64_t T, const float* x,
                          float* topk_w, void* stream);
 
 /*
- * S3.  Stable count sort of the T*k (token, slot) assignments by expert id
+ * Stable count sort of the T*k (token, slot) assignments by expert id
  * (section "Custom MoE kernel": tokens of one expert become contiguous).
  *   topk_idx        device int32 [T*k]
  *   expert_offsets  device int32 [E+1]  out: start of each expert's run,
@@ -195,7 +195,7 @@ mm_status mm_route_permute(const mm_layer_desc* desc, int64_t T, const int32_t* 
                            size_t ws_bytes, void* stream);
 
 /*
- * S4.  Per-row dynamic INT8 quantisation (eq. (6) read with b = 8 and one
+ * Per-row dynamic INT8 quantisation (eq. (6) read with b = 8 and one
  * group per row): s = (2 * max|v|) / 255, q = clamp(round_half_even(v / s),
  * -128, 127), FP32 with IEEE division; an all-zero row has s = 0, q = 0.
  *   x      device FP32 [rows][cols]
@@ -206,7 +206,7 @@ mm_status mm_act_quant_i8(int64_t rows, int64_t cols, const float* x, int8_t* q,
                           void* stream);
 
 /*
- * S5.  Routed experts' fused gate/up product with SwiGLU (section "Custom MoE
+ * Routed experts' fused gate/up product with SwiGLU (section "Custom MoE
  * kernel"), for every sorted position p of every expert e:
  *   g = x[t] W_gate[e]^T, u = x[t] W_up[e]^T, a = SiLU(g) * u, t = perm[p]/k.
  * MM_W_INT4G32:  act is x_q (int8 [T][d]) with act_scale (FP32 [T]); each
@@ -225,7 +225,7 @@ mm_status mm_expert_gateup_swiglu(const mm_layer_desc* desc, int64_t T, const vo
                                   float* h_scale, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * S6.  Routed experts' down product: f[p] = h[p] W_down[e]^T for every sorted
+ * Routed experts' down product: f[p] = h[p] W_down[e]^T for every sorted
  * position p of expert e, FP32 [T*k][d] in sorted order (gate weight not yet
  * applied).  INT4: h int8 with h_scale, exact int32 group sums then FP32
  * scales.  F32 / BF16: h as written by mm_expert_gateup_swiglu, h_scale NULL.
@@ -236,7 +236,7 @@ mm_status mm_expert_down(const mm_layer_desc* desc, int64_t T, const void* h,
                          float* f, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * S7.  The always-on shared expert (section "Divide-and-conquer architecture
+ * The always-on shared expert (section "Divide-and-conquer architecture
  * search", Finding 3): a dense SwiGLU FFN of hidden h_s on every token with
  * weight 1, using the same activation input and arithmetic as the routed
  * experts: ys [T][d] FP32.  w_gateup [2h_s][d], w_down [d][h_s].
@@ -248,7 +248,7 @@ mm_status mm_shared_expert(const mm_layer_desc* desc, int64_t T, const void* act
                            float* ys, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * S8.  Weighted combine through the inverse permutation (section "Custom MoE
+ * Weighted combine through the inverse permutation (section "Custom MoE
  * kernel"): y[t][c] = fma-chain over j = 0..k-1 of topk_w[t][j] *
  * f[inv_perm[t*k+j]][c], then + ys[t][c] (ys may be NULL).  No atomics.
  *   y  device [T][d], FP32 (MM_OUT_F32) or BF16 (MM_OUT_BF16)

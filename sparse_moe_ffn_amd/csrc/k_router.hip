@@ -14,63 +14,86 @@
 namespace mm {
 namespace {
 
-constexpr int kMaxX = 32;   // d <= 2048 keeps the token rows in registers
 constexpr int kTok = 4;     // tokens per workgroup (one per wave for the top-k)
+constexpr int kRowStride = 65;  // LDS stride of one row of 64 lane partials (padded)
 
-// Workgroup = 4 waves and 4 tokens.  Phase 1: wave w computes the logits of
-// experts w, w+4, w+8, ... for all 4 tokens (the expert's weight row is loaded
-// once per wave and reused for the 4 tokens) into LDS.  Phase 2: wave w takes
-// token w, lane e holding the logit of expert e, and does the top-k and the
-// gate weights.
-template <int kGating>
+// Workgroup = 4 waves and 4 tokens.  Phase 1: wave w takes experts w, w+4,
+// w+8, ... (at most 16); for each one, lane l forms the 4 tokens' partial sums
+// over columns j = l, l+64, ... (fused multiply-adds, ascending j) and stores
+// them to LDS.  Phase 2: lane r of the wave adds the 64 partials of row r
+// (one (token, expert) pair) as the balanced tree, adds the bias and writes
+// the logit.  Phase 3: wave w takes token w, lane e holding the logit of
+// expert e, and does the top-k and the gate weights.
+// kNX = d / 64 (0: any d, row read from memory in the loop).
+template <int kGating, int kNX>
 __global__ __launch_bounds__(256) void k_router(int64_t T, int d, int E, int k,
                                                 const float* __restrict__ x,
                                                 const float* __restrict__ wr,
                                                 const float* __restrict__ bias,
                                                 int32_t* __restrict__ idx,
                                                 float* __restrict__ w) {
+  __shared__ float s_part[4][16 * kTok][kRowStride];
   __shared__ float s_logit[kTok][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t t0 = (int64_t)blockIdx.x * kTok;
   const int nt = (int)min((int64_t)kTok, T - t0);
-  const int nx = d / kWave;
+  const int ne = (E - wave + 3) / 4;  // experts of this wave
 
-  if (nx <= kMaxX) {
-    float xv[kTok][kMaxX];
+  if constexpr (kNX > 0) {
+    float xv[kTok][kNX];
 #pragma unroll
     for (int q = 0; q < kTok; ++q)
 #pragma unroll
-      for (int i = 0; i < kMaxX; ++i)
-        if (i < nx) xv[q][i] = q < nt ? x[(t0 + q) * d + lane + kWave * i] : 0.0f;
-    for (int e = wave; e < E; e += 4) {
-      const float* we = wr + (int64_t)e * d;
-      float wv[kMaxX];
+      for (int i = 0; i < kNX; ++i) xv[q][i] = q < nt ? x[(t0 + q) * d + lane + kWave * i] : 0.0f;
+    // expert rows read one ahead (two register sets in ping-pong)
+    float wa[kNX], wb[kNX];
+    auto load_row = [&](int i, float (&wv)[kNX]) {
+      const float* we = wr + (int64_t)min(wave + 4 * i, E - 1) * d;
 #pragma unroll
-      for (int i = 0; i < kMaxX; ++i)
-        if (i < nx) wv[i] = we[lane + kWave * i];
-      const float b = bias ? bias[e] : 0.0f;
+      for (int c = 0; c < kNX; ++c) wv[c] = we[lane + kWave * c];
+    };
+    auto partials = [&](int i, const float (&wv)[kNX]) {
 #pragma unroll
       for (int q = 0; q < kTok; ++q) {
         float p = 0.0f;
 #pragma unroll
-        for (int i = 0; i < kMaxX; ++i)
-          if (i < nx) p = __builtin_fmaf(xv[q][i], wv[i], p);
-        p = tree_sum64(p);
-        if (lane == 0) s_logit[q][e] = p + b;
+        for (int c = 0; c < kNX; ++c) p = __builtin_fmaf(xv[q][c], wv[c], p);
+        s_part[wave][i * kTok + q][lane] = p;
       }
+    };
+    load_row(0, wa);
+    for (int i = 0; i < ne; i += 2) {
+      load_row(i + 1, wb);
+      partials(i, wa);
+      if (i + 1 >= ne) break;
+      load_row(i + 2, wa);
+      partials(i + 1, wb);
     }
   } else {
-    for (int e = wave; e < E; e += 4) {
-      const float* we = wr + (int64_t)e * d;
-      const float b = bias ? bias[e] : 0.0f;
+    for (int i = 0; i < ne; ++i) {
+      const float* we = wr + (int64_t)(wave + 4 * i) * d;
       for (int q = 0; q < kTok; ++q) {
         float p = 0.0f;
         if (q < nt)
           for (int j = lane; j < d; j += kWave) p = __builtin_fmaf(x[(t0 + q) * d + j], we[j], p);
-        p = tree_sum64(p);
-        if (lane == 0) s_logit[q][e] = p + b;
+        s_part[wave][i * kTok + q][lane] = p;
       }
     }
+  }
+  __syncthreads();
+  // Phase 2: lane r reduces row r = (expert slot i, token q) of its wave.
+  if (lane < ne * kTok) {
+    const float* row = s_part[wave][lane];
+    float p[64];
+#pragma unroll
+    for (int l = 0; l < 64; ++l) p[l] = row[l];
+#pragma unroll
+    for (int s2 = 1; s2 < 64; s2 <<= 1)
+#pragma unroll
+      for (int l = 0; l < 64; l += 2 * s2) p[l] = p[l] + p[l + s2];
+    const int i = lane / kTok, q = lane % kTok;
+    const int e = wave + 4 * i;
+    s_logit[q][e] = p[0] + (bias ? bias[e] : 0.0f);
   }
   __syncthreads();
   if (wave >= nt) return;
@@ -117,11 +140,26 @@ __global__ __launch_bounds__(256) void k_router(int64_t T, int d, int E, int k,
 hipError_t launch_router(int64_t T, int d, int E, int k, int gating, const float* x,
                          const float* wr, const float* bias, int32_t* idx, float* w,
                          hipStream_t st) {
-  const unsigned blocks = (unsigned)((T + kTok - 1) / kTok);
-  if (gating == 0)
-    hipLaunchKernelGGL(k_router<0>, dim3(blocks), dim3(256), 0, st, T, d, E, k, x, wr, bias, idx, w);
-  else
-    hipLaunchKernelGGL(k_router<1>, dim3(blocks), dim3(256), 0, st, T, d, E, k, x, wr, bias, idx, w);
+  const dim3 grid((unsigned)((T + kTok - 1) / kTok)), block(256);
+#define MM_ROUTER(G, NX) hipLaunchKernelGGL((k_router<G, NX>), grid, block, 0, st, T, d, E, k, x, wr, bias, idx, w)
+#define MM_ROUTER_NX(G)                 \
+  switch (d / kWave) {                  \
+    case 4: MM_ROUTER(G, 4); break;     \
+    case 8: MM_ROUTER(G, 8); break;     \
+    case 12: MM_ROUTER(G, 12); break;   \
+    case 16: MM_ROUTER(G, 16); break;   \
+    case 20: MM_ROUTER(G, 20); break;   \
+    case 24: MM_ROUTER(G, 24); break;   \
+    case 32: MM_ROUTER(G, 32); break;   \
+    default: MM_ROUTER(G, 0); break;    \
+  }
+  if (gating == 0) {
+    MM_ROUTER_NX(0)
+  } else {
+    MM_ROUTER_NX(1)
+  }
+#undef MM_ROUTER_NX
+#undef MM_ROUTER
   return hipGetLastError();
 }
 

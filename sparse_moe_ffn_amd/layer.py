@@ -1,5 +1,7 @@
 """A MoE-FFN layer object on top of the C ABI: owns the device weights and the
-per-call buffers, and issues the seven calls in order on the current stream.
+per-call buffers, and issues the seven calls on the current stream (the
+shared expert, which depends only on the quantised input, on a second stream
+joined before the combine).
 
 Weight preparation runs on the device through the library (eq. (6)
 quantisation with mm_quantize_int4g32, then mm_prepack_int4g32; or BF16
@@ -144,6 +146,23 @@ class MoELayer:
 
     def combine(self, T):
         B.combine(self.desc, T, self.f, self.inv, self.topw, self.ys, self.y)
+
+    def capture(self, x: torch.Tensor) -> "torch.cuda.CUDAGraph":
+        """Records forward(x) for the static input buffer x into a HIP graph;
+        replaying it recomputes y from whatever x holds at replay time.  The
+        library allocates nothing and records no memset, so the graph holds
+        only kernel nodes (and the shared-expert stream fork/join)."""
+        T = x.shape[0]
+        self.buffers(T)
+        warm = torch.cuda.Stream(device=self.device)
+        warm.wait_stream(torch.cuda.current_stream(self.device))
+        with torch.cuda.stream(warm):
+            self.forward(x)
+        torch.cuda.current_stream(self.device).wait_stream(warm)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.forward(x)
+        return g
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         """y = eq. (*) of x [T, d] FP32 (device).  Returns the layer's y buffer."""

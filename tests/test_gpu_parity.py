@@ -294,3 +294,31 @@ def test_decode_stack_teacher_forced(B_):
         B.rmsnorm_f32(B_, w.d, 1e-5, y, nxt)
         assert row_rel_err(np_(nxt), oracle.rmsnorm(np_(y), 1e-5)) < 1e-5
         cur = nxt
+
+
+# ------------------------------------------------------------ graph replay
+def test_graph_replay_matches_eager():
+    """The layer captured in a HIP graph (kernel nodes and the shared-expert
+    stream fork/join only) gives the eager result on every replay, with other
+    eager work and synchronisations between replays."""
+    w = wl.WORKLOADS["s_prefill"].with_(T=300)
+    lw = wl.layer_weights(w)
+    x = dev(wl.tokens(w))
+    layer = make_layer(w, lw)
+    y_ref = np_(layer.forward(x)).copy()
+    g = layer.capture(x)
+    other = make_layer(w.with_(T=77), wl.layer_weights(w, layer=1))
+    x2 = dev(wl.tokens(w, step=1, T=77))
+    for i in range(3):
+        layer.y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(np_(layer.y), y_ref), f"replay {i}"
+        other.forward(x2)
+        torch.cuda.synchronize()
+    # the graph reads x at replay time
+    x.copy_(dev(wl.tokens(w, step=5)))
+    g.replay()
+    y5 = np_(layer.y).copy()
+    ref5 = oracle_forward(w, lw, wl.tokens(w, step=5))
+    assert np.array_equal(y5, ref5.y.astype(np.float32))
