@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="issue the calls eagerly instead of replaying graphs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (5 launches) and exit: the "
+                         "reference for scaling HBM counters")
     return ap.parse_args()
 
 
@@ -60,6 +63,51 @@ def layer_work(w, T, counts=None):
     return ops, B_r, B_s
 
 
+# Kernel chosen by the library for the routed expert products (mirrors the
+# dispatch in csrc/api.hip: weight-streaming up to 512 routed rows when the
+# reduction length fits, matrix cores from 256 rows when K % 128 == 0).
+def kernel_of(w, T, gateup: bool):
+    rows, K = T * w.k, (w.d if gateup else w.h)
+    if w.wfmt != "int4g32":
+        return ("k_gateup_fp" if gateup else "k_down_fp"), "row-tile"
+    if rows <= 512 and K % 64 == 0 and K <= 2560:
+        return ("k_gemv_i4<gate/up, routed>" if gateup else "k_gemv_i4<down, routed>"), "weight-streaming"
+    if rows >= 256 and K % 128 == 0:
+        return ("k_w4a8<2,2,gate/up, routed>" if gateup else "k_w4a8<2,2,down, routed>"), "matrix-core"
+    return ("k_gateup_i4" if gateup else "k_down_i4"), "row-tile"
+
+
+KERNEL_SOURCES = ["sparse_moe_ffn_amd/csrc/k_mfma.hip", "sparse_moe_ffn_amd/csrc/k_gemv.hip",
+                  "sparse_moe_ffn_amd/csrc/common.h", "sparse_moe_ffn_amd/csrc/launch.h"]
+
+
+def kernel_source_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 counter summary (profiles/traffic.md), or None when there is
+    none or the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.md")
+    if not os.path.exists(path):
+        return None
+    sha = kernel_source_sha()
+    for line in open(path):
+        if not line.startswith("traffic:"):
+            continue
+        kv = dict(p.split("=", 1) for p in line[len("traffic:"):].split() if "=" in p)
+        if kv.get("workload") == workload and kv.get("kernel") == kernel.replace(" ", "") \
+                and kv.get("source_sha256") == sha:
+            return float(kv["bytes_per_launch"])
+    return None
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -75,9 +123,18 @@ def main():
     from sparse_moe_ffn_amd import workloads as wl
     from sparse_moe_ffn_amd.layer import MoELayer
 
-    B.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones((n // 4,), dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
+        return
+    B.load()
     w = wl.WORKLOADS[args.workload]
     if args.batch is not None:
         w = w.with_(T=args.batch)
@@ -175,64 +232,89 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     tok_s = T / (ms / 1e3)
 
-    # ---- per-call durations with HIP events on the launch stream
-    calls = ["router", "route", "act_quant", "gateup", "down", "shared", "combine"]
+    # ---- per-call durations: each call is recorded REPS times into a HIP
+    # graph of its own and replayed between two HIP events on the stream it
+    # runs on, so the figure is the kernel time (plus the graph's dispatch
+    # gap), not host launch overhead.  Every call except the shared expert
+    # (gate/up then down) is a single kernel.
+    calls = ["router", "route", "act_quant", "gateup", "gateup_gemm", "down", "shared", "combine"]
     if w.wfmt != "int4g32":
         calls.remove("act_quant")
+        calls.remove("gateup_gemm")
+    abuf = torch.empty((T * w.k, w.h), dtype=torch.float32, device=dev)
     if not w.hs:
         calls.remove("shared")
-    n_time = max(5, min(args.steps, 20))
-    acc = {c: 0.0 for c in calls}
+    # The repetitions cycle through the distinct weight sets (as the step does).
     x0 = xs[0]
-    for s in range(n_time):
-        L = layers[s % len(layers)]
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
-        ev[0].record(st)
-        for i, c in enumerate(calls):
-            if c == "router":
-                L.router(x0, T)
-            elif c == "route":
-                L.route(T)
-            elif c == "act_quant":
-                L.act_quant(x0, T)
-            elif c == "gateup":
-                L.gateup(x0, T)
-            elif c == "down":
-                L.down(T)
-            elif c == "shared":
-                L.shared(x0, T)
-            elif c == "combine":
-                L.combine(T)
-            ev[i + 1].record(st)
-        ev[-1].synchronize()
-        for i, c in enumerate(calls):
-            acc[c] += ev[i].elapsed_time(ev[i + 1])
-    per_call_us = {c: 1e3 * v / n_time for c, v in acc.items()}
+    for L in layers:
+        L.forward(x0)  # routing state for the expert calls
+    torch.cuda.synchronize()
+    REPS, REPLAYS = 10, 5
+
+    def issue(c, L):
+        if c == "router":
+            L.router(x0, T)
+        elif c == "route":
+            L.route(T)
+        elif c == "act_quant":
+            L.act_quant(x0, T)
+        elif c == "gateup":
+            L.gateup(x0, T)
+        elif c == "gateup_gemm":
+            L.gateup_f32(x0, T, abuf)
+        elif c == "down":
+            L.down(T)
+        elif c == "shared":
+            L.shared(x0, T)
+        elif c == "combine":
+            L.combine(T)
+
+    per_call_us = {}
+    for c in calls:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in range(REPS):
+                issue(c, layers[r % len(layers)])
+        g.replay()
+        torch.cuda.synchronize()
+        e0c, e1c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0c.record(st)
+        for _ in range(REPLAYS):
+            g.replay()
+        e1c.record(st)
+        e1c.synchronize()
+        per_call_us[c] = 1e3 * e0c.elapsed_time(e1c) / (REPS * REPLAYS)
+        del g
+    torch.cuda.synchronize()
 
     ops, B_r, B_s = layer_work(w, T)
-    # decode: bytes of the selected experts' weights (distinct experts counted
-    # from the ids of the last step) + shared + router + activations
     L0 = layers[0]
     n_distinct = int(np.unique(L0.idx.cpu().numpy()).size)
+    # Roofline of the dominant single kernel: the routed gate/up product
+    # (timed on its own through the FP32-output form of the gate/up call, the
+    # same kernel the step runs before its row quantiser) or the routed down
+    # product, whichever takes longer.
+    gu_key = "gateup_gemm" if "gateup_gemm" in per_call_us else "gateup"
+    dom = gu_key if per_call_us[gu_key] >= per_call_us["down"] else "down"
+    dom_ops = ops["gateup"] if dom == gu_key else ops["down"]
+    kind, path = kernel_of(w, T, dom != "down")
     if decode:
-        dom = max(("gateup", "down", "shared"), key=lambda c: per_call_us.get(c, 0.0))
-        by_call = {
-            "gateup": n_distinct * (2 * w.h * w.d) * wb,
-            "down": n_distinct * (w.d * w.h) * wb,
-            "shared": B_s,
-        }
-        achieved = by_call[dom] / (per_call_us[dom] * 1e-6) / 1e9
-        roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None,
-                "algorithmic_bytes_per_launch": by_call[dom], "launch_us": round(per_call_us[dom], 3)}
+        # bytes the kernel must stream: packed weights + scales of the experts
+        # selected in the step (distinct ids), counted once
+        nbytes = n_distinct * ((2 * w.h * w.d) if dom != "down" else (w.d * w.h)) * wb
+        achieved = nbytes / (per_call_us[dom] * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
+                "traffic": stored_traffic(w.name, kind), "kernel": kind, "path": path,
+                "algorithmic_bytes_per_launch": nbytes, "launch_us": round(per_call_us[dom], 3)}
     else:
-        dom = max(("gateup", "down", "shared"), key=lambda c: per_call_us.get(c, 0.0))
         peak = INT8_MFMA_PEAK_TOPS if w.wfmt == "int4g32" else (
             BF16_MFMA_PEAK_TFLOPS if w.wfmt == "bf16" else FP32_VALU_PEAK_TFLOPS)
-        achieved = ops[dom] / (per_call_us[dom] * 1e-6) / 1e12
-        roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 3), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 5), "traffic": None,
-                "algorithmic_ops_per_launch": ops[dom], "launch_us": round(per_call_us[dom], 3)}
+        achieved = dom_ops / (per_call_us[dom] * 1e-6) / 1e12
+        roof = {"bound": "mfma" if w.wfmt != "f32" else "alu", "achieved": round(achieved, 3),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 5),
+                "traffic": stored_traffic(w.name, kind), "kernel": kind, "path": path,
+                "algorithmic_ops_per_launch": dom_ops, "launch_us": round(per_call_us[dom], 3)}
 
     # ---- CPU oracle on a bounded sample of the same workload
     cpu = None

@@ -122,7 +122,9 @@ const char* mm_status_string(mm_status s);
 const char* mm_last_error_string(void);
 
 /* Bytes of caller workspace the named call needs for T tokens (0 if none).
- * Returns 0 for an invalid descriptor. */
+ * Returns 0 for an invalid descriptor.  Workspace holds no state between
+ * calls; calls that share a workspace buffer must not overlap in time (same
+ * stream, or synchronised). */
 size_t mm_workspace_bytes(const mm_layer_desc* desc, int64_t T, int32_t which);
 
 /*
@@ -212,7 +214,9 @@ mm_status mm_act_quant_i8(int64_t rows, int64_t cols, const float* x, int8_t* q,
  * MM_W_INT4G32:  act is x_q (int8 [T][d]) with act_scale (FP32 [T]); each
  *   output is s_x * sum_g s_w[g] * isum_g with exact int32 group sums; the row
  *   a is re-quantised per row like mm_act_quant_i8 into h (int8 [T*k][h],
- *   sorted order) and h_scale (FP32 [T*k]).
+ *   sorted order) and h_scale (FP32 [T*k]).  With h_scale NULL the FP32 rows
+ *   a themselves are written to h (FP32 [T*k][h], sorted order) and ws may
+ *   be NULL: for callers that apply their own re-quantisation.
  * MM_W_F32 / MM_W_BF16: act is x (FP32 [T][d]), act_scale and h_scale NULL;
  *   h is FP32 (MM_W_F32) or BF16 (MM_W_BF16) [T*k][h], sorted order.
  *   w_gateup        stacked [E][2h][d] (see mm_weight)

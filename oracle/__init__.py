@@ -135,8 +135,9 @@ def linear_w4a8(aq, sa, wq, ws, want_isum: bool = False):
     return (out, isum) if want_isum else out
 
 
-def ffn_w4a8(xq, sx, wgu_q, wgu_s, wd_q, wd_s, want_isum: bool = False):
-    """SwiGLU expert on INT8 rows -> (hq, hs, f[, isum_gu, isum_d])."""
+def ffn_w4a8(xq, sx, wgu_q, wgu_s, wd_q, wd_s, want_isum: bool = False, want_a: bool = False):
+    """SwiGLU expert on INT8 rows -> (hq, hs, f[, isum_gu, isum_d][, a]); a is
+    the FP32 hidden row SiLU(g) * u before its re-quantisation."""
     xq, wgu_q, wd_q = _i8(xq), _i8(wgu_q), _i8(wd_q)
     sx, wgu_s, wd_s = _f32(sx), _f32(wgu_s), _f32(wd_s)
     rows, d = xq.shape
@@ -146,9 +147,11 @@ def ffn_w4a8(xq, sx, wgu_q, wgu_s, wd_q, wd_s, want_isum: bool = False):
     f = np.empty((rows, d), np.float32)
     igu = np.empty((rows, 2 * h, d // 32), np.int32) if want_isum else None
     idn = np.empty((rows, d, h // 32), np.int32) if want_isum else None
+    a = np.empty((rows, h), np.float32) if want_a else None
     _load().ora_ffn_w4a8(_i64(rows), d, h, _p(xq), _p(sx), _p(wgu_q), _p(wgu_s), _p(wd_q),
-                         _p(wd_s), _p(hq), _p(hs), _p(f), _p(igu), _p(idn))
-    return (hq, hs, f, igu, idn) if want_isum else (hq, hs, f)
+                         _p(wd_s), _p(hq), _p(hs), _p(f), _p(igu), _p(idn), _p(a))
+    out = (hq, hs, f) + ((igu, idn) if want_isum else ())
+    return out + (a,) if want_a else out
 
 
 def ffn_float(x, wgu, wd, bf16: bool = False):

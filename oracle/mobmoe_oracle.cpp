@@ -308,11 +308,13 @@ int ora_linear_w4a8(int64_t rows, int N, int K, const int8_t* aq, const float* s
 static void ffn_w4a8_row(int d, int h, const int8_t* xq, float sx, const int8_t* wgu_q,
                          const float* wgu_s, const int8_t* wd_q, const float* wd_s,
                          int8_t* hq, float* hs, float* f, int32_t* isum_gu,
-                         int32_t* isum_d) {
+                         int32_t* isum_d, float* a_out) {
   std::vector<float> gu(2 * h);
   linear_w4a8_row(2 * h, d, xq, sx, wgu_q, wgu_s, gu.data(), isum_gu);
   std::vector<float> a(h);
   for (int o = 0; o < h; ++o) a[o] = silu32(gu[o]) * gu[h + o];
+  if (a_out)
+    for (int o = 0; o < h; ++o) a_out[o] = a[o];
   ora_quant_act_i8(1, h, a.data(), hq, hs);
   linear_w4a8_row(d, h, hq, *hs, wd_q, wd_s, f, isum_d);
 }
@@ -320,12 +322,13 @@ static void ffn_w4a8_row(int d, int h, const int8_t* xq, float sx, const int8_t*
 int ora_ffn_w4a8(int64_t rows, int d, int h, const int8_t* xq, const float* sx,
                  const int8_t* wgu_q, const float* wgu_s, const int8_t* wd_q,
                  const float* wd_s, int8_t* hq, float* hs, float* f, int32_t* isum_gu,
-                 int32_t* isum_d) {
+                 int32_t* isum_d, float* a_out) {
   if (d % kGroup || h % kGroup) return -1;
   for (int64_t r = 0; r < rows; ++r)
     ffn_w4a8_row(d, h, xq + r * d, sx[r], wgu_q, wgu_s, wd_q, wd_s, hq + r * h, hs + r,
                  f + r * d, isum_gu ? isum_gu + r * (int64_t)2 * h * (d / kGroup) : nullptr,
-                 isum_d ? isum_d + r * (int64_t)d * (h / kGroup) : nullptr);
+                 isum_d ? isum_d + r * (int64_t)d * (h / kGroup) : nullptr,
+                 a_out ? a_out + r * (int64_t)h : nullptr);
   return 0;
 }
 
@@ -488,7 +491,7 @@ int ora_forward(int d, int E, int h, int hs, int k, int wfmt, int gating, int64_
         ffn_w4a8_row(d, h, xq.data() + t * d, sx[t], gu_q.data() + e * gu_q_stride,
                      gu_s.data() + e * gu_s_stride, d_q.data() + e * d_q_stride,
                      d_s.data() + e * d_s_stride, hq.data(), &hsc,
-                     f32.data() + (t * k + j) * d, nullptr, nullptr);
+                     f32.data() + (t * k + j) * d, nullptr, nullptr, nullptr);
         if (out->hq) std::copy(hq.begin(), hq.end(), out->hq + (t * k + j) * h);
         if (out->hs) out->hs[t * k + j] = hsc;
       } else {
@@ -502,7 +505,7 @@ int ora_forward(int d, int E, int h, int hs, int k, int wfmt, int gating, int64_
         float hsc = 0.0f;
         ffn_w4a8_row(d, hs, xq.data() + t * d, sx[t], sgu_q.data(), sgu_s.data(),
                      sd_q.data(), sd_s.data(), hq.data(), &hsc, ys32.data() + t * d, nullptr,
-                     nullptr);
+                     nullptr, nullptr);
         if (out->hq_s) std::copy(hq.begin(), hq.end(), out->hq_s + t * hs);
         if (out->hs_s) out->hs_s[t] = hsc;
       } else {

@@ -132,23 +132,39 @@ mm_status check_weight(const mm_layer_desc* d, const mm_weight& w, const char* n
 
 hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
-// INT4 gate/up + SwiGLU + per-row re-quantisation: matrix-core GEMM then the
-// row quantiser for larger row counts, the fused row-tile kernel otherwise.
+// INT4 products.  Few rows per expert: the weight-streaming kernels (decode).
+// Otherwise the matrix-core kernels.  The gate/up of both writes the FP32
+// hidden rows to abuf, then the row quantiser produces hq / hs.  Shapes
+// neither supports go to the row-tile kernels, whose gate/up quantises in
+// place.
+bool use_gemv(const mm::ExpertArgs& a, int K, bool gateup) {
+  const int64_t lim = a.offsets ? mm::kGemvMaxRowsRouted : mm::kGemvMaxRowsDense;
+  return a.rows <= lim && mm::gemv_i4_fits(K, gateup);
+}
+
+bool use_mfma(const mm::ExpertArgs& a, int K) {
+  return a.rows >= mm::kMfmaMinRows && K % mm::kMfmaK == 0;
+}
+
+// hq == nullptr: the FP32 rows in abuf are the output (no re-quantisation).
 hipError_t gateup_i4(const mm::ExpertArgs& a, const int8_t* xq, const float* sx,
                      const uint8_t* wq, const float* ws, float* abuf, int8_t* hq, float* hs,
                      int32_t* isum, hipStream_t st) {
-  if (a.rows >= mm::kMfmaMinRows && a.d % mm::kMfmaK == 0) {
-    hipError_t e = mm::launch_gateup_i4_mfma(a, xq, sx, wq, ws, abuf, isum, st);
-    if (e != hipSuccess) return e;
-    return mm::launch_act_quant_i8(a.rows, a.h, abuf, hq, hs, st);
-  }
-  return mm::launch_gateup_i4(a, xq, sx, wq, ws, abuf, hq, hs, isum, st);
+  hipError_t e;
+  if (use_gemv(a, a.d, true))
+    e = mm::launch_gateup_i4_gemv(a, xq, sx, wq, ws, abuf, isum, st);
+  else if (use_mfma(a, a.d))
+    e = mm::launch_gateup_i4_mfma(a, xq, sx, wq, ws, abuf, isum, st);
+  else
+    return mm::launch_gateup_i4(a, xq, sx, wq, ws, abuf, hq, hs, isum, st);
+  if (e != hipSuccess || hq == nullptr) return e;
+  return mm::launch_act_quant_i8(a.rows, a.h, abuf, hq, hs, st);
 }
 
 hipError_t down_i4(const mm::ExpertArgs& a, const int8_t* hq, const float* hs,
                    const uint8_t* wq, const float* ws, float* f, int32_t* isum, hipStream_t st) {
-  if (a.rows >= mm::kMfmaMinRows && a.h % mm::kMfmaK == 0)
-    return mm::launch_down_i4_mfma(a, hq, hs, wq, ws, f, isum, st);
+  if (use_gemv(a, a.h, false)) return mm::launch_down_i4_gemv(a, hq, hs, wq, ws, f, isum, st);
+  if (use_mfma(a, a.h)) return mm::launch_down_i4_mfma(a, hq, hs, wq, ws, f, isum, st);
   return mm::launch_down_i4(a, hq, hs, wq, ws, f, isum, st);
 }
 
@@ -282,7 +298,11 @@ static mm_status gateup_impl(const mm_layer_desc* desc, int64_t T, const void* a
   hipStream_t st = S(stream);
   if (desc->wfmt == MM_W_INT4G32) {
     MM_REQUIRE(act_scale);
-    MM_REQUIRE(h_scale);
+    if (h_scale == nullptr)  // FP32 hidden rows straight into h
+      return hip_status(gateup_i4(a, static_cast<const int8_t*>(act), act_scale,
+                                  static_cast<const uint8_t*>(w.data), w.scales,
+                                  static_cast<float*>(h), nullptr, nullptr, isum, st),
+                        "mm_expert_gateup_swiglu");
     MM_REQUIRE(ws);
     if (ws_size < ws_bytes(desc, T, MM_WS_GATEUP))
       return fail(MM_ERR_WORKSPACE, "gate/up workspace too small (need %lld bytes)", (long long)ws_bytes(desc, T, MM_WS_GATEUP));

@@ -60,7 +60,8 @@ __device__ __forceinline__ int dot32(const uint32_t (&q)[8], const int* __restri
 constexpr int kRowsI4 = 16;
 constexpr int kRowsFp = 8;
 
-// INT4 gate/up + SwiGLU + per-row INT8 re-quantisation of the hidden row.
+// INT4 gate/up + SwiGLU + per-row INT8 re-quantisation of the hidden row
+// (skipped when hq is null: the FP32 rows in aout are then the output).
 // A rows (INT8) are staged in LDS; thread o computes gate o and up o for every
 // row of the tile and writes a = SiLU(g) * u (FP32) to the staging buffer
 // `abuf`; the block then reduces max|a| per row, and every thread quantises
@@ -131,6 +132,7 @@ __global__ __launch_bounds__(256) void k_gateup_i4(ExpertArgs a, const int8_t* _
         amax[r] = fmaxf(amax[r], fabsf(v));
       }
   }
+  if (hq == nullptr) return;  // FP32 rows only
   // per-row max|a| over the block (exact, order-free), then the row scale
   __shared__ float red[4][kRowsI4];
   __shared__ float srow[kRowsI4];

@@ -1,0 +1,254 @@
+// W4A8 products for a few rows per expert (decode batches): the weight
+// stream is the whole cost, so the work is spread over the weight matrix
+// rather than over the rows.
+//
+// MobileMoE close reading, sections "Custom MoE kernel" (per-expert product
+// over the expert's contiguous rows, fused gate/up with SwiGLU, then down)
+// and "Runtime latency" (decode is bound by the bytes of the selected
+// experts' weights).  INT4 weights per eq. (6) (section "Quantisation-aware
+// training"): output = s_act * sum_g s_w[g] * isum_g with exact int32 group
+// sums isum_g, applied as the FMA chain over g ascending -- the order of the
+// matrix-core and row-tile kernels and of the CPU oracle, so all agree bit for
+// bit.
+//
+// A workgroup owns one tile of up to kR rows of one expert and one 32-row
+// block of the weight matrix (for gate/up: the gate block and the matching up
+// block).  Its 4 waves split the quantisation groups.  Each lane reads 16
+// bytes of a pair of adjacent 512-byte chunks (groups g, g+1 of the block,
+// layout in common.h), so every wave load is one fully coalesced 1 KB access
+// and all of a workgroup's weight bytes are in flight before the first use.
+// The exact int32 group sums go to LDS; then one thread per (row, output)
+// applies the scales in group order.  Only experts that own rows have tiles,
+// so only the selected experts' weights are read.
+#include "common.h"
+#include "launch.h"
+
+namespace mm {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kMaxPairs = 10;  // group pairs per wave: K <= 2 * 32 * 4 * 10 = 2560
+
+// First row, row count and expert of tile `tile` (routed: expert-sorted rows,
+// tiles numbered expert by expert; dense: rows in order).  All threads call.
+template <int kR, bool kDense>
+__device__ void gemv_tile(const ExpertArgs& a, int tile, int& p0, int& n, int& e) {
+  __shared__ int s_p0, s_n, s_e;
+  if constexpr (kDense) {
+    p0 = tile * kR;
+    n = (int)min((int64_t)kR, a.rows - p0);
+    e = 0;
+    return;
+  }
+  if (threadIdx.x < 64) routed_tile(a.offsets, a.E, (int)a.rows, kR, tile, &s_p0, &s_n, &s_e);
+  __syncthreads();
+  p0 = s_p0;
+  n = s_n;
+  e = s_e;
+}
+
+// Partial group sums of one lane for one activation row: the lane holds 16
+// weights (x16) of each of rows rho and rho+1, for one half of a group.
+__device__ __forceinline__ void dot16x2(const uint4& w, const int4& x, int& p0, int& p1) {
+  uint32_t l0, h0, l1, h1, l2, h2, l3, h3;
+  unpack8(w.x, l0, h0);
+  unpack8(w.y, l1, h1);
+  unpack8(w.z, l2, h2);
+  unpack8(w.w, l3, h3);
+  int s = __builtin_amdgcn_sdot4((int)l0, x.x, 0, false);
+  s = __builtin_amdgcn_sdot4((int)h0, x.y, s, false);
+  s = __builtin_amdgcn_sdot4((int)l1, x.z, s, false);
+  p0 = __builtin_amdgcn_sdot4((int)h1, x.w, s, false);
+  s = __builtin_amdgcn_sdot4((int)l2, x.x, 0, false);
+  s = __builtin_amdgcn_sdot4((int)h2, x.y, s, false);
+  s = __builtin_amdgcn_sdot4((int)l3, x.z, s, false);
+  p1 = __builtin_amdgcn_sdot4((int)h3, x.w, s, false);
+}
+
+// out: gate/up -> a = SiLU(g * s) * (u * s) into out [rows][h];
+//      down    -> f = acc * s into out [rows][N].
+// K: reduction length (multiple of 64, <= 2560); RB: 32-row weight blocks per
+// output (gate/up: h / 32, down: N / 32).
+// kDense: rows are the tokens in order (shared expert); otherwise routed.
+template <int kR, bool kGateUp, bool kCapture, bool kDense>
+__global__ __launch_bounds__(256) void k_gemv_i4(ExpertArgs a, int K, int N, int RB,
+                                                 const int8_t* __restrict__ act,
+                                                 const float* __restrict__ act_scale,
+                                                 const uint8_t* __restrict__ wq,
+                                                 const float* __restrict__ wsc,
+                                                 float* __restrict__ out,
+                                                 int32_t* __restrict__ isum) {
+  constexpr int kM = kGateUp ? 2 : 1;  // weight blocks per workgroup
+  const int G = K / kGroup, GP = G / 2;
+  extern __shared__ int4 smem4[];
+  int32_t* s_is = reinterpret_cast<int32_t*>(smem4);              // [kM][kR][G][32]
+  float* s_sc = reinterpret_cast<float*>(s_is + kM * kR * G * 32);  // [kM][G][32]
+  int4* s_act = reinterpret_cast<int4*>(s_sc + kM * G * 32);        // [kR][K/16]
+  __shared__ int s_src[kR];
+  __shared__ float s_as[kR];
+
+  const int tile = (int)blockIdx.x / RB, rbo = (int)blockIdx.x % RB;
+  int p0, n, e;
+  gemv_tile<kR, kDense>(a, tile, p0, n, e);
+  if (n <= 0) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t wrows = kGateUp ? 2 * (int64_t)a.h : N;
+  int rbm[kM];
+  rbm[0] = rbo;
+  if (kGateUp) rbm[kM - 1] = rbo + a.h / 32;
+
+  // Weight loads first: pair i of this wave is groups 2*(wave + 4i) and +1.
+  // Pairs past the end re-read the last pair (valid address, never used).
+  const uint8_t* we = wq + (int64_t)e * (wrows / 32) * G * kChunkBytes;
+  uint4 wv[kMaxPairs][kM];
+#pragma unroll
+  for (int i = 0; i < kMaxPairs; ++i) {
+    const int gp = min(wave + kWaves * i, GP - 1);
+#pragma unroll
+    for (int m = 0; m < kM; ++m)
+      wv[i][m] = reinterpret_cast<const uint4*>(
+          we + ((int64_t)rbm[m] * G + 2 * gp) * kChunkBytes)[lane];
+  }
+
+  if (threadIdx.x < kR) {
+    const int r = threadIdx.x;
+    int src = -1;
+    float s = 0.0f;
+    if (r < n) {
+      src = p0 + r;
+      if (kGateUp && !kDense) {
+        src = a.perm[p0 + r] / a.k;
+        if ((unsigned)src >= (unsigned)a.T) src = 0;  // stays in bounds for a corrupt perm
+      }
+      s = act_scale[src];
+    }
+    s_src[r] = src;
+    s_as[r] = s;
+  }
+  // scales of the workgroup's blocks: G * 32 contiguous floats per block
+  const float* se = wsc + (int64_t)e * (wrows / 32) * G * 32;
+  for (int i = threadIdx.x; i < kM * G * 32; i += blockDim.x) {
+    const int m = i / (G * 32), j = i % (G * 32);
+    s_sc[i] = se[(int64_t)rbm[m] * G * 32 + j];
+  }
+  __syncthreads();  // s_src ready
+  const int c16 = K / 16;
+  for (int i = threadIdx.x; i < kR * c16; i += blockDim.x) {
+    const int r = i / c16, c = i % c16;
+    int4 v = make_int4(0, 0, 0, 0);
+    if (r < n) v = reinterpret_cast<const int4*>(act + (int64_t)s_src[r] * K)[c];
+    s_act[i] = v;
+  }
+  __syncthreads();  // activations and scales staged
+
+  // Lane geometry inside a pair: lanes 0..31 hold group 2gp, 32..63 group
+  // 2gp+1; within a group, lane l (= lane % 32) holds rows 2*(l % 16) and
+  // 2*(l % 16) + 1, columns 16 * (l / 16) .. +15.  Lanes l and l ^ 16 hold the
+  // two column halves of the same rows: each keeps one row and hands the
+  // other row's partial to its partner.
+  const int gsel = lane >> 5, half = (lane >> 4) & 1;
+  const int row = 2 * (lane & 15) + half;
+#pragma unroll
+  for (int i = 0; i < kMaxPairs; ++i) {
+    const int gp = wave + kWaves * i;
+    if (gp >= GP) break;
+    const int g = 2 * gp + gsel;
+#pragma unroll
+    for (int m = 0; m < kM; ++m) {
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        if (r >= n) break;
+        const int4 x = s_act[r * c16 + g * 2 + half];
+        int q0, q1;
+        dot16x2(wv[i][m], x, q0, q1);
+        const int send = half ? q0 : q1;
+        const int keep = half ? q1 : q0;
+        const int full = keep + __shfl_xor(send, 16);
+        s_is[((m * kR + r) * G + g) * 32 + row] = full;
+      }
+    }
+  }
+  __syncthreads();
+
+  // One thread per (row r, output column o of the block).
+  for (int t = threadIdx.x; t < n * 32; t += blockDim.x) {
+    const int r = t / 32, o = t % 32;
+    float acc[kM];
+#pragma unroll
+    for (int m = 0; m < kM; ++m) {
+      float ac = 0.0f;
+      const int32_t* is = s_is + (m * kR + r) * G * 32 + o;
+      const float* sc = s_sc + m * G * 32 + o;
+      for (int g = 0; g < G; ++g) ac = fmaf(sc[g * 32], (float)is[g * 32], ac);
+      acc[m] = ac;
+      if (kCapture) {
+        const int64_t col = (int64_t)rbm[m] * 32 + o;
+        for (int g = 0; g < G; ++g)
+          isum[((int64_t)(p0 + r) * wrows + col) * G + g] = is[g * 32] >> 4;
+      }
+    }
+    const float s = s_as[r];
+    if (kGateUp)
+      out[(int64_t)(p0 + r) * a.h + rbo * 32 + o] = silu(acc[0] * s) * (acc[kM - 1] * s);
+    else
+      out[(int64_t)(p0 + r) * N + rbo * 32 + o] = acc[0] * s;
+  }
+}
+
+constexpr int kRGemv = 4;
+
+size_t gemv_lds(int K, bool gateup) {
+  const int G = K / kGroup, m = gateup ? 2 : 1;
+  return (size_t)m * kRGemv * G * 32 * 4 + (size_t)m * G * 32 * 4 + (size_t)kRGemv * K;
+}
+
+unsigned gemv_tiles(const ExpertArgs& a) {
+  const int64_t base = (a.rows + kRGemv - 1) / kRGemv;
+  return (unsigned)(a.offsets ? base + a.E : base);
+}
+
+}  // namespace
+
+bool gemv_i4_fits(int K, bool gateup) {
+  return K % 64 == 0 && K <= 2 * kGroup * kWaves * kMaxPairs && gemv_lds(K, gateup) <= 65536;
+}
+
+hipError_t launch_gateup_i4_gemv(const ExpertArgs& a, const int8_t* xq, const float* sx,
+                                 const uint8_t* wq, const float* ws, float* a_buf, int32_t* isum,
+                                 hipStream_t st) {
+  const int RB = a.h / 32;
+  const dim3 grid(gemv_tiles(a) * RB);
+  const size_t lds = gemv_lds(a.d, true);
+  if (!a.offsets)
+    hipLaunchKernelGGL((k_gemv_i4<kRGemv, true, false, true>), grid, dim3(256), lds, st, a, a.d,
+                       2 * a.h, RB, xq, sx, wq, ws, a_buf, nullptr);
+  else if (isum)
+    hipLaunchKernelGGL((k_gemv_i4<kRGemv, true, true, false>), grid, dim3(256), lds, st, a, a.d, 2 * a.h,
+                       RB, xq, sx, wq, ws, a_buf, isum);
+  else
+    hipLaunchKernelGGL((k_gemv_i4<kRGemv, true, false, false>), grid, dim3(256), lds, st, a, a.d, 2 * a.h,
+                       RB, xq, sx, wq, ws, a_buf, isum);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_i4_gemv(const ExpertArgs& a, const int8_t* hq, const float* hs,
+                               const uint8_t* wq, const float* ws, float* f, int32_t* isum,
+                               hipStream_t st) {
+  ExpertArgs b = a;
+  b.perm = nullptr;
+  const int RB = a.d / 32;
+  const dim3 grid(gemv_tiles(b) * RB);
+  const size_t lds = gemv_lds(a.h, false);
+  if (!b.offsets)
+    hipLaunchKernelGGL((k_gemv_i4<kRGemv, false, false, true>), grid, dim3(256), lds, st, b, a.h,
+                       a.d, RB, hq, hs, wq, ws, f, nullptr);
+  else if (isum)
+    hipLaunchKernelGGL((k_gemv_i4<kRGemv, false, true, false>), grid, dim3(256), lds, st, b, a.h, a.d, RB,
+                       hq, hs, wq, ws, f, isum);
+  else
+    hipLaunchKernelGGL((k_gemv_i4<kRGemv, false, false, false>), grid, dim3(256), lds, st, b, a.h, a.d,
+                       RB, hq, hs, wq, ws, f, isum);
+  return hipGetLastError();
+}
+
+}  // namespace mm

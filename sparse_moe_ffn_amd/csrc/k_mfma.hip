@@ -39,21 +39,21 @@ constexpr int kStride16 = kKC / 16 + 1;  // LDS row stride in 16-byte units (pad
 constexpr int kXcd = 8;
 
 struct Tile {
-  int p0, n, e, split;
+  int p0, n, e, split, mt;
 };
 
 // Logical tile of this workgroup.  Tiles are numbered (expert, row tile,
 // column slice) with the slice fastest; workgroup b runs on XCD b % 8 and gets
 // logical id (b % 8) * per + b / 8, so each XCD works on a contiguous range of
 // tiles (same expert's weights in its L2).  Returns false if there is none.
-template <int kBM>
+template <int kBM, bool kDense>
 __device__ bool map_tile(const ExpertArgs& a, int nsplit, Tile& t) {
   __shared__ int s_p0, s_n, s_e, s_split;
   const int per = (int)gridDim.x / kXcd;
   const int logical = ((int)blockIdx.x % kXcd) * per + (int)blockIdx.x / kXcd;
   const int mt = logical / nsplit;
   if (threadIdx.x < 64) {
-    if (a.offsets == nullptr) {
+    if constexpr (kDense) {
       if (threadIdx.x == 0) {
         s_p0 = mt * kBM;
         s_n = max(0, min(kBM, (int)a.rows - s_p0));
@@ -69,6 +69,7 @@ __device__ bool map_tile(const ExpertArgs& a, int nsplit, Tile& t) {
   t.n = s_n;
   t.e = s_e;
   t.split = s_split;
+  t.mt = mt;
   return t.n > 0;
 }
 
@@ -193,7 +194,9 @@ __device__ __forceinline__ void compute_chunk(v16f (&acc)[kMT][kNT], const int4*
 // Otherwise: the wave's kNT tiles are consecutive output columns (slice =
 // 4 * kNT * 32 columns); output f = acc * s_row to out [rows][N].
 // kMT row tiles of 32 (kBM = 32 * kMT rows per workgroup).  K % 128 == 0.
-template <int kMT, int kNT, bool kGateUp, bool kCapture>
+// kDense: rows are the tokens in order (shared expert); otherwise routed
+// (expert-sorted rows, tiles found from the offsets).
+template <int kMT, int kNT, bool kGateUp, bool kCapture, bool kDense>
 __global__ __launch_bounds__(256) void k_w4a8(ExpertArgs a, int nsplit, int K, int N,
                                               const int8_t* __restrict__ act,
                                               const float* __restrict__ act_scale,
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(256) void k_w4a8(ExpertArgs a, int nsplit, int K, i
   __shared__ float s_scale[kBM];
   __shared__ int s_off[kBM];  // source row of each tile row in `act`, -1 for padding
   Tile t;
-  if (!map_tile<kBM>(a, nsplit, t)) return;
+  if (!map_tile<kBM, kDense>(a, nsplit, t)) return;
   const int G = K / kGroup;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = a.h;
@@ -218,7 +221,7 @@ __global__ __launch_bounds__(256) void k_w4a8(ExpertArgs a, int nsplit, int K, i
     float s = 0.0f;
     if (r < t.n) {
       int src = t.p0 + r;
-      if (kGateUp && a.perm) {
+      if (kGateUp && !kDense) {
         src = a.perm[t.p0 + r] / a.k;
         if ((unsigned)src >= (unsigned)a.T) src = 0;  // stays in bounds for a corrupt perm
       }
@@ -323,12 +326,15 @@ hipError_t launch_gateup_i4_mfma(const ExpertArgs& a, const int8_t* xq, const fl
                                  hipStream_t st) {
   const int nsplit = (a.h + 127) / 128;
   const dim3 grid(grid_for(a, 64, nsplit));
-  if (isum)
-    hipLaunchKernelGGL((k_w4a8<2, 2, true, true>), grid, dim3(256), 0, st, a, nsplit, a.d, 2 * a.h,
-                       xq, sx, wq, ws, a_buf, isum);
+  if (!a.offsets)
+    hipLaunchKernelGGL((k_w4a8<2, 2, true, false, true>), grid, dim3(256), 0, st, a, nsplit, a.d,
+                       2 * a.h, xq, sx, wq, ws, a_buf, nullptr);
+  else if (isum)
+    hipLaunchKernelGGL((k_w4a8<2, 2, true, true, false>), grid, dim3(256), 0, st, a, nsplit, a.d,
+                       2 * a.h, xq, sx, wq, ws, a_buf, isum);
   else
-    hipLaunchKernelGGL((k_w4a8<2, 2, true, false>), grid, dim3(256), 0, st, a, nsplit, a.d, 2 * a.h,
-                       xq, sx, wq, ws, a_buf, isum);
+    hipLaunchKernelGGL((k_w4a8<2, 2, true, false, false>), grid, dim3(256), 0, st, a, nsplit, a.d,
+                       2 * a.h, xq, sx, wq, ws, a_buf, isum);
   return hipGetLastError();
 }
 
@@ -343,19 +349,19 @@ hipError_t launch_down_i4_mfma(const ExpertArgs& a, const int8_t* hq, const floa
     const int nsplit = (a.d + 255) / 256;
     const dim3 grid(grid_for(b, 64, nsplit));
     if (isum)
-      hipLaunchKernelGGL((k_w4a8<2, 2, false, true>), grid, dim3(256), 0, st, b, nsplit, a.h, a.d,
+      hipLaunchKernelGGL((k_w4a8<2, 2, false, true, false>), grid, dim3(256), 0, st, b, nsplit, a.h, a.d,
                          hq, hs, wq, ws, f, isum);
     else
-      hipLaunchKernelGGL((k_w4a8<2, 2, false, false>), grid, dim3(256), 0, st, b, nsplit, a.h, a.d,
+      hipLaunchKernelGGL((k_w4a8<2, 2, false, false, false>), grid, dim3(256), 0, st, b, nsplit, a.h, a.d,
                          hq, hs, wq, ws, f, isum);
   } else {
     const int nsplit = (a.d + 127) / 128;
     const dim3 grid(grid_for(b, 32, nsplit));
     if (isum)
-      hipLaunchKernelGGL((k_w4a8<1, 1, false, true>), grid, dim3(256), 0, st, b, nsplit, a.h, a.d,
+      hipLaunchKernelGGL((k_w4a8<1, 1, false, true, true>), grid, dim3(256), 0, st, b, nsplit, a.h, a.d,
                          hq, hs, wq, ws, f, isum);
     else
-      hipLaunchKernelGGL((k_w4a8<1, 1, false, false>), grid, dim3(256), 0, st, b, nsplit, a.h, a.d,
+      hipLaunchKernelGGL((k_w4a8<1, 1, false, false, true>), grid, dim3(256), 0, st, b, nsplit, a.h, a.d,
                          hq, hs, wq, ws, f, isum);
   }
   return hipGetLastError();

@@ -38,6 +38,9 @@ __global__ __launch_bounds__(kBlockSlots) void k_route_count(int64_t Tk, int E,
   if (tid < E) counts[(int64_t)blockIdx.x * E + tid] = cnt[tid];
 }
 
+// kSingle: the whole table fits one block (T*k <= 256, decode batches); the
+// block counts its own slots and no count table is read.
+template <bool kSingle>
 __global__ __launch_bounds__(kBlockSlots) void k_route_scatter(
     int64_t Tk, int E, int64_t nblk, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -49,8 +52,17 @@ __global__ __launch_bounds__(kBlockSlots) void k_route_scatter(
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t blk = blockIdx.x;
 
-  // Per-expert sums over blocks: 4 threads per expert, interleaved blocks.
-  {
+  if constexpr (kSingle) {
+    part_before[wv][lane] = 0;
+    part_total[wv][lane] = 0;
+    wcnt[wv][lane] = 0;
+    __syncthreads();
+    if (tid < Tk) {
+      const int e = idx[tid];
+      if ((unsigned)e < (unsigned)E) atomicAdd(&part_total[0][e], 1);
+    }
+  } else {
+    // Per-expert sums over blocks: 4 threads per expert, interleaved blocks.
     int before = 0, total = 0;
     if (lane < E) {
       for (int64_t b = wv; b < nblk; b += 4) {
@@ -107,10 +119,15 @@ int64_t route_blocks(int64_t Tk) { return (Tk + kBlockSlots - 1) / kBlockSlots; 
 hipError_t launch_route(int64_t Tk, int E, const int32_t* idx, int32_t* offsets, int32_t* perm,
                         int32_t* inv_perm, int32_t* ws, hipStream_t st) {
   const int64_t nblk = route_blocks(Tk);
+  if (nblk == 1) {
+    hipLaunchKernelGGL(k_route_scatter<true>, dim3(1), dim3(kBlockSlots), 0, st, Tk, E, nblk, idx,
+                       ws, offsets, perm, inv_perm);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_route_count, dim3((unsigned)nblk), dim3(kBlockSlots), 0, st, Tk, E, idx, ws);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_route_scatter, dim3((unsigned)nblk), dim3(kBlockSlots), 0, st, Tk, E, nblk,
+  hipLaunchKernelGGL(k_route_scatter<false>, dim3((unsigned)nblk), dim3(kBlockSlots), 0, st, Tk, E, nblk,
                      idx, ws, offsets, perm, inv_perm);
   return hipGetLastError();
 }

@@ -16,6 +16,46 @@ namespace {
 
 constexpr int kTok = 4;     // tokens per workgroup (one per wave for the top-k)
 constexpr int kRowStride = 65;  // LDS stride of one row of 64 lane partials (padded)
+constexpr int64_t kSmallRouterT = 64;  // up to this many tokens: the one-token-per-workgroup form
+
+// Top-k and gate weights of one token; lane e holds the logit of expert e
+// (-inf for e >= E).  k rounds of a wave arg-max under the total order (value
+// descending, index ascending): the round's maximum, then the lowest lane
+// holding it; lane j keeps the winner of round j.  Writes idx[0..k) and
+// w[0..k).  Called by a whole wave.
+template <int kGating>
+__device__ __forceinline__ void select_topk(float mine, int lane, int E, int k,
+                                            int32_t* __restrict__ idx, float* __restrict__ w) {
+  const bool valid = lane < E;
+  bool avail = valid;
+  int my_sel = 0;
+  float m = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    const float mx = max64(avail ? mine : -INFINITY);
+    const uint64_t hits = __ballot(avail && mine == mx);
+    const int win = __ffsll((unsigned long long)hits) - 1;
+    if (j == 0) m = mx;
+    if (lane == j) my_sel = win;
+    if (lane == win) avail = false;
+  }
+  float wv;
+  if (kGating == 0) {
+    // softmax over all E logits, not renormalised over the k selected
+    const float z = valid ? exp_fp32(mine - m) : 0.0f;
+    const float S = tree_sum64(z);
+    wv = __shfl(z, my_sel) / S;
+  } else {
+    // sigmoid of each selected logit, normalised over the k selected
+    const float sg = valid ? 1.0f / (1.0f + exp_fp32(-mine)) : 0.0f;
+    const float mysg = __shfl(sg, my_sel);
+    const float S = tree_sum64(lane < k ? mysg : 0.0f);
+    wv = mysg / S;
+  }
+  if (lane < k) {
+    idx[lane] = my_sel;
+    w[lane] = wv;
+  }
+}
 
 // Workgroup = 4 waves and 4 tokens.  Phase 1: wave w takes experts w, w+4,
 // w+8, ... (at most 16); for each one, lane l forms the 4 tokens' partial sums
@@ -99,39 +139,74 @@ __global__ __launch_bounds__(256) void k_router(int64_t T, int d, int E, int k,
   if (wave >= nt) return;
   const int64_t t = t0 + wave;
   const float mine = lane < E ? s_logit[wave][lane] : -INFINITY;
+  select_topk<kGating>(mine, lane, E, k, idx + t * k, w + t * k);
+}
 
-  // Top-k: k rounds of a wave arg-max under the total order (value
-  // descending, index ascending): the round's maximum, then the lowest lane
-  // holding it.  Lane j keeps the winner of round j.
-  const bool valid = lane < E;
-  bool avail = valid;
-  int my_sel = 0;
-  float m = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    const float mx = max64(avail ? mine : -INFINITY);
-    const uint64_t hits = __ballot(avail && mine == mx);
-    const int win = __ffsll((unsigned long long)hits) - 1;
-    if (j == 0) m = mx;
-    if (lane == j) my_sel = win;
-    if (lane == win) avail = false;
-  }
+// Few tokens (decode): one token per workgroup of 16 waves; wave w takes
+// experts w, w+16, w+32, w+48 and reads all of their rows at once, so the
+// router costs about one memory round trip.  Each logit is the 64-lane tree
+// sum of its partials (the same order as above) plus the bias.
+constexpr int kSmallWaves = 16;
+constexpr int kSmallPer = 4;  // experts per wave (E <= 64)
 
-  float wv;
-  if (kGating == 0) {
-    // softmax over all E logits, not renormalised over the k selected
-    const float z = valid ? exp_fp32(mine - m) : 0.0f;
-    const float S = tree_sum64(z);
-    wv = __shfl(z, my_sel) / S;
-  } else {
-    // sigmoid of each selected logit, normalised over the k selected
-    const float sg = valid ? 1.0f / (1.0f + exp_fp32(-mine)) : 0.0f;
-    const float mysg = __shfl(sg, my_sel);
-    const float S = tree_sum64(lane < k ? mysg : 0.0f);
-    wv = mysg / S;
+template <int kGating, int kNX>
+__global__ __launch_bounds__(64 * kSmallWaves) void k_router_small(
+    int64_t T, int d, int E, int k, const float* __restrict__ x, const float* __restrict__ wr,
+    const float* __restrict__ bias, int32_t* __restrict__ idx, float* __restrict__ w) {
+  __shared__ float s_logit[64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t = blockIdx.x;
+  float xv[kNX], wv[kSmallPer][kNX];
+#pragma unroll
+  for (int i = 0; i < kSmallPer; ++i) {
+    const float* we = wr + (int64_t)min(wave + kSmallWaves * i, E - 1) * d;
+#pragma unroll
+    for (int c = 0; c < kNX; ++c) wv[i][c] = we[lane + kWave * c];
   }
-  if (lane < k) {
-    idx[t * k + lane] = my_sel;
-    w[t * k + lane] = wv;
+#pragma unroll
+  for (int c = 0; c < kNX; ++c) xv[c] = x[t * d + lane + kWave * c];
+#pragma unroll
+  for (int i = 0; i < kSmallPer; ++i) {
+    const int e = wave + kSmallWaves * i;
+    if (e >= E) break;
+    float p = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kNX; ++c) p = __builtin_fmaf(xv[c], wv[i][c], p);
+    const float l = tree_sum64(p) + (bias ? bias[e] : 0.0f);
+    if (lane == 0) s_logit[e] = l;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const float mine = lane < E ? s_logit[lane] : -INFINITY;
+  select_topk<kGating>(mine, lane, E, k, idx + t * k, w + t * k);
+}
+
+template <int kG, int kNX>
+void launch_router_nx(bool small, int64_t T, int d, int E, int k, const float* x, const float* wr,
+                      const float* bias, int32_t* idx, float* w, hipStream_t st) {
+  if constexpr (kNX > 0 && kNX <= 20) {
+    if (small) {
+      hipLaunchKernelGGL((k_router_small<kG, kNX>), dim3((unsigned)T), dim3(64 * kSmallWaves), 0,
+                         st, T, d, E, k, x, wr, bias, idx, w);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((k_router<kG, kNX>), dim3((unsigned)((T + kTok - 1) / kTok)), dim3(256), 0,
+                     st, T, d, E, k, x, wr, bias, idx, w);
+}
+
+template <int kG>
+void launch_router_g(bool small, int64_t T, int d, int E, int k, const float* x, const float* wr,
+                     const float* bias, int32_t* idx, float* w, hipStream_t st) {
+  switch (d % kWave == 0 ? d / kWave : 0) {
+    case 4: launch_router_nx<kG, 4>(small, T, d, E, k, x, wr, bias, idx, w, st); break;
+    case 8: launch_router_nx<kG, 8>(small, T, d, E, k, x, wr, bias, idx, w, st); break;
+    case 12: launch_router_nx<kG, 12>(small, T, d, E, k, x, wr, bias, idx, w, st); break;
+    case 16: launch_router_nx<kG, 16>(small, T, d, E, k, x, wr, bias, idx, w, st); break;
+    case 20: launch_router_nx<kG, 20>(small, T, d, E, k, x, wr, bias, idx, w, st); break;
+    case 24: launch_router_nx<kG, 24>(small, T, d, E, k, x, wr, bias, idx, w, st); break;
+    case 32: launch_router_nx<kG, 32>(small, T, d, E, k, x, wr, bias, idx, w, st); break;
+    default: launch_router_nx<kG, 0>(small, T, d, E, k, x, wr, bias, idx, w, st); break;
   }
 }
 
@@ -140,26 +215,12 @@ __global__ __launch_bounds__(256) void k_router(int64_t T, int d, int E, int k,
 hipError_t launch_router(int64_t T, int d, int E, int k, int gating, const float* x,
                          const float* wr, const float* bias, int32_t* idx, float* w,
                          hipStream_t st) {
-  const dim3 grid((unsigned)((T + kTok - 1) / kTok)), block(256);
-#define MM_ROUTER(G, NX) hipLaunchKernelGGL((k_router<G, NX>), grid, block, 0, st, T, d, E, k, x, wr, bias, idx, w)
-#define MM_ROUTER_NX(G)                 \
-  switch (d / kWave) {                  \
-    case 4: MM_ROUTER(G, 4); break;     \
-    case 8: MM_ROUTER(G, 8); break;     \
-    case 12: MM_ROUTER(G, 12); break;   \
-    case 16: MM_ROUTER(G, 16); break;   \
-    case 20: MM_ROUTER(G, 20); break;   \
-    case 24: MM_ROUTER(G, 24); break;   \
-    case 32: MM_ROUTER(G, 32); break;   \
-    default: MM_ROUTER(G, 0); break;    \
-  }
-  if (gating == 0) {
-    MM_ROUTER_NX(0)
-  } else {
-    MM_ROUTER_NX(1)
-  }
-#undef MM_ROUTER_NX
-#undef MM_ROUTER
+  // few tokens: one 16-wave workgroup per token (widths with a register form up to 1280)
+  const bool small = T <= kSmallRouterT;
+  if (gating == 0)
+    launch_router_g<0>(small, T, d, E, k, x, wr, bias, idx, w, st);
+  else
+    launch_router_g<1>(small, T, d, E, k, x, wr, bias, idx, w, st);
   return hipGetLastError();
 }
 

@@ -55,6 +55,20 @@ hipError_t launch_gateup_i4_mfma(const ExpertArgs& a, const int8_t* xq, const fl
 hipError_t launch_down_i4_mfma(const ExpertArgs& a, const int8_t* hq, const float* hs,
                                const uint8_t* wq, const float* ws, float* f, int32_t* isum,
                                hipStream_t st);
+// Weight-streaming forms (k_gemv.hip) for a few rows per expert: same
+// outputs as the matrix-core forms (gate/up: FP32 hidden rows to a_buf).  gemv_i4_fits(K, gateup) tells whether a
+// reduction length is supported (K % 64 == 0, K <= 2560, LDS within 64 KB).
+bool gemv_i4_fits(int K, bool gateup);
+hipError_t launch_gateup_i4_gemv(const ExpertArgs& a, const int8_t* xq, const float* sx,
+                                 const uint8_t* wq, const float* ws, float* a_buf, int32_t* isum,
+                                 hipStream_t st);
+hipError_t launch_down_i4_gemv(const ExpertArgs& a, const int8_t* hq, const float* hs,
+                               const uint8_t* wq, const float* ws, float* f, int32_t* isum,
+                               hipStream_t st);
+// Weight-streaming forms are used up to this many rows (routed: all experts
+// together; dense: the tokens).
+constexpr int64_t kGemvMaxRowsRouted = 512;
+constexpr int64_t kGemvMaxRowsDense = 64;
 // The matrix-core forms are used from this many rows on, when the reduction
 // dimension is a multiple of 128.
 constexpr int64_t kMfmaMinRows = 256;

@@ -110,11 +110,16 @@ class MoELayer:
         self.f = _empty((T * k, d), torch.float32, dv)
         self.ys = _empty((T, d), torch.float32, dv) if self.hs else None
         self.y = _empty((T, d), torch.float32 if self.desc.out_dtype == B.MM_OUT_F32 else torch.int16, dv)
-        self.ws_bytes = max(B.workspace_bytes(self.desc, T, B.MM_WS_MAX), 256)
-        self.ws = _empty((self.ws_bytes,), torch.uint8, dv)
-        # separate workspace for the shared expert so it can run concurrently
-        self.ws2_bytes = max(B.workspace_bytes(self.desc, T, B.MM_WS_SHARED), 256)
-        self.ws2 = _empty((self.ws2_bytes,), torch.uint8, dv)
+        # One workspace per call that needs one (the shared expert runs
+        # concurrently with the routed calls on a second stream).
+        self.wk_route_bytes = max(B.workspace_bytes(self.desc, T, B.MM_WS_ROUTE), 256)
+        self.wk_route = _empty((self.wk_route_bytes,), torch.uint8, dv)
+        self.wk_gu_bytes = max(B.workspace_bytes(self.desc, T, B.MM_WS_GATEUP), 256)
+        self.wk_gu = _empty((self.wk_gu_bytes,), torch.uint8, dv)
+        self.wk_dn_bytes = max(B.workspace_bytes(self.desc, T, B.MM_WS_DOWN), 256)
+        self.wk_dn = _empty((self.wk_dn_bytes,), torch.uint8, dv)
+        self.wk_sh_bytes = max(B.workspace_bytes(self.desc, T, B.MM_WS_SHARED), 256)
+        self.wk_sh = _empty((self.wk_sh_bytes,), torch.uint8, dv)
         self._T = T
 
     # The seven calls, in order.  Each uses the current torch stream.
@@ -122,7 +127,8 @@ class MoELayer:
         B.router_topk(self.desc, T, x, self.wr, self.bias, self.idx, self.topw)
 
     def route(self, T):
-        B.route_permute(self.desc, T, self.idx, self.offsets, self.perm, self.inv, self.ws, self.ws_bytes)
+        B.route_permute(self.desc, T, self.idx, self.offsets, self.perm, self.inv, self.wk_route,
+                        self.wk_route_bytes)
 
     def act_quant(self, x, T):
         B.act_quant_i8(T, self.d, x, self.xq, self.sx)
@@ -133,16 +139,24 @@ class MoELayer:
     def gateup(self, x, T, isum=None):
         a, s = self.act(x)
         B.expert_gateup_swiglu(self.desc, T, a, s, self.perm, self.offsets, self.w_gu.c(), self.hbuf,
-                               self.hscale, self.ws, self.ws_bytes, isum=isum)
+                               self.hscale, self.wk_gu, self.wk_gu_bytes, isum=isum)
+
+    def gateup_f32(self, x, T, out):
+        """Routed gate/up + SwiGLU without the re-quantisation: FP32 hidden
+        rows [T*k, h] (sorted order) into `out` (INT4 weights only).  The
+        matrix-core / weight-streaming kernel of gateup() on its own."""
+        a, s = self.act(x)
+        B.expert_gateup_swiglu(self.desc, T, a, s, self.perm, self.offsets, self.w_gu.c(), out,
+                               None, None, 0)
 
     def down(self, T, isum=None):
         B.expert_down(self.desc, T, self.hbuf, self.hscale, self.offsets, self.w_d.c(), self.f,
-                      self.ws, self.ws_bytes, isum=isum)
+                      self.wk_dn, self.wk_dn_bytes, isum=isum)
 
     def shared(self, x, T):
         a, s = self.act(x)
-        B.shared_expert(self.desc, T, a, s, self.ws_gu.c(), self.ws_d.c(), self.ys, self.ws2,
-                        self.ws2_bytes)
+        B.shared_expert(self.desc, T, a, s, self.ws_gu.c(), self.ws_d.c(), self.ys, self.wk_sh,
+                        self.wk_sh_bytes)
 
     def combine(self, T):
         B.combine(self.desc, T, self.f, self.inv, self.topw, self.ys, self.y)

@@ -71,7 +71,10 @@ def test_act_quant_bitexact(rows, cols):
 @pytest.mark.parametrize("T,d,E,k,use_bias,gating", [
     (1000, 768, 60, 4, False, 0), (257, 1280, 60, 4, True, 0), (33, 64, 8, 2, False, 0),
     (130, 256, 60, 4, False, 0), (64, 1024, 64, 8, True, 0), (77, 768, 60, 4, True, 1),
-    (5, 3072, 60, 4, False, 0)])
+    (5, 3072, 60, 4, False, 0),
+    # decode batches (one workgroup per token)
+    (1, 768, 60, 4, False, 0), (8, 1280, 60, 4, True, 0), (64, 768, 60, 4, True, 1),
+    (3, 256, 33, 3, False, 0)])
 def test_router_bitexact(T, d, E, k, use_bias, gating):
     g = rng(T + d)
     x = g.standard_normal((T, d)).astype(np.float32)
@@ -135,6 +138,7 @@ def _sorted_reference(layer, w, lw, x):
     f = np.zeros((rows, w.d))
     igu = np.zeros((rows, 2 * w.h, w.d // 32), np.int32)
     idn = np.zeros((rows, w.d, w.h // 32), np.int32)
+    a = np.zeros((rows, w.h), np.float32)
     for e in range(w.E):
         p = np.arange(off[e], off[e + 1])
         if len(p) == 0:
@@ -142,14 +146,27 @@ def _sorted_reference(layer, w, lw, x):
         tok = perm[p] // w.k
         gq, gs = oracle.quant_w4g32(lw.w_gu[e])
         dq, dsc = oracle.quant_w4g32(lw.w_d[e])
-        hq[p], hs[p], f[p], igu[p], idn[p] = oracle.ffn_w4a8(xq[tok], sx[tok], gq, gs, dq, dsc,
-                                                               want_isum=True)
-    return hq, hs, f, igu, idn
+        hq[p], hs[p], f[p], igu[p], idn[p], a[p] = oracle.ffn_w4a8(
+            xq[tok], sx[tok], gq, gs, dq, dsc, want_isum=True, want_a=True)
+    return hq, hs, f, igu, idn, a
 
 
-@pytest.mark.parametrize("name,T", [("s_prefill", 200), ("m_prefill", 70), ("l_prefill", 45)])
-def test_expert_stages_int4(name, T):
-    w = wl.WORKLOADS[name].with_(T=T)
+# The cases reach each kernel family: weight-streaming (up to 512 routed rows),
+# matrix-core (more rows, K % 128 == 0) and row-tile (the rest: K % 128 != 0,
+# or K beyond the weight-streaming limit of 2560).
+STAGE_CASES = [
+    ("s_prefill", 200, {}),                              # matrix-core
+    ("m_prefill", 70, {}),                               # weight-streaming
+    ("l_prefill", 45, {}),                               # weight-streaming, skewed routing
+    ("s_prefill", 3, {}),                                # weight-streaming, decode-sized
+    ("s_prefill", 150, {"d": 704, "h": 320, "hs": 640}),  # row-tile (K % 128 != 0)
+    ("s_prefill", 30, {"d": 2688, "hs": 0}),              # gate/up row-tile (K > 2560)
+]
+
+
+@pytest.mark.parametrize("name,T,over", STAGE_CASES)
+def test_expert_stages_int4(name, T, over):
+    w = wl.WORKLOADS[name].with_(T=T, **over)
     lw = wl.layer_weights(w)
     x = wl.tokens(w)
     layer = make_layer(w, lw)
@@ -161,12 +178,16 @@ def test_expert_stages_int4(name, T):
     rows = T * w.k
     isum_gu = torch.zeros((rows, 2 * w.h, w.d // 32), dtype=torch.int32, device=DEV)
     layer.gateup(xd, T, isum=isum_gu)
-    hq_ref, hs_ref, f_ref, igu_ref, idn_ref = _sorted_reference(layer, w, lw, x)
+    hq_ref, hs_ref, f_ref, igu_ref, idn_ref, a_ref = _sorted_reference(layer, w, lw, x)
     # exact int32 group sums of the fused gate/up product
     assert np.array_equal(np_(isum_gu), igu_ref)
     # re-quantised hidden rows and their scales
     assert np.array_equal(np_(layer.hbuf), hq_ref)
     assert np.array_equal(np_(layer.hscale), hs_ref)
+    # FP32 hidden rows (h_scale NULL): the same kernel without the re-quantisation
+    a_gpu = torch.empty((rows, w.h), dtype=torch.float32, device=DEV)
+    layer.gateup_f32(xd, T, a_gpu)
+    assert np.array_equal(np_(a_gpu), a_ref)
     # down product, stage-isolated: feed the oracle's hidden rows
     layer.hbuf.copy_(dev(hq_ref))
     layer.hscale.copy_(dev(hs_ref))
@@ -188,6 +209,10 @@ CASES = [
     ("l_prefill_bf16", 64, {}),
     ("s_prefill", 64, {"E": 8, "k": 2, "d": 128, "h": 64, "hs": 64}),
     ("s_prefill", 16, {"E": 1, "k": 1, "hs": 0}),
+    ("s_prefill", 8, {}),                                 # decode batch
+    ("l_prefill", 1, {}),                                 # decode, largest shared expert
+    ("m_prefill", 64, {}),                                # largest weight-streaming shared batch
+    ("s_prefill", 150, {"d": 704, "h": 320, "hs": 640}),  # row-tile kernels
 ]
 
 

@@ -292,6 +292,12 @@ def test_ffn_w4a8_against_dequantised_double(ora):
     assert np.all(np.abs(hd - a) <= hs[:, None] * 0.5 * (1 + 1e-4))
     fd = hd @ W(dq, ds).T
     assert (np.abs(f - fd).max(1) / np.abs(fd).max(1)).max() < 1e-5
+    # the exposed FP32 hidden row: close to the double SwiGLU, and its own
+    # per-row quantisation is exactly the hidden code row
+    a32 = ora.ffn_w4a8(xq, sx, guq, gus, dq, ds, want_a=True)[3]
+    assert (np.abs(a32 - a).max(1) / np.abs(a).max(1)).max() < 1e-5
+    hq2, hs2 = ora.quant_act_i8(a32)
+    assert np.array_equal(hq2, hq) and np.array_equal(hs2, hs)
     # and the whole thing is close to the unquantised FP32 FFN
     ref = _dense_swiglu(x.astype(np.float64), wgu.astype(np.float64), wd.astype(np.float64))
     assert np.abs(f - ref).max() / np.abs(ref).max() < 0.3
