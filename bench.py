@@ -64,16 +64,20 @@ def layer_work(w, T, counts=None):
 
 
 # Kernel chosen by the library for the routed expert products (mirrors the
-# dispatch in csrc/api.hip: weight-streaming up to 512 routed rows when the
-# reduction length fits, matrix cores from 256 rows when K % 128 == 0).
+# dispatch in csrc/api.hip and csrc/k_mfma.hip: weight-streaming up to 512
+# routed rows when the reduction length fits, matrix cores from 256 rows when
+# K % 128 == 0, with two row tiles per wave once that still gives 4096 waves).
 def kernel_of(w, T, gateup: bool):
     rows, K = T * w.k, (w.d if gateup else w.h)
+    part = "gate/up" if gateup else "down"
     if w.wfmt != "int4g32":
         return ("k_gateup_fp" if gateup else "k_down_fp"), "row-tile"
     if rows <= 512 and K % 64 == 0 and K <= 2560:
-        return ("k_gemv_i4<gate/up, routed>" if gateup else "k_gemv_i4<down, routed>"), "weight-streaming"
+        return f"k_gemv_i4<{part},routed>", "weight-streaming"
     if rows >= 256 and K % 128 == 0:
-        return ("k_w4a8<2,2,gate/up, routed>" if gateup else "k_w4a8<2,2,down, routed>"), "matrix-core"
+        nsplit = w.h // 32 if gateup else w.d // 64
+        mt = 2 if ((rows + 63) // 64 + w.E) * nsplit >= 4096 else 1
+        return f"k_w4a8w<{mt},2,{part},routed>", "matrix-core"
     return ("k_gateup_i4" if gateup else "k_down_i4"), "row-tile"
 
 

@@ -166,6 +166,40 @@ __device__ __forceinline__ void routed_tile(const int32_t* __restrict__ offsets,
   }
 }
 
+// routed_tile for a one-wave workgroup: the same lookup, with the result
+// returned wave-uniform in registers (n = 0: no such tile).  All 64 lanes call.
+__device__ __forceinline__ void routed_tile_wave(const int32_t* __restrict__ offsets, int E,
+                                                 int rows, int rows_per_tile, int mt, int& p0,
+                                                 int& n, int& e) {
+  const int lane = threadIdx.x & 63;
+  int beg = 0, end = 0;
+  if (lane < E) {
+    beg = min(max(offsets[lane], 0), rows);
+    end = min(max(offsets[lane + 1], beg), rows);
+  }
+  const int nt = (end - beg + rows_per_tile - 1) / rows_per_tile;
+  int inc = nt;
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) {
+    const int v = __shfl_up(inc, s);
+    if (lane >= s) inc += v;
+  }
+  const int first = inc - nt;
+  const bool mine = lane < E && mt >= first && mt < inc;
+  const uint64_t owners = __ballot(mine);
+  if (owners == 0ull) {
+    p0 = 0;
+    n = 0;
+    e = 0;
+    return;
+  }
+  const int own = __ffsll((unsigned long long)owners) - 1;
+  const int my_p0 = beg + (mt - first) * rows_per_tile;
+  p0 = __builtin_amdgcn_readlane(my_p0, own);
+  n = min(rows_per_tile, __builtin_amdgcn_readlane(end, own) - p0);
+  e = own;
+}
+
 // Per-row INT8 code of v given the row scale s (s > 0): clamp(rint(v / s)).
 __device__ __forceinline__ int8_t quant_i8(float v, float s) {
   float r = rintf(v / s);

@@ -10,7 +10,11 @@
 namespace mm {
 namespace {
 
-// One thread per (token, 4 consecutive columns).
+// One wave per token: the token's k sorted positions and gate weights are
+// read once and broadcast across the wave; lane l handles the float4 columns
+// l, l + 64, ...  All of a lane's gathers are issued before the sums.
+constexpr int kMaxC4 = 8;  // float4 columns per lane: d <= 2048
+
 template <bool kBF16Out>
 __global__ __launch_bounds__(256) void k_combine(int64_t T, int d, int k,
                                                  const float* __restrict__ f,
@@ -18,6 +22,72 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int d, int k,
                                                  const float* __restrict__ w,
                                                  const float* __restrict__ ys,
                                                  void* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int q = d / 4;
+  const int64_t Tk = T * k;
+  int my_p = -1;
+  float my_w = 0.0f;
+  if (lane < k) {
+    const int64_t p = inv[t * k + lane];
+    if (p >= 0 && p < Tk) my_p = (int)p;  // a corrupt inverse permutation reads nothing
+    my_w = w[t * k + lane];
+  }
+  float4 acc[kMaxC4];
+#pragma unroll
+  for (int i = 0; i < kMaxC4; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    const int p = __shfl(my_p, j);
+    const float wj = __shfl(my_w, j);
+    if (p < 0) continue;
+    const float4* fr = reinterpret_cast<const float4*>(f + (int64_t)p * d);
+    float4 v[kMaxC4];
+#pragma unroll
+    for (int i = 0; i < kMaxC4; ++i)
+      if (lane + 64 * i < q) v[i] = fr[lane + 64 * i];
+#pragma unroll
+    for (int i = 0; i < kMaxC4; ++i)
+      if (lane + 64 * i < q) {
+        acc[i].x = fmaf(wj, v[i].x, acc[i].x);
+        acc[i].y = fmaf(wj, v[i].y, acc[i].y);
+        acc[i].z = fmaf(wj, v[i].z, acc[i].z);
+        acc[i].w = fmaf(wj, v[i].w, acc[i].w);
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxC4; ++i) {
+    const int c4 = lane + 64 * i;
+    if (c4 >= q) continue;
+    float4 a = acc[i];
+    if (ys) {
+      const float4 s = reinterpret_cast<const float4*>(ys + t * d)[c4];
+      a.x += s.x;
+      a.y += s.y;
+      a.z += s.z;
+      a.w += s.w;
+    }
+    if (kBF16Out) {
+      ushort4 o;
+      o.x = f32_to_bf16(a.x);
+      o.y = f32_to_bf16(a.y);
+      o.z = f32_to_bf16(a.z);
+      o.w = f32_to_bf16(a.w);
+      reinterpret_cast<ushort4*>(y)[t * q + c4] = o;
+    } else {
+      reinterpret_cast<float4*>(y)[t * q + c4] = a;
+    }
+  }
+}
+
+// Wider rows: one thread per (token, float4 column).
+template <bool kBF16Out>
+__global__ __launch_bounds__(256) void k_combine_wide(int64_t T, int d, int k,
+                                                      const float* __restrict__ f,
+                                                      const int32_t* __restrict__ inv,
+                                                      const float* __restrict__ w,
+                                                      const float* __restrict__ ys,
+                                                      void* __restrict__ y) {
   const int q = d / 4;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= T * q) return;
@@ -59,14 +129,23 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int d, int k,
 hipError_t launch_combine(int64_t T, int d, int k, const float* f, const int32_t* inv_perm,
                           const float* w, const float* ys, void* y, bool bf16_out,
                           hipStream_t st) {
-  const int64_t n = T * (d / 4);
-  const unsigned blocks = (unsigned)((n + 255) / 256);
-  if (bf16_out)
-    hipLaunchKernelGGL(k_combine<true>, dim3(blocks), dim3(256), 0, st, T, d, k, f, inv_perm, w,
-                       ys, y);
-  else
-    hipLaunchKernelGGL(k_combine<false>, dim3(blocks), dim3(256), 0, st, T, d, k, f, inv_perm, w,
-                       ys, y);
+  if (d / 4 <= 64 * kMaxC4) {
+    const unsigned blocks = (unsigned)((T + 3) / 4);
+    if (bf16_out)
+      hipLaunchKernelGGL(k_combine<true>, dim3(blocks), dim3(256), 0, st, T, d, k, f, inv_perm, w,
+                         ys, y);
+    else
+      hipLaunchKernelGGL(k_combine<false>, dim3(blocks), dim3(256), 0, st, T, d, k, f, inv_perm, w,
+                         ys, y);
+  } else {
+    const unsigned blocks = (unsigned)((T * (d / 4) + 255) / 256);
+    if (bf16_out)
+      hipLaunchKernelGGL(k_combine_wide<true>, dim3(blocks), dim3(256), 0, st, T, d, k, f, inv_perm,
+                         w, ys, y);
+    else
+      hipLaunchKernelGGL(k_combine_wide<false>, dim3(blocks), dim3(256), 0, st, T, d, k, f,
+                         inv_perm, w, ys, y);
+  }
   return hipGetLastError();
 }
 

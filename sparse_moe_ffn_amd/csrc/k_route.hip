@@ -76,16 +76,27 @@ __global__ __launch_bounds__(kBlockSlots) void k_route_scatter(
     wcnt[wv][lane] = 0;
   }
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int e = 0; e < E; ++e) {
-      const int tot = part_total[0][e] + part_total[1][e] + part_total[2][e] + part_total[3][e];
-      const int bef = part_before[0][e] + part_before[1][e] + part_before[2][e] + part_before[3][e];
-      if (blk == 0) offsets[e] = run;
-      base[e] = run + bef;
-      run += tot;
+  // Expert offsets: exclusive scan of the totals over the experts (one lane
+  // per expert, E <= 64), then each expert's base for this block.
+  if (tid < 64) {
+    const int e = tid;
+    int tot = 0, bef = 0;
+    if (e < E) {
+      tot = part_total[0][e] + part_total[1][e] + part_total[2][e] + part_total[3][e];
+      bef = part_before[0][e] + part_before[1][e] + part_before[2][e] + part_before[3][e];
     }
-    if (blk == 0) offsets[E] = run;
+    int inc = tot;
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) {
+      const int v = __shfl_up(inc, s);
+      if (lane >= s) inc += v;
+    }
+    const int excl = inc - tot;
+    if (e < E) {
+      if (blk == 0) offsets[e] = excl;
+      base[e] = excl + bef;
+      if (blk == 0 && e == E - 1) offsets[E] = inc;
+    }
   }
 
   // Rank inside the wave: the lanes holding the same id are found with one

@@ -85,29 +85,28 @@ __global__ __launch_bounds__(256) void k_router(int64_t T, int d, int E, int k,
     for (int q = 0; q < kTok; ++q)
 #pragma unroll
       for (int i = 0; i < kNX; ++i) xv[q][i] = q < nt ? x[(t0 + q) * d + lane + kWave * i] : 0.0f;
-    // expert rows read one ahead (two register sets in ping-pong)
-    float wa[kNX], wb[kNX];
-    auto load_row = [&](int i, float (&wv)[kNX]) {
+    // expert rows read four ahead (a ring of four register sets); rows past
+    // this wave's last expert re-read expert E-1 (valid, unused)
+    float wv[4][kNX];
+    auto load_row = [&](int i, float (&dst)[kNX]) {
       const float* we = wr + (int64_t)min(wave + 4 * i, E - 1) * d;
 #pragma unroll
-      for (int c = 0; c < kNX; ++c) wv[c] = we[lane + kWave * c];
+      for (int c = 0; c < kNX; ++c) dst[c] = we[lane + kWave * c];
     };
-    auto partials = [&](int i, const float (&wv)[kNX]) {
 #pragma unroll
-      for (int q = 0; q < kTok; ++q) {
-        float p = 0.0f;
+    for (int i = 0; i < 4; ++i) load_row(i, wv[i]);
 #pragma unroll
-        for (int c = 0; c < kNX; ++c) p = __builtin_fmaf(xv[q][c], wv[c], p);
-        s_part[wave][i * kTok + q][lane] = p;
+    for (int i = 0; i < 16; ++i) {
+      if (i < ne) {
+#pragma unroll
+        for (int q = 0; q < kTok; ++q) {
+          float p = 0.0f;
+#pragma unroll
+          for (int c = 0; c < kNX; ++c) p = __builtin_fmaf(xv[q][c], wv[i % 4][c], p);
+          s_part[wave][i * kTok + q][lane] = p;
+        }
       }
-    };
-    load_row(0, wa);
-    for (int i = 0; i < ne; i += 2) {
-      load_row(i + 1, wb);
-      partials(i, wa);
-      if (i + 1 >= ne) break;
-      load_row(i + 2, wa);
-      partials(i + 1, wb);
+      if (i + 4 < 16) load_row(i + 4, wv[i % 4]);
     }
   } else {
     for (int i = 0; i < ne; ++i) {

@@ -82,6 +82,7 @@ class MoELayer:
         # on a second stream (default priority) beside the routed experts.
         self.overlap_shared = overlap_shared and bool(hs)
         self.side = torch.cuda.Stream(device=self.device) if self.overlap_shared else None
+        self._xq_ready = torch.cuda.Event() if self.overlap_shared else None
 
     @classmethod
     def from_workload(cls, w, lw, device="cuda", **kw):
@@ -182,20 +183,33 @@ class MoELayer:
         """y = eq. (*) of x [T, d] FP32 (device).  Returns the layer's y buffer."""
         T = x.shape[0]
         self.buffers(T)
-        if self.wfmt == "int4g32":
-            self.act_quant(x, T)
         main = torch.cuda.current_stream(self.device)
-        if self.overlap_shared:
+        int4 = self.wfmt == "int4g32"
+        if self.overlap_shared and self.hs:
+            # side stream: activation quantisation, then the shared expert;
+            # main stream: router and routing meanwhile, then the routed experts
+            # once the quantised activations exist
             self.side.wait_stream(main)
             with torch.cuda.stream(self.side):
+                if int4:
+                    self.act_quant(x, T)
+                    self._xq_ready.record(self.side)
                 self.shared(x, T)
-        self.router(x, T)
-        self.route(T)
-        self.gateup(x, T)
-        self.down(T)
-        if self.hs and not self.overlap_shared:
-            self.shared(x, T)
-        if self.overlap_shared:
+            self.router(x, T)
+            self.route(T)
+            if int4:
+                main.wait_event(self._xq_ready)
+            self.gateup(x, T)
+            self.down(T)
             main.wait_stream(self.side)
+        else:
+            if int4:
+                self.act_quant(x, T)
+            self.router(x, T)
+            self.route(T)
+            self.gateup(x, T)
+            self.down(T)
+            if self.hs:
+                self.shared(x, T)
         self.combine(T)
         return self.y
