@@ -66,10 +66,13 @@ def layer_work(w, T, counts=None):
 # Kernel chosen by the library for the routed expert products (mirrors the
 # dispatch in csrc/api.hip and csrc/k_mfma.hip: weight-streaming up to 512
 # routed rows when the reduction length fits, matrix cores from 256 rows when
-# K % 128 == 0, with two row tiles per wave once that still gives 4096 waves).
+# K % 128 == 0, with two row tiles per wave once that still gives 4096 waves;
+# BF16 weights always on the bf16 matrix cores).
 def kernel_of(w, T, gateup: bool):
     rows, K = T * w.k, (w.d if gateup else w.h)
     part = "gate/up" if gateup else "down"
+    if w.wfmt == "bf16":
+        return f"k_bf16w<2,{part},routed>", "matrix-core"
     if w.wfmt != "int4g32":
         return ("k_gateup_fp" if gateup else "k_down_fp"), "row-tile"
     if rows <= 512 and K % 64 == 0 and K <= 2560:

@@ -218,10 +218,14 @@ mm_status mm_act_quant_i8(int64_t rows, int64_t cols, const float* x, int8_t* q,
  *   a themselves are written to h (FP32 [T*k][h], sorted order) and ws may
  *   be NULL: for callers that apply their own re-quantisation.
  * MM_W_F32 / MM_W_BF16: act is x (FP32 [T][d]), act_scale and h_scale NULL;
- *   h is FP32 (MM_W_F32) or BF16 (MM_W_BF16) [T*k][h], sorted order.
+ *   h is FP32 (MM_W_F32) or BF16 (MM_W_BF16) [T*k][h], sorted order.  BF16:
+ *   x is rounded to BF16 (nearest even) into ws first, products accumulate
+ *   in FP32, a is rounded to BF16.
  *   w_gateup        stacked [E][2h][d] (see mm_weight)
  *   perm, expert_offsets  from mm_route_permute
- *   ws / ws_bytes   mm_workspace_bytes(desc, T, MM_WS_GATEUP)
+ *   ws / ws_bytes   mm_workspace_bytes(desc, T, MM_WS_GATEUP): INT4 staging
+ *                   of the FP32 rows a, or the BF16 copy of x; 0 bytes (ws may
+ *                   be NULL) for MM_W_F32
  */
 mm_status mm_expert_gateup_swiglu(const mm_layer_desc* desc, int64_t T, const void* act,
                                   const float* act_scale, const int32_t* perm,

@@ -84,9 +84,13 @@ SharedWs shared_ws(const mm_layer_desc* d, int64_t T) {
     w.q_off = align256(T * hs * 4);
     w.s_off = w.q_off + align256(T * hs);
     w.total = w.s_off + align256(T * 4);
+  } else if (d->wfmt == MM_W_BF16) {
+    w.a_off = 0;                               // BF16 hidden rows
+    w.q_off = align256(T * hs * 2);            // BF16 copy of x
+    w.total = w.q_off + align256(T * (int64_t)d->d_model * 2);
   } else {
     w.a_off = 0;
-    w.total = align256(T * hs * (d->wfmt == MM_W_BF16 ? 2 : 4));
+    w.total = align256(T * hs * 4);
   }
   return w;
 }
@@ -97,7 +101,9 @@ size_t ws_bytes(const mm_layer_desc* d, int64_t T, int32_t which) {
     case MM_WS_ROUTE:
       return align256((size_t)mm::route_blocks(Tk) * d->n_experts * 4);
     case MM_WS_GATEUP:
-      return d->wfmt == MM_W_INT4G32 ? align256((size_t)Tk * d->hidden * 4) : 0;
+      if (d->wfmt == MM_W_INT4G32) return align256((size_t)Tk * d->hidden * 4);
+      if (d->wfmt == MM_W_BF16) return align256((size_t)T * d->d_model * 2);  // BF16 copy of x
+      return 0;
     case MM_WS_DOWN:
       return 0;
     case MM_WS_SHARED:
@@ -314,8 +320,18 @@ static mm_status gateup_impl(const mm_layer_desc* desc, int64_t T, const void* a
   }
   if (act_scale || h_scale)
     return fail(MM_ERR_FORMAT, "act_scale and h_scale must be NULL for FP32/BF16 weights");
-  return hip_status(mm::launch_gateup_fp(a, desc->wfmt == MM_W_BF16, act, w.data, h, st),
-                    "mm_expert_gateup_swiglu");
+  if (desc->wfmt == MM_W_BF16) {  // x rounded to BF16 once, then the bf16 matrix cores
+    MM_REQUIRE(ws);
+    if (ws_size < ws_bytes(desc, T, MM_WS_GATEUP))
+      return fail(MM_ERR_WORKSPACE, "gate/up workspace too small (need %lld bytes)", (long long)ws_bytes(desc, T, MM_WS_GATEUP));
+    uint16_t* xb = static_cast<uint16_t*>(ws);
+    MM_TRY(hip_status(mm::launch_convert_bf16(T * desc->d_model, static_cast<const float*>(act), xb, st),
+                      "mm_expert_gateup_swiglu"));
+    return hip_status(mm::launch_gateup_bf16_mfma(a, xb, static_cast<const uint16_t*>(w.data),
+                                                  static_cast<uint16_t*>(h), st),
+                      "mm_expert_gateup_swiglu");
+  }
+  return hip_status(mm::launch_gateup_fp(a, false, act, w.data, h, st), "mm_expert_gateup_swiglu");
 }
 
 mm_status mm_expert_gateup_swiglu(const mm_layer_desc* desc, int64_t T, const void* act,
@@ -358,8 +374,11 @@ static mm_status down_impl(const mm_layer_desc* desc, int64_t T, const void* h,
                       "mm_expert_down");
   }
   if (h_scale) return fail(MM_ERR_FORMAT, "h_scale must be NULL for FP32/BF16 weights");
-  return hip_status(mm::launch_down_fp(a, desc->wfmt == MM_W_BF16, h, w.data, f, st),
-                    "mm_expert_down");
+  if (desc->wfmt == MM_W_BF16)
+    return hip_status(mm::launch_down_bf16_mfma(a, static_cast<const uint16_t*>(h),
+                                                static_cast<const uint16_t*>(w.data), f, st),
+                      "mm_expert_down");
+  return hip_status(mm::launch_down_fp(a, false, h, w.data, f, st), "mm_expert_down");
 }
 
 mm_status mm_expert_down(const mm_layer_desc* desc, int64_t T, const void* h,
@@ -414,11 +433,21 @@ mm_status mm_shared_expert(const mm_layer_desc* desc, int64_t T, const void* act
                       "mm_shared_expert (down)");
   }
   if (act_scale) return fail(MM_ERR_FORMAT, "act_scale must be NULL for FP32/BF16 weights");
-  const bool bf = desc->wfmt == MM_W_BF16;
   void* hbuf = base + sw.a_off;
-  MM_TRY(hip_status(mm::launch_gateup_fp(a, bf, act, w_gateup.data, hbuf, st),
+  if (desc->wfmt == MM_W_BF16) {
+    uint16_t* xb = reinterpret_cast<uint16_t*>(base + sw.q_off);
+    MM_TRY(hip_status(mm::launch_convert_bf16(T * desc->d_model, static_cast<const float*>(act), xb, st),
+                      "mm_shared_expert (x to BF16)"));
+    MM_TRY(hip_status(mm::launch_gateup_bf16_mfma(a, xb, static_cast<const uint16_t*>(w_gateup.data),
+                                                  static_cast<uint16_t*>(hbuf), st),
+                      "mm_shared_expert (gate/up)"));
+    return hip_status(mm::launch_down_bf16_mfma(a, static_cast<const uint16_t*>(hbuf),
+                                                static_cast<const uint16_t*>(w_down.data), ys, st),
+                      "mm_shared_expert (down)");
+  }
+  MM_TRY(hip_status(mm::launch_gateup_fp(a, false, act, w_gateup.data, hbuf, st),
                     "mm_shared_expert (gate/up)"));
-  return hip_status(mm::launch_down_fp(a, bf, hbuf, w_down.data, ys, st), "mm_shared_expert (down)");
+  return hip_status(mm::launch_down_fp(a, false, hbuf, w_down.data, ys, st), "mm_shared_expert (down)");
 }
 
 mm_status mm_combine(const mm_layer_desc* desc, int64_t T, const float* f,

@@ -1,0 +1,207 @@
+// BF16-weight expert products on the bf16 matrix cores
+// (v_mfma_f32_32x32x16_bf16, FP32 accumulation).
+//
+// MobileMoE close reading, section "Custom MoE kernel": per expert, one fused
+// gate/up product over its contiguous (expert-sorted) rows with SwiGLU, then
+// the down product.  In the BF16-weight format the token rows, the weights and
+// the hidden rows are BF16 (round to nearest even) and products accumulate in
+// FP32; no quantisation scales are involved, so the MFMA accumulates straight
+// into the output registers.
+//
+// Tiling.  A workgroup is one wave that owns kMT x 32 rows of one expert and
+// two 32-column tiles (gate/up: the gate tile and the matching up tile of the
+// same 32 hidden columns, so SwiGLU is applied in registers).  Each lane
+// loads 16 bytes (8 BF16 values) of its row per operand and K step of 16,
+// two K steps at a time, one stage ahead of the math; no LDS, no barriers.
+// Tiles are ordered row tile fastest, so the waves working on one column
+// slice of an expert run together and share that slice of the weights in L2.
+#include "common.h"
+#include "launch.h"
+
+namespace mm {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef const __attribute__((address_space(1))) v4i gv4i;
+
+constexpr int kXcd = 8;
+
+template <int kMT>
+struct BStage {
+  v4i a[2][kMT];
+  v4i b[2][2];
+};
+
+template <int kMT>
+__device__ __forceinline__ void bload(BStage<kMT>& st, gv4i* const (&pa)[kMT],
+                                      gv4i* const (&pb)[2], int s0) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int m = 0; m < kMT; ++m) st.a[i][m] = pa[m][2 * (s0 + i)];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) st.b[i][j] = pb[j][2 * (s0 + i)];
+  }
+}
+
+template <int kMT>
+__device__ __forceinline__ void bcompute(v16f (&acc)[kMT][2], const BStage<kMT>& st) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int m = 0; m < kMT; ++m)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[m][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(v8bf, st.a[i][m]), __builtin_bit_cast(v8bf, st.b[i][j]),
+            acc[m][j], 0, 0, 0);
+}
+
+// act: BF16 rows [.][K] (gate/up: the token rows, gathered through perm;
+// down: the sorted hidden rows); w: BF16 [E][wrows][K].  out: gate/up -> BF16
+// hidden rows [rows][h]; down -> FP32 [rows][N].  K % 32 == 0.
+template <int kMT, bool kGateUp, bool kDense>
+__global__ __launch_bounds__(64) void k_bf16w(ExpertArgs a, int nsplit, int n_mt, int K, int N,
+                                              const uint16_t* __restrict__ act,
+                                              const uint16_t* __restrict__ w,
+                                              void* __restrict__ out) {
+  constexpr int kBM = 32 * kMT;
+  const int lane = threadIdx.x;
+  const int per = (int)gridDim.x / kXcd;
+  const int logical = ((int)blockIdx.x % kXcd) * per + (int)blockIdx.x / kXcd;
+  const int mt = logical % n_mt, split = logical / n_mt;
+  if (split >= nsplit) return;
+  const int rows = (int)a.rows;
+  int p0, n, e;
+  if constexpr (kDense) {
+    p0 = mt * kBM;
+    n = min(kBM, rows - p0);
+    e = 0;
+  } else {
+    routed_tile_wave(a.offsets, a.E, rows, kBM, mt, p0, n, e);
+  }
+  if (n <= 0) return;
+  const int h = a.h;
+  int col0, rb[2];
+  if constexpr (kGateUp) {
+    col0 = split * 32;
+    rb[0] = split;
+    rb[1] = h / 32 + split;
+  } else {
+    col0 = split * 64;
+    rb[0] = 2 * split;
+    rb[1] = 2 * split + 1;
+  }
+  // this lane's activation rows (padding rows read the tile's first row;
+  // their results are never stored)
+  gv4i* pa[kMT];
+#pragma unroll
+  for (int m = 0; m < kMT; ++m) {
+    const int r = m * 32 + (lane & 31);
+    const int rr = r < n ? r : 0;
+    int src = p0 + rr;
+    if constexpr (kGateUp && !kDense) {
+      src = a.perm[p0 + rr] / a.k;
+      if ((unsigned)src >= (unsigned)a.T) src = 0;  // stays in bounds for a corrupt perm
+    }
+    pa[m] = (gv4i*)(act + (int64_t)src * K + 8 * (lane >> 5));
+  }
+  const int64_t wrows = kGateUp ? 2 * (int64_t)h : N;
+  gv4i* pb[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    pb[j] = (gv4i*)(w + ((int64_t)e * wrows + rb[j] * 32 + (lane & 31)) * K + 8 * (lane >> 5));
+
+  v16f acc[kMT][2];
+#pragma unroll
+  for (int m = 0; m < kMT; ++m)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[m][j] = v16f{};
+
+  // Stages of two K steps (32 columns); the pointers advance 64 columns per
+  // iteration; the last iteration's prefetch re-reads its own second stage.
+  const int S = K / 16;  // K steps
+  BStage<kMT> s0, s1;
+  bload(s0, pa, pb, 0);
+  for (int s = 0; s < S; s += 4) {
+    if (s + 2 >= S) {  // K % 64 == 32: a last single stage
+      __builtin_amdgcn_sched_barrier(0);
+      bcompute(acc, s0);
+      break;
+    }
+    bload(s1, pa, pb, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    bcompute(acc, s0);
+    __builtin_amdgcn_sched_barrier(0);
+    const int adv = s + 4 < S ? 4 : 2;
+#pragma unroll
+    for (int m = 0; m < kMT; ++m) pa[m] += adv * 2;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) pb[j] += adv * 2;
+    if (s + 4 < S) bload(s0, pa, pb, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    bcompute(acc, s1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+#pragma unroll
+  for (int m = 0; m < kMT; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (row >= n) continue;
+      if constexpr (kGateUp) {
+        const float v = silu(acc[m][0][r]) * acc[m][1][r];
+        reinterpret_cast<uint16_t*>(out)[(int64_t)(p0 + row) * h + col0 + (lane & 31)] =
+            f32_to_bf16(v);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          reinterpret_cast<float*>(out)[(int64_t)(p0 + row) * N + col0 + j * 32 + (lane & 31)] =
+              acc[m][j][r];
+      }
+    }
+}
+
+unsigned grid_bf16(int n_mt, int nsplit) {
+  const int64_t n = (int64_t)n_mt * nsplit;
+  return (unsigned)(kXcd * ((n + kXcd - 1) / kXcd));
+}
+
+int n_row_tiles(const ExpertArgs& a, int bm) {
+  return (int)((a.rows + bm - 1) / bm + (a.offsets ? a.E : 0));
+}
+
+}  // namespace
+
+hipError_t launch_gateup_bf16_mfma(const ExpertArgs& a, const uint16_t* xb, const uint16_t* w,
+                                   uint16_t* h_out, hipStream_t st) {
+  const int nsplit = a.h / 32, n_mt = n_row_tiles(a, 64);
+  const dim3 grid(grid_bf16(n_mt, nsplit)), block(64);
+  if (!a.offsets)
+    hipLaunchKernelGGL((k_bf16w<2, true, true>), grid, block, 0, st, a, nsplit, n_mt, a.d, 2 * a.h,
+                       xb, w, h_out);
+  else
+    hipLaunchKernelGGL((k_bf16w<2, true, false>), grid, block, 0, st, a, nsplit, n_mt, a.d,
+                       2 * a.h, xb, w, h_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_bf16_mfma(const ExpertArgs& a, const uint16_t* hb, const uint16_t* w,
+                                 float* f, hipStream_t st) {
+  ExpertArgs b = a;
+  b.perm = nullptr;
+  const int nsplit = a.d / 64, n_mt = n_row_tiles(b, 64);
+  const dim3 grid(grid_bf16(n_mt, nsplit)), block(64);
+  if (!b.offsets)
+    hipLaunchKernelGGL((k_bf16w<2, false, true>), grid, block, 0, st, b, nsplit, n_mt, a.h, a.d,
+                       hb, w, f);
+  else
+    hipLaunchKernelGGL((k_bf16w<2, false, false>), grid, block, 0, st, b, nsplit, n_mt, a.h, a.d,
+                       hb, w, f);
+  return hipGetLastError();
+}
+
+}  // namespace mm

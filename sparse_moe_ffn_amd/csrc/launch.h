@@ -73,7 +73,14 @@ constexpr int64_t kGemvMaxRowsDense = 64;
 // dimension is a multiple of 128.
 constexpr int64_t kMfmaMinRows = 256;
 constexpr int kMfmaK = 128;
-// Floating-point forms: bf16 = false uses FP32 operands, true uses BF16.
+// BF16 weights on the bf16 matrix cores (k_bf16.hip): gate/up takes the
+// token rows already rounded to BF16 (xb [T][d]) and writes BF16 hidden rows
+// [rows][h]; down writes f [rows][d] FP32.
+hipError_t launch_gateup_bf16_mfma(const ExpertArgs& a, const uint16_t* xb, const uint16_t* w,
+                                   uint16_t* h_out, hipStream_t st);
+hipError_t launch_down_bf16_mfma(const ExpertArgs& a, const uint16_t* hb, const uint16_t* w,
+                                 float* f, hipStream_t st);
+// Floating-point row-tile forms: bf16 = false uses FP32 operands, true uses BF16.
 hipError_t launch_gateup_fp(const ExpertArgs& a, bool bf16, const void* x, const void* w,
                             void* h_out, hipStream_t st);
 hipError_t launch_down_fp(const ExpertArgs& a, bool bf16, const void* hrow, const void* w,

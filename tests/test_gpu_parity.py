@@ -207,6 +207,9 @@ CASES = [
     ("m_prefill", 200, {}),
     ("l_prefill", 130, {}),
     ("l_prefill_bf16", 64, {}),
+    ("l_prefill_bf16", 300, {}),                          # bf16 matrix cores, many row tiles
+    ("l_decode_bf16", 1, {}),
+    ("s_prefill", 200, {"wfmt": "bf16"}),
     ("s_prefill", 64, {"E": 8, "k": 2, "d": 128, "h": 64, "hs": 64}),
     ("s_prefill", 16, {"E": 1, "k": 1, "hs": 0}),
     ("s_prefill", 8, {}),                                 # decode batch
