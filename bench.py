@@ -41,6 +41,11 @@ def parse():
                     help="distinct weight sets rotated across steps (0: enough to exceed the 256 MB MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="issue the calls eagerly instead of replaying graphs")
+    ap.add_argument("--path", choices=("auto", "fused", "calls"), default="auto",
+                    help="fused: the one-call layer (mm_moe_forward, one stream, fewest launches); "
+                         "calls: the seven calls with the activation quantiser and shared expert on "
+                         "a second stream; auto: fused for decode, calls for prefill (the faster "
+                         "of the two on each)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 launches) and exit: the "
@@ -174,15 +179,20 @@ def main():
     xs = [torch.from_numpy(wl.tokens(w, step=s)).to(dev) for s in range(n_inputs)]
     nxt = torch.empty((T, w.d), dtype=torch.float32, device=dev)
 
+    fused = args.path == "fused" or (args.path == "auto" and decode)
+
+    def fwd(L, src):
+        return L.forward_fused(src) if fused else L.forward(src)
+
     def eager_step(s: int):
         if decode:
             cur = xs[s % n_inputs]
             for L in layers:
-                y = L.forward(cur)
+                y = fwd(L, cur)
                 B.rmsnorm_f32(T, w.d, 1e-5, y, nxt)
                 cur = nxt
         else:
-            layers[s % n_inst].forward(xs[0])
+            fwd(layers[s % n_inst], xs[0])
 
     # The step is replayed from HIP graphs (one per weight set; for the decode
     # stack one graph for all layers): launches are recorded once.  The decode
@@ -204,7 +214,7 @@ def main():
             def stack(src):
                 cur = src
                 for L in layers:
-                    y = L.forward(cur)
+                    y = fwd(L, cur)
                     B.rmsnorm_f32(T, w.d, 1e-5, y, nxt)
                     cur = nxt
 
@@ -220,7 +230,7 @@ def main():
                 graphs[0].replay()
         else:
             for L in layers:
-                graphs.append(L.capture(xs[0]))
+                graphs.append(L.capture(xs[0], fused=fused))
 
             def step(s: int):
                 graphs[s % n_inst].replay()
@@ -365,7 +375,8 @@ def main():
         "config": {"workload": w.name, "mode": w.mode, "tokens_per_step": T, "d_model": w.d,
                    "experts": w.E, "top_k": w.k, "hidden": w.h, "shared_hidden": w.hs,
                    "weights": w.wfmt, "layers": w.layers, "router_bias": w.bias,
-                   "weight_sets_rotated": n_inst, "parallelism": "single GPU"},
+                   "weight_sets_rotated": n_inst, "parallelism": "single GPU",
+                   "path": "mm_moe_forward (one call)" if fused else "seven calls, shared expert on a second stream"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "layer_int8_frac": round(total_ops / (ms * 1e-3) / 1e12 / INT8_MFMA_PEAK_TOPS, 5)

@@ -87,7 +87,8 @@ enum {
   MM_WS_GATEUP = 1,
   MM_WS_DOWN = 2,
   MM_WS_SHARED = 3,
-  MM_WS_MAX = 4      /* the largest of the above: one buffer serves every call */
+  MM_WS_MAX = 4,     /* the largest of the above: one buffer serves every call */
+  MM_WS_FORWARD = 5  /* mm_moe_forward: every intermediate of the layer */
 };
 
 typedef struct mm_layer_desc {
@@ -264,6 +265,28 @@ mm_status mm_shared_expert(const mm_layer_desc* desc, int64_t T, const void* act
 mm_status mm_combine(const mm_layer_desc* desc, int64_t T, const float* f,
                      const int32_t* inv_perm, const float* topk_w, const float* ys, void* y,
                      void* stream);
+
+/*
+ * The whole layer in one call: eq. (*) (section "MoE preliminaries and three
+ * design factors"), the seven calls above in order with the same arithmetic
+ * and bit-identical results, issued as fewer launches on one stream.  The
+ * router pass also quantises x (INT4 weights), and the routed and shared
+ * products of each kind share one launch, as do their hidden-row quantisers.
+ *   x                  device FP32 [T][d]
+ *   w_router, bias     as mm_router_topk (bias may be NULL)
+ *   w_gateup, w_down   routed experts, as mm_expert_gateup_swiglu / mm_expert_down
+ *   ws_gateup, ws_down shared expert; ignored (may be zero) when shared_hidden == 0
+ *   topk_idx, topk_w   out: device int32 / FP32 [T][k], as mm_router_topk
+ *   y                  out: device [T][d], FP32 or BF16 per desc->out_dtype
+ *   ws / ws_bytes      mm_workspace_bytes(desc, T, MM_WS_FORWARD): the routing
+ *                      tables, quantised rows and expert outputs of the call
+ * Errors as the individual calls; nothing is queued when a check fails.
+ */
+mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
+                         const float* w_router, const float* bias, mm_weight w_gateup,
+                         mm_weight w_down, mm_weight ws_gateup, mm_weight ws_down,
+                         int32_t* topk_idx, float* topk_w, void* y, void* ws, size_t ws_bytes,
+                         void* stream);
 
 /* --------------------------------------------------- around the layer */
 

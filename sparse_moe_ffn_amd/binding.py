@@ -19,7 +19,7 @@ MM_OK, MM_ERR_NULL, MM_ERR_SHAPE, MM_ERR_ALIGN, MM_ERR_FORMAT, MM_ERR_WORKSPACE,
 MM_W_F32, MM_W_INT4G32, MM_W_BF16 = range(3)
 MM_GATE_SOFTMAX, MM_GATE_SIGMOID_NORM = range(2)
 MM_OUT_F32, MM_OUT_BF16 = range(2)
-MM_WS_ROUTE, MM_WS_GATEUP, MM_WS_DOWN, MM_WS_SHARED, MM_WS_MAX = range(5)
+MM_WS_ROUTE, MM_WS_GATEUP, MM_WS_DOWN, MM_WS_SHARED, MM_WS_MAX, MM_WS_FORWARD = range(6)
 
 WFMT = {"f32": MM_W_F32, "int4g32": MM_W_INT4G32, "bf16": MM_W_BF16}
 
@@ -29,7 +29,7 @@ EXPORTS = (
     "mm_quantize_int4g32", "mm_prepacked_bytes", "mm_prepacked_scale_bytes", "mm_prepack_int4g32",
     "mm_convert_bf16", "mm_router_topk", "mm_route_permute", "mm_act_quant_i8",
     "mm_expert_gateup_swiglu", "mm_expert_down", "mm_shared_expert", "mm_combine",
-    "mm_rmsnorm_f32", "mm_expert_gateup_swiglu_dbg", "mm_expert_down_dbg",
+    "mm_rmsnorm_f32", "mm_expert_gateup_swiglu_dbg", "mm_expert_down_dbg", "mm_moe_forward",
 )
 
 
@@ -80,6 +80,8 @@ _SIGS = {
     "mm_shared_expert": ([_DESC, _I64, _VP, _VP, Weight, Weight, _VP, _VP, _SZ, _VP], ctypes.c_int),
     "mm_combine": ([_DESC, _I64, _VP, _VP, _VP, _VP, _VP, _VP], ctypes.c_int),
     "mm_rmsnorm_f32": ([_I64, _I64, _F, _VP, _VP, _VP], ctypes.c_int),
+    "mm_moe_forward": ([_DESC, _I64, _VP, _VP, _VP, Weight, Weight, Weight, Weight, _VP, _VP, _VP,
+                        _VP, _SZ, _VP], ctypes.c_int),
 }
 
 _lib = None
@@ -209,6 +211,14 @@ def shared_expert(ds, T, act, act_scale, w_gateup, w_down, ys, ws, ws_bytes, str
 def combine(ds, T, f, inv_perm, topk_w, ys, y, stream=None):
     _check(load().mm_combine(ctypes.byref(ds), T, _ptr(f), _ptr(inv_perm), _ptr(topk_w), _ptr(ys),
                              _ptr(y), _stream(stream)), "mm_combine")
+
+
+def moe_forward(ds, T, x, w_router, bias, w_gu, w_d, ws_gu, ws_d, topk_idx, topk_w, y, ws,
+                ws_bytes, stream=None):
+    """The whole layer in one call (routed + shared experts, combine)."""
+    _check(load().mm_moe_forward(ctypes.byref(ds), T, _ptr(x), _ptr(w_router), _ptr(bias), w_gu,
+                                 w_d, ws_gu, ws_d, _ptr(topk_idx), _ptr(topk_w), _ptr(y), _ptr(ws),
+                                 ws_bytes, _stream(stream)), "mm_moe_forward")
 
 
 def rmsnorm_f32(rows, cols, eps, x, y, stream=None):

@@ -95,6 +95,40 @@ SharedWs shared_ws(const mm_layer_desc* d, int64_t T) {
   return w;
 }
 
+// mm_moe_forward workspace carve-up.
+struct FwdWs {
+  size_t off, perm, inv, route, xq, sx, xb, a_r, q_r, s_r, f, a_s, q_s, s_s, ys, total;
+};
+FwdWs fwd_ws(const mm_layer_desc* d, int64_t T) {
+  const int64_t Tk = T * d->top_k, h = d->hidden, hs = d->shared_hidden, dm = d->d_model;
+  const bool i4 = d->wfmt == MM_W_INT4G32, bf = d->wfmt == MM_W_BF16;
+  const int64_t hb = i4 ? 4 : (bf ? 2 : 4);  // bytes per hidden value before the down product
+  FwdWs w{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  w.off = take((size_t)(d->n_experts + 1) * 4);
+  w.perm = take((size_t)Tk * 4);
+  w.inv = take((size_t)Tk * 4);
+  w.route = take((size_t)mm::route_blocks(Tk) * d->n_experts * 4);
+  w.xq = take(i4 ? (size_t)T * dm : 0);
+  w.sx = take(i4 ? (size_t)T * 4 : 0);
+  w.xb = take(bf ? (size_t)T * dm * 2 : 0);
+  w.a_r = take((size_t)Tk * h * hb);
+  w.q_r = take(i4 ? (size_t)Tk * h : 0);
+  w.s_r = take(i4 ? (size_t)Tk * 4 : 0);
+  w.f = take((size_t)Tk * dm * 4);
+  w.a_s = take((size_t)T * hs * hb);
+  w.q_s = take(i4 ? (size_t)T * hs : 0);
+  w.s_s = take(i4 ? (size_t)T * 4 : 0);
+  w.ys = take(hs ? (size_t)T * dm * 4 : 0);
+  w.total = o;
+  return w;
+}
+
 size_t ws_bytes(const mm_layer_desc* d, int64_t T, int32_t which) {
   const int64_t Tk = T * d->top_k;
   switch (which) {
@@ -113,6 +147,8 @@ size_t ws_bytes(const mm_layer_desc* d, int64_t T, int32_t which) {
       for (int i = 0; i < MM_WS_MAX; ++i) m = std::max(m, ws_bytes(d, T, i));
       return m;
     }
+    case MM_WS_FORWARD:
+      return fwd_ws(d, T).total;
     default:
       return 0;
   }
@@ -148,8 +184,11 @@ bool use_gemv(const mm::ExpertArgs& a, int K, bool gateup) {
   return a.rows <= lim && mm::gemv_i4_fits(K, gateup);
 }
 
+// Matrix cores: routed from 256 rows; dense (shared expert) beyond the
+// weight-streaming range.
 bool use_mfma(const mm::ExpertArgs& a, int K) {
-  return a.rows >= mm::kMfmaMinRows && K % mm::kMfmaK == 0;
+  const int64_t lo = a.offsets ? mm::kMfmaMinRows : mm::kGemvMaxRowsDense + 1;
+  return a.rows >= lo && K % mm::kMfmaK == 0;
 }
 
 // hq == nullptr: the FP32 rows in abuf are the output (no re-quantisation).
@@ -255,7 +294,8 @@ mm_status mm_router_topk(const mm_layer_desc* desc, int64_t T, const float* x,
   MM_REQUIRE(topk_idx);
   MM_REQUIRE(topk_w);
   return hip_status(mm::launch_router(T, desc->d_model, desc->n_experts, desc->top_k, desc->gating,
-                                      x, w_router, bias, topk_idx, topk_w, S(stream)),
+                                      x, w_router, bias, topk_idx, topk_w, nullptr, nullptr,
+                                      S(stream)),
                     "mm_router_topk");
 }
 
@@ -464,6 +504,128 @@ mm_status mm_combine(const mm_layer_desc* desc, int64_t T, const float* f,
   return hip_status(mm::launch_combine(T, desc->d_model, desc->top_k, f, inv_perm, topk_w, ys, y,
                                        desc->out_dtype == MM_OUT_BF16, S(stream)),
                     "mm_combine");
+}
+
+mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
+                         const float* w_router, const float* bias, mm_weight w_gateup,
+                         mm_weight w_down, mm_weight ws_gateup, mm_weight ws_down,
+                         int32_t* topk_idx, float* topk_w, void* y, void* ws, size_t ws_size,
+                         void* stream) {
+  MM_TRY(check_desc(desc));
+  MM_TRY(check_T(desc, T));
+  if (T == 0) return MM_OK;
+  MM_REQUIRE(x);
+  MM_REQUIRE(w_router);
+  MM_OPTIONAL(bias);
+  MM_REQUIRE(topk_idx);
+  MM_REQUIRE(topk_w);
+  MM_REQUIRE(y);
+  MM_REQUIRE(ws);
+  MM_TRY(check_weight(desc, w_gateup, "w_gateup"));
+  MM_TRY(check_weight(desc, w_down, "w_down"));
+  const bool shared = desc->shared_hidden > 0;
+  if (shared) {
+    MM_TRY(check_weight(desc, ws_gateup, "ws_gateup"));
+    MM_TRY(check_weight(desc, ws_down, "ws_down"));
+  }
+  const FwdWs W = fwd_ws(desc, T);
+  if (ws_size < W.total)
+    return fail(MM_ERR_WORKSPACE, "forward workspace too small (need %lld bytes)", (long long)W.total);
+  char* base = static_cast<char*>(ws);
+  auto at = [&](size_t off) { return static_cast<void*>(base + off); };
+  const int d = desc->d_model, E = desc->n_experts, k = desc->top_k;
+  const int h = desc->hidden, hs = desc->shared_hidden;
+  const int64_t Tk = T * k;
+  int32_t* off = static_cast<int32_t*>(at(W.off));
+  int32_t* perm = static_cast<int32_t*>(at(W.perm));
+  int32_t* inv = static_cast<int32_t*>(at(W.inv));
+  float* f = static_cast<float*>(at(W.f));
+  float* ys = shared ? static_cast<float*>(at(W.ys)) : nullptr;
+  const mm::ExpertArgs ar{Tk, T, d, h, E, k, perm, off};
+  const mm::ExpertArgs as{T, T, d, hs, 1, 1, nullptr, nullptr};
+  hipStream_t st = S(stream);
+  const char* where = "mm_moe_forward";
+  const bool i4 = desc->wfmt == MM_W_INT4G32;
+  int8_t* xq = i4 ? static_cast<int8_t*>(at(W.xq)) : nullptr;
+  float* sx = i4 ? static_cast<float*>(at(W.sx)) : nullptr;
+
+  // router + top-k (+ per-token INT8 of x), then the count sort
+  MM_TRY(hip_status(mm::launch_router(T, d, E, k, desc->gating, x, w_router, bias, topk_idx, topk_w,
+                                      xq, sx, st),
+                    where));
+  MM_TRY(hip_status(mm::launch_route(Tk, E, topk_idx, off, perm, inv,
+                                     static_cast<int32_t*>(at(W.route)), st),
+                    where));
+  if (i4) {
+    const uint8_t* gq = static_cast<const uint8_t*>(w_gateup.data);
+    const uint8_t* dq = static_cast<const uint8_t*>(w_down.data);
+    const uint8_t* sgq = static_cast<const uint8_t*>(ws_gateup.data);
+    const uint8_t* sdq = static_cast<const uint8_t*>(ws_down.data);
+    float* a_r = static_cast<float*>(at(W.a_r));
+    float* a_s = static_cast<float*>(at(W.a_s));
+    int8_t* q_r = static_cast<int8_t*>(at(W.q_r));
+    int8_t* q_s = static_cast<int8_t*>(at(W.q_s));
+    float* s_r = static_cast<float*>(at(W.s_r));
+    float* s_s = static_cast<float*>(at(W.s_s));
+    // gate/up (+ SwiGLU) of both kinds, then their hidden-row quantisers
+    const bool gv = use_gemv(ar, d, true) && (!shared || use_gemv(as, d, true));
+    const bool gm = use_mfma(ar, d) && (!shared || use_mfma(as, d));
+    if (shared && gv) {
+      MM_TRY(hip_status(mm::launch_gateup_i4_gemv_pair(ar, as, xq, sx, gq, w_gateup.scales, sgq,
+                                                       ws_gateup.scales, a_r, a_s, st), where));
+      MM_TRY(hip_status(mm::launch_act_quant_i8_pair(Tk, h, a_r, q_r, s_r, T, hs, a_s, q_s, s_s, st),
+                        where));
+    } else if (shared && gm && !use_gemv(ar, d, true)) {
+      MM_TRY(hip_status(mm::launch_gateup_i4_mfma_pair(ar, as, xq, sx, gq, w_gateup.scales, sgq,
+                                                       ws_gateup.scales, a_r, a_s, st), where));
+      MM_TRY(hip_status(mm::launch_act_quant_i8_pair(Tk, h, a_r, q_r, s_r, T, hs, a_s, q_s, s_s, st),
+                        where));
+    } else {
+      MM_TRY(hip_status(gateup_i4(ar, xq, sx, gq, w_gateup.scales, a_r, q_r, s_r, nullptr, st), where));
+      if (shared)
+        MM_TRY(hip_status(gateup_i4(as, xq, sx, sgq, ws_gateup.scales, a_s, q_s, s_s, nullptr, st),
+                          where));
+    }
+    // down of both kinds
+    const bool dv = use_gemv(ar, h, false) && (!shared || use_gemv(as, hs, false));
+    const bool dm = use_mfma(ar, h) && (!shared || use_mfma(as, hs));
+    if (shared && dv) {
+      MM_TRY(hip_status(mm::launch_down_i4_gemv_pair(ar, as, q_r, s_r, q_s, s_s, dq, w_down.scales,
+                                                     sdq, ws_down.scales, f, ys, st), where));
+    } else if (shared && dm && !use_gemv(ar, h, false)) {
+      MM_TRY(hip_status(mm::launch_down_i4_mfma_pair(ar, as, q_r, s_r, q_s, s_s, dq, w_down.scales,
+                                                     sdq, ws_down.scales, f, ys, st), where));
+    } else {
+      MM_TRY(hip_status(down_i4(ar, q_r, s_r, dq, w_down.scales, f, nullptr, st), where));
+      if (shared)
+        MM_TRY(hip_status(down_i4(as, q_s, s_s, sdq, ws_down.scales, ys, nullptr, st), where));
+    }
+  } else if (desc->wfmt == MM_W_BF16) {
+    uint16_t* xb = static_cast<uint16_t*>(at(W.xb));
+    uint16_t* h_r = static_cast<uint16_t*>(at(W.a_r));
+    uint16_t* h_s = static_cast<uint16_t*>(at(W.a_s));
+    MM_TRY(hip_status(mm::launch_convert_bf16(T * d, x, xb, st), where));
+    MM_TRY(hip_status(mm::launch_gateup_bf16_mfma(ar, xb, static_cast<const uint16_t*>(w_gateup.data),
+                                                  h_r, st), where));
+    if (shared)
+      MM_TRY(hip_status(mm::launch_gateup_bf16_mfma(as, xb, static_cast<const uint16_t*>(ws_gateup.data),
+                                                    h_s, st), where));
+    MM_TRY(hip_status(mm::launch_down_bf16_mfma(ar, h_r, static_cast<const uint16_t*>(w_down.data), f,
+                                                st), where));
+    if (shared)
+      MM_TRY(hip_status(mm::launch_down_bf16_mfma(as, h_s, static_cast<const uint16_t*>(ws_down.data),
+                                                  ys, st), where));
+  } else {
+    void* h_r = at(W.a_r);
+    void* h_s = at(W.a_s);
+    MM_TRY(hip_status(mm::launch_gateup_fp(ar, false, x, w_gateup.data, h_r, st), where));
+    if (shared) MM_TRY(hip_status(mm::launch_gateup_fp(as, false, x, ws_gateup.data, h_s, st), where));
+    MM_TRY(hip_status(mm::launch_down_fp(ar, false, h_r, w_down.data, f, st), where));
+    if (shared) MM_TRY(hip_status(mm::launch_down_fp(as, false, h_s, ws_down.data, ys, st), where));
+  }
+  return hip_status(mm::launch_combine(T, d, k, f, inv, topk_w, ys, y,
+                                       desc->out_dtype == MM_OUT_BF16, st),
+                    where);
 }
 
 mm_status mm_rmsnorm_f32(int64_t rows, int64_t cols, float eps, const float* x, float* y,

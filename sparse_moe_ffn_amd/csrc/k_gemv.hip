@@ -20,6 +20,8 @@
 // The exact int32 group sums go to LDS; then one thread per (row, output)
 // applies the scales in group order.  Only experts that own rows have tiles,
 // so only the selected experts' weights are read.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -65,19 +67,34 @@ __device__ __forceinline__ void dot16x2(const uint4& w, const int4& x, int& p0, 
   p1 = __builtin_amdgcn_sdot4((int)h3, x.w, s, false);
 }
 
-// out: gate/up -> a = SiLU(g * s) * (u * s) into out [rows][h];
-//      down    -> f = acc * s into out [rows][N].
-// K: reduction length (multiple of 64, <= 2560); RB: 32-row weight blocks per
-// output (gate/up: h / 32, down: N / 32).
-// kDense: rows are the tokens in order (shared expert); otherwise routed.
+// Arguments of one weight-streaming product (a launch carries one, or the
+// routed and the shared problem together).
+struct GemvProb {
+  ExpertArgs a;
+  int K, N, RB;
+  const int8_t* act;
+  const float* act_scale;
+  const uint8_t* wq;
+  const float* wsc;
+  float* out;
+  int32_t* isum;
+};
+
+// Block `blk` of problem P.  out: gate/up -> a = SiLU(g * s) * (u * s) into
+// out [rows][h]; down -> f = acc * s into out [rows][N].  K: reduction length
+// (multiple of 64, <= 2560); RB: 32-row weight blocks per output (gate/up:
+// h / 32, down: N / 32).  kDense: rows are the tokens in order (shared
+// expert); otherwise routed.  Called by the whole workgroup.
 template <int kR, bool kGateUp, bool kCapture, bool kDense>
-__global__ __launch_bounds__(256) void k_gemv_i4(ExpertArgs a, int K, int N, int RB,
-                                                 const int8_t* __restrict__ act,
-                                                 const float* __restrict__ act_scale,
-                                                 const uint8_t* __restrict__ wq,
-                                                 const float* __restrict__ wsc,
-                                                 float* __restrict__ out,
-                                                 int32_t* __restrict__ isum) {
+__device__ __forceinline__ void gemv_block(const GemvProb& P, int blk) {
+  const ExpertArgs& a = P.a;
+  const int K = P.K, N = P.N, RB = P.RB;
+  const int8_t* __restrict__ act = P.act;
+  const float* __restrict__ act_scale = P.act_scale;
+  const uint8_t* __restrict__ wq = P.wq;
+  const float* __restrict__ wsc = P.wsc;
+  float* __restrict__ out = P.out;
+  int32_t* __restrict__ isum = P.isum;
   constexpr int kM = kGateUp ? 2 : 1;  // weight blocks per workgroup
   const int G = K / kGroup, GP = G / 2;
   extern __shared__ int4 smem4[];
@@ -87,7 +104,7 @@ __global__ __launch_bounds__(256) void k_gemv_i4(ExpertArgs a, int K, int N, int
   __shared__ int s_src[kR];
   __shared__ float s_as[kR];
 
-  const int tile = (int)blockIdx.x / RB, rbo = (int)blockIdx.x % RB;
+  const int tile = blk / RB, rbo = blk % RB;
   int p0, n, e;
   gemv_tile<kR, kDense>(a, tile, p0, n, e);
   if (n <= 0) return;
@@ -195,6 +212,20 @@ __global__ __launch_bounds__(256) void k_gemv_i4(ExpertArgs a, int K, int N, int
   }
 }
 
+template <int kR, bool kGateUp, bool kCapture, bool kDense>
+__global__ __launch_bounds__(256) void k_gemv_i4(GemvProb P) {
+  gemv_block<kR, kGateUp, kCapture, kDense>(P, (int)blockIdx.x);
+}
+
+// Routed (P0, the first n0 blocks) and shared (P1) products in one launch.
+template <int kR, bool kGateUp>
+__global__ __launch_bounds__(256) void k_gemv_i4_pair(GemvProb P0, GemvProb P1, int n0) {
+  if ((int)blockIdx.x < n0)
+    gemv_block<kR, kGateUp, false, false>(P0, (int)blockIdx.x);
+  else
+    gemv_block<kR, kGateUp, false, true>(P1, (int)blockIdx.x - n0);
+}
+
 constexpr int kRGemv = 4;
 
 size_t gemv_lds(int K, bool gateup) {
@@ -207,6 +238,40 @@ unsigned gemv_tiles(const ExpertArgs& a) {
   return (unsigned)(a.offsets ? base + a.E : base);
 }
 
+GemvProb gemv_gateup_prob(const ExpertArgs& a, const int8_t* xq, const float* sx,
+                          const uint8_t* wq, const float* ws, float* a_buf, int32_t* isum) {
+  return GemvProb{a, a.d, 2 * a.h, a.h / 32, xq, sx, wq, ws, a_buf, isum};
+}
+
+GemvProb gemv_down_prob(const ExpertArgs& a, const int8_t* hq, const float* hs,
+                        const uint8_t* wq, const float* ws, float* f, int32_t* isum) {
+  ExpertArgs b = a;
+  b.perm = nullptr;
+  return GemvProb{b, a.h, a.d, a.d / 32, hq, hs, wq, ws, f, isum};
+}
+
+template <bool kGateUp>
+hipError_t launch_gemv(const GemvProb& P, hipStream_t st) {
+  const dim3 grid(gemv_tiles(P.a) * P.RB);
+  const size_t lds = gemv_lds(P.K, kGateUp);
+  if (!P.a.offsets)
+    hipLaunchKernelGGL((k_gemv_i4<kRGemv, kGateUp, false, true>), grid, dim3(256), lds, st, P);
+  else if (P.isum)
+    hipLaunchKernelGGL((k_gemv_i4<kRGemv, kGateUp, true, false>), grid, dim3(256), lds, st, P);
+  else
+    hipLaunchKernelGGL((k_gemv_i4<kRGemv, kGateUp, false, false>), grid, dim3(256), lds, st, P);
+  return hipGetLastError();
+}
+
+template <bool kGateUp>
+hipError_t launch_gemv_pair(const GemvProb& R, const GemvProb& D, hipStream_t st) {
+  const unsigned n0 = gemv_tiles(R.a) * R.RB, n1 = gemv_tiles(D.a) * D.RB;
+  const size_t lds = std::max(gemv_lds(R.K, kGateUp), gemv_lds(D.K, kGateUp));
+  hipLaunchKernelGGL((k_gemv_i4_pair<kRGemv, kGateUp>), dim3(n0 + n1), dim3(256), lds, st, R, D,
+                     (int)n0);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool gemv_i4_fits(int K, bool gateup) {
@@ -216,39 +281,30 @@ bool gemv_i4_fits(int K, bool gateup) {
 hipError_t launch_gateup_i4_gemv(const ExpertArgs& a, const int8_t* xq, const float* sx,
                                  const uint8_t* wq, const float* ws, float* a_buf, int32_t* isum,
                                  hipStream_t st) {
-  const int RB = a.h / 32;
-  const dim3 grid(gemv_tiles(a) * RB);
-  const size_t lds = gemv_lds(a.d, true);
-  if (!a.offsets)
-    hipLaunchKernelGGL((k_gemv_i4<kRGemv, true, false, true>), grid, dim3(256), lds, st, a, a.d,
-                       2 * a.h, RB, xq, sx, wq, ws, a_buf, nullptr);
-  else if (isum)
-    hipLaunchKernelGGL((k_gemv_i4<kRGemv, true, true, false>), grid, dim3(256), lds, st, a, a.d, 2 * a.h,
-                       RB, xq, sx, wq, ws, a_buf, isum);
-  else
-    hipLaunchKernelGGL((k_gemv_i4<kRGemv, true, false, false>), grid, dim3(256), lds, st, a, a.d, 2 * a.h,
-                       RB, xq, sx, wq, ws, a_buf, isum);
-  return hipGetLastError();
+  return launch_gemv<true>(gemv_gateup_prob(a, xq, sx, wq, ws, a_buf, isum), st);
 }
 
 hipError_t launch_down_i4_gemv(const ExpertArgs& a, const int8_t* hq, const float* hs,
                                const uint8_t* wq, const float* ws, float* f, int32_t* isum,
                                hipStream_t st) {
-  ExpertArgs b = a;
-  b.perm = nullptr;
-  const int RB = a.d / 32;
-  const dim3 grid(gemv_tiles(b) * RB);
-  const size_t lds = gemv_lds(a.h, false);
-  if (!b.offsets)
-    hipLaunchKernelGGL((k_gemv_i4<kRGemv, false, false, true>), grid, dim3(256), lds, st, b, a.h,
-                       a.d, RB, hq, hs, wq, ws, f, nullptr);
-  else if (isum)
-    hipLaunchKernelGGL((k_gemv_i4<kRGemv, false, true, false>), grid, dim3(256), lds, st, b, a.h, a.d, RB,
-                       hq, hs, wq, ws, f, isum);
-  else
-    hipLaunchKernelGGL((k_gemv_i4<kRGemv, false, false, false>), grid, dim3(256), lds, st, b, a.h, a.d,
-                       RB, hq, hs, wq, ws, f, isum);
-  return hipGetLastError();
+  return launch_gemv<false>(gemv_down_prob(a, hq, hs, wq, ws, f, isum), st);
+}
+
+hipError_t launch_gateup_i4_gemv_pair(const ExpertArgs& ar, const ExpertArgs& as,
+                                      const int8_t* xq, const float* sx, const uint8_t* wq_r,
+                                      const float* ws_r, const uint8_t* wq_s, const float* ws_s,
+                                      float* abuf_r, float* abuf_s, hipStream_t st) {
+  return launch_gemv_pair<true>(gemv_gateup_prob(ar, xq, sx, wq_r, ws_r, abuf_r, nullptr),
+                                gemv_gateup_prob(as, xq, sx, wq_s, ws_s, abuf_s, nullptr), st);
+}
+
+hipError_t launch_down_i4_gemv_pair(const ExpertArgs& ar, const ExpertArgs& as,
+                                    const int8_t* hq_r, const float* hs_r, const int8_t* hq_s,
+                                    const float* hs_s, const uint8_t* wq_r, const float* ws_r,
+                                    const uint8_t* wq_s, const float* ws_s, float* f, float* ys,
+                                    hipStream_t st) {
+  return launch_gemv_pair<false>(gemv_down_prob(ar, hq_r, hs_r, wq_r, ws_r, f, nullptr),
+                                 gemv_down_prob(as, hq_s, hs_s, wq_s, ws_s, ys, nullptr), st);
 }
 
 }  // namespace mm

@@ -127,21 +127,43 @@ __device__ __forceinline__ void wcompute(v16f (&acc)[kMT][kNT], const WStage<kMT
   }
 }
 
-// kDense: rows are the tokens in order (shared expert); otherwise routed
-// (expert-sorted rows, tiles found from the offsets).  K % 128 == 0.
+// Arguments of one W4A8 product; a launch carries one, or two (the routed
+// experts and the shared expert) in the merged form.
+struct W4A8Prob {
+  ExpertArgs a;
+  int nsplit, K, N;
+  const int8_t* act;
+  const float* act_scale;
+  const uint8_t* wq;
+  const float* wsc;
+  float* out;
+  int32_t* isum;
+};
+
+// Workgroup b runs on XCD b % 8; logical tile ids are handed out so that
+// each XCD works on a contiguous range (same expert's weights in its L2).
+__device__ __forceinline__ int xcd_logical() {
+  const int per = (int)gridDim.x / kXcd;
+  return ((int)blockIdx.x % kXcd) * per + (int)blockIdx.x / kXcd;
+}
+
+// One tile (kMT row tiles x kNT column tiles) of problem P for logical id
+// `logical` = mt * nsplit + split.  kDense: rows are the tokens in order
+// (shared expert); otherwise routed (expert-sorted rows, tiles found from the
+// offsets).  K % 128 == 0.  Called by one whole wave.
 template <int kMT, int kNT, bool kGateUp, bool kCapture, bool kDense>
-__global__ __launch_bounds__(64) void k_w4a8w(ExpertArgs a, int nsplit, int K, int N,
-                                              const int8_t* __restrict__ act,
-                                              const float* __restrict__ act_scale,
-                                              const uint8_t* __restrict__ wq,
-                                              const float* __restrict__ wsc,
-                                              float* __restrict__ out,
-                                              int32_t* __restrict__ isum) {
+__device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int logical) {
   static_assert(!kGateUp || kNT == 2, "gate/up pairs one gate and one up tile");
   constexpr int kBM = 32 * kMT;
+  const ExpertArgs& a = P.a;
+  const int nsplit = P.nsplit, K = P.K, N = P.N;
+  const int8_t* __restrict__ act = P.act;
+  const float* __restrict__ act_scale = P.act_scale;
+  const uint8_t* __restrict__ wq = P.wq;
+  const float* __restrict__ wsc = P.wsc;
+  float* __restrict__ out = P.out;
+  int32_t* __restrict__ isum = P.isum;
   const int lane = threadIdx.x;
-  const int per = (int)gridDim.x / kXcd;
-  const int logical = ((int)blockIdx.x % kXcd) * per + (int)blockIdx.x / kXcd;
   const int mt = logical / nsplit, split = logical % nsplit;
   const int rows = (int)a.rows;
   int p0, n, e;
@@ -240,6 +262,22 @@ __global__ __launch_bounds__(64) void k_w4a8w(ExpertArgs a, int nsplit, int K, i
     }
 }
 
+template <int kMT, bool kGateUp, bool kCapture, bool kDense>
+__global__ __launch_bounds__(64) void k_w4a8w(W4A8Prob P) {
+  w4a8w_tile<kMT, 2, kGateUp, kCapture, kDense>(P, xcd_logical());
+}
+
+// Routed (P0, the first n0 logical tiles) and shared (P1) products of the
+// same kind in one launch.
+template <int kMT0, int kMT1, bool kGateUp>
+__global__ __launch_bounds__(64) void k_w4a8w_pair(W4A8Prob P0, W4A8Prob P1, int n0) {
+  const int l = xcd_logical();
+  if (l < n0)
+    w4a8w_tile<kMT0, 2, kGateUp, false, false>(P0, l);
+  else
+    w4a8w_tile<kMT1, 2, kGateUp, false, true>(P1, l - n0);
+}
+
 // Two row tiles per wave once that still gives at least 4 waves per SIMD
 // (256 CUs x 4 SIMDs): half the weight traffic per MFMA, fewer waves.
 bool two_row_tiles(const ExpertArgs& a, int nsplit) {
@@ -247,11 +285,67 @@ bool two_row_tiles(const ExpertArgs& a, int nsplit) {
   return tiles64 * nsplit >= 4096;
 }
 
-// Grid: 8 * ceil(tiles * nsplit / 8) workgroups, tiles = worst case.
-unsigned grid_for(const ExpertArgs& a, int bm, int nsplit) {
-  const int64_t mt = (a.rows + bm - 1) / bm + (a.offsets ? a.E : 0);
-  const int64_t n = mt * nsplit;
-  return (unsigned)(kXcd * ((n + kXcd - 1) / kXcd));
+// Logical tiles of a problem with bm-row tiles (routed: worst case).
+int64_t n_tiles(const ExpertArgs& a, int bm, int nsplit) {
+  return ((a.rows + bm - 1) / bm + (a.offsets ? a.E : 0)) * nsplit;
+}
+
+unsigned grid_of(int64_t n) { return (unsigned)(kXcd * ((n + kXcd - 1) / kXcd)); }
+
+W4A8Prob gateup_prob(const ExpertArgs& a, const int8_t* xq, const float* sx, const uint8_t* wq,
+                     const float* ws, float* a_buf, int32_t* isum) {
+  return W4A8Prob{a, a.h / 32, a.d, 2 * a.h, xq, sx, wq, ws, a_buf, isum};
+}
+
+W4A8Prob down_prob(const ExpertArgs& a, const int8_t* hq, const float* hs, const uint8_t* wq,
+                   const float* ws, float* f, int32_t* isum) {
+  ExpertArgs b = a;
+  b.perm = nullptr;
+  return W4A8Prob{b, a.d / 64, a.h, a.d, hq, hs, wq, ws, f, isum};
+}
+
+template <bool kGateUp>
+hipError_t launch_prob(const W4A8Prob& P, hipStream_t st) {
+  const dim3 block(64);
+  const ExpertArgs& a = P.a;
+  const bool dense = a.offsets == nullptr;
+  if (P.isum) {  // test twin (routed only): one row tile per wave
+    hipLaunchKernelGGL((k_w4a8w<1, kGateUp, true, false>), dim3(grid_of(n_tiles(a, 32, P.nsplit))),
+                       block, 0, st, P);
+  } else if (two_row_tiles(a, P.nsplit)) {
+    const dim3 grid(grid_of(n_tiles(a, 64, P.nsplit)));
+    if (dense)
+      hipLaunchKernelGGL((k_w4a8w<2, kGateUp, false, true>), grid, block, 0, st, P);
+    else
+      hipLaunchKernelGGL((k_w4a8w<2, kGateUp, false, false>), grid, block, 0, st, P);
+  } else {
+    const dim3 grid(grid_of(n_tiles(a, 32, P.nsplit)));
+    if (dense)
+      hipLaunchKernelGGL((k_w4a8w<1, kGateUp, false, true>), grid, block, 0, st, P);
+    else
+      hipLaunchKernelGGL((k_w4a8w<1, kGateUp, false, false>), grid, block, 0, st, P);
+  }
+  return hipGetLastError();
+}
+
+// Routed problem R and dense problem D in one launch; each keeps the row
+// tiles it would get on its own.
+template <bool kGateUp>
+hipError_t launch_pair(const W4A8Prob& R, const W4A8Prob& D, hipStream_t st) {
+  const dim3 block(64);
+  const bool r2 = two_row_tiles(R.a, R.nsplit), d2 = two_row_tiles(D.a, D.nsplit);
+  const int64_t n0 = n_tiles(R.a, r2 ? 64 : 32, R.nsplit);
+  const int64_t n1 = n_tiles(D.a, d2 ? 64 : 32, D.nsplit);
+  const dim3 grid(grid_of(n0 + n1));
+  if (r2 && d2)
+    hipLaunchKernelGGL((k_w4a8w_pair<2, 2, kGateUp>), grid, block, 0, st, R, D, (int)n0);
+  else if (r2)
+    hipLaunchKernelGGL((k_w4a8w_pair<2, 1, kGateUp>), grid, block, 0, st, R, D, (int)n0);
+  else if (d2)
+    hipLaunchKernelGGL((k_w4a8w_pair<1, 2, kGateUp>), grid, block, 0, st, R, D, (int)n0);
+  else
+    hipLaunchKernelGGL((k_w4a8w_pair<1, 1, kGateUp>), grid, block, 0, st, R, D, (int)n0);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -259,59 +353,30 @@ unsigned grid_for(const ExpertArgs& a, int bm, int nsplit) {
 hipError_t launch_gateup_i4_mfma(const ExpertArgs& a, const int8_t* xq, const float* sx,
                                  const uint8_t* wq, const float* ws, float* a_buf, int32_t* isum,
                                  hipStream_t st) {
-  const int nsplit = a.h / 32;
-  const dim3 block(64);
-  if (isum) {  // test twin: one row tile per wave
-    hipLaunchKernelGGL((k_w4a8w<1, 2, true, true, false>), dim3(grid_for(a, 32, nsplit)), block, 0,
-                       st, a, nsplit, a.d, 2 * a.h, xq, sx, wq, ws, a_buf, isum);
-  } else if (two_row_tiles(a, nsplit)) {
-    const dim3 grid(grid_for(a, 64, nsplit));
-    if (!a.offsets)
-      hipLaunchKernelGGL((k_w4a8w<2, 2, true, false, true>), grid, block, 0, st, a, nsplit, a.d,
-                         2 * a.h, xq, sx, wq, ws, a_buf, nullptr);
-    else
-      hipLaunchKernelGGL((k_w4a8w<2, 2, true, false, false>), grid, block, 0, st, a, nsplit, a.d,
-                         2 * a.h, xq, sx, wq, ws, a_buf, nullptr);
-  } else {
-    const dim3 grid(grid_for(a, 32, nsplit));
-    if (!a.offsets)
-      hipLaunchKernelGGL((k_w4a8w<1, 2, true, false, true>), grid, block, 0, st, a, nsplit, a.d,
-                         2 * a.h, xq, sx, wq, ws, a_buf, nullptr);
-    else
-      hipLaunchKernelGGL((k_w4a8w<1, 2, true, false, false>), grid, block, 0, st, a, nsplit, a.d,
-                         2 * a.h, xq, sx, wq, ws, a_buf, nullptr);
-  }
-  return hipGetLastError();
+  return launch_prob<true>(gateup_prob(a, xq, sx, wq, ws, a_buf, isum), st);
 }
 
 hipError_t launch_down_i4_mfma(const ExpertArgs& a, const int8_t* hq, const float* hs,
                                const uint8_t* wq, const float* ws, float* f, int32_t* isum,
                                hipStream_t st) {
-  ExpertArgs b = a;
-  b.perm = nullptr;
-  const int nsplit = a.d / 64;
-  const dim3 block(64);
-  if (isum) {  // test twin: one row tile per wave
-    hipLaunchKernelGGL((k_w4a8w<1, 2, false, true, false>), dim3(grid_for(b, 32, nsplit)), block, 0,
-                       st, b, nsplit, a.h, a.d, hq, hs, wq, ws, f, isum);
-  } else if (two_row_tiles(b, nsplit)) {
-    const dim3 grid(grid_for(b, 64, nsplit));
-    if (!b.offsets)
-      hipLaunchKernelGGL((k_w4a8w<2, 2, false, false, true>), grid, block, 0, st, b, nsplit, a.h,
-                         a.d, hq, hs, wq, ws, f, nullptr);
-    else
-      hipLaunchKernelGGL((k_w4a8w<2, 2, false, false, false>), grid, block, 0, st, b, nsplit, a.h,
-                         a.d, hq, hs, wq, ws, f, nullptr);
-  } else {
-    const dim3 grid(grid_for(b, 32, nsplit));
-    if (!b.offsets)
-      hipLaunchKernelGGL((k_w4a8w<1, 2, false, false, true>), grid, block, 0, st, b, nsplit, a.h,
-                         a.d, hq, hs, wq, ws, f, nullptr);
-    else
-      hipLaunchKernelGGL((k_w4a8w<1, 2, false, false, false>), grid, block, 0, st, b, nsplit, a.h,
-                         a.d, hq, hs, wq, ws, f, nullptr);
-  }
-  return hipGetLastError();
+  return launch_prob<false>(down_prob(a, hq, hs, wq, ws, f, isum), st);
+}
+
+hipError_t launch_gateup_i4_mfma_pair(const ExpertArgs& ar, const ExpertArgs& as,
+                                      const int8_t* xq, const float* sx, const uint8_t* wq_r,
+                                      const float* ws_r, const uint8_t* wq_s, const float* ws_s,
+                                      float* abuf_r, float* abuf_s, hipStream_t st) {
+  return launch_pair<true>(gateup_prob(ar, xq, sx, wq_r, ws_r, abuf_r, nullptr),
+                           gateup_prob(as, xq, sx, wq_s, ws_s, abuf_s, nullptr), st);
+}
+
+hipError_t launch_down_i4_mfma_pair(const ExpertArgs& ar, const ExpertArgs& as,
+                                    const int8_t* hq_r, const float* hs_r, const int8_t* hq_s,
+                                    const float* hs_s, const uint8_t* wq_r, const float* ws_r,
+                                    const uint8_t* wq_s, const float* ws_s, float* f, float* ys,
+                                    hipStream_t st) {
+  return launch_pair<false>(down_prob(ar, hq_r, hs_r, wq_r, ws_r, f, nullptr),
+                            down_prob(as, hq_s, hs_s, wq_s, ws_s, ys, nullptr), st);
 }
 
 }  // namespace mm

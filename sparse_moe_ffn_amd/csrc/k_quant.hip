@@ -95,15 +95,12 @@ __global__ __launch_bounds__(256) void k_act_quant_i8(int64_t rows, int64_t cols
 }
 
 // Same quantiser, rows with cols % 128 == 0: the row is read once as float2
-// per lane, kept in registers, and written as 2 codes per lane.
+// per lane, kept in registers, and written as 2 codes per lane.  One wave per
+// row r (r < rows).
 template <int kMaxV>
-__global__ __launch_bounds__(256) void k_act_quant_i8_v2(int64_t rows, int64_t cols,
-                                                         const float* __restrict__ x,
-                                                         int8_t* __restrict__ q,
-                                                         float* __restrict__ s) {
+__device__ __forceinline__ void quant_row_v2(int64_t r, int64_t cols, const float* __restrict__ x,
+                                             int8_t* __restrict__ q, float* __restrict__ s) {
   const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
   const int nv = (int)(cols / 128);
   const float2* xr = reinterpret_cast<const float2*>(x + r * cols);
   float2 v[kMaxV];
@@ -128,6 +125,35 @@ __global__ __launch_bounds__(256) void k_act_quant_i8_v2(int64_t rows, int64_t c
       }
       qr[lane + 64 * i] = (uint16_t)((uint8_t)a | ((uint16_t)(uint8_t)b << 8));
     }
+}
+
+template <int kMaxV>
+__global__ __launch_bounds__(256) void k_act_quant_i8_v2(int64_t rows, int64_t cols,
+                                                         const float* __restrict__ x,
+                                                         int8_t* __restrict__ q,
+                                                         float* __restrict__ s) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r < rows) quant_row_v2<kMaxV>(r, cols, x, q, s);
+}
+
+// Two row sets in one launch: blocks [0, nb0) cover set 0, the rest set 1.
+struct QuantRows {
+  int64_t rows, cols;
+  const float* x;
+  int8_t* q;
+  float* s;
+};
+
+template <int kMaxV>
+__global__ __launch_bounds__(256) void k_act_quant_i8_pair(QuantRows A, QuantRows B, int nb0) {
+  const int wave = threadIdx.x >> 6;
+  if ((int)blockIdx.x < nb0) {
+    const int64_t r = (int64_t)blockIdx.x * 4 + wave;
+    if (r < A.rows) quant_row_v2<kMaxV>(r, A.cols, A.x, A.q, A.s);
+  } else {
+    const int64_t r = (int64_t)(blockIdx.x - nb0) * 4 + wave;
+    if (r < B.rows) quant_row_v2<kMaxV>(r, B.cols, B.x, B.q, B.s);
+  }
 }
 
 __global__ __launch_bounds__(256) void k_convert_bf16(int64_t n, const float* __restrict__ x,
@@ -178,6 +204,21 @@ hipError_t launch_act_quant_i8(int64_t rows, int64_t cols, const float* x, int8_
   else
     hipLaunchKernelGGL(k_act_quant_i8, dim3(blocks_for(rows, 4)), dim3(256), 0, st, rows, cols, x,
                        q, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_quant_i8_pair(int64_t rows0, int64_t cols0, const float* x0, int8_t* q0,
+                                    float* s0, int64_t rows1, int64_t cols1, const float* x1,
+                                    int8_t* q1, float* s1, hipStream_t st) {
+  auto fits = [](int64_t c) { return c % 128 == 0 && c <= 128 * 24; };
+  if (!fits(cols0) || !fits(cols1)) {
+    hipError_t e = launch_act_quant_i8(rows0, cols0, x0, q0, s0, st);
+    if (e != hipSuccess) return e;
+    return launch_act_quant_i8(rows1, cols1, x1, q1, s1, st);
+  }
+  const int nb0 = (int)blocks_for(rows0, 4), nb1 = (int)blocks_for(rows1, 4);
+  hipLaunchKernelGGL(k_act_quant_i8_pair<24>, dim3(nb0 + nb1), dim3(256), 0, st,
+                     QuantRows{rows0, cols0, x0, q0, s0}, QuantRows{rows1, cols1, x1, q1, s1}, nb0);
   return hipGetLastError();
 }
 

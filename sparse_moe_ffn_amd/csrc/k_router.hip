@@ -15,7 +15,7 @@ namespace mm {
 namespace {
 
 constexpr int kTok = 4;     // tokens per workgroup (one per wave for the top-k)
-constexpr int kRowStride = 65;  // LDS stride of one row of 64 lane partials (padded)
+constexpr int kRowStride = 17;  // LDS stride of one row of 16 quad sums (padded)
 constexpr int64_t kSmallRouterT = 64;  // up to this many tokens: the one-token-per-workgroup form
 
 // Top-k and gate weights of one token; lane e holds the logit of expert e
@@ -57,21 +57,49 @@ __device__ __forceinline__ void select_topk(float mine, int lane, int E, int k,
   }
 }
 
+// The first two levels of the 64-lane tree (pairs at distance 1, then 2) in
+// registers: every lane of a quad ends with its quad's sum.
+__device__ __forceinline__ float quad_sum(float p) {
+  p = p + dpp<kDppXor1>(p);
+  return p + dpp<kDppXor2>(p);
+}
+
+// Per-token INT8 quantisation of the x row a wave holds in registers (lane l
+// holds columns l, l + 64, ...): the same rule as the row quantiser,
+// s = (2 * max|x|) / 255, q = clamp(rint(x / s)), s = 0 gives q = 0.
+template <int kNX>
+__device__ __forceinline__ void quant_row_regs(const float (&xv)[kNX], int lane, int64_t t,
+                                               int d, int8_t* __restrict__ xq,
+                                               float* __restrict__ sx) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kNX; ++c) amax = fmaxf(amax, fabsf(xv[c]));
+  amax = max64(amax);
+  const float s = (2.0f * amax) / 255.0f;
+  if (lane == 0) sx[t] = s;
+#pragma unroll
+  for (int c = 0; c < kNX; ++c) xq[t * d + lane + kWave * c] = s != 0.0f ? quant_i8(xv[c], s) : (int8_t)0;
+}
+
 // Workgroup = 4 waves and 4 tokens.  Phase 1: wave w takes experts w, w+4,
 // w+8, ... (at most 16); for each one, lane l forms the 4 tokens' partial sums
-// over columns j = l, l+64, ... (fused multiply-adds, ascending j) and stores
-// them to LDS.  Phase 2: lane r of the wave adds the 64 partials of row r
-// (one (token, expert) pair) as the balanced tree, adds the bias and writes
+// over columns j = l, l+64, ... (fused multiply-adds, ascending j), adds them
+// within its quad (the tree's first two levels) and one lane per quad stores
+// the quad sum to LDS.  Phase 2: lane r of the wave finishes the tree over the
+// 16 quad sums of row r (one (token, expert) pair), adds the bias and writes
 // the logit.  Phase 3: wave w takes token w, lane e holding the logit of
 // expert e, and does the top-k and the gate weights.
-// kNX = d / 64 (0: any d, row read from memory in the loop).
-template <int kGating, int kNX>
+// kNX = d / 64 (0: any d, row read from memory in the loop).  kQuant (kNX > 0
+// only): also writes the tokens' INT8 rows xq and scales sx.
+template <int kGating, int kNX, bool kQuant = false>
 __global__ __launch_bounds__(256) void k_router(int64_t T, int d, int E, int k,
                                                 const float* __restrict__ x,
                                                 const float* __restrict__ wr,
                                                 const float* __restrict__ bias,
                                                 int32_t* __restrict__ idx,
-                                                float* __restrict__ w) {
+                                                float* __restrict__ w,
+                                                int8_t* __restrict__ xq = nullptr,
+                                                float* __restrict__ sx = nullptr) {
   __shared__ float s_part[4][16 * kTok][kRowStride];
   __shared__ float s_logit[kTok][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -85,16 +113,23 @@ __global__ __launch_bounds__(256) void k_router(int64_t T, int d, int E, int k,
     for (int q = 0; q < kTok; ++q)
 #pragma unroll
       for (int i = 0; i < kNX; ++i) xv[q][i] = q < nt ? x[(t0 + q) * d + lane + kWave * i] : 0.0f;
-    // expert rows read four ahead (a ring of four register sets); rows past
-    // this wave's last expert re-read expert E-1 (valid, unused)
-    float wv[4][kNX];
+    if constexpr (kQuant) {
+#pragma unroll
+      for (int q = 0; q < kTok; ++q)
+        if (q < nt) quant_row_regs(xv[q], lane, t0 + q, d, xq, sx);
+    }
+    // expert rows read kRing ahead (a ring of register sets: 4 for narrow
+    // rows, 2 for wide ones to keep registers for occupancy); rows past this
+    // wave's last expert re-read expert E-1 (valid, unused)
+    constexpr int kRing = kNX <= 12 ? 4 : 2;
+    float wv[kRing][kNX];
     auto load_row = [&](int i, float (&dst)[kNX]) {
       const float* we = wr + (int64_t)min(wave + 4 * i, E - 1) * d;
 #pragma unroll
       for (int c = 0; c < kNX; ++c) dst[c] = we[lane + kWave * c];
     };
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load_row(i, wv[i]);
+    for (int i = 0; i < kRing; ++i) load_row(i, wv[i]);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (i < ne) {
@@ -102,11 +137,12 @@ __global__ __launch_bounds__(256) void k_router(int64_t T, int d, int E, int k,
         for (int q = 0; q < kTok; ++q) {
           float p = 0.0f;
 #pragma unroll
-          for (int c = 0; c < kNX; ++c) p = __builtin_fmaf(xv[q][c], wv[i % 4][c], p);
-          s_part[wave][i * kTok + q][lane] = p;
+          for (int c = 0; c < kNX; ++c) p = __builtin_fmaf(xv[q][c], wv[i % kRing][c], p);
+          p = quad_sum(p);
+          if ((lane & 3) == 0) s_part[wave][i * kTok + q][lane >> 2] = p;
         }
       }
-      if (i + 4 < 16) load_row(i + 4, wv[i % 4]);
+      if (i + kRing < 16) load_row(i + kRing, wv[i % kRing]);
     }
   } else {
     for (int i = 0; i < ne; ++i) {
@@ -115,7 +151,8 @@ __global__ __launch_bounds__(256) void k_router(int64_t T, int d, int E, int k,
         float p = 0.0f;
         if (q < nt)
           for (int j = lane; j < d; j += kWave) p = __builtin_fmaf(x[(t0 + q) * d + j], we[j], p);
-        s_part[wave][i * kTok + q][lane] = p;
+        p = quad_sum(p);
+        if ((lane & 3) == 0) s_part[wave][i * kTok + q][lane >> 2] = p;
       }
     }
   }
@@ -123,13 +160,13 @@ __global__ __launch_bounds__(256) void k_router(int64_t T, int d, int E, int k,
   // Phase 2: lane r reduces row r = (expert slot i, token q) of its wave.
   if (lane < ne * kTok) {
     const float* row = s_part[wave][lane];
-    float p[64];
+    float p[16];
 #pragma unroll
-    for (int l = 0; l < 64; ++l) p[l] = row[l];
+    for (int l = 0; l < 16; ++l) p[l] = row[l];
 #pragma unroll
-    for (int s2 = 1; s2 < 64; s2 <<= 1)
+    for (int s2 = 1; s2 < 16; s2 <<= 1)
 #pragma unroll
-      for (int l = 0; l < 64; l += 2 * s2) p[l] = p[l] + p[l + s2];
+      for (int l = 0; l < 16; l += 2 * s2) p[l] = p[l] + p[l + s2];
     const int i = lane / kTok, q = lane % kTok;
     const int e = wave + 4 * i;
     s_logit[q][e] = p[0] + (bias ? bias[e] : 0.0f);
@@ -148,10 +185,11 @@ __global__ __launch_bounds__(256) void k_router(int64_t T, int d, int E, int k,
 constexpr int kSmallWaves = 16;
 constexpr int kSmallPer = 4;  // experts per wave (E <= 64)
 
-template <int kGating, int kNX>
+template <int kGating, int kNX, bool kQuant = false>
 __global__ __launch_bounds__(64 * kSmallWaves) void k_router_small(
     int64_t T, int d, int E, int k, const float* __restrict__ x, const float* __restrict__ wr,
-    const float* __restrict__ bias, int32_t* __restrict__ idx, float* __restrict__ w) {
+    const float* __restrict__ bias, int32_t* __restrict__ idx, float* __restrict__ w,
+    int8_t* __restrict__ xq = nullptr, float* __restrict__ sx = nullptr) {
   __shared__ float s_logit[64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t t = blockIdx.x;
@@ -164,6 +202,9 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_router_small(
   }
 #pragma unroll
   for (int c = 0; c < kNX; ++c) xv[c] = x[t * d + lane + kWave * c];
+  if constexpr (kQuant) {
+    if (wave == 0) quant_row_regs(xv, lane, t, d, xq, sx);
+  }
 #pragma unroll
   for (int i = 0; i < kSmallPer; ++i) {
     const int e = wave + kSmallWaves * i;
@@ -180,47 +221,62 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_router_small(
   select_topk<kGating>(mine, lane, E, k, idx + t * k, w + t * k);
 }
 
-template <int kG, int kNX>
+template <int kG, int kNX, bool kQ>
 void launch_router_nx(bool small, int64_t T, int d, int E, int k, const float* x, const float* wr,
-                      const float* bias, int32_t* idx, float* w, hipStream_t st) {
+                      const float* bias, int32_t* idx, float* w, int8_t* xq, float* sx,
+                      hipStream_t st) {
   if constexpr (kNX > 0 && kNX <= 20) {
     if (small) {
-      hipLaunchKernelGGL((k_router_small<kG, kNX>), dim3((unsigned)T), dim3(64 * kSmallWaves), 0,
-                         st, T, d, E, k, x, wr, bias, idx, w);
+      hipLaunchKernelGGL((k_router_small<kG, kNX, kQ>), dim3((unsigned)T), dim3(64 * kSmallWaves),
+                         0, st, T, d, E, k, x, wr, bias, idx, w, xq, sx);
       return;
     }
   }
-  hipLaunchKernelGGL((k_router<kG, kNX>), dim3((unsigned)((T + kTok - 1) / kTok)), dim3(256), 0,
-                     st, T, d, E, k, x, wr, bias, idx, w);
+  hipLaunchKernelGGL((k_router<kG, kNX, kQ>), dim3((unsigned)((T + kTok - 1) / kTok)), dim3(256), 0,
+                     st, T, d, E, k, x, wr, bias, idx, w, xq, sx);
 }
 
-template <int kG>
+// Widths with a register form (d / 64 in the list below) can also quantise
+// x in the same pass (kQ); other widths never get kQ = true.
+template <int kG, bool kQ>
 void launch_router_g(bool small, int64_t T, int d, int E, int k, const float* x, const float* wr,
-                     const float* bias, int32_t* idx, float* w, hipStream_t st) {
+                     const float* bias, int32_t* idx, float* w, int8_t* xq, float* sx,
+                     hipStream_t st) {
   switch (d % kWave == 0 ? d / kWave : 0) {
-    case 4: launch_router_nx<kG, 4>(small, T, d, E, k, x, wr, bias, idx, w, st); break;
-    case 8: launch_router_nx<kG, 8>(small, T, d, E, k, x, wr, bias, idx, w, st); break;
-    case 12: launch_router_nx<kG, 12>(small, T, d, E, k, x, wr, bias, idx, w, st); break;
-    case 16: launch_router_nx<kG, 16>(small, T, d, E, k, x, wr, bias, idx, w, st); break;
-    case 20: launch_router_nx<kG, 20>(small, T, d, E, k, x, wr, bias, idx, w, st); break;
-    case 24: launch_router_nx<kG, 24>(small, T, d, E, k, x, wr, bias, idx, w, st); break;
-    case 32: launch_router_nx<kG, 32>(small, T, d, E, k, x, wr, bias, idx, w, st); break;
-    default: launch_router_nx<kG, 0>(small, T, d, E, k, x, wr, bias, idx, w, st); break;
+    case 4: launch_router_nx<kG, 4, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, st); break;
+    case 8: launch_router_nx<kG, 8, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, st); break;
+    case 12: launch_router_nx<kG, 12, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, st); break;
+    case 16: launch_router_nx<kG, 16, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, st); break;
+    case 20: launch_router_nx<kG, 20, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, st); break;
+    case 24: launch_router_nx<kG, 24, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, st); break;
+    case 32: launch_router_nx<kG, 32, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, st); break;
+    default: launch_router_nx<kG, 0, false>(small, T, d, E, k, x, wr, bias, idx, w, nullptr, nullptr, st); break;
   }
+}
+
+bool router_quant_fused(int d) {
+  const int nx = d % kWave == 0 ? d / kWave : 0;
+  return nx == 4 || nx == 8 || nx == 12 || nx == 16 || nx == 20 || nx == 24 || nx == 32;
 }
 
 }  // namespace
 
 hipError_t launch_router(int64_t T, int d, int E, int k, int gating, const float* x,
                          const float* wr, const float* bias, int32_t* idx, float* w,
-                         hipStream_t st) {
+                         int8_t* xq, float* sx, hipStream_t st) {
   // few tokens: one 16-wave workgroup per token (widths with a register form up to 1280)
   const bool small = T <= kSmallRouterT;
-  if (gating == 0)
-    launch_router_g<0>(small, T, d, E, k, x, wr, bias, idx, w, st);
-  else
-    launch_router_g<1>(small, T, d, E, k, x, wr, bias, idx, w, st);
-  return hipGetLastError();
+  const bool q = xq != nullptr && router_quant_fused(d);
+  if (gating == 0) {
+    if (q) launch_router_g<0, true>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, st);
+    else launch_router_g<0, false>(small, T, d, E, k, x, wr, bias, idx, w, nullptr, nullptr, st);
+  } else {
+    if (q) launch_router_g<1, true>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, st);
+    else launch_router_g<1, false>(small, T, d, E, k, x, wr, bias, idx, w, nullptr, nullptr, st);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || xq == nullptr || q) return e;
+  return launch_act_quant_i8(T, d, x, xq, sx, st);  // widths without the fused form
 }
 
 }  // namespace mm

@@ -14,14 +14,20 @@ hipError_t launch_prepack_int4g32(int64_t n_mat, int64_t rows, int64_t cols, con
                                   const float* sc, uint8_t* qo, float* so, hipStream_t st);
 hipError_t launch_act_quant_i8(int64_t rows, int64_t cols, const float* x, int8_t* q, float* s,
                                hipStream_t st);
+// Two row sets (e.g. the routed and the shared hidden rows) in one launch.
+hipError_t launch_act_quant_i8_pair(int64_t rows0, int64_t cols0, const float* x0, int8_t* q0,
+                                    float* s0, int64_t rows1, int64_t cols1, const float* x1,
+                                    int8_t* q1, float* s1, hipStream_t st);
 hipError_t launch_convert_bf16(int64_t n, const float* x, uint16_t* y, hipStream_t st);
 hipError_t launch_rmsnorm(int64_t rows, int64_t cols, float eps, const float* x, float* y,
                           hipStream_t st);
 
 // Router (k_router.hip)
+// xq / sx non-null: also the per-token INT8 quantisation of x (in the same
+// pass where the width has a register form, else a second kernel).
 hipError_t launch_router(int64_t T, int d, int E, int k, int gating, const float* x,
                          const float* wr, const float* bias, int32_t* idx, float* w,
-                         hipStream_t st);
+                         int8_t* xq, float* sx, hipStream_t st);
 
 // Route / permute (k_route.hip).  ws holds ceil(T*k/256) * E int32 counts.
 int64_t route_blocks(int64_t Tk);
@@ -72,6 +78,26 @@ constexpr int64_t kGemvMaxRowsDense = 64;
 // The matrix-core forms are used from this many rows on, when the reduction
 // dimension is a multiple of 128.
 constexpr int64_t kMfmaMinRows = 256;
+// Routed and shared products of one kind in a single launch (same kernels as
+// above, the routed tiles first): matrix-core and weight-streaming forms.
+hipError_t launch_gateup_i4_mfma_pair(const ExpertArgs& ar, const ExpertArgs& as,
+                                      const int8_t* xq, const float* sx, const uint8_t* wq_r,
+                                      const float* ws_r, const uint8_t* wq_s, const float* ws_s,
+                                      float* abuf_r, float* abuf_s, hipStream_t st);
+hipError_t launch_down_i4_mfma_pair(const ExpertArgs& ar, const ExpertArgs& as,
+                                    const int8_t* hq_r, const float* hs_r, const int8_t* hq_s,
+                                    const float* hs_s, const uint8_t* wq_r, const float* ws_r,
+                                    const uint8_t* wq_s, const float* ws_s, float* f, float* ys,
+                                    hipStream_t st);
+hipError_t launch_gateup_i4_gemv_pair(const ExpertArgs& ar, const ExpertArgs& as,
+                                      const int8_t* xq, const float* sx, const uint8_t* wq_r,
+                                      const float* ws_r, const uint8_t* wq_s, const float* ws_s,
+                                      float* abuf_r, float* abuf_s, hipStream_t st);
+hipError_t launch_down_i4_gemv_pair(const ExpertArgs& ar, const ExpertArgs& as,
+                                    const int8_t* hq_r, const float* hs_r, const int8_t* hq_s,
+                                    const float* hs_s, const uint8_t* wq_r, const float* ws_r,
+                                    const uint8_t* wq_s, const float* ws_s, float* f, float* ys,
+                                    hipStream_t st);
 constexpr int kMfmaK = 128;
 // BF16 weights on the bf16 matrix cores (k_bf16.hip): gate/up takes the
 // token rows already rounded to BF16 (xb [T][d]) and writes BF16 hidden rows

@@ -119,6 +119,8 @@ class MoELayer:
         self.wk_gu = _empty((self.wk_gu_bytes,), torch.uint8, dv)
         self.wk_dn_bytes = max(B.workspace_bytes(self.desc, T, B.MM_WS_DOWN), 256)
         self.wk_dn = _empty((self.wk_dn_bytes,), torch.uint8, dv)
+        self.wk_fwd_bytes = max(B.workspace_bytes(self.desc, T, B.MM_WS_FORWARD), 256)
+        self.wk_fwd = _empty((self.wk_fwd_bytes,), torch.uint8, dv)
         self.wk_sh_bytes = max(B.workspace_bytes(self.desc, T, B.MM_WS_SHARED), 256)
         self.wk_sh = _empty((self.wk_sh_bytes,), torch.uint8, dv)
         self._T = T
@@ -162,22 +164,34 @@ class MoELayer:
     def combine(self, T):
         B.combine(self.desc, T, self.f, self.inv, self.topw, self.ys, self.y)
 
-    def capture(self, x: torch.Tensor) -> "torch.cuda.CUDAGraph":
+    def capture(self, x: torch.Tensor, fused: bool = False) -> "torch.cuda.CUDAGraph":
         """Records forward(x) for the static input buffer x into a HIP graph;
         replaying it recomputes y from whatever x holds at replay time.  The
         library allocates nothing and records no memset, so the graph holds
         only kernel nodes (and the shared-expert stream fork/join)."""
         T = x.shape[0]
         self.buffers(T)
+        fwd = self.forward_fused if fused else self.forward
         warm = torch.cuda.Stream(device=self.device)
         warm.wait_stream(torch.cuda.current_stream(self.device))
         with torch.cuda.stream(warm):
-            self.forward(x)
+            fwd(x)
         torch.cuda.current_stream(self.device).wait_stream(warm)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            self.forward(x)
+            fwd(x)
         return g
+
+    def forward_fused(self, x: torch.Tensor) -> torch.Tensor:
+        """y = eq. (*) of x through the one-call entry (mm_moe_forward): same
+        results as forward(), fewer launches, one stream.  Also fills idx/topw."""
+        T = x.shape[0]
+        self.buffers(T)
+        none = B.weight(None, None)
+        B.moe_forward(self.desc, T, x, self.wr, self.bias, self.w_gu.c(), self.w_d.c(),
+                      self.ws_gu.c() if self.hs else none, self.ws_d.c() if self.hs else none,
+                      self.idx, self.topw, self.y, self.wk_fwd, self.wk_fwd_bytes)
+        return self.y
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         """y = eq. (*) of x [T, d] FP32 (device).  Returns the layer's y buffer."""

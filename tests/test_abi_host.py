@@ -133,3 +133,28 @@ def test_prepacked_sizes(lib):
     assert B.prepacked_bytes(768, 768) == 768 * 384
     assert B.prepacked_scale_bytes(768, 768) == 768 * 24 * 4
     assert B.prepacked_bytes(48, 64) == 0
+
+
+def test_forward_checks(lib):
+    """mm_moe_forward validates everything before any launch."""
+    ds = S()
+    w = B.Weight(FAKE, FAKE)
+    need = B.workspace_bytes(ds, 2048, B.MM_WS_FORWARD)
+    # at least the routing tables, the quantised rows and the expert outputs
+    assert need >= 2048 * 4 * (768 * 4 + 384 * 5) + 2048 * (768 * 5 + 1536 * 5)
+    args = lambda ws_bytes: (ctypes.byref(ds), 2048, FAKE, FAKE, None, w, w, w, w, FAKE, FAKE, FAKE,
+                             FAKE, ws_bytes, None)
+    assert lib.mm_moe_forward(*args(need - 1)) == B.MM_ERR_WORKSPACE
+    assert b"forward workspace" in lib.mm_last_error_string()
+    assert lib.mm_moe_forward(ctypes.byref(ds), 0, None, None, None, w, w, w, w, None, None, None,
+                              None, 0, None) == B.MM_OK
+    assert lib.mm_moe_forward(ctypes.byref(ds), 4, None, FAKE, None, w, w, w, w, FAKE, FAKE, FAKE,
+                              FAKE, need, None) == B.MM_ERR_NULL
+    no_scales = B.Weight(FAKE, None)
+    assert lib.mm_moe_forward(ctypes.byref(ds), 4, FAKE, FAKE, None, w, w, no_scales, w, FAKE, FAKE,
+                              FAKE, FAKE, need, None) == B.MM_ERR_NULL
+    assert b"ws_gateup.scales" in lib.mm_last_error_string()
+    # without a shared expert its weights are not looked at
+    noshared = B.desc(768, 60, 384, 0, 4)
+    zero = B.Weight(None, None)
+    assert B.workspace_bytes(noshared, 2048, B.MM_WS_FORWARD) < need

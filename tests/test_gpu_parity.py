@@ -278,6 +278,45 @@ def test_rmsnorm():
 
 
 # ------------------------------------------------------------ full sizes
+# mm_moe_forward: the one-call layer.  Cases reach its merged launches
+# (weight-streaming pair, matrix-core pair), the mixed case that falls back to
+# separate launches, the other weight formats and the no-shared layer.
+FUSED_CASES = [
+    ("s_prefill", 1, {}), ("s_prefill", 8, {}), ("s_prefill", 64, {}),   # weight-streaming pair
+    ("s_prefill", 100, {}),                                                # mixed: separate launches
+    ("s_prefill", 256, {}), ("s_prefill", 700, {}),                      # matrix-core pair
+    ("s_prefill", 120, {"hs": 0}),
+    ("m_prefill", 200, {}), ("l_prefill", 130, {}),
+    ("s_prefill", 150, {"d": 704, "h": 320, "hs": 640}),                  # row-tile kernels
+    ("l_prefill_bf16", 64, {}), ("tiny_f32", 37, {}),
+]
+
+
+@pytest.mark.parametrize("name,T,over", FUSED_CASES)
+def test_fused_forward(name, T, over):
+    w = wl.WORKLOADS[name].with_(T=T, **over)
+    lw = wl.layer_weights(w)
+    x = wl.tokens(w)
+    layer = make_layer(w, lw)
+    xd = dev(x)
+    layer.forward(xd)
+    y_calls = layer_output(layer).copy()
+    idx_calls = np_(layer.idx).copy()
+    layer.y.zero_()
+    layer.idx.zero_()
+    layer.forward_fused(xd)
+    # the same launches' arithmetic: bit-identical to the seven calls
+    assert np.array_equal(np_(layer.idx), idx_calls)
+    assert np.array_equal(layer_output(layer), y_calls)
+    ref = oracle_forward(w, lw, x)
+    assert np.array_equal(np_(layer.idx), ref.idx)
+    y = layer_output(layer)
+    if w.wfmt == "int4g32":
+        assert np.array_equal(y, ref.y.astype(np.float32))
+    else:
+        assert row_rel_err(y, ref.y) <= (TOL_BF16 if w.wfmt == "bf16" else TOL_F32)
+
+
 @pytest.mark.parametrize("name", ["s_prefill", "m_prefill", "l_prefill"])
 def test_full_size_sampled(name):
     """The prefill workload at its full token count, in the configuration the
@@ -299,6 +338,11 @@ def test_full_size_sampled(name):
     ref = oracle_forward(w, lw, x[sample])
     assert row_rel_err(np_(layer.y)[sample], ref.y) <= TOL_F32
     assert np.array_equal(np_(layer.y)[sample], ref.y.astype(np.float32))
+    # the one-call layer at full size (the launches the benchmark times)
+    y_calls = np_(layer.y).copy()
+    layer.y.zero_()
+    layer.forward_fused(dev(x))
+    assert np.array_equal(np_(layer.y), y_calls)
 
 
 # ------------------------------------------------------------ decode stack
@@ -350,3 +394,12 @@ def test_graph_replay_matches_eager():
     y5 = np_(layer.y).copy()
     ref5 = oracle_forward(w, lw, wl.tokens(w, step=5))
     assert np.array_equal(y5, ref5.y.astype(np.float32))
+    # the one-call layer in a graph: every replay equals its eager result
+    gf = layer.capture(x, fused=True)
+    for i in range(3):
+        layer.y.zero_()
+        gf.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(np_(layer.y), y5), f"fused replay {i}"
+        other.forward_fused(x2)
+        torch.cuda.synchronize()
