@@ -74,19 +74,20 @@ def layer_work(w, T, counts=None):
 # K % 128 == 0, with two row tiles per wave once that still gives 4096 waves;
 # BF16 weights always on the bf16 matrix cores).
 def kernel_of(w, T, gateup: bool):
+    """(kernel name as rocprofv3 lists it, path) of the routed gate/up or down product."""
     rows, K = T * w.k, (w.d if gateup else w.h)
-    part = "gate/up" if gateup else "down"
+    gu = "true" if gateup else "false"
     if w.wfmt == "bf16":
-        return f"k_bf16w<2,{part},routed>", "matrix-core"
+        return f"k_bf16w<2, {gu}, false>", "matrix-core"
     if w.wfmt != "int4g32":
-        return ("k_gateup_fp" if gateup else "k_down_fp"), "row-tile"
+        return ("k_gateup_fp<false>" if gateup else "k_down_fp<false>"), "row-tile"
     if rows <= 512 and K % 64 == 0 and K <= 2560:
-        return f"k_gemv_i4<{part},routed>", "weight-streaming"
+        return f"k_gemv_i4<4, {gu}, false, false>", "weight-streaming"
     if rows >= 256 and K % 128 == 0:
         nsplit = w.h // 32 if gateup else w.d // 64
         mt = 2 if ((rows + 63) // 64 + w.E) * nsplit >= 4096 else 1
-        return f"k_w4a8w<{mt},2,{part},routed>", "matrix-core"
-    return ("k_gateup_i4" if gateup else "k_down_i4"), "row-tile"
+        return f"k_w4a8w<{mt}, {gu}, false, false>", "matrix-core"
+    return ("k_gateup_i4<false>" if gateup else "k_down_i4<false>"), "row-tile"
 
 
 KERNEL_SOURCES = ["sparse_moe_ffn_amd/csrc/k_mfma.hip", "sparse_moe_ffn_amd/csrc/k_gemv.hip",

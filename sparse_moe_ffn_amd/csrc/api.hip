@@ -549,13 +549,19 @@ mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
   int8_t* xq = i4 ? static_cast<int8_t*>(at(W.xq)) : nullptr;
   float* sx = i4 ? static_cast<float*>(at(W.sx)) : nullptr;
 
-  // router + top-k (+ per-token INT8 of x), then the count sort
-  MM_TRY(hip_status(mm::launch_router(T, d, E, k, desc->gating, x, w_router, bias, topk_idx, topk_w,
-                                      xq, sx, st),
-                    where));
-  MM_TRY(hip_status(mm::launch_route(Tk, E, topk_idx, off, perm, inv,
-                                     static_cast<int32_t*>(at(W.route)), st),
-                    where));
+  // router + top-k (+ per-token INT8 of x), then the count sort; for a few
+  // tokens all of it in one workgroup
+  if (i4 && mm::launch_front_small(T, d, E, k, desc->gating, x, w_router, bias, topk_idx, topk_w,
+                                   xq, sx, off, perm, inv, st)) {
+    MM_TRY(hip_status(hipGetLastError(), where));
+  } else {
+    MM_TRY(hip_status(mm::launch_router(T, d, E, k, desc->gating, x, w_router, bias, topk_idx,
+                                        topk_w, xq, sx, st),
+                      where));
+    MM_TRY(hip_status(mm::launch_route(Tk, E, topk_idx, off, perm, inv,
+                                       static_cast<int32_t*>(at(W.route)), st),
+                      where));
+  }
   if (i4) {
     const uint8_t* gq = static_cast<const uint8_t*>(w_gateup.data);
     const uint8_t* dq = static_cast<const uint8_t*>(w_down.data);

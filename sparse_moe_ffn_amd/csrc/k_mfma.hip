@@ -71,18 +71,20 @@ struct WStage {
 
 // Loads groups g0 and g0 + 1 relative to the current pointers (the offsets
 // are compile-time constants, so they fold into the load instructions).
+// pb / ps are wave-uniform (the lane offset is added here), so the loads take
+// a scalar base and a small per-lane offset.
 template <int kMT, int kNT>
 __device__ __forceinline__ void wload(WStage<kMT, kNT>& st, gint4* const (&pa)[kMT],
                                       guint2* const (&pb)[kNT], gfloat* const (&ps)[kNT],
-                                      int g0) {
+                                      int g0, int lane) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
 #pragma unroll
     for (int m = 0; m < kMT; ++m) st.a[i][m] = pa[m][(g0 + i) * (kGroup / 16)];
 #pragma unroll
     for (int j = 0; j < kNT; ++j) {
-      st.b[i][j] = pb[j][(g0 + i) * 64];
-      st.s[i][j] = ps[j][(g0 + i) * 32];
+      st.b[i][j] = pb[j][(g0 + i) * 64 + lane];
+      st.s[i][j] = ps[j][(g0 + i) * 32 + (lane & 31)];
     }
   }
 }
@@ -153,7 +155,8 @@ __device__ __forceinline__ int xcd_logical() {
 // offsets).  K % 128 == 0.  Called by one whole wave.
 template <int kMT, int kNT, bool kGateUp, bool kCapture, bool kDense>
 __device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int logical) {
-  static_assert(!kGateUp || kNT == 2, "gate/up pairs one gate and one up tile");
+  static_assert(!kGateUp || kNT % 2 == 0, "gate/up tiles come in (gate, up) pairs");
+  constexpr int kP = kNT / 2;  // gate/up: column pairs per wave
   constexpr int kBM = 32 * kMT;
   const ExpertArgs& a = P.a;
   const int nsplit = P.nsplit, K = P.K, N = P.N;
@@ -177,10 +180,13 @@ __device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int logical) {
   if (n <= 0) return;
   const int G = K / kGroup, h = a.h;
   int col0, rb[kNT];
-  if constexpr (kGateUp) {
-    col0 = split * 32;
-    rb[0] = split;
-    rb[1] = h / 32 + split;
+  if constexpr (kGateUp) {  // tiles 0..kP-1: gate; kP..2kP-1: the matching up tiles
+    col0 = split * kP * 32;
+#pragma unroll
+    for (int p = 0; p < kP; ++p) {
+      rb[p] = split * kP + p;
+      rb[kP + p] = h / 32 + split * kP + p;
+    }
   } else {
     col0 = split * kNT * 32;
 #pragma unroll
@@ -209,8 +215,8 @@ __device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int logical) {
   gfloat* ps[kNT];
 #pragma unroll
   for (int j = 0; j < kNT; ++j) {
-    pb[j] = (guint2*)(we + (int64_t)rb[j] * G * kChunkBytes) + lane;
-    ps[j] = (gfloat*)(se + (int64_t)rb[j] * G * 32 + (lane & 31));
+    pb[j] = (guint2*)(we + (int64_t)rb[j] * G * kChunkBytes);
+    ps[j] = (gfloat*)(se + (int64_t)rb[j] * G * 32);
   }
   const Capture cap{isum, wrows, G, p0, n};
 
@@ -224,9 +230,9 @@ __device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int logical) {
   // four groups per iteration.  The last iteration's prefetch re-reads its
   // own second stage (valid addresses, result unused).  G % 4 == 0.
   WStage<kMT, kNT> s0, s1;
-  wload(s0, pa, pb, ps, 0);
+  wload(s0, pa, pb, ps, 0, lane);
   for (int g = 0; g < G; g += 4) {
-    wload(s1, pa, pb, ps, 2);
+    wload(s1, pa, pb, ps, 2, lane);
     __builtin_amdgcn_sched_barrier(0);
     wcompute<kMT, kNT, kCapture>(acc, s0, g, lane, rb, cap);
     __builtin_amdgcn_sched_barrier(0);
@@ -238,7 +244,7 @@ __device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int logical) {
       pb[j] += adv * 64;
       ps[j] += adv * 32;
     }
-    wload(s0, pa, pb, ps, 0);
+    wload(s0, pa, pb, ps, 0, lane);
     __builtin_amdgcn_sched_barrier(0);
     wcompute<kMT, kNT, kCapture>(acc, s1, g + 2, lane, rb, cap);
     __builtin_amdgcn_sched_barrier(0);
@@ -253,7 +259,10 @@ __device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int logical) {
       const int row = m * 32 + rl;
       if (row >= n) continue;
       if constexpr (kGateUp) {
-        out[(int64_t)(p0 + row) * h + col0 + (lane & 31)] = silu(acc[m][0][r] * s) * (acc[m][1][r] * s);
+#pragma unroll
+        for (int p = 0; p < kP; ++p)
+          out[(int64_t)(p0 + row) * h + col0 + p * 32 + (lane & 31)] =
+              silu(acc[m][p][r] * s) * (acc[m][kP + p][r] * s);
       } else {
 #pragma unroll
         for (int j = 0; j < kNT; ++j)

@@ -24,11 +24,11 @@ constexpr int64_t kSmallRouterT = 64;  // up to this many tokens: the one-token-
 // holding it; lane j keeps the winner of round j.  Writes idx[0..k) and
 // w[0..k).  Called by a whole wave.
 template <int kGating>
-__device__ __forceinline__ void select_topk(float mine, int lane, int E, int k,
-                                            int32_t* __restrict__ idx, float* __restrict__ w) {
+__device__ __forceinline__ void select_topk_lanes(float mine, int lane, int E, int k, int& my_sel,
+                                                  float& wv) {
   const bool valid = lane < E;
   bool avail = valid;
-  int my_sel = 0;
+  my_sel = 0;
   float m = 0.0f;
   for (int j = 0; j < k; ++j) {
     const float mx = max64(avail ? mine : -INFINITY);
@@ -38,7 +38,6 @@ __device__ __forceinline__ void select_topk(float mine, int lane, int E, int k,
     if (lane == j) my_sel = win;
     if (lane == win) avail = false;
   }
-  float wv;
   if (kGating == 0) {
     // softmax over all E logits, not renormalised over the k selected
     const float z = valid ? exp_fp32(mine - m) : 0.0f;
@@ -51,8 +50,21 @@ __device__ __forceinline__ void select_topk(float mine, int lane, int E, int k,
     const float S = tree_sum64(lane < k ? mysg : 0.0f);
     wv = mysg / S;
   }
+}
+
+// Top-k and gate weights of one token; lane e holds the logit of expert e
+// (-inf for e >= E).  k rounds of a wave arg-max under the total order (value
+// descending, index ascending): the round's maximum, then the lowest lane
+// holding it; lane j keeps the winner of round j (select_topk_lanes).  Writes
+// idx[0..k) and w[0..k).  Called by a whole wave.
+template <int kGating>
+__device__ __forceinline__ void select_topk(float mine, int lane, int E, int k,
+                                            int32_t* __restrict__ idx, float* __restrict__ w) {
+  int sel;
+  float wv;
+  select_topk_lanes<kGating>(mine, lane, E, k, sel, wv);
   if (lane < k) {
-    idx[lane] = my_sel;
+    idx[lane] = sel;
     w[lane] = wv;
   }
 }
@@ -221,6 +233,93 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_router_small(
   select_topk<kGating>(mine, lane, E, k, idx + t * k, w + t * k);
 }
 
+// Few tokens (T <= 2), the whole front of the layer in one workgroup: the
+// router logits of every token (wave w keeps the rows of experts w, w+16,
+// w+32, w+48 in registers and runs through the tokens), the per-token INT8
+// quantisation of x, the top-k and gate weights, and the stable count sort of
+// the T*k assignments (expert offsets by a wave scan, each slot's rank among
+// the earlier slots with the same expert), written exactly as mm_route_permute
+// writes them.
+constexpr int kFrontMaxT = 16;  // LDS sizing; used up to kFrontUseT tokens
+constexpr int kFrontUseT = 2;    // beyond this the per-token router workgroups are faster
+
+template <int kGating, int kNX>
+__global__ __launch_bounds__(64 * kSmallWaves) void k_front_small(
+    int64_t T, int d, int E, int k, const float* __restrict__ x, const float* __restrict__ wr,
+    const float* __restrict__ bias, int32_t* __restrict__ idx, float* __restrict__ w,
+    int8_t* __restrict__ xq, float* __restrict__ sx, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
+  __shared__ float s_logit[kFrontMaxT][64];
+  __shared__ int s_id[kFrontMaxT * 8];
+  __shared__ int s_cnt[64];
+  __shared__ int s_off[64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nt = (int)T;
+  float wv[kSmallPer][kNX];
+#pragma unroll
+  for (int i = 0; i < kSmallPer; ++i) {
+    const float* we = wr + (int64_t)min(wave + kSmallWaves * i, E - 1) * d;
+#pragma unroll
+    for (int c = 0; c < kNX; ++c) wv[i][c] = we[lane + kWave * c];
+  }
+  if (threadIdx.x < 64) s_cnt[threadIdx.x] = 0;
+  for (int t = 0; t < nt; ++t) {
+    float xv[kNX];
+#pragma unroll
+    for (int c = 0; c < kNX; ++c) xv[c] = x[(int64_t)t * d + lane + kWave * c];
+    if (wave == (t & (kSmallWaves - 1))) quant_row_regs(xv, lane, t, d, xq, sx);
+#pragma unroll
+    for (int i = 0; i < kSmallPer; ++i) {
+      const int e = wave + kSmallWaves * i;
+      if (e >= E) break;
+      float p = 0.0f;
+#pragma unroll
+      for (int c = 0; c < kNX; ++c) p = __builtin_fmaf(xv[c], wv[i][c], p);
+      const float l = tree_sum64(p) + (bias ? bias[e] : 0.0f);
+      if (lane == 0) s_logit[t][e] = l;
+    }
+  }
+  __syncthreads();
+  if (wave < nt) {  // wave t: top-k of token t
+    const int t = wave;
+    const float mine = lane < E ? s_logit[t][lane] : -INFINITY;
+    int sel;
+    float wgt;
+    select_topk_lanes<kGating>(mine, lane, E, k, sel, wgt);
+    if (lane < k) {
+      idx[t * k + lane] = sel;
+      w[t * k + lane] = wgt;
+      s_id[t * k + lane] = sel;
+      atomicAdd(&s_cnt[sel], 1);
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {  // expert offsets: exclusive scan of the counts
+    const int c = lane < E ? s_cnt[lane] : 0;
+    int inc = c;
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) {
+      const int v = __shfl_up(inc, s);
+      if (lane >= s) inc += v;
+    }
+    if (lane < E) {
+      s_off[lane] = inc - c;
+      offsets[lane] = inc - c;
+      if (lane == E - 1) offsets[E] = inc;
+    }
+  }
+  __syncthreads();
+  const int tk = nt * k;
+  if ((int)threadIdx.x < tk) {  // stable rank among the earlier slots of the same expert
+    const int slot = threadIdx.x, e = s_id[slot];
+    int rank = 0;
+    for (int q = 0; q < slot; ++q) rank += s_id[q] == e;
+    const int pos = s_off[e] + rank;
+    perm[pos] = slot;
+    inv_perm[slot] = pos;
+  }
+}
+
 template <int kG, int kNX, bool kQ>
 void launch_router_nx(bool small, int64_t T, int d, int E, int k, const float* x, const float* wr,
                       const float* bias, int32_t* idx, float* w, int8_t* xq, float* sx,
@@ -259,7 +358,37 @@ bool router_quant_fused(int d) {
   return nx == 4 || nx == 8 || nx == 12 || nx == 16 || nx == 20 || nx == 24 || nx == 32;
 }
 
+template <int kG>
+bool launch_front_g(int64_t T, int d, int E, int k, const float* x, const float* wr,
+                    const float* bias, int32_t* idx, float* w, int8_t* xq, float* sx,
+                    int32_t* offsets, int32_t* perm, int32_t* inv_perm, hipStream_t st) {
+  const dim3 grid(1), block(64 * kSmallWaves);
+#define MM_FRONT(NX)                                                                               \
+  hipLaunchKernelGGL((k_front_small<kG, NX>), grid, block, 0, st, T, d, E, k, x, wr, bias, idx, w, \
+                     xq, sx, offsets, perm, inv_perm)
+  switch (d % kWave == 0 ? d / kWave : 0) {
+    case 4: MM_FRONT(4); return true;
+    case 8: MM_FRONT(8); return true;
+    case 12: MM_FRONT(12); return true;
+    case 16: MM_FRONT(16); return true;
+    case 20: MM_FRONT(20); return true;
+    default: return false;
+  }
+#undef MM_FRONT
+}
+
 }  // namespace
+
+bool launch_front_small(int64_t T, int d, int E, int k, int gating, const float* x,
+                        const float* wr, const float* bias, int32_t* idx, float* w, int8_t* xq,
+                        float* sx, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                        hipStream_t st) {
+  if (T < 1 || T > kFrontUseT || k > 8) return false;
+  return gating == 0 ? launch_front_g<0>(T, d, E, k, x, wr, bias, idx, w, xq, sx, offsets, perm,
+                                         inv_perm, st)
+                     : launch_front_g<1>(T, d, E, k, x, wr, bias, idx, w, xq, sx, offsets, perm,
+                                         inv_perm, st);
+}
 
 hipError_t launch_router(int64_t T, int d, int E, int k, int gating, const float* x,
                          const float* wr, const float* bias, int32_t* idx, float* w,

@@ -29,6 +29,16 @@ hipError_t launch_router(int64_t T, int d, int E, int k, int gating, const float
                          const float* wr, const float* bias, int32_t* idx, float* w,
                          int8_t* xq, float* sx, hipStream_t st);
 
+// Router + top-k + INT8 of x + the count sort in one workgroup, for
+// 1 <= T <= 2 tokens (beyond that the per-token router workgroups win) and
+// the widths with a register form up to d = 1280
+// (k_router.hip).  Returns false (nothing launched) otherwise.  Outputs as
+// launch_router (with xq / sx) followed by launch_route.
+bool launch_front_small(int64_t T, int d, int E, int k, int gating, const float* x,
+                        const float* wr, const float* bias, int32_t* idx, float* w, int8_t* xq,
+                        float* sx, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                        hipStream_t st);
+
 // Route / permute (k_route.hip).  ws holds ceil(T*k/256) * E int32 counts.
 int64_t route_blocks(int64_t Tk);
 hipError_t launch_route(int64_t Tk, int E, const int32_t* idx, int32_t* offsets, int32_t* perm,

@@ -283,6 +283,7 @@ def test_rmsnorm():
 # separate launches, the other weight formats and the no-shared layer.
 FUSED_CASES = [
     ("s_prefill", 1, {}), ("s_prefill", 8, {}), ("s_prefill", 64, {}),   # weight-streaming pair
+    ("l_prefill", 1, {}), ("m_prefill", 2, {}), ("s_prefill", 3, {}),     # one-workgroup front and past it
     ("s_prefill", 100, {}),                                                # mixed: separate launches
     ("s_prefill", 256, {}), ("s_prefill", 700, {}),                      # matrix-core pair
     ("s_prefill", 120, {"hs": 0}),
@@ -403,3 +404,25 @@ def test_graph_replay_matches_eager():
         assert np.array_equal(np_(layer.y), y5), f"fused replay {i}"
         other.forward_fused(x2)
         torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------ other router rules
+@pytest.mark.parametrize("name,T,over", [
+    ("s_prefill", 300, {"E": 64, "k": 8}),    # largest expert count and top-k
+    ("l_prefill", 2, {}),                     # Zipf bias, one-workgroup front
+    ("l_prefill", 260, {}),                   # Zipf bias, matrix cores
+])
+def test_sigmoid_gating_layer(name, T, over):
+    """The layer with sigmoid gating renormalised over the k selected (the
+    alternative gate rule): same ids as softmax, weights and y exact."""
+    w = wl.WORKLOADS[name].with_(T=T, **over)
+    lw = wl.layer_weights(w)
+    x = wl.tokens(w)
+    layer = make_layer(w, lw, gating=1)
+    ref = oracle_forward(w, lw, x, gating=1)
+    for fwd in (layer.forward, layer.forward_fused):
+        layer.y.zero_()
+        fwd(dev(x))
+        assert np.array_equal(np_(layer.idx), ref.idx)
+        assert np.array_equal(np_(layer.topw), ref.w.astype(np.float32))
+        assert np.array_equal(layer_output(layer), ref.y.astype(np.float32))
