@@ -185,12 +185,20 @@ def main():
     def fwd(L, src):
         return L.forward_fused(src) if fused else L.forward(src)
 
+    def layer_then_norm(L, src, dst):
+        """One stack layer: dst = RMSNorm(layer(src)) (the combine writes it on the
+        one-call path, a separate kernel on the seven-call path)."""
+        if fused:
+            L.forward_fused(src, y_norm=dst, norm_eps=1e-5)
+        else:
+            y = L.forward(src)
+            B.rmsnorm_f32(T, w.d, 1e-5, y, dst)
+
     def eager_step(s: int):
         if decode:
             cur = xs[s % n_inputs]
             for L in layers:
-                y = fwd(L, cur)
-                B.rmsnorm_f32(T, w.d, 1e-5, y, nxt)
+                layer_then_norm(L, cur, nxt)
                 cur = nxt
         else:
             fwd(layers[s % n_inst], xs[0])
@@ -215,8 +223,7 @@ def main():
             def stack(src):
                 cur = src
                 for L in layers:
-                    y = fwd(L, cur)
-                    B.rmsnorm_f32(T, w.d, 1e-5, y, nxt)
+                    layer_then_norm(L, cur, nxt)
                     cur = nxt
 
             stack(xin)

@@ -278,6 +278,10 @@ mm_status mm_combine(const mm_layer_desc* desc, int64_t T, const float* f,
  *   ws_gateup, ws_down shared expert; ignored (may be zero) when shared_hidden == 0
  *   topk_idx, topk_w   out: device int32 / FP32 [T][k], as mm_router_topk
  *   y                  out: device [T][d], FP32 or BF16 per desc->out_dtype
+ *   y_norm, norm_eps   optional (y_norm NULL: not written): FP32 [T][d]
+ *                      RMSNorm(y) = y / sqrt(mean_c y^2 + norm_eps), unit gain, for
+ *                      the next layer of a decoder stack (outside eq. (*));
+ *                      needs FP32 y and norm_eps > 0
  *   ws / ws_bytes      mm_workspace_bytes(desc, T, MM_WS_FORWARD): the routing
  *                      tables, quantised rows and expert outputs of the call
  * Errors as the individual calls; nothing is queued when a check fails.
@@ -285,8 +289,8 @@ mm_status mm_combine(const mm_layer_desc* desc, int64_t T, const float* f,
 mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
                          const float* w_router, const float* bias, mm_weight w_gateup,
                          mm_weight w_down, mm_weight ws_gateup, mm_weight ws_down,
-                         int32_t* topk_idx, float* topk_w, void* y, void* ws, size_t ws_bytes,
-                         void* stream);
+                         int32_t* topk_idx, float* topk_w, void* y, float* y_norm,
+                         float norm_eps, void* ws, size_t ws_bytes, void* stream);
 
 /* --------------------------------------------------- around the layer */
 

@@ -81,7 +81,7 @@ _SIGS = {
     "mm_combine": ([_DESC, _I64, _VP, _VP, _VP, _VP, _VP, _VP], ctypes.c_int),
     "mm_rmsnorm_f32": ([_I64, _I64, _F, _VP, _VP, _VP], ctypes.c_int),
     "mm_moe_forward": ([_DESC, _I64, _VP, _VP, _VP, Weight, Weight, Weight, Weight, _VP, _VP, _VP,
-                        _VP, _SZ, _VP], ctypes.c_int),
+                        _VP, _F, _VP, _SZ, _VP], ctypes.c_int),
 }
 
 _lib = None
@@ -214,11 +214,13 @@ def combine(ds, T, f, inv_perm, topk_w, ys, y, stream=None):
 
 
 def moe_forward(ds, T, x, w_router, bias, w_gu, w_d, ws_gu, ws_d, topk_idx, topk_w, y, ws,
-                ws_bytes, stream=None):
-    """The whole layer in one call (routed + shared experts, combine)."""
+                ws_bytes, stream=None, y_norm=None, norm_eps=0.0):
+    """The whole layer in one call (routed + shared experts, combine); with
+    y_norm also RMSNorm(y) for the next layer of a stack."""
     _check(load().mm_moe_forward(ctypes.byref(ds), T, _ptr(x), _ptr(w_router), _ptr(bias), w_gu,
-                                 w_d, ws_gu, ws_d, _ptr(topk_idx), _ptr(topk_w), _ptr(y), _ptr(ws),
-                                 ws_bytes, _stream(stream)), "mm_moe_forward")
+                                 w_d, ws_gu, ws_d, _ptr(topk_idx), _ptr(topk_w), _ptr(y),
+                                 _ptr(y_norm), norm_eps, _ptr(ws), ws_bytes, _stream(stream)),
+           "mm_moe_forward")
 
 
 def rmsnorm_f32(rows, cols, eps, x, y, stream=None):

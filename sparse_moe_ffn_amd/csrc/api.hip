@@ -509,8 +509,8 @@ mm_status mm_combine(const mm_layer_desc* desc, int64_t T, const float* f,
 mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
                          const float* w_router, const float* bias, mm_weight w_gateup,
                          mm_weight w_down, mm_weight ws_gateup, mm_weight ws_down,
-                         int32_t* topk_idx, float* topk_w, void* y, void* ws, size_t ws_size,
-                         void* stream) {
+                         int32_t* topk_idx, float* topk_w, void* y, float* y_norm, float norm_eps,
+                         void* ws, size_t ws_size, void* stream) {
   MM_TRY(check_desc(desc));
   MM_TRY(check_T(desc, T));
   if (T == 0) return MM_OK;
@@ -520,6 +520,10 @@ mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
   MM_REQUIRE(topk_idx);
   MM_REQUIRE(topk_w);
   MM_REQUIRE(y);
+  MM_OPTIONAL(y_norm);
+  if (y_norm && desc->out_dtype != MM_OUT_F32)
+    return fail(MM_ERR_FORMAT, "y_norm needs FP32 output");
+  if (y_norm && !(norm_eps > 0.0f)) return fail(MM_ERR_SHAPE, "norm_eps must be positive");
   MM_REQUIRE(ws);
   MM_TRY(check_weight(desc, w_gateup, "w_gateup"));
   MM_TRY(check_weight(desc, w_down, "w_down"));
@@ -630,7 +634,7 @@ mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
     if (shared) MM_TRY(hip_status(mm::launch_down_fp(as, false, h_s, ws_down.data, ys, st), where));
   }
   return hip_status(mm::launch_combine(T, d, k, f, inv, topk_w, ys, y,
-                                       desc->out_dtype == MM_OUT_BF16, st),
+                                       desc->out_dtype == MM_OUT_BF16, st, y_norm, norm_eps),
                     where);
 }
 

@@ -15,13 +15,17 @@ namespace {
 // l, l + 64, ...  All of a lane's gathers are issued before the sums.
 constexpr int kMaxC4 = 8;  // float4 columns per lane: d <= 2048
 
-template <bool kBF16Out>
+// kNorm: also y_norm = y / sqrt(mean(y^2) + eps) (FP32 y only): the input of
+// the next layer in a decoder stack, from the row the wave already holds.
+template <bool kBF16Out, bool kNorm = false>
 __global__ __launch_bounds__(256) void k_combine(int64_t T, int d, int k,
                                                  const float* __restrict__ f,
                                                  const int32_t* __restrict__ inv,
                                                  const float* __restrict__ w,
                                                  const float* __restrict__ ys,
-                                                 void* __restrict__ y) {
+                                                 void* __restrict__ y,
+                                                 float* __restrict__ y_norm = nullptr,
+                                                 float eps = 0.0f) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -67,6 +71,7 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int d, int k,
       a.z += s.z;
       a.w += s.w;
     }
+    acc[i] = a;
     if (kBF16Out) {
       ushort4 o;
       o.x = f32_to_bf16(a.x);
@@ -76,6 +81,27 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int d, int k,
       reinterpret_cast<ushort4*>(y)[t * q + c4] = o;
     } else {
       reinterpret_cast<float4*>(y)[t * q + c4] = a;
+    }
+  }
+  if constexpr (kNorm) {
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kMaxC4; ++i)
+      if (lane + 64 * i < q) {
+        ss = fmaf(acc[i].x, acc[i].x, ss);
+        ss = fmaf(acc[i].y, acc[i].y, ss);
+        ss = fmaf(acc[i].z, acc[i].z, ss);
+        ss = fmaf(acc[i].w, acc[i].w, ss);
+      }
+    ss = wave_sum(ss);
+    const float inv_rms = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+    for (int i = 0; i < kMaxC4; ++i) {
+      const int c4 = lane + 64 * i;
+      if (c4 >= q) continue;
+      const float4 a = acc[i];
+      reinterpret_cast<float4*>(y_norm)[t * q + c4] =
+          make_float4(a.x * inv_rms, a.y * inv_rms, a.z * inv_rms, a.w * inv_rms);
     }
   }
 }
@@ -128,15 +154,18 @@ __global__ __launch_bounds__(256) void k_combine_wide(int64_t T, int d, int k,
 
 hipError_t launch_combine(int64_t T, int d, int k, const float* f, const int32_t* inv_perm,
                           const float* w, const float* ys, void* y, bool bf16_out,
-                          hipStream_t st) {
+                          hipStream_t st, float* y_norm, float eps) {
   if (d / 4 <= 64 * kMaxC4) {
     const unsigned blocks = (unsigned)((T + 3) / 4);
-    if (bf16_out)
+    if (y_norm)
+      hipLaunchKernelGGL((k_combine<false, true>), dim3(blocks), dim3(256), 0, st, T, d, k, f,
+                         inv_perm, w, ys, y, y_norm, eps);
+    else if (bf16_out)
       hipLaunchKernelGGL(k_combine<true>, dim3(blocks), dim3(256), 0, st, T, d, k, f, inv_perm, w,
-                         ys, y);
+                         ys, y, nullptr, 0.0f);
     else
       hipLaunchKernelGGL(k_combine<false>, dim3(blocks), dim3(256), 0, st, T, d, k, f, inv_perm, w,
-                         ys, y);
+                         ys, y, nullptr, 0.0f);
   } else {
     const unsigned blocks = (unsigned)((T * (d / 4) + 255) / 256);
     if (bf16_out)
@@ -145,6 +174,11 @@ hipError_t launch_combine(int64_t T, int d, int k, const float* f, const int32_t
     else
       hipLaunchKernelGGL(k_combine_wide<false>, dim3(blocks), dim3(256), 0, st, T, d, k, f,
                          inv_perm, w, ys, y);
+    if (y_norm) {
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return launch_rmsnorm(T, d, eps, static_cast<const float*>(y), y_norm, st);
+    }
   }
   return hipGetLastError();
 }

@@ -123,8 +123,9 @@ hipError_t launch_down_fp(const ExpertArgs& a, bool bf16, const void* hrow, cons
                           float* f, hipStream_t st);
 
 // Combine (k_combine.hip)
+// y_norm non-null (FP32 y only): also RMSNorm(y) with eps, unit gain.
 hipError_t launch_combine(int64_t T, int d, int k, const float* f, const int32_t* inv_perm,
                           const float* w, const float* ys, void* y, bool bf16_out,
-                          hipStream_t st);
+                          hipStream_t st, float* y_norm = nullptr, float eps = 0.0f);
 
 }  // namespace mm

@@ -182,15 +182,18 @@ class MoELayer:
             fwd(x)
         return g
 
-    def forward_fused(self, x: torch.Tensor) -> torch.Tensor:
+    def forward_fused(self, x: torch.Tensor, y_norm: Optional[torch.Tensor] = None,
+                      norm_eps: float = 1e-5) -> torch.Tensor:
         """y = eq. (*) of x through the one-call entry (mm_moe_forward): same
-        results as forward(), fewer launches, one stream.  Also fills idx/topw."""
+        results as forward(), fewer launches, one stream.  Also fills idx/topw,
+        and y_norm = RMSNorm(y) when given (the next layer's input in a stack)."""
         T = x.shape[0]
         self.buffers(T)
         none = B.weight(None, None)
         B.moe_forward(self.desc, T, x, self.wr, self.bias, self.w_gu.c(), self.w_d.c(),
                       self.ws_gu.c() if self.hs else none, self.ws_d.c() if self.hs else none,
-                      self.idx, self.topw, self.y, self.wk_fwd, self.wk_fwd_bytes)
+                      self.idx, self.topw, self.y, self.wk_fwd, self.wk_fwd_bytes,
+                      y_norm=y_norm, norm_eps=norm_eps if y_norm is not None else 0.0)
         return self.y
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:

@@ -143,17 +143,24 @@ def test_forward_checks(lib):
     # at least the routing tables, the quantised rows and the expert outputs
     assert need >= 2048 * 4 * (768 * 4 + 384 * 5) + 2048 * (768 * 5 + 1536 * 5)
     args = lambda ws_bytes: (ctypes.byref(ds), 2048, FAKE, FAKE, None, w, w, w, w, FAKE, FAKE, FAKE,
-                             FAKE, ws_bytes, None)
+                             None, 0.0, FAKE, ws_bytes, None)
     assert lib.mm_moe_forward(*args(need - 1)) == B.MM_ERR_WORKSPACE
     assert b"forward workspace" in lib.mm_last_error_string()
     assert lib.mm_moe_forward(ctypes.byref(ds), 0, None, None, None, w, w, w, w, None, None, None,
-                              None, 0, None) == B.MM_OK
+                              None, 0.0, None, 0, None) == B.MM_OK
     assert lib.mm_moe_forward(ctypes.byref(ds), 4, None, FAKE, None, w, w, w, w, FAKE, FAKE, FAKE,
-                              FAKE, need, None) == B.MM_ERR_NULL
+                              None, 0.0, FAKE, need, None) == B.MM_ERR_NULL
     no_scales = B.Weight(FAKE, None)
     assert lib.mm_moe_forward(ctypes.byref(ds), 4, FAKE, FAKE, None, w, w, no_scales, w, FAKE, FAKE,
-                              FAKE, FAKE, need, None) == B.MM_ERR_NULL
+                              FAKE, None, 0.0, FAKE, need, None) == B.MM_ERR_NULL
     assert b"ws_gateup.scales" in lib.mm_last_error_string()
+    # the RMSNorm output needs FP32 y and a positive eps
+    assert lib.mm_moe_forward(ctypes.byref(ds), 4, FAKE, FAKE, None, w, w, w, w, FAKE, FAKE, FAKE,
+                              FAKE, 0.0, FAKE, need, None) == B.MM_ERR_SHAPE
+    bf = B.desc(768, 60, 384, 1536, 4, "bf16", out_dtype=B.MM_OUT_BF16)
+    wb = B.Weight(FAKE, None)
+    assert lib.mm_moe_forward(ctypes.byref(bf), 4, FAKE, FAKE, None, wb, wb, wb, wb, FAKE, FAKE, FAKE,
+                              FAKE, 1e-5, FAKE, 1 << 30, None) == B.MM_ERR_FORMAT
     # without a shared expert its weights are not looked at
     noshared = B.desc(768, 60, 384, 0, 4)
     zero = B.Weight(None, None)

@@ -366,6 +366,12 @@ def test_decode_stack_teacher_forced(B_):
         nxt = torch.empty_like(y)
         B.rmsnorm_f32(B_, w.d, 1e-5, y, nxt)
         assert row_rel_err(np_(nxt), oracle.rmsnorm(np_(y), 1e-5)) < 1e-5
+        # the one-call layer, with the next layer's input from its combine
+        y_calls = np_(y).copy()
+        nxt2 = torch.empty_like(y)
+        layer.forward_fused(cur, y_norm=nxt2, norm_eps=1e-5)
+        assert np.array_equal(np_(layer.y), y_calls)
+        assert row_rel_err(np_(nxt2), oracle.rmsnorm(y_calls, 1e-5)) < 1e-5
         cur = nxt
 
 
@@ -419,6 +425,7 @@ def test_sigmoid_gating_layer(name, T, over):
     lw = wl.layer_weights(w)
     x = wl.tokens(w)
     layer = make_layer(w, lw, gating=1)
+    layer.buffers(T)
     ref = oracle_forward(w, lw, x, gating=1)
     for fwd in (layer.forward, layer.forward_fused):
         layer.y.zero_()
