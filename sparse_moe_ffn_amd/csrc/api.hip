@@ -578,13 +578,17 @@ mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
     float* s_r = static_cast<float*>(at(W.s_r));
     float* s_s = static_cast<float*>(at(W.s_s));
     // gate/up (+ SwiGLU) of both kinds, then their hidden-row quantisers
+    // (weight-streaming down of both kinds: the down workgroups quantise)
     const bool gv = use_gemv(ar, d, true) && (!shared || use_gemv(as, d, true));
     const bool gm = use_mfma(ar, d) && (!shared || use_mfma(as, d));
+    const bool dv = use_gemv(ar, h, false) && (!shared || use_gemv(as, hs, false));
+    const bool qin = shared && gv && dv && mm::gemv_i4_qin_fits(h) && mm::gemv_i4_qin_fits(hs);
     if (shared && gv) {
       MM_TRY(hip_status(mm::launch_gateup_i4_gemv_pair(ar, as, xq, sx, gq, w_gateup.scales, sgq,
                                                        ws_gateup.scales, a_r, a_s, st), where));
-      MM_TRY(hip_status(mm::launch_act_quant_i8_pair(Tk, h, a_r, q_r, s_r, T, hs, a_s, q_s, s_s, st),
-                        where));
+      if (!qin)
+        MM_TRY(hip_status(mm::launch_act_quant_i8_pair(Tk, h, a_r, q_r, s_r, T, hs, a_s, q_s, s_s,
+                                                       st), where));
     } else if (shared && gm && !use_gemv(ar, d, true)) {
       MM_TRY(hip_status(mm::launch_gateup_i4_mfma_pair(ar, as, xq, sx, gq, w_gateup.scales, sgq,
                                                        ws_gateup.scales, a_r, a_s, st), where));
@@ -597,9 +601,11 @@ mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
                           where));
     }
     // down of both kinds
-    const bool dv = use_gemv(ar, h, false) && (!shared || use_gemv(as, hs, false));
     const bool dm = use_mfma(ar, h) && (!shared || use_mfma(as, hs));
-    if (shared && dv) {
+    if (qin) {
+      MM_TRY(hip_status(mm::launch_down_i4_gemv_pair_f32in(ar, as, a_r, a_s, dq, w_down.scales, sdq,
+                                                           ws_down.scales, f, ys, st), where));
+    } else if (shared && dv) {
       MM_TRY(hip_status(mm::launch_down_i4_gemv_pair(ar, as, q_r, s_r, q_s, s_s, dq, w_down.scales,
                                                      sdq, ws_down.scales, f, ys, st), where));
     } else if (shared && dm && !use_gemv(ar, h, false)) {

@@ -78,15 +78,53 @@ struct GemvProb {
   const float* wsc;
   float* out;
   int32_t* isum;
+  // down only, instead of act/act_scale: FP32 hidden rows [rows][K] that the
+  // workgroup quantises itself (K % 128 == 0)
+  const float* actf;
 };
+
+constexpr int kMaxQV = 20;  // float2 per lane of a quantised row: K <= 128 * 20
+
+// Wave-level INT8 quantisation of one FP32 row (K % 128 == 0, K <= 128 *
+// kMaxQV) into LDS: the same rule and arithmetic as the standalone quantiser
+// (exact max|v| over the row, s = 2*amax/255, codes clamp(rint(v/s))), so
+// its codes and scale are bit-identical.  Returns s on every lane.
+__device__ __forceinline__ float quant_row_lds(const float* __restrict__ x, int K,
+                                               int8_t* __restrict__ dst, int lane) {
+  const int nv = K / 128;
+  const float2* xr = reinterpret_cast<const float2*>(x);
+  float2 v[kMaxQV];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kMaxQV; ++i)
+    if (i < nv) {
+      v[i] = xr[lane + 64 * i];
+      amax = fmaxf(amax, fmaxf(fabsf(v[i].x), fabsf(v[i].y)));
+    }
+  amax = max64(amax);
+  const float sr = (2.0f * amax) / 255.0f;
+  uint16_t* q = reinterpret_cast<uint16_t*>(dst);
+#pragma unroll
+  for (int i = 0; i < kMaxQV; ++i)
+    if (i < nv) {
+      int8_t c0 = 0, c1 = 0;
+      if (sr != 0.0f) {
+        c0 = quant_i8(v[i].x, sr);
+        c1 = quant_i8(v[i].y, sr);
+      }
+      q[lane + 64 * i] = (uint16_t)((uint8_t)c0 | ((uint16_t)(uint8_t)c1 << 8));
+    }
+  return sr;
+}
 
 // Block `blk` of problem P.  out: gate/up -> a = SiLU(g * s) * (u * s) into
 // out [rows][h]; down -> f = acc * s into out [rows][N].  K: reduction length
 // (multiple of 64, <= 2560); RB: 32-row weight blocks per output (gate/up:
 // h / 32, down: N / 32).  kDense: rows are the tokens in order (shared
 // expert); otherwise routed.  Called by the whole workgroup.
-template <int kR, bool kGateUp, bool kCapture, bool kDense>
+template <int kR, bool kGateUp, bool kCapture, bool kDense, bool kQIn = false>
 __device__ __forceinline__ void gemv_block(const GemvProb& P, int blk) {
+  static_assert(!kQIn || (!kGateUp && kR == 4), "in-kernel quantisation: down, one row per wave");
   const ExpertArgs& a = P.a;
   const int K = P.K, N = P.N, RB = P.RB;
   const int8_t* __restrict__ act = P.act;
@@ -127,7 +165,18 @@ __device__ __forceinline__ void gemv_block(const GemvProb& P, int blk) {
           we + ((int64_t)rbm[m] * G + 2 * gp) * kChunkBytes)[lane];
   }
 
-  if (threadIdx.x < kR) {
+  if constexpr (kQIn) {
+    // wave r quantises hidden row p0 + r (a padding row stays zero)
+    const int r = wave;
+    int8_t* dst = reinterpret_cast<int8_t*>(s_act) + (int64_t)r * K;
+    float sr = 0.0f;
+    if (r < n) {
+      sr = quant_row_lds(P.actf + (int64_t)(p0 + r) * K, K, dst, lane);
+    } else {
+      for (int c = lane; c < K / 16; c += 64) reinterpret_cast<int4*>(dst)[c] = make_int4(0, 0, 0, 0);
+    }
+    if (lane == 0) s_as[r] = sr;
+  } else if (threadIdx.x < kR) {
     const int r = threadIdx.x;
     int src = -1;
     float s = 0.0f;
@@ -148,15 +197,17 @@ __device__ __forceinline__ void gemv_block(const GemvProb& P, int blk) {
     const int m = i / (G * 32), j = i % (G * 32);
     s_sc[i] = se[(int64_t)rbm[m] * G * 32 + j];
   }
-  __syncthreads();  // s_src ready
+  __syncthreads();  // s_src ready (in-kernel quantisation: activations staged)
   const int c16 = K / 16;
-  for (int i = threadIdx.x; i < kR * c16; i += blockDim.x) {
-    const int r = i / c16, c = i % c16;
-    int4 v = make_int4(0, 0, 0, 0);
-    if (r < n) v = reinterpret_cast<const int4*>(act + (int64_t)s_src[r] * K)[c];
-    s_act[i] = v;
+  if constexpr (!kQIn) {
+    for (int i = threadIdx.x; i < kR * c16; i += blockDim.x) {
+      const int r = i / c16, c = i % c16;
+      int4 v = make_int4(0, 0, 0, 0);
+      if (r < n) v = reinterpret_cast<const int4*>(act + (int64_t)s_src[r] * K)[c];
+      s_act[i] = v;
+    }
+    __syncthreads();  // activations and scales staged
   }
-  __syncthreads();  // activations and scales staged
 
   // Lane geometry inside a pair: lanes 0..31 hold group 2gp, 32..63 group
   // 2gp+1; within a group, lane l (= lane % 32) holds rows 2*(l % 16) and
@@ -218,12 +269,12 @@ __global__ __launch_bounds__(256) void k_gemv_i4(GemvProb P) {
 }
 
 // Routed (P0, the first n0 blocks) and shared (P1) products in one launch.
-template <int kR, bool kGateUp>
+template <int kR, bool kGateUp, bool kQIn = false>
 __global__ __launch_bounds__(256) void k_gemv_i4_pair(GemvProb P0, GemvProb P1, int n0) {
   if ((int)blockIdx.x < n0)
-    gemv_block<kR, kGateUp, false, false>(P0, (int)blockIdx.x);
+    gemv_block<kR, kGateUp, false, false, kQIn>(P0, (int)blockIdx.x);
   else
-    gemv_block<kR, kGateUp, false, true>(P1, (int)blockIdx.x - n0);
+    gemv_block<kR, kGateUp, false, true, kQIn>(P1, (int)blockIdx.x - n0);
 }
 
 constexpr int kRGemv = 4;
@@ -263,12 +314,12 @@ hipError_t launch_gemv(const GemvProb& P, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <bool kGateUp>
+template <bool kGateUp, bool kQIn = false>
 hipError_t launch_gemv_pair(const GemvProb& R, const GemvProb& D, hipStream_t st) {
   const unsigned n0 = gemv_tiles(R.a) * R.RB, n1 = gemv_tiles(D.a) * D.RB;
   const size_t lds = std::max(gemv_lds(R.K, kGateUp), gemv_lds(D.K, kGateUp));
-  hipLaunchKernelGGL((k_gemv_i4_pair<kRGemv, kGateUp>), dim3(n0 + n1), dim3(256), lds, st, R, D,
-                     (int)n0);
+  hipLaunchKernelGGL((k_gemv_i4_pair<kRGemv, kGateUp, kQIn>), dim3(n0 + n1), dim3(256), lds, st, R,
+                     D, (int)n0);
   return hipGetLastError();
 }
 
@@ -305,6 +356,19 @@ hipError_t launch_down_i4_gemv_pair(const ExpertArgs& ar, const ExpertArgs& as,
                                     hipStream_t st) {
   return launch_gemv_pair<false>(gemv_down_prob(ar, hq_r, hs_r, wq_r, ws_r, f, nullptr),
                                  gemv_down_prob(as, hq_s, hs_s, wq_s, ws_s, ys, nullptr), st);
+}
+
+bool gemv_i4_qin_fits(int K) { return gemv_i4_fits(K, false) && K % 128 == 0 && K <= 128 * kMaxQV; }
+
+hipError_t launch_down_i4_gemv_pair_f32in(const ExpertArgs& ar, const ExpertArgs& as,
+                                          const float* a_r, const float* a_s, const uint8_t* wq_r,
+                                          const float* ws_r, const uint8_t* wq_s,
+                                          const float* ws_s, float* f, float* ys, hipStream_t st) {
+  GemvProb R = gemv_down_prob(ar, nullptr, nullptr, wq_r, ws_r, f, nullptr);
+  GemvProb D = gemv_down_prob(as, nullptr, nullptr, wq_s, ws_s, ys, nullptr);
+  R.actf = a_r;
+  D.actf = a_s;
+  return launch_gemv_pair<false, true>(R, D, st);
 }
 
 }  // namespace mm

@@ -108,6 +108,15 @@ hipError_t launch_down_i4_gemv_pair(const ExpertArgs& ar, const ExpertArgs& as,
                                     const float* hs_s, const uint8_t* wq_r, const float* ws_r,
                                     const uint8_t* wq_s, const float* ws_s, float* f, float* ys,
                                     hipStream_t st);
+// Same pair from the FP32 hidden rows a_r [Tk][h], a_s [T][hs]: each
+// workgroup quantises its rows itself (codes and scales bit-identical to
+// launch_act_quant_i8_pair), so no quantiser launch is needed.  Only when
+// gemv_i4_qin_fits(h) and gemv_i4_qin_fits(hs).
+bool gemv_i4_qin_fits(int K);
+hipError_t launch_down_i4_gemv_pair_f32in(const ExpertArgs& ar, const ExpertArgs& as,
+                                          const float* a_r, const float* a_s, const uint8_t* wq_r,
+                                          const float* ws_r, const uint8_t* wq_s,
+                                          const float* ws_s, float* f, float* ys, hipStream_t st);
 constexpr int kMfmaK = 128;
 // BF16 weights on the bf16 matrix cores (k_bf16.hip): gate/up takes the
 // token rows already rounded to BF16 (xb [T][d]) and writes BF16 hidden rows

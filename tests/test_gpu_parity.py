@@ -289,6 +289,7 @@ FUSED_CASES = [
     ("s_prefill", 120, {"hs": 0}),
     ("m_prefill", 200, {}), ("l_prefill", 130, {}),
     ("s_prefill", 150, {"d": 704, "h": 320, "hs": 640}),                  # row-tile kernels
+    ("s_prefill", 5, {"d": 704, "h": 320, "hs": 640}),                    # down pair from INT8 rows (h % 128 != 0)
     ("l_prefill_bf16", 64, {}), ("tiny_f32", 37, {}),
 ]
 
