@@ -166,26 +166,40 @@ __device__ __forceinline__ void routed_tile(const int32_t* __restrict__ offsets,
   }
 }
 
-// routed_tile for a one-wave workgroup: the same lookup, with the result
-// returned wave-uniform in registers (n = 0: no such tile).  All 64 lanes call.
-__device__ __forceinline__ void routed_tile_wave(const int32_t* __restrict__ offsets, int E,
-                                                 int rows, int rows_per_tile, int mt, int& p0,
-                                                 int& n, int& e) {
+// The routed tile table of a one-wave workgroup, in registers: lane e holds
+// expert e's row segment [beg, end) and its tiles [first, inc); total is the
+// tile count over all experts (wave-uniform).  All 64 lanes call.
+struct RoutedTiles {
+  int beg, end, first, inc, total;
+};
+
+__device__ __forceinline__ RoutedTiles routed_tiles(const int32_t* __restrict__ offsets, int E,
+                                                    int rows, int rows_per_tile) {
   const int lane = threadIdx.x & 63;
-  int beg = 0, end = 0;
+  RoutedTiles t{0, 0, 0, 0, 0};
   if (lane < E) {
-    beg = min(max(offsets[lane], 0), rows);
-    end = min(max(offsets[lane + 1], beg), rows);
+    t.beg = min(max(offsets[lane], 0), rows);
+    t.end = min(max(offsets[lane + 1], t.beg), rows);
   }
-  const int nt = (end - beg + rows_per_tile - 1) / rows_per_tile;
+  const int nt = (t.end - t.beg + rows_per_tile - 1) / rows_per_tile;
   int inc = nt;
 #pragma unroll
   for (int s = 1; s < 64; s <<= 1) {
     const int v = __shfl_up(inc, s);
     if (lane >= s) inc += v;
   }
-  const int first = inc - nt;
-  const bool mine = lane < E && mt >= first && mt < inc;
+  t.first = inc - nt;
+  t.inc = inc;
+  t.total = __builtin_amdgcn_readlane(inc, 63);
+  return t;
+}
+
+// First row, row count and expert of tile mt from the table (n = 0: no such
+// tile), wave-uniform.  All 64 lanes call.
+__device__ __forceinline__ void routed_pick(const RoutedTiles& t, int rows_per_tile, int mt,
+                                            int& p0, int& n, int& e) {
+  const int lane = threadIdx.x & 63;
+  const bool mine = mt >= t.first && mt < t.inc;  // lanes >= E: first == inc
   const uint64_t owners = __ballot(mine);
   if (owners == 0ull) {
     p0 = 0;
@@ -194,10 +208,18 @@ __device__ __forceinline__ void routed_tile_wave(const int32_t* __restrict__ off
     return;
   }
   const int own = __ffsll((unsigned long long)owners) - 1;
-  const int my_p0 = beg + (mt - first) * rows_per_tile;
+  const int my_p0 = t.beg + (mt - t.first) * rows_per_tile;
   p0 = __builtin_amdgcn_readlane(my_p0, own);
-  n = min(rows_per_tile, __builtin_amdgcn_readlane(end, own) - p0);
+  n = min(rows_per_tile, __builtin_amdgcn_readlane(t.end, own) - p0);
   e = own;
+}
+
+// routed_tile for a one-wave workgroup: the same lookup, with the result
+// returned wave-uniform in registers (n = 0: no such tile).  All 64 lanes call.
+__device__ __forceinline__ void routed_tile_wave(const int32_t* __restrict__ offsets, int E,
+                                                 int rows, int rows_per_tile, int mt, int& p0,
+                                                 int& n, int& e) {
+  routed_pick(routed_tiles(offsets, E, rows, rows_per_tile), rows_per_tile, mt, p0, n, e);
 }
 
 // Per-row INT8 code of v given the row scale s (s > 0): clamp(rint(v / s)).

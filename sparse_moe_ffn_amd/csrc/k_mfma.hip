@@ -142,19 +142,21 @@ struct W4A8Prob {
   int32_t* isum;
 };
 
-// Workgroup b runs on XCD b % 8; logical tile ids are handed out so that
-// each XCD works on a contiguous range (same expert's weights in its L2).
-__device__ __forceinline__ int xcd_logical() {
-  const int per = (int)gridDim.x / kXcd;
-  return ((int)blockIdx.x % kXcd) * per + (int)blockIdx.x / kXcd;
-}
-
-// One tile (kMT row tiles x kNT column tiles) of problem P for logical id
-// `logical` = mt * nsplit + split.  kDense: rows are the tokens in order
-// (shared expert); otherwise routed (expert-sorted rows, tiles found from the
-// offsets).  K % 128 == 0.  Called by one whole wave.
+// Workgroup b runs on XCD b % 8 as that XCD's slot b / 8.  Each XCD works
+// through a contiguous range of logical tile ids (the same expert's weights
+// stay in its L2): slot i of XCD x takes logical id x * per + i, with per the
+// problem's tile count over 8.  A routed problem's real tile count is only
+// known from the offsets, so it is counted in the kernel (the grid is sized
+// for the worst case) and the spare slots exit; the empty tail is thereby
+// spread over the XCDs instead of idling the last ones.
+//
+// One tile (kMT row tiles x kNT column tiles) of problem P for XCD x, slot
+// i; logical id = mt * nsplit + split.  kDense: rows are the tokens in order
+// (shared expert), per_dense its slots per XCD; otherwise routed
+// (expert-sorted rows, tiles found from the offsets).  K % 128 == 0.  Called
+// by one whole wave.
 template <int kMT, int kNT, bool kGateUp, bool kCapture, bool kDense>
-__device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int logical) {
+__device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int x, int i, int per_dense) {
   static_assert(!kGateUp || kNT % 2 == 0, "gate/up tiles come in (gate, up) pairs");
   constexpr int kP = kNT / 2;  // gate/up: column pairs per wave
   constexpr int kBM = 32 * kMT;
@@ -167,15 +169,23 @@ __device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int logical) {
   float* __restrict__ out = P.out;
   int32_t* __restrict__ isum = P.isum;
   const int lane = threadIdx.x;
-  const int mt = logical / nsplit, split = logical % nsplit;
   const int rows = (int)a.rows;
-  int p0, n, e;
+  int mt, split, p0, n, e;
   if constexpr (kDense) {
+    const int logical = x * per_dense + i;
+    mt = logical / nsplit;
+    split = logical % nsplit;
     p0 = mt * kBM;
     n = min(kBM, rows - p0);
     e = 0;
   } else {
-    routed_tile_wave(a.offsets, a.E, rows, kBM, mt, p0, n, e);
+    const RoutedTiles rt = routed_tiles(a.offsets, a.E, rows, kBM);
+    const int per = (rt.total * nsplit + kXcd - 1) / kXcd;
+    if (i >= per) return;
+    const int logical = x * per + i;
+    mt = logical / nsplit;
+    split = logical % nsplit;
+    routed_pick(rt, kBM, mt, p0, n, e);
   }
   if (n <= 0) return;
   const int G = K / kGroup, h = a.h;
@@ -273,18 +283,22 @@ __device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int logical) {
 
 template <int kMT, bool kGateUp, bool kCapture, bool kDense>
 __global__ __launch_bounds__(64) void k_w4a8w(W4A8Prob P) {
-  w4a8w_tile<kMT, 2, kGateUp, kCapture, kDense>(P, xcd_logical());
+  const int b = (int)blockIdx.x;
+  w4a8w_tile<kMT, 2, kGateUp, kCapture, kDense>(P, b % kXcd, b / kXcd, (int)gridDim.x / kXcd);
 }
 
-// Routed (P0, the first n0 logical tiles) and shared (P1) products of the
-// same kind in one launch.
+// Routed (P0) and shared (P1) products of the same kind in one launch.  Every
+// XCD gets its share of both: its first per1 slots take shared tiles, the
+// rest routed tiles.  Workgroups start in slot order, so the shared tiles
+// (as long as or, for down with h_s = 4h, four times as long as a routed
+// tile) go first and the short routed ones fill in behind them.
 template <int kMT0, int kMT1, bool kGateUp>
-__global__ __launch_bounds__(64) void k_w4a8w_pair(W4A8Prob P0, W4A8Prob P1, int n0) {
-  const int l = xcd_logical();
-  if (l < n0)
-    w4a8w_tile<kMT0, 2, kGateUp, false, false>(P0, l);
+__global__ __launch_bounds__(64) void k_w4a8w_pair(W4A8Prob P0, W4A8Prob P1, int per1) {
+  const int b = (int)blockIdx.x, x = b % kXcd, i = b / kXcd;
+  if (i < per1)
+    w4a8w_tile<kMT1, 2, kGateUp, false, true>(P1, x, i, per1);
   else
-    w4a8w_tile<kMT1, 2, kGateUp, false, true>(P1, l - n0);
+    w4a8w_tile<kMT0, 2, kGateUp, false, false>(P0, x, i - per1, 0);
 }
 
 // Two row tiles per wave once that still gives at least 4 waves per SIMD
@@ -345,15 +359,16 @@ hipError_t launch_pair(const W4A8Prob& R, const W4A8Prob& D, hipStream_t st) {
   const bool r2 = two_row_tiles(R.a, R.nsplit), d2 = two_row_tiles(D.a, D.nsplit);
   const int64_t n0 = n_tiles(R.a, r2 ? 64 : 32, R.nsplit);
   const int64_t n1 = n_tiles(D.a, d2 ? 64 : 32, D.nsplit);
-  const dim3 grid(grid_of(n0 + n1));
+  const int per1 = (int)(grid_of(n1) / kXcd);
+  const dim3 grid(grid_of(n0) + grid_of(n1));
   if (r2 && d2)
-    hipLaunchKernelGGL((k_w4a8w_pair<2, 2, kGateUp>), grid, block, 0, st, R, D, (int)n0);
+    hipLaunchKernelGGL((k_w4a8w_pair<2, 2, kGateUp>), grid, block, 0, st, R, D, per1);
   else if (r2)
-    hipLaunchKernelGGL((k_w4a8w_pair<2, 1, kGateUp>), grid, block, 0, st, R, D, (int)n0);
+    hipLaunchKernelGGL((k_w4a8w_pair<2, 1, kGateUp>), grid, block, 0, st, R, D, per1);
   else if (d2)
-    hipLaunchKernelGGL((k_w4a8w_pair<1, 2, kGateUp>), grid, block, 0, st, R, D, (int)n0);
+    hipLaunchKernelGGL((k_w4a8w_pair<1, 2, kGateUp>), grid, block, 0, st, R, D, per1);
   else
-    hipLaunchKernelGGL((k_w4a8w_pair<1, 1, kGateUp>), grid, block, 0, st, R, D, (int)n0);
+    hipLaunchKernelGGL((k_w4a8w_pair<1, 1, kGateUp>), grid, block, 0, st, R, D, per1);
   return hipGetLastError();
 }
 

@@ -125,10 +125,10 @@ __global__ __launch_bounds__(256) void k_router(int64_t T, int d, int E, int k,
     for (int q = 0; q < kTok; ++q)
 #pragma unroll
       for (int i = 0; i < kNX; ++i) xv[q][i] = q < nt ? x[(t0 + q) * d + lane + kWave * i] : 0.0f;
-    if constexpr (kQuant) {
+    if constexpr (kQuant) {  // wave w quantises token w (every wave holds all kTok rows)
 #pragma unroll
       for (int q = 0; q < kTok; ++q)
-        if (q < nt) quant_row_regs(xv[q], lane, t0 + q, d, xq, sx);
+        if (q == wave && q < nt) quant_row_regs(xv[q], lane, t0 + q, d, xq, sx);
     }
     // expert rows read kRing ahead (a ring of register sets: 4 for narrow
     // rows, 2 for wide ones to keep registers for occupancy); rows past this
