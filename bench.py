@@ -44,8 +44,7 @@ def parse():
     ap.add_argument("--path", choices=("auto", "fused", "calls"), default="auto",
                     help="fused: the one-call layer (mm_moe_forward, one stream, fewest launches); "
                          "calls: the seven calls with the activation quantiser and shared expert on "
-                         "a second stream; auto: fused for decode and for prefill of up to 4096 "
-                         "tokens, calls for longer prefill (the faster of the two on each)")
+                         "a second stream; auto: fused (measured faster on every workload)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 launches) and exit: the "
@@ -180,7 +179,7 @@ def main():
     xs = [torch.from_numpy(wl.tokens(w, step=s)).to(dev) for s in range(n_inputs)]
     nxt = torch.empty((T, w.d), dtype=torch.float32, device=dev)
 
-    fused = args.path == "fused" or (args.path == "auto" and (decode or T <= 4096))
+    fused = args.path in ("fused", "auto")
 
     def fwd(L, src):
         return L.forward_fused(src) if fused else L.forward(src)

@@ -553,14 +553,33 @@ mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
   int8_t* xq = i4 ? static_cast<int8_t*>(at(W.xq)) : nullptr;
   float* sx = i4 ? static_cast<float*>(at(W.sx)) : nullptr;
 
+  // Which kernels run (INT4): gate/up and down each as the weight-streaming
+  // pair (few rows), the matrix-core pair, or separate launches; both down
+  // products streaming from the FP32 hidden rows when both fit (qin).  The
+  // matrix-core pairs read group-major activations, so x_q and the hidden
+  // codes are written that way when they are used.
+  bool gv = false, gm = false, dv = false, dm = false, qin = false;
+  bool gu_mfma_pair = false, quant_pair = false, dn_mfma_pair = false;
+  if (i4) {
+    gv = use_gemv(ar, d, true) && (!shared || use_gemv(as, d, true));
+    gm = use_mfma(ar, d) && (!shared || use_mfma(as, d));
+    dv = use_gemv(ar, h, false) && (!shared || use_gemv(as, hs, false));
+    dm = use_mfma(ar, h) && (!shared || use_mfma(as, hs));
+    qin = shared && gv && dv && mm::gemv_i4_qin_fits(h) && mm::gemv_i4_qin_fits(hs);
+    gu_mfma_pair = shared && !gv && gm && !use_gemv(ar, d, true);
+    quant_pair = (shared && gv && !qin) || gu_mfma_pair;
+    dn_mfma_pair = !qin && shared && !dv && dm && !use_gemv(ar, h, false) && quant_pair;
+  }
+
   // router + top-k (+ per-token INT8 of x), then the count sort; for a few
   // tokens all of it in one workgroup
-  if (i4 && mm::launch_front_small(T, d, E, k, desc->gating, x, w_router, bias, topk_idx, topk_w,
-                                   xq, sx, off, perm, inv, st)) {
+  if (i4 && !gu_mfma_pair &&
+      mm::launch_front_small(T, d, E, k, desc->gating, x, w_router, bias, topk_idx, topk_w, xq, sx,
+                             off, perm, inv, st)) {
     MM_TRY(hip_status(hipGetLastError(), where));
   } else {
     MM_TRY(hip_status(mm::launch_router(T, d, E, k, desc->gating, x, w_router, bias, topk_idx,
-                                        topk_w, xq, sx, st),
+                                        topk_w, xq, sx, st, gu_mfma_pair),
                       where));
     MM_TRY(hip_status(mm::launch_route(Tk, E, topk_idx, off, perm, inv,
                                        static_cast<int32_t*>(at(W.route)), st),
@@ -579,36 +598,29 @@ mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
     float* s_s = static_cast<float*>(at(W.s_s));
     // gate/up (+ SwiGLU) of both kinds, then their hidden-row quantisers
     // (weight-streaming down of both kinds: the down workgroups quantise)
-    const bool gv = use_gemv(ar, d, true) && (!shared || use_gemv(as, d, true));
-    const bool gm = use_mfma(ar, d) && (!shared || use_mfma(as, d));
-    const bool dv = use_gemv(ar, h, false) && (!shared || use_gemv(as, hs, false));
-    const bool qin = shared && gv && dv && mm::gemv_i4_qin_fits(h) && mm::gemv_i4_qin_fits(hs);
     if (shared && gv) {
       MM_TRY(hip_status(mm::launch_gateup_i4_gemv_pair(ar, as, xq, sx, gq, w_gateup.scales, sgq,
                                                        ws_gateup.scales, a_r, a_s, st), where));
-      if (!qin)
-        MM_TRY(hip_status(mm::launch_act_quant_i8_pair(Tk, h, a_r, q_r, s_r, T, hs, a_s, q_s, s_s,
-                                                       st), where));
-    } else if (shared && gm && !use_gemv(ar, d, true)) {
+    } else if (gu_mfma_pair) {
       MM_TRY(hip_status(mm::launch_gateup_i4_mfma_pair(ar, as, xq, sx, gq, w_gateup.scales, sgq,
                                                        ws_gateup.scales, a_r, a_s, st), where));
-      MM_TRY(hip_status(mm::launch_act_quant_i8_pair(Tk, h, a_r, q_r, s_r, T, hs, a_s, q_s, s_s, st),
-                        where));
     } else {
       MM_TRY(hip_status(gateup_i4(ar, xq, sx, gq, w_gateup.scales, a_r, q_r, s_r, nullptr, st), where));
       if (shared)
         MM_TRY(hip_status(gateup_i4(as, xq, sx, sgq, ws_gateup.scales, a_s, q_s, s_s, nullptr, st),
                           where));
     }
+    if (quant_pair)
+      MM_TRY(hip_status(mm::launch_act_quant_i8_pair(Tk, h, a_r, q_r, s_r, T, hs, a_s, q_s, s_s, st,
+                                                     dn_mfma_pair), where));
     // down of both kinds
-    const bool dm = use_mfma(ar, h) && (!shared || use_mfma(as, hs));
     if (qin) {
       MM_TRY(hip_status(mm::launch_down_i4_gemv_pair_f32in(ar, as, a_r, a_s, dq, w_down.scales, sdq,
                                                            ws_down.scales, f, ys, st), where));
     } else if (shared && dv) {
       MM_TRY(hip_status(mm::launch_down_i4_gemv_pair(ar, as, q_r, s_r, q_s, s_s, dq, w_down.scales,
                                                      sdq, ws_down.scales, f, ys, st), where));
-    } else if (shared && dm && !use_gemv(ar, h, false)) {
+    } else if (dn_mfma_pair) {
       MM_TRY(hip_status(mm::launch_down_i4_mfma_pair(ar, as, q_r, s_r, q_s, s_s, dq, w_down.scales,
                                                      sdq, ws_down.scales, f, ys, st), where));
     } else {

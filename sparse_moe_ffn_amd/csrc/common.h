@@ -222,6 +222,15 @@ __device__ __forceinline__ void routed_tile_wave(const int32_t* __restrict__ off
   routed_pick(routed_tiles(offsets, E, rows, rows_per_tile), rows_per_tile, mt, p0, n, e);
 }
 
+// INT8 activation matrices [R][C] are row-major, or, inside the one-call
+// layer where the matrix-core kernels read them, group-major: the 32 codes of
+// (row r, group g = c / 32) at byte (g * R + r) * 32 + c % 32, so that the 32
+// rows of one MFMA tile and one group are 1 KB of contiguous memory.  Byte
+// offset of (r, c); gm_rows = R for group-major, 0 for row-major.
+__device__ __forceinline__ int64_t act_offset(int64_t r, int64_t c, int64_t cols, int64_t gm_rows) {
+  return gm_rows ? ((c >> 5) * gm_rows + r) * 32 + (c & 31) : r * cols + c;
+}
+
 // Per-row INT8 code of v given the row scale s (s > 0): clamp(rint(v / s)).
 __device__ __forceinline__ int8_t quant_i8(float v, float s) {
   float r = rintf(v / s);

@@ -12,20 +12,21 @@ namespace {
 
 // One wave per token: the token's k sorted positions and gate weights are
 // read once and broadcast across the wave; lane l handles the float4 columns
-// l, l + 64, ...  All of a lane's gathers are issued before the sums.
+// l, l + 64, ... (kC4 of them).  The gathers of up to four expert rows and the
+// shared row are all issued before the first sum, so a wave waits for memory
+// about once per four experts.
 constexpr int kMaxC4 = 8;  // float4 columns per lane: d <= 2048
 
 // kNorm: also y_norm = y / sqrt(mean(y^2) + eps) (FP32 y only): the input of
 // the next layer in a decoder stack, from the row the wave already holds.
-template <bool kBF16Out, bool kNorm = false>
+template <int kC4, bool kBF16Out, bool kNorm>
 __global__ __launch_bounds__(256) void k_combine(int64_t T, int d, int k,
                                                  const float* __restrict__ f,
                                                  const int32_t* __restrict__ inv,
                                                  const float* __restrict__ w,
                                                  const float* __restrict__ ys,
                                                  void* __restrict__ y,
-                                                 float* __restrict__ y_norm = nullptr,
-                                                 float eps = 0.0f) {
+                                                 float* __restrict__ y_norm, float eps) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -38,38 +39,52 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int d, int k,
     if (p >= 0 && p < Tk) my_p = (int)p;  // a corrupt inverse permutation reads nothing
     my_w = w[t * k + lane];
   }
-  float4 acc[kMaxC4];
+  float4 sv[kC4];
+  if (ys) {
 #pragma unroll
-  for (int i = 0; i < kMaxC4; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const int p = __shfl(my_p, j);
-    const float wj = __shfl(my_w, j);
-    if (p < 0) continue;
-    const float4* fr = reinterpret_cast<const float4*>(f + (int64_t)p * d);
-    float4 v[kMaxC4];
+    for (int i = 0; i < kC4; ++i)
+      if (lane + 64 * i < q) sv[i] = reinterpret_cast<const float4*>(ys + t * d)[lane + 64 * i];
+  }
+  float4 acc[kC4];
 #pragma unroll
-    for (int i = 0; i < kMaxC4; ++i)
-      if (lane + 64 * i < q) v[i] = fr[lane + 64 * i];
+  for (int i = 0; i < kC4; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j0 = 0; j0 < k; j0 += 4) {
+    int pj[4];
+    float wj[4];
+    float4 v[4][kC4];
 #pragma unroll
-    for (int i = 0; i < kMaxC4; ++i)
-      if (lane + 64 * i < q) {
-        acc[i].x = fmaf(wj, v[i].x, acc[i].x);
-        acc[i].y = fmaf(wj, v[i].y, acc[i].y);
-        acc[i].z = fmaf(wj, v[i].z, acc[i].z);
-        acc[i].w = fmaf(wj, v[i].w, acc[i].w);
-      }
+    for (int jj = 0; jj < 4; ++jj) {
+      pj[jj] = j0 + jj < k ? __shfl(my_p, j0 + jj) : -1;
+      wj[jj] = __shfl(my_w, j0 + jj);
+      if (pj[jj] < 0) continue;
+      const float4* fr = reinterpret_cast<const float4*>(f + (int64_t)pj[jj] * d);
+#pragma unroll
+      for (int i = 0; i < kC4; ++i)
+        if (lane + 64 * i < q) v[jj][i] = fr[lane + 64 * i];
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      if (pj[jj] < 0) continue;
+#pragma unroll
+      for (int i = 0; i < kC4; ++i)
+        if (lane + 64 * i < q) {
+          acc[i].x = fmaf(wj[jj], v[jj][i].x, acc[i].x);
+          acc[i].y = fmaf(wj[jj], v[jj][i].y, acc[i].y);
+          acc[i].z = fmaf(wj[jj], v[jj][i].z, acc[i].z);
+          acc[i].w = fmaf(wj[jj], v[jj][i].w, acc[i].w);
+        }
+    }
   }
 #pragma unroll
-  for (int i = 0; i < kMaxC4; ++i) {
+  for (int i = 0; i < kC4; ++i) {
     const int c4 = lane + 64 * i;
     if (c4 >= q) continue;
     float4 a = acc[i];
     if (ys) {
-      const float4 s = reinterpret_cast<const float4*>(ys + t * d)[c4];
-      a.x += s.x;
-      a.y += s.y;
-      a.z += s.z;
-      a.w += s.w;
+      a.x += sv[i].x;
+      a.y += sv[i].y;
+      a.z += sv[i].z;
+      a.w += sv[i].w;
     }
     acc[i] = a;
     if (kBF16Out) {
@@ -86,7 +101,7 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int d, int k,
   if constexpr (kNorm) {
     float ss = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kMaxC4; ++i)
+    for (int i = 0; i < kC4; ++i)
       if (lane + 64 * i < q) {
         ss = fmaf(acc[i].x, acc[i].x, ss);
         ss = fmaf(acc[i].y, acc[i].y, ss);
@@ -96,7 +111,7 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int d, int k,
     ss = wave_sum(ss);
     const float inv_rms = 1.0f / sqrtf(ss / (float)d + eps);
 #pragma unroll
-    for (int i = 0; i < kMaxC4; ++i) {
+    for (int i = 0; i < kC4; ++i) {
       const int c4 = lane + 64 * i;
       if (c4 >= q) continue;
       const float4 a = acc[i];
@@ -104,6 +119,22 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int d, int k,
           make_float4(a.x * inv_rms, a.y * inv_rms, a.z * inv_rms, a.w * inv_rms);
     }
   }
+}
+
+template <int kC4>
+void launch_combine_c4(int64_t T, int d, int k, const float* f, const int32_t* inv_perm,
+                       const float* w, const float* ys, void* y, bool bf16_out, hipStream_t st,
+                       float* y_norm, float eps) {
+  const unsigned blocks = (unsigned)((T + 3) / 4);
+  if (y_norm)
+    hipLaunchKernelGGL((k_combine<kC4, false, true>), dim3(blocks), dim3(256), 0, st, T, d, k, f,
+                       inv_perm, w, ys, y, y_norm, eps);
+  else if (bf16_out)
+    hipLaunchKernelGGL((k_combine<kC4, true, false>), dim3(blocks), dim3(256), 0, st, T, d, k, f,
+                       inv_perm, w, ys, y, nullptr, 0.0f);
+  else
+    hipLaunchKernelGGL((k_combine<kC4, false, false>), dim3(blocks), dim3(256), 0, st, T, d, k, f,
+                       inv_perm, w, ys, y, nullptr, 0.0f);
 }
 
 // Wider rows: one thread per (token, float4 column).
@@ -156,16 +187,16 @@ hipError_t launch_combine(int64_t T, int d, int k, const float* f, const int32_t
                           const float* w, const float* ys, void* y, bool bf16_out,
                           hipStream_t st, float* y_norm, float eps) {
   if (d / 4 <= 64 * kMaxC4) {
-    const unsigned blocks = (unsigned)((T + 3) / 4);
-    if (y_norm)
-      hipLaunchKernelGGL((k_combine<false, true>), dim3(blocks), dim3(256), 0, st, T, d, k, f,
-                         inv_perm, w, ys, y, y_norm, eps);
-    else if (bf16_out)
-      hipLaunchKernelGGL(k_combine<true>, dim3(blocks), dim3(256), 0, st, T, d, k, f, inv_perm, w,
-                         ys, y, nullptr, 0.0f);
-    else
-      hipLaunchKernelGGL(k_combine<false>, dim3(blocks), dim3(256), 0, st, T, d, k, f, inv_perm, w,
-                         ys, y, nullptr, 0.0f);
+    switch ((d / 4 + 63) / 64) {
+      case 1: launch_combine_c4<1>(T, d, k, f, inv_perm, w, ys, y, bf16_out, st, y_norm, eps); break;
+      case 2: launch_combine_c4<2>(T, d, k, f, inv_perm, w, ys, y, bf16_out, st, y_norm, eps); break;
+      case 3: launch_combine_c4<3>(T, d, k, f, inv_perm, w, ys, y, bf16_out, st, y_norm, eps); break;
+      case 4: launch_combine_c4<4>(T, d, k, f, inv_perm, w, ys, y, bf16_out, st, y_norm, eps); break;
+      case 5: launch_combine_c4<5>(T, d, k, f, inv_perm, w, ys, y, bf16_out, st, y_norm, eps); break;
+      case 6: launch_combine_c4<6>(T, d, k, f, inv_perm, w, ys, y, bf16_out, st, y_norm, eps); break;
+      case 7: launch_combine_c4<7>(T, d, k, f, inv_perm, w, ys, y, bf16_out, st, y_norm, eps); break;
+      default: launch_combine_c4<8>(T, d, k, f, inv_perm, w, ys, y, bf16_out, st, y_norm, eps); break;
+    }
   } else {
     const unsigned blocks = (unsigned)((T * (d / 4) + 255) / 256);
     if (bf16_out)

@@ -69,18 +69,20 @@ struct WStage {
   float s[2][kNT];
 };
 
-// Loads groups g0 and g0 + 1 relative to the current pointers (the offsets
-// are compile-time constants, so they fold into the load instructions).
-// pb / ps are wave-uniform (the lane offset is added here), so the loads take
-// a scalar base and a small per-lane offset.
+// Loads groups g0 and g0 + 1 relative to the current pointers (row-major
+// activations: the offsets are compile-time constants and fold into the load
+// instructions; group-major: astride, the 16-byte units from one group to
+// the next, is the row count times 2).  pb / ps are wave-uniform (the lane
+// offset is added here), so the loads take a scalar base and a small
+// per-lane offset.
 template <int kMT, int kNT>
 __device__ __forceinline__ void wload(WStage<kMT, kNT>& st, gint4* const (&pa)[kMT],
                                       guint2* const (&pb)[kNT], gfloat* const (&ps)[kNT],
-                                      int g0, int lane) {
+                                      int g0, int lane, int astride) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
 #pragma unroll
-    for (int m = 0; m < kMT; ++m) st.a[i][m] = pa[m][(g0 + i) * (kGroup / 16)];
+    for (int m = 0; m < kMT; ++m) st.a[i][m] = pa[m][(g0 + i) * astride];
 #pragma unroll
     for (int j = 0; j < kNT; ++j) {
       st.b[i][j] = pb[j][(g0 + i) * 64 + lane];
@@ -153,9 +155,11 @@ struct W4A8Prob {
 // One tile (kMT row tiles x kNT column tiles) of problem P for XCD x, slot
 // i; logical id = mt * nsplit + split.  kDense: rows are the tokens in order
 // (shared expert), per_dense its slots per XCD; otherwise routed
-// (expert-sorted rows, tiles found from the offsets).  K % 128 == 0.  Called
-// by one whole wave.
-template <int kMT, int kNT, bool kGateUp, bool kCapture, bool kDense>
+// (expert-sorted rows, tiles found from the offsets).  kGM: the activations
+// are group-major (act_offset in common.h), so a tile's 32 rows of one group
+// are read from one contiguous kilobyte when the rows are consecutive.
+// K % 128 == 0.  Called by one whole wave.
+template <int kMT, int kNT, bool kGateUp, bool kCapture, bool kDense, bool kGM = false>
 __device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int x, int i, int per_dense) {
   static_assert(!kGateUp || kNT % 2 == 0, "gate/up tiles come in (gate, up) pairs");
   constexpr int kP = kNT / 2;  // gate/up: column pairs per wave
@@ -215,7 +219,7 @@ __device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int x, int i, int 
       src = a.perm[p0 + rr] / a.k;
       if ((unsigned)src >= (unsigned)a.T) src = 0;  // stays in bounds for a corrupt perm
     }
-    pa[m] = (gint4*)(act + (int64_t)src * K + 16 * (lane >> 5));
+    pa[m] = (gint4*)(act + (int64_t)src * (kGM ? 32 : K) + 16 * (lane >> 5));
     srow[m] = act_scale[src];
   }
   const int64_t wrows = kGateUp ? 2 * (int64_t)h : N;
@@ -229,6 +233,8 @@ __device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int x, int i, int 
     ps[j] = (gfloat*)(se + (int64_t)rb[j] * G * 32);
   }
   const Capture cap{isum, wrows, G, p0, n};
+  // activation rows: x_q has T, the hidden rows have `rows`
+  const int astride = kGM ? 2 * (int)(kGateUp ? a.T : a.rows) : kGroup / 16;
 
   v16f acc[kMT][kNT];
 #pragma unroll
@@ -240,21 +246,21 @@ __device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int x, int i, int 
   // four groups per iteration.  The last iteration's prefetch re-reads its
   // own second stage (valid addresses, result unused).  G % 4 == 0.
   WStage<kMT, kNT> s0, s1;
-  wload(s0, pa, pb, ps, 0, lane);
+  wload(s0, pa, pb, ps, 0, lane, astride);
   for (int g = 0; g < G; g += 4) {
-    wload(s1, pa, pb, ps, 2, lane);
+    wload(s1, pa, pb, ps, 2, lane, astride);
     __builtin_amdgcn_sched_barrier(0);
     wcompute<kMT, kNT, kCapture>(acc, s0, g, lane, rb, cap);
     __builtin_amdgcn_sched_barrier(0);
     const int adv = g + 4 < G ? 4 : 2;
 #pragma unroll
-    for (int m = 0; m < kMT; ++m) pa[m] += adv * (kGroup / 16);
+    for (int m = 0; m < kMT; ++m) pa[m] += adv * astride;
 #pragma unroll
     for (int j = 0; j < kNT; ++j) {
       pb[j] += adv * 64;
       ps[j] += adv * 32;
     }
-    wload(s0, pa, pb, ps, 0, lane);
+    wload(s0, pa, pb, ps, 0, lane, astride);
     __builtin_amdgcn_sched_barrier(0);
     wcompute<kMT, kNT, kCapture>(acc, s1, g + 2, lane, rb, cap);
     __builtin_amdgcn_sched_barrier(0);
@@ -287,7 +293,8 @@ __global__ __launch_bounds__(64) void k_w4a8w(W4A8Prob P) {
   w4a8w_tile<kMT, 2, kGateUp, kCapture, kDense>(P, b % kXcd, b / kXcd, (int)gridDim.x / kXcd);
 }
 
-// Routed (P0) and shared (P1) products of the same kind in one launch.  Every
+// Routed (P0) and shared (P1) products of the same kind in one launch, both
+// with group-major activations (the one-call layer writes them so).  Every
 // XCD gets its share of both: its first per1 slots take shared tiles, the
 // rest routed tiles.  Workgroups start in slot order, so the shared tiles
 // (as long as or, for down with h_s = 4h, four times as long as a routed
@@ -296,9 +303,9 @@ template <int kMT0, int kMT1, bool kGateUp>
 __global__ __launch_bounds__(64) void k_w4a8w_pair(W4A8Prob P0, W4A8Prob P1, int per1) {
   const int b = (int)blockIdx.x, x = b % kXcd, i = b / kXcd;
   if (i < per1)
-    w4a8w_tile<kMT1, 2, kGateUp, false, true>(P1, x, i, per1);
+    w4a8w_tile<kMT1, 2, kGateUp, false, true, true>(P1, x, i, per1);
   else
-    w4a8w_tile<kMT0, 2, kGateUp, false, false>(P0, x, i - per1, 0);
+    w4a8w_tile<kMT0, 2, kGateUp, false, false, true>(P0, x, i - per1, 0);
 }
 
 // Two row tiles per wave once that still gives at least 4 waves per SIMD

@@ -96,10 +96,12 @@ __global__ __launch_bounds__(256) void k_act_quant_i8(int64_t rows, int64_t cols
 
 // Same quantiser, rows with cols % 128 == 0: the row is read once as float2
 // per lane, kept in registers, and written as 2 codes per lane.  One wave per
-// row r (r < rows).
+// row r (r < rows).  gm_rows: 0 row-major codes, else group-major with that
+// many rows.
 template <int kMaxV>
 __device__ __forceinline__ void quant_row_v2(int64_t r, int64_t cols, const float* __restrict__ x,
-                                             int8_t* __restrict__ q, float* __restrict__ s) {
+                                             int8_t* __restrict__ q, float* __restrict__ s,
+                                             int64_t gm_rows) {
   const int lane = threadIdx.x & 63;
   const int nv = (int)(cols / 128);
   const float2* xr = reinterpret_cast<const float2*>(x + r * cols);
@@ -114,7 +116,6 @@ __device__ __forceinline__ void quant_row_v2(int64_t r, int64_t cols, const floa
   amax = max64(amax);
   const float sr = (2.0f * amax) / 255.0f;
   if (lane == 0) s[r] = sr;
-  uint16_t* qr = reinterpret_cast<uint16_t*>(q + r * cols);
 #pragma unroll
   for (int i = 0; i < kMaxV; ++i)
     if (i < nv) {
@@ -123,7 +124,8 @@ __device__ __forceinline__ void quant_row_v2(int64_t r, int64_t cols, const floa
         a = quant_i8(v[i].x, sr);
         b = quant_i8(v[i].y, sr);
       }
-      qr[lane + 64 * i] = (uint16_t)((uint8_t)a | ((uint16_t)(uint8_t)b << 8));
+      *reinterpret_cast<uint16_t*>(q + act_offset(r, 2 * (lane + 64 * i), cols, gm_rows)) =
+          (uint16_t)((uint8_t)a | ((uint16_t)(uint8_t)b << 8));
     }
 }
 
@@ -131,9 +133,9 @@ template <int kMaxV>
 __global__ __launch_bounds__(256) void k_act_quant_i8_v2(int64_t rows, int64_t cols,
                                                          const float* __restrict__ x,
                                                          int8_t* __restrict__ q,
-                                                         float* __restrict__ s) {
+                                                         float* __restrict__ s, int64_t gm_rows) {
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r < rows) quant_row_v2<kMaxV>(r, cols, x, q, s);
+  if (r < rows) quant_row_v2<kMaxV>(r, cols, x, q, s, gm_rows);
 }
 
 // Two row sets in one launch: blocks [0, nb0) cover set 0, the rest set 1.
@@ -142,6 +144,7 @@ struct QuantRows {
   const float* x;
   int8_t* q;
   float* s;
+  int64_t gm_rows;
 };
 
 template <int kMaxV>
@@ -149,10 +152,10 @@ __global__ __launch_bounds__(256) void k_act_quant_i8_pair(QuantRows A, QuantRow
   const int wave = threadIdx.x >> 6;
   if ((int)blockIdx.x < nb0) {
     const int64_t r = (int64_t)blockIdx.x * 4 + wave;
-    if (r < A.rows) quant_row_v2<kMaxV>(r, A.cols, A.x, A.q, A.s);
+    if (r < A.rows) quant_row_v2<kMaxV>(r, A.cols, A.x, A.q, A.s, A.gm_rows);
   } else {
     const int64_t r = (int64_t)(blockIdx.x - nb0) * 4 + wave;
-    if (r < B.rows) quant_row_v2<kMaxV>(r, B.cols, B.x, B.q, B.s);
+    if (r < B.rows) quant_row_v2<kMaxV>(r, B.cols, B.x, B.q, B.s, B.gm_rows);
   }
 }
 
@@ -197,10 +200,12 @@ hipError_t launch_prepack_int4g32(int64_t n_mat, int64_t rows, int64_t cols, con
 }
 
 hipError_t launch_act_quant_i8(int64_t rows, int64_t cols, const float* x, int8_t* q, float* s,
-                               hipStream_t st) {
+                               hipStream_t st, bool group_major) {
   if (cols % 128 == 0 && cols <= 128 * 24)
     hipLaunchKernelGGL(k_act_quant_i8_v2<24>, dim3(blocks_for(rows, 4)), dim3(256), 0, st, rows,
-                       cols, x, q, s);
+                       cols, x, q, s, group_major ? rows : (int64_t)0);
+  else if (group_major)
+    return hipErrorInvalidValue;  // group-major codes only for cols % 128 == 0
   else
     hipLaunchKernelGGL(k_act_quant_i8, dim3(blocks_for(rows, 4)), dim3(256), 0, st, rows, cols, x,
                        q, s);
@@ -209,16 +214,18 @@ hipError_t launch_act_quant_i8(int64_t rows, int64_t cols, const float* x, int8_
 
 hipError_t launch_act_quant_i8_pair(int64_t rows0, int64_t cols0, const float* x0, int8_t* q0,
                                     float* s0, int64_t rows1, int64_t cols1, const float* x1,
-                                    int8_t* q1, float* s1, hipStream_t st) {
+                                    int8_t* q1, float* s1, hipStream_t st, bool group_major) {
   auto fits = [](int64_t c) { return c % 128 == 0 && c <= 128 * 24; };
   if (!fits(cols0) || !fits(cols1)) {
-    hipError_t e = launch_act_quant_i8(rows0, cols0, x0, q0, s0, st);
+    hipError_t e = launch_act_quant_i8(rows0, cols0, x0, q0, s0, st, group_major);
     if (e != hipSuccess) return e;
-    return launch_act_quant_i8(rows1, cols1, x1, q1, s1, st);
+    return launch_act_quant_i8(rows1, cols1, x1, q1, s1, st, group_major);
   }
   const int nb0 = (int)blocks_for(rows0, 4), nb1 = (int)blocks_for(rows1, 4);
+  const int64_t g0 = group_major ? rows0 : 0, g1 = group_major ? rows1 : 0;
   hipLaunchKernelGGL(k_act_quant_i8_pair<24>, dim3(nb0 + nb1), dim3(256), 0, st,
-                     QuantRows{rows0, cols0, x0, q0, s0}, QuantRows{rows1, cols1, x1, q1, s1}, nb0);
+                     QuantRows{rows0, cols0, x0, q0, s0, g0}, QuantRows{rows1, cols1, x1, q1, s1, g1},
+                     nb0);
   return hipGetLastError();
 }
 

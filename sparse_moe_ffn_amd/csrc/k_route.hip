@@ -5,7 +5,10 @@
 // are contiguous and each expert runs one batched product on its slice.
 // Inference routing is dropless (section "Supervised fine-tuning").
 //
-// Two kernels, no host synchronisation and no order-dependent atomics:
+// Up to kOneMax slots: one workgroup does it all (k_route_one, below); past
+// that, one workgroup's scattered writes take longer than a second launch.
+// Beyond that, two kernels, no host synchronisation and no order-dependent
+// atomics:
 //   k_route_count    one workgroup per block of 256 slots: per-expert counts
 //                    of the block (integer LDS atomics; the result does not
 //                    depend on their order) -> ws[block][E].
@@ -123,6 +126,100 @@ __global__ __launch_bounds__(kBlockSlots) void k_route_scatter(
   }
 }
 
+// Whole table in one workgroup of 16 waves.  Wave w owns the contiguous
+// chunk [w * C, (w + 1) * C) of slots and walks it in rounds of 64: the lanes
+// of a round holding the same id are found with one ballot per id bit, so a
+// slot's rank among equal ids of earlier lanes is a popcount and the round's
+// count per id is added by the lowest such lane (no atomics).  Pass 1 gives
+// each wave's count per id; from those, one wave forms the expert offsets and
+// each wave's base per id (offset + counts of the earlier waves); pass 2 walks
+// the chunk again and writes perm / inv_perm.  The ids stay in registers
+// between the passes.
+constexpr int kOneWaves = 16;
+constexpr int kOneRounds = 2;  // rounds per wave: up to 16 * 64 * 2 slots
+constexpr int64_t kOneMax = (int64_t)kOneWaves * 64 * kOneRounds;
+
+__global__ __launch_bounds__(64 * kOneWaves) void k_route_one(int64_t Tk, int E,
+                                                              const int32_t* __restrict__ idx,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ perm,
+                                                              int32_t* __restrict__ inv_perm) {
+  __shared__ int wc[kOneWaves][64];  // pass 1: count per (wave, id); then base per (wave, id)
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int C = (int)((Tk + kOneWaves * 64 - 1) / (kOneWaves * 64)) * 64;  // chunk, multiple of 64
+  const int rounds = C / 64;
+  const int64_t c0 = (int64_t)wv * C;
+  wc[wv][lane] = 0;
+  int ev[kOneRounds];
+#pragma unroll
+  for (int r = 0; r < kOneRounds; ++r) {
+    ev[r] = -1;
+    const int64_t slot = c0 + r * 64 + lane;
+    if (r < rounds && slot < Tk) ev[r] = idx[slot];
+  }
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  auto same_of = [&](int eraw, bool& valid, int& e) {
+    valid = (unsigned)eraw < (unsigned)E;  // out-of-range ids are skipped
+    e = valid ? eraw : 0;
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 6; ++b) {
+      const uint64_t ones = __ballot(valid && ((e >> b) & 1));
+      same &= ((e >> b) & 1) ? ones : ~ones;
+    }
+    return same;
+  };
+  // wc[wv][.] is written by this wave only, in program order: no barrier
+  // is needed between its rounds.
+#pragma unroll
+  for (int r = 0; r < kOneRounds; ++r) {
+    if (r >= rounds) break;
+    bool valid;
+    int e;
+    const uint64_t same = same_of(ev[r], valid, e);
+    if (valid && __popcll(same & below) == 0) wc[wv][e] += __popcll(same);
+  }
+  __syncthreads();
+  if (wv == 0) {  // lane e: offsets and per-wave bases of id e
+    int tot = 0;
+    if (lane < E)
+      for (int w = 0; w < kOneWaves; ++w) tot += wc[w][lane];
+    int inc = tot;
+#pragma unroll
+    for (int s2 = 1; s2 < 64; s2 <<= 1) {
+      const int v = __shfl_up(inc, s2);
+      if (lane >= s2) inc += v;
+    }
+    int base = inc - tot;
+    if (lane < E) {
+      offsets[lane] = base;
+      if (lane == E - 1) offsets[E] = inc;
+      for (int w = 0; w < kOneWaves; ++w) {
+        const int c = wc[w][lane];
+        wc[w][lane] = base;
+        base += c;
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kOneRounds; ++r) {
+    if (r >= rounds) break;
+    bool valid;
+    int e;
+    const uint64_t same = same_of(ev[r], valid, e);
+    const int rank = __popcll(same & below);
+    int pos = 0;
+    if (valid) pos = wc[wv][e] + rank;
+    if (valid && rank == 0) wc[wv][e] += __popcll(same);  // after every lane read its base
+    if (valid) {
+      const int64_t slot = c0 + r * 64 + lane;
+      perm[pos] = (int32_t)slot;
+      inv_perm[slot] = pos;
+    }
+  }
+}
+
 }  // namespace
 
 int64_t route_blocks(int64_t Tk) { return (Tk + kBlockSlots - 1) / kBlockSlots; }
@@ -130,6 +227,11 @@ int64_t route_blocks(int64_t Tk) { return (Tk + kBlockSlots - 1) / kBlockSlots; 
 hipError_t launch_route(int64_t Tk, int E, const int32_t* idx, int32_t* offsets, int32_t* perm,
                         int32_t* inv_perm, int32_t* ws, hipStream_t st) {
   const int64_t nblk = route_blocks(Tk);
+  if (nblk > 1 && Tk <= kOneMax) {
+    hipLaunchKernelGGL(k_route_one, dim3(1), dim3(64 * kOneWaves), 0, st, Tk, E, idx, offsets, perm,
+                       inv_perm);
+    return hipGetLastError();
+  }
   if (nblk == 1) {
     hipLaunchKernelGGL(k_route_scatter<true>, dim3(1), dim3(kBlockSlots), 0, st, Tk, E, nblk, idx,
                        ws, offsets, perm, inv_perm);

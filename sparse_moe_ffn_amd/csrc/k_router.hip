@@ -79,10 +79,11 @@ __device__ __forceinline__ float quad_sum(float p) {
 // Per-token INT8 quantisation of the x row a wave holds in registers (lane l
 // holds columns l, l + 64, ...): the same rule as the row quantiser,
 // s = (2 * max|x|) / 255, q = clamp(rint(x / s)), s = 0 gives q = 0.
+// gm_rows: 0 row-major codes, else group-major with that many rows.
 template <int kNX>
 __device__ __forceinline__ void quant_row_regs(const float (&xv)[kNX], int lane, int64_t t,
                                                int d, int8_t* __restrict__ xq,
-                                               float* __restrict__ sx) {
+                                               float* __restrict__ sx, int64_t gm_rows) {
   float amax = 0.0f;
 #pragma unroll
   for (int c = 0; c < kNX; ++c) amax = fmaxf(amax, fabsf(xv[c]));
@@ -90,7 +91,8 @@ __device__ __forceinline__ void quant_row_regs(const float (&xv)[kNX], int lane,
   const float s = (2.0f * amax) / 255.0f;
   if (lane == 0) sx[t] = s;
 #pragma unroll
-  for (int c = 0; c < kNX; ++c) xq[t * d + lane + kWave * c] = s != 0.0f ? quant_i8(xv[c], s) : (int8_t)0;
+  for (int c = 0; c < kNX; ++c)
+    xq[act_offset(t, lane + kWave * c, d, gm_rows)] = s != 0.0f ? quant_i8(xv[c], s) : (int8_t)0;
 }
 
 // Workgroup = 4 waves and 4 tokens.  Phase 1: wave w takes experts w, w+4,
@@ -111,7 +113,8 @@ __global__ __launch_bounds__(256) void k_router(int64_t T, int d, int E, int k,
                                                 int32_t* __restrict__ idx,
                                                 float* __restrict__ w,
                                                 int8_t* __restrict__ xq = nullptr,
-                                                float* __restrict__ sx = nullptr) {
+                                                float* __restrict__ sx = nullptr,
+                                                int64_t gm_rows = 0) {
   __shared__ float s_part[4][16 * kTok][kRowStride];
   __shared__ float s_logit[kTok][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -128,7 +131,7 @@ __global__ __launch_bounds__(256) void k_router(int64_t T, int d, int E, int k,
     if constexpr (kQuant) {  // wave w quantises token w (every wave holds all kTok rows)
 #pragma unroll
       for (int q = 0; q < kTok; ++q)
-        if (q == wave && q < nt) quant_row_regs(xv[q], lane, t0 + q, d, xq, sx);
+        if (q == wave && q < nt) quant_row_regs(xv[q], lane, t0 + q, d, xq, sx, gm_rows);
     }
     // expert rows read kRing ahead (a ring of register sets: 4 for narrow
     // rows, 2 for wide ones to keep registers for occupancy); rows past this
@@ -201,7 +204,7 @@ template <int kGating, int kNX, bool kQuant = false>
 __global__ __launch_bounds__(64 * kSmallWaves) void k_router_small(
     int64_t T, int d, int E, int k, const float* __restrict__ x, const float* __restrict__ wr,
     const float* __restrict__ bias, int32_t* __restrict__ idx, float* __restrict__ w,
-    int8_t* __restrict__ xq = nullptr, float* __restrict__ sx = nullptr) {
+    int8_t* __restrict__ xq = nullptr, float* __restrict__ sx = nullptr, int64_t gm_rows = 0) {
   __shared__ float s_logit[64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t t = blockIdx.x;
@@ -215,7 +218,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_router_small(
 #pragma unroll
   for (int c = 0; c < kNX; ++c) xv[c] = x[t * d + lane + kWave * c];
   if constexpr (kQuant) {
-    if (wave == 0) quant_row_regs(xv, lane, t, d, xq, sx);
+    if (wave == 0) quant_row_regs(xv, lane, t, d, xq, sx, gm_rows);
   }
 #pragma unroll
   for (int i = 0; i < kSmallPer; ++i) {
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_front_small(
     float xv[kNX];
 #pragma unroll
     for (int c = 0; c < kNX; ++c) xv[c] = x[(int64_t)t * d + lane + kWave * c];
-    if (wave == (t & (kSmallWaves - 1))) quant_row_regs(xv, lane, t, d, xq, sx);
+    if (wave == (t & (kSmallWaves - 1))) quant_row_regs(xv, lane, t, d, xq, sx, 0);
 #pragma unroll
     for (int i = 0; i < kSmallPer; ++i) {
       const int e = wave + kSmallWaves * i;
@@ -323,33 +326,33 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_front_small(
 template <int kG, int kNX, bool kQ>
 void launch_router_nx(bool small, int64_t T, int d, int E, int k, const float* x, const float* wr,
                       const float* bias, int32_t* idx, float* w, int8_t* xq, float* sx,
-                      hipStream_t st) {
+                      int64_t gm, hipStream_t st) {
   if constexpr (kNX > 0 && kNX <= 20) {
     if (small) {
       hipLaunchKernelGGL((k_router_small<kG, kNX, kQ>), dim3((unsigned)T), dim3(64 * kSmallWaves),
-                         0, st, T, d, E, k, x, wr, bias, idx, w, xq, sx);
+                         0, st, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm);
       return;
     }
   }
   hipLaunchKernelGGL((k_router<kG, kNX, kQ>), dim3((unsigned)((T + kTok - 1) / kTok)), dim3(256), 0,
-                     st, T, d, E, k, x, wr, bias, idx, w, xq, sx);
+                     st, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm);
 }
 
 // Widths with a register form (d / 64 in the list below) can also quantise
 // x in the same pass (kQ); other widths never get kQ = true.
 template <int kG, bool kQ>
 void launch_router_g(bool small, int64_t T, int d, int E, int k, const float* x, const float* wr,
-                     const float* bias, int32_t* idx, float* w, int8_t* xq, float* sx,
+                     const float* bias, int32_t* idx, float* w, int8_t* xq, float* sx, int64_t gm,
                      hipStream_t st) {
   switch (d % kWave == 0 ? d / kWave : 0) {
-    case 4: launch_router_nx<kG, 4, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, st); break;
-    case 8: launch_router_nx<kG, 8, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, st); break;
-    case 12: launch_router_nx<kG, 12, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, st); break;
-    case 16: launch_router_nx<kG, 16, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, st); break;
-    case 20: launch_router_nx<kG, 20, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, st); break;
-    case 24: launch_router_nx<kG, 24, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, st); break;
-    case 32: launch_router_nx<kG, 32, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, st); break;
-    default: launch_router_nx<kG, 0, false>(small, T, d, E, k, x, wr, bias, idx, w, nullptr, nullptr, st); break;
+    case 4: launch_router_nx<kG, 4, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, st); break;
+    case 8: launch_router_nx<kG, 8, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, st); break;
+    case 12: launch_router_nx<kG, 12, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, st); break;
+    case 16: launch_router_nx<kG, 16, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, st); break;
+    case 20: launch_router_nx<kG, 20, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, st); break;
+    case 24: launch_router_nx<kG, 24, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, st); break;
+    case 32: launch_router_nx<kG, 32, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, st); break;
+    default: launch_router_nx<kG, 0, false>(small, T, d, E, k, x, wr, bias, idx, w, nullptr, nullptr, 0, st); break;
   }
 }
 
@@ -392,20 +395,21 @@ bool launch_front_small(int64_t T, int d, int E, int k, int gating, const float*
 
 hipError_t launch_router(int64_t T, int d, int E, int k, int gating, const float* x,
                          const float* wr, const float* bias, int32_t* idx, float* w,
-                         int8_t* xq, float* sx, hipStream_t st) {
+                         int8_t* xq, float* sx, hipStream_t st, bool xq_group_major) {
+  const int64_t gm = xq_group_major ? T : 0;
   // few tokens: one 16-wave workgroup per token (widths with a register form up to 1280)
   const bool small = T <= kSmallRouterT;
   const bool q = xq != nullptr && router_quant_fused(d);
   if (gating == 0) {
-    if (q) launch_router_g<0, true>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, st);
-    else launch_router_g<0, false>(small, T, d, E, k, x, wr, bias, idx, w, nullptr, nullptr, st);
+    if (q) launch_router_g<0, true>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, st);
+    else launch_router_g<0, false>(small, T, d, E, k, x, wr, bias, idx, w, nullptr, nullptr, 0, st);
   } else {
-    if (q) launch_router_g<1, true>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, st);
-    else launch_router_g<1, false>(small, T, d, E, k, x, wr, bias, idx, w, nullptr, nullptr, st);
+    if (q) launch_router_g<1, true>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, st);
+    else launch_router_g<1, false>(small, T, d, E, k, x, wr, bias, idx, w, nullptr, nullptr, 0, st);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || xq == nullptr || q) return e;
-  return launch_act_quant_i8(T, d, x, xq, sx, st);  // widths without the fused form
+  return launch_act_quant_i8(T, d, x, xq, sx, st, xq_group_major);  // widths without the fused form
 }
 
 }  // namespace mm

@@ -12,12 +12,14 @@ hipError_t launch_quantize_int4g32(int64_t rows, int64_t cols, const float* w, u
                                    float* s, hipStream_t st);
 hipError_t launch_prepack_int4g32(int64_t n_mat, int64_t rows, int64_t cols, const uint8_t* qc,
                                   const float* sc, uint8_t* qo, float* so, hipStream_t st);
+// group_major: the codes in the group-major layout (act_offset in common.h;
+// cols % 128 == 0 only), for the merged matrix-core launches.
 hipError_t launch_act_quant_i8(int64_t rows, int64_t cols, const float* x, int8_t* q, float* s,
-                               hipStream_t st);
+                               hipStream_t st, bool group_major = false);
 // Two row sets (e.g. the routed and the shared hidden rows) in one launch.
 hipError_t launch_act_quant_i8_pair(int64_t rows0, int64_t cols0, const float* x0, int8_t* q0,
                                     float* s0, int64_t rows1, int64_t cols1, const float* x1,
-                                    int8_t* q1, float* s1, hipStream_t st);
+                                    int8_t* q1, float* s1, hipStream_t st, bool group_major = false);
 hipError_t launch_convert_bf16(int64_t n, const float* x, uint16_t* y, hipStream_t st);
 hipError_t launch_rmsnorm(int64_t rows, int64_t cols, float eps, const float* x, float* y,
                           hipStream_t st);
@@ -27,7 +29,7 @@ hipError_t launch_rmsnorm(int64_t rows, int64_t cols, float eps, const float* x,
 // pass where the width has a register form, else a second kernel).
 hipError_t launch_router(int64_t T, int d, int E, int k, int gating, const float* x,
                          const float* wr, const float* bias, int32_t* idx, float* w,
-                         int8_t* xq, float* sx, hipStream_t st);
+                         int8_t* xq, float* sx, hipStream_t st, bool xq_group_major = false);
 
 // Router + top-k + INT8 of x + the count sort in one workgroup, for
 // 1 <= T <= 2 tokens (beyond that the per-token router workgroups win) and
@@ -88,8 +90,11 @@ constexpr int64_t kGemvMaxRowsDense = 64;
 // The matrix-core forms are used from this many rows on, when the reduction
 // dimension is a multiple of 128.
 constexpr int64_t kMfmaMinRows = 256;
-// Routed and shared products of one kind in a single launch (same kernels as
-// above, the routed tiles first): matrix-core and weight-streaming forms.
+// Routed and shared products of one kind in a single launch: matrix-core
+// and weight-streaming forms.  The matrix-core pair reads its INT8
+// activations (x_q [T][d] for gate/up; the hidden rows [Tk][h], [T][hs] for
+// down) in the group-major layout; the weight-streaming pair reads them
+// row-major.
 hipError_t launch_gateup_i4_mfma_pair(const ExpertArgs& ar, const ExpertArgs& as,
                                       const int8_t* xq, const float* sx, const uint8_t* wq_r,
                                       const float* ws_r, const uint8_t* wq_s, const float* ws_s,

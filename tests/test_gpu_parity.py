@@ -104,7 +104,8 @@ def test_router_ties_pick_lowest_index():
 
 # ------------------------------------------------------------ routing
 @pytest.mark.parametrize("T,E,k,skew", [(3000, 60, 4, False), (2048, 60, 4, True), (1, 60, 4, False),
-                                         (513, 1, 1, False), (100, 64, 8, True), (8192, 60, 4, True)])
+                                         (513, 1, 1, False), (100, 64, 8, True), (8192, 60, 4, True),
+                                         (400, 60, 4, False)])  # one workgroup for 257..2048 slots, else one block or two kernels
 def test_route_permute_bitexact(T, E, k, skew):
     g = rng(T * 7 + E)
     if skew:
