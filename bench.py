@@ -89,6 +89,20 @@ def kernel_of(w, T, gateup: bool):
     return ("k_gateup_i4<false>" if gateup else "k_down_i4<false>"), "row-tile"
 
 
+def pair_kernel_of(w, T):
+    """rocprofv3 name of the merged routed+shared gate/up kernel mm_moe_forward
+    launches for this workload, or None when it takes another form (mirrors
+    csrc/api.hip: neither side weight-streaming, both on the matrix cores)."""
+    if w.wfmt != "int4g32" or not w.hs or w.d % 128:
+        return None
+    rows = T * w.k
+    if rows <= 512 or rows < 256 or T <= 64:
+        return None
+    r2 = ((rows + 63) // 64 + w.E) * (w.h // 32) >= 4096
+    d2 = ((T + 63) // 64) * (w.hs // 32) >= 4096
+    return f"k_w4a8w_pair<{2 if r2 else 1}, {2 if d2 else 1}, true>"
+
+
 KERNEL_SOURCES = ["sparse_moe_ffn_amd/csrc/k_mfma.hip", "sparse_moe_ffn_amd/csrc/k_gemv.hip",
                   "sparse_moe_ffn_amd/csrc/common.h", "sparse_moe_ffn_amd/csrc/launch.h"]
 
@@ -268,6 +282,15 @@ def main():
     abuf = torch.empty((T * w.k, w.h), dtype=torch.float32, device=dev)
     if not w.hs:
         calls.remove("shared")
+    pair_kind = pair_kernel_of(w, T) if fused else None
+    if pair_kind:
+        # the merged gate/up kernel of the one-call step, on its own: FP32
+        # hidden rows from x_q in the group-major layout it reads there
+        calls.append("gateup_pair")
+        xq_gm = torch.empty((T, w.d), dtype=torch.int8, device=dev)
+        sx_gm = torch.empty((T,), dtype=torch.float32, device=dev)
+        sbuf = torch.empty((T, w.hs), dtype=torch.float32, device=dev)
+        B.act_quant_i8_layout(T, w.d, xs[0], xq_gm, sx_gm, B.MM_ACT_GROUP_MAJOR)
     # The repetitions cycle through the distinct weight sets (as the step does).
     x0 = xs[0]
     for L in layers:
@@ -292,6 +315,8 @@ def main():
             L.shared(x0, T)
         elif c == "combine":
             L.combine(T)
+        elif c == "gateup_pair":
+            L.gateup_pair_f32(T, xq_gm, abuf, sbuf)
 
     per_call_us = {}
     for c in calls:
@@ -314,14 +339,21 @@ def main():
     ops, B_r, B_s = layer_work(w, T)
     L0 = layers[0]
     n_distinct = int(np.unique(L0.idx.cpu().numpy()).size)
-    # Roofline of the dominant single kernel: the routed gate/up product
-    # (timed on its own through the FP32-output form of the gate/up call, the
-    # same kernel the step runs before its row quantiser) or the routed down
-    # product, whichever takes longer.
+    # Roofline of the dominant single kernel of the step.  One-call step with
+    # the merged matrix-core gate/up: that kernel (routed and shared gate/up
+    # in one launch), timed on its own through mm_expert_gateup_pair_f32.
+    # Otherwise the routed gate/up product (timed through the FP32-output
+    # form of the gate/up call, the same kernel the step runs before its row
+    # quantiser) or the routed down product, whichever takes longer.
     gu_key = "gateup_gemm" if "gateup_gemm" in per_call_us else "gateup"
-    dom = gu_key if per_call_us[gu_key] >= per_call_us["down"] else "down"
-    dom_ops = ops["gateup"] if dom == gu_key else ops["down"]
-    kind, path = kernel_of(w, T, dom != "down")
+    if pair_kind:
+        dom = "gateup_pair"
+        dom_ops = ops["gateup"] + ops["shared"] * 2 // 3  # shared gate/up: 2 of its 3 d x h_s products
+        kind, path = pair_kind, "matrix-core, routed + shared gate/up in one launch"
+    else:
+        dom = gu_key if per_call_us[gu_key] >= per_call_us["down"] else "down"
+        dom_ops = ops["gateup"] if dom == gu_key else ops["down"]
+        kind, path = kernel_of(w, T, dom != "down")
     if decode:
         # bytes the kernel must stream: packed weights + scales of the experts
         # selected in the step (distinct ids), counted once

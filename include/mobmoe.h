@@ -208,6 +208,24 @@ mm_status mm_route_permute(const mm_layer_desc* desc, int64_t T, const int32_t* 
 mm_status mm_act_quant_i8(int64_t rows, int64_t cols, const float* x, int8_t* q, float* scale,
                           void* stream);
 
+/* Layouts of an INT8 code matrix [rows][cols]. */
+enum {
+  MM_ACT_ROW_MAJOR = 0,   /* code (r, c) at byte r * cols + c                         */
+  MM_ACT_GROUP_MAJOR = 1  /* code (r, c) at byte ((c / 32) * rows + r) * 32 + c % 32:
+                             the 32 codes of one row and one quantisation group are
+                             contiguous, and so are consecutive rows of one group
+                             (what the merged matrix-core products read); needs
+                             cols % 128 == 0                                          */
+};
+
+/*
+ * mm_act_quant_i8 with the codes written in `layout` (MM_ACT_*); the same
+ * codes and scales.  MM_ERR_SHAPE for MM_ACT_GROUP_MAJOR with cols % 128 != 0,
+ * MM_ERR_FORMAT for an unknown layout.
+ */
+mm_status mm_act_quant_i8_layout(int64_t rows, int64_t cols, const float* x, int8_t* q,
+                                 float* scale, int32_t layout, void* stream);
+
 /*
  * Routed experts' fused gate/up product with SwiGLU (section "Custom MoE
  * kernel"), for every sorted position p of every expert e:
@@ -232,6 +250,26 @@ mm_status mm_expert_gateup_swiglu(const mm_layer_desc* desc, int64_t T, const vo
                                   const float* act_scale, const int32_t* perm,
                                   const int32_t* expert_offsets, mm_weight w_gateup, void* h,
                                   float* h_scale, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The routed experts' and the shared expert's gate/up products with SwiGLU
+ * (sections "Custom MoE kernel" and "Divide-and-conquer architecture
+ * search", Finding 3) in one launch, INT4 weights only, as mm_moe_forward
+ * runs them for larger batches: the arithmetic of mm_expert_gateup_swiglu
+ * with h_scale = NULL (FP32 hidden rows, bit-identical), from x_q in
+ * MM_ACT_GROUP_MAJOR.
+ *   xq, sx            x_q int8 [T][d] (group-major) and its FP32 scales [T]
+ *   perm, expert_offsets  from mm_route_permute
+ *   w_gateup          routed, stacked [E][2h][d]; ws_gateup shared [2h_s][d]
+ *   h_r               out: FP32 [T*k][h], sorted order
+ *   h_s               out: FP32 [T][h_s]
+ * Needs desc->wfmt == MM_W_INT4G32 (else MM_ERR_FORMAT), shared_hidden > 0
+ * and d % 128 == 0 (else MM_ERR_SHAPE).
+ */
+mm_status mm_expert_gateup_pair_f32(const mm_layer_desc* desc, int64_t T, const int8_t* xq,
+                                    const float* sx, const int32_t* perm,
+                                    const int32_t* expert_offsets, mm_weight w_gateup,
+                                    mm_weight ws_gateup, float* h_r, float* h_s, void* stream);
 
 /*
  * Routed experts' down product: f[p] = h[p] W_down[e]^T for every sorted

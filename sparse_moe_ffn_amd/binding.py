@@ -20,6 +20,7 @@ MM_W_F32, MM_W_INT4G32, MM_W_BF16 = range(3)
 MM_GATE_SOFTMAX, MM_GATE_SIGMOID_NORM = range(2)
 MM_OUT_F32, MM_OUT_BF16 = range(2)
 MM_WS_ROUTE, MM_WS_GATEUP, MM_WS_DOWN, MM_WS_SHARED, MM_WS_MAX, MM_WS_FORWARD = range(6)
+MM_ACT_ROW_MAJOR, MM_ACT_GROUP_MAJOR = range(2)
 
 WFMT = {"f32": MM_W_F32, "int4g32": MM_W_INT4G32, "bf16": MM_W_BF16}
 
@@ -30,6 +31,7 @@ EXPORTS = (
     "mm_convert_bf16", "mm_router_topk", "mm_route_permute", "mm_act_quant_i8",
     "mm_expert_gateup_swiglu", "mm_expert_down", "mm_shared_expert", "mm_combine",
     "mm_rmsnorm_f32", "mm_expert_gateup_swiglu_dbg", "mm_expert_down_dbg", "mm_moe_forward",
+    "mm_act_quant_i8_layout", "mm_expert_gateup_pair_f32",
 )
 
 
@@ -70,6 +72,9 @@ _SIGS = {
     "mm_router_topk": ([_DESC, _I64, _VP, _VP, _VP, _VP, _VP, _VP], ctypes.c_int),
     "mm_route_permute": ([_DESC, _I64, _VP, _VP, _VP, _VP, _VP, _SZ, _VP], ctypes.c_int),
     "mm_act_quant_i8": ([_I64, _I64, _VP, _VP, _VP, _VP], ctypes.c_int),
+    "mm_act_quant_i8_layout": ([_I64, _I64, _VP, _VP, _VP, _I32, _VP], ctypes.c_int),
+    "mm_expert_gateup_pair_f32": ([_DESC, _I64, _VP, _VP, _VP, _VP, Weight, Weight, _VP, _VP, _VP],
+                                  ctypes.c_int),
     "mm_expert_gateup_swiglu": ([_DESC, _I64, _VP, _VP, _VP, _VP, Weight, _VP, _VP, _VP, _SZ, _VP],
                                 ctypes.c_int),
     "mm_expert_gateup_swiglu_dbg": ([_DESC, _I64, _VP, _VP, _VP, _VP, Weight, _VP, _VP, _VP, _SZ,
@@ -175,6 +180,17 @@ def route_permute(ds, T, topk_idx, offsets, perm, inv_perm, ws, ws_bytes, stream
 def act_quant_i8(rows, cols, x, q, scale, stream=None):
     _check(load().mm_act_quant_i8(rows, cols, _ptr(x), _ptr(q), _ptr(scale), _stream(stream)),
            "mm_act_quant_i8")
+
+
+def act_quant_i8_layout(rows, cols, x, q, scale, layout, stream=None):
+    _check(load().mm_act_quant_i8_layout(rows, cols, _ptr(x), _ptr(q), _ptr(scale), layout,
+                                         _stream(stream)), "mm_act_quant_i8_layout")
+
+
+def expert_gateup_pair_f32(ds, T, xq, sx, perm, offsets, w_gu, ws_gu, h_r, h_s, stream=None):
+    _check(load().mm_expert_gateup_pair_f32(ctypes.byref(ds), T, _ptr(xq), _ptr(sx), _ptr(perm),
+                                            _ptr(offsets), w_gu, ws_gu, _ptr(h_r), _ptr(h_s),
+                                            _stream(stream)), "mm_expert_gateup_pair_f32")
 
 
 def expert_gateup_swiglu(ds, T, act, act_scale, perm, offsets, w, h, h_scale, ws, ws_bytes,

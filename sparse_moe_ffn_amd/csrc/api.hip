@@ -374,6 +374,51 @@ static mm_status gateup_impl(const mm_layer_desc* desc, int64_t T, const void* a
   return hip_status(mm::launch_gateup_fp(a, false, act, w.data, h, st), "mm_expert_gateup_swiglu");
 }
 
+mm_status mm_act_quant_i8_layout(int64_t rows, int64_t cols, const float* x, int8_t* q,
+                                 float* scale, int32_t layout, void* stream) {
+  if (layout != MM_ACT_ROW_MAJOR && layout != MM_ACT_GROUP_MAJOR)
+    return fail(MM_ERR_FORMAT, "unknown activation layout %d", (int)layout);
+  if (rows < 0 || cols <= 0) return fail(MM_ERR_SHAPE, "bad shape");
+  if (layout == MM_ACT_GROUP_MAJOR && cols % 128 != 0)
+    return fail(MM_ERR_SHAPE, "group-major codes need cols %% 128 == 0");
+  if (rows == 0) return MM_OK;
+  MM_REQUIRE(x);
+  MM_REQUIRE(q);
+  MM_REQUIRE(scale);
+  return hip_status(mm::launch_act_quant_i8(rows, cols, x, q, scale, S(stream),
+                                            layout == MM_ACT_GROUP_MAJOR),
+                    "mm_act_quant_i8_layout");
+}
+
+mm_status mm_expert_gateup_pair_f32(const mm_layer_desc* desc, int64_t T, const int8_t* xq,
+                                    const float* sx, const int32_t* perm,
+                                    const int32_t* expert_offsets, mm_weight w_gateup,
+                                    mm_weight ws_gateup, float* h_r, float* h_s, void* stream) {
+  MM_TRY(check_desc(desc));
+  MM_TRY(check_T(desc, T));
+  if (desc->wfmt != MM_W_INT4G32) return fail(MM_ERR_FORMAT, "the merged gate/up takes INT4 weights");
+  if (desc->shared_hidden <= 0) return fail(MM_ERR_SHAPE, "the merged gate/up needs a shared expert");
+  if (desc->d_model % 128 != 0) return fail(MM_ERR_SHAPE, "the merged gate/up needs d %% 128 == 0");
+  if (T == 0) return MM_OK;
+  MM_REQUIRE(xq);
+  MM_REQUIRE(sx);
+  MM_REQUIRE(perm);
+  MM_REQUIRE(expert_offsets);
+  MM_REQUIRE(h_r);
+  MM_REQUIRE(h_s);
+  MM_TRY(check_weight(desc, w_gateup, "w_gateup"));
+  MM_TRY(check_weight(desc, ws_gateup, "ws_gateup"));
+  const int k = desc->top_k;
+  const mm::ExpertArgs ar{T * k, T, desc->d_model, desc->hidden, desc->n_experts, k, perm,
+                          expert_offsets};
+  const mm::ExpertArgs as{T, T, desc->d_model, desc->shared_hidden, 1, 1, nullptr, nullptr};
+  return hip_status(mm::launch_gateup_i4_mfma_pair(
+                        ar, as, xq, sx, static_cast<const uint8_t*>(w_gateup.data), w_gateup.scales,
+                        static_cast<const uint8_t*>(ws_gateup.data), ws_gateup.scales, h_r, h_s,
+                        S(stream)),
+                    "mm_expert_gateup_pair_f32");
+}
+
 mm_status mm_expert_gateup_swiglu(const mm_layer_desc* desc, int64_t T, const void* act,
                                   const float* act_scale, const int32_t* perm,
                                   const int32_t* expert_offsets, mm_weight w_gateup, void* h,

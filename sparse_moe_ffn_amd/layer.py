@@ -152,6 +152,15 @@ class MoELayer:
         B.expert_gateup_swiglu(self.desc, T, a, s, self.perm, self.offsets, self.w_gu.c(), out,
                                None, None, 0)
 
+    def gateup_pair_f32(self, T, xq_gm, h_r, h_s):
+        """Routed and shared gate/up + SwiGLU in one launch, FP32 hidden rows
+        into h_r [T*k, h] (sorted order) and h_s [T, h_s], from x_q in the
+        group-major layout (with this layer's scales self.sx): the merged
+        matrix-core kernel mm_moe_forward runs for larger batches, on its own
+        (INT4 weights, shared expert)."""
+        B.expert_gateup_pair_f32(self.desc, T, xq_gm, self.sx, self.perm, self.offsets,
+                                 self.w_gu.c(), self.ws_gu.c(), h_r, h_s)
+
     def down(self, T, isum=None):
         B.expert_down(self.desc, T, self.hbuf, self.hscale, self.offsets, self.w_d.c(), self.f,
                       self.wk_dn, self.wk_dn_bytes, isum=isum)

@@ -165,3 +165,27 @@ def test_forward_checks(lib):
     noshared = B.desc(768, 60, 384, 0, 4)
     zero = B.Weight(None, None)
     assert B.workspace_bytes(noshared, 2048, B.MM_WS_FORWARD) < need
+
+
+def test_layout_and_pair_checks(lib):
+    """mm_act_quant_i8_layout and mm_expert_gateup_pair_f32 validate before any launch."""
+    I32 = ctypes.c_int32
+    assert lib.mm_act_quant_i8_layout(4, 768, FAKE, FAKE, FAKE, I32(2), None) == B.MM_ERR_FORMAT
+    assert lib.mm_act_quant_i8_layout(4, 704, FAKE, FAKE, FAKE, I32(B.MM_ACT_GROUP_MAJOR),
+                                      None) == B.MM_ERR_SHAPE
+    assert lib.mm_act_quant_i8_layout(4, 768, None, FAKE, FAKE, I32(B.MM_ACT_GROUP_MAJOR),
+                                      None) == B.MM_ERR_NULL
+    assert lib.mm_act_quant_i8_layout(0, 768, None, None, None, I32(B.MM_ACT_ROW_MAJOR),
+                                      None) == B.MM_OK
+    ds = S()
+    w = B.Weight(FAKE, FAKE)
+    args = lambda d, T, x, wu: (ctypes.byref(d), T, x, FAKE, FAKE, FAKE, wu, wu, FAKE, FAKE, None)
+    assert lib.mm_expert_gateup_pair_f32(*args(ds, 0, None, w)) == B.MM_OK
+    assert lib.mm_expert_gateup_pair_f32(*args(ds, 4, None, w)) == B.MM_ERR_NULL
+    assert lib.mm_expert_gateup_pair_f32(*args(ds, 4, FAKE, B.Weight(FAKE, None))) == B.MM_ERR_NULL
+    bf = B.desc(768, 60, 384, 1536, 4, "bf16")
+    assert lib.mm_expert_gateup_pair_f32(*args(bf, 4, FAKE, B.Weight(FAKE, None))) == B.MM_ERR_FORMAT
+    noshared = B.desc(768, 60, 384, 0, 4)
+    assert lib.mm_expert_gateup_pair_f32(*args(noshared, 4, FAKE, w)) == B.MM_ERR_SHAPE
+    odd = B.desc(704, 60, 320, 640, 4)
+    assert lib.mm_expert_gateup_pair_f32(*args(odd, 4, FAKE, w)) == B.MM_ERR_SHAPE

@@ -198,6 +198,44 @@ def test_expert_stages_int4(name, T, over):
     assert np.array_equal(np_(layer.f), f_ref)
 
 
+@pytest.mark.parametrize("name,T,over", [("s_prefill", 200, {}), ("s_prefill", 37, {}),
+                                         ("m_prefill", 300, {}), ("l_prefill", 130, {})])
+def test_gateup_pair_f32(name, T, over):
+    """The merged routed+shared gate/up launch (mm_expert_gateup_pair_f32) from
+    group-major x_q: the group-major codes are the row-major ones moved, and the
+    FP32 hidden rows equal the single gate/up call's and the oracle's."""
+    w = wl.WORKLOADS[name].with_(T=T, **over)
+    lw = wl.layer_weights(w)
+    x = wl.tokens(w)
+    layer = make_layer(w, lw)
+    xd = dev(x)
+    layer.buffers(T)
+    layer.router(xd, T)
+    layer.route(T)
+    layer.act_quant(xd, T)
+    G = w.d // 32
+    xq_gm = torch.empty((T, w.d), dtype=torch.int8, device=DEV)
+    sx_gm = torch.empty((T,), dtype=torch.float32, device=DEV)
+    B.act_quant_i8_layout(T, w.d, xd, xq_gm, sx_gm, B.MM_ACT_GROUP_MAJOR)
+    rm = np_(layer.xq)
+    assert np.array_equal(np_(xq_gm).reshape(G, T, 32), rm.reshape(T, G, 32).transpose(1, 0, 2))
+    assert np.array_equal(np_(sx_gm), np_(layer.sx))
+    rows = T * w.k
+    h_r = torch.empty((rows, w.h), dtype=torch.float32, device=DEV)
+    h_s = torch.empty((T, w.hs), dtype=torch.float32, device=DEV)
+    layer.gateup_pair_f32(T, xq_gm, h_r, h_s)
+    a_one = torch.empty((rows, w.h), dtype=torch.float32, device=DEV)
+    layer.gateup_f32(xd, T, a_one)
+    assert np.array_equal(np_(h_r), np_(a_one))
+    a_ref = _sorted_reference(layer, w, lw, x)[5]
+    assert np.array_equal(np_(h_r), a_ref)
+    xq, sx = oracle.quant_act_i8(x)
+    gq, gs = oracle.quant_w4g32(lw.ws_gu)
+    dq, dsc = oracle.quant_w4g32(lw.ws_d)
+    a_s = oracle.ffn_w4a8(xq, sx, gq, gs, dq, dsc, want_a=True)[-1]
+    assert np.array_equal(np_(h_s), a_s)
+
+
 # ------------------------------------------------------------ whole layer
 CASES = [
     ("tiny_f32", 128, {}),
