@@ -216,54 +216,66 @@ def main():
         else:
             fwd(layers[s % n_inst], xs[0])
 
-    # The step is replayed from HIP graphs (one per weight set; for the decode
-    # stack one graph for all layers): launches are recorded once.  The decode
-    # input is copied into the graph's static input buffer before each replay.
-    graphs = []
+    # The steps are replayed from HIP graphs: the W warm-up steps are recorded
+    # into one graph and the K timed steps into another, replayed once each
+    # (as a model's forward graph holds all of its layers, the per-replay
+    # launch cost is paid once for the whole sequence, not once per step).
+    # Prefill step s runs weight set s % n_inst; a decode step copies its
+    # fresh input into the stack's input buffer, then runs the whole stack.
     if args.eager:
-        step = eager_step
-    else:
-        if decode:
-            xin = torch.empty((T, w.d), dtype=torch.float32, device=dev)
-            for L in layers:
-                L.buffers(T)
-            warm = torch.cuda.Stream(device=dev)
-            warm.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(warm):
-                xin.copy_(xs[0])
-            torch.cuda.current_stream().wait_stream(warm)
+        def run_warmup():
+            for s in range(args.warmup):
+                eager_step(s)
 
-            def stack(src):
-                cur = src
+        def run_timed():
+            for s in range(args.warmup, args.warmup + args.steps):
+                eager_step(s)
+    else:
+        xin = torch.empty((T, w.d), dtype=torch.float32, device=dev)
+        for L in layers:
+            L.buffers(T)
+
+        def graph_step(s: int):
+            if decode:
+                xin.copy_(xs[s % n_inputs])
+                cur = xin
                 for L in layers:
                     layer_then_norm(L, cur, nxt)
                     cur = nxt
+            else:
+                fwd(layers[s % n_inst], xs[0])
 
-            stack(xin)
-            torch.cuda.synchronize()
+        side = torch.cuda.Stream(device=dev)  # first (uncaptured) run of every launch
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for s in range(n_inst if not decode else 1):
+                graph_step(s)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+
+        def record(s0: int, n: int):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                stack(xin)
-            graphs.append(g)
+                for s in range(s0, s0 + n):
+                    graph_step(s)
+            return g
 
-            def step(s: int):
-                xin.copy_(xs[s % n_inputs])
-                graphs[0].replay()
-        else:
-            for L in layers:
-                graphs.append(L.capture(xs[0], fused=fused))
+        g_warm = record(0, args.warmup) if args.warmup else None
+        g_timed = record(args.warmup, args.steps)
 
-            def step(s: int):
-                graphs[s % n_inst].replay()
+        def run_warmup():
+            if g_warm is not None:
+                g_warm.replay()
 
-    for s in range(args.warmup):
-        step(s)
+        def run_timed():
+            g_timed.replay()
+
+    run_warmup()
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(st)
-    for s in range(args.steps):
-        step(args.warmup + s)
+    run_timed()
     e1.record(st)
     e1.synchronize()
     torch.cuda.synchronize()

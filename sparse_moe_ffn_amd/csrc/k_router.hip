@@ -128,11 +128,6 @@ __global__ __launch_bounds__(256) void k_router(int64_t T, int d, int E, int k,
     for (int q = 0; q < kTok; ++q)
 #pragma unroll
       for (int i = 0; i < kNX; ++i) xv[q][i] = q < nt ? x[(t0 + q) * d + lane + kWave * i] : 0.0f;
-    if constexpr (kQuant) {  // wave w quantises token w (every wave holds all kTok rows)
-#pragma unroll
-      for (int q = 0; q < kTok; ++q)
-        if (q == wave && q < nt) quant_row_regs(xv[q], lane, t0 + q, d, xq, sx, gm_rows);
-    }
     // expert rows read kRing ahead (a ring of register sets: 4 for narrow
     // rows, 2 for wide ones to keep registers for occupancy); rows past this
     // wave's last expert re-read expert E-1 (valid, unused)
@@ -145,6 +140,13 @@ __global__ __launch_bounds__(256) void k_router(int64_t T, int d, int E, int k,
     };
 #pragma unroll
     for (int i = 0; i < kRing; ++i) load_row(i, wv[i]);
+    // wave w quantises token w (every wave holds all kTok rows), while the
+    // first expert rows are in flight
+    if constexpr (kQuant) {
+#pragma unroll
+      for (int q = 0; q < kTok; ++q)
+        if (q == wave && q < nt) quant_row_regs(xv[q], lane, t0 + q, d, xq, sx, gm_rows);
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (i < ne) {
