@@ -113,7 +113,8 @@ FwdWs fwd_ws(const mm_layer_desc* d, int64_t T) {
   w.off = take((size_t)(d->n_experts + 1) * 4);
   w.perm = take((size_t)Tk * 4);
   w.inv = take((size_t)Tk * 4);
-  w.route = take((size_t)mm::route_blocks(Tk) * d->n_experts * 4);
+  w.route = take(std::max((size_t)mm::route_blocks(Tk) * d->n_experts * 4,
+                          (size_t)d->n_experts * (size_t)mm::route_hist_stride(T)));
   w.xq = take(i4 ? (size_t)T * dm : 0);
   w.sx = take(i4 ? (size_t)T * 4 : 0);
   w.xb = take(bf ? (size_t)T * dm * 2 : 0);
@@ -623,12 +624,20 @@ mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
                              off, perm, inv, st)) {
     MM_TRY(hip_status(hipGetLastError(), where));
   } else {
+    // many tokens: the router also counts the experts of each of its
+    // workgroups, and the count sort is one kernel
+    const bool hist = mm::route_hist_applies(T, k);
+    uint8_t* hbuf = hist ? static_cast<uint8_t*>(at(W.route)) : nullptr;
     MM_TRY(hip_status(mm::launch_router(T, d, E, k, desc->gating, x, w_router, bias, topk_idx,
-                                        topk_w, xq, sx, st, gu_mfma_pair),
+                                        topk_w, xq, sx, st, gu_mfma_pair, hbuf,
+                                        hist ? mm::route_hist_stride(T) : 0),
                       where));
-    MM_TRY(hip_status(mm::launch_route(Tk, E, topk_idx, off, perm, inv,
-                                       static_cast<int32_t*>(at(W.route)), st),
-                      where));
+    if (hist)
+      MM_TRY(hip_status(mm::launch_route_hist(T, k, E, topk_idx, hbuf, off, perm, inv, st), where));
+    else
+      MM_TRY(hip_status(mm::launch_route(Tk, E, topk_idx, off, perm, inv,
+                                         static_cast<int32_t*>(at(W.route)), st),
+                        where));
   }
   if (i4) {
     const uint8_t* gq = static_cast<const uint8_t*>(w_gateup.data);

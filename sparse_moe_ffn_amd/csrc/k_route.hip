@@ -41,13 +41,21 @@ __global__ __launch_bounds__(kBlockSlots) void k_route_count(int64_t Tk, int E,
   if (tid < E) counts[(int64_t)blockIdx.x * E + tid] = cnt[tid];
 }
 
-// kSingle: the whole table fits one block (T*k <= 256, decode batches); the
-// block counts its own slots and no count table is read.
-template <bool kSingle>
+// Sources of the per-expert counts of the earlier blocks and of all blocks:
+// kCounts the table of k_route_count; kSingle none (the whole table fits one
+// block, T*k <= 256, decode batches: the block counts its own slots); kHist
+// the router's per-workgroup counts (4 tokens, 4k slots each; bytes
+// hist[e * hstride + b], b < nrb; rpb router workgroups per block), so no
+// counting kernel runs.
+enum { kCounts = 0, kSingle = 1, kHist = 2 };
+
+template <int kMode>
 __global__ __launch_bounds__(kBlockSlots) void k_route_scatter(
     int64_t Tk, int E, int64_t nblk, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+    const uint8_t* __restrict__ hist = nullptr, int64_t nrb = 0, int64_t hstride = 0,
+    int rpb = 0) {
   __shared__ int part_before[4][64];
   __shared__ int part_total[4][64];
   __shared__ int base[64];    // offsets[e] + count of e in earlier blocks
@@ -55,7 +63,7 @@ __global__ __launch_bounds__(kBlockSlots) void k_route_scatter(
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t blk = blockIdx.x;
 
-  if constexpr (kSingle) {
+  if constexpr (kMode == kSingle) {
     part_before[wv][lane] = 0;
     part_total[wv][lane] = 0;
     wcnt[wv][lane] = 0;
@@ -64,6 +72,28 @@ __global__ __launch_bounds__(kBlockSlots) void k_route_scatter(
       const int e = idx[tid];
       if ((unsigned)e < (unsigned)E) atomicAdd(&part_total[0][e], 1);
     }
+  } else if constexpr (kMode == kHist) {
+    // expert `lane`, quarter `wv` of the router workgroups, 16 bytes a load
+    // (hstride % 64 == 0; bytes past nrb are not counted)
+    int before = 0, total = 0;
+    if (lane < E) {
+      const int64_t q = hstride / 4, b0 = wv * q, bend = blk * rpb;  // router blocks before this block
+      const uint4* row = reinterpret_cast<const uint4*>(hist + (int64_t)lane * hstride + b0);
+      for (int64_t c = 0; c < q / 16; ++c) {
+        const uint4 v = row[c];
+        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int64_t b = b0 + 16 * c + i;
+          const int n = (int)((wd[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+          if (b < nrb) total += n;
+          if (b < bend) before += n;
+        }
+      }
+    }
+    part_before[wv][lane] = before;
+    part_total[wv][lane] = total;
+    wcnt[wv][lane] = 0;
   } else {
     // Per-expert sums over blocks: 4 threads per expert, interleaved blocks.
     int before = 0, total = 0;
@@ -233,15 +263,34 @@ hipError_t launch_route(int64_t Tk, int E, const int32_t* idx, int32_t* offsets,
     return hipGetLastError();
   }
   if (nblk == 1) {
-    hipLaunchKernelGGL(k_route_scatter<true>, dim3(1), dim3(kBlockSlots), 0, st, Tk, E, nblk, idx,
-                       ws, offsets, perm, inv_perm);
+    hipLaunchKernelGGL(k_route_scatter<kSingle>, dim3(1), dim3(kBlockSlots), 0, st, Tk, E, nblk, idx,
+                       ws, offsets, perm, inv_perm, nullptr, 0, 0, 0);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(k_route_count, dim3((unsigned)nblk), dim3(kBlockSlots), 0, st, Tk, E, idx, ws);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_route_scatter<false>, dim3((unsigned)nblk), dim3(kBlockSlots), 0, st, Tk, E, nblk,
-                     idx, ws, offsets, perm, inv_perm);
+  hipLaunchKernelGGL(k_route_scatter<kCounts>, dim3((unsigned)nblk), dim3(kBlockSlots), 0, st, Tk, E,
+                     nblk, idx, ws, offsets, perm, inv_perm, nullptr, 0, 0, 0);
+  return hipGetLastError();
+}
+
+int64_t route_hist_stride(int64_t T) { return ((T + 3) / 4 + 63) / 64 * 64; }
+
+// Where launch_route would run the two-kernel sort and the router writes
+// the histogram (more than 64 tokens: the 4-token router form).
+bool route_hist_applies(int64_t T, int k) {
+  return T > 64 && T * k > kOneMax && kBlockSlots % (4 * k) == 0;
+}
+
+hipError_t launch_route_hist(int64_t T, int k, int E, const int32_t* idx, const uint8_t* hist,
+                             int32_t* offsets, int32_t* perm, int32_t* inv_perm, hipStream_t st) {
+  const int64_t Tk = T * k, nblk = route_blocks(Tk);
+  if (kBlockSlots % (4 * k) != 0) return hipErrorInvalidValue;
+  const int rpb = kBlockSlots / (4 * k);  // 4-token router workgroups per block of slots
+  hipLaunchKernelGGL(k_route_scatter<kHist>, dim3((unsigned)nblk), dim3(kBlockSlots), 0, st, Tk, E,
+                     nblk, idx, nullptr, offsets, perm, inv_perm, hist, (T + 3) / 4,
+                     route_hist_stride(T), rpb);
   return hipGetLastError();
 }
 

@@ -104,7 +104,10 @@ __device__ __forceinline__ void quant_row_regs(const float (&xv)[kNX], int lane,
 // the logit.  Phase 3: wave w takes token w, lane e holding the logit of
 // expert e, and does the top-k and the gate weights.
 // kNX = d / 64 (0: any d, row read from memory in the loop).  kQuant (kNX > 0
-// only): also writes the tokens' INT8 rows xq and scales sx.
+// only): also writes the tokens' INT8 rows xq and scales sx.  hist (may be
+// NULL): the workgroup's count of each expert over its kTok tokens' k picks,
+// one byte at hist[e * hist_stride + blockIdx.x] for e < E (the count sort
+// reads it instead of counting the ids again).
 template <int kGating, int kNX, bool kQuant = false>
 __global__ __launch_bounds__(256) void k_router(int64_t T, int d, int E, int k,
                                                 const float* __restrict__ x,
@@ -114,10 +117,14 @@ __global__ __launch_bounds__(256) void k_router(int64_t T, int d, int E, int k,
                                                 float* __restrict__ w,
                                                 int8_t* __restrict__ xq = nullptr,
                                                 float* __restrict__ sx = nullptr,
-                                                int64_t gm_rows = 0) {
+                                                int64_t gm_rows = 0,
+                                                uint8_t* __restrict__ hist = nullptr,
+                                                int64_t hist_stride = 0) {
   __shared__ float s_part[4][16 * kTok][kRowStride];
   __shared__ float s_logit[kTok][64];
+  __shared__ int s_hist[64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (hist != nullptr && threadIdx.x < 64) s_hist[threadIdx.x] = 0;
   const int64_t t0 = (int64_t)blockIdx.x * kTok;
   const int nt = (int)min((int64_t)kTok, T - t0);
   const int ne = (E - wave + 3) / 4;  // experts of this wave
@@ -189,10 +196,23 @@ __global__ __launch_bounds__(256) void k_router(int64_t T, int d, int E, int k,
     s_logit[q][e] = p[0] + (bias ? bias[e] : 0.0f);
   }
   __syncthreads();
-  if (wave >= nt) return;
-  const int64_t t = t0 + wave;
-  const float mine = lane < E ? s_logit[wave][lane] : -INFINITY;
-  select_topk<kGating>(mine, lane, E, k, idx + t * k, w + t * k);
+  if (wave < nt) {
+    const int64_t t = t0 + wave;
+    const float mine = lane < E ? s_logit[wave][lane] : -INFINITY;
+    int sel;
+    float wv;
+    select_topk_lanes<kGating>(mine, lane, E, k, sel, wv);
+    if (lane < k) {
+      idx[t * k + lane] = sel;
+      w[t * k + lane] = wv;
+      if (hist != nullptr) atomicAdd(&s_hist[sel], 1);  // a count: order does not matter
+    }
+  }
+  if (hist != nullptr) {
+    __syncthreads();
+    if ((int)threadIdx.x < E)
+      hist[threadIdx.x * hist_stride + blockIdx.x] = (uint8_t)s_hist[threadIdx.x];
+  }
 }
 
 // Few tokens (decode): one token per workgroup of 16 waves; wave w takes
@@ -328,7 +348,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_front_small(
 template <int kG, int kNX, bool kQ>
 void launch_router_nx(bool small, int64_t T, int d, int E, int k, const float* x, const float* wr,
                       const float* bias, int32_t* idx, float* w, int8_t* xq, float* sx,
-                      int64_t gm, hipStream_t st) {
+                      int64_t gm, uint8_t* g_hist, int64_t g_hist_stride, hipStream_t st) {
   if constexpr (kNX > 0 && kNX <= 20) {
     if (small) {
       hipLaunchKernelGGL((k_router_small<kG, kNX, kQ>), dim3((unsigned)T), dim3(64 * kSmallWaves),
@@ -337,7 +357,7 @@ void launch_router_nx(bool small, int64_t T, int d, int E, int k, const float* x
     }
   }
   hipLaunchKernelGGL((k_router<kG, kNX, kQ>), dim3((unsigned)((T + kTok - 1) / kTok)), dim3(256), 0,
-                     st, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm);
+                     st, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, g_hist, g_hist_stride);
 }
 
 // Widths with a register form (d / 64 in the list below) can also quantise
@@ -345,16 +365,16 @@ void launch_router_nx(bool small, int64_t T, int d, int E, int k, const float* x
 template <int kG, bool kQ>
 void launch_router_g(bool small, int64_t T, int d, int E, int k, const float* x, const float* wr,
                      const float* bias, int32_t* idx, float* w, int8_t* xq, float* sx, int64_t gm,
-                     hipStream_t st) {
+                     uint8_t* hist, int64_t hist_stride, hipStream_t st) {
   switch (d % kWave == 0 ? d / kWave : 0) {
-    case 4: launch_router_nx<kG, 4, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, st); break;
-    case 8: launch_router_nx<kG, 8, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, st); break;
-    case 12: launch_router_nx<kG, 12, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, st); break;
-    case 16: launch_router_nx<kG, 16, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, st); break;
-    case 20: launch_router_nx<kG, 20, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, st); break;
-    case 24: launch_router_nx<kG, 24, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, st); break;
-    case 32: launch_router_nx<kG, 32, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, st); break;
-    default: launch_router_nx<kG, 0, false>(small, T, d, E, k, x, wr, bias, idx, w, nullptr, nullptr, 0, st); break;
+    case 4: launch_router_nx<kG, 4, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, hist, hist_stride, st); break;
+    case 8: launch_router_nx<kG, 8, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, hist, hist_stride, st); break;
+    case 12: launch_router_nx<kG, 12, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, hist, hist_stride, st); break;
+    case 16: launch_router_nx<kG, 16, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, hist, hist_stride, st); break;
+    case 20: launch_router_nx<kG, 20, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, hist, hist_stride, st); break;
+    case 24: launch_router_nx<kG, 24, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, hist, hist_stride, st); break;
+    case 32: launch_router_nx<kG, 32, kQ>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, hist, hist_stride, st); break;
+    default: launch_router_nx<kG, 0, false>(small, T, d, E, k, x, wr, bias, idx, w, nullptr, nullptr, 0, hist, hist_stride, st); break;
   }
 }
 
@@ -397,17 +417,19 @@ bool launch_front_small(int64_t T, int d, int E, int k, int gating, const float*
 
 hipError_t launch_router(int64_t T, int d, int E, int k, int gating, const float* x,
                          const float* wr, const float* bias, int32_t* idx, float* w,
-                         int8_t* xq, float* sx, hipStream_t st, bool xq_group_major) {
+                         int8_t* xq, float* sx, hipStream_t st, bool xq_group_major,
+                         uint8_t* hist, int64_t hist_stride) {
   const int64_t gm = xq_group_major ? T : 0;
   // few tokens: one 16-wave workgroup per token (widths with a register form up to 1280)
   const bool small = T <= kSmallRouterT;
+  if (hist != nullptr && small) return hipErrorInvalidValue;  // the per-token form counts nothing
   const bool q = xq != nullptr && router_quant_fused(d);
   if (gating == 0) {
-    if (q) launch_router_g<0, true>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, st);
-    else launch_router_g<0, false>(small, T, d, E, k, x, wr, bias, idx, w, nullptr, nullptr, 0, st);
+    if (q) launch_router_g<0, true>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, hist, hist_stride, st);
+    else launch_router_g<0, false>(small, T, d, E, k, x, wr, bias, idx, w, nullptr, nullptr, 0, hist, hist_stride, st);
   } else {
-    if (q) launch_router_g<1, true>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, st);
-    else launch_router_g<1, false>(small, T, d, E, k, x, wr, bias, idx, w, nullptr, nullptr, 0, st);
+    if (q) launch_router_g<1, true>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, hist, hist_stride, st);
+    else launch_router_g<1, false>(small, T, d, E, k, x, wr, bias, idx, w, nullptr, nullptr, 0, hist, hist_stride, st);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || xq == nullptr || q) return e;

@@ -29,7 +29,10 @@ hipError_t launch_rmsnorm(int64_t rows, int64_t cols, float eps, const float* x,
 // pass where the width has a register form, else a second kernel).
 hipError_t launch_router(int64_t T, int d, int E, int k, int gating, const float* x,
                          const float* wr, const float* bias, int32_t* idx, float* w,
-                         int8_t* xq, float* sx, hipStream_t st, bool xq_group_major = false);
+                         int8_t* xq, float* sx, hipStream_t st, bool xq_group_major = false,
+                         uint8_t* hist = nullptr, int64_t hist_stride = 0);
+// hist (T > 64 only): each 4-token router workgroup's count of every expert,
+// byte hist[e * hist_stride + b], b < ceil(T / 4); input of launch_route_hist.
 
 // Router + top-k + INT8 of x + the count sort in one workgroup, for
 // 1 <= T <= 2 tokens (beyond that the per-token router workgroups win) and
@@ -43,6 +46,13 @@ bool launch_front_small(int64_t T, int d, int E, int k, int gating, const float*
 
 // Route / permute (k_route.hip).  ws holds ceil(T*k/256) * E int32 counts.
 int64_t route_blocks(int64_t Tk);
+// Count sort from the router's per-workgroup expert counts (launch_router
+// with hist): one kernel instead of two.  hist holds E rows of
+// route_hist_stride(T) bytes.
+int64_t route_hist_stride(int64_t T);
+bool route_hist_applies(int64_t T, int k);
+hipError_t launch_route_hist(int64_t T, int k, int E, const int32_t* idx, const uint8_t* hist,
+                             int32_t* offsets, int32_t* perm, int32_t* inv_perm, hipStream_t st);
 hipError_t launch_route(int64_t Tk, int E, const int32_t* idx, int32_t* offsets, int32_t* perm,
                         int32_t* inv_perm, int32_t* ws, hipStream_t st);
 
