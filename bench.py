@@ -84,7 +84,7 @@ def kernel_of(w, T, gateup: bool):
         return f"k_gemv_i4<4, {gu}, false, false>", "weight-streaming"
     if rows >= 256 and K % 128 == 0:
         nsplit = w.h // 32 if gateup else w.d // 64
-        mt = 2 if ((rows + 63) // 64 + w.E) * nsplit >= 4096 else 1
+        mt = 2 if ((rows + 63) // 64 + min(w.E, rows)) * nsplit >= 4096 else 1
         return f"k_w4a8w<{mt}, {gu}, false, false>", "matrix-core"
     return ("k_gateup_i4<false>" if gateup else "k_down_i4<false>"), "row-tile"
 
@@ -98,7 +98,7 @@ def pair_kernel_of(w, T):
     rows = T * w.k
     if rows <= 512 or rows < 256 or T <= 64:
         return None
-    r2 = ((rows + 63) // 64 + w.E) * (w.h // 32) >= 4096
+    r2 = ((rows + 63) // 64 + min(w.E, rows)) * (w.h // 32) >= 4096
     d2 = ((T + 63) // 64) * (w.hs // 32) >= 4096
     return f"k_w4a8w_pair<{2 if r2 else 1}, {2 if d2 else 1}, true>"
 

@@ -171,7 +171,7 @@ unsigned grid_bf16(int n_mt, int nsplit) {
 }
 
 int n_row_tiles(const ExpertArgs& a, int bm) {
-  return (int)((a.rows + bm - 1) / bm + (a.offsets ? a.E : 0));
+  return (int)tile_bound(a, bm);
 }
 
 }  // namespace

@@ -4,6 +4,7 @@
 // write the same output and no atomics are needed:
 //   y[t][c] = fma(w[t][k-1], f[inv[t*k+k-1]][c], ... fma(w[t][0], f[inv[t*k]][c], 0))
 //             + ys[t][c]
+#include "combine_row.h"
 #include "common.h"
 #include "launch.h"
 
@@ -27,98 +28,9 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int d, int k,
                                                  const float* __restrict__ ys,
                                                  void* __restrict__ y,
                                                  float* __restrict__ y_norm, float eps) {
-  const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const int q = d / 4;
-  const int64_t Tk = T * k;
-  int my_p = -1;
-  float my_w = 0.0f;
-  if (lane < k) {
-    const int64_t p = inv[t * k + lane];
-    if (p >= 0 && p < Tk) my_p = (int)p;  // a corrupt inverse permutation reads nothing
-    my_w = w[t * k + lane];
-  }
-  float4 sv[kC4];
-  if (ys) {
-#pragma unroll
-    for (int i = 0; i < kC4; ++i)
-      if (lane + 64 * i < q) sv[i] = reinterpret_cast<const float4*>(ys + t * d)[lane + 64 * i];
-  }
-  float4 acc[kC4];
-#pragma unroll
-  for (int i = 0; i < kC4; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j0 = 0; j0 < k; j0 += 4) {
-    int pj[4];
-    float wj[4];
-    float4 v[4][kC4];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      pj[jj] = j0 + jj < k ? __shfl(my_p, j0 + jj) : -1;
-      wj[jj] = __shfl(my_w, j0 + jj);
-      if (pj[jj] < 0) continue;
-      const float4* fr = reinterpret_cast<const float4*>(f + (int64_t)pj[jj] * d);
-#pragma unroll
-      for (int i = 0; i < kC4; ++i)
-        if (lane + 64 * i < q) v[jj][i] = fr[lane + 64 * i];
-    }
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      if (pj[jj] < 0) continue;
-#pragma unroll
-      for (int i = 0; i < kC4; ++i)
-        if (lane + 64 * i < q) {
-          acc[i].x = fmaf(wj[jj], v[jj][i].x, acc[i].x);
-          acc[i].y = fmaf(wj[jj], v[jj][i].y, acc[i].y);
-          acc[i].z = fmaf(wj[jj], v[jj][i].z, acc[i].z);
-          acc[i].w = fmaf(wj[jj], v[jj][i].w, acc[i].w);
-        }
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < kC4; ++i) {
-    const int c4 = lane + 64 * i;
-    if (c4 >= q) continue;
-    float4 a = acc[i];
-    if (ys) {
-      a.x += sv[i].x;
-      a.y += sv[i].y;
-      a.z += sv[i].z;
-      a.w += sv[i].w;
-    }
-    acc[i] = a;
-    if (kBF16Out) {
-      ushort4 o;
-      o.x = f32_to_bf16(a.x);
-      o.y = f32_to_bf16(a.y);
-      o.z = f32_to_bf16(a.z);
-      o.w = f32_to_bf16(a.w);
-      reinterpret_cast<ushort4*>(y)[t * q + c4] = o;
-    } else {
-      reinterpret_cast<float4*>(y)[t * q + c4] = a;
-    }
-  }
-  if constexpr (kNorm) {
-    float ss = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kC4; ++i)
-      if (lane + 64 * i < q) {
-        ss = fmaf(acc[i].x, acc[i].x, ss);
-        ss = fmaf(acc[i].y, acc[i].y, ss);
-        ss = fmaf(acc[i].z, acc[i].z, ss);
-        ss = fmaf(acc[i].w, acc[i].w, ss);
-      }
-    ss = wave_sum(ss);
-    const float inv_rms = 1.0f / sqrtf(ss / (float)d + eps);
-#pragma unroll
-    for (int i = 0; i < kC4; ++i) {
-      const int c4 = lane + 64 * i;
-      if (c4 >= q) continue;
-      const float4 a = acc[i];
-      reinterpret_cast<float4*>(y_norm)[t * q + c4] =
-          make_float4(a.x * inv_rms, a.y * inv_rms, a.z * inv_rms, a.w * inv_rms);
-    }
-  }
+  combine_token<kC4, kBF16Out, kNorm>(t, T, d, k, f, inv, w, ys, y, y_norm, eps, nullptr);
 }
 
 template <int kC4>

@@ -9,7 +9,7 @@
 //   s_act * sum_g s_w[g] * isum_g,  isum_g = exact int32 sum over group g.
 //
 // A workgroup owns one tile of up to kRows rows of one expert.  The routed
-// grid is sized for the worst case (ceil(rows/kRows) + E tiles); each
+// grid is sized for the worst case (ceil(rows/kRows) + min(E, rows) tiles); each
 // workgroup derives its (expert, tile) from expert_offsets on the device and
 // exits if it has none.
 #include "common.h"
@@ -295,8 +295,7 @@ __global__ __launch_bounds__(256) void k_down_fp(ExpertArgs a, const void* __res
 }
 
 unsigned tiles_for(const ExpertArgs& a, int rows_per_tile) {
-  const int64_t base = (a.rows + rows_per_tile - 1) / rows_per_tile;
-  return (unsigned)(a.offsets ? base + a.E : base);
+  return (unsigned)tile_bound(a, rows_per_tile);
 }
 
 }  // namespace

@@ -141,10 +141,21 @@ __device__ __forceinline__ void gemv_block(const GemvProb& P, int blk) {
   int4* s_act = reinterpret_cast<int4*>(s_sc + kM * G * 32);        // [kR][K/16]
   __shared__ int s_src[kR];
   __shared__ float s_as[kR];
+  __shared__ float s_tsc[kR];
+  const int c16 = K / 16;
 
+  // Routed gate/up of at most kR tokens: every token row (and its scale) is
+  // staged before the tile is known (its rows are some of these tokens), so
+  // the activation loads do not wait for the offsets and the permutation.
+  const bool pre = kGateUp && !kDense && a.T <= kR;
+  if (pre) {
+    for (int i = threadIdx.x; i < (int)a.T * c16; i += blockDim.x)
+      s_act[i] = reinterpret_cast<const int4*>(act)[i];  // rows 0..T-1 of x_q [T][K]
+    if ((int)threadIdx.x < (int)a.T) s_tsc[threadIdx.x] = act_scale[threadIdx.x];
+  }
   const int tile = blk / RB, rbo = blk % RB;
   int p0, n, e;
-  gemv_tile<kR, kDense>(a, tile, p0, n, e);
+  gemv_tile<kR, kDense>(a, tile, p0, n, e);  // (routed: a barrier, after which the above is visible)
   if (n <= 0) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t wrows = kGateUp ? 2 * (int64_t)a.h : N;
@@ -183,10 +194,10 @@ __device__ __forceinline__ void gemv_block(const GemvProb& P, int blk) {
     if (r < n) {
       src = p0 + r;
       if (kGateUp && !kDense) {
-        src = a.perm[p0 + r] / a.k;
+        src = a.T == 1 ? 0 : a.perm[p0 + r] / a.k;
         if ((unsigned)src >= (unsigned)a.T) src = 0;  // stays in bounds for a corrupt perm
       }
-      s = act_scale[src];
+      s = pre ? s_tsc[src] : act_scale[src];
     }
     s_src[r] = src;
     s_as[r] = s;
@@ -198,8 +209,7 @@ __device__ __forceinline__ void gemv_block(const GemvProb& P, int blk) {
     s_sc[i] = se[(int64_t)rbm[m] * G * 32 + j];
   }
   __syncthreads();  // s_src ready (in-kernel quantisation: activations staged)
-  const int c16 = K / 16;
-  if constexpr (!kQIn) {
+  if (!kQIn && !pre) {
     for (int i = threadIdx.x; i < kR * c16; i += blockDim.x) {
       const int r = i / c16, c = i % c16;
       int4 v = make_int4(0, 0, 0, 0);
@@ -226,7 +236,7 @@ __device__ __forceinline__ void gemv_block(const GemvProb& P, int blk) {
 #pragma unroll
       for (int r = 0; r < kR; ++r) {
         if (r >= n) break;
-        const int4 x = s_act[r * c16 + g * 2 + half];
+        const int4 x = s_act[(pre ? s_src[r] : r) * c16 + g * 2 + half];
         int q0, q1;
         dot16x2(wv[i][m], x, q0, q1);
         const int send = half ? q0 : q1;
@@ -284,10 +294,7 @@ size_t gemv_lds(int K, bool gateup) {
   return (size_t)m * kRGemv * G * 32 * 4 + (size_t)m * G * 32 * 4 + (size_t)kRGemv * K;
 }
 
-unsigned gemv_tiles(const ExpertArgs& a) {
-  const int64_t base = (a.rows + kRGemv - 1) / kRGemv;
-  return (unsigned)(a.offsets ? base + a.E : base);
-}
+unsigned gemv_tiles(const ExpertArgs& a) { return (unsigned)tile_bound(a, kRGemv); }
 
 GemvProb gemv_gateup_prob(const ExpertArgs& a, const int8_t* xq, const float* sx,
                           const uint8_t* wq, const float* ws, float* a_buf, int32_t* isum) {

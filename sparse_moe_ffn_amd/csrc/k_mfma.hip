@@ -311,13 +311,13 @@ __global__ __launch_bounds__(64) void k_w4a8w_pair(W4A8Prob P0, W4A8Prob P1, int
 // Two row tiles per wave once that still gives at least 4 waves per SIMD
 // (256 CUs x 4 SIMDs): half the weight traffic per MFMA, fewer waves.
 bool two_row_tiles(const ExpertArgs& a, int nsplit) {
-  const int64_t tiles64 = (a.rows + 63) / 64 + (a.offsets ? a.E : 0);
+  const int64_t tiles64 = tile_bound(a, 64);
   return tiles64 * nsplit >= 4096;
 }
 
 // Logical tiles of a problem with bm-row tiles (routed: worst case).
 int64_t n_tiles(const ExpertArgs& a, int bm, int nsplit) {
-  return ((a.rows + bm - 1) / bm + (a.offsets ? a.E : 0)) * nsplit;
+  return tile_bound(a, bm) * nsplit;
 }
 
 unsigned grid_of(int64_t n) { return (unsigned)(kXcd * ((n + kXcd - 1) / kXcd)); }

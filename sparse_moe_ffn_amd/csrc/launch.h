@@ -65,6 +65,14 @@ struct ExpertArgs {
   const int32_t* perm;
   const int32_t* offsets;
 };
+// Grid size in tiles of bm rows: dense ceil(rows / bm); routed (tiles per
+// expert from the offsets, known only on the device) the bound ceil(rows /
+// bm) + min(E, rows): every expert that owns rows adds at most one partial
+// tile, and at most min(E, rows) experts own rows.
+inline int64_t tile_bound(const ExpertArgs& a, int64_t bm) {
+  const int64_t full = (a.rows + bm - 1) / bm;
+  return a.offsets ? full + (a.rows < a.E ? a.rows : (int64_t)a.E) : full;
+}
 // INT4 gate/up + SwiGLU + per-row INT8 re-quantisation: hq [rows][h], hs [rows].
 // a_buf [rows][h] FP32 is staging space for the unquantised hidden rows.
 hipError_t launch_gateup_i4(const ExpertArgs& a, const int8_t* xq, const float* sx,
