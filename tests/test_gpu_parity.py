@@ -330,6 +330,9 @@ FUSED_CASES = [
     ("s_prefill", 150, {"d": 704, "h": 320, "hs": 640}),                  # row-tile kernels
     ("s_prefill", 5, {"d": 704, "h": 320, "hs": 640}),                    # down pair from INT8 rows (h % 128 != 0)
     ("l_prefill_bf16", 64, {}), ("tiny_f32", 37, {}),
+    ("s_prefill", 4, {}),                                                  # token rows staged before the tile lookup
+    ("s_prefill", 1500, {"E": 16, "k": 2}),                                # count sort from router histograms, k = 2
+    ("s_prefill", 2300, {"E": 1, "k": 1}),                                 # ... one expert, k = 1
 ]
 
 
