@@ -238,4 +238,24 @@ __device__ __forceinline__ int8_t quant_i8(float v, float s) {
   return (int8_t)(int)r;
 }
 
+// The same code without a division per element.  y = quant_recip(s), once
+// per row: the hardware reciprocal (within 1 ulp of 1/s), or NaN for tiny s.
+// With |v| <= amax, |v / s| <= 127.5, so t = v * y differs from the rounded
+// quotient fl(v / s) by less than 4e-5 (1 ulp of 1/s and two roundings, each
+// relative 2^-23 or less, at most 128 in size).  Unless t lies within 2^-12
+// of a half-integer, both are then strictly inside the same interval
+// (k - 1/2, k + 1/2) and round to the same k; in that window (and for NaN
+// y) the IEEE quotient is taken instead.  Codes are thus identical to
+// quant_i8(v, s).
+__device__ __forceinline__ float quant_recip(float s) {
+  return s >= 0x1p-100f ? __builtin_amdgcn_rcpf(s) : __builtin_nanf("");
+}
+__device__ __forceinline__ int8_t quant_i8(float v, float s, float y) {
+  const float t = v * y;
+  float r = rintf(t);
+  if (!(fabsf(t - r) < 0.5f - 0x1p-12f)) r = rintf(v / s);
+  r = fminf(fmaxf(r, -128.0f), 127.0f);
+  return (int8_t)(int)r;
+}
+
 }  // namespace mm

@@ -102,15 +102,15 @@ __device__ __forceinline__ float quant_row_lds(const float* __restrict__ x, int 
       amax = fmaxf(amax, fmaxf(fabsf(v[i].x), fabsf(v[i].y)));
     }
   amax = max64(amax);
-  const float sr = (2.0f * amax) / 255.0f;
+  const float sr = (2.0f * amax) / 255.0f, yr = quant_recip(sr);
   uint16_t* q = reinterpret_cast<uint16_t*>(dst);
 #pragma unroll
   for (int i = 0; i < kMaxQV; ++i)
     if (i < nv) {
       int8_t c0 = 0, c1 = 0;
       if (sr != 0.0f) {
-        c0 = quant_i8(v[i].x, sr);
-        c1 = quant_i8(v[i].y, sr);
+        c0 = quant_i8(v[i].x, sr, yr);
+        c1 = quant_i8(v[i].y, sr, yr);
       }
       q[lane + 64 * i] = (uint16_t)((uint8_t)c0 | ((uint16_t)(uint8_t)c1 << 8));
     }

@@ -3,6 +3,8 @@
 //
 // eq. (6) and the INT8 activation rule are from the section "Quantisation-
 // aware training" of the MobileMoE close reading (paper-archivist.com).
+#include <utility>
+
 #include "common.h"
 #include "launch.h"
 
@@ -114,15 +116,15 @@ __device__ __forceinline__ void quant_row_v2(int64_t r, int64_t cols, const floa
       amax = fmaxf(amax, fmaxf(fabsf(v[i].x), fabsf(v[i].y)));
     }
   amax = max64(amax);
-  const float sr = (2.0f * amax) / 255.0f;
+  const float sr = (2.0f * amax) / 255.0f, yr = quant_recip(sr);
   if (lane == 0) s[r] = sr;
 #pragma unroll
   for (int i = 0; i < kMaxV; ++i)
     if (i < nv) {
       int8_t a = 0, b = 0;
       if (sr != 0.0f) {
-        a = quant_i8(v[i].x, sr);
-        b = quant_i8(v[i].y, sr);
+        a = quant_i8(v[i].x, sr, yr);
+        b = quant_i8(v[i].y, sr, yr);
       }
       *reinterpret_cast<uint16_t*>(q + act_offset(r, 2 * (lane + 64 * i), cols, gm_rows)) =
           (uint16_t)((uint8_t)a | ((uint16_t)(uint8_t)b << 8));
@@ -138,7 +140,9 @@ __global__ __launch_bounds__(256) void k_act_quant_i8_v2(int64_t rows, int64_t c
   if (r < rows) quant_row_v2<kMaxV>(r, cols, x, q, s, gm_rows);
 }
 
-// Two row sets in one launch: blocks [0, nb0) cover set 0, the rest set 1.
+// Two row sets in one launch: blocks [0, nb0) cover set 0, the rest set 1
+// (the launcher puts the set with the longer rows first, so that its waves,
+// the longest, start first and the short ones fill in behind them).
 struct QuantRows {
   int64_t rows, cols;
   const float* x;
@@ -221,11 +225,11 @@ hipError_t launch_act_quant_i8_pair(int64_t rows0, int64_t cols0, const float* x
     if (e != hipSuccess) return e;
     return launch_act_quant_i8(rows1, cols1, x1, q1, s1, st, group_major);
   }
-  const int nb0 = (int)blocks_for(rows0, 4), nb1 = (int)blocks_for(rows1, 4);
-  const int64_t g0 = group_major ? rows0 : 0, g1 = group_major ? rows1 : 0;
-  hipLaunchKernelGGL(k_act_quant_i8_pair<24>, dim3(nb0 + nb1), dim3(256), 0, st,
-                     QuantRows{rows0, cols0, x0, q0, s0, g0}, QuantRows{rows1, cols1, x1, q1, s1, g1},
-                     nb0);
+  QuantRows A{rows0, cols0, x0, q0, s0, group_major ? rows0 : 0};
+  QuantRows B{rows1, cols1, x1, q1, s1, group_major ? rows1 : 0};
+  if (B.cols > A.cols) std::swap(A, B);
+  const int nbA = (int)blocks_for(A.rows, 4), nbB = (int)blocks_for(B.rows, 4);
+  hipLaunchKernelGGL(k_act_quant_i8_pair<24>, dim3(nbA + nbB), dim3(256), 0, st, A, B, nbA);
   return hipGetLastError();
 }
 

@@ -88,11 +88,11 @@ __device__ __forceinline__ void quant_row_regs(const float (&xv)[kNX], int lane,
 #pragma unroll
   for (int c = 0; c < kNX; ++c) amax = fmaxf(amax, fabsf(xv[c]));
   amax = max64(amax);
-  const float s = (2.0f * amax) / 255.0f;
+  const float s = (2.0f * amax) / 255.0f, y = quant_recip(s);
   if (lane == 0) sx[t] = s;
 #pragma unroll
   for (int c = 0; c < kNX; ++c)
-    xq[act_offset(t, lane + kWave * c, d, gm_rows)] = s != 0.0f ? quant_i8(xv[c], s) : (int8_t)0;
+    xq[act_offset(t, lane + kWave * c, d, gm_rows)] = s != 0.0f ? quant_i8(xv[c], s, y) : (int8_t)0;
 }
 
 // Workgroup = 4 waves and 4 tokens.  Phase 1: wave w takes experts w, w+4,

@@ -67,6 +67,53 @@ def test_act_quant_bitexact(rows, cols):
     assert np.array_equal(np_(s), s_ref)
 
 
+def halfway_rows(cols, amaxes, seed):
+    """Rows whose entries sit on and next to the rounding boundaries of the
+    INT8 rule: fl((k + 1/2) * s) and its neighbours 1 and 2 ulps away, for
+    every k with |k + 1/2| <= 126.5, s = fl(2 * amax / 255), amax the row's
+    first entry (the rest random below it)."""
+    g = rng(seed)
+    rows = []
+    for A in amaxes:
+        A = np.float32(A)
+        s = np.float32(np.float32(2.0) * A) / np.float32(255.0)
+        mid = (np.arange(-127, 127, dtype=np.float32) + np.float32(0.5)) * s
+        vals = [mid]
+        for n in (1, 2):
+            up, dn = mid.copy(), mid.copy()
+            for _ in range(n):
+                up = np.nextafter(up, np.float32(np.inf))
+                dn = np.nextafter(dn, np.float32(-np.inf))
+            vals += [up, dn]
+        v = np.concatenate(vals).astype(np.float32)
+        v = v[np.abs(v) <= A]
+        row = (g.uniform(-1, 1, cols) * A * 0.9).astype(np.float32)
+        m = min(cols - 1, v.size)
+        row[1:1 + m] = v[:m]
+        row[0] = A
+        g.shuffle(row[1:])
+        rows.append(row)
+    return np.stack(rows)
+
+
+# Quotients on or within two ulps of a half-integer (the codes there depend on
+# the exact FP32 quotient), tiny rows (scale below 2^-100) and a subnormal row.
+@pytest.mark.parametrize("cols", [768, 1536])
+def test_act_quant_halfway_bitexact(cols):
+    x = halfway_rows(cols, [1.0, 3.7, 1e-3, 123.456, 2.5e-30, 7e-36, 0.1, 5e4, 1.1754944e-38 * 3], 7)
+    rows = x.shape[0]
+    q_ref, s_ref = oracle.quant_act_i8(x)
+    for layout in (B.MM_ACT_ROW_MAJOR, B.MM_ACT_GROUP_MAJOR):
+        q = torch.empty((rows, cols), dtype=torch.int8, device=DEV)
+        s = torch.empty((rows,), dtype=torch.float32, device=DEV)
+        B.act_quant_i8_layout(rows, cols, dev(x), q, s, layout)
+        qh = np_(q)
+        if layout == B.MM_ACT_GROUP_MAJOR:  # byte (g * rows + r) * 32 + c % 32
+            qh = qh.reshape(cols // 32, rows, 32).transpose(1, 0, 2).reshape(rows, cols)
+        assert np.array_equal(s_ref, np_(s))
+        assert np.array_equal(qh, q_ref)
+
+
 # ------------------------------------------------------------ router
 @pytest.mark.parametrize("T,d,E,k,use_bias,gating", [
     (1000, 768, 60, 4, False, 0), (257, 1280, 60, 4, True, 0), (33, 64, 8, 2, False, 0),
