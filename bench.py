@@ -391,17 +391,18 @@ def main():
         cores = max(1, min(16, os.cpu_count() or 1))
         lw = wl.layer_weights(w, layer=0)
         xall = wl.tokens(w, step=0)
+        # grow the sample until it takes a quarter of the target time or
+        # covers the whole step (each call also quantises the weights, so the
+        # first, small sample overstates the per-token cost)
         n = min(T, 16)
-        t1 = time.time()
-        oracle.forward(xall[:n], lw.wr, lw.bias, lw.w_gu, lw.w_d, lw.ws_gu, lw.ws_d, k=w.k,
-                       wfmt=w.wfmt, nthreads=cores)
-        dt = time.time() - t1
-        if dt < args.cpu_seconds / 4 and n < T:
-            n = int(min(T, max(n, n * args.cpu_seconds / max(dt, 1e-3))))
+        while True:
             t1 = time.time()
             oracle.forward(xall[:n], lw.wr, lw.bias, lw.w_gu, lw.w_d, lw.ws_gu, lw.ws_d, k=w.k,
                            wfmt=w.wfmt, nthreads=cores)
             dt = time.time() - t1
+            if dt >= args.cpu_seconds / 4 or n >= T:
+                break
+            n = int(min(T, max(2 * n, n * args.cpu_seconds / max(dt, 1e-3))))
         layers_per_step = w.layers if decode else 1
         cpu = {"value": round(n / dt / layers_per_step, 2), "unit": "tokens/s", "cores": cores,
                "kind": "oracle",
