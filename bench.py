@@ -138,8 +138,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the layer shards by tokens with replicated weights; see DESIGN.md).", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the layer would shard by tokens with replicated weights).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
