@@ -62,6 +62,9 @@ __global__ __launch_bounds__(kBlockSlots) void k_route_scatter(
   __shared__ int wcnt[4][64];  // count of e in each wave of this block
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t blk = blockIdx.x;
+  // this thread's slot id, read first so that its latency overlaps the counts
+  const int64_t slot = blk * kBlockSlots + tid;
+  const int eraw = slot < Tk ? idx[slot] : -1;
 
   if constexpr (kMode == kSingle) {
     part_before[wv][lane] = 0;
@@ -134,8 +137,6 @@ __global__ __launch_bounds__(kBlockSlots) void k_route_scatter(
 
   // Rank inside the wave: the lanes holding the same id are found with one
   // ballot per id bit (ids < 64).
-  const int64_t slot = blk * kBlockSlots + tid;
-  const int eraw = slot < Tk ? idx[slot] : -1;
   const bool valid = (unsigned)eraw < (unsigned)E;  // out-of-range ids are skipped
   const int e = valid ? eraw : 0;
   uint64_t same = __ballot(valid);
