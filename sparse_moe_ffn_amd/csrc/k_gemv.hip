@@ -163,17 +163,19 @@ __device__ __forceinline__ void gemv_block(const GemvProb& P, int blk) {
   rbm[0] = rbo;
   if (kGateUp) rbm[kM - 1] = rbo + a.h / 32;
 
-  // Weight loads first: pair i of this wave is groups 2*(wave + 4i) and +1.
-  // Pairs past the end re-read the last pair (valid address, never used).
+  // Weight loads first: pair i of this wave is groups 2*(wave + 4i) and +1
+  // (pairs past the end are neither loaded nor used).
   const uint8_t* we = wq + (int64_t)e * (wrows / 32) * G * kChunkBytes;
   uint4 wv[kMaxPairs][kM];
 #pragma unroll
   for (int i = 0; i < kMaxPairs; ++i) {
-    const int gp = min(wave + kWaves * i, GP - 1);
+    const int gp = wave + kWaves * i;
+    if (gp < GP) {
 #pragma unroll
-    for (int m = 0; m < kM; ++m)
-      wv[i][m] = reinterpret_cast<const uint4*>(
-          we + ((int64_t)rbm[m] * G + 2 * gp) * kChunkBytes)[lane];
+      for (int m = 0; m < kM; ++m)
+        wv[i][m] = reinterpret_cast<const uint4*>(
+            we + ((int64_t)rbm[m] * G + 2 * gp) * kChunkBytes)[lane];
+    }
   }
 
   if constexpr (kQIn) {
