@@ -165,6 +165,154 @@ __global__ __launch_bounds__(64) void k_bf16w(ExpertArgs a, int nsplit, int n_mt
     }
 }
 
+// Workgroup-tiled form for shapes with enough rows: 4 waves share one tile of
+// 128 rows of one expert and 128 weight rows (gate/up: the 64 gate rows and
+// the 64 matching up rows of 64 hidden columns; down: 128 output columns),
+// staged through LDS in K blocks of 32 (double-buffered; the global loads of
+// block kb + 1 are in flight during the math of block kb).  Wave (wm, wn)
+// computes rows wm*64 .. +63 against weight rows wn*32 .. +31 and 64 + wn*32
+// .. +31 (gate/up) or wn*64 .. +63 (down), 2 x 2 MFMA tiles, so each operand
+// byte read from global memory feeds two waves' MFMAs.  LDS rows are padded
+// to 80 bytes, which keeps the 16-byte fragment reads of 8 consecutive lanes
+// on distinct banks.
+constexpr int kLBM = 128;   // rows (and weight rows) per workgroup
+constexpr int kLBK = 32;    // K block
+constexpr int kLRow = 40;   // LDS row stride in BF16 elements (80 bytes)
+
+template <bool kGateUp, bool kDense>
+__global__ __launch_bounds__(256) void k_bf16_lds(ExpertArgs a, int nsplit, int n_mt, int K,
+                                                  int N, const uint16_t* __restrict__ act,
+                                                  const uint16_t* __restrict__ w,
+                                                  void* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kLBM * kLRow];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kLBM * kLRow];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int per = (int)gridDim.x / kXcd;
+  const int logical = ((int)blockIdx.x % kXcd) * per + (int)blockIdx.x / kXcd;
+  const int mt = logical % n_mt, split = logical / n_mt;
+  if (split >= nsplit) return;  // the whole workgroup
+  const int rows = (int)a.rows;
+  int p0, n, e;
+  if constexpr (kDense) {
+    p0 = mt * kLBM;
+    n = min(kLBM, rows - p0);
+    e = 0;
+  } else {
+    routed_tile_wave(a.offsets, a.E, rows, kLBM, mt, p0, n, e);  // every wave: same tile
+  }
+  if (n <= 0) return;  // the whole workgroup
+  const int h = a.h;
+  const int64_t wrows = kGateUp ? 2 * (int64_t)h : N;
+
+  // Global -> LDS: thread t moves 16 bytes (8 values) of rows t/4 and t/4 + 64
+  // of both operands per K block (chunk t % 4 of the block's 32 values).
+  const int lr = tid >> 2, lc = (tid & 3) * 8;
+  const uint16_t* ga[2];
+  const uint16_t* gb[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = lr + 64 * i;
+    const int rr = r < n ? r : 0;  // padding rows read the tile's first row (never stored)
+    int src = p0 + rr;
+    if constexpr (kGateUp && !kDense) {
+      src = a.perm[p0 + rr] / a.k;
+      if ((unsigned)src >= (unsigned)a.T) src = 0;  // stays in bounds for a corrupt perm
+    }
+    ga[i] = act + (int64_t)src * K + lc;
+    // weight row r of the tile
+    int64_t wr;
+    if constexpr (kGateUp) wr = r < 64 ? split * 64 + r : h + split * 64 + (r - 64);
+    else wr = (int64_t)split * kLBM + r;
+    gb[i] = w + ((int64_t)e * wrows + wr) * K + lc;
+  }
+  v4i ra0, ra1, rb0, rb1;  // one K block of both operands in flight
+  // this lane's fragment rows in the tile
+  const int fr = lane & 31, fk = 8 * (lane >> 5);
+  int arow[2], brow[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) arow[m] = wm * 64 + m * 32 + fr;
+  if constexpr (kGateUp) {
+    brow[0] = wn * 32 + fr;
+    brow[1] = 64 + wn * 32 + fr;
+  } else {
+    brow[0] = wn * 64 + fr;
+    brow[1] = wn * 64 + 32 + fr;
+  }
+
+  v16f acc[2][2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[m][j] = v16f{};
+
+  const int KB = K / kLBK;
+  uint16_t* const sa0 = &sA[0][lr * kLRow + lc];
+  uint16_t* const sb0 = &sB[0][lr * kLRow + lc];
+  constexpr int kBuf = kLBM * kLRow, kHalf = 64 * kLRow;
+  ra0 = *reinterpret_cast<const v4i*>(ga[0]);
+  ra1 = *reinterpret_cast<const v4i*>(ga[1]);
+  rb0 = *reinterpret_cast<const v4i*>(gb[0]);
+  rb1 = *reinterpret_cast<const v4i*>(gb[1]);
+  *reinterpret_cast<v4i*>(sa0) = ra0;
+  *reinterpret_cast<v4i*>(sa0 + kHalf) = ra1;
+  *reinterpret_cast<v4i*>(sb0) = rb0;
+  *reinterpret_cast<v4i*>(sb0 + kHalf) = rb1;
+  __syncthreads();
+  for (int kb = 0; kb < KB; ++kb) {
+    const int cur = kb & 1;
+    if (kb + 1 < KB) {
+      const int o = (kb + 1) * kLBK;
+      ra0 = *reinterpret_cast<const v4i*>(ga[0] + o);
+      ra1 = *reinterpret_cast<const v4i*>(ga[1] + o);
+      rb0 = *reinterpret_cast<const v4i*>(gb[0] + o);
+      rb1 = *reinterpret_cast<const v4i*>(gb[1] + o);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      v4i fa[2], fb[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        fa[m] = *reinterpret_cast<const v4i*>(&sA[cur][arow[m] * kLRow + ks * 16 + fk]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        fb[j] = *reinterpret_cast<const v4i*>(&sB[cur][brow[j] * kLRow + ks * 16 + fk]);
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[m][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(v8bf, fa[m]), __builtin_bit_cast(v8bf, fb[j]), acc[m][j], 0, 0, 0);
+    }
+    if (kb + 1 < KB) {
+      const int nb = (cur ^ 1) * kBuf;
+      *reinterpret_cast<v4i*>(sa0 + nb) = ra0;
+      *reinterpret_cast<v4i*>(sa0 + nb + kHalf) = ra1;
+      *reinterpret_cast<v4i*>(sb0 + nb) = rb0;
+      *reinterpret_cast<v4i*>(sb0 + nb + kHalf) = rb1;
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * 64 + m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (row >= n) continue;
+      if constexpr (kGateUp) {
+        const float v = silu(acc[m][0][r]) * acc[m][1][r];
+        reinterpret_cast<uint16_t*>(out)[(int64_t)(p0 + row) * h + split * 64 + wn * 32 + fr] =
+            f32_to_bf16(v);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          reinterpret_cast<float*>(out)[(int64_t)(p0 + row) * N + split * kLBM + wn * 64 + j * 32 +
+                                        fr] = acc[m][j][r];
+      }
+    }
+}
+
 unsigned grid_bf16(int n_mt, int nsplit) {
   const int64_t n = (int64_t)n_mt * nsplit;
   return (unsigned)(kXcd * ((n + kXcd - 1) / kXcd));
@@ -178,6 +326,17 @@ int n_row_tiles(const ExpertArgs& a, int bm) {
 
 hipError_t launch_gateup_bf16_mfma(const ExpertArgs& a, const uint16_t* xb, const uint16_t* w,
                                    uint16_t* h_out, hipStream_t st) {
+  if (a.h % 64 == 0 && a.d % kLBK == 0 && a.rows >= kLBM) {
+    const int nsplit = a.h / 64, n_mt = n_row_tiles(a, kLBM);
+    const dim3 grid(grid_bf16(n_mt, nsplit)), block(256);
+    if (!a.offsets)
+      hipLaunchKernelGGL((k_bf16_lds<true, true>), grid, block, 0, st, a, nsplit, n_mt, a.d,
+                         2 * a.h, xb, w, h_out);
+    else
+      hipLaunchKernelGGL((k_bf16_lds<true, false>), grid, block, 0, st, a, nsplit, n_mt, a.d,
+                         2 * a.h, xb, w, h_out);
+    return hipGetLastError();
+  }
   const int nsplit = a.h / 32, n_mt = n_row_tiles(a, 64);
   const dim3 grid(grid_bf16(n_mt, nsplit)), block(64);
   if (!a.offsets)
@@ -193,6 +352,17 @@ hipError_t launch_down_bf16_mfma(const ExpertArgs& a, const uint16_t* hb, const 
                                  float* f, hipStream_t st) {
   ExpertArgs b = a;
   b.perm = nullptr;
+  if (a.d % kLBM == 0 && a.h % kLBK == 0 && a.rows >= kLBM) {
+    const int nsplit = a.d / kLBM, n_mt = n_row_tiles(b, kLBM);
+    const dim3 grid(grid_bf16(n_mt, nsplit)), block(256);
+    if (!b.offsets)
+      hipLaunchKernelGGL((k_bf16_lds<false, true>), grid, block, 0, st, b, nsplit, n_mt, a.h, a.d,
+                         hb, w, f);
+    else
+      hipLaunchKernelGGL((k_bf16_lds<false, false>), grid, block, 0, st, b, nsplit, n_mt, a.h,
+                         a.d, hb, w, f);
+    return hipGetLastError();
+  }
   const int nsplit = a.d / 64, n_mt = n_row_tiles(b, 64);
   const dim3 grid(grid_bf16(n_mt, nsplit)), block(64);
   if (!b.offsets)

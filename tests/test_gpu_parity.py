@@ -436,6 +436,28 @@ def test_full_size_sampled(name):
     assert np.array_equal(np_(layer.y), y_calls)
 
 
+def test_full_size_sampled_bf16():
+    """The BF16-weight L prefill at its full token count (8192 tokens, the
+    workgroup-tiled BF16 matrix-core kernels): routing checked in full, y on a
+    sample of tokens within the BF16 bound; the one-call layer matches the
+    seven calls bit for bit."""
+    w = wl.WORKLOADS["l_prefill_bf16"]
+    lw = wl.layer_weights(w)
+    x = wl.tokens(w)
+    layer = make_layer(w, lw)
+    layer.forward(dev(x))
+    i_ref, _, _ = oracle.router(x, lw.wr, lw.bias, k=w.k)
+    assert np.array_equal(np_(layer.idx), i_ref)
+    sample = np.unique(np.concatenate([[0, w.T - 1], rng(12).choice(w.T, 30, replace=False)]))
+    ref = oracle_forward(w, lw, x[sample])
+    y = layer_output(layer)
+    assert row_rel_err(y[sample], ref.y) <= TOL_BF16
+    y_calls = np_(layer.y).copy()
+    layer.y.zero_()
+    layer.forward_fused(dev(x))
+    assert np.array_equal(np_(layer.y), y_calls)
+
+
 # ------------------------------------------------------------ decode stack
 @pytest.mark.parametrize("B_", [1, 8, 64])
 def test_decode_stack_teacher_forced(B_):
