@@ -77,6 +77,8 @@ def kernel_of(w, T, gateup: bool):
     rows, K = T * w.k, (w.d if gateup else w.h)
     gu = "true" if gateup else "false"
     if w.wfmt == "bf16":
+        if rows >= 128 and (w.h % 64 == 0 if gateup else w.d % 128 == 0):
+            return f"k_bf16_lds<{gu}, false>", "matrix-core, workgroup-tiled (LDS)"
         return f"k_bf16w<2, {gu}, false>", "matrix-core"
     if w.wfmt != "int4g32":
         return ("k_gateup_fp<false>" if gateup else "k_down_fp<false>"), "row-tile"
