@@ -313,6 +313,126 @@ __global__ __launch_bounds__(256) void k_bf16_lds(ExpertArgs a, int nsplit, int 
     }
 }
 
+// Few rows (decode batches): weight-streaming form.  A workgroup of 4 waves
+// owns one tile of up to kGR rows of one expert (routed: found from the
+// offsets, so only experts that own rows are read; dense: rows in order) and
+// 4 outputs: gate/up -- wave w takes hidden column j = 4 * block + w, i.e.
+// gate row j and up row h + j, and applies SwiGLU; down -- wave w takes
+// output rows 8 * block + 2w and + 1.  Lane l holds the 8-value chunks l,
+// l + 64, ... of K of its two weight rows and of the tile's activation rows
+// (16-byte loads, all issued before the math), forms FP32 partial dot
+// products of the BF16 values and the wave adds them up.
+constexpr int kGR = 4;     // rows per tile
+constexpr int kGMaxC = 5;  // 8-value chunks per lane: K <= 64 * 8 * 5 = 2560
+
+__device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+__device__ __forceinline__ float dot8(const uint4& wv, const uint4& xv, float acc) {
+  acc = fmaf(bf_lo(wv.x), bf_lo(xv.x), acc);
+  acc = fmaf(bf_hi(wv.x), bf_hi(xv.x), acc);
+  acc = fmaf(bf_lo(wv.y), bf_lo(xv.y), acc);
+  acc = fmaf(bf_hi(wv.y), bf_hi(xv.y), acc);
+  acc = fmaf(bf_lo(wv.z), bf_lo(xv.z), acc);
+  acc = fmaf(bf_hi(wv.z), bf_hi(xv.z), acc);
+  acc = fmaf(bf_lo(wv.w), bf_lo(xv.w), acc);
+  return fmaf(bf_hi(wv.w), bf_hi(xv.w), acc);
+}
+
+template <bool kGateUp, bool kDense>
+__global__ __launch_bounds__(256) void k_bf16_gemv(ExpertArgs a, int K, int N, int nblk,
+                                                   const uint16_t* __restrict__ act,
+                                                   const uint16_t* __restrict__ w,
+                                                   void* __restrict__ out) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tile = (int)blockIdx.x / nblk, blk = (int)blockIdx.x % nblk;
+  const int rows = (int)a.rows;
+  int p0, n, e;
+  if constexpr (kDense) {
+    p0 = tile * kGR;
+    n = min(kGR, rows - p0);
+    e = 0;
+  } else {
+    routed_tile_wave(a.offsets, a.E, rows, kGR, tile, p0, n, e);  // every wave: same tile
+  }
+  if (n <= 0) return;
+  const int h = a.h;
+  const int64_t wrows = kGateUp ? 2 * (int64_t)h : N;
+  int r0, r1;
+  if constexpr (kGateUp) {
+    r0 = blk * 4 + wave;
+    r1 = h + r0;
+  } else {
+    r0 = blk * 8 + 2 * wave;
+    r1 = r0 + 1;
+  }
+  const uint4* w0 = reinterpret_cast<const uint4*>(w + ((int64_t)e * wrows + r0) * K);
+  const uint4* w1 = reinterpret_cast<const uint4*>(w + ((int64_t)e * wrows + r1) * K);
+  const int nc = K / 8;
+  uint4 wv0[kGMaxC], wv1[kGMaxC], xv[kGR][kGMaxC];
+#pragma unroll
+  for (int c = 0; c < kGMaxC; ++c) {
+    const int ch = lane + 64 * c;
+    if (ch < nc) {
+      wv0[c] = w0[ch];
+      wv1[c] = w1[ch];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kGR; ++r) {
+    if (r >= n) break;
+    int src = p0 + r;
+    if constexpr (kGateUp && !kDense) {
+      src = a.perm[p0 + r] / a.k;
+      if ((unsigned)src >= (unsigned)a.T) src = 0;  // stays in bounds for a corrupt perm
+    }
+    const uint4* xr = reinterpret_cast<const uint4*>(act + (int64_t)src * K);
+#pragma unroll
+    for (int c = 0; c < kGMaxC; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < nc) xv[r][c] = xr[ch];
+    }
+  }
+  float acc0[kGR], acc1[kGR];
+#pragma unroll
+  for (int r = 0; r < kGR; ++r) {
+    acc0[r] = 0.0f;
+    acc1[r] = 0.0f;
+    if (r >= n) continue;
+#pragma unroll
+    for (int c = 0; c < kGMaxC; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < nc) {
+        acc0[r] = dot8(wv0[c], xv[r][c], acc0[r]);
+        acc1[r] = dot8(wv1[c], xv[r][c], acc1[r]);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kGR; ++r) {
+    if (r >= n) break;
+    const float g = wave_sum(acc0[r]), u = wave_sum(acc1[r]);
+    if (lane == 0) {
+      if constexpr (kGateUp) {
+        reinterpret_cast<uint16_t*>(out)[(int64_t)(p0 + r) * h + r0] = f32_to_bf16(silu(g) * u);
+      } else {
+        float* o = reinterpret_cast<float*>(out) + (int64_t)(p0 + r) * N;
+        o[r0] = g;
+        o[r1] = u;
+      }
+    }
+  }
+}
+
+// The weight-streaming form applies: few rows (a decode batch), K a multiple
+// of 8 up to 2560, and whole groups of outputs (gate/up: h % 4, down: N % 8).
+bool bf16_gemv_fits(const ExpertArgs& a, int K, bool gateup, int N) {
+  const bool few = a.offsets ? a.rows <= 64 : a.rows <= 16;
+  return few && K % 8 == 0 && K <= 64 * 8 * kGMaxC && (gateup ? a.h % 4 == 0 : N % 8 == 0);
+}
+
+unsigned gemv_tiles_bf16(const ExpertArgs& a) { return (unsigned)tile_bound(a, kGR); }
+
 unsigned grid_bf16(int n_mt, int nsplit) {
   const int64_t n = (int64_t)n_mt * nsplit;
   return (unsigned)(kXcd * ((n + kXcd - 1) / kXcd));
@@ -326,6 +446,17 @@ int n_row_tiles(const ExpertArgs& a, int bm) {
 
 hipError_t launch_gateup_bf16_mfma(const ExpertArgs& a, const uint16_t* xb, const uint16_t* w,
                                    uint16_t* h_out, hipStream_t st) {
+  if (bf16_gemv_fits(a, a.d, true, 2 * a.h)) {
+    const int nblk = a.h / 4;
+    const dim3 grid(gemv_tiles_bf16(a) * nblk), block(256);
+    if (!a.offsets)
+      hipLaunchKernelGGL((k_bf16_gemv<true, true>), grid, block, 0, st, a, a.d, 2 * a.h, nblk, xb,
+                         w, h_out);
+    else
+      hipLaunchKernelGGL((k_bf16_gemv<true, false>), grid, block, 0, st, a, a.d, 2 * a.h, nblk, xb,
+                         w, h_out);
+    return hipGetLastError();
+  }
   if (a.h % 64 == 0 && a.d % kLBK == 0 && a.rows >= kLBM) {
     const int nsplit = a.h / 64, n_mt = n_row_tiles(a, kLBM);
     const dim3 grid(grid_bf16(n_mt, nsplit)), block(256);
@@ -352,6 +483,17 @@ hipError_t launch_down_bf16_mfma(const ExpertArgs& a, const uint16_t* hb, const 
                                  float* f, hipStream_t st) {
   ExpertArgs b = a;
   b.perm = nullptr;
+  if (bf16_gemv_fits(b, a.h, false, a.d)) {
+    const int nblk = a.d / 8;
+    const dim3 grid(gemv_tiles_bf16(b) * nblk), block(256);
+    if (!b.offsets)
+      hipLaunchKernelGGL((k_bf16_gemv<false, true>), grid, block, 0, st, b, a.h, a.d, nblk, hb, w,
+                         f);
+    else
+      hipLaunchKernelGGL((k_bf16_gemv<false, false>), grid, block, 0, st, b, a.h, a.d, nblk, hb, w,
+                         f);
+    return hipGetLastError();
+  }
   if (a.d % kLBM == 0 && a.h % kLBK == 0 && a.rows >= kLBM) {
     const int nsplit = a.d / kLBM, n_mt = n_row_tiles(b, kLBM);
     const dim3 grid(grid_bf16(n_mt, nsplit)), block(256);

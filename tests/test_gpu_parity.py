@@ -294,7 +294,9 @@ CASES = [
     ("l_prefill", 130, {}),
     ("l_prefill_bf16", 64, {}),
     ("l_prefill_bf16", 300, {}),                          # bf16 matrix cores, many row tiles
-    ("l_decode_bf16", 1, {}),
+    ("l_decode_bf16", 1, {}),                             # bf16 weight-streaming kernels
+    ("l_decode_bf16", 16, {}),                            # ... 64 routed rows, 16 shared
+    ("l_decode_bf16", 17, {}),                            # ... shared expert back on the matrix cores
     ("s_prefill", 200, {"wfmt": "bf16"}),
     ("s_prefill", 64, {"E": 8, "k": 2, "d": 128, "h": 64, "hs": 64}),
     ("s_prefill", 16, {"E": 1, "k": 1, "hs": 0}),
@@ -376,7 +378,7 @@ FUSED_CASES = [
     ("m_prefill", 200, {}), ("l_prefill", 130, {}),
     ("s_prefill", 150, {"d": 704, "h": 320, "hs": 640}),                  # row-tile kernels
     ("s_prefill", 5, {"d": 704, "h": 320, "hs": 640}),                    # down pair from INT8 rows (h % 128 != 0)
-    ("l_prefill_bf16", 64, {}), ("tiny_f32", 37, {}),
+    ("l_prefill_bf16", 64, {}), ("tiny_f32", 37, {}), ("l_decode_bf16", 8, {}),
     ("s_prefill", 4, {}),                                                  # token rows staged before the tile lookup
     ("s_prefill", 1500, {"E": 16, "k": 2}),                                # count sort from router histograms, k = 2
     ("s_prefill", 2300, {"E": 1, "k": 1}),                                 # ... one expert, k = 1
