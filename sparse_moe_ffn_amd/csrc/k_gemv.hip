@@ -89,18 +89,23 @@ constexpr int kMaxQV = 20;  // float2 per lane of a quantised row: K <= 128 * 20
 // kMaxQV) into LDS: the same rule and arithmetic as the standalone quantiser
 // (exact max|v| over the row, s = 2*amax/255, codes clamp(rint(v/s))), so
 // its codes and scale are bit-identical.  Returns s on every lane.
-__device__ __forceinline__ float quant_row_lds(const float* __restrict__ x, int K,
-                                               int8_t* __restrict__ dst, int lane) {
+__device__ __forceinline__ void load_row_regs(const float* __restrict__ x, int K, float2 (&v)[kMaxQV],
+                                              int lane) {
   const int nv = K / 128;
   const float2* xr = reinterpret_cast<const float2*>(x);
-  float2 v[kMaxQV];
+#pragma unroll
+  for (int i = 0; i < kMaxQV; ++i)
+    if (i < nv) v[i] = xr[lane + 64 * i];
+}
+
+// The quantisation of a row already held in registers (load_row_regs).
+__device__ __forceinline__ float quant_regs_lds(const float2 (&v)[kMaxQV], int K,
+                                                int8_t* __restrict__ dst, int lane) {
+  const int nv = K / 128;
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < kMaxQV; ++i)
-    if (i < nv) {
-      v[i] = xr[lane + 64 * i];
-      amax = fmaxf(amax, fmaxf(fabsf(v[i].x), fabsf(v[i].y)));
-    }
+    if (i < nv) amax = fmaxf(amax, fmaxf(fabsf(v[i].x), fabsf(v[i].y)));
   amax = max64(amax);
   const float sr = (2.0f * amax) / 255.0f, yr = quant_recip(sr);
   uint16_t* q = reinterpret_cast<uint16_t*>(dst);
@@ -115,6 +120,13 @@ __device__ __forceinline__ float quant_row_lds(const float* __restrict__ x, int 
       q[lane + 64 * i] = (uint16_t)((uint8_t)c0 | ((uint16_t)(uint8_t)c1 << 8));
     }
   return sr;
+}
+
+__device__ __forceinline__ float quant_row_lds(const float* __restrict__ x, int K,
+                                               int8_t* __restrict__ dst, int lane) {
+  float2 v[kMaxQV];
+  load_row_regs(x, K, v, lane);
+  return quant_regs_lds(v, K, dst, lane);
 }
 
 // Block `blk` of problem P.  out: gate/up -> a = SiLU(g * s) * (u * s) into
@@ -153,6 +165,15 @@ __device__ __forceinline__ void gemv_block(const GemvProb& P, int blk) {
       s_act[i] = reinterpret_cast<const int4*>(act)[i];  // rows 0..T-1 of x_q [T][K]
     if ((int)threadIdx.x < (int)a.T) s_tsc[threadIdx.x] = act_scale[threadIdx.x];
   }
+  // In-kernel quantisation of a routed problem of at most kR rows: wave w
+  // reads hidden row w before the tile is known (the tile's rows are some
+  // of these), so those loads do not wait for the offsets either.
+  const bool preq = kQIn && !kDense && a.rows <= kR;
+  float2 qv[kMaxQV];
+  if constexpr (kQIn) {
+    const int w = (int)(threadIdx.x >> 6);
+    if (preq && w < (int)a.rows) load_row_regs(P.actf + (int64_t)w * K, K, qv, threadIdx.x & 63);
+  }
   const int tile = blk / RB, rbo = blk % RB;
   int p0, n, e;
   gemv_tile<kR, kDense>(a, tile, p0, n, e);  // (routed: a barrier, after which the above is visible)
@@ -179,16 +200,25 @@ __device__ __forceinline__ void gemv_block(const GemvProb& P, int blk) {
   }
 
   if constexpr (kQIn) {
-    // wave r quantises hidden row p0 + r (a padding row stays zero)
+    // slot r of the staged rows holds hidden row p0 + r (padding slots stay
+    // zero): quantised by wave r, or with pre-read rows by the wave holding
+    // that row (wave p0 + r); wave r clears slot r when r >= n
     const int r = wave;
     int8_t* dst = reinterpret_cast<int8_t*>(s_act) + (int64_t)r * K;
-    float sr = 0.0f;
-    if (r < n) {
-      sr = quant_row_lds(P.actf + (int64_t)(p0 + r) * K, K, dst, lane);
-    } else {
+    if (r >= n) {
       for (int c = lane; c < K / 16; c += 64) reinterpret_cast<int4*>(dst)[c] = make_int4(0, 0, 0, 0);
+      if (lane == 0) s_as[r] = 0.0f;
     }
-    if (lane == 0) s_as[r] = sr;
+    if (preq) {
+      const int slot = wave - p0;
+      if (slot >= 0 && slot < n) {
+        const float sr = quant_regs_lds(qv, K, reinterpret_cast<int8_t*>(s_act) + (int64_t)slot * K, lane);
+        if (lane == 0) s_as[slot] = sr;
+      }
+    } else if (r < n) {
+      const float sr = quant_row_lds(P.actf + (int64_t)(p0 + r) * K, K, dst, lane);
+      if (lane == 0) s_as[r] = sr;
+    }
   } else if (threadIdx.x < kR) {
     const int r = threadIdx.x;
     int src = -1;
