@@ -42,6 +42,42 @@ __device__ __forceinline__ void combine_token(int64_t t, int64_t T, int d, int k
   float4 acc[kC4];
 #pragma unroll
   for (int i = 0; i < kC4; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (Tk <= 4) {
+    // every row of f fits the four row buffers (one token): read them all
+    // before the positions arrive, then take row inv[t*k+j] for j ascending
+    // (rows past the last are read as row 0: valid, never taken)
+    float4 v0[kC4], v1[kC4], v2[kC4], v3[kC4];
+    const float4* f4 = reinterpret_cast<const float4*>(f);
+    const int q1 = Tk > 1 ? q : 0, q2 = Tk > 2 ? 2 * q : 0, q3 = Tk > 3 ? 3 * q : 0;
+#pragma unroll
+    for (int i = 0; i < kC4; ++i) {
+      const int c = min(lane + 64 * i, q - 1);
+      v0[i] = f4[c];
+      v1[i] = f4[q1 + c];
+      v2[i] = f4[q2 + c];
+      v3[i] = f4[q3 + c];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = j < k ? __shfl(my_p, j) : -1;
+      const float wj = __shfl(my_w, j & 63);
+      if (p < 0) continue;
+      // p is the same on every lane: a branch, not a select per element
+      auto fma_row = [&](const float4 (&u)[kC4]) {
+#pragma unroll
+        for (int i = 0; i < kC4; ++i) {
+          acc[i].x = fmaf(wj, u[i].x, acc[i].x);
+          acc[i].y = fmaf(wj, u[i].y, acc[i].y);
+          acc[i].z = fmaf(wj, u[i].z, acc[i].z);
+          acc[i].w = fmaf(wj, u[i].w, acc[i].w);
+        }
+      };
+      if (p == 0) fma_row(v0);
+      else if (p == 1) fma_row(v1);
+      else if (p == 2) fma_row(v2);
+      else fma_row(v3);
+    }
+  } else
   for (int j0 = 0; j0 < k; j0 += 4) {
     int pj[4];
     float wj[4];
