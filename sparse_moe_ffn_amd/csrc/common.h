@@ -198,7 +198,6 @@ __device__ __forceinline__ RoutedTiles routed_tiles(const int32_t* __restrict__ 
 // tile), wave-uniform.  All 64 lanes call.
 __device__ __forceinline__ void routed_pick(const RoutedTiles& t, int rows_per_tile, int mt,
                                             int& p0, int& n, int& e) {
-  const int lane = threadIdx.x & 63;
   const bool mine = mt >= t.first && mt < t.inc;  // lanes >= E: first == inc
   const uint64_t owners = __ballot(mine);
   if (owners == 0ull) {

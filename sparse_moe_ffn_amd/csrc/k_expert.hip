@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void k_gateup_i4(ExpertArgs a, const int8_t* _
   if (n <= 0) return;
   const int d = a.d, h = a.h, G = d / kGroup, N2 = 2 * h;
   if (threadIdx.x < kRowsI4) {
-    int tok = threadIdx.x < n ? (a.perm ? a.perm[p0 + threadIdx.x] / a.k : p0 + threadIdx.x) : 0;
+    int tok = (int)threadIdx.x < n ? (a.perm ? a.perm[p0 + threadIdx.x] / a.k : p0 + threadIdx.x) : 0;
     if ((unsigned)tok >= (unsigned)a.T) tok = 0;  // stays in bounds for a corrupt perm
     s_tok[threadIdx.x] = tok;
   }

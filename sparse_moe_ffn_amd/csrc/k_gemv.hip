@@ -330,14 +330,14 @@ unsigned gemv_tiles(const ExpertArgs& a) { return (unsigned)tile_bound(a, kRGemv
 
 GemvProb gemv_gateup_prob(const ExpertArgs& a, const int8_t* xq, const float* sx,
                           const uint8_t* wq, const float* ws, float* a_buf, int32_t* isum) {
-  return GemvProb{a, a.d, 2 * a.h, a.h / 32, xq, sx, wq, ws, a_buf, isum};
+  return GemvProb{a, a.d, 2 * a.h, a.h / 32, xq, sx, wq, ws, a_buf, isum, nullptr};
 }
 
 GemvProb gemv_down_prob(const ExpertArgs& a, const int8_t* hq, const float* hs,
                         const uint8_t* wq, const float* ws, float* f, int32_t* isum) {
   ExpertArgs b = a;
   b.perm = nullptr;
-  return GemvProb{b, a.h, a.d, a.d / 32, hq, hs, wq, ws, f, isum};
+  return GemvProb{b, a.h, a.d, a.d / 32, hq, hs, wq, ws, f, isum, nullptr};
 }
 
 template <bool kGateUp>
