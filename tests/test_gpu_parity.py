@@ -382,6 +382,8 @@ FUSED_CASES = [
     ("s_prefill", 4, {}),                                                  # token rows staged before the tile lookup
     ("s_prefill", 1500, {"E": 16, "k": 2}),                                # count sort from router histograms, k = 2
     ("s_prefill", 2300, {"E": 1, "k": 1}),                                 # ... one expert, k = 1
+    ("l_decode", 1, {}), ("m_decode", 1, {}),                              # one token: one-workgroup front, widths 1280 / 1024
+    ("s_prefill", 1, {"E": 64, "k": 8}), ("s_prefill", 1, {"d": 256, "h": 128, "hs": 512}),
 ]
 
 
@@ -530,6 +532,7 @@ def test_graph_replay_matches_eager():
 @pytest.mark.parametrize("name,T,over", [
     ("s_prefill", 300, {"E": 64, "k": 8}),    # largest expert count and top-k
     ("l_prefill", 2, {}),                     # Zipf bias, one-workgroup front
+    ("l_prefill", 1, {}),                     # Zipf bias, one token
     ("l_prefill", 260, {}),                   # Zipf bias, matrix cores
 ])
 def test_sigmoid_gating_layer(name, T, over):
