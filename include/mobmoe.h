@@ -70,12 +70,17 @@ enum {
   MM_W_BF16 = 2      /* BF16 weights and activations, FP32 accumulation         */
 };
 
-/* Gating rules (mm_layer_desc.gating). */
+/* Gating rules (mm_layer_desc.gating): one of the first two, optionally
+   with MM_GATE_BIAS_SELECT_ONLY added. */
 enum {
   MM_GATE_SOFTMAX = 0,      /* softmax over all E logits, no renormalisation    */
-  MM_GATE_SIGMOID_NORM = 1  /* sigmoid of each selected logit, divided by their
+  MM_GATE_SIGMOID_NORM = 1, /* sigmoid of each selected logit, divided by their
                                sum over the k selected (training-time gate of the
                                "Pre-training" section)                           */
+  MM_GATE_BIAS_SELECT_ONLY = 2 /* the router bias steers the selection only: the
+                               experts are ranked by logit + bias, the gate
+                               weights use the logits without it (the load-
+                               balancing bias of the "Pre-training" section)     */
 };
 
 /* Output dtypes (mm_layer_desc.out_dtype): y of mm_combine. */
@@ -174,7 +179,9 @@ mm_status mm_convert_bf16(int64_t n, const float* x, uint16_t* y, void* stream);
  * with fused multiply-adds for j = l, l+64, ... ascending; then a balanced
  * pairwise tree (pairs at distance 1, 2, 4, ..., 32); then + bias[e].  Experts
  * are ranked by (logit descending, index ascending).  MM_GATE_SOFTMAX gives
- * w = exp(l_i - max l) / sum over all E of exp(l_e - max l).
+ * w = exp(l_i - max l) / sum over all E of exp(l_e - max l).  With
+ * MM_GATE_BIAS_SELECT_ONLY the ranking uses logit + bias[e] and the gate
+ * weights the logits without the bias.
  */
 mm_status mm_router_topk(const mm_layer_desc* desc, int64_t T, const float* x,
                          const float* w_router, const float* bias, int32_t* topk_idx,

@@ -91,7 +91,9 @@ def quant_act_i8(x: np.ndarray):
 
 
 def router(x, wr, bias, k: int, gating: int = 0):
-    """FP32 router -> (idx int32 [T,k], w float64 [T,k], logits float32 [T,E])."""
+    """FP32 router -> (idx int32 [T,k], w float64 [T,k], logits float32 [T,E]).
+    gating: 0 softmax, 1 sigmoid renormalised over the k; plus 2: the bias
+    takes part in the selection only (logits then holds logit + bias)."""
     x, wr = _f32(x), _f32(wr)
     T, d = x.shape
     E = wr.shape[0]
@@ -99,12 +101,15 @@ def router(x, wr, bias, k: int, gating: int = 0):
     idx = np.empty((T, k), np.int32)
     w = np.empty((T, k), np.float64)
     lib = _load()
-    if gating == 0:
+    sel_only = (gating >> 1) & 1
+    if gating & 1 == 0:
         logits = np.empty((T, E), np.float32)
-        rc = lib.ora_router(_i64(T), d, E, k, _p(x), _p(wr), _p(b), _p(logits), _p(idx), _p(w))
+        rc = lib.ora_router(_i64(T), d, E, k, _p(x), _p(wr), _p(b), _p(logits), _p(idx), _p(w),
+                            sel_only)
     else:
         logits = None
-        rc = lib.ora_router_sigmoid(_i64(T), d, E, k, _p(x), _p(wr), _p(b), _p(idx), _p(w))
+        rc = lib.ora_router_sigmoid(_i64(T), d, E, k, _p(x), _p(wr), _p(b), _p(idx), _p(w),
+                                    sel_only)
     if rc:
         raise ValueError("ora_router: bad shapes")
     return idx, w, logits
@@ -251,7 +256,7 @@ def forward(x, wr, bias, w_gu, w_d, ws_gu, ws_d, *, k: int, wfmt: str = "int4g32
     r = LayerResult(
         y=np.empty((T, d), np.float64), idx=np.empty((T, k), np.int32),
         w=np.empty((T, k), np.float64),
-        logits=np.empty((T, E), np.float32) if gating == 0 else None,
+        logits=np.empty((T, E), np.float32) if gating & 1 == 0 else None,
         f=np.empty((T, k, d), np.float64), ys=np.empty((T, d), np.float64) if hs else None)
     if fm == 1:
         r.xq, r.sx = np.empty((T, d), np.int8), np.empty((T,), np.float32)

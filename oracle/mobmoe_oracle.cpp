@@ -180,23 +180,37 @@ static float router_logit(const float* x, const float* w, int d, float bias) {
 //   gate weights: softmax over ALL E logits, not renormalised over the k, in
 //     FP32: m = max_e l_e, z_e = exp_ref(l_e - m), S = tree64 of z_0..z_{E-1}
 //     padded with zeros to 64 entries, w[t][j] = z_idx / S.
-// logits_out [T][E] FP32 is optional.  Returns -1 on bad shapes.
+// With select_only_bias the bias takes part in the selection only (the
+// load-balancing bias of the "Pre-training" section, which steers routing but
+// not the gate values): experts are ranked by (logit + bias) and the gate
+// weights are computed from the logits without the bias, m then being the
+// maximum of those.
+// logits_out [T][E] FP32 is optional (the ranked values).  Returns -1 on bad shapes.
 int ora_router(int64_t T, int d, int E, int k, const float* x, const float* wr,
-               const float* bias, float* logits_out, int32_t* idx, double* w) {
+               const float* bias, float* logits_out, int32_t* idx, double* w,
+               int select_only_bias) {
   if (d % 64 || E < 1 || k < 1 || k > E) return -1;
-  std::vector<float> lg(E);
+  std::vector<float> lg(E), gl(E);
   std::vector<int> order(E);
   for (int64_t t = 0; t < T; ++t) {
-    for (int e = 0; e < E; ++e)
-      lg[e] = router_logit(x + t * d, wr + (int64_t)e * d, d, bias ? bias[e] : 0.0f);
+    for (int e = 0; e < E; ++e) {
+      if (select_only_bias) {
+        gl[e] = router_logit(x + t * d, wr + (int64_t)e * d, d, 0.0f);
+        lg[e] = gl[e] + (bias ? bias[e] : 0.0f);
+      } else {
+        lg[e] = router_logit(x + t * d, wr + (int64_t)e * d, d, bias ? bias[e] : 0.0f);
+        gl[e] = lg[e];
+      }
+    }
     if (logits_out)
       for (int e = 0; e < E; ++e) logits_out[t * E + e] = lg[e];
     for (int e = 0; e < E; ++e) order[e] = e;
     std::stable_sort(order.begin(), order.end(),
                      [&](int a, int b) { return lg[a] > lg[b]; });
-    const float m = lg[order[0]];
+    float m = gl[0];
+    for (int e = 1; e < E; ++e) m = std::max(m, gl[e]);
     float z[64], zs[64];
-    for (int e = 0; e < 64; ++e) z[e] = e < E ? exp_ref(lg[e] - m) : 0.0f;
+    for (int e = 0; e < 64; ++e) z[e] = e < E ? exp_ref(gl[e] - m) : 0.0f;
     std::copy(z, z + 64, zs);
     const float S = tree64(zs);
     for (int j = 0; j < k; ++j) {
@@ -212,19 +226,27 @@ int ora_router(int64_t T, int d, int E, int k, const float* x, const float* wr,
 // (the training-time gate of the "Pre-training" section): selection as above
 // on the (biased) logits, FP32: g_j = 1 / (1 + exp_ref(-l_j)) for the k
 // selected, S = tree64 of g_0..g_{k-1} padded with zeros, w_j = g_j / S.
+// With select_only_bias, l_j in g_j is the logit without the bias.
 int ora_router_sigmoid(int64_t T, int d, int E, int k, const float* x, const float* wr,
-                       const float* bias, int32_t* idx, double* w) {
+                       const float* bias, int32_t* idx, double* w, int select_only_bias) {
   if (d % 64 || E < 1 || k < 1 || k > E) return -1;
-  std::vector<float> lg(E);
+  std::vector<float> lg(E), gl(E);
   std::vector<int> order(E);
   for (int64_t t = 0; t < T; ++t) {
-    for (int e = 0; e < E; ++e)
-      lg[e] = router_logit(x + t * d, wr + (int64_t)e * d, d, bias ? bias[e] : 0.0f);
+    for (int e = 0; e < E; ++e) {
+      if (select_only_bias) {
+        gl[e] = router_logit(x + t * d, wr + (int64_t)e * d, d, 0.0f);
+        lg[e] = gl[e] + (bias ? bias[e] : 0.0f);
+      } else {
+        lg[e] = router_logit(x + t * d, wr + (int64_t)e * d, d, bias ? bias[e] : 0.0f);
+        gl[e] = lg[e];
+      }
+    }
     for (int e = 0; e < E; ++e) order[e] = e;
     std::stable_sort(order.begin(), order.end(),
                      [&](int a, int b) { return lg[a] > lg[b]; });
     float g[64], gs[64];
-    for (int j = 0; j < 64; ++j) g[j] = j < k ? 1.0f / (1.0f + exp_ref(-lg[order[j]])) : 0.0f;
+    for (int j = 0; j < 64; ++j) g[j] = j < k ? 1.0f / (1.0f + exp_ref(-gl[order[j]])) : 0.0f;
     std::copy(g, g + 64, gs);
     const float S = tree64(gs);
     for (int j = 0; j < k; ++j) {
@@ -414,7 +436,8 @@ int ora_rmsnorm(int64_t rows, int cols, double eps, const float* x, double* y) {
 //   wfmt 0: FP32 weights and activations, no quantisation.
 //   wfmt 1: INT4 group-32 weights (eq. (6)), per-token INT8 activations.
 //   wfmt 2: BF16 weights and activations, output rounded to BF16.
-//   gating 0: softmax over all E, no renormalisation; 1: sigmoid + top-k norm.
+//   gating 0: softmax over all E, no renormalisation; 1: sigmoid + top-k norm;
+//   plus 2: the bias takes part in the selection only (see ora_router).
 // Inputs (FP32, row-major): x [T][d]; wr [E][d]; bias [E] (nullable);
 //   w_gu [E][2h][d] (gate rows first, then up rows); w_d [E][d][h];
 //   ws_gu [2hs][d]; ws_d [d][hs] (both ignored when hs == 0).
@@ -439,11 +462,13 @@ int ora_forward(int d, int E, int h, int hs, int k, int wfmt, int gating, int64_
                 const float* w_d, const float* ws_gu, const float* ws_d, int nthreads,
                 ora_out* out) {
   if (d % 64 || h % kGroup || hs % kGroup || k < 1 || k > E || !out || !out->y) return -1;
-  if (wfmt < 0 || wfmt > 2 || gating < 0 || gating > 1) return -1;
+  if (wfmt < 0 || wfmt > 2 || gating < 0 || gating > 3) return -1;
+  const int sel_only = gating >> 1;  // gating | 2: the bias steers the selection only
   std::vector<int32_t> idx(T * k);
   std::vector<double> w(T * k);
-  int rc = gating == 0 ? ora_router(T, d, E, k, x, wr, bias, out->logits, idx.data(), w.data())
-                       : ora_router_sigmoid(T, d, E, k, x, wr, bias, idx.data(), w.data());
+  int rc = (gating & 1) == 0
+               ? ora_router(T, d, E, k, x, wr, bias, out->logits, idx.data(), w.data(), sel_only)
+               : ora_router_sigmoid(T, d, E, k, x, wr, bias, idx.data(), w.data(), sel_only);
   if (rc) return rc;
   if (out->idx) std::copy(idx.begin(), idx.end(), out->idx);
   if (out->w) std::copy(w.begin(), w.end(), out->w);

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "libmobmoe.so")
 
 MM_OK, MM_ERR_NULL, MM_ERR_SHAPE, MM_ERR_ALIGN, MM_ERR_FORMAT, MM_ERR_WORKSPACE, MM_ERR_HIP = range(7)
 MM_W_F32, MM_W_INT4G32, MM_W_BF16 = range(3)
-MM_GATE_SOFTMAX, MM_GATE_SIGMOID_NORM = range(2)
+MM_GATE_SOFTMAX, MM_GATE_SIGMOID_NORM, MM_GATE_BIAS_SELECT_ONLY = 0, 1, 2
 MM_OUT_F32, MM_OUT_BF16 = range(2)
 MM_WS_ROUTE, MM_WS_GATEUP, MM_WS_DOWN, MM_WS_SHARED, MM_WS_MAX, MM_WS_FORWARD = range(6)
 MM_ACT_ROW_MAJOR, MM_ACT_GROUP_MAJOR = range(2)

@@ -57,7 +57,7 @@ mm_status check_desc(const mm_layer_desc* d) {
     return fail(MM_ERR_SHAPE, "top_k %lld must be in [1, min(8, n_experts)]", (long long)(d->top_k));
   if (d->wfmt < MM_W_F32 || d->wfmt > MM_W_BF16)
     return fail(MM_ERR_FORMAT, "unknown weight format %lld", (long long)(d->wfmt));
-  if (d->gating < MM_GATE_SOFTMAX || d->gating > MM_GATE_SIGMOID_NORM)
+  if (d->gating < 0 || d->gating > (MM_GATE_SIGMOID_NORM | MM_GATE_BIAS_SELECT_ONLY))
     return fail(MM_ERR_FORMAT, "unknown gating rule %lld", (long long)(d->gating));
   if (d->out_dtype < MM_OUT_F32 || d->out_dtype > MM_OUT_BF16)
     return fail(MM_ERR_FORMAT, "unknown output dtype %lld", (long long)(d->out_dtype));

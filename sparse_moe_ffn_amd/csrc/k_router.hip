@@ -23,33 +23,49 @@ constexpr int64_t kSmallRouterT = 64;  // up to this many tokens: the one-token-
 // descending, index ascending): the round's maximum, then the lowest lane
 // holding it; lane j keeps the winner of round j.  Writes idx[0..k) and
 // w[0..k).  Called by a whole wave.
+// gl: the logit the gate weight is computed from (mine itself, or with the
+// selection-only bias the logit without that bias).  kGating & 1: sigmoid
+// rule; the softmax subtracts the maximum of gl over the experts.
 template <int kGating>
-__device__ __forceinline__ void select_topk_lanes(float mine, int lane, int E, int k, int& my_sel,
-                                                  float& wv) {
+__device__ __forceinline__ void select_topk_lanes(float mine, float gl, int lane, int E, int k,
+                                                  int& my_sel, float& wv) {
   const bool valid = lane < E;
   bool avail = valid;
   my_sel = 0;
-  float m = 0.0f;
   for (int j = 0; j < k; ++j) {
     const float mx = max64(avail ? mine : -INFINITY);
     const uint64_t hits = __ballot(avail && mine == mx);
     const int win = __ffsll((unsigned long long)hits) - 1;
-    if (j == 0) m = mx;
     if (lane == j) my_sel = win;
     if (lane == win) avail = false;
   }
-  if (kGating == 0) {
+  if ((kGating & 1) == 0) {
     // softmax over all E logits, not renormalised over the k selected
-    const float z = valid ? exp_fp32(mine - m) : 0.0f;
+    const float m = max64(valid ? gl : -INFINITY);
+    const float z = valid ? exp_fp32(gl - m) : 0.0f;
     const float S = tree_sum64(z);
     wv = __shfl(z, my_sel) / S;
   } else {
     // sigmoid of each selected logit, normalised over the k selected
-    const float sg = valid ? 1.0f / (1.0f + exp_fp32(-mine)) : 0.0f;
+    const float sg = valid ? 1.0f / (1.0f + exp_fp32(-gl)) : 0.0f;
     const float mysg = __shfl(sg, my_sel);
     const float S = tree_sum64(lane < k ? mysg : 0.0f);
     wv = mysg / S;
   }
+}
+
+// Lane e's ranking value and gate logit from the stored logit without the
+// bias (row[e], e < E): the ranking value is logit + bias[e] (-inf for e >=
+// E); the gate logit is the same value, or with the selection-only bias
+// (kGating & 2, the load-balancing bias of the "Pre-training" section) the
+// logit without the bias.
+template <int kGating>
+__device__ __forceinline__ void biased_logit(const float* row, const float* __restrict__ bias,
+                                             int lane, int E, float& mine, float& gl) {
+  const float raw = lane < E ? row[lane] : 0.0f;
+  const float b = raw + (bias && lane < E ? bias[lane] : 0.0f);
+  mine = lane < E ? b : -INFINITY;
+  gl = (kGating & 2) ? raw : b;
 }
 
 // Top-k and gate weights of one token; lane e holds the logit of expert e
@@ -58,11 +74,11 @@ __device__ __forceinline__ void select_topk_lanes(float mine, int lane, int E, i
 // holding it; lane j keeps the winner of round j (select_topk_lanes).  Writes
 // idx[0..k) and w[0..k).  Called by a whole wave.
 template <int kGating>
-__device__ __forceinline__ void select_topk(float mine, int lane, int E, int k,
+__device__ __forceinline__ void select_topk(float mine, float gl, int lane, int E, int k,
                                             int32_t* __restrict__ idx, float* __restrict__ w) {
   int sel;
   float wv;
-  select_topk_lanes<kGating>(mine, lane, E, k, sel, wv);
+  select_topk_lanes<kGating>(mine, gl, lane, E, k, sel, wv);
   if (lane < k) {
     idx[lane] = sel;
     w[lane] = wv;
@@ -193,15 +209,16 @@ __global__ __launch_bounds__(256) void k_router(int64_t T, int d, int E, int k,
       for (int l = 0; l < 16; l += 2 * s2) p[l] = p[l] + p[l + s2];
     const int i = lane / kTok, q = lane % kTok;
     const int e = wave + 4 * i;
-    s_logit[q][e] = p[0] + (bias ? bias[e] : 0.0f);
+    s_logit[q][e] = p[0];  // the bias is added at the selection
   }
   __syncthreads();
   if (wave < nt) {
     const int64_t t = t0 + wave;
-    const float mine = lane < E ? s_logit[wave][lane] : -INFINITY;
+    float mine, gl;
+    biased_logit<kGating>(s_logit[wave], bias, lane, E, mine, gl);
     int sel;
     float wv;
-    select_topk_lanes<kGating>(mine, lane, E, k, sel, wv);
+    select_topk_lanes<kGating>(mine, gl, lane, E, k, sel, wv);
     if (lane < k) {
       idx[t * k + lane] = sel;
       w[t * k + lane] = wv;
@@ -249,13 +266,14 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_router_small(
     float p = 0.0f;
 #pragma unroll
     for (int c = 0; c < kNX; ++c) p = __builtin_fmaf(xv[c], wv[i][c], p);
-    const float l = tree_sum64(p) + (bias ? bias[e] : 0.0f);
+    const float l = tree_sum64(p);  // the bias is added at the selection
     if (lane == 0) s_logit[e] = l;
   }
   __syncthreads();
   if (wave != 0) return;
-  const float mine = lane < E ? s_logit[lane] : -INFINITY;
-  select_topk<kGating>(mine, lane, E, k, idx + t * k, w + t * k);
+  float mine, gl;
+  biased_logit<kGating>(s_logit, bias, lane, E, mine, gl);
+  select_topk<kGating>(mine, gl, lane, E, k, idx + t * k, w + t * k);
 }
 
 // Few tokens (T <= 2), the whole front of the layer in one workgroup: the
@@ -300,17 +318,18 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_front_small(
       float p = 0.0f;
 #pragma unroll
       for (int c = 0; c < kNX; ++c) p = __builtin_fmaf(xv[c], wv[i][c], p);
-      const float l = tree_sum64(p) + (bias ? bias[e] : 0.0f);
+      const float l = tree_sum64(p);  // the bias is added at the selection
       if (lane == 0) s_logit[t][e] = l;
     }
   }
   __syncthreads();
   if (wave < nt) {  // wave t: top-k of token t
     const int t = wave;
-    const float mine = lane < E ? s_logit[t][lane] : -INFINITY;
+    float mine, gl;
+    biased_logit<kGating>(s_logit[t], bias, lane, E, mine, gl);
     int sel;
     float wgt;
-    select_topk_lanes<kGating>(mine, lane, E, k, sel, wgt);
+    select_topk_lanes<kGating>(mine, gl, lane, E, k, sel, wgt);
     if (lane < k) {
       idx[t * k + lane] = sel;
       w[t * k + lane] = wgt;
@@ -409,10 +428,12 @@ bool launch_front_small(int64_t T, int d, int E, int k, int gating, const float*
                         float* sx, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                         hipStream_t st) {
   if (T < 1 || T > kFrontUseT || k > 8) return false;
-  return gating == 0 ? launch_front_g<0>(T, d, E, k, x, wr, bias, idx, w, xq, sx, offsets, perm,
-                                         inv_perm, st)
-                     : launch_front_g<1>(T, d, E, k, x, wr, bias, idx, w, xq, sx, offsets, perm,
-                                         inv_perm, st);
+  switch (gating) {
+    case 0: return launch_front_g<0>(T, d, E, k, x, wr, bias, idx, w, xq, sx, offsets, perm, inv_perm, st);
+    case 1: return launch_front_g<1>(T, d, E, k, x, wr, bias, idx, w, xq, sx, offsets, perm, inv_perm, st);
+    case 2: return launch_front_g<2>(T, d, E, k, x, wr, bias, idx, w, xq, sx, offsets, perm, inv_perm, st);
+    default: return launch_front_g<3>(T, d, E, k, x, wr, bias, idx, w, xq, sx, offsets, perm, inv_perm, st);
+  }
 }
 
 hipError_t launch_router(int64_t T, int d, int E, int k, int gating, const float* x,
@@ -424,13 +445,16 @@ hipError_t launch_router(int64_t T, int d, int E, int k, int gating, const float
   const bool small = T <= kSmallRouterT;
   if (hist != nullptr && small) return hipErrorInvalidValue;  // the per-token form counts nothing
   const bool q = xq != nullptr && router_quant_fused(d);
-  if (gating == 0) {
-    if (q) launch_router_g<0, true>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, hist, hist_stride, st);
-    else launch_router_g<0, false>(small, T, d, E, k, x, wr, bias, idx, w, nullptr, nullptr, 0, hist, hist_stride, st);
-  } else {
-    if (q) launch_router_g<1, true>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, hist, hist_stride, st);
-    else launch_router_g<1, false>(small, T, d, E, k, x, wr, bias, idx, w, nullptr, nullptr, 0, hist, hist_stride, st);
+#define MM_ROUTER_G(G)                                                                            \
+  if (q) launch_router_g<G, true>(small, T, d, E, k, x, wr, bias, idx, w, xq, sx, gm, hist, hist_stride, st); \
+  else launch_router_g<G, false>(small, T, d, E, k, x, wr, bias, idx, w, nullptr, nullptr, 0, hist, hist_stride, st)
+  switch (gating) {
+    case 0: MM_ROUTER_G(0); break;
+    case 1: MM_ROUTER_G(1); break;
+    case 2: MM_ROUTER_G(2); break;
+    default: MM_ROUTER_G(3); break;
   }
+#undef MM_ROUTER_G
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || xq == nullptr || q) return e;
   return launch_act_quant_i8(T, d, x, xq, sx, st, xq_group_major);  // widths without the fused form

@@ -58,7 +58,8 @@ def test_desc_validation(lib):
     for ds in bad:
         assert lib.mm_router_topk(ctypes.byref(ds), 4, FAKE, FAKE, None, FAKE, FAKE, None) == B.MM_ERR_SHAPE
         assert B.workspace_bytes(ds, 4) == 0
-    for ds in (B.desc(768, 60, 384, 0, 4, wfmt=7), B.desc(768, 60, 384, 0, 4, gating=3),
+    for ds in (B.desc(768, 60, 384, 0, 4, wfmt=7), B.desc(768, 60, 384, 0, 4, gating=4),
+               B.desc(768, 60, 384, 0, 4, gating=-1),
                B.desc(768, 60, 384, 0, 4, out_dtype=2)):
         assert lib.mm_router_topk(ctypes.byref(ds), 4, FAKE, FAKE, None, FAKE, FAKE, None) == B.MM_ERR_FORMAT
     assert lib.mm_router_topk(None, 4, FAKE, FAKE, None, FAKE, FAKE, None) == B.MM_ERR_NULL

@@ -528,6 +528,30 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
 
 
+# ------------------------------------------------------------ selection-only bias
+@pytest.mark.parametrize("name,T,gating", [
+    ("l_prefill", 1, 2), ("l_prefill", 2, 3),    # one-workgroup front
+    ("l_prefill", 37, 2),                        # one workgroup per token
+    ("l_prefill", 260, 3),                       # 4-token router workgroups, matrix cores
+    ("l_prefill", 2300, 2),                      # ... with the count sort from router histograms
+])
+def test_selection_only_bias_layer(name, T, gating):
+    """The Zipf bias steering the selection only (MM_GATE_BIAS_SELECT_ONLY):
+    ids, gate weights and y exact against the oracle, both entry points."""
+    w = wl.WORKLOADS[name].with_(T=T)
+    lw = wl.layer_weights(w)
+    x = wl.tokens(w)
+    layer = make_layer(w, lw, gating=gating)
+    layer.buffers(T)
+    ref = oracle_forward(w, lw, x, gating=gating)
+    for fwd in (layer.forward, layer.forward_fused):
+        layer.y.zero_()
+        fwd(dev(x))
+        assert np.array_equal(np_(layer.idx), ref.idx)
+        assert np.array_equal(np_(layer.topw), ref.w.astype(np.float32))
+        assert np.array_equal(layer_output(layer), ref.y.astype(np.float32))
+
+
 # ------------------------------------------------------------ other router rules
 @pytest.mark.parametrize("name,T,over", [
     ("s_prefill", 300, {"E": 64, "k": 8}),    # largest expert count and top-k

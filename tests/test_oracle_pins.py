@@ -231,6 +231,43 @@ def test_router_sigmoid_gate(ora):
     np.testing.assert_allclose(w_g, ref, rtol=1e-6)
 
 
+def test_router_selection_only_bias(ora):
+    """Bias that steers the selection only (gating | 2): the ids are those of
+    the biased ranking, the gate weights those of the unbiased logits."""
+    g = rng(12)
+    x = g.standard_normal((32, 128)).astype(np.float32)
+    wr = (g.standard_normal((60, 128)) * 0.1).astype(np.float32)
+    bias = (g.standard_normal(60) * 0.5).astype(np.float32)
+    _, _, raw = ora.router(x, wr, None, k=4, gating=0)            # logits without the bias
+    raw64 = raw.astype(np.float64)
+    for base in (0, 1):
+        i_b, _, _ = ora.router(x, wr, bias, k=4, gating=base)     # bias in selection and gate
+        i_s, w_s, _ = ora.router(x, wr, bias, k=4, gating=base | 2)
+        assert np.array_equal(i_s, i_b)                          # the same ranking
+        biased = raw64 + bias.astype(np.float64)
+        assert np.array_equal(i_s[:, 0], np.argmax(biased, 1))
+        sel = np.take_along_axis(raw64, i_s, 1)
+        if base == 0:
+            p = np.exp(raw64 - raw64.max(1, keepdims=True))
+            p /= p.sum(1, keepdims=True)
+            ref = np.take_along_axis(p, i_s, 1)
+        else:
+            ref = expit(sel) / expit(sel).sum(1, keepdims=True)
+        np.testing.assert_allclose(w_s, ref, rtol=1e-6)
+        # a zero bias changes nothing
+        i0, w0, _ = ora.router(x, wr, np.zeros(60, np.float32), k=4, gating=base | 2)
+        i1, w1, _ = ora.router(x, wr, None, k=4, gating=base)
+        assert np.array_equal(i0, i1) and np.array_equal(w0, w1)
+    # a large bias forces the routing but not the gate values
+    forced = np.zeros(60, np.float32)
+    forced[[7, 19, 33, 58]] = [100, 110, 120, 130]                # gaps far above the logits' spread
+    i_f, w_f, _ = ora.router(x, wr, forced, k=4, gating=2)
+    assert np.all(i_f == [58, 33, 19, 7])
+    p = np.exp(raw64 - raw64.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    np.testing.assert_allclose(w_f, p[:, [58, 33, 19, 7]], rtol=1e-6)
+
+
 # ----------------------------------------------------------------- routing
 def test_route_invariants_and_stable_sort(ora):
     g = rng(11)
