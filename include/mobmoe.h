@@ -339,6 +339,27 @@ mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
 
 /* --------------------------------------------------- around the layer */
 
+/*
+ * W4A8 dense linear: eq. (6) INT4 group-32 weights with FP32 scales against
+ * per-row INT8 activations (section "Quantisation-aware training": every
+ * linear layer runs this way, the attention and embedding projections around
+ * the MoE-FFN included):
+ *   y[r][o] = s_x[r] * (fma chain over g ascending of s_w[o][g] * isum_g(r, o)),
+ *   isum_g the exact int32 sum over the 32 inputs of group g; FP32 output.
+ *   rows          activation rows (0: no-op)
+ *   in_features   K, a positive multiple of 64
+ *   out_features  N, a positive multiple of 64; rows * max(K, N) < 2^31
+ *   xq, sx        device int8 [rows][K] row-major codes and FP32 [rows] scales
+ *                 (mm_act_quant_i8)
+ *   w             prepacked INT4 [N][K] (mm_prepack_int4g32 with n_mat = 1) and
+ *                 its prepacked scales
+ *   y             device FP32 [rows][N]
+ * Results are those of the expert down product (same kernels), bit for bit.
+ * Errors: MM_ERR_NULL / MM_ERR_ALIGN (pointers, 16-byte aligned), MM_ERR_SHAPE.
+ */
+mm_status mm_linear_w4a8(int64_t rows, int64_t in_features, int64_t out_features,
+                         const int8_t* xq, const float* sx, mm_weight w, float* y, void* stream);
+
 /* Row RMSNorm with unit gain used between stacked layers of the decode
  * workload (not part of eq. (*)): y = x / sqrt(mean(x^2) + eps), FP32. */
 mm_status mm_rmsnorm_f32(int64_t rows, int64_t cols, float eps, const float* x, float* y,

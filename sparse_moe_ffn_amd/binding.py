@@ -31,7 +31,7 @@ EXPORTS = (
     "mm_convert_bf16", "mm_router_topk", "mm_route_permute", "mm_act_quant_i8",
     "mm_expert_gateup_swiglu", "mm_expert_down", "mm_shared_expert", "mm_combine",
     "mm_rmsnorm_f32", "mm_expert_gateup_swiglu_dbg", "mm_expert_down_dbg", "mm_moe_forward",
-    "mm_act_quant_i8_layout", "mm_expert_gateup_pair_f32",
+    "mm_act_quant_i8_layout", "mm_expert_gateup_pair_f32", "mm_linear_w4a8",
 )
 
 
@@ -85,6 +85,7 @@ _SIGS = {
     "mm_shared_expert": ([_DESC, _I64, _VP, _VP, Weight, Weight, _VP, _VP, _SZ, _VP], ctypes.c_int),
     "mm_combine": ([_DESC, _I64, _VP, _VP, _VP, _VP, _VP, _VP], ctypes.c_int),
     "mm_rmsnorm_f32": ([_I64, _I64, _F, _VP, _VP, _VP], ctypes.c_int),
+    "mm_linear_w4a8": ([_I64, _I64, _I64, _VP, _VP, Weight, _VP, _VP], ctypes.c_int),
     "mm_moe_forward": ([_DESC, _I64, _VP, _VP, _VP, Weight, Weight, Weight, Weight, _VP, _VP, _VP,
                         _VP, _F, _VP, _SZ, _VP], ctypes.c_int),
 }
@@ -237,6 +238,13 @@ def moe_forward(ds, T, x, w_router, bias, w_gu, w_d, ws_gu, ws_d, topk_idx, topk
                                  w_d, ws_gu, ws_d, _ptr(topk_idx), _ptr(topk_w), _ptr(y),
                                  _ptr(y_norm), norm_eps, _ptr(ws), ws_bytes, _stream(stream)),
            "mm_moe_forward")
+
+
+def linear_w4a8(rows, in_features, out_features, xq, sx, w, y, stream=None):
+    """y [rows, out] FP32 = W4A8 product of x_q [rows, in] (scales sx) and the
+    prepacked INT4 weight w (a Weight) [out, in]."""
+    _check(load().mm_linear_w4a8(rows, in_features, out_features, _ptr(xq), _ptr(sx), w, _ptr(y),
+                                 _stream(stream)), "mm_linear_w4a8")
 
 
 def rmsnorm_f32(rows, cols, eps, x, y, stream=None):

@@ -710,6 +710,27 @@ mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
                     where);
 }
 
+mm_status mm_linear_w4a8(int64_t rows, int64_t in_features, int64_t out_features,
+                         const int8_t* xq, const float* sx, mm_weight w, float* y, void* stream) {
+  if (rows < 0) return fail(MM_ERR_SHAPE, "rows %lld is negative", (long long)rows);
+  if (in_features < 64 || in_features % 64 || out_features < 64 || out_features % 64)
+    return fail(MM_ERR_SHAPE, "in/out features %lld x %lld must be positive multiples of 64",
+                (long long)in_features, (long long)out_features);
+  if (rows * std::max(in_features, out_features) >= (int64_t(1) << 31))
+    return fail(MM_ERR_SHAPE, "rows * features must stay below 2^31");
+  if (rows == 0) return MM_OK;
+  MM_REQUIRE(xq);
+  MM_REQUIRE(sx);
+  MM_REQUIRE(w.data);
+  MM_REQUIRE(w.scales);
+  MM_REQUIRE(y);
+  // the dense down-product form: out = a.d = N features from a.h = K inputs
+  const mm::ExpertArgs a{rows, rows, (int)out_features, (int)in_features, 1, 1, nullptr, nullptr};
+  return hip_status(down_i4(a, xq, sx, static_cast<const uint8_t*>(w.data), w.scales, y, nullptr,
+                            S(stream)),
+                    "mm_linear_w4a8");
+}
+
 mm_status mm_rmsnorm_f32(int64_t rows, int64_t cols, float eps, const float* x, float* y,
                          void* stream) {
   if (rows < 0 || cols <= 0) return fail(MM_ERR_SHAPE, "bad shape");

@@ -190,3 +190,17 @@ def test_layout_and_pair_checks(lib):
     assert lib.mm_expert_gateup_pair_f32(*args(noshared, 4, FAKE, w)) == B.MM_ERR_SHAPE
     odd = B.desc(704, 60, 320, 640, 4)
     assert lib.mm_expert_gateup_pair_f32(*args(odd, 4, FAKE, w)) == B.MM_ERR_SHAPE
+
+
+def test_linear_w4a8_checks(lib):
+    """The dense W4A8 linear: shape, NULL and alignment checks on the host
+    (nothing reaches a device); zero rows is a no-op without pointers."""
+    W = B.weight(None, None)
+    Wf = B.Weight(FAKE, FAKE)
+    f = lib.mm_linear_w4a8
+    assert f(0, 768, 256, None, None, W, None, None) == B.MM_OK
+    for rows, K, N in [(-1, 768, 256), (4, 100, 256), (4, 768, 96), (4, 0, 64), (1 << 22, 1024, 64)]:
+        assert f(rows, K, N, FAKE, FAKE, Wf, FAKE, None) == B.MM_ERR_SHAPE
+    assert f(4, 768, 256, None, FAKE, Wf, FAKE, None) == B.MM_ERR_NULL
+    assert f(4, 768, 256, FAKE, FAKE, W, FAKE, None) == B.MM_ERR_NULL
+    assert f(4, 768, 256, FAKE, FAKE, Wf, MISALIGNED, None) == B.MM_ERR_ALIGN

@@ -114,6 +114,31 @@ def test_act_quant_halfway_bitexact(cols):
         assert np.array_equal(qh, q_ref)
 
 
+# ------------------------------------------------------------ dense W4A8 linear
+@pytest.mark.parametrize("rows,K,N", [
+    (1, 768, 256), (7, 768, 768), (64, 1280, 256),   # weight-streaming (decode rows)
+    (65, 1024, 1024), (300, 1280, 1280), (2048, 768, 768), (130, 3072, 640),  # matrix cores
+    (3, 3072, 128),                                    # row-tile kernel (K beyond the streaming form)
+])
+def test_linear_w4a8_bitexact(rows, K, N):
+    """mm_linear_w4a8 (an attention / embedding projection in W4A8) against the
+    oracle's linear, bit for bit, from device-quantised weights and rows."""
+    from sparse_moe_ffn_amd.layer import prepare_weight
+    g = rng(rows * 7 + K + N)
+    x = g.standard_normal((rows, K)).astype(np.float32)
+    wt = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    xq_ref, sx_ref = oracle.quant_act_i8(x)
+    wq_ref, ws_ref = oracle.quant_w4g32(wt)
+    y_ref = oracle.linear_w4a8(xq_ref, sx_ref, wq_ref, ws_ref)
+    dw = prepare_weight(wt, "int4g32", DEV)
+    xq = torch.empty((rows, K), dtype=torch.int8, device=DEV)
+    sx = torch.empty((rows,), dtype=torch.float32, device=DEV)
+    B.act_quant_i8(rows, K, dev(x), xq, sx)
+    y = torch.empty((rows, N), dtype=torch.float32, device=DEV)
+    B.linear_w4a8(rows, K, N, xq, sx, dw.c(), y)
+    assert np.array_equal(np_(y), y_ref)
+
+
 # ------------------------------------------------------------ router
 @pytest.mark.parametrize("T,d,E,k,use_bias,gating", [
     (1000, 768, 60, 4, False, 0), (257, 1280, 60, 4, True, 0), (33, 64, 8, 2, False, 0),
