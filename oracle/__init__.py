@@ -190,6 +190,22 @@ def combine_f32(f, w, ys):
     return y
 
 
+def attn_decode(q, kq, vq, ks, vs, T: int):
+    """GQA attention of one token per sequence over an INT8 KV cache, double.
+    q [B, n_h, d_h]; kq / vq int8 [B, n_kv, max_T, d_h]; ks / vs [B, n_kv, max_T];
+    positions 0..T-1 of the cache are used.  Returns out [B, n_h, d_h] float64."""
+    q, ks, vs = _f32(q), _f32(ks), _f32(vs)
+    kq, vq = _i8(kq), _i8(vq)
+    B, nh, dh = q.shape
+    nkv, maxT = kq.shape[1], kq.shape[2]
+    out = np.empty((B, nh, dh), np.float64)
+    rc = _load().ora_attn_decode(_i64(B), nh, nkv, dh, _i64(T), _i64(maxT), _p(q), _p(kq), _p(vq),
+                                 _p(ks), _p(vs), _p(out))
+    if rc:
+        raise ValueError("ora_attn_decode: bad shapes")
+    return out
+
+
 def exp_ref(x):
     """The FP32 exponential the INT4 path uses (Cody-Waite + Taylor)."""
     x = _f32(x)

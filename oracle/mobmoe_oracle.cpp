@@ -564,4 +564,51 @@ void ora_round_bf16(int64_t n, const float* x, float* y) {
   for (int64_t i = 0; i < n; ++i) y[i] = round_bf16(x[i]);
 }
 
+// ---------------------------------------------------------------------------
+// Grouped-query attention of one new token per sequence over an INT8 KV cache
+// (the decoder block around the MoE-FFN: GQA with n_kv key/value heads of
+// width d_h, KV cache held in 8 bits; sections "MoE preliminaries and three
+// design factors" and eq. (5)).  Plain definition in double:
+//   query head h reads key/value head g = h / (n_h / n_kv);
+//   k_t = s_k[t] * k_q[t], v_t = s_v[t] * v_q[t] (the cached codes and the
+//   per-(position, head) scales);
+//   score_t = (q_h . k_t) / sqrt(d_h), p = softmax over t = 0..T-1,
+//   out_h = sum_t p_t v_t.
+// Layouts: q [B][n_h][d_h] FP32; caches [B][n_kv][max_T][d_h] int8, scales
+// [B][n_kv][max_T] FP32 (positions 0..T-1 used); out [B][n_h][d_h] double.
+int ora_attn_decode(int64_t B, int nh, int nkv, int dh, int64_t T, int64_t maxT, const float* q,
+                    const int8_t* kq, const int8_t* vq, const float* ks, const float* vs,
+                    double* out) {
+  if (B < 0 || nkv < 1 || nh < nkv || nh % nkv || dh < 1 || T < 1 || T > maxT) return -1;
+  const int grp = nh / nkv;
+  std::vector<double> sc(T);
+  for (int64_t b = 0; b < B; ++b)
+    for (int h = 0; h < nh; ++h) {
+      const int g = h / grp;
+      const float* qh = q + (b * nh + h) * dh;
+      const int64_t base = (b * nkv + g) * maxT;
+      double m = -INFINITY;
+      for (int64_t t = 0; t < T; ++t) {
+        double dot = 0.0;
+        for (int c = 0; c < dh; ++c)
+          dot += (double)qh[c] * ((double)ks[base + t] * (double)kq[(base + t) * dh + c]);
+        sc[t] = dot / std::sqrt((double)dh);
+        m = std::max(m, sc[t]);
+      }
+      double den = 0.0;
+      for (int64_t t = 0; t < T; ++t) {
+        sc[t] = std::exp(sc[t] - m);
+        den += sc[t];
+      }
+      double* o = out + (b * nh + h) * dh;
+      for (int c = 0; c < dh; ++c) {
+        double acc = 0.0;
+        for (int64_t t = 0; t < T; ++t)
+          acc += sc[t] * ((double)vs[base + t] * (double)vq[(base + t) * dh + c]);
+        o[c] = acc / den;
+      }
+    }
+  return 0;
+}
+
 }  // extern "C"

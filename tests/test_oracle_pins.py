@@ -542,3 +542,62 @@ def test_layer_shapes_reproduce_printed_parameter_counts():
         assert abs(act - g[f"active_params_{key}"]["value"]) <= g[f"active_params_{key}"]["tol"]
         assert abs(tot - g[f"total_params_{key}"]["value"]) <= g[f"total_params_{key}"]["tol"]
         assert abs(w.d / n_l - g["aspect_ratio_d_over_layers"]["value"]) <= g["aspect_ratio_d_over_layers"]["tol"]
+
+
+# ----------------------------------------------------------------- GQA decode attention
+def _kv_case(g, B, nh, nkv, dh, maxT):
+    q = g.standard_normal((B, nh, dh)).astype(np.float32)
+    kq = g.integers(-128, 128, (B, nkv, maxT, dh)).astype(np.int8)
+    vq = g.integers(-128, 128, (B, nkv, maxT, dh)).astype(np.int8)
+    ks = (g.uniform(0.5, 1.5, (B, nkv, maxT)) / 127).astype(np.float32)
+    vs = (g.uniform(0.5, 1.5, (B, nkv, maxT)) / 127).astype(np.float32)
+    return q, kq, vq, ks, vs
+
+
+def test_attn_decode_against_library_sdpa(ora):
+    """Dequantised cache through torch's scaled dot-product attention (float64,
+    key/value heads repeated for the query-head groups)."""
+    import torch
+    g = rng(20)
+    B, nh, nkv, dh, maxT, T = 2, 12, 4, 64, 40, 33
+    q, kq, vq, ks, vs = _kv_case(g, B, nh, nkv, dh, maxT)
+    out = ora.attn_decode(q, kq, vq, ks, vs, T)
+    k = torch.from_numpy(kq[:, :, :T].astype(np.float64) * ks[:, :, :T, None].astype(np.float64))
+    v = torch.from_numpy(vq[:, :, :T].astype(np.float64) * vs[:, :, :T, None].astype(np.float64))
+    grp = nh // nkv
+    k = k.repeat_interleave(grp, dim=1)
+    v = v.repeat_interleave(grp, dim=1)
+    qq = torch.from_numpy(q.astype(np.float64))[:, :, None, :]
+    ref = torch.nn.functional.scaled_dot_product_attention(qq, k, v)[:, :, 0, :].numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_attn_decode_special_cases(ora):
+    g = rng(21)
+    B, nh, nkv, dh, maxT = 1, 8, 4, 64, 16
+    q, kq, vq, ks, vs = _kv_case(g, B, nh, nkv, dh, maxT)
+    deq_v = vq.astype(np.float64) * vs[..., None].astype(np.float64)
+    # one position: every head returns its group's value row
+    out = ora.attn_decode(q, kq, vq, ks, vs, 1)
+    for h in range(nh):
+        np.testing.assert_array_equal(out[0, h], deq_v[0, h // 2, 0])
+    # identical keys: uniform weights, the mean of the values
+    kq2 = np.broadcast_to(kq[:, :, :1], kq.shape).copy()
+    ks2 = np.broadcast_to(ks[:, :, :1], ks.shape).copy()
+    out = ora.attn_decode(q, kq2, vq, ks2, vs, 10)
+    for h in range(nh):
+        np.testing.assert_allclose(out[0, h], deq_v[0, h // 2, :10].mean(0), rtol=1e-12, atol=1e-15)
+    # positions past T never matter
+    kq3, vq3 = kq.copy(), vq.copy()
+    kq3[:, :, 10:] = 127
+    vq3[:, :, 10:] = -128
+    np.testing.assert_array_equal(ora.attn_decode(q, kq3, vq3, ks, vs, 10),
+                                  ora.attn_decode(q, kq, vq, ks, vs, 10))
+    # grouped heads: equal queries in one group give equal outputs; another group differs
+    q4 = q.copy()
+    q4[0, 1] = q4[0, 0]
+    o4 = ora.attn_decode(q4, kq, vq, ks, vs, 12)
+    np.testing.assert_array_equal(o4[0, 0], o4[0, 1])
+    q4[0, 2] = q4[0, 0]
+    o5 = ora.attn_decode(q4, kq, vq, ks, vs, 12)
+    assert not np.allclose(o5[0, 2], o5[0, 0])
