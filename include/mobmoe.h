@@ -360,6 +360,52 @@ mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
 mm_status mm_linear_w4a8(int64_t rows, int64_t in_features, int64_t out_features,
                          const int8_t* xq, const float* sx, mm_weight w, float* y, void* stream);
 
+/* --------------------------------------------- GQA decode attention, INT8 KV */
+
+/*
+ * Grouped-query attention around the MoE-FFN (section "MoE preliminaries and
+ * three design factors": each layer is GQA attention plus the FFN; eq. (5):
+ * the KV cache is held in b_kv = 8 bits; n_kv = 4, d_h = 64 in "Pre-training").
+ * Cache layout, caller-owned: codes [B][n_kv][max_T][d_h] int8 and scales
+ * [B][n_kv][max_T] FP32, one symmetric INT8 scale per (position, head) vector
+ * by the activation rule (s = 2 max|v| / 255, codes clamp(rint(v / s))).
+ * v1 limits: d_h = 64; n_h a multiple of n_kv with n_h / n_kv <= 8.
+ */
+
+/* Workspace of mm_attn_decode_i8 for B sequences of at most max_len positions
+ * (0 for invalid sizes). */
+size_t mm_attn_workspace_bytes(int64_t B, int32_t n_kv, int64_t max_len);
+
+/*
+ * Appends one token's keys and values: k_new, v_new FP32 [B][n_kv][d_h] are
+ * quantised per (sequence, head) vector into position pos[b] (device int32
+ * [B]) of the caches; positions outside [0, max_T) are skipped.  Codes and
+ * scales are bit-identical to mm_act_quant_i8 on the [B * n_kv][d_h] rows.
+ * Errors: MM_ERR_NULL / MM_ERR_ALIGN, MM_ERR_SHAPE.  B = 0 is a no-op.
+ */
+mm_status mm_kv_append_i8(int64_t B, int32_t n_kv, int32_t d_h, int64_t max_T, const int32_t* pos,
+                          const float* k_new, const float* v_new, int8_t* k_cache,
+                          int8_t* v_cache, float* k_scale, float* v_scale, void* stream);
+
+/*
+ * One new token per sequence: for query head h (key/value head h / (n_h /
+ * n_kv)), out[b][h] = sum over t < lens[b] of p_t * s_v[t] v_q[t], p the
+ * softmax over t of s_k[t] (q[b][h] . k_q[t]) / sqrt(d_h).  FP32 arithmetic
+ * in any order (tolerance-checked against the oracle's double evaluation).
+ *   q       device FP32 [B][n_h][d_h] (positions already encoded)
+ *   lens    device int32 [B], each in [1, max_len] (clamped to it; a length of
+ *           0 gives a zero output row)
+ *   max_len host bound on lens, 1 <= max_len <= max_T; sizes the workspace
+ *   out     device FP32 [B][n_h][d_h]
+ *   ws      device workspace of mm_attn_workspace_bytes(B, n_kv, max_len)
+ * Errors: MM_ERR_NULL / MM_ERR_ALIGN, MM_ERR_SHAPE, MM_ERR_WORKSPACE.
+ */
+mm_status mm_attn_decode_i8(int64_t B, int32_t n_h, int32_t n_kv, int32_t d_h, int64_t max_T,
+                            int64_t max_len, const int32_t* lens, const float* q,
+                            const int8_t* k_cache, const int8_t* v_cache, const float* k_scale,
+                            const float* v_scale, float* out, void* ws, size_t ws_bytes,
+                            void* stream);
+
 /* Row RMSNorm with unit gain used between stacked layers of the decode
  * workload (not part of eq. (*)): y = x / sqrt(mean(x^2) + eps), FP32. */
 mm_status mm_rmsnorm_f32(int64_t rows, int64_t cols, float eps, const float* x, float* y,

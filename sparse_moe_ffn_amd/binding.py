@@ -32,6 +32,7 @@ EXPORTS = (
     "mm_expert_gateup_swiglu", "mm_expert_down", "mm_shared_expert", "mm_combine",
     "mm_rmsnorm_f32", "mm_expert_gateup_swiglu_dbg", "mm_expert_down_dbg", "mm_moe_forward",
     "mm_act_quant_i8_layout", "mm_expert_gateup_pair_f32", "mm_linear_w4a8",
+    "mm_attn_workspace_bytes", "mm_kv_append_i8", "mm_attn_decode_i8",
 )
 
 
@@ -86,6 +87,11 @@ _SIGS = {
     "mm_combine": ([_DESC, _I64, _VP, _VP, _VP, _VP, _VP, _VP], ctypes.c_int),
     "mm_rmsnorm_f32": ([_I64, _I64, _F, _VP, _VP, _VP], ctypes.c_int),
     "mm_linear_w4a8": ([_I64, _I64, _I64, _VP, _VP, Weight, _VP, _VP], ctypes.c_int),
+    "mm_attn_workspace_bytes": ([_I64, _I32, _I64], _SZ),
+    "mm_kv_append_i8": ([_I64, _I32, _I32, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
+                        ctypes.c_int),
+    "mm_attn_decode_i8": ([_I64, _I32, _I32, _I32, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                           _VP, _SZ, _VP], ctypes.c_int),
     "mm_moe_forward": ([_DESC, _I64, _VP, _VP, _VP, Weight, Weight, Weight, Weight, _VP, _VP, _VP,
                         _VP, _F, _VP, _SZ, _VP], ctypes.c_int),
 }
@@ -245,6 +251,25 @@ def linear_w4a8(rows, in_features, out_features, xq, sx, w, y, stream=None):
     prepacked INT4 weight w (a Weight) [out, in]."""
     _check(load().mm_linear_w4a8(rows, in_features, out_features, _ptr(xq), _ptr(sx), w, _ptr(y),
                                  _stream(stream)), "mm_linear_w4a8")
+
+
+def attn_workspace_bytes(B, n_kv, max_len) -> int:
+    return int(load().mm_attn_workspace_bytes(B, n_kv, max_len))
+
+
+def kv_append_i8(B, n_kv, d_h, max_T, pos, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
+                 stream=None):
+    _check(load().mm_kv_append_i8(B, n_kv, d_h, max_T, _ptr(pos), _ptr(k_new), _ptr(v_new),
+                                  _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                  _stream(stream)), "mm_kv_append_i8")
+
+
+def attn_decode_i8(B, n_h, n_kv, d_h, max_T, max_len, lens, q, k_cache, v_cache, k_scale, v_scale,
+                   out, ws, ws_bytes, stream=None):
+    _check(load().mm_attn_decode_i8(B, n_h, n_kv, d_h, max_T, max_len, _ptr(lens), _ptr(q),
+                                    _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                    _ptr(out), _ptr(ws), ws_bytes, _stream(stream)),
+           "mm_attn_decode_i8")
 
 
 def rmsnorm_f32(rows, cols, eps, x, y, stream=None):

@@ -731,6 +731,65 @@ mm_status mm_linear_w4a8(int64_t rows, int64_t in_features, int64_t out_features
                     "mm_linear_w4a8");
 }
 
+static mm_status check_attn(int64_t B, int32_t n_h, int32_t n_kv, int32_t d_h, int64_t max_T) {
+  if (B < 0) return fail(MM_ERR_SHAPE, "B %lld is negative", (long long)B);
+  if (d_h != 64) return fail(MM_ERR_SHAPE, "d_h %d must be 64", (int)d_h);
+  if (n_kv < 1 || n_h < n_kv || n_h % n_kv || n_h / n_kv > 8)
+    return fail(MM_ERR_SHAPE, "n_h %d must be a multiple of n_kv %d, at most 8 times it", (int)n_h,
+                (int)n_kv);
+  if (max_T < 1 || B * n_kv * max_T * d_h >= (int64_t(1) << 40))
+    return fail(MM_ERR_SHAPE, "max_T %lld out of range", (long long)max_T);
+  return MM_OK;
+}
+
+size_t mm_attn_workspace_bytes(int64_t B, int32_t n_kv, int64_t max_len) {
+  if (B < 0 || n_kv < 1 || max_len < 1) return 0;
+  return std::max<size_t>(mm::attn_partial_bytes(B, n_kv, max_len), 256);
+}
+
+mm_status mm_kv_append_i8(int64_t B, int32_t n_kv, int32_t d_h, int64_t max_T, const int32_t* pos,
+                          const float* k_new, const float* v_new, int8_t* k_cache,
+                          int8_t* v_cache, float* k_scale, float* v_scale, void* stream) {
+  MM_TRY(check_attn(B, n_kv, n_kv, d_h, max_T));
+  if (B == 0) return MM_OK;
+  MM_REQUIRE(pos);
+  MM_REQUIRE(k_new);
+  MM_REQUIRE(v_new);
+  MM_REQUIRE(k_cache);
+  MM_REQUIRE(v_cache);
+  MM_REQUIRE(k_scale);
+  MM_REQUIRE(v_scale);
+  return hip_status(mm::launch_kv_append(B, n_kv, max_T, pos, k_new, v_new, k_cache, v_cache,
+                                         k_scale, v_scale, S(stream)),
+                    "mm_kv_append_i8");
+}
+
+mm_status mm_attn_decode_i8(int64_t B, int32_t n_h, int32_t n_kv, int32_t d_h, int64_t max_T,
+                            int64_t max_len, const int32_t* lens, const float* q,
+                            const int8_t* k_cache, const int8_t* v_cache, const float* k_scale,
+                            const float* v_scale, float* out, void* ws, size_t ws_bytes,
+                            void* stream) {
+  MM_TRY(check_attn(B, n_h, n_kv, d_h, max_T));
+  if (max_len < 1 || max_len > max_T)
+    return fail(MM_ERR_SHAPE, "max_len %lld must be in [1, max_T]", (long long)max_len);
+  if (B == 0) return MM_OK;
+  MM_REQUIRE(lens);
+  MM_REQUIRE(q);
+  MM_REQUIRE(k_cache);
+  MM_REQUIRE(v_cache);
+  MM_REQUIRE(k_scale);
+  MM_REQUIRE(v_scale);
+  MM_REQUIRE(out);
+  MM_REQUIRE(ws);
+  if (ws_bytes < mm::attn_partial_bytes(B, n_kv, max_len))
+    return fail(MM_ERR_WORKSPACE, "attention workspace too small (need %zu bytes)",
+                mm::attn_partial_bytes(B, n_kv, max_len));
+  return hip_status(mm::launch_attn_decode(B, n_h, n_kv, max_T, max_len, lens, q, k_cache, v_cache,
+                                           k_scale, v_scale, static_cast<float*>(ws), out,
+                                           S(stream)),
+                    "mm_attn_decode_i8");
+}
+
 mm_status mm_rmsnorm_f32(int64_t rows, int64_t cols, float eps, const float* x, float* y,
                          void* stream) {
   if (rows < 0 || cols <= 0) return fail(MM_ERR_SHAPE, "bad shape");

@@ -160,4 +160,15 @@ hipError_t launch_combine(int64_t T, int d, int k, const float* f, const int32_t
                           const float* w, const float* ys, void* y, bool bf16_out,
                           hipStream_t st, float* y_norm = nullptr, float eps = 0.0f);
 
+// Decode attention over an INT8 KV cache (k_attn.hip).  Head width 64, up
+// to 8 query heads per key/value head.
+size_t attn_partial_bytes(int64_t B, int nkv, int64_t max_len);
+hipError_t launch_kv_append(int64_t B, int nkv, int64_t maxT, const int32_t* pos,
+                            const float* k_new, const float* v_new, int8_t* kc, int8_t* vc,
+                            float* ks, float* vs, hipStream_t st);
+hipError_t launch_attn_decode(int64_t B, int nh, int nkv, int64_t maxT, int64_t max_len,
+                              const int32_t* lens, const float* q, const int8_t* kc,
+                              const int8_t* vc, const float* ks, const float* vs, float* part,
+                              float* out, hipStream_t st);
+
 }  // namespace mm

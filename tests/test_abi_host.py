@@ -204,3 +204,19 @@ def test_linear_w4a8_checks(lib):
     assert f(4, 768, 256, None, FAKE, Wf, FAKE, None) == B.MM_ERR_NULL
     assert f(4, 768, 256, FAKE, FAKE, W, FAKE, None) == B.MM_ERR_NULL
     assert f(4, 768, 256, FAKE, FAKE, Wf, MISALIGNED, None) == B.MM_ERR_ALIGN
+
+
+def test_attention_checks(lib):
+    """KV append and decode attention: shape, workspace, NULL checks on the host."""
+    a, d = lib.mm_kv_append_i8, lib.mm_attn_decode_i8
+    assert a(0, 4, 64, 16, None, None, None, None, None, None, None, None) == B.MM_OK
+    for nkv, dh, maxT in [(0, 64, 16), (4, 32, 16), (4, 64, 0)]:
+        assert a(2, nkv, dh, maxT, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.MM_ERR_SHAPE
+    assert a(2, 4, 64, 16, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.MM_ERR_NULL
+    ws = lib.mm_attn_workspace_bytes(2, 4, 16)
+    assert ws > 0 and lib.mm_attn_workspace_bytes(2, 0, 16) == 0
+    args = (FAKE,) * 7
+    for nh, nkv, ml in [(12, 5, 16), (40, 4, 16), (12, 4, 0), (12, 4, 17)]:
+        assert d(2, nh, nkv, 64, 16, ml, *args, FAKE, ws, None) == B.MM_ERR_SHAPE
+    assert d(2, 12, 4, 64, 16, 16, *args, FAKE, ws - 4, None) == B.MM_ERR_WORKSPACE
+    assert d(2, 12, 4, 64, 16, 16, None, *args[1:], FAKE, ws, None) == B.MM_ERR_NULL

@@ -139,6 +139,76 @@ def test_linear_w4a8_bitexact(rows, K, N):
     assert np.array_equal(np_(y), y_ref)
 
 
+# ------------------------------------------------------------ GQA decode attention, INT8 KV cache
+def _quant_rows_i8(x):
+    """Cache contents for float vectors [..., 64] by the oracle's INT8 row rule."""
+    q, s = oracle.quant_act_i8(x.reshape(-1, x.shape[-1]))
+    return q.reshape(x.shape), s.reshape(x.shape[:-1])
+
+
+@pytest.mark.parametrize("B_,nh,nkv,maxT,lens", [
+    (1, 12, 4, 64, [1]),                         # S heads, one position
+    (2, 12, 4, 300, [300, 17]),                  # ragged lengths, partial chunks
+    (3, 16, 4, 1024, [1000, 256, 257]),          # M heads, chunk edges
+    (1, 20, 4, 8192, [8192]),                    # L heads at the 8K context
+    (4, 8, 8, 128, [5, 128, 64, 0]),             # one query head per key/value head; empty row
+])
+def test_attn_decode_i8(B_, nh, nkv, maxT, lens):
+    """mm_attn_decode_i8 against the oracle's double evaluation per sequence;
+    per (sequence, head) row max|gpu - oracle| / max|oracle| <= 1e-4."""
+    g = rng(sum(lens) + nh)
+    q = g.standard_normal((B_, nh, 64)).astype(np.float32)
+    kf = g.standard_normal((B_, nkv, maxT, 64)).astype(np.float32)
+    vf = g.standard_normal((B_, nkv, maxT, 64)).astype(np.float32)
+    kq, ks = _quant_rows_i8(kf)
+    vq, vs = _quant_rows_i8(vf)
+    max_len = max(max(lens), 1)
+    ws_bytes = B.attn_workspace_bytes(B_, nkv, max_len)
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=DEV)
+    out = torch.empty((B_, nh, 64), dtype=torch.float32, device=DEV)
+    lens_d = dev(np.array(lens, np.int32))
+    B.attn_decode_i8(B_, nh, nkv, 64, maxT, max_len, lens_d, dev(q), dev(kq), dev(vq), dev(ks),
+                     dev(vs), out, ws, ws_bytes)
+    got = np_(out)
+    for b in range(B_):
+        if lens[b] == 0:
+            assert np.all(got[b] == 0.0)
+            continue
+        ref = oracle.attn_decode(q[b:b + 1], kq[b:b + 1], vq[b:b + 1], ks[b:b + 1], vs[b:b + 1],
+                                 lens[b])[0]
+        err = np.abs(got[b] - ref).max(1) / np.abs(ref).max(1)
+        assert err.max() <= 1e-4, (b, err.max())
+
+
+def test_kv_append_i8_bitexact():
+    """mm_kv_append_i8 writes each new vector's codes and scale (the oracle's
+    INT8 row rule) at its sequence's position and nothing else."""
+    g = rng(31)
+    B_, nkv, maxT = 3, 4, 50
+    kn = g.standard_normal((B_, nkv, 64)).astype(np.float32)
+    vn = g.standard_normal((B_, nkv, 64)).astype(np.float32)
+    vn[1, 2] = 0.0                                           # an all-zero vector: scale 0, codes 0
+    pos = np.array([0, 37, 49], np.int32)
+    kc = torch.full((B_, nkv, maxT, 64), 77, dtype=torch.int8, device=DEV)
+    vc = torch.full((B_, nkv, maxT, 64), 77, dtype=torch.int8, device=DEV)
+    ksd = torch.full((B_, nkv, maxT), -1.0, dtype=torch.float32, device=DEV)
+    vsd = torch.full((B_, nkv, maxT), -1.0, dtype=torch.float32, device=DEV)
+    B.kv_append_i8(B_, nkv, 64, maxT, dev(pos), dev(kn), dev(vn), kc, vc, ksd, vsd)
+    kq, ks = _quant_rows_i8(kn)
+    vq, vs = _quant_rows_i8(vn)
+    kch, vch, ksh, vsh = np_(kc), np_(vc), np_(ksd), np_(vsd)
+    for b in range(B_):
+        assert np.array_equal(kch[b, :, pos[b]], kq[b]) and np.array_equal(vch[b, :, pos[b]], vq[b])
+        assert np.array_equal(ksh[b, :, pos[b]], ks[b]) and np.array_equal(vsh[b, :, pos[b]], vs[b])
+        others = [t for t in range(maxT) if t != pos[b]]
+        assert np.all(kch[b, :, others] == 77) and np.all(ksh[b, :, others] == -1.0)
+    # positions outside the cache are skipped
+    before = np_(kc).copy()
+    B.kv_append_i8(B_, nkv, 64, maxT, dev(np.array([-1, maxT, maxT + 5], np.int32)), dev(kn),
+                   dev(vn), kc, vc, ksd, vsd)
+    assert np.array_equal(np_(kc), before)
+
+
 # ------------------------------------------------------------ router
 @pytest.mark.parametrize("T,d,E,k,use_bias,gating", [
     (1000, 768, 60, 4, False, 0), (257, 1280, 60, 4, True, 0), (33, 64, 8, 2, False, 0),
