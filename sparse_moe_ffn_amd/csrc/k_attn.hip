@@ -2,7 +2,8 @@
 // the decoder-block neighbour of the MoE-FFN (MobileMoE close reading: each
 // layer is GQA attention with n_kv key/value heads plus the FFN, section "MoE
 // preliminaries and three design factors"; the KV cache is held in 8 bits,
-// eq. (5); n_kv = 4 and d_h = 64 in section "Pre-training").
+// eq. (5) in section "On-device objective and memory function"; n_kv = 4 and
+// d_h = 64 in section "Pre-training").
 //
 // Cache layout: codes [B][n_kv][max_T][64] int8 and scales [B][n_kv][max_T]
 // FP32: one symmetric INT8 scale per (position, head) vector, the row rule of
