@@ -46,6 +46,15 @@ def parse():
                          "calls: the seven calls with the activation quantiser and shared expert on "
                          "a second stream; auto: fused (measured faster on every workload)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
+    ap.add_argument("--op", choices=("layer", "attn_decode", "linear"), default="layer",
+                    help="layer: the MoE-FFN layer (default); attn_decode: GQA decode attention "
+                         "over an INT8 KV cache (--batch sequences, --context positions, --heads "
+                         "query heads, 4 key/value heads); linear: the dense W4A8 projection "
+                         "(--batch rows, --in-features, --out-features)")
+    ap.add_argument("--context", type=int, default=8192, help="attn_decode: cached positions per sequence")
+    ap.add_argument("--heads", type=int, default=12, help="attn_decode: query heads (S: 12, M: 16, L: 20)")
+    ap.add_argument("--in-features", type=int, default=768, help="linear: K")
+    ap.add_argument("--out-features", type=int, default=768, help="linear: N")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 launches) and exit: the "
                          "reference for scaling HBM counters")
@@ -111,23 +120,26 @@ KERNEL_SOURCES = ["sparse_moe_ffn_amd/csrc/k_mfma.hip", "sparse_moe_ffn_amd/csrc
                   "sparse_moe_ffn_amd/csrc/common.h", "sparse_moe_ffn_amd/csrc/launch.h"]
 
 
-def kernel_source_sha():
+ATTN_SOURCES = ["sparse_moe_ffn_amd/csrc/k_attn.hip", "sparse_moe_ffn_amd/csrc/common.h"]
+
+
+def kernel_source_sha(sources=None):
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str, kernel: str):
-    """HBM bytes per launch of `kernel` on `workload` from the committed
-    rocprofv3 counter summary (profiles/traffic.md), or None when there is
-    none or the kernel sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "traffic.md")
+def stored_traffic(workload: str, kernel: str, summary: str = "traffic.md", sources=None):
+    """HBM bytes per launch of `kernel` on `workload` from a committed
+    rocprofv3 counter summary under profiles/, or None when there is none or
+    the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", summary)
     if not os.path.exists(path):
         return None
-    sha = kernel_source_sha()
+    sha = kernel_source_sha(sources)
     for line in open(path):
         if not line.startswith("traffic:"):
             continue
@@ -165,6 +177,10 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
         return
     B.load()
+    if args.op == "attn_decode":
+        return bench_attn(args, dev)
+    if args.op == "linear":
+        return bench_linear(args, dev)
     w = wl.WORKLOADS[args.workload]
     if args.batch is not None:
         w = w.with_(T=args.batch)
@@ -451,6 +467,159 @@ def main():
         "distinct_experts_last_step": n_distinct,
     }
     print(json.dumps(out), flush=True)
+
+
+def _time_graphs(issue, warmup: int, steps: int):
+    """Warm-up steps recorded into one HIP graph and the timed steps into
+    another; returns the mean ms per timed step (HIP events on the stream the
+    calls run on)."""
+    import torch
+    st = torch.cuda.current_stream()
+    gw, gt = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gw):
+        for i in range(max(warmup, 1)):
+            issue(i)
+    with torch.cuda.graph(gt):
+        for i in range(steps):
+            issue(warmup + i)
+    gw.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    gt.replay()
+    e1.record(st)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def bench_attn(args, dev):
+    """GQA decode attention of one new token per sequence over an INT8 KV cache
+    (d_h = 64, 4 key/value heads): bytes of the cache read per second.  Caches
+    of random codes and positive scales (seeded), enough of them rotated that
+    every step reads HBM rather than the 256 MB MALL."""
+    import torch
+    from sparse_moe_ffn_amd import binding as B
+    Bn, nh, nkv, T = args.batch or 32, args.heads, 4, args.context
+    per = Bn * nkv * T * 136  # 64 + 64 code bytes and two FP32 scales per position and head
+    n_inst = max(2, math.ceil(2.3 * MALL_BYTES / per))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    caches = []
+    for _ in range(n_inst):
+        kc = torch.randint(-127, 128, (Bn, nkv, T, 64), dtype=torch.int8, device=dev, generator=gen)
+        vc = torch.randint(-127, 128, (Bn, nkv, T, 64), dtype=torch.int8, device=dev, generator=gen)
+        ks = torch.rand((Bn, nkv, T), device=dev, generator=gen) * 0.04 + 1e-3
+        vs = torch.rand((Bn, nkv, T), device=dev, generator=gen) * 0.04 + 1e-3
+        caches.append((kc, vc, ks, vs))
+    q = torch.randn((Bn, nh, 64), device=dev, generator=gen)
+    lens = torch.full((Bn,), T, dtype=torch.int32, device=dev)
+    wsb = B.attn_workspace_bytes(Bn, nkv, T)
+    ws = torch.empty((wsb,), dtype=torch.uint8, device=dev)
+    out = torch.empty((Bn, nh, 64), dtype=torch.float32, device=dev)
+
+    def issue(i):
+        kc, vc, ks, vs = caches[i % n_inst]
+        B.attn_decode_i8(Bn, nh, nkv, 64, T, T, lens, q, kc, vc, ks, vs, out, ws, wsb)
+
+    ms = _time_graphs(issue, args.warmup, args.steps)
+    nbytes = per + Bn * nh * 64 * 8  # cache + q and output
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        kc, vc, ks, vs = (t.cpu().numpy() for t in caches[0])
+        qh = q.cpu().numpy()
+        n = 1
+        while True:
+            t1 = time.time()
+            oracle.attn_decode(qh[:n], kc[:n], vc[:n], ks[:n], vs[:n], T)
+            dt = time.time() - t1
+            if dt >= args.cpu_seconds / 4 or n >= Bn:
+                break
+            n = int(min(Bn, max(2 * n, n * args.cpu_seconds / 4 / max(dt, 1e-3))))
+        cpu = {"value": round(n * nkv * T * 136 / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{n} of the {Bn} sequences, {T} positions each, oracle.attn_decode "
+                         f"(double, one thread), {dt:.1f}s"}
+    out_line = {
+        "metric": "decode attention over an INT8 KV cache: cache bytes read per second",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8 codes, f32 arithmetic",
+        "data": "synthetic",
+        "config": {"workload": "gqa_decode_attention", "sequences": Bn, "context": T,
+                   "query_heads": nh, "kv_heads": nkv, "head_dim": 64, "caches_rotated": n_inst,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 5),
+                     "traffic": stored_traffic(f"gqa_decode_attention_b{Bn}_h{nh}_t{T}",
+                                               "k_attn_split+k_attn_merge",
+                                               "gqa_decode_attention_kernels.md", ATTN_SOURCES),
+                     "kernel": "k_attn_split + k_attn_merge (one mm_attn_decode_i8 call)",
+                     "algorithmic_bytes_per_launch": nbytes, "launch_us": round(ms * 1e3, 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out_line), flush=True)
+
+
+def bench_linear(args, dev):
+    """Dense W4A8 linear (eq. (6) INT4 weights, per-row INT8 activations), as
+    in the projections around the MoE layer: int8 ops per second."""
+    import numpy as np
+    import torch
+    from sparse_moe_ffn_amd import binding as B
+    from sparse_moe_ffn_amd.layer import prepare_weight
+    rows, K, N = args.batch or 2048, args.in_features, args.out_features
+    g = np.random.default_rng(4321)
+    n_inst = 9
+    wts = [prepare_weight((g.standard_normal((N, K)) * 0.02).astype(np.float32), "int4g32", dev)
+           for _ in range(n_inst)]
+    x = torch.from_numpy(g.standard_normal((rows, K)).astype(np.float32)).to(dev)
+    xq = torch.empty((rows, K), dtype=torch.int8, device=dev)
+    sx = torch.empty((rows,), dtype=torch.float32, device=dev)
+    B.act_quant_i8(rows, K, x, xq, sx)
+    y = torch.empty((rows, N), dtype=torch.float32, device=dev)
+
+    def issue(i):
+        B.linear_w4a8(rows, K, N, xq, sx, wts[i % n_inst].c(), y)
+
+    ms = _time_graphs(issue, args.warmup, args.steps)
+    ops = 2.0 * rows * K * N
+    tops = ops / (ms * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        wq, wsc = oracle.quant_w4g32((g.standard_normal((N, K)) * 0.02).astype(np.float32))
+        aq, sa = oracle.quant_act_i8(x.cpu().numpy())
+        n = min(rows, 8)
+        while True:
+            t1 = time.time()
+            oracle.linear_w4a8(aq[:n], sa[:n], wq, wsc)
+            dt = time.time() - t1
+            if dt >= args.cpu_seconds / 4 or n >= rows:
+                break
+            n = int(min(rows, max(2 * n, n * args.cpu_seconds / 4 / max(dt, 1e-3))))
+        cpu = {"value": round(2.0 * n * K * N / dt / 1e12, 6), "unit": "TOP/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{n} of the {rows} rows, oracle.linear_w4a8 (one thread), {dt:.1f}s"}
+    out_line = {
+        "metric": "dense W4A8 linear: int8 ops per second",
+        "value": round(tops, 3), "unit": "TOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": "w4a8_linear", "rows": rows, "in_features": K, "out_features": N,
+                   "weight_sets_rotated": n_inst, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma" if rows > 64 else "hbm",
+                     "achieved": round(tops, 3) if rows > 64 else round(N * K * 0.625 / (ms * 1e-3) / 1e9, 2),
+                     "peak": INT8_MFMA_PEAK_TOPS if rows > 64 else HBM_PEAK_GBS,
+                     "unit": "TFLOP/s" if rows > 64 else "GB/s",
+                     "frac": round(tops / INT8_MFMA_PEAK_TOPS, 5) if rows > 64
+                     else round(N * K * 0.625 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
+                     "traffic": None, "kernel": "mm_linear_w4a8 (one launch)",
+                     "launch_us": round(ms * 1e3, 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out_line), flush=True)
 
 
 if __name__ == "__main__":
