@@ -287,3 +287,48 @@ def forward(x, wr, bias, w_gu, w_d, ws_gu, ws_d, *, k: int, wfmt: str = "int4g32
     if rc:
         raise ValueError("ora_forward: bad shapes or formats")
     return r
+
+
+def bias_update(idx, bias, E: int, lam: float = 1e-3):
+    """Aux-loss-free balancing step -> (new bias float32 [E], load int32 [E])."""
+    idx = np.ascontiguousarray(idx, np.int32)
+    T, k = idx.shape
+    b = np.array(bias, np.float32, copy=True)
+    load = np.empty((E,), np.int32)
+    rc = _load().ora_bias_update(_i64(T), E, k, _p(idx), ctypes.c_float(lam), _p(b), _p(load))
+    if rc:
+        raise ValueError("ora_bias_update: expert id out of range")
+    return b, load
+
+
+def capacity(T: int, k: int, E: int, num: int = 3, den: int = 2) -> int:
+    """Per-expert buffer rows of drop-and-pad: ceil((num/den) * T*k / E), exact."""
+    return -(-(T * k * num) // (E * den))
+
+
+def drop_pad(idx, E: int, C: int):
+    """Drop-and-pad dispatch -> (buf [E, C], offsets_c [E+1], perm_c [T*k], inv_c [T*k]) int32."""
+    idx = np.ascontiguousarray(idx, np.int32)
+    T, k = idx.shape
+    buf = np.empty((E, C), np.int32)
+    offs = np.empty((E + 1,), np.int32)
+    perm = np.empty((T * k,), np.int32)
+    inv = np.empty((T * k,), np.int32)
+    rc = _load().ora_drop_pad(_i64(T), E, k, _i64(C), _p(idx), _p(buf), _p(offs), _p(perm), _p(inv))
+    if rc:
+        raise ValueError("ora_drop_pad: bad ids or capacity")
+    return buf, offs, perm, inv
+
+
+def fake_quant(x, bits: int, group: int, gout=None):
+    """QAT fake quantisation (eq. (6)) -> xbar, or (xbar, gin) when gout is given."""
+    x = _f32(x)
+    rows, cols = x.reshape(-1, x.shape[-1]).shape
+    xbar = np.empty_like(x)
+    g = None if gout is None else _f32(gout)
+    gin = None if gout is None else np.empty_like(x)
+    rc = _load().ora_fake_quant(_i64(rows), _i64(cols), bits, _i64(group), _p(x), _p(xbar), _p(g),
+                                _p(gin))
+    if rc:
+        raise ValueError("ora_fake_quant: bad bits or group")
+    return xbar if gout is None else (xbar, gin)

@@ -16,6 +16,9 @@
 //        - section "Quantisation-aware training", eq. (6): symmetric group
 //          quantiser, group size 32, b = 4 for weights; activations are
 //          quantised to INT8 on the fly; router stays FP32.
+//        - section "Pre-training", MoE stability and efficiency lists: the
+//          aux-loss-free expert-bias update and drop-and-pad dispatch with
+//          capacity factor 1.5 (training side).
 //        - section "Custom MoE kernel": count-sort of tokens by expert id,
 //          one fused gate/up product per expert, SwiGLU, down product,
 //          weighted scatter back through the inverse permutation.
@@ -606,6 +609,119 @@ int ora_attn_decode(int64_t B, int nh, int nkv, int dh, int64_t T, int64_t maxT,
         for (int64_t t = 0; t < T; ++t)
           acc += sc[t] * ((double)vs[base + t] * (double)vq[(base + t) * dh + c]);
         o[c] = acc / den;
+      }
+    }
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
+// Training-side pieces of the layer: [P1] section "Pre-training" (the MoE
+// stability list: balancing through an expert bias updated from the batch's
+// load, no auxiliary loss; the efficiency list: drop-and-pad dispatch with
+// capacity factor 1.5) and section "Quantisation-aware training" (eq. (6)
+// applied as fake quantisation during training).
+
+// Aux-loss-free balancing.  load_e = number of (token, slot) assignments of
+// the batch routed to e; the mean load is T*k/E.  Every bias moves by lambda
+// towards balance:
+//   b_e <- b_e + lambda   if load_e is below the mean,
+//   b_e <- b_e - lambda   if above, unchanged if equal   (one FP32 add),
+// the comparison taken exactly in integers (T*k against E*load_e).
+// load (optional) receives load_e.  Returns -1 if an id is out of range.
+int ora_bias_update(int64_t T, int E, int k, const int32_t* idx, float lambda, float* bias,
+                    int32_t* load) {
+  std::vector<int64_t> c(E, 0);
+  for (int64_t i = 0; i < T * k; ++i) {
+    if (idx[i] < 0 || idx[i] >= E) return -1;
+    c[idx[i]]++;
+  }
+  for (int e = 0; e < E; ++e) {
+    const int64_t below = T * k - (int64_t)E * c[e];  // > 0: load under the mean
+    if (below > 0) bias[e] = bias[e] + lambda;
+    else if (below < 0) bias[e] = bias[e] - lambda;
+    if (load) load[e] = (int32_t)c[e];
+  }
+  return 0;
+}
+
+// Drop-and-pad dispatch: every expert gets a buffer of C rows.  Reading:
+// assignments are admitted in token order (t ascending, then slot j); the
+// first C of an expert are kept, the rest dropped (their term leaves the
+// sum of eq. (*)).
+//   buf[e][p]   = id t*k+j of expert e's p-th kept assignment, -1 for the
+//                 padding rows p >= kept_e                      [E][C]
+// and the kept assignments as a dropless routing:
+//   offsets_c   = exclusive prefix sum of kept_e = min(load_e, C)   [E+1]
+//   perm_c[offsets_c[e] + p] = buf[e][p] for p < kept_e               [T*k]
+//                 (entries past offsets_c[E] set to -1)
+//   inv_c[t*k+j] = its row in perm_c, -1 if dropped                 [T*k]
+int ora_drop_pad(int64_t T, int E, int k, int64_t C, const int32_t* idx, int32_t* buf,
+                 int32_t* offsets_c, int32_t* perm_c, int32_t* inv_c) {
+  if (C < 0) return -1;
+  for (int64_t i = 0; i < T * k; ++i)
+    if (idx[i] < 0 || idx[i] >= E) return -1;
+  std::vector<int64_t> fill(E, 0);
+  for (int64_t i = 0; i < (int64_t)E * C; ++i) buf[i] = -1;
+  for (int64_t t = 0; t < T; ++t)
+    for (int j = 0; j < k; ++j) {
+      const int64_t a = t * k + j;
+      const int e = idx[a];
+      if (fill[e] < C) buf[(int64_t)e * C + fill[e]] = (int32_t)a;
+      fill[e]++;
+    }
+  int64_t run = 0;
+  for (int e = 0; e < E; ++e) {
+    offsets_c[e] = (int32_t)run;
+    run += std::min(fill[e], C);
+  }
+  offsets_c[E] = (int32_t)run;
+  for (int64_t a = 0; a < T * k; ++a) {
+    perm_c[a] = -1;
+    inv_c[a] = -1;
+  }
+  for (int e = 0; e < E; ++e)
+    for (int64_t p = 0; p < std::min(fill[e], C); ++p) {
+      const int32_t a = buf[(int64_t)e * C + p];
+      perm_c[offsets_c[e] + p] = a;
+      inv_c[a] = (int32_t)(offsets_c[e] + p);
+    }
+  return 0;
+}
+
+// Fake quantisation (QAT), eq. (6) with b bits over groups of `group`
+// consecutive elements of a row (weights: b = 4, group 32; activations:
+// b = 8, group = the row):
+//   s = (2 * max|x_g|) / (2^b - 1)                    (FP32, IEEE division)
+//   u = round_half_even(x / s)                        (FP32 division)
+//   xbar = s * clamp(u, -2^(b-1), 2^(b-1) - 1)        (FP32 product)
+// Backward with straight-through rounding: the derivative of the rounding is
+// taken as 1 and the clamp's as its own at u, so
+//   gin = gout where -2^(b-1) <= u <= 2^(b-1) - 1, else 0;
+// an all-zero group (s = 0) gives xbar = 0 and passes the gradient.  Since
+// |x / s| <= (2^b - 1) / 2, only a positive group maximum whose quotient
+// rounds up to 2^(b-1) is clipped.  xbar and the gradient pair are optional.
+int ora_fake_quant(int64_t rows, int64_t cols, int bits, int64_t group, const float* x,
+                   float* xbar, const float* gout, float* gin) {
+  if ((bits != 4 && bits != 8) || group < 1 || cols % group) return -1;
+  const float levels = bits == 4 ? 15.0f : 255.0f;
+  const float qmin = bits == 4 ? -8.0f : -128.0f, qmax = bits == 4 ? 7.0f : 127.0f;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t g0 = 0; g0 < cols; g0 += group) {
+      const int64_t base = r * cols + g0;
+      float amax = 0.0f;
+      for (int64_t c = 0; c < group; ++c) amax = std::max(amax, std::fabs(x[base + c]));
+      const float s = (2.0f * amax) / levels;
+      for (int64_t c = 0; c < group; ++c) {
+        const int64_t i = base + c;
+        bool pass = true;
+        float v = 0.0f;
+        if (s != 0.0f) {
+          const float u = std::nearbyint(x[i] / s);
+          pass = u >= qmin && u <= qmax;
+          v = s * std::min(std::max(u, qmin), qmax);
+        }
+        if (xbar) xbar[i] = v;
+        if (gin) gin[i] = pass ? gout[i] : 0.0f;
       }
     }
   return 0;

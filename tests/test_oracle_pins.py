@@ -601,3 +601,137 @@ def test_attn_decode_special_cases(ora):
     q4[0, 2] = q4[0, 0]
     o5 = ora.attn_decode(q4, kq, vq, ks, vs, 12)
     assert not np.allclose(o5[0, 2], o5[0, 0])
+
+
+# ----------------------------------------------------------------- training side
+def test_bias_update_pins(ora):
+    """Aux-loss-free balancing: balanced load leaves the bias bit-identical;
+    otherwise each bias moves by exactly +-lambda (FP32) towards balance, the
+    direction decided by the exact load against the mean (np.bincount)."""
+    E, k, lam = 60, 4, np.float32(1e-3)
+    g = rng(40)
+    bias = g.standard_normal(E).astype(np.float32)
+    T = 60
+    idx = ((np.arange(T)[:, None] * k + np.arange(k)[None, :]) % E).astype(np.int32)
+    nb, load = ora.bias_update(idx, bias, E, float(lam))
+    assert np.array_equal(load, np.full(E, 4)) and np.array_equal(nb.view(np.int32), bias.view(np.int32))
+    T = 333
+    idx = np.stack([g.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    idx[:50, 0] = 7                                            # make expert 7 overloaded
+    idx[:50] = np.where((idx[:50] == 7) & (np.arange(k) > 0), (idx[:50] + 1) % E, idx[:50])
+    nb, load = ora.bias_update(idx, bias, E, float(lam))
+    cnt = np.bincount(idx.ravel(), minlength=E)
+    assert np.array_equal(load, cnt)
+    mean = Fraction(T * k, E)
+    for e in range(E):
+        want = bias[e] + lam if cnt[e] < mean else (bias[e] - lam if cnt[e] > mean else bias[e])
+        assert nb[e] == np.float32(want)
+    assert nb[7] == np.float32(bias[7] - lam)
+    # all load on two experts of four
+    nb, _ = ora.bias_update(np.array([[0, 1]] * 10, np.int32), np.zeros(4, np.float32), 4, 0.5)
+    assert list(nb) == [-0.5, -0.5, 0.5, 0.5]
+    with pytest.raises(ValueError):
+        ora.bias_update(np.array([[0, 4]], np.int32), np.zeros(4, np.float32), 4)
+
+
+def test_drop_pad_capacity_pin(ora):
+    import math
+    for T, k, E in [(2048, 4, 60), (8192, 4, 60), (1, 4, 60), (7, 2, 3), (100, 1, 100)]:
+        assert ora.capacity(T, k, E) == math.ceil(Fraction(3, 2) * T * k / E)
+    assert ora.capacity(2048, 4, 60) == 205
+
+
+def test_drop_pad_pins(ora):
+    """Drop-and-pad against a sort-based construction (np.flatnonzero per
+    expert), and against the dropless count sort when nothing overflows."""
+    g = rng(41)
+    E, k, T = 12, 3, 50
+    idx = np.stack([g.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    idx[:20, 0] = 5                                   # expert 5 over capacity
+    idx[:20] = np.where((idx[:20] == 5) & (np.arange(k) > 0), (idx[:20] + 1) % E, idx[:20])
+    C = ora.capacity(T, k, E)
+    buf, offs, perm, inv = ora.drop_pad(idx, E, C)
+    flat = idx.ravel()
+    kept_total = 0
+    for e in range(E):
+        ids = np.flatnonzero(flat == e)               # assignment ids in token order
+        kept = ids[:C]
+        assert np.array_equal(buf[e, :len(kept)], kept) and np.all(buf[e, len(kept):] == -1)
+        assert offs[e] == kept_total and np.array_equal(perm[kept_total:kept_total + len(kept)], kept)
+        assert np.array_equal(inv[kept], kept_total + np.arange(len(kept)))
+        assert np.all(inv[ids[C:]] == -1)
+        kept_total += len(kept)
+    assert offs[E] == kept_total and np.all(perm[kept_total:] == -1)
+    assert (flat == 5).sum() > C and kept_total < T * k      # something was dropped
+    # capacity above every load: the dropless count sort
+    ro, rp, ri = ora.route(idx, E)
+    buf, offs, perm, inv = ora.drop_pad(idx, E, T * k)
+    assert np.array_equal(offs, ro) and np.array_equal(perm, rp) and np.array_equal(inv, ri)
+    # capacity 0 drops everything
+    buf, offs, perm, inv = ora.drop_pad(idx, E, 0)
+    assert buf.size == 0 and np.all(offs == 0) and np.all(perm == -1) and np.all(inv == -1)
+
+
+def test_fake_quant_forward_pins(ora):
+    """Forward equals the eq. (6) codes of the quantisers times their scales
+    (weights: b=4, group 32; activations: b=8, one group per row); error at
+    most s/2 except a clipped positive maximum."""
+    w = _crafted_weights()
+    q, s = ora.quant_w4g32(w)
+    want = (np.repeat(s, 32, axis=1) * q.astype(np.float32)).astype(np.float32)
+    wb = ora.fake_quant(w, 4, 32)
+    assert np.array_equal(wb, want)
+    assert np.all(wb[0, :32] == 0.0)
+    x = (rng(42).standard_normal((9, 200)) * 3).astype(np.float32)
+    x[3] = 0.0
+    qa, sa = ora.quant_act_i8(x)
+    xb = ora.fake_quant(x, 8, 200)
+    assert np.array_equal(xb, (sa[:, None] * qa.astype(np.float32)).astype(np.float32))
+    err = np.abs(xb.astype(np.float64) - x)
+    clipped = (xb == (sa[:, None] * np.float32(127)).astype(np.float32)) & (x > 0)
+    assert np.all(err[~clipped] <= sa[:, None].repeat(200, 1)[~clipped] * 0.5 * (1 + 1e-6))
+    with pytest.raises(ValueError):
+        ora.fake_quant(x, 5, 200)
+
+
+def test_fake_quant_ste_against_torch(ora):
+    """Straight-through gradient against torch's per-channel fake quantiser
+    (autograd), one channel per group of 32, scale s_g, zero point 0, range
+    [-8, 7]; all-zero groups pass the gradient.  torch scales by the
+    reciprocal where eq. (6) divides; the two quotients round differently
+    only at a group maximum, whose quotient lies within an ulp of 7.5, and
+    those entries are compared with the division's own decision instead."""
+    import torch
+    g = rng(43)
+    w = (g.standard_normal((64, 256)) * 0.05).astype(np.float32)
+    # groups whose positive maximum sits exactly on 7.5 * s or just off it
+    w[0, :32] = np.linspace(-0.7, 1.0, 32, dtype=np.float32)
+    w[1, :32] = np.linspace(-1.0, 0.9, 32, dtype=np.float32)
+    w[2, 32:64] = 0.0
+    gout = g.standard_normal(w.shape).astype(np.float32)
+    wb, gin = ora.fake_quant(w, 4, 32, gout)
+    _, s = ora.quant_w4g32(w)
+    xs = torch.from_numpy(w.reshape(-1, 32)).requires_grad_(True)
+    sc = torch.from_numpy(s.reshape(-1).copy())
+    nz = sc > 0
+    sc_t = torch.where(nz, sc, torch.ones_like(sc))
+    y = torch.fake_quantize_per_channel_affine(xs, sc_t, torch.zeros_like(sc, dtype=torch.int32), 0, -8, 7)
+    y.backward(torch.from_numpy(gout.reshape(-1, 32)))
+    gt = xs.grad.numpy().copy()
+    gt[~nz.numpy()] = gout.reshape(-1, 32)[~nz.numpy()]
+    q_div = np.rint(w.reshape(-1, 32) / np.where(s.reshape(-1, 1) > 0, s.reshape(-1, 1), 1)).astype(np.float32)
+    q_mul = np.rint(w.reshape(-1, 32) * (np.float32(1) / np.where(s.reshape(-1, 1) > 0, s.reshape(-1, 1), 1)).astype(np.float32))
+    same = q_div == q_mul
+    gm = np.abs(w.reshape(-1, 32)).max(1, keepdims=True)
+    is_max = np.abs(w.reshape(-1, 32)) == gm
+    assert np.all(is_max[~same])
+    assert np.array_equal(gin.reshape(-1, 32)[same], gt[same])
+    assert np.array_equal(wb.reshape(-1, 32)[same], y.detach().numpy()[same])
+    # at the excluded maxima the gradient passes iff the quotient rounds into range
+    g_div = np.where(q_div <= 7, gout.reshape(-1, 32), 0.0)
+    assert np.array_equal(gin.reshape(-1, 32)[~same], g_div[~same])
+    clipped = (gin == 0) & (gout != 0)
+    # only positive group maxima are ever clipped, and they are (a quotient
+    # at or above 7.5 is common: s is rounded to FP32)
+    assert np.all((is_max & (w.reshape(-1, 32) > 0))[clipped.reshape(-1, 32)])
+    assert clipped.sum() > 10
