@@ -406,6 +406,71 @@ mm_status mm_attn_decode_i8(int64_t B, int32_t n_h, int32_t n_kv, int32_t d_h, i
                             const float* v_scale, float* out, void* ws, size_t ws_bytes,
                             void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Training side of the layer (MobileMoE close reading, section "Pre-training":
+ * the MoE stability list balances load through an expert bias updated from
+ * the batch, without an auxiliary loss; the efficiency list gives every expert
+ * a fixed token buffer, drop-and-pad with capacity factor 1.5; section
+ * "Quantisation-aware training": eq. (6) applied as fake quantisation).
+ * ------------------------------------------------------------------------- */
+
+/*
+ * Aux-loss-free balancing step.  load_e = number of the T*k ids in topk_idx
+ * (device int32 [T][k]) equal to e; every bias (device FP32 [E], updated in
+ * place) moves by lambda towards balance: + lambda if load_e < T*k/E,
+ * - lambda if above, unchanged if equal (compared exactly in integers; one
+ * FP32 add).  load (device int32 [E], may be NULL) receives load_e.  Ids
+ * outside [0, E) are not counted.  Bit-identical to the oracle.
+ * Errors: MM_ERR_NULL / MM_ERR_ALIGN, MM_ERR_SHAPE (E outside [1, 4096],
+ * T*k >= 2^31).  T = 0 is a no-op.
+ */
+mm_status mm_bias_update(int64_t T, int32_t E, int32_t k, const int32_t* topk_idx, float lambda,
+                         float* bias, int32_t* load, void* stream);
+
+/* Per-expert buffer rows of drop-and-pad: ceil((num / den) * T * k / E) in
+ * exact integer arithmetic (num / den = 3 / 2 for the factor 1.5); -1 for
+ * invalid arguments. */
+int64_t mm_drop_pad_capacity(int64_t T, int32_t k, int32_t E, int32_t num, int32_t den);
+
+/*
+ * Drop-and-pad dispatch from the stable count sort of mm_route_permute
+ * (offsets [E+1], perm and inv_perm [T*k], all device int32) and the ids
+ * topk_idx [T][k]: assignments are admitted in token order and the first
+ * `capacity` of each expert kept.  Outputs (device int32):
+ *   buf       [E][capacity]  assignment id t*k+j of expert e's p-th kept
+ *                            assignment, -1 for padding rows
+ *   offsets_c [E+1]          exclusive prefix sum of min(load_e, capacity)
+ *   perm_c    [T*k]          kept assignments expert by expert, -1 past
+ *                            offsets_c[E]
+ *   inv_c     [T*k]          row of each assignment in perm_c, -1 if dropped
+ * (offsets_c, perm_c, inv_c are a routing the expert calls and the combine
+ * take as they take the dropless one; the combine skips -1 rows).
+ * Bit-identical to the oracle.  buf may be NULL when E * capacity = 0.
+ * Errors: MM_ERR_NULL / MM_ERR_ALIGN, MM_ERR_SHAPE (E outside [1, 4096],
+ * negative capacity, E * capacity or T*k >= 2^31).
+ */
+mm_status mm_drop_pad(int64_t T, int32_t E, int32_t k, int64_t capacity, const int32_t* topk_idx,
+                      const int32_t* offsets, const int32_t* perm, const int32_t* inv_perm,
+                      int32_t* buf, int32_t* offsets_c, int32_t* perm_c, int32_t* inv_c,
+                      void* stream);
+
+/*
+ * Fake quantisation of QAT, eq. (6) with b = bits over groups of `group`
+ * consecutive elements of each row of x (device FP32 [rows][cols]):
+ * s = (2 max|x_g|) / (2^b - 1), u = round_half_even(x / s) (IEEE quotient),
+ *   x_bar = s * clamp(u, -2^(b-1), 2^(b-1) - 1)                (FP32)
+ * and its straight-through backward (rounding's derivative taken as 1, the
+ * clamp's at u):  grad_in = grad_out where u lies in the clamp range, else 0;
+ * an all-zero group gives x_bar = 0 and passes the gradient.  x_bar (may be
+ * NULL) and the pair grad_out / grad_in (both NULL or both set) are device
+ * FP32 [rows][cols]; either or both are computed in one pass.
+ * bits 4 or 8; group 32 (cols a multiple of 32) or group = cols (one group
+ * per row, cols a multiple of 4).  Bit-identical to the oracle.
+ * Errors: MM_ERR_NULL / MM_ERR_ALIGN, MM_ERR_SHAPE.
+ */
+mm_status mm_fake_quant(int64_t rows, int64_t cols, int32_t bits, int64_t group, const float* x,
+                        float* x_bar, const float* grad_out, float* grad_in, void* stream);
+
 /* Row RMSNorm with unit gain used between stacked layers of the decode
  * workload (not part of eq. (*)): y = x / sqrt(mean(x^2) + eps), FP32. */
 mm_status mm_rmsnorm_f32(int64_t rows, int64_t cols, float eps, const float* x, float* y,

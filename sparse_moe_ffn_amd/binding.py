@@ -33,6 +33,7 @@ EXPORTS = (
     "mm_rmsnorm_f32", "mm_expert_gateup_swiglu_dbg", "mm_expert_down_dbg", "mm_moe_forward",
     "mm_act_quant_i8_layout", "mm_expert_gateup_pair_f32", "mm_linear_w4a8",
     "mm_attn_workspace_bytes", "mm_kv_append_i8", "mm_attn_decode_i8",
+    "mm_bias_update", "mm_drop_pad_capacity", "mm_drop_pad", "mm_fake_quant",
 )
 
 
@@ -92,6 +93,11 @@ _SIGS = {
                         ctypes.c_int),
     "mm_attn_decode_i8": ([_I64, _I32, _I32, _I32, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                            _VP, _SZ, _VP], ctypes.c_int),
+    "mm_bias_update": ([_I64, _I32, _I32, _VP, _F, _VP, _VP, _VP], ctypes.c_int),
+    "mm_drop_pad_capacity": ([_I64, _I32, _I32, _I32, _I32], _I64),
+    "mm_drop_pad": ([_I64, _I32, _I32, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
+                    ctypes.c_int),
+    "mm_fake_quant": ([_I64, _I64, _I32, _I64, _VP, _VP, _VP, _VP, _VP], ctypes.c_int),
     "mm_moe_forward": ([_DESC, _I64, _VP, _VP, _VP, Weight, Weight, Weight, Weight, _VP, _VP, _VP,
                         _VP, _F, _VP, _SZ, _VP], ctypes.c_int),
 }
@@ -270,6 +276,27 @@ def attn_decode_i8(B, n_h, n_kv, d_h, max_T, max_len, lens, q, k_cache, v_cache,
                                     _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
                                     _ptr(out), _ptr(ws), ws_bytes, _stream(stream)),
            "mm_attn_decode_i8")
+
+
+def bias_update(T, E, k, topk_idx, lam, bias, load_out=None, stream=None):
+    _check(load().mm_bias_update(T, E, k, _ptr(topk_idx), lam, _ptr(bias), _ptr(load_out),
+                                     _stream(stream)), "mm_bias_update")
+
+
+def drop_pad_capacity(T, k, E, num=3, den=2) -> int:
+    return int(load().mm_drop_pad_capacity(T, k, E, num, den))
+
+
+def drop_pad(T, E, k, capacity, topk_idx, offsets, perm, inv_perm, buf, offsets_c, perm_c, inv_c,
+             stream=None):
+    _check(load().mm_drop_pad(T, E, k, capacity, _ptr(topk_idx), _ptr(offsets), _ptr(perm),
+                                  _ptr(inv_perm), _ptr(buf), _ptr(offsets_c), _ptr(perm_c),
+                                  _ptr(inv_c), _stream(stream)), "mm_drop_pad")
+
+
+def fake_quant(rows, cols, bits, group, x, x_bar=None, grad_out=None, grad_in=None, stream=None):
+    _check(load().mm_fake_quant(rows, cols, bits, group, _ptr(x), _ptr(x_bar), _ptr(grad_out),
+                                    _ptr(grad_in), _stream(stream)), "mm_fake_quant")
 
 
 def rmsnorm_f32(rows, cols, eps, x, y, stream=None):

@@ -8,6 +8,7 @@
 
 #include "../../include/mobmoe.h"
 #include "launch.h"
+#include "launch_train.h"
 
 namespace {
 
@@ -788,6 +789,70 @@ mm_status mm_attn_decode_i8(int64_t B, int32_t n_h, int32_t n_kv, int32_t d_h, i
                                            k_scale, v_scale, static_cast<float*>(ws), out,
                                            S(stream)),
                     "mm_attn_decode_i8");
+}
+
+mm_status mm_bias_update(int64_t T, int32_t E, int32_t k, const int32_t* topk_idx, float lambda,
+                         float* bias, int32_t* load, void* stream) {
+  if (T < 0 || E < 1 || E > 4096 || k < 1 || T * k >= (int64_t(1) << 31))
+    return fail(MM_ERR_SHAPE, "bias update: T %lld, E %d, k %d out of range", (long long)T, (int)E,
+                (int)k);
+  if (T == 0) return MM_OK;
+  MM_REQUIRE(topk_idx);
+  MM_REQUIRE(bias);
+  MM_OPTIONAL(load);
+  return hip_status(mm::launch_bias_update(T * k, E, topk_idx, lambda, bias, load, S(stream)),
+                    "mm_bias_update");
+}
+
+int64_t mm_drop_pad_capacity(int64_t T, int32_t k, int32_t E, int32_t num, int32_t den) {
+  if (T < 0 || k < 1 || E < 1 || num < 1 || den < 1 || T * k >= (int64_t(1) << 31)) return -1;
+  const int64_t a = T * k * num, b = (int64_t)E * den;
+  return (a + b - 1) / b;
+}
+
+mm_status mm_drop_pad(int64_t T, int32_t E, int32_t k, int64_t capacity, const int32_t* topk_idx,
+                      const int32_t* offsets, const int32_t* perm, const int32_t* inv_perm,
+                      int32_t* buf, int32_t* offsets_c, int32_t* perm_c, int32_t* inv_c,
+                      void* stream) {
+  if (T < 0 || E < 1 || E > 4096 || k < 1 || capacity < 0 || T * k >= (int64_t(1) << 31) ||
+      (int64_t)E * capacity >= (int64_t(1) << 31))
+    return fail(MM_ERR_SHAPE, "drop-and-pad: T %lld, E %d, k %d, capacity %lld out of range",
+                (long long)T, (int)E, (int)k, (long long)capacity);
+  MM_REQUIRE(offsets);
+  MM_REQUIRE(offsets_c);
+  if ((int64_t)E * capacity > 0) MM_REQUIRE(buf);
+  if (T > 0) {
+    MM_REQUIRE(topk_idx);
+    MM_REQUIRE(perm);
+    MM_REQUIRE(inv_perm);
+    MM_REQUIRE(perm_c);
+    MM_REQUIRE(inv_c);
+  }
+  return hip_status(mm::launch_drop_pad(T * k, E, capacity, topk_idx, offsets, perm, inv_perm, buf,
+                                        offsets_c, perm_c, inv_c, S(stream)),
+                    "mm_drop_pad");
+}
+
+mm_status mm_fake_quant(int64_t rows, int64_t cols, int32_t bits, int64_t group, const float* x,
+                        float* x_bar, const float* grad_out, float* grad_in, void* stream) {
+  if (rows < 0 || cols < 1 || (bits != 4 && bits != 8))
+    return fail(MM_ERR_SHAPE, "fake quant: rows %lld, cols %lld, bits %d", (long long)rows,
+                (long long)cols, (int)bits);
+  const bool row_group = group == cols;
+  if (!(group == 32 && cols % 32 == 0) && !(row_group && cols % 4 == 0))
+    return fail(MM_ERR_SHAPE, "fake quant: group %lld must be 32 (cols a multiple of 32) or cols "
+                "(a multiple of 4)", (long long)group);
+  if (rows * cols >= (int64_t(1) << 40)) return fail(MM_ERR_SHAPE, "fake quant: too large");
+  if ((grad_out == nullptr) != (grad_in == nullptr))
+    return fail(MM_ERR_NULL, "fake quant: grad_out and grad_in must both be set or both NULL");
+  if (rows == 0) return MM_OK;
+  MM_REQUIRE(x);
+  MM_OPTIONAL(x_bar);
+  MM_OPTIONAL(grad_out);
+  MM_OPTIONAL(grad_in);
+  return hip_status(mm::launch_fake_quant(rows, cols, bits, row_group && group != 32, x, x_bar,
+                                          grad_out, grad_in, S(stream)),
+                    "mm_fake_quant");
 }
 
 mm_status mm_rmsnorm_f32(int64_t rows, int64_t cols, float eps, const float* x, float* y,

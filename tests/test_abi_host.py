@@ -22,7 +22,7 @@ def lib():
 
 def header_symbols():
     src = open(os.path.join(ROOT, "include", "mobmoe.h")).read()
-    return set(re.findall(r"^(?:mm_status|const char\*|size_t)\s+(mm_\w+)\(", src, re.M))
+    return set(re.findall(r"^(?:mm_status|const char\*|size_t|int64_t)\s+(mm_\w+)\(", src, re.M))
 
 
 def test_header_and_binding_agree():
@@ -220,3 +220,30 @@ def test_attention_checks(lib):
         assert d(2, nh, nkv, 64, 16, ml, *args, FAKE, ws, None) == B.MM_ERR_SHAPE
     assert d(2, 12, 4, 64, 16, 16, *args, FAKE, ws - 4, None) == B.MM_ERR_WORKSPACE
     assert d(2, 12, 4, 64, 16, 16, None, *args[1:], FAKE, ws, None) == B.MM_ERR_NULL
+
+
+def test_training_side_checks(lib):
+    """Bias update, drop-and-pad and fake quantisation: host-side checks,
+    and the exact capacity arithmetic."""
+    from fractions import Fraction
+    import math
+    assert lib.mm_bias_update(0, 60, 4, None, 1e-3, None, None, None) == B.MM_OK
+    for E, k in [(0, 4), (4097, 4), (60, 0)]:
+        assert lib.mm_bias_update(8, E, k, FAKE, 1e-3, FAKE, None, None) == B.MM_ERR_SHAPE
+    assert lib.mm_bias_update(8, 60, 4, None, 1e-3, FAKE, None, None) == B.MM_ERR_NULL
+    for T, k, E in [(2048, 4, 60), (8192, 4, 60), (1, 4, 60), (7, 2, 3), (0, 4, 60)]:
+        assert lib.mm_drop_pad_capacity(T, k, E, 3, 2) == math.ceil(Fraction(3, 2) * T * k / E)
+    assert lib.mm_drop_pad_capacity(8, 4, 0, 3, 2) == -1
+    args = (FAKE,) * 8
+    assert lib.mm_drop_pad(8, 60, 4, -1, *args, None) == B.MM_ERR_SHAPE
+    assert lib.mm_drop_pad(8, 0, 4, 10, *args, None) == B.MM_ERR_SHAPE
+    assert lib.mm_drop_pad(8, 60, 4, 10, None, *args[1:], None) == B.MM_ERR_NULL
+    assert lib.mm_drop_pad(8, 60, 4, 10, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == B.MM_ERR_NULL
+    fq = lib.mm_fake_quant
+    assert fq(4, 64, 5, 32, FAKE, FAKE, None, None, None) == B.MM_ERR_SHAPE
+    assert fq(4, 48, 4, 32, FAKE, FAKE, None, None, None) == B.MM_ERR_SHAPE
+    assert fq(4, 64, 4, 16, FAKE, FAKE, None, None, None) == B.MM_ERR_SHAPE
+    assert fq(4, 66, 8, 66, FAKE, FAKE, None, None, None) == B.MM_ERR_SHAPE
+    assert fq(4, 64, 4, 32, FAKE, FAKE, FAKE, None, None) == B.MM_ERR_NULL
+    assert fq(4, 64, 4, 32, None, FAKE, None, None, None) == B.MM_ERR_NULL
+    assert fq(0, 64, 4, 32, None, None, None, None, None) == B.MM_OK

@@ -269,6 +269,95 @@ def test_route_permute_bitexact(T, E, k, skew):
     assert np.array_equal(np_(inv), i_ref)
 
 
+# ------------------------------------------------------------ training side
+def _skewed_ids(g, T, E, k):
+    p = np.arange(1, E + 1, dtype=np.float64) ** -1.2
+    p /= p.sum()
+    return np.stack([g.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("T,E,k", [(2048, 60, 4), (1, 60, 4), (65536, 60, 4), (15, 4, 2)])
+def test_bias_update_bitexact(T, E, k):
+    """mm_bias_update: loads and updated biases bit-identical to the oracle."""
+    g = rng(T + E)
+    idx = _skewed_ids(g, T, E, k)
+    bias = g.standard_normal(E).astype(np.float32)
+    bd = dev(bias)
+    load = torch.empty((E,), dtype=torch.int32, device=DEV)
+    B.bias_update(T, E, k, dev(idx), 1e-3, bd, load)
+    ref, ref_load = oracle.bias_update(idx, bias, E, 1e-3)
+    assert np.array_equal(np_(load), ref_load)
+    assert np.array_equal(np_(bd).view(np.int32), ref.view(np.int32))
+    # balanced routing: biases unchanged
+    idx = ((np.arange(E)[:, None] * k + np.arange(k)[None, :]) % E).astype(np.int32)
+    bd = dev(bias)
+    B.bias_update(E, E, k, dev(idx), 1e-3, bd)
+    assert np.array_equal(np_(bd).view(np.int32), bias.view(np.int32))
+
+
+@pytest.mark.parametrize("T,E,k", [(2048, 60, 4), (8192, 60, 4), (3, 60, 4), (37, 8, 2)])
+def test_drop_pad_bitexact(T, E, k):
+    """mm_drop_pad after mm_route_permute: padded table and kept routing
+    bit-identical to the oracle at capacity factor 1.5, 0, 1 and above every load."""
+    g = rng(T * 3 + E)
+    idx = _skewed_ids(g, T, E, k)
+    ds = B.desc(64, E, 64, 0, k)
+    off = torch.empty((E + 1,), dtype=torch.int32, device=DEV)
+    perm = torch.empty((T * k,), dtype=torch.int32, device=DEV)
+    inv = torch.empty((T * k,), dtype=torch.int32, device=DEV)
+    nb = B.workspace_bytes(ds, T, B.MM_WS_ROUTE)
+    ws = torch.empty((nb,), dtype=torch.uint8, device=DEV)
+    idx_d = dev(idx)
+    B.route_permute(ds, T, idx_d, off, perm, inv, ws, nb)
+    cap = B.drop_pad_capacity(T, k, E)
+    assert cap == oracle.capacity(T, k, E)
+    dropped_some = False
+    for C in [cap, 0, 1, T * k]:
+        buf = torch.full((max(E * C, 1),), 7, dtype=torch.int32, device=DEV)
+        offc = torch.empty((E + 1,), dtype=torch.int32, device=DEV)
+        permc = torch.full((T * k,), 7, dtype=torch.int32, device=DEV)
+        invc = torch.full((T * k,), 7, dtype=torch.int32, device=DEV)
+        B.drop_pad(T, E, k, C, idx_d, off, perm, inv, buf, offc, permc, invc)
+        rb, ro, rp, ri = oracle.drop_pad(idx, E, C)
+        assert np.array_equal(np_(buf)[:E * C], rb.ravel()), C
+        assert np.array_equal(np_(offc), ro), C
+        assert np.array_equal(np_(permc), rp), C
+        assert np.array_equal(np_(invc), ri), C
+        dropped_some |= C == cap and ro[E] < T * k
+    if T >= 2048:
+        assert dropped_some          # the skewed routing overflows some expert at factor 1.5
+
+
+@pytest.mark.parametrize("rows,cols,bits,group", [(4096, 384, 4, 32), (771, 768, 4, 32),
+                                                  (2053, 768, 8, 768), (5, 4, 8, 4),
+                                                  (64, 1536, 4, 1536), (8, 32, 8, 32)])
+def test_fake_quant_bitexact(rows, cols, bits, group):
+    """mm_fake_quant forward and straight-through backward bit-identical to
+    the oracle, with all-zero groups, exact +-maxima and tiny values."""
+    g = rng(rows + cols + bits)
+    x = (g.standard_normal((rows, cols)) * 0.05).astype(np.float32)
+    x[0, :min(group, cols)] = 0.0
+    if rows > 2:
+        x[1, :min(32, cols)] = np.linspace(-1, 1, min(32, cols), dtype=np.float32)
+        x[2, :min(32, cols)] = 1e-30
+    go = g.standard_normal((rows, cols)).astype(np.float32)
+    xb = torch.empty((rows, cols), dtype=torch.float32, device=DEV)
+    gi = torch.empty((rows, cols), dtype=torch.float32, device=DEV)
+    xd, god = dev(x), dev(go)
+    B.fake_quant(rows, cols, bits, group, xd, xb, god, gi)
+    rxb, rgi = oracle.fake_quant(x, bits, group, go)
+    assert np.array_equal(np_(xb).view(np.int32), rxb.view(np.int32))
+    assert np.array_equal(np_(gi).view(np.int32), rgi.view(np.int32))
+    assert (rgi == 0).sum() > 0 or bits == 8     # some positive maxima clip at b = 4
+    # forward only, and backward only
+    xb2 = torch.empty_like(xb)
+    B.fake_quant(rows, cols, bits, group, xd, xb2)
+    assert torch.equal(xb2, xb)
+    gi2 = torch.empty_like(gi)
+    B.fake_quant(rows, cols, bits, group, xd, None, god, gi2)
+    assert torch.equal(gi2, gi)
+
+
 # ------------------------------------------------------------ expert stages
 def _sorted_reference(layer, w, lw, x):
     """Oracle per-sorted-row gate/up and down results for the layer's routing."""
