@@ -332,3 +332,34 @@ def fake_quant(x, bits: int, group: int, gout=None):
     if rc:
         raise ValueError("ora_fake_quant: bad bits or group")
     return xbar if gout is None else (xbar, gin)
+
+
+def expert_train_forward(offsets, xs, wgu, wd):
+    """QAT forward of the routed experts over expert-ordered rows ->
+    (gu [R, 2h], abar [R, h], f [R, d]) float32."""
+    offsets = np.ascontiguousarray(offsets, np.int32)
+    xs, wgu, wd = _f32(xs), _f32(wgu), _f32(wd)
+    E, h2, d = wgu.shape
+    h = h2 // 2
+    R = xs.shape[0]
+    gu = np.empty((R, 2 * h), np.float32)
+    abar = np.empty((R, h), np.float32)
+    f = np.empty((R, d), np.float32)
+    _load().ora_expert_train_forward(E, d, h, _p(offsets), _p(xs), _p(wgu), _p(wd), _p(gu), _p(abar),
+                                     _p(f))
+    return gu, abar, f
+
+
+def expert_backward(offsets, xs, wgu, wd, gu, df):
+    """Backward of expert_train_forward -> (dxs [R, d], dwgu [E, 2h, d], dwd [E, d, h]) float64."""
+    offsets = np.ascontiguousarray(offsets, np.int32)
+    xs, wgu, wd, gu, df = _f32(xs), _f32(wgu), _f32(wd), _f32(gu), _f32(df)
+    E, h2, d = wgu.shape
+    h = h2 // 2
+    R = xs.shape[0]
+    dxs = np.empty((R, d), np.float64)
+    dwgu = np.empty((E, 2 * h, d), np.float64)
+    dwd = np.empty((E, d, h), np.float64)
+    _load().ora_expert_backward(E, d, h, _p(offsets), _p(xs), _p(wgu), _p(wd), _p(gu), _p(df),
+                                _p(dxs), _p(dwgu), _p(dwd))
+    return dxs, dwgu, dwd

@@ -727,4 +727,113 @@ int ora_fake_quant(int64_t rows, int64_t cols, int bits, int64_t group, const fl
   return 0;
 }
 
+// ---------------------------------------------------------------------------
+// QAT forward and backward of the routed experts ([P1] "Pre-training":
+// every expert's FFN batched into grouped matrix products; "Quantisation-
+// aware training": weights and activations fake-quantised, eq. (6)).  Rows
+// are the kept assignments in expert order: expert e owns rows
+// [offsets[e], offsets[e+1]) of xs (the fake-quantised input rows).
+// Weights are fake-quantised FP32: wgu [E][2h][d] (gate rows first), wd
+// [E][d][h].  Per row r of expert e:
+//   gu = wgu_e xs_r                           (gate g = gu[0:h], up u = gu[h:2h])
+//   a  = silu32(g) * u                         (FP32, the SwiGLU of R6)
+//   abar = fake quant of a, b = 8, one group per row (eq. (6))
+//   f  = wd_e abar
+// Products and sums in double; the a / abar step in FP32 as stated, since
+// it decides INT8 codes.
+static void train_act_row(int h, const float* gu_row, float* a, float* abar, float* pass) {
+  float amax = 0.0f;
+  for (int j = 0; j < h; ++j) {
+    a[j] = silu32(gu_row[j]) * gu_row[h + j];
+    amax = std::max(amax, std::fabs(a[j]));
+  }
+  const float s = (2.0f * amax) / 255.0f;
+  for (int j = 0; j < h; ++j) {
+    if (s == 0.0f) {
+      abar[j] = 0.0f;
+      pass[j] = 1.0f;
+      continue;
+    }
+    const float u = std::nearbyint(a[j] / s);
+    pass[j] = (u >= -128.0f && u <= 127.0f) ? 1.0f : 0.0f;
+    abar[j] = s * std::min(std::max(u, -128.0f), 127.0f);
+  }
+}
+
+int ora_expert_train_forward(int E, int d, int h, const int32_t* offsets, const float* xs,
+                             const float* wgu, const float* wd, float* gu, float* abar, float* f) {
+  std::vector<float> a(h), pass(h);
+  for (int e = 0; e < E; ++e) {
+    const float* Wg = wgu + (int64_t)e * 2 * h * d;
+    const float* Wd = wd + (int64_t)e * d * h;
+    for (int64_t r = offsets[e]; r < offsets[e + 1]; ++r) {
+      const float* x = xs + r * d;
+      float* g = gu + r * 2 * h;
+      for (int j = 0; j < 2 * h; ++j) {
+        double acc = 0.0;
+        for (int c = 0; c < d; ++c) acc += (double)Wg[(int64_t)j * d + c] * (double)x[c];
+        g[j] = (float)acc;
+      }
+      train_act_row(h, g, a.data(), abar + r * h, pass.data());
+      for (int c = 0; c < d; ++c) {
+        double acc = 0.0;
+        for (int j = 0; j < h; ++j) acc += (double)Wd[(int64_t)c * h + j] * (double)abar[r * h + j];
+        f[r * d + c] = (float)acc;
+      }
+    }
+  }
+  return 0;
+}
+
+// Backward of the above given the forward's gu and the gradient df of the
+// expert output rows (straight-through rounding in the activation quantiser,
+// its clamp differentiated at the rounded quotient; the row scale held
+// constant):
+//   dabar = wd_e^T df_r;  da = dabar * pass(a)
+//   dg = da * u * silu'(g),  du = da * silu(g),   silu'(g) = sig(g) (1 + g (1 - sig(g)))
+//   dxs_r = wgu_e^T [dg, du]
+//   dwd_e  = sum over the expert's rows of df_r abar_r^T      [d][h]
+//   dwgu_e = sum over the expert's rows of [dg, du]_r xs_r^T [2h][d]
+// abar and pass are recomputed from gu by the FP32 rule above; everything
+// else in double.  An expert without rows gets zero weight gradients.
+int ora_expert_backward(int E, int d, int h, const int32_t* offsets, const float* xs,
+                        const float* wgu, const float* wd, const float* gu, const float* df,
+                        double* dxs, double* dwgu, double* dwd) {
+  std::vector<float> a(h), abar(h), pass(h);
+  std::vector<double> dgu(2 * h);
+  for (int e = 0; e < E; ++e) {
+    const float* Wg = wgu + (int64_t)e * 2 * h * d;
+    const float* Wd = wd + (int64_t)e * d * h;
+    double* dWg = dwgu + (int64_t)e * 2 * h * d;
+    double* dWd = dwd + (int64_t)e * d * h;
+    for (int64_t i = 0; i < (int64_t)2 * h * d; ++i) dWg[i] = 0.0;
+    for (int64_t i = 0; i < (int64_t)d * h; ++i) dWd[i] = 0.0;
+    for (int64_t r = offsets[e]; r < offsets[e + 1]; ++r) {
+      const float* g = gu + r * 2 * h;
+      const float* x = xs + r * d;
+      const float* dfr = df + r * d;
+      train_act_row(h, g, a.data(), abar.data(), pass.data());
+      for (int j = 0; j < h; ++j) {
+        double dab = 0.0;
+        for (int c = 0; c < d; ++c) dab += (double)Wd[(int64_t)c * h + j] * (double)dfr[c];
+        const double da = dab * pass[j];
+        const double gj = g[j], uj = g[h + j];
+        const double sig = 1.0 / (1.0 + std::exp(-gj));
+        dgu[j] = da * uj * sig * (1.0 + gj * (1.0 - sig));
+        dgu[h + j] = da * gj * sig;
+      }
+      for (int c = 0; c < d; ++c) {
+        double acc = 0.0;
+        for (int j = 0; j < 2 * h; ++j) acc += (double)Wg[(int64_t)j * d + c] * dgu[j];
+        dxs[r * d + c] = acc;
+      }
+      for (int c = 0; c < d; ++c)
+        for (int j = 0; j < h; ++j) dWd[(int64_t)c * h + j] += (double)dfr[c] * (double)abar[j];
+      for (int j = 0; j < 2 * h; ++j)
+        for (int c = 0; c < d; ++c) dWg[(int64_t)j * d + c] += dgu[j] * (double)x[c];
+    }
+  }
+  return 0;
+}
+
 }  // extern "C"

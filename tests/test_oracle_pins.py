@@ -735,3 +735,71 @@ def test_fake_quant_ste_against_torch(ora):
     # at or above 7.5 is common: s is rounded to FP32)
     assert np.all((is_max & (w.reshape(-1, 32) > 0))[clipped.reshape(-1, 32)])
     assert clipped.sum() > 10
+
+
+def _expert_case(g, E=3, d=64, h=32, counts=(5, 0, 7)):
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offs[-1])
+    xs = g.standard_normal((R, d)).astype(np.float32)
+    wgu = (g.standard_normal((E, 2 * h, d)) * 0.2).astype(np.float32)
+    wd = (g.standard_normal((E, d, h)) * 0.2).astype(np.float32)
+    return offs, xs, wgu, wd
+
+
+def _act32(ora, gu, h):
+    g, u = gu[:, :h], gu[:, h:]
+    return ((g / (np.float32(1) + ora.exp_ref(-g))).astype(np.float32) * u).astype(np.float32)
+
+
+def test_expert_train_forward_pins(ora):
+    """QAT expert forward: gate/up and down products equal float64 matrix
+    products per expert; abar equals the pinned activation fake quantiser
+    applied to the FP32 SwiGLU."""
+    g = rng(50)
+    offs, xs, wgu, wd = _expert_case(g)
+    gu, abar, f = ora.expert_train_forward(offs, xs, wgu, wd)
+    h = wgu.shape[1] // 2
+    for e in range(len(offs) - 1):
+        r0, r1 = offs[e], offs[e + 1]
+        want = xs[r0:r1].astype(np.float64) @ wgu[e].astype(np.float64).T
+        np.testing.assert_allclose(gu[r0:r1], want, rtol=1e-6, atol=1e-6)
+        np.testing.assert_allclose(f[r0:r1], abar[r0:r1].astype(np.float64) @ wd[e].astype(np.float64).T,
+                                   rtol=1e-6, atol=1e-6)
+    assert np.array_equal(abar, ora.fake_quant(_act32(ora, gu, h), 8, h))
+
+
+def test_expert_backward_against_autograd(ora):
+    """QAT expert backward against torch autograd (float64) of the same
+    forward, with the activation quantiser as a straight-through node whose
+    values and pass mask come from the pinned fake quantiser; an expert
+    without rows gets zero weight gradients."""
+    import torch
+    g = rng(51)
+    offs, xs, wgu, wd = _expert_case(g)
+    gu, abar, _ = ora.expert_train_forward(offs, xs, wgu, wd)
+    h = wgu.shape[1] // 2
+    a32 = _act32(ora, gu, h)
+    # planted clips: make some rows' maximum exactly hit the clamp path
+    _, pass_ = ora.fake_quant(a32, 8, h, np.ones_like(a32))
+    df = g.standard_normal((xs.shape[0], xs.shape[1])).astype(np.float32)
+    dxs, dwgu, dwd = ora.expert_backward(offs, xs, wgu, wd, gu, df)
+    X = torch.tensor(xs, dtype=torch.float64, requires_grad=True)
+    Wg = torch.tensor(wgu, dtype=torch.float64, requires_grad=True)
+    Wd = torch.tensor(wd, dtype=torch.float64, requires_grad=True)
+    loss = 0.0
+    for e in range(len(offs) - 1):
+        r0, r1 = int(offs[e]), int(offs[e + 1])
+        if r1 == r0:
+            continue
+        GU = X[r0:r1] @ Wg[e].T
+        G, U = GU[:, :h], GU[:, h:]
+        A = G * torch.sigmoid(G) * U
+        Ab = torch.tensor(abar[r0:r1], dtype=torch.float64) + (A - A.detach()) * torch.tensor(pass_[r0:r1], dtype=torch.float64)
+        F = Ab @ Wd[e].T
+        loss = loss + (F * torch.tensor(df[r0:r1], dtype=torch.float64)).sum()
+    loss.backward()
+    np.testing.assert_allclose(dxs, X.grad.numpy(), rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(dwgu, Wg.grad.numpy(), rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(dwd, Wd.grad.numpy(), rtol=1e-9, atol=1e-9)
+    assert np.all(dwgu[1] == 0) and np.all(dwd[1] == 0)
+    assert (pass_ == 0).sum() >= 1          # some row maximum clips
