@@ -471,6 +471,59 @@ mm_status mm_drop_pad(int64_t T, int32_t E, int32_t k, int64_t capacity, const i
 mm_status mm_fake_quant(int64_t rows, int64_t cols, int32_t bits, int64_t group, const float* x,
                         float* x_bar, const float* grad_out, float* grad_in, void* stream);
 
+/*
+ * Row gather for the training passes: dst[r] = scale[perm[r]] * src[perm[r] / k]
+ * for r < R (scale NULL: 1; perm[r] < 0: a zero row).  src device FP32 [*][d],
+ * dst [R][d], perm device int32 [R] (e.g. perm_c of mm_drop_pad), scale
+ * device FP32 per assignment t*k+j (e.g. the gate weights, to form the
+ * expert output gradient w_tj dy_t).  d a multiple of 4.
+ * Errors: MM_ERR_NULL / MM_ERR_ALIGN, MM_ERR_SHAPE.
+ */
+mm_status mm_gather_rows(int64_t R, int64_t d, int32_t k, const int32_t* perm, const float* scale,
+                         const float* src, float* dst, void* stream);
+
+/*
+ * QAT forward of the routed experts over expert-ordered rows (section
+ * "Pre-training": the experts batched into grouped matrix products; eq. (6)
+ * fake quantisation).  Expert e owns rows [offsets[e], offsets[e+1]) (device
+ * int32 [E+1], offsets[E] = R) of xs (device FP32 [R][d], the fake-quantised
+ * input rows); w_gu FP32 [E][2h][d] (gate rows first) and w_d FP32 [E][d][h]
+ * are the fake-quantised weights.  Per row:
+ *   gu = w_gu_e xs_r                 -> gu    [R][2h]  (FP32 matrix cores)
+ *   a_bar = fake quant (b = 8, per row) of silu(g) * u  -> a_bar [R][h]
+ *   f = w_d_e a_bar_r                -> f     [R][d]
+ * gu and a_bar are what mm_expert_backward_f32 takes.  d, h multiples of 16.
+ * Errors: MM_ERR_NULL / MM_ERR_ALIGN, MM_ERR_SHAPE.
+ */
+mm_status mm_expert_train_forward_f32(int32_t E, int32_t d, int32_t h, int64_t R,
+                                      const int32_t* offsets, const float* xs, const float* w_gu,
+                                      const float* w_d, float* gu, float* a_bar, float* f,
+                                      void* stream);
+
+/* Workspace of mm_expert_backward_f32: 12 * R * h bytes (0 for invalid sizes). */
+size_t mm_expert_backward_workspace_bytes(int64_t R, int32_t h);
+
+/*
+ * Backward of mm_expert_train_forward_f32 given the gradient df of the
+ * expert output rows (device FP32 [R][d]) and the forward's gu and a_bar:
+ *   da = (w_d_e^T df_r) * pass   (straight-through rounding; the clamp of the
+ *        INT8 activation quantiser differentiated at the rounded quotient)
+ *   dg = da u silu'(g), du = da silu(g)
+ *   dxs   [R][d]      = w_gu_e^T [dg, du]
+ *   dw_d  [E][d][h]   = sum over the expert's rows of df_r a_bar_r^T
+ *   dw_gu [E][2h][d]  = sum over the expert's rows of [dg, du]_r xs_r^T
+ * (experts without rows get zero weight gradients).  The gradients are with
+ * respect to the fake-quantised operands; mm_fake_quant's backward carries
+ * them to the latent weights and inputs.  FP32 matrix cores, FP32 sums:
+ * tolerance-checked against the oracle's double evaluation.
+ * Errors: MM_ERR_NULL / MM_ERR_ALIGN, MM_ERR_SHAPE, MM_ERR_WORKSPACE.
+ */
+mm_status mm_expert_backward_f32(int32_t E, int32_t d, int32_t h, int64_t R, const int32_t* offsets,
+                                 const float* xs, const float* w_gu, const float* w_d,
+                                 const float* gu, const float* a_bar, const float* df, float* dxs,
+                                 float* dw_gu, float* dw_d, void* ws, size_t ws_bytes,
+                                 void* stream);
+
 /* Row RMSNorm with unit gain used between stacked layers of the decode
  * workload (not part of eq. (*)): y = x / sqrt(mean(x^2) + eps), FP32. */
 mm_status mm_rmsnorm_f32(int64_t rows, int64_t cols, float eps, const float* x, float* y,

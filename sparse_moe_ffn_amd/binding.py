@@ -34,6 +34,8 @@ EXPORTS = (
     "mm_act_quant_i8_layout", "mm_expert_gateup_pair_f32", "mm_linear_w4a8",
     "mm_attn_workspace_bytes", "mm_kv_append_i8", "mm_attn_decode_i8",
     "mm_bias_update", "mm_drop_pad_capacity", "mm_drop_pad", "mm_fake_quant",
+    "mm_gather_rows", "mm_expert_train_forward_f32", "mm_expert_backward_workspace_bytes",
+    "mm_expert_backward_f32",
 )
 
 
@@ -98,6 +100,11 @@ _SIGS = {
     "mm_drop_pad": ([_I64, _I32, _I32, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
                     ctypes.c_int),
     "mm_fake_quant": ([_I64, _I64, _I32, _I64, _VP, _VP, _VP, _VP, _VP], ctypes.c_int),
+    "mm_gather_rows": ([_I64, _I64, _I32, _VP, _VP, _VP, _VP, _VP], ctypes.c_int),
+    "mm_expert_train_forward_f32": ([_I32, _I32, _I32, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
+                                    ctypes.c_int),
+    "mm_expert_backward_workspace_bytes": ([_I64, _I32], _SZ),
+    "mm_expert_backward_f32": ([_I32, _I32, _I32, _I64] + [_VP] * 11 + [_SZ, _VP], ctypes.c_int),
     "mm_moe_forward": ([_DESC, _I64, _VP, _VP, _VP, Weight, Weight, Weight, Weight, _VP, _VP, _VP,
                         _VP, _F, _VP, _SZ, _VP], ctypes.c_int),
 }
@@ -297,6 +304,29 @@ def drop_pad(T, E, k, capacity, topk_idx, offsets, perm, inv_perm, buf, offsets_
 def fake_quant(rows, cols, bits, group, x, x_bar=None, grad_out=None, grad_in=None, stream=None):
     _check(load().mm_fake_quant(rows, cols, bits, group, _ptr(x), _ptr(x_bar), _ptr(grad_out),
                                     _ptr(grad_in), _stream(stream)), "mm_fake_quant")
+
+
+def gather_rows(R, d, k, perm, scale, src, dst, stream=None):
+    _check(load().mm_gather_rows(R, d, k, _ptr(perm), _ptr(scale), _ptr(src), _ptr(dst),
+                                 _stream(stream)), "mm_gather_rows")
+
+
+def expert_train_forward_f32(E, d, h, R, offsets, xs, w_gu, w_d, gu, a_bar, f, stream=None):
+    _check(load().mm_expert_train_forward_f32(E, d, h, R, _ptr(offsets), _ptr(xs), _ptr(w_gu),
+                                              _ptr(w_d), _ptr(gu), _ptr(a_bar), _ptr(f),
+                                              _stream(stream)), "mm_expert_train_forward_f32")
+
+
+def expert_backward_workspace_bytes(R, h) -> int:
+    return int(load().mm_expert_backward_workspace_bytes(R, h))
+
+
+def expert_backward_f32(E, d, h, R, offsets, xs, w_gu, w_d, gu, a_bar, df, dxs, dw_gu, dw_d, ws,
+                        ws_bytes, stream=None):
+    _check(load().mm_expert_backward_f32(E, d, h, R, _ptr(offsets), _ptr(xs), _ptr(w_gu), _ptr(w_d),
+                                         _ptr(gu), _ptr(a_bar), _ptr(df), _ptr(dxs), _ptr(dw_gu),
+                                         _ptr(dw_d), _ptr(ws), ws_bytes, _stream(stream)),
+           "mm_expert_backward_f32")
 
 
 def rmsnorm_f32(rows, cols, eps, x, y, stream=None):

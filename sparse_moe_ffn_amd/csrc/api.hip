@@ -855,6 +855,79 @@ mm_status mm_fake_quant(int64_t rows, int64_t cols, int32_t bits, int64_t group,
                     "mm_fake_quant");
 }
 
+mm_status mm_gather_rows(int64_t R, int64_t d, int32_t k, const int32_t* perm, const float* scale,
+                         const float* src, float* dst, void* stream) {
+  if (R < 0 || d < 4 || d % 4 || k < 1 || R * d >= (int64_t(1) << 40))
+    return fail(MM_ERR_SHAPE, "gather rows: R %lld, d %lld, k %d", (long long)R, (long long)d, (int)k);
+  if (R == 0) return MM_OK;
+  MM_REQUIRE(perm);
+  MM_OPTIONAL(scale);
+  MM_REQUIRE(src);
+  MM_REQUIRE(dst);
+  return hip_status(mm::launch_gather_rows(R, d, k, perm, scale, src, dst, S(stream)),
+                    "mm_gather_rows");
+}
+
+static mm_status check_train(int32_t E, int32_t d, int32_t h, int64_t R) {
+  if (E < 1 || E > 4096 || d < 16 || d % 16 || h < 16 || h % 16 || R < 0 ||
+      R >= (int64_t(1) << 31) || R * 2 * h >= (int64_t(1) << 40) || R * d >= (int64_t(1) << 40))
+    return fail(MM_ERR_SHAPE, "expert training pass: E %d, d %d, h %d, R %lld (d, h multiples of 16)",
+                (int)E, (int)d, (int)h, (long long)R);
+  return MM_OK;
+}
+
+mm_status mm_expert_train_forward_f32(int32_t E, int32_t d, int32_t h, int64_t R,
+                                      const int32_t* offsets, const float* xs, const float* w_gu,
+                                      const float* w_d, float* gu, float* a_bar, float* f,
+                                      void* stream) {
+  MM_TRY(check_train(E, d, h, R));
+  if (R == 0) return MM_OK;
+  MM_REQUIRE(offsets);
+  MM_REQUIRE(xs);
+  MM_REQUIRE(w_gu);
+  MM_REQUIRE(w_d);
+  MM_REQUIRE(gu);
+  MM_REQUIRE(a_bar);
+  MM_REQUIRE(f);
+  return hip_status(mm::launch_expert_train_forward(E, d, h, R, offsets, xs, w_gu, w_d, gu, a_bar, f,
+                                                    S(stream)),
+                    "mm_expert_train_forward_f32");
+}
+
+size_t mm_expert_backward_workspace_bytes(int64_t R, int32_t h) {
+  if (R < 0 || h < 1) return 0;
+  return std::max<size_t>((size_t)R * 3 * h * sizeof(float), 256);
+}
+
+mm_status mm_expert_backward_f32(int32_t E, int32_t d, int32_t h, int64_t R, const int32_t* offsets,
+                                 const float* xs, const float* w_gu, const float* w_d,
+                                 const float* gu, const float* a_bar, const float* df, float* dxs,
+                                 float* dw_gu, float* dw_d, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  MM_TRY(check_train(E, d, h, R));
+  MM_REQUIRE(offsets);
+  MM_REQUIRE(w_gu);
+  MM_REQUIRE(w_d);
+  MM_REQUIRE(dw_gu);
+  MM_REQUIRE(dw_d);
+  if (R > 0) {
+    MM_REQUIRE(xs);
+    MM_REQUIRE(gu);
+    MM_REQUIRE(a_bar);
+    MM_REQUIRE(df);
+    MM_REQUIRE(dxs);
+    MM_REQUIRE(ws);
+    if (ws_bytes < (size_t)R * 3 * h * sizeof(float))
+      return fail(MM_ERR_WORKSPACE, "expert backward workspace too small (need %zu bytes)",
+                  (size_t)R * 3 * h * sizeof(float));
+  }
+  float* dabar = static_cast<float*>(ws);
+  float* dgu = dabar + R * h;
+  return hip_status(mm::launch_expert_backward(E, d, h, R, offsets, xs, w_gu, w_d, gu, a_bar, df,
+                                               dxs, dw_gu, dw_d, dabar, dgu, S(stream)),
+                    "mm_expert_backward_f32");
+}
+
 mm_status mm_rmsnorm_f32(int64_t rows, int64_t cols, float eps, const float* x, float* y,
                          void* stream) {
   if (rows < 0 || cols <= 0) return fail(MM_ERR_SHAPE, "bad shape");

@@ -1,0 +1,274 @@
+// Training passes of the routed experts (MobileMoE close reading, section
+// "Pre-training": the experts' FFNs batched into grouped matrix products;
+// section "Quantisation-aware training": weights and activations fake-
+// quantised by eq. (6), gradients passed straight through the rounding).
+//
+// Grouped FP32 products on the FP32 matrix cores (v_mfma_f32_32x32x2_f32:
+// FP32 products, FP32 sums): C[m][n] = sum over k of A(m, k) B(k, n) with
+//   A(m, k) = A[m * lda + k]  (kAK)   or  A[k * lda + m]
+//   B(k, n) = B[n * ldb + k]  (kBK)   or  B[k * ldb + n].
+// Grouped by rows (!kGroupK): group e owns rows [off[e], off[e+1]) of A and
+// C and multiplies them by its own B (B + e * strideB); K is fixed.
+// Grouped by the reduction (kGroupK): group e sums k over [off[e], off[e+1])
+// into its own C (C + e * strideC); M and N are fixed.
+// Workgroup tile 64 x 64, four waves of 32 x 32, K slices of 16 staged
+// through LDS (k-major rows of 64 + 4 floats), the next slice's loads issued
+// before the current slice's matrix instructions.
+#include "common.h"
+#include "launch_train.h"
+
+namespace mm {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kBM = 64, kBN = 64, kBK = 16, kLd = 68;
+
+template <bool kAK, bool kBK_, bool kGroupK>
+__global__ __launch_bounds__(256) void k_gemm_f32(int E, int64_t M, int64_t N, int64_t K,
+                                                  const int32_t* __restrict__ off,
+                                                  const float* __restrict__ A, int64_t lda,
+                                                  const float* __restrict__ B, int64_t ldb,
+                                                  int64_t strideB, float* __restrict__ C,
+                                                  int64_t ldc, int64_t strideC) {
+  __shared__ float sA[kBK][kLd];
+  __shared__ float sB[kBK][kLd];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  int e;
+  int64_t m0, mEnd, n0, k0, kEnd;
+  if constexpr (kGroupK) {
+    const int64_t ntn = (N + kBN - 1) / kBN;
+    e = blockIdx.y;
+    m0 = (int64_t)(blockIdx.x / ntn) * kBM;
+    n0 = (int64_t)(blockIdx.x % ntn) * kBN;
+    mEnd = M;
+    k0 = off[e];
+    kEnd = off[e + 1];
+    C += (int64_t)e * strideC;
+  } else {
+    // find this workgroup's group and row tile: groups hold ceil(rows / 64) tiles each
+    int64_t bx = blockIdx.x;
+    e = -1;
+    for (int g = 0; g < E; ++g) {
+      const int64_t tiles = (off[g + 1] - off[g] + kBM - 1) / kBM;
+      if (bx < tiles) {
+        e = g;
+        break;
+      }
+      bx -= tiles;
+    }
+    if (e < 0) return;  // past the last tile (the grid is an upper bound)
+    m0 = off[e] + bx * kBM;
+    mEnd = off[e + 1];
+    n0 = (int64_t)blockIdx.y * kBN;
+    k0 = 0;
+    kEnd = K;
+    B += (int64_t)e * strideB;
+  }
+
+  // this thread's share of a K slice: one float4 of A and one of B
+  float4 ra, rb;
+  auto load = [&](int64_t k) {
+    if constexpr (kAK) {
+      const int64_t m = m0 + (t >> 2), kk = k + (t & 3) * 4;
+      ra = m < mEnd ? *reinterpret_cast<const float4*>(A + m * lda + kk) : make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
+      const int64_t kk = k + (t >> 4), m = m0 + (t & 15) * 4;
+      ra = (kk < kEnd && m < mEnd) ? *reinterpret_cast<const float4*>(A + kk * lda + m)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if constexpr (kBK_) {
+      const int64_t n = n0 + (t >> 2), kk = k + (t & 3) * 4;
+      rb = n < N ? *reinterpret_cast<const float4*>(B + n * ldb + kk) : make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
+      const int64_t kk = k + (t >> 4), n = n0 + (t & 15) * 4;
+      rb = (kk < kEnd && n < N) ? *reinterpret_cast<const float4*>(B + kk * ldb + n)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto store = [&]() {
+    if constexpr (kAK) {
+      const int mi = t >> 2, k4 = (t & 3) * 4;
+      sA[k4][mi] = ra.x;
+      sA[k4 + 1][mi] = ra.y;
+      sA[k4 + 2][mi] = ra.z;
+      sA[k4 + 3][mi] = ra.w;
+    } else {
+      *reinterpret_cast<float4*>(&sA[t >> 4][(t & 15) * 4]) = ra;
+    }
+    if constexpr (kBK_) {
+      const int ni = t >> 2, k4 = (t & 3) * 4;
+      sB[k4][ni] = rb.x;
+      sB[k4 + 1][ni] = rb.y;
+      sB[k4 + 2][ni] = rb.z;
+      sB[k4 + 3][ni] = rb.w;
+    } else {
+      *reinterpret_cast<float4*>(&sB[t >> 4][(t & 15) * 4]) = rb;
+    }
+  };
+
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  const int half = lane >> 5, li = lane & 31;
+  if (k0 < kEnd) load(k0);
+  for (int64_t k = k0; k < kEnd; k += kBK) {
+    __syncthreads();  // the previous slice's reads are done
+    store();
+    __syncthreads();
+    if (k + kBK < kEnd) load(k + kBK);
+#pragma unroll
+    for (int kk = 0; kk < kBK; kk += 2) {
+      const float a = sA[kk + half][wm * 32 + li];
+      const float b = sB[kk + half][wn * 32 + li];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+    }
+  }
+  // acc[r] holds row 8 (r / 4) + 4 half + r % 4, column li of the wave's 32 x 32
+  const int64_t col = n0 + wn * 32 + li;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t row = m0 + wm * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+    if (row < mEnd && col < N) C[row * ldc + col] = acc[r];
+  }
+}
+
+// Forward activation of one expert row (one wave per row): a = silu(g) * u
+// (FP32), then abar = eq. (6) fake quantisation of a with b = 8, one group
+// per row.  a is written to abar first and read back by the same lane.
+__global__ __launch_bounds__(256) void k_train_act(int64_t R, int h, const float* __restrict__ gu,
+                                                   float* __restrict__ abar) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= R) return;
+  const float* g = gu + r * 2 * h;
+  float* o = abar + r * h;
+  float amax = 0.0f;
+  for (int j = lane; j < h; j += 64) {
+    const float a = silu(g[j]) * g[h + j];
+    o[j] = a;
+    amax = fmaxf(amax, fabsf(a));
+  }
+  amax = max64(amax);
+  const float s = (2.0f * amax) / 255.0f;
+  for (int j = lane; j < h; j += 64) {
+    const float a = o[j];
+    o[j] = s == 0.0f ? 0.0f : s * fminf(fmaxf(rintf(a / s), -128.0f), 127.0f);
+  }
+}
+
+// Backward of the activation (one wave per row): the quantiser's pass flag
+// from a recomputed bit for bit, then
+//   da = dabar * pass, dg = da u sig(g) (1 + g (1 - sig(g))), du = da g sig(g).
+__global__ __launch_bounds__(256) void k_train_act_bwd(int64_t R, int h, const float* __restrict__ gu,
+                                                       const float* __restrict__ dabar,
+                                                       float* __restrict__ dgu) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= R) return;
+  const float* g = gu + r * 2 * h;
+  float amax = 0.0f;
+  for (int j = lane; j < h; j += 64) amax = fmaxf(amax, fabsf(silu(g[j]) * g[h + j]));
+  amax = max64(amax);
+  const float s = (2.0f * amax) / 255.0f;
+  for (int j = lane; j < h; j += 64) {
+    const float gj = g[j], uj = g[h + j];
+    const float a = silu(gj) * uj;
+    bool pass = true;
+    if (s != 0.0f) {
+      const float q = rintf(a / s);
+      pass = q >= -128.0f && q <= 127.0f;
+    }
+    const float da = pass ? dabar[r * h + j] : 0.0f;
+    const float sig = 1.0f / (1.0f + expf(-gj));
+    dgu[r * 2 * h + j] = da * uj * sig * (1.0f + gj * (1.0f - sig));
+    dgu[r * 2 * h + h + j] = da * gj * sig;
+  }
+}
+
+// dst[r] = scale[perm[r]] * src[perm[r] / k] (scale NULL: 1), zero rows for
+// negative entries; one wave per row.
+__global__ __launch_bounds__(256) void k_gather_rows(int64_t R, int64_t q4, int k,
+                                                     const int32_t* __restrict__ perm,
+                                                     const float* __restrict__ scale,
+                                                     const float4* __restrict__ src,
+                                                     float4* __restrict__ dst) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= R) return;
+  const int32_t a = perm[r];
+  const float w = a < 0 ? 0.0f : (scale ? scale[a] : 1.0f);
+  const int64_t t = a < 0 ? 0 : a / k;
+  for (int64_t c = lane; c < q4; c += 64) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (a >= 0) {
+      v = src[t * q4 + c];
+      v.x *= w;
+      v.y *= w;
+      v.z *= w;
+      v.w *= w;
+    }
+    dst[r * q4 + c] = v;
+  }
+}
+
+template <bool kAK, bool kBK_, bool kGroupK>
+hipError_t gemm(int E, int64_t R, int64_t M, int64_t N, int64_t K, const int32_t* off, const float* A,
+                int64_t lda, const float* B, int64_t ldb, int64_t strideB, float* C, int64_t ldc,
+                int64_t strideC, hipStream_t st) {
+  dim3 grid;
+  if (kGroupK)
+    grid = dim3((unsigned)(((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN)), (unsigned)E);
+  else
+    grid = dim3((unsigned)((R + kBM - 1) / kBM + E), (unsigned)((N + kBN - 1) / kBN));
+  hipLaunchKernelGGL((k_gemm_f32<kAK, kBK_, kGroupK>), grid, dim3(256), 0, st, E, M, N, K, off, A, lda,
+                     B, ldb, strideB, C, ldc, strideC);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gather_rows(int64_t R, int64_t d, int k, const int32_t* perm, const float* scale,
+                              const float* src, float* dst, hipStream_t st) {
+  hipLaunchKernelGGL(k_gather_rows, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, st, R, d / 4, k, perm,
+                     scale, reinterpret_cast<const float4*>(src), reinterpret_cast<float4*>(dst));
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_train_forward(int E, int d, int h, int64_t R, const int32_t* off,
+                                       const float* xs, const float* wgu, const float* wd, float* gu,
+                                       float* abar, float* f, hipStream_t st) {
+  hipError_t e = gemm<true, true, false>(E, R, R, 2 * h, d, off, xs, d, wgu, d, (int64_t)2 * h * d, gu,
+                                         2 * h, 0, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_train_act, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, st, R, h, gu, abar);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return gemm<true, true, false>(E, R, R, d, h, off, abar, h, wd, h, (int64_t)d * h, f, d, 0, st);
+}
+
+hipError_t launch_expert_backward(int E, int d, int h, int64_t R, const int32_t* off, const float* xs,
+                                  const float* wgu, const float* wd, const float* gu,
+                                  const float* abar, const float* df, float* dxs, float* dwgu,
+                                  float* dwd, float* dabar, float* dgu, hipStream_t st) {
+  // dabar = df wd_e  [R][h]
+  hipError_t e = gemm<true, false, false>(E, R, R, h, d, off, df, d, wd, h, (int64_t)d * h, dabar, h, 0,
+                                          st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_train_act_bwd, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, st, R, h, gu, dabar,
+                     dgu);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // dxs = dgu wgu_e  [R][d]
+  if ((e = gemm<true, false, false>(E, R, R, d, 2 * h, off, dgu, 2 * h, wgu, d, (int64_t)2 * h * d, dxs,
+                                    d, 0, st)) != hipSuccess)
+    return e;
+  // dwd_e = df^T abar over the expert's rows  [d][h]
+  if ((e = gemm<false, false, true>(E, R, d, h, 0, off, df, d, abar, h, 0, dwd, h, (int64_t)d * h,
+                                    st)) != hipSuccess)
+    return e;
+  // dwgu_e = dgu^T xs  [2h][d]
+  return gemm<false, false, true>(E, R, 2 * h, d, 0, off, dgu, 2 * h, xs, d, 0, dwgu, d,
+                                  (int64_t)2 * h * d, st);
+}
+
+}  // namespace mm

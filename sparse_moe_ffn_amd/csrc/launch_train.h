@@ -23,3 +23,22 @@ hipError_t launch_fake_quant(int64_t rows, int64_t cols, int bits, bool row_grou
                              float* xbar, const float* gout, float* gin, hipStream_t st);
 
 }  // namespace mm
+
+namespace mm {
+
+// dst[r] = scale[perm[r]] * src[perm[r] / k] (d a multiple of 4).
+hipError_t launch_gather_rows(int64_t R, int64_t d, int k, const int32_t* perm, const float* scale,
+                              const float* src, float* dst, hipStream_t st);
+
+// QAT forward of the experts over expert-ordered rows (d, h multiples of 16).
+hipError_t launch_expert_train_forward(int E, int d, int h, int64_t R, const int32_t* off,
+                                       const float* xs, const float* wgu, const float* wd, float* gu,
+                                       float* abar, float* f, hipStream_t st);
+
+// Its backward; dabar [R][h] and dgu [R][2h] are scratch.
+hipError_t launch_expert_backward(int E, int d, int h, int64_t R, const int32_t* off, const float* xs,
+                                  const float* wgu, const float* wd, const float* gu,
+                                  const float* abar, const float* df, float* dxs, float* dwgu,
+                                  float* dwd, float* dabar, float* dgu, hipStream_t st);
+
+}  // namespace mm

@@ -247,3 +247,17 @@ def test_training_side_checks(lib):
     assert fq(4, 64, 4, 32, FAKE, FAKE, FAKE, None, None) == B.MM_ERR_NULL
     assert fq(4, 64, 4, 32, None, FAKE, None, None, None) == B.MM_ERR_NULL
     assert fq(0, 64, 4, 32, None, None, None, None, None) == B.MM_OK
+
+
+def test_expert_training_checks(lib):
+    f, b = lib.mm_expert_train_forward_f32, lib.mm_expert_backward_f32
+    for E, d, h in [(0, 64, 32), (3, 60, 32), (3, 64, 24), (5000, 64, 32)]:
+        assert f(E, d, h, 10, *(FAKE,) * 7, None) == B.MM_ERR_SHAPE
+    assert f(3, 64, 32, 0, *(None,) * 7, None) == B.MM_OK
+    assert f(3, 64, 32, 10, None, *(FAKE,) * 6, None) == B.MM_ERR_NULL
+    ws = lib.mm_expert_backward_workspace_bytes(10, 32)
+    assert ws == 10 * 3 * 32 * 4
+    assert b(3, 64, 32, 10, *(FAKE,) * 11, ws - 4, None) == B.MM_ERR_WORKSPACE
+    assert b(3, 64, 32, 10, *(FAKE,) * 10, None, ws, None) == B.MM_ERR_NULL
+    assert lib.mm_gather_rows(4, 6, 2, FAKE, None, FAKE, FAKE, None) == B.MM_ERR_SHAPE
+    assert lib.mm_gather_rows(4, 8, 2, None, None, FAKE, FAKE, None) == B.MM_ERR_NULL

@@ -358,6 +358,113 @@ def test_fake_quant_bitexact(rows, cols, bits, group):
     assert torch.equal(gi2, gi)
 
 
+def _expert_rows_case(g, E, d, h, counts):
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offs[-1])
+    xs = (g.standard_normal((R, d))).astype(np.float32)
+    wgu = (g.standard_normal((E, 2 * h, d)) * (1.0 / np.sqrt(d))).astype(np.float32)
+    wd = (g.standard_normal((E, d, h)) * (1.0 / np.sqrt(h))).astype(np.float32)
+    return offs, xs, wgu, wd
+
+
+def _row_rel(got, ref):
+    ref = ref.reshape(-1, ref.shape[-1]).astype(np.float64)
+    got = got.reshape(ref.shape).astype(np.float64)
+    den = np.maximum(np.abs(ref).max(1), 1e-30)
+    return np.abs(got - ref).max(1) / den
+
+
+EXPERT_SHAPES = [(3, 64, 32, [5, 0, 70]), (60, 768, 384, None), (4, 128, 1536 // 4, [0, 1, 129, 64])]
+
+
+@pytest.mark.parametrize("E,d,h,counts", EXPERT_SHAPES)
+def test_expert_train_forward(E, d, h, counts):
+    """mm_expert_train_forward_f32 against the oracle: gate/up and down
+    products within 1e-4 per row; INT8 activation codes equal except where
+    FP32 and double products straddle a rounding boundary (one step, rare;
+    rows holding such a code get 5e-3 on f)."""
+    g = rng(E + d + h)
+    if counts is None:
+        counts = list(np.bincount(_skewed_ids(g, 150, E, 4).ravel(), minlength=E))
+    offs, xs, wgu, wd = _expert_rows_case(g, E, d, h, counts)
+    R = xs.shape[0]
+    gu = torch.empty((R, 2 * h), device=DEV)
+    ab = torch.empty((R, h), device=DEV)
+    f = torch.empty((R, d), device=DEV)
+    B.expert_train_forward_f32(E, d, h, R, dev(offs), dev(xs), dev(wgu), dev(wd), gu, ab, f)
+    rgu, rab, rf = oracle.expert_train_forward(offs, xs, wgu, wd)
+    assert _row_rel(np_(gu), rgu).max() <= 1e-4
+    gab = np_(ab)
+    s = (2.0 * np.abs(rab).max(1) / 255.0).astype(np.float32)  # an upper bound of each row's step
+    # the row scale follows the row's FP32 products, so s * code may differ
+    # in its last bits everywhere; a code that differs moves by a whole step
+    rowmax = np.maximum(np.abs(rab).max(1, keepdims=True), 1e-30)
+    diff = np.abs(gab.astype(np.float64) - rab) > 1e-4 * rowmax
+    assert diff.sum() <= max(2, diff.size // 1000)
+    assert np.all(np.abs(gab - rab)[diff] <= 1.01 * np.repeat(np.maximum(s, 1e-30)[:, None], h, 1)[diff])
+    flip_rows = diff.any(1)
+    err = _row_rel(np_(f), rf)
+    assert err[~flip_rows].max(initial=0) <= 1e-4
+    # a flipped code j of row r moves f[r][c] by one step s_r times |wd_e[c][j]|
+    gf = np_(f).astype(np.float64)
+    expert_of = np.repeat(np.arange(E), counts)
+    for r in np.flatnonzero(flip_rows):
+        js = np.flatnonzero(diff[r])
+        bound = 1e-4 * np.abs(rf[r]).max() + 1.01 * s[r] * np.abs(wd[expert_of[r]][:, js]).sum(1)
+        assert np.all(np.abs(gf[r] - rf[r]) <= bound), r
+
+
+@pytest.mark.parametrize("E,d,h,counts", EXPERT_SHAPES)
+def test_expert_backward(E, d, h, counts):
+    """mm_expert_backward_f32 against the oracle's double backward on the
+    oracle's own forward state: dxs per row and every expert's weight
+    gradients within 1e-4 (of the row / matrix maximum); zero for experts
+    without rows."""
+    g = rng(E * 3 + d + h)
+    if counts is None:
+        counts = list(np.bincount(_skewed_ids(g, 150, E, 4).ravel(), minlength=E))
+    offs, xs, wgu, wd = _expert_rows_case(g, E, d, h, counts)
+    R = xs.shape[0]
+    rgu, rab, _ = oracle.expert_train_forward(offs, xs, wgu, wd)
+    df = g.standard_normal((R, d)).astype(np.float32)
+    rdx, rdwgu, rdwd = oracle.expert_backward(offs, xs, wgu, wd, rgu, df)
+    dx = torch.empty((R, d), device=DEV)
+    dwgu = torch.full((E, 2 * h, d), 7.0, device=DEV)
+    dwd = torch.full((E, d, h), 7.0, device=DEV)
+    wsb = B.expert_backward_workspace_bytes(R, h)
+    ws = torch.empty((wsb,), dtype=torch.uint8, device=DEV)
+    B.expert_backward_f32(E, d, h, R, dev(offs), dev(xs), dev(wgu), dev(wd), dev(rgu), dev(rab),
+                          dev(df), dx, dwgu, dwd, ws, wsb)
+    assert _row_rel(np_(dx), rdx).max() <= 1e-4
+    gw, gd = np_(dwgu), np_(dwd)
+    for e in range(E):
+        if counts[e] == 0:
+            assert np.all(gw[e] == 0) and np.all(gd[e] == 0)
+            continue
+        for got, ref in ((gw[e], rdwgu[e]), (gd[e], rdwd[e])):
+            assert np.abs(got - ref).max() <= 1e-4 * np.abs(ref).max(), e
+
+
+def test_gather_rows_bitexact():
+    """mm_gather_rows: dst[r] = scale[perm[r]] * src[perm[r] // k] (FP32
+    product), zero rows for -1."""
+    g = rng(60)
+    T, k, d = 37, 4, 768
+    src = g.standard_normal((T, d)).astype(np.float32)
+    w = g.random(T * k).astype(np.float32)
+    perm = g.permutation(T * k).astype(np.int32)
+    perm[5] = -1
+    dst = torch.empty((T * k, d), device=DEV)
+    B.gather_rows(T * k, d, k, dev(perm), dev(w), dev(src), dst)
+    want = src[np.maximum(perm, 0) // k] * w[np.maximum(perm, 0)][:, None]
+    want[5] = 0.0
+    assert np.array_equal(np_(dst), want.astype(np.float32))
+    B.gather_rows(T * k, d, k, dev(perm), None, dev(src), dst)
+    want = src[np.maximum(perm, 0) // k].copy()
+    want[5] = 0.0
+    assert np.array_equal(np_(dst), want)
+
+
 # ------------------------------------------------------------ expert stages
 def _sorted_reference(layer, w, lw, x):
     """Oracle per-sorted-row gate/up and down results for the layer's routing."""
