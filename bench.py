@@ -46,11 +46,12 @@ def parse():
                          "calls: the seven calls with the activation quantiser and shared expert on "
                          "a second stream; auto: fused (measured faster on every workload)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
-    ap.add_argument("--op", choices=("layer", "attn_decode", "linear"), default="layer",
+    ap.add_argument("--op", choices=("layer", "attn_decode", "linear", "train_step"), default="layer",
                     help="layer: the MoE-FFN layer (default); attn_decode: GQA decode attention "
                          "over an INT8 KV cache (--batch sequences, --context positions, --heads "
                          "query heads, 4 key/value heads); linear: the dense W4A8 projection "
-                         "(--batch rows, --in-features, --out-features)")
+                         "(--batch rows, --in-features, --out-features); train_step: one QAT "
+                         "training step of the S layer's routed experts (--batch tokens)")
     ap.add_argument("--context", type=int, default=8192, help="attn_decode: cached positions per sequence")
     ap.add_argument("--heads", type=int, default=12, help="attn_decode: query heads (S: 12, M: 16, L: 20)")
     ap.add_argument("--in-features", type=int, default=768, help="linear: K")
@@ -181,6 +182,8 @@ def main():
         return bench_attn(args, dev)
     if args.op == "linear":
         return bench_linear(args, dev)
+    if args.op == "train_step":
+        return bench_train(args, dev)
     w = wl.WORKLOADS[args.workload]
     if args.batch is not None:
         w = w.with_(T=args.batch)
@@ -620,6 +623,119 @@ def bench_linear(args, dev):
         "cpu_baseline": cpu,
     }
     print(json.dumps(out_line), flush=True)
+
+
+def bench_train(args, dev):
+    """One QAT training step of the routed experts of the MobileMoE-S layer
+    (d = 768, 60 experts of h = 384, top-4): balancing-bias update, count
+    sort, drop-and-pad at capacity factor 1.5, eq. (6) fake quantisation of
+    the latent FP32 weights and of the input rows, row gathers, the grouped
+    forward and backward products, and the straight-through weight
+    gradients.  Routing ids and upstream gradients are seeded synthetic."""
+    import numpy as np
+    import torch
+    from sparse_moe_ffn_amd import binding as B
+    T, E, k, d, h = args.batch or 2048, 60, 4, 768, 384
+    Tk = T * k
+    g = np.random.default_rng(777)
+    # mildly uneven loads (expert probability ~ rank^-0.3: about 3 % of the
+    # assignments overflow capacity 1.5), as the balancing bias keeps them
+    p = np.arange(1, E + 1, dtype=np.float64) ** -0.3
+    p = p[g.permutation(E)]
+    p /= p.sum()
+    idx = np.stack([g.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    idx_d = torch.from_numpy(idx).to(dev)
+    w_gate = f32(g.random(Tk))
+    wgu = f32(g.standard_normal((E, 2 * h, d)) / np.sqrt(d))
+    wd = f32(g.standard_normal((E, d, h)) / np.sqrt(h))
+    x = f32(g.standard_normal((T, d)))
+    dy = f32(g.standard_normal((T, d)))
+    bias = torch.zeros((E,), device=dev)
+    C = B.drop_pad_capacity(T, k, E)
+    ds = B.desc(d, E, h, 0, k)
+    off = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    perm = torch.empty((Tk,), dtype=torch.int32, device=dev)
+    inv = torch.empty((Tk,), dtype=torch.int32, device=dev)
+    nb = B.workspace_bytes(ds, T, B.MM_WS_ROUTE)
+    rws = torch.empty((nb,), dtype=torch.uint8, device=dev)
+    buf = torch.empty((E * C,), dtype=torch.int32, device=dev)
+    offc = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    permc = torch.empty((Tk,), dtype=torch.int32, device=dev)
+    invc = torch.empty((Tk,), dtype=torch.int32, device=dev)
+    wgu_b, wd_b, x_b = torch.empty_like(wgu), torch.empty_like(wd), torch.empty_like(x)
+    xs = torch.empty((Tk, d), device=dev)
+    dfs = torch.empty((Tk, d), device=dev)
+    gu = torch.empty((Tk, 2 * h), device=dev)
+    ab = torch.empty((Tk, h), device=dev)
+    fo = torch.empty((Tk, d), device=dev)
+    dxs = torch.empty((Tk, d), device=dev)
+    dwgu, dwd = torch.empty_like(wgu), torch.empty_like(wd)
+    gwgu, gwd = torch.empty_like(wgu), torch.empty_like(wd)
+    wsb = B.expert_backward_workspace_bytes(Tk, h)
+    ws = torch.empty((wsb,), dtype=torch.uint8, device=dev)
+
+    calls = {
+        "bias_update": lambda: B.bias_update(T, E, k, idx_d, 1e-3, bias),
+        "route": lambda: B.route_permute(ds, T, idx_d, off, perm, inv, rws, nb),
+        "drop_pad": lambda: B.drop_pad(T, E, k, C, idx_d, off, perm, inv, buf, offc, permc, invc),
+        "fake_quant_w": lambda: (B.fake_quant(E * 2 * h, d, 4, 32, wgu, wgu_b),
+                                 B.fake_quant(E * d, h, 4, 32, wd, wd_b)),
+        "fake_quant_x": lambda: B.fake_quant(T, d, 8, d, x, x_b),
+        "gather": lambda: (B.gather_rows(Tk, d, k, permc, None, x_b, xs),
+                           B.gather_rows(Tk, d, k, permc, w_gate, dy, dfs)),
+        "forward": lambda: B.expert_train_forward_f32(E, d, h, Tk, offc, xs, wgu_b, wd_b, gu, ab, fo),
+        "backward": lambda: B.expert_backward_f32(E, d, h, Tk, offc, xs, wgu_b, wd_b, gu, ab, dfs, dxs,
+                                                  dwgu, dwd, ws, wsb),
+        "ste_w": lambda: (B.fake_quant(E * 2 * h, d, 4, 32, wgu, None, dwgu, gwgu),
+                          B.fake_quant(E * d, h, 4, 32, wd, None, dwd, gwd)),
+    }
+
+    def step(_i=0):
+        for c in calls.values():
+            c()
+
+    ms = _time_graphs(step, args.warmup, args.steps)
+    kept = int(offc[E].item())
+    per_call = {}
+    for name, c in calls.items():
+        per_call[name] = round(1e3 * _time_graphs(lambda _i, c=c: c(), 1, 10), 3)
+    flops_fwd = 6.0 * kept * h * d
+    flops_bwd = 12.0 * kept * h * d
+    bw_tf = flops_bwd / (per_call["backward"] * 1e-6) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        # sample: the first expert's kept rows, forward and backward
+        offs_h = offc.cpu().numpy()
+        n_rows = int(offs_h[1])
+        o = offs_h[:2].copy()
+        xs_h, wg_h, wd_h = xs[:n_rows].cpu().numpy(), wgu_b[:1].cpu().numpy(), wd_b[:1].cpu().numpy()
+        t1 = time.time()
+        gu_o, _, _ = oracle.expert_train_forward(o, xs_h, wg_h, wd_h)
+        oracle.expert_backward(o, xs_h, wg_h, wd_h, gu_o, dfs[:n_rows].cpu().numpy())
+        dt = time.time() - t1
+        cpu = {"value": round(n_rows / k / dt, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"expert 0 ({n_rows} kept rows = {n_rows / k:.0f} token equivalents) forward + "
+                         f"backward, oracle.expert_train_forward + expert_backward (double, one thread), "
+                         f"{dt:.1f}s"}
+    out = {
+        "metric": "QAT training step of the routed experts (forward + backward, drop-and-pad 1.5): tokens/s",
+        "value": round(T / (ms * 1e-3), 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32 (fake-quantised operands)",
+        "data": "synthetic",
+        "config": {"workload": "s_train_experts", "tokens": T, "d_model": d, "experts": E, "top_k": k,
+                   "hidden": h, "capacity": C, "kept_rows": kept, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(bw_tf, 3), "peak": FP32_VALU_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(bw_tf / FP32_VALU_PEAK_TFLOPS, 5), "traffic": None,
+                     "kernel": "k_gemm_f32 x4 + k_train_act_bwd (one mm_expert_backward_f32 call)",
+                     "algorithmic_flops_per_launch": flops_bwd, "launch_us": per_call["backward"]},
+        "cpu_baseline": cpu,
+        "per_call_us": per_call,
+        "forward_tflops": round(flops_fwd / (per_call["forward"] * 1e-6) / 1e12, 3),
+    }
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":
