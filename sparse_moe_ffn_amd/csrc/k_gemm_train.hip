@@ -11,8 +11,7 @@
 // C and multiplies them by its own B (B + e * strideB); K is fixed.
 // Grouped by the reduction (kGroupK): group e sums k over [off[e], off[e+1])
 // into its own C (C + e * strideC); M and N are fixed.
-// Workgroup tile 64 x 64, four waves of 32 x 32, K slices of 16 staged
-// through LDS (k-major rows of 64 + 4 floats), the next slice's loads issued
+// K slices of 16 are staged through LDS, the next slice's loads issued
 // before the current slice's matrix instructions.
 #include "common.h"
 #include "launch_train.h"
@@ -22,19 +21,26 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 64, kBN = 64, kBK = 16, kLd = 68;
+constexpr int kBK = 16;
 
-template <bool kAK, bool kBK_, bool kGroupK>
+// Workgroup tile (32 kWM kTM) x (32 (4 / kWM) kTN): four waves in a kWM x
+// (4 / kWM) grid, each holding kTM x kTN blocks of 32 x 32 accumulators.  Two LDS buffers of K
+// slices (k-major rows of the tile width + 4 floats): slice i + 1 is stored
+// while slice i is multiplied, one barrier per slice.
+template <bool kAK, bool kBK_, bool kGroupK, int kWM, int kTM, int kTN>
 __global__ __launch_bounds__(256) void k_gemm_f32(int E, int64_t M, int64_t N, int64_t K,
                                                   const int32_t* __restrict__ off,
                                                   const float* __restrict__ A, int64_t lda,
                                                   const float* __restrict__ B, int64_t ldb,
                                                   int64_t strideB, float* __restrict__ C,
                                                   int64_t ldc, int64_t strideC) {
-  __shared__ float sA[kBK][kLd];
-  __shared__ float sB[kBK][kLd];
+  constexpr int kWN = 4 / kWM;
+  constexpr int kBM = 32 * kWM * kTM, kBN = 32 * kWN * kTN, kLdA = kBM + 4, kLdB = kBN + 4;
+  constexpr int kNA = (kBM * 4 + 255) / 256, kNB = (kBN * 4 + 255) / 256;  // float4 per thread
+  __shared__ float sA[2][kBK][kLdA];
+  __shared__ float sB[2][kBK][kLdB];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % kWM, wn = wave / kWM;
   int e;
   int64_t m0, mEnd, n0, k0, kEnd;
   if constexpr (kGroupK) {
@@ -47,7 +53,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(int E, int64_t M, int64_t N, i
     kEnd = off[e + 1];
     C += (int64_t)e * strideC;
   } else {
-    // find this workgroup's group and row tile: groups hold ceil(rows / 64) tiles each
+    // find this workgroup's group and row tile: groups hold ceil(rows / kBM) tiles each
     int64_t bx = blockIdx.x;
     e = -1;
     for (int g = 0; g < E; ++g) {
@@ -67,71 +73,115 @@ __global__ __launch_bounds__(256) void k_gemm_f32(int E, int64_t M, int64_t N, i
     B += (int64_t)e * strideB;
   }
 
-  // this thread's share of a K slice: one float4 of A and one of B
-  float4 ra, rb;
+  // this thread's share of a K slice: kNA float4 of A and kNB of B
+  float4 ra[kNA], rb[kNB];
   auto load = [&](int64_t k) {
-    if constexpr (kAK) {
-      const int64_t m = m0 + (t >> 2), kk = k + (t & 3) * 4;
-      ra = m < mEnd ? *reinterpret_cast<const float4*>(A + m * lda + kk) : make_float4(0.f, 0.f, 0.f, 0.f);
-    } else {
-      const int64_t kk = k + (t >> 4), m = m0 + (t & 15) * 4;
-      ra = (kk < kEnd && m < mEnd) ? *reinterpret_cast<const float4*>(A + kk * lda + m)
-                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < kNA; ++i) {
+      const int u = t + 256 * i;
+      if (u >= kBM * 4) break;
+      if constexpr (kAK) {
+        const int64_t m = m0 + (u >> 2), kk = k + (u & 3) * 4;
+        ra[i] = m < mEnd ? *reinterpret_cast<const float4*>(A + m * lda + kk)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+      } else {
+        const int64_t kk = k + u / (kBM / 4), m = m0 + (u % (kBM / 4)) * 4;
+        ra[i] = (kk < kEnd && m < mEnd) ? *reinterpret_cast<const float4*>(A + kk * lda + m)
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
-    if constexpr (kBK_) {
-      const int64_t n = n0 + (t >> 2), kk = k + (t & 3) * 4;
-      rb = n < N ? *reinterpret_cast<const float4*>(B + n * ldb + kk) : make_float4(0.f, 0.f, 0.f, 0.f);
-    } else {
-      const int64_t kk = k + (t >> 4), n = n0 + (t & 15) * 4;
-      rb = (kk < kEnd && n < N) ? *reinterpret_cast<const float4*>(B + kk * ldb + n)
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < kNB; ++i) {
+      const int u = t + 256 * i;
+      if (u >= kBN * 4) break;
+      if constexpr (kBK_) {
+        const int64_t n = n0 + (u >> 2), kk = k + (u & 3) * 4;
+        rb[i] = n < N ? *reinterpret_cast<const float4*>(B + n * ldb + kk)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+      } else {
+        const int64_t kk = k + u / (kBN / 4), n = n0 + (u % (kBN / 4)) * 4;
+        rb[i] = (kk < kEnd && n < N) ? *reinterpret_cast<const float4*>(B + kk * ldb + n)
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
   };
-  auto store = [&]() {
-    if constexpr (kAK) {
-      const int mi = t >> 2, k4 = (t & 3) * 4;
-      sA[k4][mi] = ra.x;
-      sA[k4 + 1][mi] = ra.y;
-      sA[k4 + 2][mi] = ra.z;
-      sA[k4 + 3][mi] = ra.w;
-    } else {
-      *reinterpret_cast<float4*>(&sA[t >> 4][(t & 15) * 4]) = ra;
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kNA; ++i) {
+      const int u = t + 256 * i;
+      if (u >= kBM * 4) break;
+      if constexpr (kAK) {
+        const int mi = u >> 2, k4 = (u & 3) * 4;
+        sA[buf][k4][mi] = ra[i].x;
+        sA[buf][k4 + 1][mi] = ra[i].y;
+        sA[buf][k4 + 2][mi] = ra[i].z;
+        sA[buf][k4 + 3][mi] = ra[i].w;
+      } else {
+        *reinterpret_cast<float4*>(&sA[buf][u / (kBM / 4)][(u % (kBM / 4)) * 4]) = ra[i];
+      }
     }
-    if constexpr (kBK_) {
-      const int ni = t >> 2, k4 = (t & 3) * 4;
-      sB[k4][ni] = rb.x;
-      sB[k4 + 1][ni] = rb.y;
-      sB[k4 + 2][ni] = rb.z;
-      sB[k4 + 3][ni] = rb.w;
-    } else {
-      *reinterpret_cast<float4*>(&sB[t >> 4][(t & 15) * 4]) = rb;
+#pragma unroll
+    for (int i = 0; i < kNB; ++i) {
+      const int u = t + 256 * i;
+      if (u >= kBN * 4) break;
+      if constexpr (kBK_) {
+        const int ni = u >> 2, k4 = (u & 3) * 4;
+        sB[buf][k4][ni] = rb[i].x;
+        sB[buf][k4 + 1][ni] = rb[i].y;
+        sB[buf][k4 + 2][ni] = rb[i].z;
+        sB[buf][k4 + 3][ni] = rb[i].w;
+      } else {
+        *reinterpret_cast<float4*>(&sB[buf][u / (kBN / 4)][(u % (kBN / 4)) * 4]) = rb[i];
+      }
     }
   };
 
-  f32x16 acc;
+  f32x16 acc[kTM][kTN];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kTN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   const int half = lane >> 5, li = lane & 31;
-  if (k0 < kEnd) load(k0);
+  if (k0 < kEnd) {
+    load(k0);
+    store(0);
+  }
+  __syncthreads();
+  int cur = 0;
   for (int64_t k = k0; k < kEnd; k += kBK) {
-    __syncthreads();  // the previous slice's reads are done
-    store();
-    __syncthreads();
-    if (k + kBK < kEnd) load(k + kBK);
+    const bool more = k + kBK < kEnd;
+    if (more) load(k + kBK);
 #pragma unroll
     for (int kk = 0; kk < kBK; kk += 2) {
-      const float a = sA[kk + half][wm * 32 + li];
-      const float b = sB[kk + half][wn * 32 + li];
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
-    }
-  }
-  // acc[r] holds row 8 (r / 4) + 4 half + r % 4, column li of the wave's 32 x 32
-  const int64_t col = n0 + wn * 32 + li;
+      float a[kTM], b[kTN];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int64_t row = m0 + wm * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-    if (row < mEnd && col < N) C[row * ldc + col] = acc[r];
+      for (int i = 0; i < kTM; ++i) a[i] = sA[cur][kk + half][wm * 32 * kTM + 32 * i + li];
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) b[j] = sB[cur][kk + half][wn * 32 * kTN + 32 * j + li];
+#pragma unroll
+      for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) store(cur ^ 1);  // its last readers finished before the previous barrier
+    __syncthreads();
+    cur ^= 1;
   }
+  // acc[i][j][r] holds row 8 (r / 4) + 4 half + r % 4, column li of block (i, j)
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+      const int64_t col = n0 + wn * 32 * kTN + 32 * j + li;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm * 32 * kTM + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (row < mEnd && col < N) C[row * ldc + col] = acc[i][j][r];
+      }
+    }
 }
 
 // Forward activation of one expert row (one wave per row): a = silu(g) * u
@@ -213,17 +263,21 @@ __global__ __launch_bounds__(256) void k_gather_rows(int64_t R, int64_t q4, int 
   }
 }
 
+// 64 x 64 tiles for every form (measured on the S expert shapes: as fast
+// as or faster than 32 x 128, 64 x 128 and 128 x 128).
 template <bool kAK, bool kBK_, bool kGroupK>
 hipError_t gemm(int E, int64_t R, int64_t M, int64_t N, int64_t K, const int32_t* off, const float* A,
                 int64_t lda, const float* B, int64_t ldb, int64_t strideB, float* C, int64_t ldc,
                 int64_t strideC, hipStream_t st) {
+  constexpr int kWM = 2, kTM = 1, kTN = 1;
+  constexpr int kBM = 32 * kWM * kTM, kBN = 32 * (4 / kWM) * kTN;
   dim3 grid;
   if (kGroupK)
     grid = dim3((unsigned)(((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN)), (unsigned)E);
   else
     grid = dim3((unsigned)((R + kBM - 1) / kBM + E), (unsigned)((N + kBN - 1) / kBN));
-  hipLaunchKernelGGL((k_gemm_f32<kAK, kBK_, kGroupK>), grid, dim3(256), 0, st, E, M, N, K, off, A, lda,
-                     B, ldb, strideB, C, ldc, strideC);
+  hipLaunchKernelGGL((k_gemm_f32<kAK, kBK_, kGroupK, kWM, kTM, kTN>), grid, dim3(256), 0, st, E, M, N, K,
+                     off, A, lda, B, ldb, strideB, C, ldc, strideC);
   return hipGetLastError();
 }
 
