@@ -445,6 +445,109 @@ def test_expert_backward(E, d, h, counts):
             assert np.abs(got - ref).max() <= 1e-4 * np.abs(ref).max(), e
 
 
+def test_expert_training_full_size_sampled():
+    """The S training step at T = 2048 in the launch configuration of
+    bench.py --op train_step (routing with expert probability ~ rank^-0.3,
+    capacity 1.5, compacted rows bounded by T*k): drop-and-pad exact on the
+    whole batch; forward and backward of three whole experts (rows and weight
+    gradients) against the oracle."""
+    T, E, k, d, h = 2048, 60, 4, 768, 384
+    g = rng(2048)
+    p = np.arange(1, E + 1, dtype=np.float64) ** -0.3
+    p = p[g.permutation(E)]
+    p /= p.sum()
+    idx = np.stack([g.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    ds = B.desc(d, E, h, 0, k)
+    off = torch.empty((E + 1,), dtype=torch.int32, device=DEV)
+    perm = torch.empty((T * k,), dtype=torch.int32, device=DEV)
+    inv = torch.empty((T * k,), dtype=torch.int32, device=DEV)
+    nb = B.workspace_bytes(ds, T, B.MM_WS_ROUTE)
+    rws = torch.empty((nb,), dtype=torch.uint8, device=DEV)
+    idx_d = dev(idx)
+    B.route_permute(ds, T, idx_d, off, perm, inv, rws, nb)
+    C = B.drop_pad_capacity(T, k, E)
+    buf = torch.empty((E * C,), dtype=torch.int32, device=DEV)
+    offc = torch.empty((E + 1,), dtype=torch.int32, device=DEV)
+    permc = torch.empty((T * k,), dtype=torch.int32, device=DEV)
+    invc = torch.empty((T * k,), dtype=torch.int32, device=DEV)
+    B.drop_pad(T, E, k, C, idx_d, off, perm, inv, buf, offc, permc, invc)
+    rb, ro, rp, ri = oracle.drop_pad(idx, E, C)
+    assert np.array_equal(np_(offc), ro) and np.array_equal(np_(permc), rp)
+    assert np.array_equal(np_(invc), ri) and np.array_equal(np_(buf), rb.ravel())
+    Tk = T * k
+    x = g.standard_normal((T, d)).astype(np.float32)
+    wgu = (g.standard_normal((E, 2 * h, d)) / np.sqrt(d)).astype(np.float32)
+    wd = (g.standard_normal((E, d, h)) / np.sqrt(h)).astype(np.float32)
+    xs = torch.empty((Tk, d), device=DEV)
+    B.gather_rows(Tk, d, k, permc, None, dev(x), xs)
+    gu = torch.empty((Tk, 2 * h), device=DEV)
+    ab = torch.empty((Tk, h), device=DEV)
+    f = torch.empty((Tk, d), device=DEV)
+    B.expert_train_forward_f32(E, d, h, Tk, offc, xs, dev(wgu), dev(wd), gu, ab, f)
+    df = g.standard_normal((Tk, d)).astype(np.float32)
+    dxs = torch.empty((Tk, d), device=DEV)
+    dwgu = torch.empty((E, 2 * h, d), device=DEV)
+    dwd = torch.empty((E, d, h), device=DEV)
+    wsb = B.expert_backward_workspace_bytes(Tk, h)
+    ws = torch.empty((wsb,), dtype=torch.uint8, device=DEV)
+    # the backward runs on the oracle's forward state for the sampled experts
+    ref_state = {}
+    xs_h = x[np.maximum(rp, 0) // k]
+    for e in (0, 17, 59):
+        r0, r1 = int(ro[e]), int(ro[e + 1])
+        o = np.array([0, r1 - r0], np.int32)
+        ref_state[e] = (r0, r1, o) + oracle.expert_train_forward(o, xs_h[r0:r1], wgu[e:e + 1], wd[e:e + 1])
+    gu_in = np_(gu).copy()
+    ab_in = np_(ab).copy()
+    for e, (r0, r1, o, rgu, rab, rf) in ref_state.items():
+        assert _row_rel(gu_in[r0:r1], rgu).max() <= 1e-4
+        gu_in[r0:r1], ab_in[r0:r1] = rgu, rab
+        ferr = _row_rel(np_(f)[r0:r1], rf)
+        diff = np.abs(np_(ab)[r0:r1].astype(np.float64) - rab) > 1e-4 * np.maximum(
+            np.abs(rab).max(1, keepdims=True), 1e-30)
+        assert diff.sum() <= max(2, diff.size // 1000)
+        flips = diff.any(1)
+        assert ferr[~flips].max(initial=0) <= 1e-4
+        step = (2.0 * np.abs(rab).max(1) / 255.0).astype(np.float32)
+        for r in np.flatnonzero(flips):
+            js = np.flatnonzero(diff[r])
+            bound = 1e-4 * np.abs(rf[r]).max() + 1.01 * step[r] * np.abs(wd[e][:, js]).sum(1)
+            assert np.all(np.abs(np_(f)[r0 + r].astype(np.float64) - rf[r]) <= bound)
+    B.expert_backward_f32(E, d, h, Tk, offc, xs, dev(wgu), dev(wd), dev(gu_in), dev(ab_in), dev(df),
+                          dxs, dwgu, dwd, ws, wsb)
+    gdx, gw, gd = np_(dxs), np_(dwgu), np_(dwd)
+    for e, (r0, r1, o, rgu, rab, rf) in ref_state.items():
+        rdx, rdw, rdd = oracle.expert_backward(o, xs_h[r0:r1], wgu[e:e + 1], wd[e:e + 1], rgu, df[r0:r1])
+        assert _row_rel(gdx[r0:r1], rdx).max() <= 1e-4
+        assert np.abs(gw[e] - rdw[0]).max() <= 1e-4 * np.abs(rdw[0]).max()
+        assert np.abs(gd[e] - rdd[0]).max() <= 1e-4 * np.abs(rdd[0]).max()
+
+
+def test_attn_decode_full_size_sampled():
+    """Decode attention in the launch configuration of bench.py --op
+    attn_decode (32 sequences, 12 query heads over 4 key/value heads, 8192
+    positions, workspace for the whole batch), checked on three sequences."""
+    Bn, nh, nkv, T = 32, 12, 4, 8192
+    g = rng(8192)
+    kc = torch.randint(-127, 128, (Bn, nkv, T, 64), dtype=torch.int8, device=DEV)
+    vc = torch.randint(-127, 128, (Bn, nkv, T, 64), dtype=torch.int8, device=DEV)
+    ks = dev((g.random((Bn, nkv, T)) * 0.04 + 1e-3).astype(np.float32))
+    vs = dev((g.random((Bn, nkv, T)) * 0.04 + 1e-3).astype(np.float32))
+    q = g.standard_normal((Bn, nh, 64)).astype(np.float32)
+    lens = np.full(Bn, T, np.int32)
+    lens[5] = 4097
+    wsb = B.attn_workspace_bytes(Bn, nkv, T)
+    ws = torch.empty((wsb,), dtype=torch.uint8, device=DEV)
+    out = torch.empty((Bn, nh, 64), device=DEV)
+    B.attn_decode_i8(Bn, nh, nkv, 64, T, T, dev(lens), dev(q), kc, vc, ks, vs, out, ws, wsb)
+    got = np_(out)
+    for b in (0, 5, 31):
+        ref = oracle.attn_decode(q[b:b + 1], np_(kc[b:b + 1]), np_(vc[b:b + 1]), np_(ks[b:b + 1]),
+                                 np_(vs[b:b + 1]), int(lens[b]))[0]
+        err = np.abs(got[b] - ref).max(1) / np.abs(ref).max(1)
+        assert err.max() <= 1e-4, (b, err.max())
+
+
 def test_gather_rows_bitexact():
     """mm_gather_rows: dst[r] = scale[perm[r]] * src[perm[r] // k] (FP32
     product), zero rows for -1."""
