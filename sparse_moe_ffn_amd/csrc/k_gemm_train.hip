@@ -73,35 +73,40 @@ __global__ __launch_bounds__(256) void k_gemm_f32(int E, int64_t M, int64_t N, i
     B += (int64_t)e * strideB;
   }
 
-  // this thread's share of a K slice: kNA float4 of A and kNB of B
+  // this thread's share of a K slice: kNA float4 of A and kNB of B.  The
+  // loads are unconditional from addresses clamped into the operands (out-of-
+  // range elements are zeroed on the way into LDS): a predicated load would
+  // split the code into branches, and the compiler then waits for each load
+  // before issuing the next.
   float4 ra[kNA], rb[kNB];
+  bool va[kNA], vb[kNB];
   auto load = [&](int64_t k) {
 #pragma unroll
     for (int i = 0; i < kNA; ++i) {
       const int u = t + 256 * i;
-      if (u >= kBM * 4) break;
+      if ((kBM * 4) % 256 != 0 && u >= kBM * 4) break;
       if constexpr (kAK) {
         const int64_t m = m0 + (u >> 2), kk = k + (u & 3) * 4;
-        ra[i] = m < mEnd ? *reinterpret_cast<const float4*>(A + m * lda + kk)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
+        va[i] = m < mEnd;
+        ra[i] = *reinterpret_cast<const float4*>(A + min(m, mEnd - 1) * lda + kk);
       } else {
         const int64_t kk = k + u / (kBM / 4), m = m0 + (u % (kBM / 4)) * 4;
-        ra[i] = (kk < kEnd && m < mEnd) ? *reinterpret_cast<const float4*>(A + kk * lda + m)
-                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+        va[i] = kk < kEnd && m < mEnd;
+        ra[i] = *reinterpret_cast<const float4*>(A + min(kk, kEnd - 1) * lda + min(m, mEnd - 4));
       }
     }
 #pragma unroll
     for (int i = 0; i < kNB; ++i) {
       const int u = t + 256 * i;
-      if (u >= kBN * 4) break;
+      if ((kBN * 4) % 256 != 0 && u >= kBN * 4) break;
       if constexpr (kBK_) {
         const int64_t n = n0 + (u >> 2), kk = k + (u & 3) * 4;
-        rb[i] = n < N ? *reinterpret_cast<const float4*>(B + n * ldb + kk)
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
+        vb[i] = n < N;
+        rb[i] = *reinterpret_cast<const float4*>(B + min(n, N - 1) * ldb + kk);
       } else {
         const int64_t kk = k + u / (kBN / 4), n = n0 + (u % (kBN / 4)) * 4;
-        rb[i] = (kk < kEnd && n < N) ? *reinterpret_cast<const float4*>(B + kk * ldb + n)
-                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+        vb[i] = kk < kEnd && n < N;
+        rb[i] = *reinterpret_cast<const float4*>(B + min(kk, kEnd - 1) * ldb + min(n, N - 4));
       }
     }
   };
@@ -109,7 +114,8 @@ __global__ __launch_bounds__(256) void k_gemm_f32(int E, int64_t M, int64_t N, i
 #pragma unroll
     for (int i = 0; i < kNA; ++i) {
       const int u = t + 256 * i;
-      if (u >= kBM * 4) break;
+      if ((kBM * 4) % 256 != 0 && u >= kBM * 4) break;
+      if (!va[i]) ra[i] = make_float4(0.f, 0.f, 0.f, 0.f);
       if constexpr (kAK) {
         const int mi = u >> 2, k4 = (u & 3) * 4;
         sA[buf][k4][mi] = ra[i].x;
@@ -123,7 +129,8 @@ __global__ __launch_bounds__(256) void k_gemm_f32(int E, int64_t M, int64_t N, i
 #pragma unroll
     for (int i = 0; i < kNB; ++i) {
       const int u = t + 256 * i;
-      if (u >= kBN * 4) break;
+      if ((kBN * 4) % 256 != 0 && u >= kBN * 4) break;
+      if (!vb[i]) rb[i] = make_float4(0.f, 0.f, 0.f, 0.f);
       if constexpr (kBK_) {
         const int ni = u >> 2, k4 = (u & 3) * 4;
         sB[buf][k4][ni] = rb[i].x;
