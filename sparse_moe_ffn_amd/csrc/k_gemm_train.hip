@@ -3,8 +3,9 @@
 // section "Quantisation-aware training": weights and activations fake-
 // quantised by eq. (6), gradients passed straight through the rounding).
 //
-// Grouped FP32 products on the FP32 matrix cores (v_mfma_f32_32x32x2_f32:
-// FP32 products, FP32 sums): C[m][n] = sum over k of A(m, k) B(k, n) with
+// Grouped FP32 products on the FP32 matrix cores (v_mfma_f32_16x16x4_f32:
+// FP32 products, FP32 sums; this form issues at close to the chip's FP32
+// matrix rate, the 32 x 32 x 2 form at about 85 % of it): C[m][n] = sum over k of A(m, k) B(k, n) with
 //   A(m, k) = A[m * lda + k]  (kAK)   or  A[k * lda + m]
 //   B(k, n) = B[n * ldb + k]  (kBK)   or  B[k * ldb + n].
 // Grouped by rows (!kGroupK): group e owns rows [off[e], off[e+1]) of A and
@@ -19,14 +20,16 @@
 namespace mm {
 namespace {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBK = 16;
 
 // Workgroup tile (32 kWM kTM) x (32 (4 / kWM) kTN): four waves in a kWM x
-// (4 / kWM) grid, each holding kTM x kTN blocks of 32 x 32 accumulators.  Two LDS buffers of K
-// slices (k-major rows of the tile width + 4 floats): slice i + 1 is stored
-// while slice i is multiplied, one barrier per slice.
+// (4 / kWM) grid, each holding 2 kTM x 2 kTN blocks of 16 x 16 accumulators
+// (independent chains).  Two LDS buffers of K slices (k-major rows of the
+// tile width + 16 floats, so the four k rows one fragment read touches fall
+// in disjoint bank halves): slice i + 1 is stored while slice i is
+// multiplied, one barrier per slice.
 template <bool kAK, bool kBK_, bool kGroupK, int kWM, int kTM, int kTN>
 __global__ __launch_bounds__(256) void k_gemm_f32(int E, int64_t M, int64_t N, int64_t K,
                                                   const int32_t* __restrict__ off,
@@ -35,7 +38,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(int E, int64_t M, int64_t N, i
                                                   int64_t strideB, float* __restrict__ C,
                                                   int64_t ldc, int64_t strideC) {
   constexpr int kWN = 4 / kWM;
-  constexpr int kBM = 32 * kWM * kTM, kBN = 32 * kWN * kTN, kLdA = kBM + 4, kLdB = kBN + 4;
+  constexpr int kBM = 32 * kWM * kTM, kBN = 32 * kWN * kTN, kLdA = kBM + 16, kLdB = kBN + 16;
   constexpr int kNA = (kBM * 4 + 255) / 256, kNB = (kBN * 4 + 255) / 256;  // float4 per thread
   __shared__ float sA[2][kBK][kLdA];
   __shared__ float sB[2][kBK][kLdB];
@@ -143,14 +146,14 @@ __global__ __launch_bounds__(256) void k_gemm_f32(int E, int64_t M, int64_t N, i
     }
   };
 
-  f32x16 acc[kTM][kTN];
+  f32x4 acc[2 * kTM][2 * kTN];
 #pragma unroll
-  for (int i = 0; i < kTM; ++i)
+  for (int i = 0; i < 2 * kTM; ++i)
 #pragma unroll
-    for (int j = 0; j < kTN; ++j)
+    for (int j = 0; j < 2 * kTN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  const int half = lane >> 5, li = lane & 31;
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
+  const int quad = lane >> 4, li = lane & 15;
   if (k0 < kEnd) {
     load(k0);
     store(0);
@@ -161,31 +164,32 @@ __global__ __launch_bounds__(256) void k_gemm_f32(int E, int64_t M, int64_t N, i
     const bool more = k + kBK < kEnd;
     if (more) load(k + kBK);
 #pragma unroll
-    for (int kk = 0; kk < kBK; kk += 2) {
-      float a[kTM], b[kTN];
+    for (int kk = 0; kk < kBK; kk += 4) {
+      // fragments: A[i][k] and B[k][j] with i, j = lane % 16, k = kk + lane / 16
+      float a[2 * kTM], b[2 * kTN];
 #pragma unroll
-      for (int i = 0; i < kTM; ++i) a[i] = sA[cur][kk + half][wm * 32 * kTM + 32 * i + li];
+      for (int i = 0; i < 2 * kTM; ++i) a[i] = sA[cur][kk + quad][wm * 32 * kTM + 16 * i + li];
 #pragma unroll
-      for (int j = 0; j < kTN; ++j) b[j] = sB[cur][kk + half][wn * 32 * kTN + 32 * j + li];
+      for (int j = 0; j < 2 * kTN; ++j) b[j] = sB[cur][kk + quad][wn * 32 * kTN + 16 * j + li];
 #pragma unroll
-      for (int i = 0; i < kTM; ++i)
+      for (int i = 0; i < 2 * kTM; ++i)
 #pragma unroll
-        for (int j = 0; j < kTN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2 * kTN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
     }
     if (more) store(cur ^ 1);  // its last readers finished before the previous barrier
     __syncthreads();
     cur ^= 1;
   }
-  // acc[i][j][r] holds row 8 (r / 4) + 4 half + r % 4, column li of block (i, j)
+  // acc[i][j][r] holds row 4 (lane / 16) + r, column lane % 16 of block (i, j)
 #pragma unroll
-  for (int i = 0; i < kTM; ++i)
+  for (int i = 0; i < 2 * kTM; ++i)
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) {
-      const int64_t col = n0 + wn * 32 * kTN + 32 * j + li;
+    for (int j = 0; j < 2 * kTN; ++j) {
+      const int64_t col = n0 + wn * 32 * kTN + 16 * j + li;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 32 * kTM + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = m0 + wm * 32 * kTM + 16 * i + 4 * quad + r;
         if (row < mEnd && col < N) C[row * ldc + col] = acc[i][j][r];
       }
     }
