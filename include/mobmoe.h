@@ -443,8 +443,8 @@ int64_t mm_drop_pad_capacity(int64_t T, int32_t k, int32_t E, int32_t num, int32
  *   perm_c    [T*k]          kept assignments expert by expert, -1 past
  *                            offsets_c[E]
  *   inv_c     [T*k]          row of each assignment in perm_c, -1 if dropped
- * (offsets_c, perm_c, inv_c are a routing the expert calls and the combine
- * take as they take the dropless one; the combine skips -1 rows).
+ * (offsets_c, perm_c, inv_c have the layout of the dropless routing; the
+ * combine takes inv_c as its inverse permutation and skips the -1 rows).
  * Bit-identical to the oracle.  buf may be NULL when E * capacity = 0.
  * Errors: MM_ERR_NULL / MM_ERR_ALIGN, MM_ERR_SHAPE (E outside [1, 4096],
  * negative capacity, E * capacity or T*k >= 2^31).

@@ -548,6 +548,40 @@ def test_attn_decode_full_size_sampled():
         assert err.max() <= 1e-4, (b, err.max())
 
 
+def test_combine_after_drop_pad():
+    """A dropped batch: mm_combine over the kept routing of mm_drop_pad
+    (inverse with -1 for dropped assignments) equals the oracle's FP32
+    combine with the dropped gate weights set to zero, bit for bit."""
+    g = rng(77)
+    T, E, k, d = 300, 8, 4, 256
+    idx = _skewed_ids(g, T, E, k)
+    ds = B.desc(d, E, 64, 0, k)
+    off = torch.empty((E + 1,), dtype=torch.int32, device=DEV)
+    perm = torch.empty((T * k,), dtype=torch.int32, device=DEV)
+    inv = torch.empty((T * k,), dtype=torch.int32, device=DEV)
+    nb = B.workspace_bytes(ds, T, B.MM_WS_ROUTE)
+    ws = torch.empty((nb,), dtype=torch.uint8, device=DEV)
+    idx_d = dev(idx)
+    B.route_permute(ds, T, idx_d, off, perm, inv, ws, nb)
+    C = B.drop_pad_capacity(T, k, E, 1, 1)       # capacity factor 1: the skewed routing overflows
+    buf = torch.empty((E * C,), dtype=torch.int32, device=DEV)
+    offc = torch.empty((E + 1,), dtype=torch.int32, device=DEV)
+    permc = torch.empty((T * k,), dtype=torch.int32, device=DEV)
+    invc = torch.empty((T * k,), dtype=torch.int32, device=DEV)
+    B.drop_pad(T, E, k, C, idx_d, off, perm, inv, buf, offc, permc, invc)
+    _, ro, rp, ri = oracle.drop_pad(idx, E, C)
+    assert ro[E] < T * k
+    f = g.standard_normal((T * k, d)).astype(np.float32)     # kept rows in expert order
+    w = g.random((T, k)).astype(np.float32)
+    ys = g.standard_normal((T, d)).astype(np.float32)
+    y = torch.empty((T, d), device=DEV)
+    B.combine(ds, T, dev(f), invc, dev(w), dev(ys), y)
+    kept = ri >= 0
+    f_tok = np.where(kept[:, None], f[np.maximum(ri, 0)], 0.0).astype(np.float32).reshape(T, k, d)
+    w_kept = np.where(kept.reshape(T, k), w, 0.0).astype(np.float32)
+    assert np.array_equal(np_(y), oracle.combine_f32(f_tok, w_kept, ys))
+
+
 def test_gather_rows_bitexact():
     """mm_gather_rows: dst[r] = scale[perm[r]] * src[perm[r] // k] (FP32
     product), zero rows for -1."""
