@@ -626,16 +626,20 @@ def bench_linear(args, dev):
 
 
 def bench_train(args, dev):
-    """One QAT training step of the routed experts of the MobileMoE-S layer
-    (d = 768, 60 experts of h = 384, top-4): balancing-bias update, count
+    """One QAT training step of the MobileMoE-S layer's FFN part (d = 768, 60
+    routed experts of h = 384, top-4, shared expert of h_s = 1536; the
+    router's own backward is not part of it): balancing-bias update, count
     sort, drop-and-pad at capacity factor 1.5, eq. (6) fake quantisation of
     the latent FP32 weights and of the input rows, row gathers, the grouped
-    forward and backward products, and the straight-through weight
-    gradients.  Routing ids and upstream gradients are seeded synthetic."""
+    forward products of the routed and shared experts and the combine into
+    y, their backward, the token gradient (combine of the routed input
+    gradients plus the shared one) through the input quantiser, and the
+    straight-through weight gradients.  Routing ids, gate weights and dy are
+    seeded synthetic."""
     import numpy as np
     import torch
     from sparse_moe_ffn_amd import binding as B
-    T, E, k, d, h = args.batch or 2048, 60, 4, 768, 384
+    T, E, k, d, h, hs = args.batch or 2048, 60, 4, 768, 384, 1536
     Tk = T * k
     g = np.random.default_rng(777)
     # mildly uneven loads (expert probability ~ rank^-0.3: about 3 % of the
@@ -649,6 +653,9 @@ def bench_train(args, dev):
     w_gate = f32(g.random(Tk))
     wgu = f32(g.standard_normal((E, 2 * h, d)) / np.sqrt(d))
     wd = f32(g.standard_normal((E, d, h)) / np.sqrt(h))
+    sgu = f32(g.standard_normal((1, 2 * hs, d)) / np.sqrt(d))
+    sd = f32(g.standard_normal((1, d, hs)) / np.sqrt(hs))
+    topw = f32(g.random((T, k)))
     x = f32(g.standard_normal((T, d)))
     dy = f32(g.standard_normal((T, d)))
     bias = torch.zeros((E,), device=dev)
@@ -672,23 +679,45 @@ def bench_train(args, dev):
     dxs = torch.empty((Tk, d), device=dev)
     dwgu, dwd = torch.empty_like(wgu), torch.empty_like(wd)
     gwgu, gwd = torch.empty_like(wgu), torch.empty_like(wd)
-    wsb = B.expert_backward_workspace_bytes(Tk, h)
+    wsb = max(B.expert_backward_workspace_bytes(Tk, h), B.expert_backward_workspace_bytes(T, hs))
     ws = torch.empty((wsb,), dtype=torch.uint8, device=dev)
+    soff = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    sgu_b, sd_b = torch.empty_like(sgu), torch.empty_like(sd)
+    s_gu = torch.empty((T, 2 * hs), device=dev)
+    s_ab = torch.empty((T, hs), device=dev)
+    s_f = torch.empty((T, d), device=dev)
+    s_dx = torch.empty((T, d), device=dev)
+    s_dgu, s_dd = torch.empty_like(sgu), torch.empty_like(sd)
+    s_ggu, s_gd = torch.empty_like(sgu), torch.empty_like(sd)
+    ones = torch.ones((T, k), device=dev)
+    y = torch.empty((T, d), device=dev)
+    dx_b, dx = torch.empty((T, d), device=dev), torch.empty((T, d), device=dev)
 
     calls = {
         "bias_update": lambda: B.bias_update(T, E, k, idx_d, 1e-3, bias),
         "route": lambda: B.route_permute(ds, T, idx_d, off, perm, inv, rws, nb),
         "drop_pad": lambda: B.drop_pad(T, E, k, C, idx_d, off, perm, inv, buf, offc, permc, invc),
         "fake_quant_w": lambda: (B.fake_quant(E * 2 * h, d, 4, 32, wgu, wgu_b),
-                                 B.fake_quant(E * d, h, 4, 32, wd, wd_b)),
+                                 B.fake_quant(E * d, h, 4, 32, wd, wd_b),
+                                 B.fake_quant(2 * hs, d, 4, 32, sgu, sgu_b),
+                                 B.fake_quant(d, hs, 4, 32, sd, sd_b)),
         "fake_quant_x": lambda: B.fake_quant(T, d, 8, d, x, x_b),
         "gather": lambda: (B.gather_rows(Tk, d, k, permc, None, x_b, xs),
                            B.gather_rows(Tk, d, k, permc, w_gate, dy, dfs)),
         "forward": lambda: B.expert_train_forward_f32(E, d, h, Tk, offc, xs, wgu_b, wd_b, gu, ab, fo),
+        "shared_forward": lambda: B.expert_train_forward_f32(1, d, hs, T, soff, x_b, sgu_b, sd_b, s_gu,
+                                                             s_ab, s_f),
+        "combine_y": lambda: B.combine(ds, T, fo, invc, topw, s_f, y),
         "backward": lambda: B.expert_backward_f32(E, d, h, Tk, offc, xs, wgu_b, wd_b, gu, ab, dfs, dxs,
                                                   dwgu, dwd, ws, wsb),
+        "shared_backward": lambda: B.expert_backward_f32(1, d, hs, T, soff, x_b, sgu_b, sd_b, s_gu, s_ab,
+                                                         dy, s_dx, s_dgu, s_dd, ws, wsb),
+        "combine_dx": lambda: (B.combine(ds, T, dxs, invc, ones, s_dx, dx_b),
+                               B.fake_quant(T, d, 8, d, x, None, dx_b, dx)),
         "ste_w": lambda: (B.fake_quant(E * 2 * h, d, 4, 32, wgu, None, dwgu, gwgu),
-                          B.fake_quant(E * d, h, 4, 32, wd, None, dwd, gwd)),
+                          B.fake_quant(E * d, h, 4, 32, wd, None, dwd, gwd),
+                          B.fake_quant(2 * hs, d, 4, 32, sgu, None, s_dgu, s_ggu),
+                          B.fake_quant(d, hs, 4, 32, sd, None, s_dd, s_gd)),
     }
 
     def step(_i=0):
@@ -702,6 +731,7 @@ def bench_train(args, dev):
         per_call[name] = round(1e3 * _time_graphs(lambda _i, c=c: c(), 1, 10), 3)
     flops_fwd = 6.0 * kept * h * d
     flops_bwd = 12.0 * kept * h * d
+    flops_step = 18.0 * (kept * h + T * hs) * d
     bw_tf = flops_bwd / (per_call["backward"] * 1e-6) / 1e12
     cpu = None
     if not args.no_cpu_baseline:
@@ -720,13 +750,14 @@ def bench_train(args, dev):
                          f"backward, oracle.expert_train_forward + expert_backward (double, one thread), "
                          f"{dt:.1f}s"}
     out = {
-        "metric": "QAT training step of the routed experts (forward + backward, drop-and-pad 1.5): tokens/s",
+        "metric": "QAT training step of the MoE-FFN layer (routed + shared experts, forward + backward, drop-and-pad 1.5): tokens/s",
         "value": round(T / (ms * 1e-3), 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32 (fake-quantised operands)",
         "data": "synthetic",
-        "config": {"workload": "s_train_experts", "tokens": T, "d_model": d, "experts": E, "top_k": k,
-                   "hidden": h, "capacity": C, "kept_rows": kept, "parallelism": "single GPU"},
+        "config": {"workload": "s_train_ffn", "tokens": T, "d_model": d, "experts": E, "top_k": k,
+                   "hidden": h, "shared_hidden": hs, "capacity": C, "kept_rows": kept,
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(bw_tf, 3), "peak": FP32_VALU_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(bw_tf / FP32_VALU_PEAK_TFLOPS, 5), "traffic": None,
                      "kernel": "k_gemm_f32 x4 + k_train_act_bwd (one mm_expert_backward_f32 call)",
@@ -734,6 +765,7 @@ def bench_train(args, dev):
         "cpu_baseline": cpu,
         "per_call_us": per_call,
         "forward_tflops": round(flops_fwd / (per_call["forward"] * 1e-6) / 1e12, 3),
+        "step_matrix_tflops": round(flops_step / (ms * 1e-3) / 1e12, 3),
     }
     print(json.dumps(out), flush=True)
 

@@ -374,7 +374,8 @@ def _row_rel(got, ref):
     return np.abs(got - ref).max(1) / den
 
 
-EXPERT_SHAPES = [(3, 64, 32, [5, 0, 70]), (60, 768, 384, None), (4, 128, 1536 // 4, [0, 1, 129, 64])]
+EXPERT_SHAPES = [(3, 64, 32, [5, 0, 70]), (60, 768, 384, None), (4, 128, 1536 // 4, [0, 1, 129, 64]),
+                 (1, 768, 1536, [197])]          # the S shared expert: one group of every token
 
 
 @pytest.mark.parametrize("E,d,h,counts", EXPERT_SHAPES)
