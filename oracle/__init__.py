@@ -363,3 +363,21 @@ def expert_backward(offsets, xs, wgu, wd, gu, df):
     _load().ora_expert_backward(E, d, h, _p(offsets), _p(xs), _p(wgu), _p(wd), _p(gu), _p(df),
                                 _p(dxs), _p(dwgu), _p(dwd))
     return dxs, dwgu, dwd
+
+
+def router_backward(x, wr, bias, idx, f, inv, dy, gating: int = 0, lambda_z: float = 1e-4, dx=None):
+    """Router backward of the training step -> (dz [T, E], dwr [E, d], dx [T, d]) float64;
+    dx accumulates onto the given array (zeros if None)."""
+    x, wr, f, dy = _f32(x), _f32(wr), _f32(f), _f32(dy)
+    b = None if bias is None else _f32(bias)
+    idx = np.ascontiguousarray(idx, np.int32)
+    inv = np.ascontiguousarray(inv, np.int32)
+    T, d = x.shape
+    E = wr.shape[0]
+    k = idx.shape[1]
+    dz = np.empty((T, E), np.float64)
+    dwr = np.empty((E, d), np.float64)
+    dxo = np.zeros((T, d), np.float64) if dx is None else np.array(dx, np.float64, copy=True)
+    _load().ora_router_backward(_i64(T), d, E, k, gating, _p(x), _p(wr), _p(b), _p(idx), _p(f), _p(inv),
+                                _p(dy), ctypes.c_double(lambda_z), _p(dz), _p(dwr), _p(dxo))
+    return dz, dwr, dxo

@@ -836,4 +836,71 @@ int ora_expert_backward(int E, int d, int h, const int32_t* offsets, const float
   return 0;
 }
 
+// Router backward of the training step ([P1] "Pre-training", stability list:
+// FP32 router, router z-loss with weight lambda_z, sigmoid gating with
+// per-token top-k renormalisation as the training gate).  Given the
+// gradient dy of the layer output and the kept expert outputs f (rows of the
+// kept routing, inv[t*k+j] its row or -1 when dropped):
+//   g_j   = dy_t . f_inv(t,j)  (0 when dropped)        gradient of gate weight j
+//   z     = the logits the gate reads: x_t Wr^T + bias (or without the bias
+//           when gating & 2: selection-only bias)
+//   softmax gate (gating & 1 == 0): w_j = p_idx(j), p = softmax(z) over all E:
+//           dz_e = p_e (G_e - sum_j p_idx(j) g_j), G_e = g_j if e = idx(j), else 0
+//   sigmoid gate: w_j = sig(z_idx(j)) / S, S = sum over the k of sig:
+//           dz_idx(j) = sig'(z_idx(j)) / S (g_j - sum_i w_i g_i), other e: 0
+//   z-loss  (lambda_z / T) sum_t lse(z_t)^2 adds (2 lambda_z / T) lse(z_t) softmax(z_t)_e
+//   dWr = dz^T x  [E][d];  dx_t += dz_t Wr  [T][d] (accumulated into dx)
+// The bias gets no gradient (it follows the load).  Double precision.
+int ora_router_backward(int64_t T, int d, int E, int k, int gating, const float* x, const float* wr,
+                        const float* bias, const int32_t* idx, const float* f, const int32_t* inv,
+                        const float* dy, double lambda_z, double* dz, double* dwr, double* dx) {
+  std::vector<double> z(E), p(E), g(k);
+  for (int64_t i = 0; i < (int64_t)E * d; ++i) dwr[i] = 0.0;
+  for (int64_t t = 0; t < T; ++t) {
+    const float* xt = x + t * d;
+    for (int e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int c = 0; c < d; ++c) acc += (double)xt[c] * (double)wr[(int64_t)e * d + c];
+      z[e] = acc + ((bias && !(gating & 2)) ? (double)bias[e] : 0.0);
+    }
+    for (int j = 0; j < k; ++j) {
+      const int32_t r = inv[t * k + j];
+      double acc = 0.0;
+      if (r >= 0)
+        for (int c = 0; c < d; ++c) acc += (double)dy[t * d + c] * (double)f[(int64_t)r * d + c];
+      g[j] = acc;
+    }
+    double m = -INFINITY;
+    for (int e = 0; e < E; ++e) m = std::max(m, z[e]);
+    double S = 0.0;
+    for (int e = 0; e < E; ++e) S += std::exp(z[e] - m);
+    for (int e = 0; e < E; ++e) p[e] = std::exp(z[e] - m) / S;
+    const double lse = m + std::log(S);
+    double* dzt = dz + t * E;
+    for (int e = 0; e < E; ++e) dzt[e] = 2.0 * lambda_z / (double)T * lse * p[e];
+    if (!(gating & 1)) {
+      double pg = 0.0;
+      for (int j = 0; j < k; ++j) pg += p[idx[t * k + j]] * g[j];
+      for (int e = 0; e < E; ++e) dzt[e] -= p[e] * pg;
+      for (int j = 0; j < k; ++j) dzt[idx[t * k + j]] += p[idx[t * k + j]] * g[j];
+    } else {
+      double Ssig = 0.0;
+      std::vector<double> sg(k);
+      for (int j = 0; j < k; ++j) {
+        sg[j] = 1.0 / (1.0 + std::exp(-z[idx[t * k + j]]));
+        Ssig += sg[j];
+      }
+      double wg = 0.0;
+      for (int j = 0; j < k; ++j) wg += sg[j] / Ssig * g[j];
+      for (int j = 0; j < k; ++j) dzt[idx[t * k + j]] += sg[j] * (1.0 - sg[j]) / Ssig * (g[j] - wg);
+    }
+    for (int e = 0; e < E; ++e)
+      for (int c = 0; c < d; ++c) {
+        dwr[(int64_t)e * d + c] += dzt[e] * (double)xt[c];
+        dx[t * d + c] += dzt[e] * (double)wr[(int64_t)e * d + c];
+      }
+  }
+  return 0;
+}
+
 }  // extern "C"

@@ -803,3 +803,42 @@ def test_expert_backward_against_autograd(ora):
     np.testing.assert_allclose(dwd, Wd.grad.numpy(), rtol=1e-9, atol=1e-9)
     assert np.all(dwgu[1] == 0) and np.all(dwd[1] == 0)
     assert (pass_ == 0).sum() >= 1          # some row maximum clips
+
+
+@pytest.mark.parametrize("gating", [0, 1, 2, 3])
+def test_router_backward_against_autograd(ora, gating):
+    """Router backward against torch autograd (float64) of the gate and the
+    z-loss: y_t = sum_j w_tj f_tj with the expert outputs held fixed,
+    loss = sum y . dy + (lambda_z / T) sum_t lse(z_t)^2; dropped assignments
+    contribute nothing; the bias gets no gradient."""
+    import torch
+    g = rng(60 + gating)
+    T, d, E, k = 9, 32, 12, 3
+    x = g.standard_normal((T, d)).astype(np.float32)
+    wr = (g.standard_normal((E, d)) * 0.3).astype(np.float32)
+    bias = g.standard_normal(E).astype(np.float32)
+    z_sel = x.astype(np.float64) @ wr.T.astype(np.float64) + bias
+    idx = np.argsort(-z_sel, axis=1, kind="stable")[:, :k].astype(np.int32)
+    inv = g.permutation(T * k).astype(np.int32)
+    inv[[2, 7]] = -1                                   # two dropped assignments
+    f = g.standard_normal((T * k, d)).astype(np.float32)
+    dy = g.standard_normal((T, d)).astype(np.float32)
+    lz = 0.05
+    dz, dwr, dx = ora.router_backward(x, wr, bias, idx, f, inv, dy, gating, lz)
+    X = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    W = torch.tensor(wr, dtype=torch.float64, requires_grad=True)
+    Z = X @ W.T + (0.0 if gating & 2 else torch.tensor(bias, dtype=torch.float64))
+    Z.retain_grad()
+    I = torch.tensor(idx, dtype=torch.int64)
+    if gating & 1:
+        s = torch.sigmoid(Z).gather(1, I)
+        wts = s / s.sum(1, keepdim=True)
+    else:
+        wts = torch.softmax(Z, 1).gather(1, I)
+    fr = torch.tensor(np.where(inv[:, None] >= 0, f[np.maximum(inv, 0)], 0.0), dtype=torch.float64).reshape(T, k, d)
+    y = (wts[:, :, None] * fr).sum(1)
+    loss = (y * torch.tensor(dy, dtype=torch.float64)).sum() + lz / T * (torch.logsumexp(Z, 1) ** 2).sum()
+    loss.backward()
+    np.testing.assert_allclose(dz, Z.grad.numpy(), rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(dwr, W.grad.numpy(), rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(dx, X.grad.numpy(), rtol=1e-9, atol=1e-12)
