@@ -524,6 +524,28 @@ mm_status mm_expert_backward_f32(int32_t E, int32_t d, int32_t h, int64_t R, con
                                  float* dw_gu, float* dw_d, void* ws, size_t ws_bytes,
                                  void* stream);
 
+/*
+ * Router backward of the training step (section "Pre-training", stability
+ * list: FP32 router, router z-loss, softmax or sigmoid-renormalised gate by
+ * desc->gating).  Inputs: x FP32 [T][d] (the router input), w_router FP32
+ * [E][d], bias [E] (may be NULL), topk_idx int32 [T][k], f FP32 [*][d] the
+ * expert output rows of the kept routing with inv int32 [T*k] (row, or -1
+ * when dropped), dy FP32 [T][d] the gradient of the layer output.
+ *   g_j = dy_t . f_inv(t,j);  z = x_t Wr^T (+ bias unless selection-only)
+ *   softmax gate: dz = p * (G - <p, G>), sigmoid gate: dz_idx(j) =
+ *   sig'(z)/S (g_j - sum_i w_i g_i); both plus (2 lambda_z / T) lse(z) p
+ * Outputs: dz FP32 [T][E], dw_router FP32 [E][d], and dx FP32 [T][d] += dz Wr
+ * (accumulated: pass the experts' token gradient, or zeros).  The bias gets
+ * no gradient.  E <= 64 and a multiple of 4, d a multiple of 16.  FP32
+ * arithmetic, tolerance-checked against the oracle's double evaluation.
+ * Errors: MM_ERR_NULL / MM_ERR_ALIGN, MM_ERR_SHAPE.
+ */
+mm_status mm_router_backward_f32(const mm_layer_desc* desc, int64_t T, const float* x,
+                                 const float* w_router, const float* bias, const int32_t* topk_idx,
+                                 const float* f, const int32_t* inv, const float* dy,
+                                 float lambda_z, float* dz, float* dw_router, float* dx,
+                                 void* stream);
+
 /* Row RMSNorm with unit gain used between stacked layers of the decode
  * workload (not part of eq. (*)): y = x / sqrt(mean(x^2) + eps), FP32. */
 mm_status mm_rmsnorm_f32(int64_t rows, int64_t cols, float eps, const float* x, float* y,

@@ -35,7 +35,7 @@ EXPORTS = (
     "mm_attn_workspace_bytes", "mm_kv_append_i8", "mm_attn_decode_i8",
     "mm_bias_update", "mm_drop_pad_capacity", "mm_drop_pad", "mm_fake_quant",
     "mm_gather_rows", "mm_expert_train_forward_f32", "mm_expert_backward_workspace_bytes",
-    "mm_expert_backward_f32",
+    "mm_expert_backward_f32", "mm_router_backward_f32",
 )
 
 
@@ -105,6 +105,7 @@ _SIGS = {
                                     ctypes.c_int),
     "mm_expert_backward_workspace_bytes": ([_I64, _I32], _SZ),
     "mm_expert_backward_f32": ([_I32, _I32, _I32, _I64] + [_VP] * 11 + [_SZ, _VP], ctypes.c_int),
+    "mm_router_backward_f32": ([_DESC, _I64] + [_VP] * 7 + [_F] + [_VP] * 4, ctypes.c_int),
     "mm_moe_forward": ([_DESC, _I64, _VP, _VP, _VP, Weight, Weight, Weight, Weight, _VP, _VP, _VP,
                         _VP, _F, _VP, _SZ, _VP], ctypes.c_int),
 }
@@ -327,6 +328,14 @@ def expert_backward_f32(E, d, h, R, offsets, xs, w_gu, w_d, gu, a_bar, df, dxs, 
                                          _ptr(gu), _ptr(a_bar), _ptr(df), _ptr(dxs), _ptr(dw_gu),
                                          _ptr(dw_d), _ptr(ws), ws_bytes, _stream(stream)),
            "mm_expert_backward_f32")
+
+
+def router_backward_f32(ds, T, x, w_router, bias, topk_idx, f, inv, dy, lambda_z, dz, dw_router, dx,
+                        stream=None):
+    _check(load().mm_router_backward_f32(ctypes.byref(ds), T, _ptr(x), _ptr(w_router), _ptr(bias),
+                                         _ptr(topk_idx), _ptr(f), _ptr(inv), _ptr(dy), lambda_z,
+                                         _ptr(dz), _ptr(dw_router), _ptr(dx), _stream(stream)),
+           "mm_router_backward_f32")
 
 
 def rmsnorm_f32(rows, cols, eps, x, y, stream=None):

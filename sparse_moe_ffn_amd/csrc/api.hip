@@ -928,6 +928,32 @@ mm_status mm_expert_backward_f32(int32_t E, int32_t d, int32_t h, int64_t R, con
                     "mm_expert_backward_f32");
 }
 
+mm_status mm_router_backward_f32(const mm_layer_desc* desc, int64_t T, const float* x,
+                                 const float* w_router, const float* bias, const int32_t* topk_idx,
+                                 const float* f, const int32_t* inv, const float* dy,
+                                 float lambda_z, float* dz, float* dw_router, float* dx,
+                                 void* stream) {
+  MM_REQUIRE(desc);
+  const int E = desc->n_experts, d = desc->d_model, k = desc->top_k;
+  if (T < 1 || E < 4 || E > 64 || E % 4 || d < 16 || d % 16 || k < 1 || k > E ||
+      desc->gating < 0 || desc->gating > 3 || T * (int64_t)d >= (int64_t(1) << 40))
+    return fail(MM_ERR_SHAPE, "router backward: T %lld, E %d (<= 64, multiple of 4), d %d "
+                "(multiple of 16), k %d", (long long)T, E, d, k);
+  MM_REQUIRE(x);
+  MM_REQUIRE(w_router);
+  MM_OPTIONAL(bias);
+  MM_REQUIRE(topk_idx);
+  MM_REQUIRE(f);
+  MM_REQUIRE(inv);
+  MM_REQUIRE(dy);
+  MM_REQUIRE(dz);
+  MM_REQUIRE(dw_router);
+  MM_REQUIRE(dx);
+  return hip_status(mm::launch_router_backward(T, d, E, k, desc->gating, x, w_router, bias, topk_idx,
+                                               f, inv, dy, lambda_z, dz, dw_router, dx, S(stream)),
+                    "mm_router_backward_f32");
+}
+
 mm_status mm_rmsnorm_f32(int64_t rows, int64_t cols, float eps, const float* x, float* y,
                          void* stream) {
   if (rows < 0 || cols <= 0) return fail(MM_ERR_SHAPE, "bad shape");

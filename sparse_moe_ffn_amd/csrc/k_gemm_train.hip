@@ -52,8 +52,8 @@ __global__ __launch_bounds__(256) void k_gemm_f32(int E, int64_t M, int64_t N, i
     m0 = (int64_t)(blockIdx.x / ntn) * kBM;
     n0 = (int64_t)(blockIdx.x % ntn) * kBN;
     mEnd = M;
-    k0 = off[e];
-    kEnd = off[e + 1];
+    k0 = off ? off[e] : 0;  // no offsets: one group over [0, K)
+    kEnd = off ? off[e + 1] : K;
     C += (int64_t)e * strideC;
   } else {
     // find this workgroup's group and row tile: groups hold ceil(rows / kBM) tiles each
@@ -276,6 +276,90 @@ __global__ __launch_bounds__(256) void k_gather_rows(int64_t R, int64_t q4, int 
 
 // 64 x 64 tiles for every form (measured on the S expert shapes: as fast
 // as or faster than 32 x 128, 64 x 128 and 128 x 128).
+// Router backward, one wave per token: lane e < E holds the logit z_e the
+// gate reads (FP32, x_t . Wr_e (+ bias)), the wave the gate-weight
+// gradients g_j = dy_t . f_inv(t,j); then dz_e of the softmax (or
+// sigmoid-renormalised) gate plus the z-loss term, written to dz [T][E], and
+// dx_t += sum_e dz_e Wr_e with lanes over the columns.
+__global__ __launch_bounds__(256) void k_router_bwd(int64_t T, int d, int E, int k, int gating,
+                                                    const float* __restrict__ x,
+                                                    const float* __restrict__ wr,
+                                                    const float* __restrict__ bias,
+                                                    const int32_t* __restrict__ idx,
+                                                    const float* __restrict__ f,
+                                                    const int32_t* __restrict__ inv,
+                                                    const float* __restrict__ dy, float zscale,
+                                                    float* __restrict__ dz, float* __restrict__ dx) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int q = d / 4;
+  const float4* x4 = reinterpret_cast<const float4*>(x + t * d);
+  const bool live = lane < E;
+  float z = 0.0f;
+  if (live) {
+    const float4* w4 = reinterpret_cast<const float4*>(wr + (int64_t)lane * d);
+    for (int c = 0; c < q; ++c) {
+      const float4 a = x4[c], b = w4[c];
+      z = fmaf(a.x, b.x, z);
+      z = fmaf(a.y, b.y, z);
+      z = fmaf(a.z, b.z, z);
+      z = fmaf(a.w, b.w, z);
+    }
+    if (bias && !(gating & 2)) z += bias[lane];
+  }
+  // gradient of each gate weight: G_e = g_j where e = idx(j)
+  float G = 0.0f;
+  bool sel = false;
+  const float4* dy4 = reinterpret_cast<const float4*>(dy + t * d);
+  for (int j = 0; j < k; ++j) {
+    const int32_t r = inv[t * k + j];
+    float part = 0.0f;
+    if (r >= 0) {
+      const float4* f4 = reinterpret_cast<const float4*>(f + (int64_t)r * d);
+      for (int c = lane; c < q; c += 64) {
+        const float4 a = dy4[c], b = f4[c];
+        part = fmaf(a.x, b.x, part);
+        part = fmaf(a.y, b.y, part);
+        part = fmaf(a.z, b.z, part);
+        part = fmaf(a.w, b.w, part);
+      }
+    }
+    const float gj = wave_sum(part);
+    if (lane == idx[t * k + j]) {
+      G = gj;
+      sel = true;
+    }
+  }
+  const float m = max64(live ? z : -INFINITY);
+  const float ex = live ? expf(z - m) : 0.0f;
+  const float S = wave_sum(ex);
+  const float p = ex / S;
+  float dze = live ? zscale * (m + logf(S)) * p : 0.0f;
+  if (!(gating & 1)) {
+    const float pg = wave_sum(sel ? p * G : 0.0f);
+    dze += live ? p * (G - pg) : 0.0f;
+  } else {
+    const float sg = sel ? 1.0f / (1.0f + expf(-z)) : 0.0f;
+    const float Ss = wave_sum(sg);
+    const float wg = wave_sum(sel ? sg / Ss * G : 0.0f);
+    if (sel) dze += sg * (1.0f - sg) / Ss * (G - wg);
+  }
+  if (live) dz[t * E + lane] = dze;
+  for (int c = lane; c < q; c += 64) {
+    float4 acc = reinterpret_cast<float4*>(dx + t * d)[c];
+    for (int e = 0; e < E; ++e) {
+      const float de = __shfl(dze, e);
+      const float4 w = reinterpret_cast<const float4*>(wr + (int64_t)e * d)[c];
+      acc.x = fmaf(de, w.x, acc.x);
+      acc.y = fmaf(de, w.y, acc.y);
+      acc.z = fmaf(de, w.z, acc.z);
+      acc.w = fmaf(de, w.w, acc.w);
+    }
+    reinterpret_cast<float4*>(dx + t * d)[c] = acc;
+  }
+}
+
 template <bool kAK, bool kBK_, bool kGroupK>
 hipError_t gemm(int E, int64_t R, int64_t M, int64_t N, int64_t K, const int32_t* off, const float* A,
                 int64_t lda, const float* B, int64_t ldb, int64_t strideB, float* C, int64_t ldc,
@@ -293,6 +377,18 @@ hipError_t gemm(int E, int64_t R, int64_t M, int64_t N, int64_t K, const int32_t
 }
 
 }  // namespace
+
+hipError_t launch_router_backward(int64_t T, int d, int E, int k, int gating, const float* x,
+                                  const float* wr, const float* bias, const int32_t* idx,
+                                  const float* f, const int32_t* inv, const float* dy, float lambda_z,
+                                  float* dz, float* dwr, float* dx, hipStream_t st) {
+  hipLaunchKernelGGL(k_router_bwd, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, T, d, E, k, gating,
+                     x, wr, bias, idx, f, inv, dy, (float)(2.0 * lambda_z / (double)T), dz, dx);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // dWr = dz^T x: one group over the T tokens
+  return gemm<false, false, true>(1, T, E, d, T, nullptr, dz, E, x, d, 0, dwr, d, 0, st);
+}
 
 hipError_t launch_gather_rows(int64_t R, int64_t d, int k, const int32_t* perm, const float* scale,
                               const float* src, float* dst, hipStream_t st) {

@@ -42,3 +42,13 @@ hipError_t launch_expert_backward(int E, int d, int h, int64_t R, const int32_t*
                                   float* dwd, float* dabar, float* dgu, hipStream_t st);
 
 }  // namespace mm
+
+namespace mm {
+
+// Router backward of the training step (E <= 64, E and d multiples of 4 and 16).
+hipError_t launch_router_backward(int64_t T, int d, int E, int k, int gating, const float* x,
+                                  const float* wr, const float* bias, const int32_t* idx,
+                                  const float* f, const int32_t* inv, const float* dy, float lambda_z,
+                                  float* dz, float* dwr, float* dx, hipStream_t st);
+
+}  // namespace mm

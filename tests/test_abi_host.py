@@ -261,3 +261,13 @@ def test_expert_training_checks(lib):
     assert b(3, 64, 32, 10, *(FAKE,) * 10, None, ws, None) == B.MM_ERR_NULL
     assert lib.mm_gather_rows(4, 6, 2, FAKE, None, FAKE, FAKE, None) == B.MM_ERR_SHAPE
     assert lib.mm_gather_rows(4, 8, 2, None, None, FAKE, FAKE, None) == B.MM_ERR_NULL
+
+
+def test_router_backward_checks(lib):
+    rb = lib.mm_router_backward_f32
+    for E, d in [(62, 768), (68, 768), (60, 760)]:
+        ds = B.desc(d, E, 384, 0, 4)
+        assert rb(ctypes.byref(ds), 8, *(FAKE,) * 7, 1e-4, FAKE, FAKE, FAKE, None) == B.MM_ERR_SHAPE
+    ds = B.desc(768, 60, 384, 0, 4)
+    assert rb(ctypes.byref(ds), 0, *(FAKE,) * 7, 1e-4, FAKE, FAKE, FAKE, None) == B.MM_ERR_SHAPE
+    assert rb(ctypes.byref(ds), 8, *(FAKE,) * 7, 1e-4, FAKE, None, FAKE, None) == B.MM_ERR_NULL

@@ -583,6 +583,36 @@ def test_combine_after_drop_pad():
     assert np.array_equal(np_(y), oracle.combine_f32(f_tok, w_kept, ys))
 
 
+@pytest.mark.parametrize("gating", [0, 1, 2, 3])
+def test_router_backward(gating):
+    """mm_router_backward_f32 against the oracle's double evaluation at the
+    S router shape (T = 2048, E = 60, top-4, d = 768) with dropped
+    assignments and the pages' z-loss weight: dz per token and dWr within
+    1e-4 of the row / matrix maximum, dx (accumulated onto a given
+    gradient) within 1e-4 per row."""
+    g = rng(90 + gating)
+    T, E, k, d = 2048, 60, 4, 768
+    x = g.standard_normal((T, d)).astype(np.float32)
+    wr = (g.standard_normal((E, d)) * 0.02).astype(np.float32)
+    bias = (g.standard_normal(E) * 0.1).astype(np.float32)
+    idx = _skewed_ids(g, T, E, k)
+    inv = g.permutation(T * k).astype(np.int32)
+    inv[g.random(T * k) < 0.03] = -1
+    f = g.standard_normal((T * k, d)).astype(np.float32)
+    dy = g.standard_normal((T, d)).astype(np.float32)
+    dx0 = g.standard_normal((T, d)).astype(np.float32)
+    ds = B.desc(d, E, 384, 0, k, gating=gating)
+    dz = torch.empty((T, E), device=DEV)
+    dwr = torch.empty((E, d), device=DEV)
+    dx = dev(dx0)
+    B.router_backward_f32(ds, T, dev(x), dev(wr), dev(bias), dev(idx), dev(f), dev(inv), dev(dy), 1e-4,
+                          dz, dwr, dx)
+    rdz, rdwr, rdx = oracle.router_backward(x, wr, bias, idx, f, inv, dy, gating, 1e-4, dx=dx0)
+    assert _row_rel(np_(dz), rdz).max() <= 1e-4
+    assert np.abs(np_(dwr) - rdwr).max() <= 1e-4 * np.abs(rdwr).max()
+    assert _row_rel(np_(dx), rdx).max() <= 1e-4
+
+
 def test_gather_rows_bitexact():
     """mm_gather_rows: dst[r] = scale[perm[r]] * src[perm[r] // k] (FP32
     product), zero rows for -1."""
