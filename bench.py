@@ -626,41 +626,36 @@ def bench_linear(args, dev):
 
 
 def bench_train(args, dev):
-    """One QAT training step of the MobileMoE-S layer's FFN part (d = 768, 60
-    routed experts of h = 384, top-4, shared expert of h_s = 1536; the
-    router's own backward is not part of it): balancing-bias update, count
+    """One QAT training step of the MobileMoE-S MoE-FFN layer (d = 768, 60
+    routed experts of h = 384, top-4, shared expert of h_s = 1536): the FP32
+    router with the pages' training gate (sigmoid, top-k renormalised, the
+    balancing bias in the selection only), balancing-bias update, count
     sort, drop-and-pad at capacity factor 1.5, eq. (6) fake quantisation of
     the latent FP32 weights and of the input rows, row gathers, the grouped
     forward products of the routed and shared experts and the combine into
-    y, their backward, the token gradient (combine of the routed input
-    gradients plus the shared one) through the input quantiser, and the
-    straight-through weight gradients.  Routing ids, gate weights and dy are
-    seeded synthetic."""
+    y; then their backward, the token gradient (combine of the routed input
+    gradients plus the shared one) through the input quantiser, the router
+    backward with the z-loss, and the straight-through weight gradients.
+    Inputs x and dy and the latent weights are seeded synthetic."""
     import numpy as np
     import torch
     from sparse_moe_ffn_amd import binding as B
     T, E, k, d, h, hs = args.batch or 2048, 60, 4, 768, 384, 1536
     Tk = T * k
     g = np.random.default_rng(777)
-    # mildly uneven loads (expert probability ~ rank^-0.3: about 3 % of the
-    # assignments overflow capacity 1.5), as the balancing bias keeps them
-    p = np.arange(1, E + 1, dtype=np.float64) ** -0.3
-    p = p[g.permutation(E)]
-    p /= p.sum()
-    idx = np.stack([g.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
     f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
-    idx_d = torch.from_numpy(idx).to(dev)
-    w_gate = f32(g.random(Tk))
+    idx_d = torch.empty((T, k), dtype=torch.int32, device=dev)
+    wr = f32(g.standard_normal((E, d)) * 0.05)
     wgu = f32(g.standard_normal((E, 2 * h, d)) / np.sqrt(d))
     wd = f32(g.standard_normal((E, d, h)) / np.sqrt(h))
     sgu = f32(g.standard_normal((1, 2 * hs, d)) / np.sqrt(d))
     sd = f32(g.standard_normal((1, d, hs)) / np.sqrt(hs))
-    topw = f32(g.random((T, k)))
+    topw = torch.empty((T, k), device=dev)
     x = f32(g.standard_normal((T, d)))
     dy = f32(g.standard_normal((T, d)))
     bias = torch.zeros((E,), device=dev)
     C = B.drop_pad_capacity(T, k, E)
-    ds = B.desc(d, E, h, 0, k)
+    ds = B.desc(d, E, h, 0, k, gating=B.MM_GATE_SIGMOID_NORM | B.MM_GATE_BIAS_SELECT_ONLY)
     off = torch.empty((E + 1,), dtype=torch.int32, device=dev)
     perm = torch.empty((Tk,), dtype=torch.int32, device=dev)
     inv = torch.empty((Tk,), dtype=torch.int32, device=dev)
@@ -692,8 +687,11 @@ def bench_train(args, dev):
     ones = torch.ones((T, k), device=dev)
     y = torch.empty((T, d), device=dev)
     dx_b, dx = torch.empty((T, d), device=dev), torch.empty((T, d), device=dev)
+    dz = torch.empty((T, E), device=dev)
+    dwr = torch.empty((E, d), device=dev)
 
     calls = {
+        "router": lambda: B.router_topk(ds, T, x, wr, bias, idx_d, topw),
         "bias_update": lambda: B.bias_update(T, E, k, idx_d, 1e-3, bias),
         "route": lambda: B.route_permute(ds, T, idx_d, off, perm, inv, rws, nb),
         "drop_pad": lambda: B.drop_pad(T, E, k, C, idx_d, off, perm, inv, buf, offc, permc, invc),
@@ -703,7 +701,7 @@ def bench_train(args, dev):
                                  B.fake_quant(d, hs, 4, 32, sd, sd_b)),
         "fake_quant_x": lambda: B.fake_quant(T, d, 8, d, x, x_b),
         "gather": lambda: (B.gather_rows(Tk, d, k, permc, None, x_b, xs),
-                           B.gather_rows(Tk, d, k, permc, w_gate, dy, dfs)),
+                           B.gather_rows(Tk, d, k, permc, topw, dy, dfs)),
         "forward": lambda: B.expert_train_forward_f32(E, d, h, Tk, offc, xs, wgu_b, wd_b, gu, ab, fo),
         "shared_forward": lambda: B.expert_train_forward_f32(1, d, hs, T, soff, x_b, sgu_b, sd_b, s_gu,
                                                              s_ab, s_f),
@@ -714,6 +712,8 @@ def bench_train(args, dev):
                                                          dy, s_dx, s_dgu, s_dd, ws, wsb),
         "combine_dx": lambda: (B.combine(ds, T, dxs, invc, ones, s_dx, dx_b),
                                B.fake_quant(T, d, 8, d, x, None, dx_b, dx)),
+        "router_backward": lambda: B.router_backward_f32(ds, T, x, wr, bias, idx_d, fo, invc, dy, 1e-4,
+                                                         dz, dwr, dx),
         "ste_w": lambda: (B.fake_quant(E * 2 * h, d, 4, 32, wgu, None, dwgu, gwgu),
                           B.fake_quant(E * d, h, 4, 32, wd, None, dwd, gwd),
                           B.fake_quant(2 * hs, d, 4, 32, sgu, None, s_dgu, s_ggu),
@@ -750,7 +750,7 @@ def bench_train(args, dev):
                          f"backward, oracle.expert_train_forward + expert_backward (double, one thread), "
                          f"{dt:.1f}s"}
     out = {
-        "metric": "QAT training step of the MoE-FFN layer (routed + shared experts, forward + backward, drop-and-pad 1.5): tokens/s",
+        "metric": "QAT training step of the MoE-FFN layer (router, routed + shared experts, forward + backward, drop-and-pad 1.5): tokens/s",
         "value": round(T / (ms * 1e-3), 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32 (fake-quantised operands)",
