@@ -26,6 +26,7 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 INT8_MFMA_PEAK_TOPS = 5000.0    # MI355X dense int8 MFMA
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 FP32_VALU_PEAK_TFLOPS = 157.3
+FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense FP32 matrix
 MALL_BYTES = 256 << 20
 
 
@@ -758,8 +759,8 @@ def bench_train(args, dev):
         "config": {"workload": "s_train_ffn", "tokens": T, "d_model": d, "experts": E, "top_k": k,
                    "hidden": h, "shared_hidden": hs, "capacity": C, "kept_rows": kept,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(bw_tf, 3), "peak": FP32_VALU_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(bw_tf / FP32_VALU_PEAK_TFLOPS, 5), "traffic": None,
+        "roofline": {"bound": "mfma", "achieved": round(bw_tf, 3), "peak": FP32_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(bw_tf / FP32_MFMA_PEAK_TFLOPS, 5), "traffic": None,
                      "kernel": "k_gemm_f32 x4 + k_train_act_bwd (one mm_expert_backward_f32 call)",
                      "algorithmic_flops_per_launch": flops_bwd, "launch_us": per_call["backward"]},
         "cpu_baseline": cpu,
