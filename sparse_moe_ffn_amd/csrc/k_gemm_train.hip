@@ -412,17 +412,19 @@ hipError_t launch_expert_backward(int E, int d, int h, int64_t R, const int32_t*
                                   const float* wgu, const float* wd, const float* gu,
                                   const float* abar, const float* df, float* dxs, float* dwgu,
                                   float* dwd, float* dabar, float* dgu, hipStream_t st) {
-  // dabar = df wd_e  [R][h]
-  hipError_t e = gemm<true, false, false>(E, R, R, h, d, off, df, d, wd, h, (int64_t)d * h, dabar, h, 0,
-                                          st);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_train_act_bwd, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, st, R, h, gu, dabar,
-                     dgu);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  // dxs = dgu wgu_e  [R][d]
-  if ((e = gemm<true, false, false>(E, R, R, d, 2 * h, off, dgu, 2 * h, wgu, d, (int64_t)2 * h * d, dxs,
-                                    d, 0, st)) != hipSuccess)
-    return e;
+  hipError_t e;
+  if (R > 0) {  // no kept rows: no row products, but the weight gradients below are still zeroed
+    // dabar = df wd_e  [R][h]
+    e = gemm<true, false, false>(E, R, R, h, d, off, df, d, wd, h, (int64_t)d * h, dabar, h, 0, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_train_act_bwd, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, st, R, h, gu,
+                       dabar, dgu);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // dxs = dgu wgu_e  [R][d]
+    if ((e = gemm<true, false, false>(E, R, R, d, 2 * h, off, dgu, 2 * h, wgu, d, (int64_t)2 * h * d,
+                                      dxs, d, 0, st)) != hipSuccess)
+      return e;
+  }
   // dwd_e = df^T abar over the expert's rows  [d][h]
   if ((e = gemm<false, false, true>(E, R, d, h, 0, off, df, d, abar, h, 0, dwd, h, (int64_t)d * h,
                                     st)) != hipSuccess)

@@ -476,6 +476,66 @@ def test_bf16_layer_close_to_f32(ora):
     assert np.abs(a.y - b.y).max() / np.abs(a.y).max() < 2e-2
 
 
+def _bf16_ffn_torch(x, wgu, wd, round_x=True, round_w=True, round_a=True):
+    """BF16-weight SwiGLU FFN evaluated independently of the oracle: torch's
+    bfloat16 conversion (round to nearest even) of x, of both weights and of
+    the hidden row (through FP32, as an FP32 kernel rounds it), every product
+    and sum in float64.  The flags drop one rounding each, to show that the
+    pin below can see it."""
+    torch = pytest.importorskip("torch")
+    bf = lambda a, on: (torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16)
+                        .to(torch.float64) if on else torch.from_numpy(a.astype(np.float64)))
+    h = wd.shape[1]
+    gu = bf(x, round_x) @ bf(wgu, round_w).T
+    g, u = gu[:, :h], gu[:, h:]
+    a = g * torch.sigmoid(g) * u
+    if round_a:
+        a = a.to(torch.float32).to(torch.bfloat16).to(torch.float64)
+    return (a @ bf(wd, round_w).T).numpy()
+
+
+def test_bf16_ffn_against_torch_casts(ora):
+    """The BF16 path (R15: x, weights and the hidden row rounded to BF16,
+    sums in higher precision) equals an independent torch evaluation to
+    1e-9 of each row's maximum; evaluations without one of the three
+    roundings miss it by orders of magnitude more."""
+    g = rng(40)
+    d, h, rows = 256, 128, 24
+    x = g.standard_normal((rows, d)).astype(np.float32)
+    wgu = (g.standard_normal((2 * h, d)) * 0.02).astype(np.float32)
+    wd = (g.standard_normal((d, h)) * 0.02).astype(np.float32)
+    got = ora.ffn_float(x, wgu, wd, bf16=True)
+    rel = lambda a, b: float((np.abs(a - b).max(1) / np.abs(b).max(1)).max())
+    assert rel(got, _bf16_ffn_torch(x, wgu, wd)) < 1e-9
+    for drop in ("round_x", "round_w", "round_a"):
+        assert rel(got, _bf16_ffn_torch(x, wgu, wd, **{drop: False})) > 1e-5, drop
+
+
+def test_bf16_layer_against_torch_casts(ora):
+    """Whole BF16 layer: each selected expert and the shared expert from the
+    independent torch evaluation, combined with the router's weights in
+    float64, the output rounded to BF16 (through FP32) -- equal to the
+    oracle's layer except where a value sits within rounding of a BF16 tie."""
+    torch = pytest.importorskip("torch")
+    g = rng(41)
+    E, d, h, hs, T, k = 8, 128, 64, 256, 12, 4
+    x = g.standard_normal((T, d)).astype(np.float32)
+    wr, wgu, wd, sgu, sd = _mk(E, d, h, hs, 42)
+    r = ora.forward(x, wr, None, wgu, wd, sgu, sd, k=k, wfmt="bf16")
+    ys = _bf16_ffn_torch(x, sgu, sd)
+    y = ys.copy()
+    for t in range(T):
+        for j in range(k):
+            e = r.idx[t, j]
+            y[t] += r.w[t, j] * _bf16_ffn_torch(x[t:t + 1], wgu[e], wd[e])[0]
+    yb = torch.from_numpy(y).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert float((np.abs(r.ys - ys).max(1) / np.abs(ys).max(1)).max()) < 1e-9
+    # one BF16 ulp is 2^-8 relative: rounding may differ only for y within 1e-9 of a tie
+    diff = r.y != yb
+    assert diff.mean() < 1e-3
+    assert np.all(np.abs(r.y - yb)[diff] <= np.abs(yb)[diff] * 2.0 ** -7)
+
+
 def test_exp_ref_accuracy(ora):
     x = np.linspace(-87.3, 88.7, 3_000_001, dtype=np.float32)
     y = ora.exp_ref(x).astype(np.float64)
@@ -515,6 +575,23 @@ def test_rmsnorm_closed_form(ora):
     z = rng(31).standard_normal((4, 96)).astype(np.float32)
     yz = ora.rmsnorm(z, eps=0.0)
     np.testing.assert_allclose((yz ** 2).mean(1), 1.0, rtol=1e-12)
+
+
+def test_rmsnorm_eps_closed_form(ora):
+    """With eps > 0 a constant row c gives c / sqrt(c^2 + eps) in every
+    column (eps inside the square root, added to the mean square); at
+    c^2 = 10 eps that is 4.7 % below the eps = 0 value, so a dropped or
+    misplaced eps fails."""
+    for c, eps in ((0.01, 1e-5), (-0.03, 1e-5), (2.0, 0.5)):
+        x = np.full((3, 128), c, np.float32)
+        y = ora.rmsnorm(x, eps=eps)
+        c64 = float(np.float32(c))
+        np.testing.assert_allclose(y, c64 / np.sqrt(c64 * c64 + eps), rtol=1e-14)
+    # a row with a known mean square: values +-a, mean square a^2
+    a = np.float32(0.02)
+    x = np.tile(np.array([a, -a], np.float32), (2, 48))
+    y = ora.rmsnorm(x, eps=1e-4)
+    np.testing.assert_allclose(np.abs(y), float(a) / np.sqrt(float(a) ** 2 + 1e-4), rtol=1e-14)
 
 
 def test_oracle_rejects_bad_shapes(ora):
