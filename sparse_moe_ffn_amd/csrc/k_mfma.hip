@@ -52,83 +52,69 @@ struct Capture {
   int G, p0, n;
 };
 
-// One wave's registers for two groups: activation fragments, packed weight
-// fragments and scales.
-// Global-address-space views: loads through them are global_load (not flat),
-// which keeps the memory counter in order and lets the prefetch stay in
-// flight across the math.
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef const __attribute__((address_space(1))) v4i gint4;
 typedef const __attribute__((address_space(1))) v2u guint2;
 typedef const __attribute__((address_space(1))) float gfloat;
 
+// One group's registers: activation fragments, packed weight fragments and
+// scales.  Global-address-space views: loads through them are global_load
+// (not flat), which keeps the memory counter in order and lets the
+// prefetches stay in flight across the math.
 template <int kMT, int kNT>
-struct WStage {
-  v4i a[2][kMT];
-  v2u b[2][kNT];
-  float s[2][kNT];
+struct WSlot {
+  v4i a[kMT];
+  v2u b[kNT];
+  float s[kNT];
 };
 
-// Loads groups g0 and g0 + 1 relative to the current pointers (row-major
-// activations: the offsets are compile-time constants and fold into the load
-// instructions; group-major: astride, the 16-byte units from one group to
-// the next, is the row count times 2).  pb / ps are wave-uniform (the lane
-// offset is added here), so the loads take a scalar base and a small
-// per-lane offset.
-template <int kMT, int kNT>
-__device__ __forceinline__ void wload(WStage<kMT, kNT>& st, gint4* const (&pa)[kMT],
-                                      guint2* const (&pb)[kNT], gfloat* const (&ps)[kNT],
-                                      int g0, int lane, int astride) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-#pragma unroll
-    for (int m = 0; m < kMT; ++m) st.a[i][m] = pa[m][(g0 + i) * astride];
-#pragma unroll
-    for (int j = 0; j < kNT; ++j) {
-      st.b[i][j] = pb[j][(g0 + i) * 64 + lane];
-      st.s[i][j] = ps[j][(g0 + i) * 32 + (lane & 31)];
-    }
-  }
-}
-
-// Two groups: per group one MFMA per (row tile, column tile) from a zero
-// accumulator (the exact int32 group sum), then acc = fma(scale, sum, acc).
-// The epilogue of one tile is placed after the next tile's MFMA so that the
-// matrix core and the vector ALU work at the same time.
+// One group: per (row tile, column tile) one MFMA from a zero accumulator
+// (the exact int32 group sum), then acc = fma(scale, sum, acc).  Each
+// tile's weights are unpacked just before their first MFMA, and the
+// epilogue of one product is issued after the next product's MFMA, so the
+// matrix core and the vector ALU work at the same time with two MFMA
+// results live.
 template <int kMT, int kNT, bool kCapture>
-__device__ __forceinline__ void wcompute(v16f (&acc)[kMT][kNT], const WStage<kMT, kNT>& st,
-                                         int g0, int lane, const int (&rb)[kNT],
-                                         const Capture& cap) {
+__device__ __forceinline__ void wcompute1(v16f (&acc)[kMT][kNT], const WSlot<kMT, kNT>& st, int g,
+                                          int lane, const int (&rb)[kNT], const Capture& cap) {
+  v4i bv[kNT];
+  v16i Rp;
+  int pm = 0, pj = 0;
+  auto epi = [&](const v16i& R, int m, int j) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    v4i bv[kNT];
+    for (int r = 0; r < 16; ++r) acc[m][j][r] = fmaf(st.s[j], (float)R[r], acc[m][j][r]);
+    if (kCapture) {
 #pragma unroll
-    for (int j = 0; j < kNT; ++j) bv[j] = unpack16(make_uint2(st.b[i][j].x, st.b[i][j].y));
-    v16i R[kMT][kNT];
-#pragma unroll
-    for (int m = 0; m < kMT; ++m)
-#pragma unroll
-      for (int j = 0; j < kNT; ++j)
-        R[m][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(st.a[i][m], bv[j], v16i{}, 0, 0, 0);
-#pragma unroll
-    for (int m = 0; m < kMT; ++m)
-#pragma unroll
-      for (int j = 0; j < kNT; ++j) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[m][j][r] = fmaf(st.s[i][j], (float)R[m][j][r], acc[m][j][r]);
-        if (kCapture) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if (row < cap.n) {
-              const int64_t col = (int64_t)rb[j] * 32 + (lane & 31);
-              cap.isum[(((int64_t)(cap.p0 + row)) * cap.wrows + col) * cap.G + g0 + i] =
-                  R[m][j][r] >> 4;
-            }
-          }
+      for (int r = 0; r < 16; ++r) {
+        const int row = m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row < cap.n) {
+          const int64_t col = (int64_t)rb[j] * 32 + (lane & 31);
+          cap.isum[(((int64_t)(cap.p0 + row)) * cap.wrows + col) * cap.G + g] = R[r] >> 4;
         }
       }
-  }
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < kNT; ++j)
+#pragma unroll
+    for (int m = 0; m < kMT; ++m) {
+      if (m == 0) bv[j] = unpack16(make_uint2(st.b[j].x, st.b[j].y));
+      const v16i R = __builtin_amdgcn_mfma_i32_32x32x32_i8(st.a[m], bv[j], v16i{}, 0, 0, 0);
+      if (j + m > 0) epi(Rp, pm, pj);
+      Rp = R;
+      pm = m;
+      pj = j;
+    }
+  epi(Rp, pm, pj);
+#pragma unroll
+  for (int j = 0; j < kNT; ++j)
+#pragma unroll
+    for (int m = 0; m < kMT; ++m) {
+      if (m == 0) __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU: unpack tile j
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
+      if (j + m > 0) __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);  // VALU: previous epilogue
+    }
+  __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);
 }
 
 // Arguments of one W4A8 product; a launch carries one, or two (the routed
@@ -208,7 +194,8 @@ __device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int x, int i, int 
   }
   // source row of this lane's A rows (padding rows read the tile's first row;
   // their results are never stored) and its activation scale
-  gint4* pa[kMT];
+  // (byte offsets from the activation base fit 32 bits: rows * K < 2^31)
+  uint32_t aoff[kMT];
   float srow[kMT];
 #pragma unroll
   for (int m = 0; m < kMT; ++m) {
@@ -219,22 +206,23 @@ __device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int x, int i, int 
       src = a.perm[p0 + rr] / a.k;
       if ((unsigned)src >= (unsigned)a.T) src = 0;  // stays in bounds for a corrupt perm
     }
-    pa[m] = (gint4*)(act + (int64_t)src * (kGM ? 32 : K) + 16 * (lane >> 5));
+    aoff[m] = (uint32_t)src * (uint32_t)(kGM ? 32 : K) + 16u * (uint32_t)(lane >> 5);
     srow[m] = act_scale[src];
   }
   const int64_t wrows = kGateUp ? 2 * (int64_t)h : N;
   const uint8_t* we = wq + (int64_t)e * (wrows / 32) * G * kChunkBytes;
   const float* se = wsc + (int64_t)e * (wrows / 32) * G * 32;
-  guint2* pb[kNT];
-  gfloat* ps[kNT];
+  const uint8_t* pb[kNT];  // wave-uniform bases (scalar registers)
+  const uint8_t* ps[kNT];
 #pragma unroll
   for (int j = 0; j < kNT; ++j) {
-    pb[j] = (guint2*)(we + (int64_t)rb[j] * G * kChunkBytes);
-    ps[j] = (gfloat*)(se + (int64_t)rb[j] * G * 32);
+    pb[j] = we + (int64_t)rb[j] * G * kChunkBytes;
+    ps[j] = (const uint8_t*)(se + (int64_t)rb[j] * G * 32);
   }
   const Capture cap{isum, wrows, G, p0, n};
-  // activation rows: x_q has T, the hidden rows have `rows`
-  const int astride = kGM ? 2 * (int)(kGateUp ? a.T : a.rows) : kGroup / 16;
+  // bytes from one group of an activation row to the next (x_q has T rows,
+  // the hidden rows `rows`)
+  const uint32_t astride = kGM ? 32u * (uint32_t)(kGateUp ? a.T : a.rows) : 32u;
 
   v16f acc[kMT][kNT];
 #pragma unroll
@@ -242,28 +230,35 @@ __device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int x, int i, int 
 #pragma unroll
     for (int j = 0; j < kNT; ++j) acc[m][j] = v16f{};
 
-  // Two register stages in ping-pong, each two groups; the pointers advance
-  // four groups per iteration.  The last iteration's prefetch re-reads its
-  // own second stage (valid addresses, result unused).  G % 4 == 0.
-  WStage<kMT, kNT> s0, s1;
-  wload(s0, pa, pb, ps, 0, lane, astride);
-  for (int g = 0; g < G; g += 4) {
-    wload(s1, pa, pb, ps, 2, lane, astride);
-    __builtin_amdgcn_sched_barrier(0);
-    wcompute<kMT, kNT, kCapture>(acc, s0, g, lane, rb, cap);
-    __builtin_amdgcn_sched_barrier(0);
-    const int adv = g + 4 < G ? 4 : 2;
+  // Register ring of kD single-group slots: slot i % kD holds group i,
+  // loaded kD - 1 groups before its products (the last groups re-load group
+  // G - 1: valid addresses, results unused).  Every load is a scalar base
+  // plus a 32-bit lane offset.  G % kD == 0.
+  constexpr int kD = 4;
+  WSlot<kMT, kNT> sl[kD];
+  auto load = [&](WSlot<kMT, kNT>& st, int g) {
 #pragma unroll
-    for (int m = 0; m < kMT; ++m) pa[m] += adv * astride;
+    for (int m = 0; m < kMT; ++m) st.a[m] = *(gint4*)(act + (aoff[m] + (uint32_t)g * astride));
 #pragma unroll
     for (int j = 0; j < kNT; ++j) {
-      pb[j] += adv * 64;
-      ps[j] += adv * 32;
+      st.b[j] = *(guint2*)(pb[j] + (uint32_t)(g * kChunkBytes + lane * 8));
+      st.s[j] = *(gfloat*)(ps[j] + (uint32_t)(g * 128 + (lane & 31) * 4));
     }
-    wload(s0, pa, pb, ps, 0, lane, astride);
+  };
+  // the first slots in slot order (the counter wait at the loop head must
+  // find slot 0 oldest, as it is on every later iteration)
+#pragma unroll
+  for (int i = 0; i < kD - 1; ++i) {
+    load(sl[i], i);
     __builtin_amdgcn_sched_barrier(0);
-    wcompute<kMT, kNT, kCapture>(acc, s1, g + 2, lane, rb, cap);
-    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int g = 0; g < G; g += kD) {
+#pragma unroll
+    for (int i = 0; i < kD; ++i) {
+      load(sl[(i + kD - 1) % kD], min(g + i + kD - 1, G - 1));
+      wcompute1<kMT, kNT, kCapture>(acc, sl[i], g + i, lane, rb, cap);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
 #pragma unroll
