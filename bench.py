@@ -118,8 +118,22 @@ def pair_kernel_of(w, T):
     return f"k_w4a8w_pair<{2 if r2 else 1}, {2 if d2 else 1}, true>"
 
 
-KERNEL_SOURCES = ["sparse_moe_ffn_amd/csrc/k_mfma.hip", "sparse_moe_ffn_amd/csrc/k_gemv.hip",
-                  "sparse_moe_ffn_amd/csrc/common.h", "sparse_moe_ffn_amd/csrc/launch.h"]
+def pair_gemv_kernel_of(w, T):
+    """rocprofv3 name of the merged weight-streaming gate/up kernel
+    mm_moe_forward launches for decode batches (routed rows <= 512, shared
+    rows <= 64, reduction fits), or None."""
+    if w.wfmt != "int4g32" or not w.hs:
+        return None
+    rows, K = T * w.k, w.d
+    if rows <= 512 and T <= 64 and K % 64 == 0 and K <= 2560:
+        return "k_gemv_i4_pair<4, true, false>"
+    return None
+
+
+# Every library source: stored counter figures are valid only for the code
+# they were taken on.
+KERNEL_SOURCES = sorted(os.path.relpath(f, ROOT) for pat in ("*.hip", "*.h") for f in
+                        __import__("glob").glob(os.path.join(ROOT, "sparse_moe_ffn_amd", "csrc", pat)))
 
 
 ATTN_SOURCES = ["sparse_moe_ffn_amd/csrc/k_attn.hip", "sparse_moe_ffn_amd/csrc/common.h"]
@@ -134,10 +148,11 @@ def kernel_source_sha(sources=None):
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str, kernel: str, summary: str = "traffic.md", sources=None):
-    """HBM bytes per launch of `kernel` on `workload` from a committed
-    rocprofv3 counter summary under profiles/, or None when there is none or
-    the kernel sources changed since the counters were taken."""
+def stored_traffic(workload: str, kernel: str, summary: str = "traffic.md", sources=None, key=None):
+    """HBM bytes per launch of `kernel` (or per step, kernel "step") on
+    `workload` at `key` tokens per step from a committed rocprofv3 counter
+    summary under profiles/, or None when there is none or the kernel sources
+    changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", summary)
     if not os.path.exists(path):
         return None
@@ -147,7 +162,7 @@ def stored_traffic(workload: str, kernel: str, summary: str = "traffic.md", sour
             continue
         kv = dict(p.split("=", 1) for p in line[len("traffic:"):].split() if "=" in p)
         if kv.get("workload") == workload and kv.get("kernel") == kernel.replace(" ", "") \
-                and kv.get("source_sha256") == sha:
+                and kv.get("source_sha256") == sha and (key is None or kv.get("tokens") == str(key)):
             return float(kv["bytes_per_launch"])
     return None
 
@@ -318,26 +333,12 @@ def main():
 
     # ---- per-call durations: each call is recorded REPS times into a HIP
     # graph of its own and replayed between two HIP events on the stream it
-    # runs on, so the figure is the kernel time (plus the graph's dispatch
-    # gap), not host launch overhead.  Every call except the shared expert
-    # (gate/up then down) is a single kernel.
-    calls = ["router", "route", "act_quant", "gateup", "gateup_gemm", "down", "shared", "combine"]
+    # runs on (kernel time plus the graph's dispatch gap, no host launch cost).
+    calls = ["router", "route", "act_quant", "gateup", "down", "shared", "combine"]
     if w.wfmt != "int4g32":
         calls.remove("act_quant")
-        calls.remove("gateup_gemm")
-    abuf = torch.empty((T * w.k, w.h), dtype=torch.float32, device=dev)
     if not w.hs:
         calls.remove("shared")
-    pair_kind = pair_kernel_of(w, T) if fused else None
-    if pair_kind:
-        # the merged gate/up kernel of the one-call step, on its own: FP32
-        # hidden rows from x_q in the group-major layout it reads there
-        calls.append("gateup_pair")
-        xq_gm = torch.empty((T, w.d), dtype=torch.int8, device=dev)
-        sx_gm = torch.empty((T,), dtype=torch.float32, device=dev)
-        sbuf = torch.empty((T, w.hs), dtype=torch.float32, device=dev)
-        B.act_quant_i8_layout(T, w.d, xs[0], xq_gm, sx_gm, B.MM_ACT_GROUP_MAJOR)
-    # The repetitions cycle through the distinct weight sets (as the step does).
     x0 = xs[0]
     for L in layers:
         L.forward(x0)  # routing state for the expert calls
@@ -353,16 +354,12 @@ def main():
             L.act_quant(x0, T)
         elif c == "gateup":
             L.gateup(x0, T)
-        elif c == "gateup_gemm":
-            L.gateup_f32(x0, T, abuf)
         elif c == "down":
             L.down(T)
         elif c == "shared":
             L.shared(x0, T)
         elif c == "combine":
             L.combine(T)
-        elif c == "gateup_pair":
-            L.gateup_pair_f32(T, xq_gm, abuf, sbuf)
 
     per_call_us = {}
     for c in calls:
@@ -382,69 +379,150 @@ def main():
         del g
     torch.cuda.synchronize()
 
+    # ---- the layer's gate/up product stage inside the step (the largest
+    # product: routed and shared gate/up with SwiGLU, one merged launch where
+    # the one-call layer uses one): mm_moe_forward records HIP events around
+    # it on its stream (mm_set_profile_events); the step runs eagerly with a
+    # fresh event pair per layer call, so the figure is that stage's time in
+    # the step's own context (the same launches a kernel trace of the step
+    # shows).
+    stage_us = None
+    if fused:
+        pairs = []
+
+        def timed_fwd(L, src, dst=None):
+            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            B.set_profile_events(*ev)
+            if dst is not None:
+                L.forward_fused(src, y_norm=dst, norm_eps=1e-5)
+            else:
+                L.forward_fused(src)
+            pairs.append(ev)
+
+        for s in range(3):
+            if decode:
+                cur = xs[s % n_inputs]
+                stack = layers if w.layers > 1 else [layers[s % n_inst]]
+                for i, L in enumerate(stack):
+                    if i + 1 < len(stack):
+                        timed_fwd(L, cur, nxt)
+                        cur = nxt
+                    else:
+                        timed_fwd(L, cur)
+            else:
+                timed_fwd(layers[s % n_inst], xs[0])
+        B.set_profile_events(None, None)
+        torch.cuda.synchronize()
+        times = [a.elapsed_time(b) * 1e3 for a, b in pairs]
+        stage_us = sum(times) / len(times)
+
     ops, B_r, B_s = layer_work(w, T)
-    L0 = layers[0]
-    n_distinct = int(np.unique(L0.idx.cpu().numpy()).size)
-    # Roofline of the dominant single kernel of the step.  One-call step with
-    # the merged matrix-core gate/up: that kernel (routed and shared gate/up
-    # in one launch), timed on its own through mm_expert_gateup_pair_f32.
-    # Otherwise the routed gate/up product (timed through the FP32-output
-    # form of the gate/up call, the same kernel the step runs before its row
-    # quantiser) or the routed down product, whichever takes longer.
-    gu_key = "gateup_gemm" if "gateup_gemm" in per_call_us else "gateup"
-    if pair_kind:
-        dom = "gateup_pair"
-        dom_ops = ops["gateup"] + ops["shared"] * 2 // 3  # shared gate/up: 2 of its 3 d x h_s products
-        kind, path = pair_kind, "matrix-core, routed + shared gate/up in one launch"
-    else:
-        dom = gu_key if per_call_us[gu_key] >= per_call_us["down"] else "down"
-        dom_ops = ops["gateup"] if dom == gu_key else ops["down"]
-        kind, path = kernel_of(w, T, dom != "down")
+    n_layers = w.layers if decode else 1
+    # distinct routed experts each layer selected in its last call (decode bytes)
+    distinct = [int(np.unique(L.idx.cpu().numpy()).size) for L in layers]
+    n_distinct = distinct[0]
+    layer_ops = ops["gateup"] + ops["down"] + ops["shared"]
+    gu_ops = ops["gateup"] + ops["shared"] * 2 // 3  # shared gate/up: 2 of its 3 d x h_s products
+    wb_r = B_r / (3 * w.d * w.h)  # bytes per weight
     if decode:
-        # bytes the kernel must stream: packed weights + scales of the experts
-        # selected in the step (distinct ids), counted once
-        nbytes = n_distinct * ((2 * w.h * w.d) if dom != "down" else (w.d * w.h)) * wb
-        achieved = nbytes / (per_call_us[dom] * 1e-6) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
-                "traffic": stored_traffic(w.name, kind), "kernel": kind, "path": path,
-                "algorithmic_bytes_per_launch": nbytes, "launch_us": round(per_call_us[dom], 3)}
+        # bytes the step must move: per layer the packed weights and scales of
+        # the distinct selected experts, the shared expert's, the FP32 router,
+        # and the token rows in and out
+        per_layer = [u * B_r + B_s + 4 * w.E * w.d + 8 * T * w.d for u in distinct[:n_layers]]
+        if w.layers == 1:
+            per_layer = [sum(u * B_r for u in distinct) / len(distinct) + B_s + 4 * w.E * w.d
+                         + 8 * T * w.d]
+        step_bytes = sum(per_layer)
+        achieved = step_bytes / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 5),
+                "traffic": stored_traffic(w.name, "step", key=T),
+                "scope": "whole step (every launch of the layer stack)",
+                "algorithmic_bytes_per_step": int(step_bytes)}
+        if stage_us:
+            gu_bytes = n_distinct * 2 * w.h * w.d * wb_r + 2 * w.hs * w.d * wb_r
+            ka = gu_bytes / (stage_us * 1e-6) / 1e9
+            kind, path = kernel_of(w, T, True)
+            roof["kernel"] = {"stage": "gate/up (routed + shared)", "kernel": pair_gemv_kernel_of(w, T) or kind,
+                              "launch_us": round(stage_us, 3), "achieved": round(ka, 2),
+                              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ka / HBM_PEAK_GBS, 5),
+                              "algorithmic_bytes_per_launch": int(gu_bytes),
+                              "traffic": stored_traffic(w.name, pair_gemv_kernel_of(w, T) or kind, key=T),
+                              "timing": "HIP events around the stage inside eager steps"}
     else:
         peak = INT8_MFMA_PEAK_TOPS if w.wfmt == "int4g32" else (
             BF16_MFMA_PEAK_TFLOPS if w.wfmt == "bf16" else FP32_VALU_PEAK_TFLOPS)
-        achieved = dom_ops / (per_call_us[dom] * 1e-6) / 1e12
+        unit = "TOP/s" if w.wfmt == "int4g32" else "TFLOP/s"
+        achieved = layer_ops / (ms * 1e-3) / 1e12
         roof = {"bound": "mfma" if w.wfmt != "f32" else "alu", "achieved": round(achieved, 3),
-                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 5),
-                "traffic": stored_traffic(w.name, kind), "kernel": kind, "path": path,
-                "algorithmic_ops_per_launch": dom_ops, "launch_us": round(per_call_us[dom], 3)}
+                "peak": peak, "unit": unit, "frac": round(achieved / peak, 5),
+                "traffic": stored_traffic(w.name, "step", key=T),
+                "scope": "whole step (router, count sort, quantisers, products, combine)",
+                "algorithmic_ops_per_step": int(layer_ops)}
+        if stage_us:
+            ka = gu_ops / (stage_us * 1e-6) / 1e12
+            kind = pair_kernel_of(w, T)
+            kind = kind or kernel_of(w, T, True)[0]
+            roof["kernel"] = {"stage": "gate/up (routed + shared)", "kernel": kind,
+                              "launch_us": round(stage_us, 3), "achieved": round(ka, 3), "peak": peak,
+                              "unit": unit, "frac": round(ka / peak, 5),
+                              "algorithmic_ops_per_launch": int(gu_ops),
+                              "traffic": stored_traffic(w.name, kind, key=T),
+                              "timing": "HIP events around the stage inside eager steps"}
 
-    # ---- CPU oracle on a bounded sample of the same workload
+    # ---- CPU oracle on a bounded sample of the same workload: single thread
+    # and all of this process's host cores.  Each figure is the slope between
+    # two token counts, so the oracle's per-call weight quantisation (a fixed
+    # cost per call) drops out.
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        cores = max(1, min(16, os.cpu_count() or 1))
+        try:
+            ncpu = len(os.sched_getaffinity(0))
+        except AttributeError:
+            ncpu = os.cpu_count() or 1
+        cores = max(1, min(16, ncpu))
+        model = "unknown"
+        try:
+            for line in open("/proc/cpuinfo"):
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
         lw = wl.layer_weights(w, layer=0)
         xall = wl.tokens(w, step=0)
-        # grow the sample until it takes a quarter of the target time or
-        # covers the whole step (each call also quantises the weights, so the
-        # first, small sample overstates the per-token cost)
-        n = min(T, 16)
-        while True:
+
+        def run(n, threads):
             t1 = time.time()
             oracle.forward(xall[:n], lw.wr, lw.bias, lw.w_gu, lw.w_d, lw.ws_gu, lw.ws_d, k=w.k,
-                           wfmt=w.wfmt, nthreads=cores)
-            dt = time.time() - t1
-            if dt >= args.cpu_seconds / 4 or n >= T:
-                break
-            n = int(min(T, max(2 * n, n * args.cpu_seconds / max(dt, 1e-3))))
-        layers_per_step = w.layers if decode else 1
-        cpu = {"value": round(n / dt / layers_per_step, 2), "unit": "tokens/s", "cores": cores,
-               "kind": "oracle",
-               "sample": f"{n} of the {T} tokens of {w.name}, one layer, oracle.forward (includes its "
-                         f"per-call weight quantisation), {dt:.1f}s"
-                         + (f"; per-step rate = per-layer rate / {layers_per_step} layers" if decode else "")}
+                           wfmt=w.wfmt, nthreads=threads)
+            return time.time() - t1
 
-    total_ops = (ops["gateup"] + ops["down"] + ops["shared"]) * (w.layers if decode else 1)
+        def rate(threads, budget):
+            n1 = min(T, 8 if threads == 1 else 4 * threads)
+            t1 = run(n1, threads)
+            n2 = n1
+            while n2 < T:
+                n2 = min(T, max(2 * n2, int(n2 * budget / max(t1, 1e-3))))
+                t2 = run(n2, threads)
+                if t2 - t1 >= budget / 2 or n2 >= T:
+                    break
+            if n2 == n1:  # the whole workload in the first call
+                return n1 / t1, n1, t1
+            return (n2 - n1) / max(t2 - t1, 1e-9), n2, t2
+
+        r1, n1s, t1s = rate(1, args.cpu_seconds / 3)
+        rn, nns, tns = rate(cores, args.cpu_seconds / 3)
+        per = n_layers
+        cpu = {"value": round(rn / per, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+               "single_thread": round(r1 / per, 2), "cpu_model": model,
+               "sample": f"{w.name}, one layer of the oracle (oracle.forward, the plain C++ evaluation of "
+                         f"eq. (*)): rate = token-count slope between two calls (excludes the per-call "
+                         f"weight quantisation); {cores} threads up to {nns} tokens ({tns:.1f} s), one "
+                         f"thread up to {n1s} tokens ({t1s:.1f} s)"
+                         + (f"; per-step rate = per-layer rate / {per} layers" if per > 1 else "")}
+
     out = {
         "metric": "MoE-layer tokens/s (prefill T=2048/8192, decode B=1-64) + % HBM/MFMA peak",
         "value": round(tok_s, 2),
@@ -465,8 +543,6 @@ def main():
                    "path": "mm_moe_forward (one call)" if fused else "seven calls, shared expert on a second stream"},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "layer_int8_frac": round(total_ops / (ms * 1e-3) / 1e12 / INT8_MFMA_PEAK_TOPS, 5)
-        if w.wfmt == "int4g32" else None,
         "per_call_us": {c: round(v, 3) for c, v in per_call_us.items()},
         "distinct_experts_last_step": n_distinct,
     }

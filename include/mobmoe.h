@@ -337,6 +337,19 @@ mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
                          int32_t* topk_idx, float* topk_w, void* y, float* y_norm,
                          float norm_eps, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Measurement hook for benchmarks and profilers (not part of eq. (*)): with
+ * start and stop both non-NULL (hipEvent_t handles the caller created),
+ * every following mm_moe_forward records `start` on its stream right before
+ * the launch(es) of its gate/up product stage (the layer's largest product:
+ * routed and shared gate/up with SwiGLU, one merged launch where the layer
+ * uses one) and `stop` right after them, so the caller can time that stage
+ * inside the step with hipEventElapsedTime.  Both NULL switch it off.  The
+ * setting is process-wide; set it from one thread while no mm_moe_forward
+ * call is in flight.  Returns MM_ERR_NULL if exactly one is NULL.
+ */
+mm_status mm_set_profile_events(void* start, void* stop);
+
 /* --------------------------------------------------- around the layer */
 
 /*

@@ -35,7 +35,7 @@ EXPORTS = (
     "mm_attn_workspace_bytes", "mm_kv_append_i8", "mm_attn_decode_i8",
     "mm_bias_update", "mm_drop_pad_capacity", "mm_drop_pad", "mm_fake_quant",
     "mm_gather_rows", "mm_expert_train_forward_f32", "mm_expert_backward_workspace_bytes",
-    "mm_expert_backward_f32", "mm_router_backward_f32",
+    "mm_expert_backward_f32", "mm_router_backward_f32", "mm_set_profile_events",
 )
 
 
@@ -106,6 +106,7 @@ _SIGS = {
     "mm_expert_backward_workspace_bytes": ([_I64, _I32], _SZ),
     "mm_expert_backward_f32": ([_I32, _I32, _I32, _I64] + [_VP] * 11 + [_SZ, _VP], ctypes.c_int),
     "mm_router_backward_f32": ([_DESC, _I64] + [_VP] * 7 + [_F] + [_VP] * 4, ctypes.c_int),
+    "mm_set_profile_events": ([_VP, _VP], ctypes.c_int),
     "mm_moe_forward": ([_DESC, _I64, _VP, _VP, _VP, Weight, Weight, Weight, Weight, _VP, _VP, _VP,
                         _VP, _F, _VP, _SZ, _VP], ctypes.c_int),
 }
@@ -258,6 +259,19 @@ def moe_forward(ds, T, x, w_router, bias, w_gu, w_d, ws_gu, ws_d, topk_idx, topk
                                  w_d, ws_gu, ws_d, _ptr(topk_idx), _ptr(topk_w), _ptr(y),
                                  _ptr(y_norm), norm_eps, _ptr(ws), ws_bytes, _stream(stream)),
            "mm_moe_forward")
+
+
+def set_profile_events(start=None, stop=None):
+    """Events (torch.cuda.Event, created with enable_timing=True, or None)
+    that mm_moe_forward records around its gate/up product stage; None, None
+    switches the hook off."""
+    def handle(ev):
+        if ev is None:
+            return None
+        if not ev.cuda_event:  # torch creates the event on its first record
+            ev.record()
+        return ev.cuda_event
+    _check(load().mm_set_profile_events(handle(start), handle(stop)), "mm_set_profile_events")
 
 
 def linear_w4a8(rows, in_features, out_features, xq, sx, w, y, stream=None):

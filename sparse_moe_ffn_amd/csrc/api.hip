@@ -553,6 +553,16 @@ mm_status mm_combine(const mm_layer_desc* desc, int64_t T, const float* f,
                     "mm_combine");
 }
 
+static hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
+
+mm_status mm_set_profile_events(void* start, void* stop) {
+  if ((start == nullptr) != (stop == nullptr))
+    return fail(MM_ERR_NULL, "profile events: give both or neither");
+  g_prof_start = static_cast<hipEvent_t>(start);
+  g_prof_stop = static_cast<hipEvent_t>(stop);
+  return MM_OK;
+}
+
 mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
                          const float* w_router, const float* bias, mm_weight w_gateup,
                          mm_weight w_down, mm_weight ws_gateup, mm_weight ws_down,
@@ -653,6 +663,7 @@ mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
     float* s_s = static_cast<float*>(at(W.s_s));
     // gate/up (+ SwiGLU) of both kinds, then their hidden-row quantisers
     // (weight-streaming down of both kinds: the down workgroups quantise)
+    if (g_prof_start) MM_TRY(hip_status(hipEventRecord(g_prof_start, st), where));
     if (shared && gv) {
       MM_TRY(hip_status(mm::launch_gateup_i4_gemv_pair(ar, as, xq, sx, gq, w_gateup.scales, sgq,
                                                        ws_gateup.scales, a_r, a_s, st), where));
@@ -665,6 +676,7 @@ mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
         MM_TRY(hip_status(gateup_i4(as, xq, sx, sgq, ws_gateup.scales, a_s, q_s, s_s, nullptr, st),
                           where));
     }
+    if (g_prof_stop) MM_TRY(hip_status(hipEventRecord(g_prof_stop, st), where));
     if (quant_pair)
       MM_TRY(hip_status(mm::launch_act_quant_i8_pair(Tk, h, a_r, q_r, s_r, T, hs, a_s, q_s, s_s, st,
                                                      dn_mfma_pair), where));
@@ -688,11 +700,13 @@ mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
     uint16_t* h_r = static_cast<uint16_t*>(at(W.a_r));
     uint16_t* h_s = static_cast<uint16_t*>(at(W.a_s));
     MM_TRY(hip_status(mm::launch_convert_bf16(T * d, x, xb, st), where));
+    if (g_prof_start) MM_TRY(hip_status(hipEventRecord(g_prof_start, st), where));
     MM_TRY(hip_status(mm::launch_gateup_bf16_mfma(ar, xb, static_cast<const uint16_t*>(w_gateup.data),
                                                   h_r, st), where));
     if (shared)
       MM_TRY(hip_status(mm::launch_gateup_bf16_mfma(as, xb, static_cast<const uint16_t*>(ws_gateup.data),
                                                     h_s, st), where));
+    if (g_prof_stop) MM_TRY(hip_status(hipEventRecord(g_prof_stop, st), where));
     MM_TRY(hip_status(mm::launch_down_bf16_mfma(ar, h_r, static_cast<const uint16_t*>(w_down.data), f,
                                                 st), where));
     if (shared)
@@ -701,8 +715,10 @@ mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
   } else {
     void* h_r = at(W.a_r);
     void* h_s = at(W.a_s);
+    if (g_prof_start) MM_TRY(hip_status(hipEventRecord(g_prof_start, st), where));
     MM_TRY(hip_status(mm::launch_gateup_fp(ar, false, x, w_gateup.data, h_r, st), where));
     if (shared) MM_TRY(hip_status(mm::launch_gateup_fp(as, false, x, ws_gateup.data, h_s, st), where));
+    if (g_prof_stop) MM_TRY(hip_status(hipEventRecord(g_prof_stop, st), where));
     MM_TRY(hip_status(mm::launch_down_fp(ar, false, h_r, w_down.data, f, st), where));
     if (shared) MM_TRY(hip_status(mm::launch_down_fp(as, false, h_s, ws_down.data, ys, st), where));
   }

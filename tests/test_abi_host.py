@@ -271,3 +271,9 @@ def test_router_backward_checks(lib):
     ds = B.desc(768, 60, 384, 0, 4)
     assert rb(ctypes.byref(ds), 0, *(FAKE,) * 7, 1e-4, FAKE, FAKE, FAKE, None) == B.MM_ERR_SHAPE
     assert rb(ctypes.byref(ds), 8, *(FAKE,) * 7, 1e-4, FAKE, None, FAKE, None) == B.MM_ERR_NULL
+
+
+def test_profile_events_checks(lib):
+    assert lib.mm_set_profile_events(FAKE, None) == B.MM_ERR_NULL
+    assert lib.mm_set_profile_events(None, FAKE) == B.MM_ERR_NULL
+    assert lib.mm_set_profile_events(None, None) == B.MM_OK
