@@ -42,10 +42,12 @@ def parse():
                     help="distinct weight sets rotated across steps (0: enough to exceed the 256 MB MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="issue the calls eagerly instead of replaying graphs")
-    ap.add_argument("--path", choices=("auto", "fused", "calls"), default="auto",
-                    help="fused: the one-call layer (mm_moe_forward, one stream, fewest launches); "
+    ap.add_argument("--path", choices=("auto", "decode", "fused", "calls"), default="auto",
+                    help="decode: the layer as one kernel launch (mm_moe_decode, 1..4 tokens, INT4); "
+                         "fused: the one-call layer (mm_moe_forward, one stream, fewest launches); "
                          "calls: the seven calls with the activation quantiser and shared expert on "
-                         "a second stream; auto: fused (measured faster on every workload)")
+                         "a second stream; auto: decode where it applies, else fused (measured "
+                         "fastest on every workload)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
     ap.add_argument("--op", choices=("layer", "attn_decode", "linear", "train_step"), default="layer",
                     help="layer: the MoE-FFN layer (default); attn_decode: GQA decode attention "
@@ -232,15 +234,22 @@ def main():
     xs = [torch.from_numpy(wl.tokens(w, step=s)).to(dev) for s in range(n_inputs)]
     nxt = torch.empty((T, w.d), dtype=torch.float32, device=dev)
 
-    fused = args.path in ("fused", "auto")
+    one_launch = args.path in ("decode", "auto") and all(L.decode_supported(T) for L in layers)
+    if args.path == "decode" and not one_launch:
+        sys.exit(f"--path decode: no one-launch form for {w.name} at T={T}")
+    fused = args.path in ("fused", "auto") or one_launch
 
     def fwd(L, src):
+        if one_launch:
+            return L.forward_decode(src)
         return L.forward_fused(src) if fused else L.forward(src)
 
     def layer_then_norm(L, src, dst):
         """One stack layer: dst = RMSNorm(layer(src)) (the combine writes it on the
         one-call path, a separate kernel on the seven-call path)."""
-        if fused:
+        if one_launch:
+            L.forward_decode(src, y_norm=dst, norm_eps=1e-5)
+        elif fused:
             L.forward_fused(src, y_norm=dst, norm_eps=1e-5)
         else:
             y = L.forward(src)
@@ -386,17 +395,24 @@ def main():
     # fresh event pair per layer call, so the figure is that stage's time in
     # the step's own context (the same launches a kernel trace of the step
     # shows).
+    # On the one-launch path the stage is the whole layer: the events go
+    # around each layer's single launch.
     stage_us = None
     if fused:
         pairs = []
 
         def timed_fwd(L, src, dst=None):
             ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            B.set_profile_events(*ev)
-            if dst is not None:
-                L.forward_fused(src, y_norm=dst, norm_eps=1e-5)
+            if one_launch:
+                ev[0].record(st)
+                L.forward_decode(src, y_norm=dst, norm_eps=1e-5)
+                ev[1].record(st)
             else:
-                L.forward_fused(src)
+                B.set_profile_events(*ev)
+                if dst is not None:
+                    L.forward_fused(src, y_norm=dst, norm_eps=1e-5)
+                else:
+                    L.forward_fused(src)
             pairs.append(ev)
 
         for s in range(3):
@@ -439,7 +455,16 @@ def main():
                 "traffic": stored_traffic(w.name, "step", key=T),
                 "scope": "whole step (every launch of the layer stack)",
                 "algorithmic_bytes_per_step": int(step_bytes)}
-        if stage_us:
+        if stage_us and one_launch:
+            lb = step_bytes / n_layers
+            ka = lb / (stage_us * 1e-6) / 1e9
+            roof["kernel"] = {"stage": "whole layer (one launch)", "kernel": "k_decode_fused",
+                              "launch_us": round(stage_us, 3), "achieved": round(ka, 2),
+                              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ka / HBM_PEAK_GBS, 5),
+                              "algorithmic_bytes_per_launch": int(lb),
+                              "traffic": stored_traffic(w.name, "k_decode_fused", key=T),
+                              "timing": "HIP events around each layer's launch inside eager steps"}
+        elif stage_us:
             gu_bytes = n_distinct * 2 * w.h * w.d * wb_r + 2 * w.hs * w.d * wb_r
             ka = gu_bytes / (stage_us * 1e-6) / 1e9
             kind, path = kernel_of(w, T, True)
@@ -540,7 +565,9 @@ def main():
                    "experts": w.E, "top_k": w.k, "hidden": w.h, "shared_hidden": w.hs,
                    "weights": w.wfmt, "layers": w.layers, "router_bias": w.bias,
                    "weight_sets_rotated": n_inst, "parallelism": "single GPU",
-                   "path": "mm_moe_forward (one call)" if fused else "seven calls, shared expert on a second stream"},
+                   "path": ("mm_moe_decode (one launch per layer)" if one_launch else
+                            "mm_moe_forward (one call)" if fused else
+                            "seven calls, shared expert on a second stream")},
         "roofline": roof,
         "cpu_baseline": cpu,
         "per_call_us": {c: round(v, 3) for c, v in per_call_us.items()},

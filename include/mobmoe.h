@@ -93,7 +93,8 @@ enum {
   MM_WS_DOWN = 2,
   MM_WS_SHARED = 3,
   MM_WS_MAX = 4,     /* the largest of the above: one buffer serves every call */
-  MM_WS_FORWARD = 5  /* mm_moe_forward: every intermediate of the layer */
+  MM_WS_FORWARD = 5, /* mm_moe_forward: every intermediate of the layer */
+  MM_WS_DECODE = 6   /* mm_moe_decode: its state and intermediates (any T <= 4) */
 };
 
 typedef struct mm_layer_desc {
@@ -336,6 +337,38 @@ mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
                          mm_weight w_down, mm_weight ws_gateup, mm_weight ws_down,
                          int32_t* topk_idx, float* topk_w, void* y, float* y_norm,
                          float norm_eps, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * mm_moe_forward for a decode step of 1 to 4 tokens as ONE kernel launch
+ * (section "Runtime latency": a few tokens are bound by the selected experts'
+ * weight bytes, so the separate launches' dependency gaps dominate; section
+ * "Custom MoE kernel", principle (2): the layer's steps fused).  Arguments,
+ * outputs and errors as mm_moe_forward, with the same arithmetic in the same
+ * order, so the results are bit-identical to it.  INT4 weights only
+ * (MM_ERR_FORMAT otherwise).  The launch's workgroups pass the routing,
+ * hidden rows and expert outputs to one another through `ws`, which holds a
+ * small state between calls:
+ *   ws / ws_bytes  mm_workspace_bytes(desc, T, MM_WS_DECODE), one size for
+ *                  every T <= 4.  Zero-fill it once before its first use;
+ *                  every call leaves it ready for the next.  Calls that
+ *                  share a ws must not overlap in time (same stream, or
+ *                  synchronised).  The uint32 at byte offset 16 counts waits
+ *                  inside the kernel that gave up (a call that raises it has
+ *                  undefined outputs); only the caller clears it.
+ * MM_ERR_SHAPE when mm_moe_decode_supported(desc, T) is 0; MM_ERR_HIP also
+ * when the device cannot hold every workgroup of the launch at once (the
+ * workgroups wait for one another).
+ */
+mm_status mm_moe_decode(const mm_layer_desc* desc, int64_t T, const float* x,
+                        const float* w_router, const float* bias, mm_weight w_gateup,
+                        mm_weight w_down, mm_weight ws_gateup, mm_weight ws_down,
+                        int32_t* topk_idx, float* topk_w, void* y, float* y_norm,
+                        float norm_eps, void* ws, size_t ws_bytes, void* stream);
+
+/* 1 if mm_moe_decode has a form for this layer and T (INT4 weights,
+ * 1 <= T <= 4, d % 128 == 0 and d <= 1280, h and h_s (or h_s = 0) multiples
+ * of 128 up to 2560, and the weight-streaming products' limits), else 0. */
+int32_t mm_moe_decode_supported(const mm_layer_desc* desc, int64_t T);
 
 /*
  * Measurement hook for benchmarks and profilers (not part of eq. (*)): with

@@ -19,7 +19,7 @@ MM_OK, MM_ERR_NULL, MM_ERR_SHAPE, MM_ERR_ALIGN, MM_ERR_FORMAT, MM_ERR_WORKSPACE,
 MM_W_F32, MM_W_INT4G32, MM_W_BF16 = range(3)
 MM_GATE_SOFTMAX, MM_GATE_SIGMOID_NORM, MM_GATE_BIAS_SELECT_ONLY = 0, 1, 2
 MM_OUT_F32, MM_OUT_BF16 = range(2)
-MM_WS_ROUTE, MM_WS_GATEUP, MM_WS_DOWN, MM_WS_SHARED, MM_WS_MAX, MM_WS_FORWARD = range(6)
+MM_WS_ROUTE, MM_WS_GATEUP, MM_WS_DOWN, MM_WS_SHARED, MM_WS_MAX, MM_WS_FORWARD, MM_WS_DECODE = range(7)
 MM_ACT_ROW_MAJOR, MM_ACT_GROUP_MAJOR = range(2)
 
 WFMT = {"f32": MM_W_F32, "int4g32": MM_W_INT4G32, "bf16": MM_W_BF16}
@@ -36,6 +36,7 @@ EXPORTS = (
     "mm_bias_update", "mm_drop_pad_capacity", "mm_drop_pad", "mm_fake_quant",
     "mm_gather_rows", "mm_expert_train_forward_f32", "mm_expert_backward_workspace_bytes",
     "mm_expert_backward_f32", "mm_router_backward_f32", "mm_set_profile_events",
+    "mm_moe_decode", "mm_moe_decode_supported",
 )
 
 
@@ -109,6 +110,9 @@ _SIGS = {
     "mm_set_profile_events": ([_VP, _VP], ctypes.c_int),
     "mm_moe_forward": ([_DESC, _I64, _VP, _VP, _VP, Weight, Weight, Weight, Weight, _VP, _VP, _VP,
                         _VP, _F, _VP, _SZ, _VP], ctypes.c_int),
+    "mm_moe_decode": ([_DESC, _I64, _VP, _VP, _VP, Weight, Weight, Weight, Weight, _VP, _VP, _VP,
+                       _VP, _F, _VP, _SZ, _VP], ctypes.c_int),
+    "mm_moe_decode_supported": ([_DESC, _I64], _I32),
 }
 
 _lib = None
@@ -259,6 +263,21 @@ def moe_forward(ds, T, x, w_router, bias, w_gu, w_d, ws_gu, ws_d, topk_idx, topk
                                  w_d, ws_gu, ws_d, _ptr(topk_idx), _ptr(topk_w), _ptr(y),
                                  _ptr(y_norm), norm_eps, _ptr(ws), ws_bytes, _stream(stream)),
            "mm_moe_forward")
+
+
+def moe_decode(ds, T, x, w_router, bias, w_gu, w_d, ws_gu, ws_d, topk_idx, topk_w, y, ws,
+               ws_bytes, stream=None, y_norm=None, norm_eps=0.0):
+    """moe_forward for 1..4 tokens as one kernel launch.  ws
+    (workspace_bytes(ds, T, MM_WS_DECODE)) holds state between calls: zero it
+    once before the first call; calls sharing it must not overlap."""
+    _check(load().mm_moe_decode(ctypes.byref(ds), T, _ptr(x), _ptr(w_router), _ptr(bias), w_gu,
+                                w_d, ws_gu, ws_d, _ptr(topk_idx), _ptr(topk_w), _ptr(y),
+                                _ptr(y_norm), norm_eps, _ptr(ws), ws_bytes, _stream(stream)),
+           "mm_moe_decode")
+
+
+def moe_decode_supported(ds, T) -> bool:
+    return bool(load().mm_moe_decode_supported(ctypes.byref(ds), T))
 
 
 def set_profile_events(start=None, stop=None):

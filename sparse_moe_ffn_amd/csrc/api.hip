@@ -131,6 +131,34 @@ FwdWs fwd_ws(const mm_layer_desc* d, int64_t T) {
   return w;
 }
 
+// mm_moe_decode workspace carve-up: the state block first, then the
+// intermediates sized for 4 tokens (the same layout serves every T <= 4).
+constexpr int64_t kDecodeMaxT = 4;
+struct DecWs {
+  size_t state, a_r, a_s, f, ys, total;
+};
+DecWs dec_ws(const mm_layer_desc* d) {
+  const int64_t T = kDecodeMaxT, Tk = T * d->top_k, dm = d->d_model;
+  DecWs w{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  w.state = take(mm::decode_fused_state_bytes());
+  w.a_r = take((size_t)Tk * d->hidden * 4);
+  w.a_s = take((size_t)T * d->shared_hidden * 4);
+  w.f = take((size_t)Tk * dm * 4);
+  w.ys = take((size_t)T * dm * 4);
+  w.total = o;
+  return w;
+}
+bool decode_applies(const mm_layer_desc* d, int64_t T) {
+  return d->wfmt == MM_W_INT4G32 &&
+         mm::decode_fused_fits(T, d->d_model, d->n_experts, d->top_k, d->hidden, d->shared_hidden);
+}
+
 size_t ws_bytes(const mm_layer_desc* d, int64_t T, int32_t which) {
   const int64_t Tk = T * d->top_k;
   switch (which) {
@@ -151,6 +179,8 @@ size_t ws_bytes(const mm_layer_desc* d, int64_t T, int32_t which) {
     }
     case MM_WS_FORWARD:
       return fwd_ws(d, T).total;
+    case MM_WS_DECODE:
+      return decode_applies(d, std::max<int64_t>(T, 1)) ? dec_ws(d).total : 0;
     default:
       return 0;
   }
@@ -725,6 +755,81 @@ mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
   return hip_status(mm::launch_combine(T, d, k, f, inv, topk_w, ys, y,
                                        desc->out_dtype == MM_OUT_BF16, st, y_norm, norm_eps),
                     where);
+}
+
+int32_t mm_moe_decode_supported(const mm_layer_desc* desc, int64_t T) {
+  if (check_desc(desc) != MM_OK) return 0;
+  return decode_applies(desc, T) ? 1 : 0;
+}
+
+mm_status mm_moe_decode(const mm_layer_desc* desc, int64_t T, const float* x,
+                        const float* w_router, const float* bias, mm_weight w_gateup,
+                        mm_weight w_down, mm_weight ws_gateup, mm_weight ws_down,
+                        int32_t* topk_idx, float* topk_w, void* y, float* y_norm, float norm_eps,
+                        void* ws, size_t ws_size, void* stream) {
+  MM_TRY(check_desc(desc));
+  if (T < 0) return fail(MM_ERR_SHAPE, "T %lld is negative", (long long)T);
+  if (T == 0) return MM_OK;
+  if (desc->wfmt != MM_W_INT4G32) return fail(MM_ERR_FORMAT, "mm_moe_decode needs INT4 weights");
+  if (!decode_applies(desc, T))
+    return fail(MM_ERR_SHAPE,
+                "mm_moe_decode: no one-launch form for T=%lld d=%d h=%d h_s=%d (T <= 4, d %% 128 == 0, "
+                "d <= 1280, h and h_s multiples of 128 up to 2560)",
+                (long long)T, desc->d_model, desc->hidden, desc->shared_hidden);
+  MM_REQUIRE(x);
+  MM_REQUIRE(w_router);
+  MM_OPTIONAL(bias);
+  MM_REQUIRE(topk_idx);
+  MM_REQUIRE(topk_w);
+  MM_REQUIRE(y);
+  MM_OPTIONAL(y_norm);
+  if (y_norm && desc->out_dtype != MM_OUT_F32)
+    return fail(MM_ERR_FORMAT, "y_norm needs FP32 output");
+  if (y_norm && !(norm_eps > 0.0f)) return fail(MM_ERR_SHAPE, "norm_eps must be positive");
+  MM_REQUIRE(ws);
+  MM_TRY(check_weight(desc, w_gateup, "w_gateup"));
+  MM_TRY(check_weight(desc, w_down, "w_down"));
+  const bool shared = desc->shared_hidden > 0;
+  if (shared) {
+    MM_TRY(check_weight(desc, ws_gateup, "ws_gateup"));
+    MM_TRY(check_weight(desc, ws_down, "ws_down"));
+  }
+  const DecWs W = dec_ws(desc);
+  if (ws_size < W.total)
+    return fail(MM_ERR_WORKSPACE, "decode workspace too small (need %lld bytes)", (long long)W.total);
+  char* base = static_cast<char*>(ws);
+  mm::DecodeFusedArgs a{};
+  a.T = T;
+  a.d = desc->d_model;
+  a.E = desc->n_experts;
+  a.k = desc->top_k;
+  a.h = desc->hidden;
+  a.hs = desc->shared_hidden;
+  a.gating = desc->gating;
+  a.x = x;
+  a.wr = w_router;
+  a.bias = bias;
+  a.gq = static_cast<const uint8_t*>(w_gateup.data);
+  a.gs = w_gateup.scales;
+  a.dq = static_cast<const uint8_t*>(w_down.data);
+  a.ds = w_down.scales;
+  a.sgq = shared ? static_cast<const uint8_t*>(ws_gateup.data) : nullptr;
+  a.sgs = shared ? ws_gateup.scales : nullptr;
+  a.sdq = shared ? static_cast<const uint8_t*>(ws_down.data) : nullptr;
+  a.sds = shared ? ws_down.scales : nullptr;
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  a.y = y;
+  a.y_norm = y_norm;
+  a.eps = norm_eps;
+  a.out_bf16 = desc->out_dtype == MM_OUT_BF16;
+  a.state = base + W.state;
+  a.a_r = reinterpret_cast<float*>(base + W.a_r);
+  a.a_s = reinterpret_cast<float*>(base + W.a_s);
+  a.f = reinterpret_cast<float*>(base + W.f);
+  a.ys = reinterpret_cast<float*>(base + W.ys);
+  a.spin_limit = 1u << 20;
+  return hip_status(mm::launch_decode_fused(a, S(stream)), "mm_moe_decode");
 }
 
 mm_status mm_linear_w4a8(int64_t rows, int64_t in_features, int64_t out_features,

@@ -160,6 +160,43 @@ hipError_t launch_combine(int64_t T, int d, int k, const float* f, const int32_t
                           const float* w, const float* ys, void* y, bool bf16_out,
                           hipStream_t st, float* y_norm = nullptr, float eps = 0.0f);
 
+// The whole layer for 1..4 tokens in one launch (k_decode.hip), INT4
+// weights; the same outputs as the separate launches.  state: a zeroed block
+// of decode_fused_state_bytes() (counters + logit table) that each call leaves
+// zeroed (word 4 excepted: it counts waits that gave up).  grid_out: the
+// launched workgroup count.  hipErrorInvalidConfiguration if the grid cannot
+// be resident at once.
+struct DecodeFusedArgs {
+  int64_t T;
+  int d, E, k, h, hs, gating;
+  const float* x;
+  const float* wr;
+  const float* bias;
+  const uint8_t* gq;
+  const float* gs;
+  const uint8_t* dq;
+  const float* ds;
+  const uint8_t* sgq;
+  const float* sgs;
+  const uint8_t* sdq;
+  const float* sds;
+  int32_t* topk_idx;
+  float* topk_w;
+  void* y;
+  float* y_norm;
+  float eps;
+  bool out_bf16;
+  void* state;
+  float* a_r;
+  float* a_s;
+  float* f;
+  float* ys;
+  uint32_t spin_limit;
+};
+bool decode_fused_fits(int64_t T, int d, int E, int k, int h, int hs);
+size_t decode_fused_state_bytes();
+hipError_t launch_decode_fused(const DecodeFusedArgs& a, hipStream_t st, int* grid_out = nullptr);
+
 // Decode attention over an INT8 KV cache (k_attn.hip).  Head width 64, up
 // to 8 query heads per key/value head.
 size_t attn_partial_bytes(int64_t B, int nkv, int64_t max_len);

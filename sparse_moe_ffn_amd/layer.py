@@ -205,6 +205,33 @@ class MoELayer:
                       y_norm=y_norm, norm_eps=norm_eps if y_norm is not None else 0.0)
         return self.y
 
+    def decode_supported(self, T: int) -> bool:
+        """True when forward_decode has a one-launch form for T tokens."""
+        return B.moe_decode_supported(self.desc, T)
+
+    def forward_decode(self, x: torch.Tensor, y_norm: Optional[torch.Tensor] = None,
+                       norm_eps: float = 1e-5) -> torch.Tensor:
+        """forward_fused for 1..4 tokens as ONE kernel launch (mm_moe_decode):
+        bit-identical results.  The layer keeps the call's state buffer
+        (zeroed once here, left zeroed by every call)."""
+        T = x.shape[0]
+        self.buffers(T)
+        if getattr(self, "wk_dec", None) is None:
+            self.wk_dec_bytes = max(B.workspace_bytes(self.desc, 4, B.MM_WS_DECODE), 256)
+            self.wk_dec = torch.zeros((self.wk_dec_bytes,), dtype=torch.uint8, device=self.device)
+        none = B.weight(None, None)
+        B.moe_decode(self.desc, T, x, self.wr, self.bias, self.w_gu.c(), self.w_d.c(),
+                     self.ws_gu.c() if self.hs else none, self.ws_d.c() if self.hs else none,
+                     self.idx, self.topw, self.y, self.wk_dec, self.wk_dec_bytes,
+                     y_norm=y_norm, norm_eps=norm_eps if y_norm is not None else 0.0)
+        return self.y
+
+    def decode_status(self) -> int:
+        """Waits inside mm_moe_decode that gave up so far (0 when healthy)."""
+        if getattr(self, "wk_dec", None) is None:
+            return 0
+        return int(self.wk_dec[16:20].view(torch.int32).item())
+
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         """y = eq. (*) of x [T, d] FP32 (device).  Returns the layer's y buffer."""
         T = x.shape[0]

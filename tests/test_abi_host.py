@@ -22,7 +22,7 @@ def lib():
 
 def header_symbols():
     src = open(os.path.join(ROOT, "include", "mobmoe.h")).read()
-    return set(re.findall(r"^(?:mm_status|const char\*|size_t|int64_t)\s+(mm_\w+)\(", src, re.M))
+    return set(re.findall(r"^(?:mm_status|const char\*|size_t|int64_t|int32_t)\s+(mm_\w+)\(", src, re.M))
 
 
 def test_header_and_binding_agree():
@@ -166,6 +166,40 @@ def test_forward_checks(lib):
     noshared = B.desc(768, 60, 384, 0, 4)
     zero = B.Weight(None, None)
     assert B.workspace_bytes(noshared, 2048, B.MM_WS_FORWARD) < need
+
+
+def test_decode_checks(lib):
+    """mm_moe_decode: the one-launch form's limits and every argument check
+    happen on the host before the launch."""
+    ds = S()
+    w = B.Weight(FAKE, FAKE)
+    for T in (1, 2, 3, 4):
+        assert B.moe_decode_supported(ds, T)
+    assert not B.moe_decode_supported(ds, 5) and not B.moe_decode_supported(ds, 0)
+    need = B.workspace_bytes(ds, 1, B.MM_WS_DECODE)
+    # one size for every T <= 4: state + routed rows/outputs for 4 tokens
+    assert need == B.workspace_bytes(ds, 4, B.MM_WS_DECODE)
+    assert need >= 4 * 4 * (384 + 768) * 4 + 4 * (1536 + 768) * 4
+    assert B.workspace_bytes(ds, 5, B.MM_WS_DECODE) == 0
+    args = lambda T, ws_bytes, y_norm=None, eps=0.0, d=ds, wt=w: (
+        ctypes.byref(d), T, FAKE, FAKE, None, wt, wt, wt, wt, FAKE, FAKE, FAKE, y_norm, eps, FAKE,
+        ws_bytes, None)
+    assert lib.mm_moe_decode(*args(1, need - 1)) == B.MM_ERR_WORKSPACE
+    assert lib.mm_moe_decode(*args(5, need)) == B.MM_ERR_SHAPE
+    assert lib.mm_moe_decode(*args(-1, need)) == B.MM_ERR_SHAPE
+    assert lib.mm_moe_decode(*args(0, need)) == B.MM_OK
+    assert lib.mm_moe_decode(*args(2, need, FAKE, 0.0)) == B.MM_ERR_SHAPE  # eps must be positive
+    bf = B.desc(768, 60, 384, 1536, 4, "bf16")
+    assert lib.mm_moe_decode(*args(2, need, d=bf, wt=B.Weight(FAKE, None))) == B.MM_ERR_FORMAT
+    assert not B.moe_decode_supported(bf, 1)
+    wide = B.desc(1536, 60, 768, 3072, 4)  # d beyond the one-launch router's 1280
+    assert not B.moe_decode_supported(wide, 1)
+    odd = B.desc(704, 60, 320, 640, 4)     # d % 128 != 0
+    assert not B.moe_decode_supported(odd, 1)
+    assert lib.mm_moe_decode(*args(1, need, d=odd)) == B.MM_ERR_SHAPE
+    unaligned = FAKE + 4
+    assert lib.mm_moe_decode(ctypes.byref(ds), 1, unaligned, FAKE, None, w, w, w, w, FAKE, FAKE,
+                             FAKE, None, 0.0, FAKE, need, None) == B.MM_ERR_ALIGN
 
 
 def test_layout_and_pair_checks(lib):
