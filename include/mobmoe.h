@@ -365,6 +365,26 @@ mm_status mm_moe_decode(const mm_layer_desc* desc, int64_t T, const float* x,
                         int32_t* topk_idx, float* topk_w, void* y, float* y_norm,
                         float norm_eps, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * mm_moe_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without ws / ws_bytes, the same checks and bit-identical
+ * results.  Its state and intermediates live in a fixed device array of
+ * 512 KiB inside the library, one per GPU, held until the process ends; the
+ * call allocates nothing.  The first call on a GPU looks the array up and
+ * queues one small kernel on `stream` that clears its state block; every call
+ * leaves it cleared.  All calls on one GPU share that array: calls that
+ * overlap in time on one GPU (other streams, other threads) race and give
+ * undefined results.  MM_ERR_WORKSPACE when the layer needs more than the
+ * array holds (4 tokens' rows: 4*k*(h + d) + 4*(h_s + d) floats plus 1280
+ * bytes of state, each part rounded up to 256 bytes).
+ */
+mm_status mm_moe_decode_noalloc(const mm_layer_desc* desc, int64_t T, const float* x,
+                                const float* w_router, const float* bias, mm_weight w_gateup,
+                                mm_weight w_down, mm_weight ws_gateup, mm_weight ws_down,
+                                int32_t* topk_idx, float* topk_w, void* y, float* y_norm,
+                                float norm_eps, void* stream);
+
 /* 1 if mm_moe_decode has a form for this layer and T (INT4 weights,
  * 1 <= T <= 4, d % 128 == 0 and d <= 1280, h and h_s (or h_s = 0) multiples
  * of 128 up to 2560, and the weight-streaming products' limits), else 0. */

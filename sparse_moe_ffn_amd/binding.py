@@ -36,7 +36,7 @@ EXPORTS = (
     "mm_bias_update", "mm_drop_pad_capacity", "mm_drop_pad", "mm_fake_quant",
     "mm_gather_rows", "mm_expert_train_forward_f32", "mm_expert_backward_workspace_bytes",
     "mm_expert_backward_f32", "mm_router_backward_f32", "mm_set_profile_events",
-    "mm_moe_decode", "mm_moe_decode_supported",
+    "mm_moe_decode", "mm_moe_decode_supported", "mm_moe_decode_noalloc",
 )
 
 
@@ -113,6 +113,8 @@ _SIGS = {
     "mm_moe_decode": ([_DESC, _I64, _VP, _VP, _VP, Weight, Weight, Weight, Weight, _VP, _VP, _VP,
                        _VP, _F, _VP, _SZ, _VP], ctypes.c_int),
     "mm_moe_decode_supported": ([_DESC, _I64], _I32),
+    "mm_moe_decode_noalloc": ([_DESC, _I64, _VP, _VP, _VP, Weight, Weight, Weight, Weight, _VP, _VP,
+                               _VP, _VP, _F, _VP], ctypes.c_int),
 }
 
 _lib = None
@@ -274,6 +276,16 @@ def moe_decode(ds, T, x, w_router, bias, w_gu, w_d, ws_gu, ws_d, topk_idx, topk_
                                 w_d, ws_gu, ws_d, _ptr(topk_idx), _ptr(topk_w), _ptr(y),
                                 _ptr(y_norm), norm_eps, _ptr(ws), ws_bytes, _stream(stream)),
            "mm_moe_decode")
+
+
+def moe_decode_noalloc(ds, T, x, w_router, bias, w_gu, w_d, ws_gu, ws_d, topk_idx, topk_w, y,
+                       stream=None, y_norm=None, norm_eps=0.0):
+    """moe_decode without a workspace: the library's fixed device scratch
+    (one per GPU, shared by every call on it; calls must not overlap)."""
+    _check(load().mm_moe_decode_noalloc(ctypes.byref(ds), T, _ptr(x), _ptr(w_router), _ptr(bias),
+                                        w_gu, w_d, ws_gu, ws_d, _ptr(topk_idx), _ptr(topk_w),
+                                        _ptr(y), _ptr(y_norm), norm_eps, _stream(stream)),
+           "mm_moe_decode_noalloc")
 
 
 def moe_decode_supported(ds, T) -> bool:

@@ -247,6 +247,81 @@ hipError_t down_i4(const mm::ExpertArgs& a, const int8_t* hq, const float* hs,
 
 }  // namespace
 
+namespace {
+
+// mm_moe_decode and mm_moe_decode_noalloc: every check, then the launch on
+// the workspace from get_ws(needed bytes, &base) (called after the checks).
+template <class GetWs>
+mm_status moe_decode_impl(const char* where, const mm_layer_desc* desc, int64_t T, const float* x,
+                          const float* w_router, const float* bias, mm_weight w_gateup,
+                          mm_weight w_down, mm_weight ws_gateup, mm_weight ws_down,
+                          int32_t* topk_idx, float* topk_w, void* y, float* y_norm, float norm_eps,
+                          void* stream, const GetWs& get_ws) {
+  MM_TRY(check_desc(desc));
+  if (T < 0) return fail(MM_ERR_SHAPE, "T %lld is negative", (long long)T);
+  if (T == 0) return MM_OK;
+  if (desc->wfmt != MM_W_INT4G32) return fail(MM_ERR_FORMAT, "%s needs INT4 weights", where);
+  if (!decode_applies(desc, T))
+    return fail(MM_ERR_SHAPE,
+                "%s: no one-launch form for T=%lld d=%d h=%d h_s=%d (T <= 4, d %% 128 == 0, "
+                "d <= 1280, h and h_s multiples of 128 up to 2560)",
+                where, (long long)T, desc->d_model, desc->hidden, desc->shared_hidden);
+  MM_REQUIRE(x);
+  MM_REQUIRE(w_router);
+  MM_OPTIONAL(bias);
+  MM_REQUIRE(topk_idx);
+  MM_REQUIRE(topk_w);
+  MM_REQUIRE(y);
+  MM_OPTIONAL(y_norm);
+  if (y_norm && desc->out_dtype != MM_OUT_F32)
+    return fail(MM_ERR_FORMAT, "y_norm needs FP32 output");
+  if (y_norm && !(norm_eps > 0.0f)) return fail(MM_ERR_SHAPE, "norm_eps must be positive");
+  MM_TRY(check_weight(desc, w_gateup, "w_gateup"));
+  MM_TRY(check_weight(desc, w_down, "w_down"));
+  const bool shared = desc->shared_hidden > 0;
+  if (shared) {
+    MM_TRY(check_weight(desc, ws_gateup, "ws_gateup"));
+    MM_TRY(check_weight(desc, ws_down, "ws_down"));
+  }
+  const DecWs W = dec_ws(desc);
+  char* base = nullptr;
+  MM_TRY(get_ws(W.total, &base));
+  mm::DecodeFusedArgs a{};
+  a.T = T;
+  a.d = desc->d_model;
+  a.E = desc->n_experts;
+  a.k = desc->top_k;
+  a.h = desc->hidden;
+  a.hs = desc->shared_hidden;
+  a.gating = desc->gating;
+  a.x = x;
+  a.wr = w_router;
+  a.bias = bias;
+  a.gq = static_cast<const uint8_t*>(w_gateup.data);
+  a.gs = w_gateup.scales;
+  a.dq = static_cast<const uint8_t*>(w_down.data);
+  a.ds = w_down.scales;
+  a.sgq = shared ? static_cast<const uint8_t*>(ws_gateup.data) : nullptr;
+  a.sgs = shared ? ws_gateup.scales : nullptr;
+  a.sdq = shared ? static_cast<const uint8_t*>(ws_down.data) : nullptr;
+  a.sds = shared ? ws_down.scales : nullptr;
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  a.y = y;
+  a.y_norm = y_norm;
+  a.eps = norm_eps;
+  a.out_bf16 = desc->out_dtype == MM_OUT_BF16;
+  a.state = base + W.state;
+  a.a_r = reinterpret_cast<float*>(base + W.a_r);
+  a.a_s = reinterpret_cast<float*>(base + W.a_s);
+  a.f = reinterpret_cast<float*>(base + W.f);
+  a.ys = reinterpret_cast<float*>(base + W.ys);
+  a.spin_limit = 1u << 20;
+  return hip_status(mm::launch_decode_fused(a, S(stream)), where);
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* mm_version(void) { return "libmobmoe 0.1 (gfx950)"; }
@@ -767,69 +842,35 @@ mm_status mm_moe_decode(const mm_layer_desc* desc, int64_t T, const float* x,
                         mm_weight w_down, mm_weight ws_gateup, mm_weight ws_down,
                         int32_t* topk_idx, float* topk_w, void* y, float* y_norm, float norm_eps,
                         void* ws, size_t ws_size, void* stream) {
-  MM_TRY(check_desc(desc));
-  if (T < 0) return fail(MM_ERR_SHAPE, "T %lld is negative", (long long)T);
-  if (T == 0) return MM_OK;
-  if (desc->wfmt != MM_W_INT4G32) return fail(MM_ERR_FORMAT, "mm_moe_decode needs INT4 weights");
-  if (!decode_applies(desc, T))
-    return fail(MM_ERR_SHAPE,
-                "mm_moe_decode: no one-launch form for T=%lld d=%d h=%d h_s=%d (T <= 4, d %% 128 == 0, "
-                "d <= 1280, h and h_s multiples of 128 up to 2560)",
-                (long long)T, desc->d_model, desc->hidden, desc->shared_hidden);
-  MM_REQUIRE(x);
-  MM_REQUIRE(w_router);
-  MM_OPTIONAL(bias);
-  MM_REQUIRE(topk_idx);
-  MM_REQUIRE(topk_w);
-  MM_REQUIRE(y);
-  MM_OPTIONAL(y_norm);
-  if (y_norm && desc->out_dtype != MM_OUT_F32)
-    return fail(MM_ERR_FORMAT, "y_norm needs FP32 output");
-  if (y_norm && !(norm_eps > 0.0f)) return fail(MM_ERR_SHAPE, "norm_eps must be positive");
-  MM_REQUIRE(ws);
-  MM_TRY(check_weight(desc, w_gateup, "w_gateup"));
-  MM_TRY(check_weight(desc, w_down, "w_down"));
-  const bool shared = desc->shared_hidden > 0;
-  if (shared) {
-    MM_TRY(check_weight(desc, ws_gateup, "ws_gateup"));
-    MM_TRY(check_weight(desc, ws_down, "ws_down"));
-  }
-  const DecWs W = dec_ws(desc);
-  if (ws_size < W.total)
-    return fail(MM_ERR_WORKSPACE, "decode workspace too small (need %lld bytes)", (long long)W.total);
-  char* base = static_cast<char*>(ws);
-  mm::DecodeFusedArgs a{};
-  a.T = T;
-  a.d = desc->d_model;
-  a.E = desc->n_experts;
-  a.k = desc->top_k;
-  a.h = desc->hidden;
-  a.hs = desc->shared_hidden;
-  a.gating = desc->gating;
-  a.x = x;
-  a.wr = w_router;
-  a.bias = bias;
-  a.gq = static_cast<const uint8_t*>(w_gateup.data);
-  a.gs = w_gateup.scales;
-  a.dq = static_cast<const uint8_t*>(w_down.data);
-  a.ds = w_down.scales;
-  a.sgq = shared ? static_cast<const uint8_t*>(ws_gateup.data) : nullptr;
-  a.sgs = shared ? ws_gateup.scales : nullptr;
-  a.sdq = shared ? static_cast<const uint8_t*>(ws_down.data) : nullptr;
-  a.sds = shared ? ws_down.scales : nullptr;
-  a.topk_idx = topk_idx;
-  a.topk_w = topk_w;
-  a.y = y;
-  a.y_norm = y_norm;
-  a.eps = norm_eps;
-  a.out_bf16 = desc->out_dtype == MM_OUT_BF16;
-  a.state = base + W.state;
-  a.a_r = reinterpret_cast<float*>(base + W.a_r);
-  a.a_s = reinterpret_cast<float*>(base + W.a_s);
-  a.f = reinterpret_cast<float*>(base + W.f);
-  a.ys = reinterpret_cast<float*>(base + W.ys);
-  a.spin_limit = 1u << 20;
-  return hip_status(mm::launch_decode_fused(a, S(stream)), "mm_moe_decode");
+  auto get_ws = [&](size_t need, char** base) -> mm_status {
+    MM_REQUIRE(ws);
+    if (ws_size < need)
+      return fail(MM_ERR_WORKSPACE, "decode workspace too small (need %lld bytes)", (long long)need);
+    *base = static_cast<char*>(ws);
+    return MM_OK;
+  };
+  return moe_decode_impl("mm_moe_decode", desc, T, x, w_router, bias, w_gateup, w_down, ws_gateup,
+                         ws_down, topk_idx, topk_w, y, y_norm, norm_eps, stream, get_ws);
+}
+
+mm_status mm_moe_decode_noalloc(const mm_layer_desc* desc, int64_t T, const float* x,
+                                const float* w_router, const float* bias, mm_weight w_gateup,
+                                mm_weight w_down, mm_weight ws_gateup, mm_weight ws_down,
+                                int32_t* topk_idx, float* topk_w, void* y, float* y_norm,
+                                float norm_eps, void* stream) {
+  auto get_ws = [&](size_t need, char** base) -> mm_status {
+    if (need > mm::decode_scratch_capacity())
+      return fail(MM_ERR_WORKSPACE,
+                  "mm_moe_decode_noalloc: the layer needs %lld bytes of scratch, the fixed "
+                  "device scratch holds %lld (use mm_moe_decode with a workspace)",
+                  (long long)need, (long long)mm::decode_scratch_capacity());
+    void* p = nullptr;
+    MM_TRY(hip_status(mm::decode_scratch(&p, S(stream)), "mm_moe_decode_noalloc"));
+    *base = static_cast<char*>(p);
+    return MM_OK;
+  };
+  return moe_decode_impl("mm_moe_decode_noalloc", desc, T, x, w_router, bias, w_gateup, w_down,
+                         ws_gateup, ws_down, topk_idx, topk_w, y, y_norm, norm_eps, stream, get_ws);
 }
 
 mm_status mm_linear_w4a8(int64_t rows, int64_t in_features, int64_t out_features,

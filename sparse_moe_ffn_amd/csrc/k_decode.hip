@@ -367,6 +367,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 
 }  // namespace
 
+// Scratch of the no-allocation entry point (mm_moe_decode_noalloc): the
+// state block and intermediates of mm_moe_decode in a fixed device array,
+// for callers that cannot allocate.  Each device holds its own copy at its
+// own address (hipGetSymbolAddress once per device); in host code the name
+// is only a handle for that lookup.  Zero at load; cleared once more when a
+// device's address is first taken; every call leaves the counters zero.
+constexpr size_t kDecodeScratchBytes = size_t(512) << 10;
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+__global__ void k_clear_words(uint32_t* p, int n) {
+  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i < n) p[i] = 0u;
+}
+
+}  // namespace
+
+size_t decode_scratch_capacity() { return kDecodeScratchBytes; }
+
+hipError_t decode_scratch(void** out, hipStream_t st) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    // the state block starts at zero (a kernel, not a memset node: the call
+    // may be under stream capture)
+    const int words = (int)(decode_fused_state_bytes() / 4);
+    hipLaunchKernelGGL(k_clear_words, dim3((words + 255) / 256), dim3(256), 0, st,
+                       static_cast<uint32_t*>(p), words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
 bool decode_fused_fits(int64_t T, int d, int E, int k, int h, int hs) {
   return T >= 1 && T <= kDecMaxT && k >= 1 && k <= 8 && E >= 1 && E <= 64 && d % 128 == 0 &&
          d <= kWave * kRouterNX && h % 64 == 0 && hs % 64 == 0 && gemv_i4_fits(d, true) &&

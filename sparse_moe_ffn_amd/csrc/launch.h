@@ -196,6 +196,11 @@ struct DecodeFusedArgs {
 bool decode_fused_fits(int64_t T, int d, int E, int k, int h, int hs);
 size_t decode_fused_state_bytes();
 hipError_t launch_decode_fused(const DecodeFusedArgs& a, hipStream_t st, int* grid_out = nullptr);
+// The no-allocation form's device scratch (k_decode.hip): its size, and its
+// address on the current device (looked up, and its state block cleared on
+// stream st, at the first call per device).
+size_t decode_scratch_capacity();
+hipError_t decode_scratch(void** out, hipStream_t st);
 
 // Decode attention over an INT8 KV cache (k_attn.hip).  Head width 64, up
 // to 8 query heads per key/value head.

@@ -202,6 +202,26 @@ def test_decode_checks(lib):
                              FAKE, None, 0.0, FAKE, need, None) == B.MM_ERR_ALIGN
 
 
+def test_decode_noalloc_checks(lib):
+    """The no-allocation decode form: the checks of mm_moe_decode, and a layer
+    whose state and rows exceed the fixed 512 KiB device scratch is refused on
+    the host (before the scratch is looked up)."""
+    w = B.Weight(FAKE, FAKE)
+    args = lambda d, T: (ctypes.byref(d), T, FAKE, FAKE, None, w, w, w, w, FAKE, FAKE, FAKE, None,
+                         0.0, None)
+    big = B.desc(1280, 64, 2560, 2560, 8)  # 32 slots of 2560 + 1280 floats: over 512 KiB
+    assert B.moe_decode_supported(big, 4)
+    assert B.workspace_bytes(big, 4, B.MM_WS_DECODE) > 512 * 1024
+    assert lib.mm_moe_decode_noalloc(*args(big, 4)) == B.MM_ERR_WORKSPACE
+    assert b"512" in lib.mm_last_error_string() or b"524288" in lib.mm_last_error_string()
+    ds = S()
+    assert B.workspace_bytes(ds, 4, B.MM_WS_DECODE) <= 512 * 1024
+    assert lib.mm_moe_decode_noalloc(*args(ds, 5)) == B.MM_ERR_SHAPE
+    assert lib.mm_moe_decode_noalloc(*args(ds, 0)) == B.MM_OK
+    assert lib.mm_moe_decode_noalloc(ctypes.byref(ds), 1, None, FAKE, None, w, w, w, w, FAKE, FAKE,
+                                     FAKE, None, 0.0, None) == B.MM_ERR_NULL
+
+
 def test_layout_and_pair_checks(lib):
     """mm_act_quant_i8_layout and mm_expert_gateup_pair_f32 validate before any launch."""
     I32 = ctypes.c_int32
