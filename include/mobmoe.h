@@ -376,8 +376,8 @@ mm_status mm_moe_decode(const mm_layer_desc* desc, int64_t T, const float* x,
  * leaves it cleared.  All calls on one GPU share that array: calls that
  * overlap in time on one GPU (other streams, other threads) race and give
  * undefined results.  MM_ERR_WORKSPACE when the layer needs more than the
- * array holds (4 tokens' rows: 4*k*(h + d) + 4*(h_s + d) floats plus 1280
- * bytes of state, each part rounded up to 256 bytes).
+ * array holds (4 tokens' rows: 4*k*(h + d) + 4*(h_s + d) floats plus about
+ * 21 KB of state, each part rounded up to 256 bytes).
  */
 mm_status mm_moe_decode_noalloc(const mm_layer_desc* desc, int64_t T, const float* x,
                                 const float* w_router, const float* bias, mm_weight w_gateup,

@@ -146,11 +146,12 @@ DecWs dec_ws(const mm_layer_desc* d) {
     o += align256(bytes);
     return at;
   };
+  // the hand-off buffers hold 8 bytes per value (value and call tag)
   w.state = take(mm::decode_fused_state_bytes());
-  w.a_r = take((size_t)Tk * d->hidden * 4);
-  w.a_s = take((size_t)T * d->shared_hidden * 4);
-  w.f = take((size_t)Tk * dm * 4);
-  w.ys = take((size_t)T * dm * 4);
+  w.a_r = take((size_t)Tk * d->hidden * 8);
+  w.a_s = take((size_t)T * d->shared_hidden * 8);
+  w.f = take((size_t)Tk * dm * 8);
+  w.ys = take((size_t)T * dm * 8);
   w.total = o;
   return w;
 }
@@ -312,10 +313,10 @@ mm_status moe_decode_impl(const char* where, const mm_layer_desc* desc, int64_t 
   a.eps = norm_eps;
   a.out_bf16 = desc->out_dtype == MM_OUT_BF16;
   a.state = base + W.state;
-  a.a_r = reinterpret_cast<float*>(base + W.a_r);
-  a.a_s = reinterpret_cast<float*>(base + W.a_s);
-  a.f = reinterpret_cast<float*>(base + W.f);
-  a.ys = reinterpret_cast<float*>(base + W.ys);
+  a.a_r = base + W.a_r;
+  a.a_s = base + W.a_s;
+  a.f = base + W.f;
+  a.ys = base + W.ys;
   a.spin_limit = 1u << 20;
   return hip_status(mm::launch_decode_fused(a, S(stream)), where);
 }

@@ -23,18 +23,21 @@
 //                 wait for the logits, redo the top-k and the count sort in
 //                 workgroup memory, then the tile's product
 //   shared down   d/32 blocks: weights issued, then wait for the shared
-//                 gate/up, quantise the hidden rows, product into ys
+//                 hidden rows, quantise them, product into ys
 //   routed down   Umax * d/32 blocks: routing as above, weights issued, wait
-//                 for the tile's gate/up, product into f
-//   combine       one workgroup: topk_idx / topk_w, then (after every down
-//                 block) the weighted combine, optional RMSNorm
-// A producer makes its stores visible at device scope (a workgroup barrier,
-// then one device-scope release increment of the stage's counter); a consumer
-// polls the counter (bounded: a wait that gives up bumps the status word and
-// goes on, so the kernel always ends), fences with device-scope acquire, then
-// a barrier (the pattern of a grid-wide barrier, across the XCDs' L2s).  The
-// last workgroup to finish resets the counters, so each call leaves the state
-// as it found it.
+//                 for the tile's hidden rows, product into f
+//   combine       one workgroup: topk_idx / topk_w, then (as the expert
+//                 outputs arrive) the weighted combine, optional RMSNorm
+// Every value handed from one workgroup to another (logits, hidden rows,
+// expert outputs) is a flag-in-word: the FP32 bits with this call's tag in
+// the upper half of one 64-bit word, stored and polled with device-scope
+// atomic accesses (LLWait in gemv_block.h), so a consumer waits for the data
+// itself, with no counter, no fence and no cache invalidation.  The tag is
+// the state's call count + 1, read at the start; the last workgroup to finish
+// (counted on the exit counter) bumps the call count and clears the exit
+// counter, so each call leaves the state ready for the next.  Polls are
+// bounded: a wait that gives up bumps the status word and goes on, so the
+// kernel always ends.
 #include <algorithm>
 #include <mutex>
 
@@ -51,18 +54,16 @@ constexpr int kDecMaxT = 4;
 constexpr int kDecMaxSlots = kDecMaxT * 8;  // T * k, k <= 8
 constexpr int kRouterNX = 20;               // d / 64 <= 20
 constexpr int kLogitStride = 64;            // logit table [T][64]
+// The logit table is written in kLogitCopies copies, kLogitCopyStride words
+// apart (so they sit in different memory channels); a consumer reads copy
+// blockIdx % kLogitCopies, which spreads the polls of every routed
+// workgroup.
+constexpr int kLogitCopies = 8;
+constexpr int kLogitCopyStride = kDecMaxT * kLogitStride + 32;
 
-// Counter words at the start of the state.
-enum : int {
-  kCtrRouter = 0,    // router workgroups done
-  kCtrSharedGU = 1,  // shared gate/up blocks done
-  kCtrDown = 2,      // down blocks (both kinds) done
-  kCtrExit = 3,      // workgroups finished
-  kCtrStatus = 4,    // waits that gave up (never reset here)
-  kCtrTile = 8,      // routed gate/up blocks done, one word per tile
-  kCtrWords = 64
-};
-static_assert(kCtrTile + kDecMaxSlots <= kCtrWords, "tile counters fit the counter block");
+// State words: the call count (word 0), the give-up count (word 4), and the
+// exit counter on a line of its own; then the logit copies (64-bit words).
+enum : int { kCallCount = 0, kStatus = 4, kExit = 64, kStateWords = 128 };
 
 struct DecodeArgs {
   int T, d, E, k, h, hs;
@@ -83,40 +84,14 @@ struct DecodeArgs {
   float* y_norm;
   float eps;
   int out_bf16;
-  uint32_t* ctr;  // kCtrWords counters
-  float* logits;  // [T][kLogitStride]
-  float* a_r;     // [T*k][h] routed hidden rows, expert-sorted
-  float* a_s;     // [T][hs]
-  float* f;       // [T*k][d] routed outputs, expert-sorted
-  float* ys;      // [T][d]
+  uint32_t* state;   // kStateWords words
+  uint64_t* logits;  // kLogitCopies copies of [T][kLogitStride], flag-in-word
+  uint64_t* a_r;     // [T*k][h] routed hidden rows, expert-sorted, flag-in-word
+  uint64_t* a_s;     // [T][hs]
+  uint64_t* f;       // [T*k][d] routed outputs, expert-sorted
+  uint64_t* ys;      // [T][d]
   uint32_t spin_limit;
 };
-
-// The workgroup's stores are ordered before one device-scope release
-// increment of the stage's counter.
-__device__ __forceinline__ void signal_done(uint32_t* c) {
-  __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Waits until *c >= target (thread 0 polls, at most spin_limit times; giving
-// up bumps the status word), then fences so that the producers' stores are
-// seen by the whole workgroup.
-__device__ __forceinline__ void wait_count(uint32_t* c, uint32_t target, uint32_t* status,
-                                           uint32_t spin_limit) {
-  if (threadIdx.x == 0) {
-    uint32_t n = 0;
-    while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      if (++n >= spin_limit) {
-        __hip_atomic_fetch_add(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  }
-  __syncthreads();
-}
 
 // Routing of the call in workgroup memory, identical to the router kernels'
 // top-k and mm_route_permute's stable count sort.
@@ -126,15 +101,30 @@ struct RouteTab {
   int32_t inv[kDecMaxSlots];
   int32_t idx[kDecMaxSlots];
   float w[kDecMaxSlots];
+  int32_t tiles[kTileWords];  // every expert of the call owns one tile (FusedTiles)
 };
+static_assert(kFusedTiles >= kDecMaxSlots, "one tile per slot at most");
 
 template <int kGating>
-__device__ __forceinline__ void build_routing(const DecodeArgs& A, RouteTab& R) {
+__device__ __forceinline__ void build_routing(const DecodeArgs& A, const LLWait& L, RouteTab& R) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int E = A.E, k = A.k, Tk = A.T * A.k;
-  if (wave < A.T) {  // wave t: top-k of token t
+  if (wave < A.T) {  // wave t: top-k of token t, once its logits have arrived
+    const uint64_t* row =
+        A.logits + (blockIdx.x % kLogitCopies) * kLogitCopyStride + wave * kLogitStride;
+    float raw = 0.0f;
+    uint32_t n = 0;
+    for (;;) {
+      bool ok = true;
+      if (lane < E) {
+        const uint64_t w = ll_get(row + lane);
+        ok = ll_ready(w, L.tag);
+        raw = ll_value(w);
+      }
+      if (ll_settle(ok, n, L)) break;
+    }
     float mine, gl;
-    biased_logit<kGating>(A.logits + wave * kLogitStride, A.bias, lane, E, mine, gl);
+    biased_value<kGating>(raw, A.bias, lane, E, mine, gl);
     int sel;
     float wgt;
     select_topk_lanes<kGating>(mine, gl, lane, E, k, sel, wgt);
@@ -144,19 +134,30 @@ __device__ __forceinline__ void build_routing(const DecodeArgs& A, RouteTab& R) 
     }
   }
   __syncthreads();
-  if (wave == 0) {  // expert offsets: exclusive scan of the counts
-    int c = 0;
-    for (int s = 0; s < Tk; ++s) c += R.idx[s] == lane;
-    if (lane >= E) c = 0;
-    int inc = c;
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) {
-      const int v = __shfl_up(inc, s);
-      if (lane >= s) inc += v;
+  if (wave == 0) {
+    // lane e: its count and its offset (the slots with a lower expert: the
+    // exclusive scan of the counts), and, for experts with rows, its tile
+    // (one per expert, T <= 4 rows) numbered in expert order
+    int c = 0, below = 0;
+    for (int s = 0; s < Tk; ++s) {
+      const int v = R.idx[s];
+      c += v == lane;
+      below += v < lane;
     }
-    if (lane < E) {
-      R.off[lane] = inc - c;
-      if (lane == E - 1) R.off[E] = inc;
+    const bool has = lane < E && c > 0;
+    const uint64_t used = __ballot(has);
+    if (lane < E) R.off[lane] = below;
+    if (lane == 0) {
+      R.off[E] = Tk;
+      R.tiles[kTileCount] = __popcll(used);
+    }
+    if (has) {
+      // experts with rows below this lane (mbcnt: set bits of `used` under the lane)
+      const int u = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(used >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)used, 0u));
+      R.tiles[kTileP0 + u] = below;
+      R.tiles[kTileN + u] = c;
+      R.tiles[kTileE + u] = lane;
     }
   }
   __syncthreads();
@@ -173,109 +174,139 @@ __device__ __forceinline__ void build_routing(const DecodeArgs& A, RouteTab& R) 
 
 // Router workgroup g: wave w computes the logits of expert 4g + w for every
 // token (the router kernels' order: lane partials over columns l, l+64, ...
-// with fused multiply-adds, then the 64-lane tree).
-__device__ __forceinline__ void router_role(const DecodeArgs& A, int g) {
+// with fused multiply-adds, then the 64-lane tree).  The token rows are
+// staged in workgroup memory (xs: T*d floats) so that all of them are read
+// at once; every logit goes to each of the kLogitCopies copies of the table.
+__device__ __forceinline__ void router_role(const DecodeArgs& A, const LLWait& L, int g, float* xs) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int e = 4 * g + wave, nx = A.d / kWave;
+  float wv[kRouterNX];
   if (e < A.E) {
-    float wv[kRouterNX];
     const float* we = A.wr + (int64_t)e * A.d;
 #pragma unroll
     for (int c = 0; c < kRouterNX; ++c)
       if (c < nx) wv[c] = we[lane + kWave * c];
+  }
+  for (int i = threadIdx.x; i < A.T * A.d / 4; i += 256)
+    reinterpret_cast<float4*>(xs)[i] = reinterpret_cast<const float4*>(A.x)[i];
+  __syncthreads();
+  if (e < A.E) {
 #pragma unroll
     for (int t = 0; t < kDecMaxT; ++t) {
       if (t >= A.T) break;
       float p = 0.0f;
 #pragma unroll
       for (int c = 0; c < kRouterNX; ++c)
-        if (c < nx) p = __builtin_fmaf(A.x[(int64_t)t * A.d + lane + kWave * c], wv[c], p);
+        if (c < nx) p = __builtin_fmaf(xs[t * A.d + lane + kWave * c], wv[c], p);
       const float l = tree_sum64(p);  // the bias is added at the selection
-      if (lane == 0) A.logits[t * kLogitStride + e] = l;
+      if (lane < kLogitCopies) ll_put(A.logits + lane * kLogitCopyStride + t * kLogitStride + e, l, L.tag);
     }
   }
-  signal_done(A.ctr + kCtrRouter);
 }
 
-// Combine of token t by wave t, the arithmetic of combine_token: per output
-// column the gate-weighted FMA chain over the token's k expert rows (j
-// ascending, from 0), then + ys; with norm_lds, RMSNorm from the per-lane sum
-// of squares over the lane's columns l, l+64, ... (x, y, z, w in order) and
-// the wave butterfly sum.  norm_lds: [d] floats of workgroup memory.
-constexpr int kMaxChunks = 5;  // float4 columns per lane: d <= 1280
-
+// Combine of token t (one workgroup per token), the arithmetic of
+// combine_token: per output column the gate-weighted FMA chain over the
+// token's k expert rows (j ascending, from 0), then + ys; then RMSNorm from
+// the per-lane sum of squares over the lane's columns l, l+64, ... of float4
+// (x, y, z, w in order) and the wave butterfly sum.  Thread tid takes the
+// columns tid + 256 m of every row: it waits for its words of the k expert
+// rows and the ys row (one wait for k = 4 with ys and d <= 1024, two for
+// d = 1280) and forms y for those columns itself; for the norm, wave 0 forms
+// the sum of squares in combine_token's order from the y row in workgroup
+// memory.
 template <bool kBF16Out, bool kNorm>
-__device__ __forceinline__ void combine_small(const DecodeArgs& A, const RouteTab& R, int t,
-                                              float4* norm_lds) {
-  const int lane = threadIdx.x & 63, k = A.k, q = A.d / 4;
-  int pj[8];
-  float wj[8];
+__device__ __forceinline__ void combine_token_ll(const DecodeArgs& A, const LLWait& L,
+                                                 const RouteTab& R, int t, float* lds) {
+  __shared__ float s_inv_rms;
+  const int k = A.k, d = A.d;
+  const bool shared = A.hs > 0;
+  const int nrows = k + (shared ? 1 : 0);
+  constexpr int kRows = 5, kCols = 4;  // per wait: 5 rows x 1024 columns
+  float* yrow = lds;                   // [d], for the norm
+  for (int c0 = 0; c0 < d; c0 += 256 * kCols) {
+    float acc[kCols];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    pj[j] = j < k ? R.inv[t * k + j] : 0;
-    wj[j] = j < k ? R.w[t * k + j] : 0.0f;
-  }
-  const float4* f4 = reinterpret_cast<const float4*>(A.f);
-  const float4* ys4 = A.hs > 0 ? reinterpret_cast<const float4*>(A.ys) + (int64_t)t * q : nullptr;
-  float ss = 0.0f;
+    for (int m = 0; m < kCols; ++m) acc[m] = 0.0f;
+    for (int r0 = 0; r0 < nrows; r0 += kRows) {
+      const uint64_t* rp[kRows];
+      float wr[kRows];
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
-    const int c4 = lane + 64 * i;
-    if (c4 >= q) break;
-    float4 v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < k) v[j] = f4[(int64_t)pj[j] * q + c4];
-    float4 sv = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (ys4) sv = ys4[c4];
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < k) {
-        a.x = fmaf(wj[j], v[j].x, a.x);
-        a.y = fmaf(wj[j], v[j].y, a.y);
-        a.z = fmaf(wj[j], v[j].z, a.z);
-        a.w = fmaf(wj[j], v[j].w, a.w);
+      for (int jj = 0; jj < kRows; ++jj) {
+        const int j = min(r0 + jj, nrows - 1);
+        rp[jj] = j < k ? A.f + (int64_t)__builtin_amdgcn_readfirstlane(R.inv[t * k + j]) * d
+                       : A.ys + (int64_t)t * d;
+        wr[jj] = j < k ? R.w[t * k + j] : 0.0f;
       }
-    if (ys4) {
-      a.x += sv.x;
-      a.y += sv.y;
-      a.z += sv.z;
-      a.w += sv.w;
+      uint64_t w[kRows][kCols];
+      uint32_t n = 0;
+      for (;;) {
+        // every load of the round is issued before any is looked at
+        // (positions past the row or the row count re-read a valid word
+        // and are ignored)
+#pragma unroll
+        for (int jj = 0; jj < kRows; ++jj)
+#pragma unroll
+          for (int m = 0; m < kCols; ++m)
+            w[jj][m] = ll_get(rp[jj] + min(c0 + (int)threadIdx.x + 256 * m, d - 1));
+        bool ok = true;
+#pragma unroll
+        for (int jj = 0; jj < kRows; ++jj)
+#pragma unroll
+          for (int m = 0; m < kCols; ++m) {
+            const bool used = r0 + jj < nrows && c0 + (int)threadIdx.x + 256 * m < d;
+            ok = ok & (!used || ll_ready(w[jj][m], L.tag));
+          }
+        if (ll_settle_wg(ok, n, L)) break;
+      }
+      // rows in order: the expert rows into the FMA chain, the ys row added
+#pragma unroll
+      for (int jj = 0; jj < kRows; ++jj) {
+        const int j = r0 + jj;
+        if (j >= nrows) break;
+#pragma unroll
+        for (int m = 0; m < kCols; ++m) {
+          const float v = ll_value(w[jj][m]);
+          acc[m] = j < k ? fmaf(wr[jj], v, acc[m]) : acc[m] + v;
+        }
+      }
     }
-    if (kBF16Out) {
-      ushort4 o;
-      o.x = f32_to_bf16(a.x);
-      o.y = f32_to_bf16(a.y);
-      o.z = f32_to_bf16(a.z);
-      o.w = f32_to_bf16(a.w);
-      reinterpret_cast<ushort4*>(A.y)[(int64_t)t * q + c4] = o;
-    } else {
-      reinterpret_cast<float4*>(A.y)[(int64_t)t * q + c4] = a;
-    }
-    if (kNorm) {
-      ss = fmaf(a.x, a.x, ss);
-      ss = fmaf(a.y, a.y, ss);
-      ss = fmaf(a.z, a.z, ss);
-      ss = fmaf(a.w, a.w, ss);
-      norm_lds[c4] = a;
+#pragma unroll
+    for (int m = 0; m < kCols; ++m) {
+      const int c = c0 + (int)threadIdx.x + 256 * m;
+      if (c < d) {
+        if (kBF16Out)
+          reinterpret_cast<uint16_t*>(A.y)[(int64_t)t * d + c] = f32_to_bf16(acc[m]);
+        else
+          reinterpret_cast<float*>(A.y)[(int64_t)t * d + c] = acc[m];
+        if (kNorm) yrow[c] = acc[m];
+      }
     }
   }
   if constexpr (kNorm) {
-    ss = wave_sum(ss);
-    const float inv_rms = 1.0f / sqrtf(ss / (float)A.d + A.eps);
-    for (int c4 = lane; c4 < q; c4 += 64) {
-      const float4 a = norm_lds[c4];
-      reinterpret_cast<float4*>(A.y_norm)[(int64_t)t * q + c4] =
-          make_float4(a.x * inv_rms, a.y * inv_rms, a.z * inv_rms, a.w * inv_rms);
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      const float4* y4 = reinterpret_cast<const float4*>(yrow);
+      float ss = 0.0f;
+      for (int c4 = threadIdx.x; c4 < d / 4; c4 += 64) {
+        const float4 a = y4[c4];
+        ss = fmaf(a.x, a.x, ss);
+        ss = fmaf(a.y, a.y, ss);
+        ss = fmaf(a.z, a.z, ss);
+        ss = fmaf(a.w, a.w, ss);
+      }
+      ss = wave_sum(ss);
+      if (threadIdx.x == 0) s_inv_rms = 1.0f / sqrtf(ss / (float)d + A.eps);
     }
+    __syncthreads();
+    const float inv_rms = s_inv_rms;
+    for (int c = threadIdx.x; c < d; c += 256) A.y_norm[(int64_t)t * d + c] = yrow[c] * inv_rms;
   }
 }
 
 // Launch shape: workgroups per role (each loops over its role's blocks with
 // that stride) and the blocks per role.
 struct DecodeGrid {
-  int router, sgu_b, rgu_b, sdn_b, rdn_b;  // blocks
+  int router, sgu_b, rgu_b, sdn_b, rdn_b;  // blocks (router: workgroups)
   int sgu_w, rgu_w, sdn_w, rdn_w;          // workgroups
 };
 
@@ -284,83 +315,83 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     DecodeArgs A, DecodeGrid G) {
   __shared__ RouteTab R;
   extern __shared__ int4 smem4[];
-  uint32_t* ctr = A.ctr;
-  uint32_t* status = ctr + kCtrStatus;
+  const uint32_t count = __hip_atomic_load(A.state + kCallCount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const LLWait L{__builtin_amdgcn_readfirstlane(count) + 1u, A.spin_limit, A.state + kStatus};
   const int T = A.T, d = A.d, h = A.h, hs = A.hs, Tk = A.T * A.k;
   int b = (int)blockIdx.x;
   bool routed = false;  // routing table built (uniform over the workgroup)
   auto routing = [&]() {
     if (routed) return;
-    wait_count(ctr + kCtrRouter, (uint32_t)G.router, status, A.spin_limit);
-    build_routing<kGating>(A, R);
+    build_routing<kGating>(A, L, R);
     routed = true;
   };
 
   if (b < G.router) {
-    router_role(A, b);
+    router_role(A, L, b, reinterpret_cast<float*>(smem4));
   } else if ((b -= G.router) < G.sgu_w) {
     const ExpertArgs as{T, T, d, hs, 1, 1, nullptr, nullptr};
-    const GemvProb P{as, d, 2 * hs, hs / 32, nullptr, nullptr, A.sgq, A.sgs, A.a_s, nullptr, A.x};
+    const GemvProb P{as, d, 2 * hs, hs / 32, nullptr, nullptr, A.sgq, A.sgs,
+                     reinterpret_cast<float*>(A.a_s), nullptr, A.x, L};
 #pragma clang loop unroll(disable)
     for (int blk = b; blk < G.sgu_b; blk += G.sgu_w) {
       gemv_block<kRGemv, true, false, true, false, true, true>(P, blk);
-      signal_done(ctr + kCtrSharedGU);
+      __syncthreads();
     }
   } else if ((b -= G.sgu_w) < G.rgu_w) {
     const ExpertArgs ar{Tk, T, d, h, A.E, A.k, R.perm, R.off};
-    const GemvProb P{ar, d, 2 * h, h / 32, nullptr, nullptr, A.gq, A.gs, A.a_r, nullptr, A.x};
+    const GemvProb P{ar, d, 2 * h, h / 32, nullptr, nullptr, A.gq, A.gs,
+                     reinterpret_cast<float*>(A.a_r), nullptr, A.x, L, R.tiles};
 #pragma clang loop unroll(disable)
     for (int blk = b; blk < G.rgu_b; blk += G.rgu_w) {
       gemv_block<kRGemv, true, false, false, false, true, true>(P, blk, routing);
-      signal_done(ctr + kCtrTile + blk / (h / 32));
+      __syncthreads();
     }
   } else if ((b -= G.rgu_w) < G.sdn_w) {
     const ExpertArgs as{T, T, d, hs, 1, 1, nullptr, nullptr};
-    const GemvProb P{as, hs, d, d / 32, nullptr, nullptr, A.sdq, A.sds, A.ys, nullptr, A.a_s};
-    auto ready = [&]() { wait_count(ctr + kCtrSharedGU, (uint32_t)G.sgu_b, status, A.spin_limit); };
+    const GemvProb P{as, hs, d, d / 32, nullptr, nullptr, A.sdq, A.sds,
+                     reinterpret_cast<float*>(A.ys), nullptr, reinterpret_cast<const float*>(A.a_s), L};
 #pragma clang loop unroll(disable)
     for (int blk = b; blk < G.sdn_b; blk += G.sdn_w) {
-      gemv_block<kRGemv, false, false, true, true, true, false>(P, blk, NoHook(), ready);
-      signal_done(ctr + kCtrDown);
+      gemv_block<kRGemv, false, false, true, true, true, false>(P, blk);
+      __syncthreads();
     }
   } else if ((b -= G.sdn_w) < G.rdn_w) {
     const ExpertArgs ar{Tk, T, d, h, A.E, A.k, nullptr, R.off};
-    const GemvProb P{ar, h, d, d / 32, nullptr, nullptr, A.dq, A.dsc, A.f, nullptr, A.a_r};
+    const GemvProb P{ar, h, d, d / 32, nullptr, nullptr, A.dq, A.dsc,
+                     reinterpret_cast<float*>(A.f), nullptr, reinterpret_cast<const float*>(A.a_r), L,
+                     R.tiles};
 #pragma clang loop unroll(disable)
     for (int blk = b; blk < G.rdn_b; blk += G.rdn_w) {
-      const int u = blk / (d / 32);
-      auto ready = [&]() { wait_count(ctr + kCtrTile + u, (uint32_t)(h / 32), status, A.spin_limit); };
-      gemv_block<kRGemv, false, false, false, true, true, false>(P, blk, routing, ready);
-      signal_done(ctr + kCtrDown);
+      gemv_block<kRGemv, false, false, false, true, true, false>(P, blk, routing);
+      __syncthreads();
     }
   } else {
+    // combine workgroup of token t = b
+    const int t = b - G.rdn_w;
     routing();
-    if ((int)threadIdx.x < Tk) {
-      A.topk_idx[threadIdx.x] = R.idx[threadIdx.x];
-      A.topk_w[threadIdx.x] = R.w[threadIdx.x];
+    if ((int)threadIdx.x < A.k) {
+      A.topk_idx[t * A.k + threadIdx.x] = R.idx[t * A.k + threadIdx.x];
+      A.topk_w[t * A.k + threadIdx.x] = R.w[t * A.k + threadIdx.x];
     }
-    wait_count(ctr + kCtrDown, (uint32_t)(G.sdn_b + G.rdn_b), status, A.spin_limit);
-    const int t = threadIdx.x >> 6;
-    float4* nbuf = reinterpret_cast<float4*>(smem4) + (int64_t)t * (d / 4);
-    if (t < T) {
-      if (A.y_norm)
-        combine_small<false, true>(A, R, t, nbuf);
-      else if (A.out_bf16)
-        combine_small<true, false>(A, R, t, nullptr);
-      else
-        combine_small<false, false>(A, R, t, nullptr);
-    }
+    float* lds = reinterpret_cast<float*>(smem4);
+    if (A.y_norm)
+      combine_token_ll<false, true>(A, L, R, t, lds);
+    else if (A.out_bf16)
+      combine_token_ll<true, false>(A, L, R, t, lds);
+    else
+      combine_token_ll<false, false>(A, L, R, t, lds);
   }
 
-  // The last workgroup out resets the counters: every other workgroup has
-  // passed all of its waits by the time it counts itself out.
+  // The last workgroup out (every other one has finished all of its waits
+  // when it counts itself out) moves the call count on and clears the exit
+  // counter.
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t before =
-        __hip_atomic_fetch_add(ctr + kCtrExit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(A.state + kExit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (before == gridDim.x - 1) {
-      for (int i = 0; i < kCtrWords; ++i)
-        if (i != kCtrStatus) __hip_atomic_store(ctr + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(A.state + kCallCount, L.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(A.state + kExit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -372,7 +403,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 // for callers that cannot allocate.  Each device holds its own copy at its
 // own address (hipGetSymbolAddress once per device); in host code the name
 // is only a handle for that lookup.  Zero at load; cleared once more when a
-// device's address is first taken; every call leaves the counters zero.
+// device's address is first taken; every call leaves the state ready for the
+// next (see the call count above).
 constexpr size_t kDecodeScratchBytes = size_t(512) << 10;
 static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
 
@@ -420,7 +452,9 @@ bool decode_fused_fits(int64_t T, int d, int E, int k, int h, int hs) {
          gemv_i4_qin_fits(h) && (hs == 0 || gemv_i4_qin_fits(hs));
 }
 
-size_t decode_fused_state_bytes() { return (size_t)kCtrWords * 4 + (size_t)kDecMaxT * kLogitStride * 4; }
+size_t decode_fused_state_bytes() {
+  return (size_t)kStateWords * 4 + (size_t)kLogitCopies * kLogitCopyStride * 8;
+}
 
 namespace {
 
@@ -482,12 +516,12 @@ hipError_t launch_decode_fused(const DecodeFusedArgs& a, hipStream_t st, int* gr
   A.y_norm = a.y_norm;
   A.eps = a.eps;
   A.out_bf16 = a.out_bf16 ? 1 : 0;
-  A.ctr = static_cast<uint32_t*>(a.state);
-  A.logits = reinterpret_cast<float*>(static_cast<char*>(a.state) + kCtrWords * 4);
-  A.a_r = a.a_r;
-  A.a_s = a.a_s;
-  A.f = a.f;
-  A.ys = a.ys;
+  A.state = static_cast<uint32_t*>(a.state);
+  A.logits = reinterpret_cast<uint64_t*>(static_cast<char*>(a.state) + kStateWords * 4);
+  A.a_r = static_cast<uint64_t*>(a.a_r);
+  A.a_s = static_cast<uint64_t*>(a.a_s);
+  A.f = static_cast<uint64_t*>(a.f);
+  A.ys = static_cast<uint64_t*>(a.ys);
   A.spin_limit = a.spin_limit;
   // Blocks per role: every expert of the call owns one 4-row tile (at most
   // min(T*k, E) of them); tiles that turn out unused return at once.
@@ -521,7 +555,7 @@ hipError_t launch_decode_fused(const DecodeFusedArgs& a, hipStream_t st, int* gr
     G.rgu_w = wg(G.rgu_b);
     G.sdn_w = wg(G.sdn_b);
     G.rdn_w = wg(G.rdn_b);
-    grid = G.router + G.sgu_w + G.rgu_w + G.sdn_w + G.rdn_w + 1;
+    grid = G.router + G.sgu_w + G.rgu_w + G.sdn_w + G.rdn_w + (int)a.T;
     if (grid <= cap) break;
     if (G.sgu_w <= 1 && G.rgu_w <= 1 && G.sdn_w <= 1 && G.rdn_w <= 1) return hipErrorInvalidConfiguration;
   }

@@ -161,9 +161,10 @@ hipError_t launch_combine(int64_t T, int d, int k, const float* f, const int32_t
                           hipStream_t st, float* y_norm = nullptr, float eps = 0.0f);
 
 // The whole layer for 1..4 tokens in one launch (k_decode.hip), INT4
-// weights; the same outputs as the separate launches.  state: a zeroed block
-// of decode_fused_state_bytes() (counters + logit table) that each call leaves
-// zeroed (word 4 excepted: it counts waits that gave up).  grid_out: the
+// weights; the same outputs as the separate launches.  state: a block of
+// decode_fused_state_bytes() (call count, exit counter, logit table), and
+// a_r / a_s / f / ys, zeroed before first use; each call leaves them ready
+// for the next (word 4 of the state counts waits that gave up).  grid_out: the
 // launched workgroup count.  hipErrorInvalidConfiguration if the grid cannot
 // be resident at once.
 struct DecodeFusedArgs {
@@ -187,10 +188,10 @@ struct DecodeFusedArgs {
   float eps;
   bool out_bf16;
   void* state;
-  float* a_r;
-  float* a_s;
-  float* f;
-  float* ys;
+  void* a_r;  // flag-in-word buffers: 8 bytes per value
+  void* a_s;
+  void* f;
+  void* ys;
   uint32_t spin_limit;
 };
 bool decode_fused_fits(int64_t T, int d, int E, int k, int h, int hs);

@@ -52,12 +52,17 @@ __device__ __forceinline__ void select_topk_lanes(float mine, float gl, int lane
 // (kGating & 2, the load-balancing bias of the "Pre-training" section) the
 // logit without the bias.
 template <int kGating>
-__device__ __forceinline__ void biased_logit(const float* row, const float* __restrict__ bias,
-                                             int lane, int E, float& mine, float& gl) {
-  const float raw = lane < E ? row[lane] : 0.0f;
+__device__ __forceinline__ void biased_value(float raw, const float* __restrict__ bias, int lane,
+                                             int E, float& mine, float& gl) {
   const float b = raw + (bias && lane < E ? bias[lane] : 0.0f);
   mine = lane < E ? b : -INFINITY;
   gl = (kGating & 2) ? raw : b;
+}
+
+template <int kGating>
+__device__ __forceinline__ void biased_logit(const float* row, const float* __restrict__ bias,
+                                             int lane, int E, float& mine, float& gl) {
+  biased_value<kGating>(lane < E ? row[lane] : 0.0f, bias, lane, E, mine, gl);
 }
 
 // Per-token INT8 quantisation of the x row a wave holds in registers (lane l
