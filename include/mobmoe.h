@@ -219,11 +219,17 @@ mm_status mm_act_quant_i8(int64_t rows, int64_t cols, const float* x, int8_t* q,
 /* Layouts of an INT8 code matrix [rows][cols]. */
 enum {
   MM_ACT_ROW_MAJOR = 0,   /* code (r, c) at byte r * cols + c                         */
-  MM_ACT_GROUP_MAJOR = 1  /* code (r, c) at byte ((c / 32) * rows + r) * 32 + c % 32:
+  MM_ACT_GROUP_MAJOR = 1, /* code (r, c) at byte ((c / 32) * rows + r) * 32 + c % 32:
                              the 32 codes of one row and one quantisation group are
-                             contiguous, and so are consecutive rows of one group
-                             (what the merged matrix-core products read); needs
-                             cols % 128 == 0                                          */
+                             contiguous, and so are consecutive rows of one group;
+                             needs cols % 128 == 0                                    */
+  MM_ACT_F16_PAIRED = 2   /* 16-bit values, row-major [rows][cols] (q holds 2 * rows *
+                             cols bytes); inside each aligned block of 8 columns,
+                             column c (0..7) sits at slot c / 2 (c even) or 4 + c / 2
+                             (c odd) and holds the code as an IEEE half value, divided
+                             by 16 for c >= 4 (exact).  What the f16 merged products
+                             (mm_expert_gateup_pair_f32, mm_expert_down_pair_f32)
+                             read; needs cols % 128 == 0                              */
 };
 
 /*
@@ -262,22 +268,44 @@ mm_status mm_expert_gateup_swiglu(const mm_layer_desc* desc, int64_t T, const vo
 /*
  * The routed experts' and the shared expert's gate/up products with SwiGLU
  * (sections "Custom MoE kernel" and "Divide-and-conquer architecture
- * search", Finding 3) in one launch, INT4 weights only, as mm_moe_forward
- * runs them for larger batches: the arithmetic of mm_expert_gateup_swiglu
- * with h_scale = NULL (FP32 hidden rows, bit-identical), from x_q in
- * MM_ACT_GROUP_MAJOR.
- *   xq, sx            x_q int8 [T][d] (group-major) and its FP32 scales [T]
+ * search", Finding 3) in one launch, INT4 weights only: the arithmetic of
+ * mm_expert_gateup_swiglu with h_scale = NULL (FP32 hidden rows,
+ * bit-identical).  This form takes the exact group sums from the f16 matrix
+ * cores (INT8 and INT4 codes are exact f16 values and every partial sum is an
+ * integer below 2^24), so each output needs one FP32 multiply-add per group
+ * and no integer-to-float conversion; workgroups of four waves share the
+ * activation and weight tiles through LDS.
+ *   xq, sx            x_q as MM_ACT_F16_PAIRED codes [T][d] and its FP32
+ *                     scales [T] (mm_act_quant_i8_layout)
  *   perm, expert_offsets  from mm_route_permute
  *   w_gateup          routed, stacked [E][2h][d]; ws_gateup shared [2h_s][d]
  *   h_r               out: FP32 [T*k][h], sorted order
  *   h_s               out: FP32 [T][h_s]
- * Needs desc->wfmt == MM_W_INT4G32 (else MM_ERR_FORMAT), shared_hidden > 0
- * and d % 128 == 0 (else MM_ERR_SHAPE).
+ * Needs desc->wfmt == MM_W_INT4G32 (else MM_ERR_FORMAT), shared_hidden > 0,
+ * d % 128 == 0 and h, h_s % 64 == 0 (else MM_ERR_SHAPE).
  */
-mm_status mm_expert_gateup_pair_f32(const mm_layer_desc* desc, int64_t T, const int8_t* xq,
+mm_status mm_expert_gateup_pair_f32(const mm_layer_desc* desc, int64_t T, const void* xq,
                                     const float* sx, const int32_t* perm,
                                     const int32_t* expert_offsets, mm_weight w_gateup,
                                     mm_weight ws_gateup, float* h_r, float* h_s, void* stream);
+
+/*
+ * The routed experts' and the shared expert's down products in one launch on
+ * the f16 matrix cores, as mm_expert_gateup_pair_f32 (the arithmetic of
+ * mm_expert_down and mm_shared_expert's down product, bit-identical).
+ *   hq_r, hs_r   routed hidden rows as MM_ACT_F16_PAIRED codes [T*k][h]
+ *                (sorted order) and their scales [T*k]
+ *   hq_s, hs_s   shared hidden rows, MM_ACT_F16_PAIRED [T][h_s], scales [T]
+ *   expert_offsets  from mm_route_permute
+ *   w_down [E][d][h], ws_down [d][h_s]
+ *   f            out: FP32 [T*k][d], sorted order (gate weight not applied)
+ *   ys           out: FP32 [T][d]
+ * Same requirements as mm_expert_gateup_pair_f32.
+ */
+mm_status mm_expert_down_pair_f32(const mm_layer_desc* desc, int64_t T, const void* hq_r,
+                                  const float* hs_r, const void* hq_s, const float* hs_s,
+                                  const int32_t* expert_offsets, mm_weight w_down,
+                                  mm_weight ws_down, float* f, float* ys, void* stream);
 
 /*
  * Routed experts' down product: f[p] = h[p] W_down[e]^T for every sorted
@@ -631,6 +659,19 @@ mm_status mm_expert_down_dbg(const mm_layer_desc* desc, int64_t T, const void* h
                              const float* h_scale, const int32_t* expert_offsets,
                              mm_weight w_down, float* f, void* ws, size_t ws_bytes,
                              int32_t* isum, void* stream);
+/* ... and of the merged products: isum_r [T*k][2h][d/32] and isum_s
+ * [T][2h_s][d/32] (gate/up), isum_r [T*k][d][h/32] and isum_s [T][d][h_s/32]
+ * (down), each the exact group sum of one (row, weight row, group). */
+mm_status mm_expert_gateup_pair_f32_dbg(const mm_layer_desc* desc, int64_t T, const void* xq,
+                                        const float* sx, const int32_t* perm,
+                                        const int32_t* expert_offsets, mm_weight w_gateup,
+                                        mm_weight ws_gateup, float* h_r, float* h_s,
+                                        int32_t* isum_r, int32_t* isum_s, void* stream);
+mm_status mm_expert_down_pair_f32_dbg(const mm_layer_desc* desc, int64_t T, const void* hq_r,
+                                      const float* hs_r, const void* hq_s, const float* hs_s,
+                                      const int32_t* expert_offsets, mm_weight w_down,
+                                      mm_weight ws_down, float* f, float* ys, int32_t* isum_r,
+                                      int32_t* isum_s, void* stream);
 
 #ifdef __cplusplus
 }

@@ -20,7 +20,7 @@ MM_W_F32, MM_W_INT4G32, MM_W_BF16 = range(3)
 MM_GATE_SOFTMAX, MM_GATE_SIGMOID_NORM, MM_GATE_BIAS_SELECT_ONLY = 0, 1, 2
 MM_OUT_F32, MM_OUT_BF16 = range(2)
 MM_WS_ROUTE, MM_WS_GATEUP, MM_WS_DOWN, MM_WS_SHARED, MM_WS_MAX, MM_WS_FORWARD, MM_WS_DECODE = range(7)
-MM_ACT_ROW_MAJOR, MM_ACT_GROUP_MAJOR = range(2)
+MM_ACT_ROW_MAJOR, MM_ACT_GROUP_MAJOR, MM_ACT_F16_PAIRED = range(3)
 
 WFMT = {"f32": MM_W_F32, "int4g32": MM_W_INT4G32, "bf16": MM_W_BF16}
 
@@ -37,6 +37,7 @@ EXPORTS = (
     "mm_gather_rows", "mm_expert_train_forward_f32", "mm_expert_backward_workspace_bytes",
     "mm_expert_backward_f32", "mm_router_backward_f32", "mm_set_profile_events",
     "mm_moe_decode", "mm_moe_decode_supported", "mm_moe_decode_noalloc",
+    "mm_expert_gateup_pair_f32_dbg", "mm_expert_down_pair_f32", "mm_expert_down_pair_f32_dbg",
 )
 
 
@@ -80,6 +81,12 @@ _SIGS = {
     "mm_act_quant_i8_layout": ([_I64, _I64, _VP, _VP, _VP, _I32, _VP], ctypes.c_int),
     "mm_expert_gateup_pair_f32": ([_DESC, _I64, _VP, _VP, _VP, _VP, Weight, Weight, _VP, _VP, _VP],
                                   ctypes.c_int),
+    "mm_expert_gateup_pair_f32_dbg": ([_DESC, _I64, _VP, _VP, _VP, _VP, Weight, Weight, _VP, _VP,
+                                       _VP, _VP, _VP], ctypes.c_int),
+    "mm_expert_down_pair_f32": ([_DESC, _I64, _VP, _VP, _VP, _VP, _VP, Weight, Weight, _VP, _VP,
+                                 _VP], ctypes.c_int),
+    "mm_expert_down_pair_f32_dbg": ([_DESC, _I64, _VP, _VP, _VP, _VP, _VP, Weight, Weight, _VP,
+                                     _VP, _VP, _VP, _VP], ctypes.c_int),
     "mm_expert_gateup_swiglu": ([_DESC, _I64, _VP, _VP, _VP, _VP, Weight, _VP, _VP, _VP, _SZ, _VP],
                                 ctypes.c_int),
     "mm_expert_gateup_swiglu_dbg": ([_DESC, _I64, _VP, _VP, _VP, _VP, Weight, _VP, _VP, _VP, _SZ,
@@ -215,10 +222,32 @@ def act_quant_i8_layout(rows, cols, x, q, scale, layout, stream=None):
                                          _stream(stream)), "mm_act_quant_i8_layout")
 
 
-def expert_gateup_pair_f32(ds, T, xq, sx, perm, offsets, w_gu, ws_gu, h_r, h_s, stream=None):
-    _check(load().mm_expert_gateup_pair_f32(ctypes.byref(ds), T, _ptr(xq), _ptr(sx), _ptr(perm),
-                                            _ptr(offsets), w_gu, ws_gu, _ptr(h_r), _ptr(h_s),
-                                            _stream(stream)), "mm_expert_gateup_pair_f32")
+def expert_gateup_pair_f32(ds, T, xq, sx, perm, offsets, w_gu, ws_gu, h_r, h_s, stream=None,
+                           isum_r=None, isum_s=None):
+    lib = load()
+    if isum_r is None:
+        _check(lib.mm_expert_gateup_pair_f32(ctypes.byref(ds), T, _ptr(xq), _ptr(sx), _ptr(perm),
+                                             _ptr(offsets), w_gu, ws_gu, _ptr(h_r), _ptr(h_s),
+                                             _stream(stream)), "mm_expert_gateup_pair_f32")
+    else:
+        _check(lib.mm_expert_gateup_pair_f32_dbg(ctypes.byref(ds), T, _ptr(xq), _ptr(sx),
+                                                 _ptr(perm), _ptr(offsets), w_gu, ws_gu, _ptr(h_r),
+                                                 _ptr(h_s), _ptr(isum_r), _ptr(isum_s),
+                                                 _stream(stream)), "mm_expert_gateup_pair_f32_dbg")
+
+
+def expert_down_pair_f32(ds, T, hq_r, hs_r, hq_s, hs_s, offsets, w_d, ws_d, f, ys, stream=None,
+                         isum_r=None, isum_s=None):
+    lib = load()
+    if isum_r is None:
+        _check(lib.mm_expert_down_pair_f32(ctypes.byref(ds), T, _ptr(hq_r), _ptr(hs_r), _ptr(hq_s),
+                                           _ptr(hs_s), _ptr(offsets), w_d, ws_d, _ptr(f), _ptr(ys),
+                                           _stream(stream)), "mm_expert_down_pair_f32")
+    else:
+        _check(lib.mm_expert_down_pair_f32_dbg(ctypes.byref(ds), T, _ptr(hq_r), _ptr(hs_r),
+                                               _ptr(hq_s), _ptr(hs_s), _ptr(offsets), w_d, ws_d,
+                                               _ptr(f), _ptr(ys), _ptr(isum_r), _ptr(isum_s),
+                                               _stream(stream)), "mm_expert_down_pair_f32_dbg")
 
 
 def expert_gateup_swiglu(ds, T, act, act_scale, perm, offsets, w, h, h_scale, ws, ws_bytes,

@@ -484,29 +484,41 @@ static mm_status gateup_impl(const mm_layer_desc* desc, int64_t T, const void* a
 
 mm_status mm_act_quant_i8_layout(int64_t rows, int64_t cols, const float* x, int8_t* q,
                                  float* scale, int32_t layout, void* stream) {
-  if (layout != MM_ACT_ROW_MAJOR && layout != MM_ACT_GROUP_MAJOR)
+  if (layout != MM_ACT_ROW_MAJOR && layout != MM_ACT_GROUP_MAJOR && layout != MM_ACT_F16_PAIRED)
     return fail(MM_ERR_FORMAT, "unknown activation layout %d", (int)layout);
   if (rows < 0 || cols <= 0) return fail(MM_ERR_SHAPE, "bad shape");
-  if (layout == MM_ACT_GROUP_MAJOR && cols % 128 != 0)
-    return fail(MM_ERR_SHAPE, "group-major codes need cols %% 128 == 0");
+  if (layout != MM_ACT_ROW_MAJOR && cols % 128 != 0)
+    return fail(MM_ERR_SHAPE, "group-major and f16 paired codes need cols %% 128 == 0");
   if (rows == 0) return MM_OK;
   MM_REQUIRE(x);
   MM_REQUIRE(q);
   MM_REQUIRE(scale);
-  return hip_status(mm::launch_act_quant_i8(rows, cols, x, q, scale, S(stream),
-                                            layout == MM_ACT_GROUP_MAJOR),
+  const int lay = layout == MM_ACT_GROUP_MAJOR ? mm::kActGroupMajor
+                  : layout == MM_ACT_F16_PAIRED ? mm::kActF16Paired
+                                                : mm::kActRowMajor;
+  return hip_status(mm::launch_act_quant_i8(rows, cols, x, q, scale, S(stream), lay),
                     "mm_act_quant_i8_layout");
 }
 
-mm_status mm_expert_gateup_pair_f32(const mm_layer_desc* desc, int64_t T, const int8_t* xq,
-                                    const float* sx, const int32_t* perm,
-                                    const int32_t* expert_offsets, mm_weight w_gateup,
-                                    mm_weight ws_gateup, float* h_r, float* h_s, void* stream) {
+namespace {
+
+// Checks shared by the merged product entries: INT4 weights, a shared
+// expert, and widths the f16 matrix-core products take.
+mm_status check_pair(const mm_layer_desc* desc, int64_t T, const char* what) {
   MM_TRY(check_desc(desc));
   MM_TRY(check_T(desc, T));
-  if (desc->wfmt != MM_W_INT4G32) return fail(MM_ERR_FORMAT, "the merged gate/up takes INT4 weights");
-  if (desc->shared_hidden <= 0) return fail(MM_ERR_SHAPE, "the merged gate/up needs a shared expert");
-  if (desc->d_model % 128 != 0) return fail(MM_ERR_SHAPE, "the merged gate/up needs d %% 128 == 0");
+  if (desc->wfmt != MM_W_INT4G32) return fail(MM_ERR_FORMAT, "the merged %s takes INT4 weights", what);
+  if (desc->shared_hidden <= 0) return fail(MM_ERR_SHAPE, "the merged %s needs a shared expert", what);
+  if (!mm::f16_products_fit(desc->d_model, desc->hidden, desc->shared_hidden))
+    return fail(MM_ERR_SHAPE, "the merged %s needs d %% 128 == 0 and h, h_s %% 64 == 0", what);
+  return MM_OK;
+}
+
+mm_status gateup_pair_impl(const mm_layer_desc* desc, int64_t T, const void* xq, const float* sx,
+                           const int32_t* perm, const int32_t* expert_offsets, mm_weight w_gateup,
+                           mm_weight ws_gateup, float* h_r, float* h_s, int32_t* isum_r,
+                           int32_t* isum_s, void* stream, const char* where) {
+  MM_TRY(check_pair(desc, T, "gate/up"));
   if (T == 0) return MM_OK;
   MM_REQUIRE(xq);
   MM_REQUIRE(sx);
@@ -520,11 +532,81 @@ mm_status mm_expert_gateup_pair_f32(const mm_layer_desc* desc, int64_t T, const 
   const mm::ExpertArgs ar{T * k, T, desc->d_model, desc->hidden, desc->n_experts, k, perm,
                           expert_offsets};
   const mm::ExpertArgs as{T, T, desc->d_model, desc->shared_hidden, 1, 1, nullptr, nullptr};
-  return hip_status(mm::launch_gateup_i4_mfma_pair(
-                        ar, as, xq, sx, static_cast<const uint8_t*>(w_gateup.data), w_gateup.scales,
+  return hip_status(mm::launch_gateup_f16_pair(
+                        ar, as, static_cast<const uint16_t*>(xq), sx,
+                        static_cast<const uint8_t*>(w_gateup.data), w_gateup.scales,
                         static_cast<const uint8_t*>(ws_gateup.data), ws_gateup.scales, h_r, h_s,
-                        S(stream)),
-                    "mm_expert_gateup_pair_f32");
+                        isum_r, isum_s, S(stream)),
+                    where);
+}
+
+mm_status down_pair_impl(const mm_layer_desc* desc, int64_t T, const void* hq_r,
+                         const float* hs_r, const void* hq_s, const float* hs_s,
+                         const int32_t* expert_offsets, mm_weight w_down, mm_weight ws_down,
+                         float* f, float* ys, int32_t* isum_r, int32_t* isum_s, void* stream,
+                         const char* where) {
+  MM_TRY(check_pair(desc, T, "down"));
+  if (T == 0) return MM_OK;
+  MM_REQUIRE(hq_r);
+  MM_REQUIRE(hs_r);
+  MM_REQUIRE(hq_s);
+  MM_REQUIRE(hs_s);
+  MM_REQUIRE(expert_offsets);
+  MM_REQUIRE(f);
+  MM_REQUIRE(ys);
+  MM_TRY(check_weight(desc, w_down, "w_down"));
+  MM_TRY(check_weight(desc, ws_down, "ws_down"));
+  const int k = desc->top_k;
+  const mm::ExpertArgs ar{T * k, T, desc->d_model, desc->hidden, desc->n_experts, k, nullptr,
+                          expert_offsets};
+  const mm::ExpertArgs as{T, T, desc->d_model, desc->shared_hidden, 1, 1, nullptr, nullptr};
+  return hip_status(mm::launch_down_f16_pair(
+                        ar, as, static_cast<const uint16_t*>(hq_r), hs_r,
+                        static_cast<const uint16_t*>(hq_s), hs_s,
+                        static_cast<const uint8_t*>(w_down.data), w_down.scales,
+                        static_cast<const uint8_t*>(ws_down.data), ws_down.scales, f, ys, isum_r,
+                        isum_s, S(stream)),
+                    where);
+}
+
+}  // namespace
+
+mm_status mm_expert_gateup_pair_f32(const mm_layer_desc* desc, int64_t T, const void* xq,
+                                    const float* sx, const int32_t* perm,
+                                    const int32_t* expert_offsets, mm_weight w_gateup,
+                                    mm_weight ws_gateup, float* h_r, float* h_s, void* stream) {
+  return gateup_pair_impl(desc, T, xq, sx, perm, expert_offsets, w_gateup, ws_gateup, h_r, h_s,
+                          nullptr, nullptr, stream, "mm_expert_gateup_pair_f32");
+}
+
+mm_status mm_expert_gateup_pair_f32_dbg(const mm_layer_desc* desc, int64_t T, const void* xq,
+                                        const float* sx, const int32_t* perm,
+                                        const int32_t* expert_offsets, mm_weight w_gateup,
+                                        mm_weight ws_gateup, float* h_r, float* h_s,
+                                        int32_t* isum_r, int32_t* isum_s, void* stream) {
+  MM_REQUIRE(isum_r);
+  MM_REQUIRE(isum_s);
+  return gateup_pair_impl(desc, T, xq, sx, perm, expert_offsets, w_gateup, ws_gateup, h_r, h_s,
+                          isum_r, isum_s, stream, "mm_expert_gateup_pair_f32_dbg");
+}
+
+mm_status mm_expert_down_pair_f32(const mm_layer_desc* desc, int64_t T, const void* hq_r,
+                                  const float* hs_r, const void* hq_s, const float* hs_s,
+                                  const int32_t* expert_offsets, mm_weight w_down,
+                                  mm_weight ws_down, float* f, float* ys, void* stream) {
+  return down_pair_impl(desc, T, hq_r, hs_r, hq_s, hs_s, expert_offsets, w_down, ws_down, f, ys,
+                        nullptr, nullptr, stream, "mm_expert_down_pair_f32");
+}
+
+mm_status mm_expert_down_pair_f32_dbg(const mm_layer_desc* desc, int64_t T, const void* hq_r,
+                                      const float* hs_r, const void* hq_s, const float* hs_s,
+                                      const int32_t* expert_offsets, mm_weight w_down,
+                                      mm_weight ws_down, float* f, float* ys, int32_t* isum_r,
+                                      int32_t* isum_s, void* stream) {
+  MM_REQUIRE(isum_r);
+  MM_REQUIRE(isum_s);
+  return down_pair_impl(desc, T, hq_r, hs_r, hq_s, hs_s, expert_offsets, w_down, ws_down, f, ys,
+                        isum_r, isum_s, stream, "mm_expert_down_pair_f32_dbg");
 }
 
 mm_status mm_expert_gateup_swiglu(const mm_layer_desc* desc, int64_t T, const void* act,
@@ -733,6 +815,7 @@ mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
     quant_pair = (shared && gv && !qin) || gu_mfma_pair;
     dn_mfma_pair = !qin && shared && !dv && dm && !use_gemv(ar, h, false) && quant_pair;
   }
+  const int xq_layout = gu_mfma_pair ? mm::kActGroupMajor : mm::kActRowMajor;
 
   // router + top-k (+ per-token INT8 of x), then the count sort; for a few
   // tokens all of it in one workgroup
@@ -746,7 +829,7 @@ mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
     const bool hist = mm::route_hist_applies(T, k);
     uint8_t* hbuf = hist ? static_cast<uint8_t*>(at(W.route)) : nullptr;
     MM_TRY(hip_status(mm::launch_router(T, d, E, k, desc->gating, x, w_router, bias, topk_idx,
-                                        topk_w, xq, sx, st, gu_mfma_pair, hbuf,
+                                        topk_w, xq, sx, st, xq_layout, hbuf,
                                         hist ? mm::route_hist_stride(T) : 0),
                       where));
     if (hist)
@@ -785,7 +868,8 @@ mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
     if (g_prof_stop) MM_TRY(hip_status(hipEventRecord(g_prof_stop, st), where));
     if (quant_pair)
       MM_TRY(hip_status(mm::launch_act_quant_i8_pair(Tk, h, a_r, q_r, s_r, T, hs, a_s, q_s, s_s, st,
-                                                     dn_mfma_pair), where));
+                                                     dn_mfma_pair ? mm::kActGroupMajor
+                                                                  : mm::kActRowMajor), where));
     // down of both kinds
     if (qin) {
       MM_TRY(hip_status(mm::launch_down_i4_gemv_pair_f32in(ar, as, a_r, a_s, dq, w_down.scales, sdq,

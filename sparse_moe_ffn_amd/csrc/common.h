@@ -230,6 +230,38 @@ __device__ __forceinline__ int64_t act_offset(int64_t r, int64_t c, int64_t cols
   return gm_rows ? ((c >> 5) * gm_rows + r) * 32 + (c & 31) : r * cols + c;
 }
 
+// F16 paired activation codes, the operand form of the f16 matrix-core
+// products (k_w4f16.hip): a row-major [R][C] matrix of 16-bit values in which
+// each aligned block of 8 columns is reordered -- column c of the block
+// (0..7) sits at slot (c odd ? 4 + c/2 : c/2) -- and column c holds its INT8
+// code as an f16 value, divided by 16 for c >= 4 (exact: at most 8
+// significant bits).  This matches the order in which those kernels unpack the
+// prepacked INT4 weights (two nibbles per 32-bit operand, the high nibbles of
+// a byte scaled by 16), so the product of each pair is exactly code * weight.
+// Passed as gm_rows = kF16Paired where a quantiser takes a layout.
+constexpr int64_t kF16Paired = -1;
+
+__device__ __forceinline__ int64_t f16p_index(int64_t r, int64_t c, int64_t cols) {
+  const int cc = (int)(c & 7);
+  return r * cols + (c & ~(int64_t)7) + ((cc & 1) ? 4 + (cc >> 1) : (cc >> 1));
+}
+
+__device__ __forceinline__ uint16_t f16p_value(int code, int64_t c) {
+  const float v = (c & 4) ? (float)code * 0.0625f : (float)code;
+  return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
+// Stores one INT8 code in the layout gm_rows names: 0 row-major int8, > 0
+// group-major int8 (that many rows), kF16Paired f16 paired (q is then a
+// buffer of 2 * R * C bytes).
+__device__ __forceinline__ void store_code(void* q, int64_t r, int64_t c, int64_t cols,
+                                           int64_t gm_rows, int code) {
+  if (gm_rows == kF16Paired)
+    static_cast<uint16_t*>(q)[f16p_index(r, c, cols)] = f16p_value(code, c);
+  else
+    static_cast<int8_t*>(q)[act_offset(r, c, cols, gm_rows)] = (int8_t)code;
+}
+
 // Per-row INT8 code of v given the row scale s (s > 0): clamp(rint(v / s)).
 __device__ __forceinline__ int8_t quant_i8(float v, float s) {
   float r = rintf(v / s);

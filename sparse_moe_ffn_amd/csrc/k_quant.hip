@@ -131,6 +131,52 @@ __device__ __forceinline__ void quant_row_v2(int64_t r, int64_t cols, const floa
     }
 }
 
+// Same quantiser writing f16 paired codes (common.h): lane l holds columns
+// 4 j .. 4 j + 3, j = l + 64 i, read as float4; those are columns 0..3 (j
+// even) or 4..7 (j odd) of an 8-column block, which land in slots 0, 4, 1, 5
+// (as the codes) or 2, 6, 3, 7 (the codes divided by 16): two 4-byte stores.
+// cols % 128 == 0.
+template <int kMaxV4>
+__device__ __forceinline__ void quant_row_f16p(int64_t r, int64_t cols,
+                                               const float* __restrict__ x,
+                                               uint16_t* __restrict__ q, float* __restrict__ s) {
+  const int lane = threadIdx.x & 63;
+  const int n4 = (int)(cols / 4);
+  const float4* xr = reinterpret_cast<const float4*>(x + r * cols);
+  float4 v[kMaxV4];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kMaxV4; ++i) {
+    const int j = lane + 64 * i;
+    if (j < n4) {
+      v[i] = xr[j];
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+    }
+  }
+  amax = max64(amax);
+  const float sr = (2.0f * amax) / 255.0f, yr = quant_recip(sr);
+  if (lane == 0) s[r] = sr;
+#pragma unroll
+  for (int i = 0; i < kMaxV4; ++i) {
+    const int j = lane + 64 * i;
+    if (j < n4) {
+      int c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+      if (sr != 0.0f) {
+        c0 = quant_i8(v[i].x, sr, yr);
+        c1 = quant_i8(v[i].y, sr, yr);
+        c2 = quant_i8(v[i].z, sr, yr);
+        c3 = quant_i8(v[i].w, sr, yr);
+      }
+      const int hi = j & 1;  // columns 4..7 of the block
+      const float m = hi ? 0.0625f : 1.0f;
+      auto h = [&](int c) { return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)((float)c * m)); };
+      uint32_t* row = reinterpret_cast<uint32_t*>(q + r * cols + 8 * (j >> 1));
+      row[hi] = h(c0) | (h(c2) << 16);
+      row[2 + hi] = h(c1) | (h(c3) << 16);
+    }
+  }
+}
+
 template <int kMaxV>
 __global__ __launch_bounds__(256) void k_act_quant_i8_v2(int64_t rows, int64_t cols,
                                                          const float* __restrict__ x,
@@ -138,6 +184,15 @@ __global__ __launch_bounds__(256) void k_act_quant_i8_v2(int64_t rows, int64_t c
                                                          float* __restrict__ s, int64_t gm_rows) {
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r < rows) quant_row_v2<kMaxV>(r, cols, x, q, s, gm_rows);
+}
+
+template <int kMaxV4>
+__global__ __launch_bounds__(256) void k_act_quant_f16p(int64_t rows, int64_t cols,
+                                                        const float* __restrict__ x,
+                                                        uint16_t* __restrict__ q,
+                                                        float* __restrict__ s) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r < rows) quant_row_f16p<kMaxV4>(r, cols, x, q, s);
 }
 
 // Two row sets in one launch: blocks [0, nb0) cover set 0, the rest set 1
@@ -160,6 +215,18 @@ __global__ __launch_bounds__(256) void k_act_quant_i8_pair(QuantRows A, QuantRow
   } else {
     const int64_t r = (int64_t)(blockIdx.x - nb0) * 4 + wave;
     if (r < B.rows) quant_row_v2<kMaxV>(r, B.cols, B.x, B.q, B.s, B.gm_rows);
+  }
+}
+
+template <int kMaxV4>
+__global__ __launch_bounds__(256) void k_act_quant_f16p_pair(QuantRows A, QuantRows B, int nb0) {
+  const int wave = threadIdx.x >> 6;
+  if ((int)blockIdx.x < nb0) {
+    const int64_t r = (int64_t)blockIdx.x * 4 + wave;
+    if (r < A.rows) quant_row_f16p<kMaxV4>(r, A.cols, A.x, reinterpret_cast<uint16_t*>(A.q), A.s);
+  } else {
+    const int64_t r = (int64_t)(blockIdx.x - nb0) * 4 + wave;
+    if (r < B.rows) quant_row_f16p<kMaxV4>(r, B.cols, B.x, reinterpret_cast<uint16_t*>(B.q), B.s);
   }
 }
 
@@ -204,12 +271,18 @@ hipError_t launch_prepack_int4g32(int64_t n_mat, int64_t rows, int64_t cols, con
 }
 
 hipError_t launch_act_quant_i8(int64_t rows, int64_t cols, const float* x, int8_t* q, float* s,
-                               hipStream_t st, bool group_major) {
+                               hipStream_t st, int layout) {
+  if (layout == kActF16Paired) {
+    if (cols % 128 != 0 || cols > 256 * 12) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_act_quant_f16p<12>, dim3(blocks_for(rows, 4)), dim3(256), 0, st, rows,
+                       cols, x, reinterpret_cast<uint16_t*>(q), s);
+    return hipGetLastError();
+  }
   if (cols % 128 == 0 && cols <= 128 * 24)
     hipLaunchKernelGGL(k_act_quant_i8_v2<24>, dim3(blocks_for(rows, 4)), dim3(256), 0, st, rows,
-                       cols, x, q, s, group_major ? rows : (int64_t)0);
-  else if (group_major)
-    return hipErrorInvalidValue;  // group-major codes only for cols % 128 == 0
+                       cols, x, q, s, act_gm_rows(layout, rows));
+  else if (layout != kActRowMajor)
+    return hipErrorInvalidValue;  // other layouts only for cols % 128 == 0
   else
     hipLaunchKernelGGL(k_act_quant_i8, dim3(blocks_for(rows, 4)), dim3(256), 0, st, rows, cols, x,
                        q, s);
@@ -218,18 +291,21 @@ hipError_t launch_act_quant_i8(int64_t rows, int64_t cols, const float* x, int8_
 
 hipError_t launch_act_quant_i8_pair(int64_t rows0, int64_t cols0, const float* x0, int8_t* q0,
                                     float* s0, int64_t rows1, int64_t cols1, const float* x1,
-                                    int8_t* q1, float* s1, hipStream_t st, bool group_major) {
+                                    int8_t* q1, float* s1, hipStream_t st, int layout) {
   auto fits = [](int64_t c) { return c % 128 == 0 && c <= 128 * 24; };
   if (!fits(cols0) || !fits(cols1)) {
-    hipError_t e = launch_act_quant_i8(rows0, cols0, x0, q0, s0, st, group_major);
+    hipError_t e = launch_act_quant_i8(rows0, cols0, x0, q0, s0, st, layout);
     if (e != hipSuccess) return e;
-    return launch_act_quant_i8(rows1, cols1, x1, q1, s1, st, group_major);
+    return launch_act_quant_i8(rows1, cols1, x1, q1, s1, st, layout);
   }
-  QuantRows A{rows0, cols0, x0, q0, s0, group_major ? rows0 : 0};
-  QuantRows B{rows1, cols1, x1, q1, s1, group_major ? rows1 : 0};
+  QuantRows A{rows0, cols0, x0, q0, s0, act_gm_rows(layout, rows0)};
+  QuantRows B{rows1, cols1, x1, q1, s1, act_gm_rows(layout, rows1)};
   if (B.cols > A.cols) std::swap(A, B);
   const int nbA = (int)blocks_for(A.rows, 4), nbB = (int)blocks_for(B.rows, 4);
-  hipLaunchKernelGGL(k_act_quant_i8_pair<24>, dim3(nbA + nbB), dim3(256), 0, st, A, B, nbA);
+  if (layout == kActF16Paired)
+    hipLaunchKernelGGL(k_act_quant_f16p_pair<12>, dim3(nbA + nbB), dim3(256), 0, st, A, B, nbA);
+  else
+    hipLaunchKernelGGL(k_act_quant_i8_pair<24>, dim3(nbA + nbB), dim3(256), 0, st, A, B, nbA);
   return hipGetLastError();
 }
 

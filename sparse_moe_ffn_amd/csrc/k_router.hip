@@ -370,9 +370,9 @@ bool launch_front_small(int64_t T, int d, int E, int k, int gating, const float*
 
 hipError_t launch_router(int64_t T, int d, int E, int k, int gating, const float* x,
                          const float* wr, const float* bias, int32_t* idx, float* w,
-                         int8_t* xq, float* sx, hipStream_t st, bool xq_group_major,
+                         int8_t* xq, float* sx, hipStream_t st, int xq_layout,
                          uint8_t* hist, int64_t hist_stride) {
-  const int64_t gm = xq_group_major ? T : 0;
+  const int64_t gm = act_gm_rows(xq_layout, T);
   // few tokens: one 16-wave workgroup per token (widths with a register form up to 1280)
   const bool small = T <= kSmallRouterT;
   if (hist != nullptr && small) return hipErrorInvalidValue;  // the per-token form counts nothing
@@ -389,7 +389,7 @@ hipError_t launch_router(int64_t T, int d, int E, int k, int gating, const float
 #undef MM_ROUTER_G
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || xq == nullptr || q) return e;
-  return launch_act_quant_i8(T, d, x, xq, sx, st, xq_group_major);  // widths without the fused form
+  return launch_act_quant_i8(T, d, x, xq, sx, st, xq_layout);  // widths without the fused form
 }
 
 }  // namespace mm

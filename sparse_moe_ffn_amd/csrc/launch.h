@@ -5,21 +5,32 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.h"
+
 namespace mm {
+
+// Layouts of the INT8 activation codes a quantiser writes (common.h):
+// row-major int8, group-major int8, or f16 paired (2 bytes per code, the
+// operand form of the f16 matrix-core products).
+enum ActLayout : int { kActRowMajor = 0, kActGroupMajor = 1, kActF16Paired = 2 };
+// gm_rows argument of the device code for a matrix of `rows` rows.
+inline int64_t act_gm_rows(int layout, int64_t rows) {
+  return layout == kActGroupMajor ? rows : layout == kActF16Paired ? kF16Paired : 0;
+}
 
 // Quantisation, packing, conversions (k_quant.hip)
 hipError_t launch_quantize_int4g32(int64_t rows, int64_t cols, const float* w, uint8_t* q,
                                    float* s, hipStream_t st);
 hipError_t launch_prepack_int4g32(int64_t n_mat, int64_t rows, int64_t cols, const uint8_t* qc,
                                   const float* sc, uint8_t* qo, float* so, hipStream_t st);
-// group_major: the codes in the group-major layout (act_offset in common.h;
-// cols % 128 == 0 only), for the merged matrix-core launches.
+// layout: ActLayout of the codes (group-major and f16 paired: cols % 128 == 0
+// only); q holds rows * cols bytes, twice that for f16 paired.
 hipError_t launch_act_quant_i8(int64_t rows, int64_t cols, const float* x, int8_t* q, float* s,
-                               hipStream_t st, bool group_major = false);
+                               hipStream_t st, int layout = kActRowMajor);
 // Two row sets (e.g. the routed and the shared hidden rows) in one launch.
 hipError_t launch_act_quant_i8_pair(int64_t rows0, int64_t cols0, const float* x0, int8_t* q0,
                                     float* s0, int64_t rows1, int64_t cols1, const float* x1,
-                                    int8_t* q1, float* s1, hipStream_t st, bool group_major = false);
+                                    int8_t* q1, float* s1, hipStream_t st, int layout = kActRowMajor);
 hipError_t launch_convert_bf16(int64_t n, const float* x, uint16_t* y, hipStream_t st);
 hipError_t launch_rmsnorm(int64_t rows, int64_t cols, float eps, const float* x, float* y,
                           hipStream_t st);
@@ -29,7 +40,7 @@ hipError_t launch_rmsnorm(int64_t rows, int64_t cols, float eps, const float* x,
 // pass where the width has a register form, else a second kernel).
 hipError_t launch_router(int64_t T, int d, int E, int k, int gating, const float* x,
                          const float* wr, const float* bias, int32_t* idx, float* w,
-                         int8_t* xq, float* sx, hipStream_t st, bool xq_group_major = false,
+                         int8_t* xq, float* sx, hipStream_t st, int xq_layout = kActRowMajor,
                          uint8_t* hist = nullptr, int64_t hist_stride = 0);
 // hist (T > 64 only): each 4-token router workgroup's count of every expert,
 // byte hist[e * hist_stride + b], b < ceil(T / 4); input of launch_route_hist.
@@ -141,6 +152,22 @@ hipError_t launch_down_i4_gemv_pair_f32in(const ExpertArgs& ar, const ExpertArgs
                                           const float* ws_r, const uint8_t* wq_s,
                                           const float* ws_s, float* f, float* ys, hipStream_t st);
 constexpr int kMfmaK = 128;
+// The same pairs on the f16 matrix cores with exact group sums (k_w4f16.hip):
+// activations as f16 paired codes (x16 [T][d]; the hidden rows h16_r [Tk][h],
+// h16_s [T][hs]); bit-identical outputs.  isum_r / isum_s non-null (tests):
+// also the exact group sums [rows][wrows][K / 32].  f16_products_fit: widths
+// they take (K % 64 == 0, h and hs % 64 == 0, d % 128 == 0).
+bool f16_products_fit(int d, int h, int hs);
+hipError_t launch_gateup_f16_pair(const ExpertArgs& ar, const ExpertArgs& as, const uint16_t* x16,
+                                  const float* sx, const uint8_t* wq_r, const float* ws_r,
+                                  const uint8_t* wq_s, const float* ws_s, float* abuf_r,
+                                  float* abuf_s, int32_t* isum_r, int32_t* isum_s,
+                                  hipStream_t st);
+hipError_t launch_down_f16_pair(const ExpertArgs& ar, const ExpertArgs& as, const uint16_t* h16_r,
+                                const float* hs_r, const uint16_t* h16_s, const float* hs_s,
+                                const uint8_t* wq_r, const float* ws_r, const uint8_t* wq_s,
+                                const float* ws_s, float* f, float* ys, int32_t* isum_r,
+                                int32_t* isum_s, hipStream_t st);
 // BF16 weights on the bf16 matrix cores (k_bf16.hip): gate/up takes the
 // token rows already rounded to BF16 (xb [T][d]) and writes BF16 hidden rows
 // [rows][h]; down writes f [rows][d] FP32.

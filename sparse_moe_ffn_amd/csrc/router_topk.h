@@ -68,7 +68,7 @@ __device__ __forceinline__ void biased_logit(const float* row, const float* __re
 // Per-token INT8 quantisation of the x row a wave holds in registers (lane l
 // holds columns l, l + 64, ...): the same rule as the row quantiser,
 // s = (2 * max|x|) / 255, q = clamp(rint(x / s)), s = 0 gives q = 0.
-// gm_rows: 0 row-major codes, else group-major with that many rows.
+// gm_rows: the layout as in store_code (common.h).
 template <int kNX>
 __device__ __forceinline__ void quant_row_regs(const float (&xv)[kNX], int lane, int64_t t,
                                                int d, int8_t* __restrict__ xq,
@@ -81,7 +81,7 @@ __device__ __forceinline__ void quant_row_regs(const float (&xv)[kNX], int lane,
   if (lane == 0) sx[t] = s;
 #pragma unroll
   for (int c = 0; c < kNX; ++c)
-    xq[act_offset(t, lane + kWave * c, d, gm_rows)] = s != 0.0f ? quant_i8(xv[c], s, y) : (int8_t)0;
+    store_code(xq, t, lane + kWave * c, d, gm_rows, s != 0.0f ? quant_i8(xv[c], s, y) : 0);
 }
 
 }  // namespace mm

@@ -152,14 +152,22 @@ class MoELayer:
         B.expert_gateup_swiglu(self.desc, T, a, s, self.perm, self.offsets, self.w_gu.c(), out,
                                None, None, 0)
 
-    def gateup_pair_f32(self, T, xq_gm, h_r, h_s):
+    def gateup_pair_f32(self, T, xq16, h_r, h_s, isum_r=None, isum_s=None):
         """Routed and shared gate/up + SwiGLU in one launch, FP32 hidden rows
-        into h_r [T*k, h] (sorted order) and h_s [T, h_s], from x_q in the
-        group-major layout (with this layer's scales self.sx): the merged
+        into h_r [T*k, h] (sorted order) and h_s [T, h_s], from x_q as f16
+        paired codes (with this layer's scales self.sx): the merged
         matrix-core kernel mm_moe_forward runs for larger batches, on its own
-        (INT4 weights, shared expert)."""
-        B.expert_gateup_pair_f32(self.desc, T, xq_gm, self.sx, self.perm, self.offsets,
-                                 self.w_gu.c(), self.ws_gu.c(), h_r, h_s)
+        (INT4 weights, shared expert).  isum_r / isum_s: also the exact group
+        sums."""
+        B.expert_gateup_pair_f32(self.desc, T, xq16, self.sx, self.perm, self.offsets,
+                                 self.w_gu.c(), self.ws_gu.c(), h_r, h_s, isum_r=isum_r,
+                                 isum_s=isum_s)
+
+    def down_pair_f32(self, T, hq_r, hs_r, hq_s, hs_s, f, ys, isum_r=None, isum_s=None):
+        """Routed and shared down products in one launch from f16 paired
+        hidden codes: f [T*k, d] (sorted order) and ys [T, d]."""
+        B.expert_down_pair_f32(self.desc, T, hq_r, hs_r, hq_s, hs_s, self.offsets, self.w_d.c(),
+                               self.ws_d.c(), f, ys, isum_r=isum_r, isum_s=isum_s)
 
     def down(self, T, isum=None):
         B.expert_down(self.desc, T, self.hbuf, self.hscale, self.offsets, self.w_d.c(), self.f,

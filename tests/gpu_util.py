@@ -51,6 +51,20 @@ def decode_prepacked(qp: np.ndarray, sp: np.ndarray, n: int, rows: int, cols: in
     return q, s
 
 
+def decode_f16_paired(q16: np.ndarray, cols: int) -> np.ndarray:
+    """Inverse of the f16 paired code layout (include/mobmoe.h,
+    MM_ACT_F16_PAIRED): 16-bit values [rows, cols] -> int8 codes [rows, cols].
+    Slot s of each 8-column block holds column 2s (s < 4) or 2(s-4)+1, as a
+    half value divided by 16 for columns 4..7 of the block."""
+    v = q16.view(np.float16).astype(np.float32).reshape(-1, cols // 8, 8)
+    col_of_slot = np.array([0, 2, 4, 6, 1, 3, 5, 7])
+    out = np.empty_like(v)
+    out[:, :, col_of_slot] = v
+    out[:, :, 4:] *= 16.0
+    assert np.array_equal(out, np.rint(out)), "f16 paired values are not whole codes"
+    return out.reshape(-1, cols).astype(np.int8)
+
+
 def row_rel_err(gpu: np.ndarray, ref: np.ndarray) -> float:
     """max over rows of max_c |gpu - ref| / max_c |ref|."""
     g = gpu.astype(np.float64).reshape(gpu.shape[0], -1)

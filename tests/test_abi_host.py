@@ -223,13 +223,14 @@ def test_decode_noalloc_checks(lib):
 
 
 def test_layout_and_pair_checks(lib):
-    """mm_act_quant_i8_layout and mm_expert_gateup_pair_f32 validate before any launch."""
+    """mm_act_quant_i8_layout and the merged product entries validate before
+    any launch."""
     I32 = ctypes.c_int32
-    assert lib.mm_act_quant_i8_layout(4, 768, FAKE, FAKE, FAKE, I32(2), None) == B.MM_ERR_FORMAT
-    assert lib.mm_act_quant_i8_layout(4, 704, FAKE, FAKE, FAKE, I32(B.MM_ACT_GROUP_MAJOR),
-                                      None) == B.MM_ERR_SHAPE
-    assert lib.mm_act_quant_i8_layout(4, 768, None, FAKE, FAKE, I32(B.MM_ACT_GROUP_MAJOR),
-                                      None) == B.MM_ERR_NULL
+    assert lib.mm_act_quant_i8_layout(4, 768, FAKE, FAKE, FAKE, I32(3), None) == B.MM_ERR_FORMAT
+    assert lib.mm_act_quant_i8_layout(4, 768, FAKE, FAKE, FAKE, I32(-1), None) == B.MM_ERR_FORMAT
+    for lay in (B.MM_ACT_GROUP_MAJOR, B.MM_ACT_F16_PAIRED):
+        assert lib.mm_act_quant_i8_layout(4, 704, FAKE, FAKE, FAKE, I32(lay), None) == B.MM_ERR_SHAPE
+        assert lib.mm_act_quant_i8_layout(4, 768, None, FAKE, FAKE, I32(lay), None) == B.MM_ERR_NULL
     assert lib.mm_act_quant_i8_layout(0, 768, None, None, None, I32(B.MM_ACT_ROW_MAJOR),
                                       None) == B.MM_OK
     ds = S()
@@ -238,12 +239,30 @@ def test_layout_and_pair_checks(lib):
     assert lib.mm_expert_gateup_pair_f32(*args(ds, 0, None, w)) == B.MM_OK
     assert lib.mm_expert_gateup_pair_f32(*args(ds, 4, None, w)) == B.MM_ERR_NULL
     assert lib.mm_expert_gateup_pair_f32(*args(ds, 4, FAKE, B.Weight(FAKE, None))) == B.MM_ERR_NULL
+    assert lib.mm_expert_gateup_pair_f32(*args(ds, 4, FAKE + 8, w)) == B.MM_ERR_ALIGN
     bf = B.desc(768, 60, 384, 1536, 4, "bf16")
     assert lib.mm_expert_gateup_pair_f32(*args(bf, 4, FAKE, B.Weight(FAKE, None))) == B.MM_ERR_FORMAT
     noshared = B.desc(768, 60, 384, 0, 4)
     assert lib.mm_expert_gateup_pair_f32(*args(noshared, 4, FAKE, w)) == B.MM_ERR_SHAPE
-    odd = B.desc(704, 60, 320, 640, 4)
-    assert lib.mm_expert_gateup_pair_f32(*args(odd, 4, FAKE, w)) == B.MM_ERR_SHAPE
+    for odd in (B.desc(704, 60, 320, 640, 4), B.desc(768, 60, 352, 1536, 4),
+                B.desc(768, 60, 384, 1504, 4)):
+        assert lib.mm_expert_gateup_pair_f32(*args(odd, 4, FAKE, w)) == B.MM_ERR_SHAPE
+    # the group-sum twin needs its two extra outputs
+    assert lib.mm_expert_gateup_pair_f32_dbg(ctypes.byref(ds), 4, FAKE, FAKE, FAKE, FAKE, w, w, FAKE,
+                                             FAKE, None, FAKE, None) == B.MM_ERR_NULL
+    # the merged down products
+    dargs = lambda d, T, hr, wu, f: (ctypes.byref(d), T, hr, FAKE, FAKE, FAKE, FAKE, wu, wu, f,
+                                     FAKE, None)
+    assert lib.mm_expert_down_pair_f32(*dargs(ds, 0, None, w, None)) == B.MM_OK
+    assert lib.mm_expert_down_pair_f32(*dargs(ds, 4, None, w, FAKE)) == B.MM_ERR_NULL
+    assert lib.mm_expert_down_pair_f32(*dargs(ds, 4, FAKE, w, None)) == B.MM_ERR_NULL
+    assert lib.mm_expert_down_pair_f32(*dargs(ds, 4, FAKE, B.Weight(FAKE, None), FAKE)) == \
+        B.MM_ERR_NULL
+    assert lib.mm_expert_down_pair_f32(*dargs(bf, 4, FAKE, B.Weight(FAKE, None), FAKE)) == \
+        B.MM_ERR_FORMAT
+    assert lib.mm_expert_down_pair_f32(*dargs(noshared, 4, FAKE, w, FAKE)) == B.MM_ERR_SHAPE
+    assert lib.mm_expert_down_pair_f32_dbg(ctypes.byref(ds), 4, FAKE, FAKE, FAKE, FAKE, FAKE, w, w,
+                                           FAKE, FAKE, FAKE, None, None) == B.MM_ERR_NULL
 
 
 def test_linear_w4a8_checks(lib):

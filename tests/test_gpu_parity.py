@@ -15,8 +15,8 @@ import torch
 import oracle
 from sparse_moe_ffn_amd import binding as B
 from sparse_moe_ffn_amd import workloads as wl
-from gpu_util import (DEV, bf16_bits_to_f32, decode_prepacked, layer_output, make_layer, np_,
-                            oracle_forward, row_rel_err, unpack_canonical)
+from gpu_util import (DEV, bf16_bits_to_f32, decode_f16_paired, decode_prepacked, layer_output,
+                      make_layer, np_, oracle_forward, row_rel_err, unpack_canonical)
 
 pytestmark = pytest.mark.gpu
 
@@ -103,13 +103,16 @@ def test_act_quant_halfway_bitexact(cols):
     x = halfway_rows(cols, [1.0, 3.7, 1e-3, 123.456, 2.5e-30, 7e-36, 0.1, 5e4, 1.1754944e-38 * 3], 7)
     rows = x.shape[0]
     q_ref, s_ref = oracle.quant_act_i8(x)
-    for layout in (B.MM_ACT_ROW_MAJOR, B.MM_ACT_GROUP_MAJOR):
-        q = torch.empty((rows, cols), dtype=torch.int8, device=DEV)
+    for layout in (B.MM_ACT_ROW_MAJOR, B.MM_ACT_GROUP_MAJOR, B.MM_ACT_F16_PAIRED):
+        f16 = layout == B.MM_ACT_F16_PAIRED
+        q = torch.empty((rows, cols), dtype=torch.int16 if f16 else torch.int8, device=DEV)
         s = torch.empty((rows,), dtype=torch.float32, device=DEV)
         B.act_quant_i8_layout(rows, cols, dev(x), q, s, layout)
         qh = np_(q)
         if layout == B.MM_ACT_GROUP_MAJOR:  # byte (g * rows + r) * 32 + c % 32
             qh = qh.reshape(cols // 32, rows, 32).transpose(1, 0, 2).reshape(rows, cols)
+        elif f16:
+            qh = decode_f16_paired(qh, cols)
         assert np.array_equal(s_ref, np_(s))
         assert np.array_equal(qh, q_ref)
 
@@ -755,12 +758,28 @@ def test_expert_stages_int4(name, T, over):
     assert np.array_equal(np_(layer.f), f_ref)
 
 
-@pytest.mark.parametrize("name,T,over", [("s_prefill", 200, {}), ("s_prefill", 37, {}),
-                                         ("m_prefill", 300, {}), ("l_prefill", 130, {})])
+# Merged routed+shared products on the f16 matrix cores (the standalone merged
+# entries): ragged expert tiles, empty experts (skewed L routing), a tail of
+# one row, E = 1, and row counts from a single tile to many (dense problems
+# in 64- and 128-row tiles).
+PAIR_CASES = [("s_prefill", 200, {}), ("s_prefill", 37, {}), ("m_prefill", 300, {}),
+              ("l_prefill", 130, {}), ("s_prefill", 129, {"E": 1, "k": 1}),
+              ("s_prefill", 33, {"E": 64, "k": 8})]
+
+
+def _shared_reference(w, lw, x):
+    xq, sx = oracle.quant_act_i8(x)
+    gq, gs = oracle.quant_w4g32(lw.ws_gu)
+    dq, dsc = oracle.quant_w4g32(lw.ws_d)
+    return oracle.ffn_w4a8(xq, sx, gq, gs, dq, dsc, want_isum=True, want_a=True)
+
+
+@pytest.mark.parametrize("name,T,over", PAIR_CASES)
 def test_gateup_pair_f32(name, T, over):
     """The merged routed+shared gate/up launch (mm_expert_gateup_pair_f32) from
-    group-major x_q: the group-major codes are the row-major ones moved, and the
-    FP32 hidden rows equal the single gate/up call's and the oracle's."""
+    f16 paired x codes: the codes equal the row-major ones, the exact group
+    sums equal the oracle's, and the FP32 hidden rows equal the single
+    gate/up call's and the oracle's bit for bit."""
     w = wl.WORKLOADS[name].with_(T=T, **over)
     lw = wl.layer_weights(w)
     x = wl.tokens(w)
@@ -770,27 +789,71 @@ def test_gateup_pair_f32(name, T, over):
     layer.router(xd, T)
     layer.route(T)
     layer.act_quant(xd, T)
-    G = w.d // 32
-    xq_gm = torch.empty((T, w.d), dtype=torch.int8, device=DEV)
-    sx_gm = torch.empty((T,), dtype=torch.float32, device=DEV)
-    B.act_quant_i8_layout(T, w.d, xd, xq_gm, sx_gm, B.MM_ACT_GROUP_MAJOR)
-    rm = np_(layer.xq)
-    assert np.array_equal(np_(xq_gm).reshape(G, T, 32), rm.reshape(T, G, 32).transpose(1, 0, 2))
-    assert np.array_equal(np_(sx_gm), np_(layer.sx))
+    xq16 = torch.empty((T, w.d), dtype=torch.int16, device=DEV)
+    sx16 = torch.empty((T,), dtype=torch.float32, device=DEV)
+    B.act_quant_i8_layout(T, w.d, xd, xq16, sx16, B.MM_ACT_F16_PAIRED)
+    assert np.array_equal(decode_f16_paired(np_(xq16), w.d), np_(layer.xq))
+    assert np.array_equal(np_(sx16), np_(layer.sx))
     rows = T * w.k
+    G = w.d // 32
     h_r = torch.empty((rows, w.h), dtype=torch.float32, device=DEV)
     h_s = torch.empty((T, w.hs), dtype=torch.float32, device=DEV)
-    layer.gateup_pair_f32(T, xq_gm, h_r, h_s)
+    i_r = torch.zeros((rows, 2 * w.h, G), dtype=torch.int32, device=DEV)
+    i_s = torch.zeros((T, 2 * w.hs, G), dtype=torch.int32, device=DEV)
+    layer.gateup_pair_f32(T, xq16, h_r, h_s, isum_r=i_r, isum_s=i_s)
+    ref = _sorted_reference(layer, w, lw, x)
+    assert np.array_equal(np_(i_r), ref[3])
+    assert np.array_equal(np_(h_r), ref[5])
+    sref = _shared_reference(w, lw, x)
+    assert np.array_equal(np_(i_s), sref[3])
+    assert np.array_equal(np_(h_s), sref[5])
+    # the production form (no group sums written) gives the same rows
+    h_r2 = torch.empty_like(h_r)
+    h_s2 = torch.empty_like(h_s)
+    layer.gateup_pair_f32(T, xq16, h_r2, h_s2)
+    assert np.array_equal(np_(h_r2), np_(h_r))
+    assert np.array_equal(np_(h_s2), np_(h_s))
     a_one = torch.empty((rows, w.h), dtype=torch.float32, device=DEV)
     layer.gateup_f32(xd, T, a_one)
     assert np.array_equal(np_(h_r), np_(a_one))
-    a_ref = _sorted_reference(layer, w, lw, x)[5]
-    assert np.array_equal(np_(h_r), a_ref)
-    xq, sx = oracle.quant_act_i8(x)
-    gq, gs = oracle.quant_w4g32(lw.ws_gu)
-    dq, dsc = oracle.quant_w4g32(lw.ws_d)
-    a_s = oracle.ffn_w4a8(xq, sx, gq, gs, dq, dsc, want_a=True)[-1]
-    assert np.array_equal(np_(h_s), a_s)
+
+
+@pytest.mark.parametrize("name,T,over", PAIR_CASES)
+def test_down_pair_f32(name, T, over):
+    """The merged routed+shared down launch (mm_expert_down_pair_f32),
+    stage-isolated: the oracle's hidden codes go in as f16 paired codes, the
+    exact group sums and the FP32 outputs equal the oracle's bit for bit."""
+    w = wl.WORKLOADS[name].with_(T=T, **over)
+    lw = wl.layer_weights(w)
+    x = wl.tokens(w)
+    layer = make_layer(w, lw)
+    xd = dev(x)
+    layer.buffers(T)
+    layer.router(xd, T)
+    layer.route(T)
+    rows = T * w.k
+    hq_ref, hs_ref, f_ref, _, idn_ref, a_ref = _sorted_reference(layer, w, lw, x)
+    shq, shs, sys_, _, sidn, sa = _shared_reference(w, lw, x)
+    # the hidden codes through the f16 paired quantiser (codes equal the oracle's)
+    hq_r = torch.empty((rows, w.h), dtype=torch.int16, device=DEV)
+    hs_r = torch.empty((rows,), dtype=torch.float32, device=DEV)
+    hq_s = torch.empty((T, w.hs), dtype=torch.int16, device=DEV)
+    hs_s = torch.empty((T,), dtype=torch.float32, device=DEV)
+    B.act_quant_i8_layout(rows, w.h, dev(a_ref), hq_r, hs_r, B.MM_ACT_F16_PAIRED)
+    B.act_quant_i8_layout(T, w.hs, dev(sa), hq_s, hs_s, B.MM_ACT_F16_PAIRED)
+    assert np.array_equal(decode_f16_paired(np_(hq_r), w.h), hq_ref)
+    assert np.array_equal(np_(hs_r), hs_ref)
+    assert np.array_equal(decode_f16_paired(np_(hq_s), w.hs), shq)
+    assert np.array_equal(np_(hs_s), shs)
+    f = torch.empty((rows, w.d), dtype=torch.float32, device=DEV)
+    ys = torch.empty((T, w.d), dtype=torch.float32, device=DEV)
+    i_r = torch.zeros((rows, w.d, w.h // 32), dtype=torch.int32, device=DEV)
+    i_s = torch.zeros((T, w.d, w.hs // 32), dtype=torch.int32, device=DEV)
+    layer.down_pair_f32(T, hq_r, hs_r, hq_s, hs_s, f, ys, isum_r=i_r, isum_s=i_s)
+    assert np.array_equal(np_(i_r), idn_ref)
+    assert np.array_equal(np_(f), f_ref.astype(np.float32))
+    assert np.array_equal(np_(i_s), sidn)
+    assert np.array_equal(np_(ys), sys_.astype(np.float32))
 
 
 # ------------------------------------------------------------ whole layer
