@@ -156,6 +156,11 @@ size_t mm_prepacked_scale_bytes(int64_t rows, int64_t cols);
  * Rearranges `n_mat` stacked canonical INT4 matrices [n_mat][rows][cols]
  * (layout of mm_quantize_int4g32) into the kernels' layout.  The prepacked
  * layout is private to this library version: pass it only to the calls below.
+ * It keeps each group scale as s / 16 in FP32 (the kernels unpack nibbles as
+ * 16 q).  For every group with s >= 2^-122 (max|W| >= 7.5 * 2^-122) that
+ * quotient is exact and the products are bit-identical to s * sum; below,
+ * s / 16 is subnormal and may round, and that group's term is then exact only
+ * to within 2^-149 / (s / 16) relative.
  *   q_canon, s_canon   device, canonical nibbles and scales
  *   q_out, s_out       device, n_mat * mm_prepacked_bytes / _scale_bytes
  */

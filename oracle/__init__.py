@@ -39,8 +39,15 @@ def build(force: bool = True) -> str:
 
 
 def _load():
+    """Loads the oracle library (MOBMOE_ORACLE_LIB names another build of the
+    same source, e.g. the sanitizer build of tests/test_sanitizers.py)."""
     global _lib
     if _lib is None:
+        other = os.environ.get("MOBMOE_ORACLE_LIB")
+        if other:
+            _lib = ctypes.CDLL(other)
+            _lib.ora_version.restype = ctypes.c_char_p
+            return _lib
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build(force=True)
         _lib = ctypes.CDLL(_LIB)

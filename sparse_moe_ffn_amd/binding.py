@@ -13,7 +13,9 @@ import os
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmobmoe.so")
+# MOBMOE_LIB names another build of the same sources (the host-sanitizer build
+# of the argument checks, tests/test_sanitizers.py).
+LIB_PATH = os.environ.get("MOBMOE_LIB") or os.path.join(HERE, "libmobmoe.so")
 
 MM_OK, MM_ERR_NULL, MM_ERR_SHAPE, MM_ERR_ALIGN, MM_ERR_FORMAT, MM_ERR_WORKSPACE, MM_ERR_HIP = range(7)
 MM_W_F32, MM_W_INT4G32, MM_W_BF16 = range(3)

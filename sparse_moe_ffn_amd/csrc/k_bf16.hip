@@ -8,13 +8,20 @@
 // FP32; no quantisation scales are involved, so the MFMA accumulates straight
 // into the output registers.
 //
-// Tiling.  A workgroup is one wave that owns kMT x 32 rows of one expert and
-// two 32-column tiles (gate/up: the gate tile and the matching up tile of the
-// same 32 hidden columns, so SwiGLU is applied in registers).  Each lane
-// loads 16 bytes (8 BF16 values) of its row per operand and K step of 16,
-// two K steps at a time, one stage ahead of the math; no LDS, no barriers.
-// Tiles are ordered row tile fastest, so the waves working on one column
-// slice of an expert run together and share that slice of the weights in L2.
+// Three forms, chosen by row count (launch_*_bf16_mfma below):
+//  - k_bf16_lds, 128 rows and more: four waves share a 128-row x 128-weight-row
+//    tile staged through LDS in double-buffered K blocks of 32 (each global
+//    byte feeds two waves' matrix-core products);
+//  - k_bf16w, fewer rows: a workgroup is one wave that owns kMT x 32 rows of
+//    one expert and two 32-column tiles (gate/up: the gate tile and the
+//    matching up tile of the same 32 hidden columns, so SwiGLU is applied in
+//    registers); each lane loads 16 bytes (8 BF16 values) of its row per
+//    operand and K step of 16, two K steps at a time, one stage ahead of the
+//    math; no LDS, no barriers; tiles are ordered row tile fastest, so the
+//    waves working on one column slice of an expert share it in L2;
+//  - k_bf16_gemv, decode batches (a few rows per expert): weight streaming,
+//    each wave one weight row pair with all of its 16-byte loads issued before
+//    the math, FP32 dot products reduced across the wave.
 #include "common.h"
 #include "launch.h"
 

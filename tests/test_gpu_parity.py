@@ -142,6 +142,39 @@ def test_linear_w4a8_bitexact(rows, K, N):
     assert np.array_equal(np_(y), y_ref)
 
 
+@pytest.mark.parametrize("rows", [1, 65])
+def test_linear_w4a8_tiny_scales(rows):
+    """Weight groups whose scale s falls below 2^-122 (the prepacked s / 16 is
+    then subnormal, include/mobmoe.h): every output column whose groups all
+    have s >= 2^-122 stays bit-exact; the columns with tiny groups stay within
+    the documented rounding of s / 16 (2^-149 / (s / 16) relative per group)."""
+    from sparse_moe_ffn_amd.layer import prepare_weight
+    K, N = 768, 256
+    g = rng(4242 + rows)
+    x = g.standard_normal((rows, K)).astype(np.float32)
+    wt = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    wt[0] *= np.float32(5e-36)       # s about 1.3e-38: s / 16 subnormal
+    wt[1, :32] *= np.float32(5e-35)  # one tiny group in an otherwise normal row
+    wt[2] *= np.float32(2.0 ** -110)  # s about 2^-114: exact
+    xq_ref, sx_ref = oracle.quant_act_i8(x)
+    wq_ref, ws_ref = oracle.quant_w4g32(wt)
+    assert ws_ref[0].max() < 2.0 ** -122 and ws_ref[2].min() > 2.0 ** -122
+    y_ref = oracle.linear_w4a8(xq_ref, sx_ref, wq_ref, ws_ref)
+    dw = prepare_weight(wt, "int4g32", DEV)
+    xq = torch.empty((rows, K), dtype=torch.int8, device=DEV)
+    sx = torch.empty((rows,), dtype=torch.float32, device=DEV)
+    B.act_quant_i8(rows, K, dev(x), xq, sx)
+    yd = torch.empty((rows, N), dtype=torch.float32, device=DEV)
+    B.linear_w4a8(rows, K, N, xq, sx, dw.c(), yd)
+    y = np_(yd)
+    tiny = (ws_ref < 2.0 ** -122).any(axis=1)
+    assert list(np.flatnonzero(tiny)) == [0, 1]
+    assert np.array_equal(y[:, ~tiny], y_ref[:, ~tiny])
+    for c in (0, 1):
+        err = np.abs(y[:, c].astype(np.float64) - y_ref[:, c]).max()
+        assert err <= 1e-5 * np.abs(y_ref[:, c]).max() + 2.0 ** -149
+
+
 # ------------------------------------------------------------ GQA decode attention, INT8 KV cache
 def _quant_rows_i8(x):
     """Cache contents for float vectors [..., 64] by the oracle's INT8 row rule."""
