@@ -154,7 +154,7 @@ def test_linear_w4a8_tiny_scales(rows):
     x = g.standard_normal((rows, K)).astype(np.float32)
     wt = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
     wt[0] *= np.float32(5e-36)       # s about 1.3e-38: s / 16 subnormal
-    wt[1, :32] *= np.float32(5e-35)  # one tiny group in an otherwise normal row
+    wt[1, :32] *= np.float32(5e-36)  # one tiny group in an otherwise normal row
     wt[2] *= np.float32(2.0 ** -110)  # s about 2^-114: exact
     xq_ref, sx_ref = oracle.quant_act_i8(x)
     wq_ref, ws_ref = oracle.quant_w4g32(wt)
@@ -1095,6 +1095,49 @@ def test_decode_stack_teacher_forced(B_):
         assert np.array_equal(np_(layer.y), y_calls)
         assert row_rel_err(np_(nxt2), oracle.rmsnorm(y_calls, 1e-5)) < 1e-5
         cur = nxt
+
+
+@pytest.mark.parametrize("B_", [1, 8])
+def test_decode_stack_free_running(B_):
+    """The 20-layer S decode stack run free: the device layers (the one-launch
+    layer for B = 1, the one-call layer for B = 8) feed each layer's
+    RMS-normalised output to the next.  Every layer is checked against the
+    oracle on the input the device layer received (routing and y bit-exact,
+    the device RMSNorm within 1e-6 of the oracle's).  Beside it the oracle
+    runs its own free trajectory; the two RMSNorms round differently (FP32 on
+    the device, double then FP32 in the oracle), so the trajectories agree
+    until such an ulp moves an INT8 code across a rounding boundary, and then
+    part ways (the stack has no residual path, so random layers amplify any
+    difference).  The test prints the routing flips and row errors of the two
+    free trajectories per layer."""
+    w = wl.WORKLOADS["s_decode"].with_(T=B_)
+    x = wl.tokens(w, step=0)
+    cur_dev = dev(x)
+    cur_ref = x.copy()
+    flips, errs = [], []
+    for l in range(w.layers):
+        lw = wl.layer_weights(w, layer=l)
+        layer = make_layer(w, lw)
+        xin = np_(cur_dev).copy()
+        nxt = torch.empty_like(cur_dev)
+        if layer.decode_supported(B_):
+            layer.forward_decode(cur_dev, y_norm=nxt, norm_eps=1e-5)
+        else:
+            layer.forward_fused(cur_dev, y_norm=nxt, norm_eps=1e-5)
+        y = np_(layer.y).copy()
+        forced = oracle_forward(w, lw, xin)
+        assert np.array_equal(np_(layer.idx), forced.idx), f"layer {l}"
+        assert np.array_equal(y, forced.y.astype(np.float32)), f"layer {l}"
+        assert row_rel_err(np_(nxt), oracle.rmsnorm(y, 1e-5)) < 1e-6, f"layer {l}"
+        free = forced if l == 0 else oracle_forward(w, lw, cur_ref)
+        flips.append(int((np.sort(np_(layer.idx), 1) != np.sort(free.idx, 1)).any(1).sum()))
+        errs.append(row_rel_err(y, free.y))
+        cur_dev = nxt
+        cur_ref = oracle.rmsnorm(free.y.astype(np.float32), 1e-5).astype(np.float32)
+        del layer
+    print(f"B = {B_}: free trajectories, tokens with a routing flip per layer {flips}; "
+          f"max row error per layer {[f'{e:.1e}' for e in errs]}")
+    assert flips[0] == 0 and errs[0] == 0.0
 
 
 # ------------------------------------------------------------ graph replay
