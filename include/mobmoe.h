@@ -471,6 +471,14 @@ mm_status mm_linear_w4a8(int64_t rows, int64_t in_features, int64_t out_features
  * v1 limits: d_h = 64; n_h a multiple of n_kv with n_h / n_kv <= 8.
  */
 
+/* Bytes of one INT8 KV cache (keys or values) of the layout above for B
+ * sequences of max_T positions: which = MM_KV_CODES gives the codes
+ * (B * n_kv * max_T * d_h, one byte per value: eq. (5)'s b_kv = 8 term for
+ * one layer's keys or values), MM_KV_SCALES their FP32 scales (4 bytes per
+ * (position, head) vector).  0 for invalid sizes. */
+enum { MM_KV_CODES = 0, MM_KV_SCALES = 1 };
+size_t mm_kv_cache_bytes(int64_t B, int32_t n_kv, int32_t d_h, int64_t max_T, int32_t which);
+
 /* Workspace of mm_attn_decode_i8 for B sequences of at most max_len positions
  * (0 for invalid sizes). */
 size_t mm_attn_workspace_bytes(int64_t B, int32_t n_kv, int64_t max_len);
@@ -649,6 +657,17 @@ mm_status mm_router_backward_f32(const mm_layer_desc* desc, int64_t T, const flo
  * workload (not part of eq. (*)): y = x / sqrt(mean(x^2) + eps), FP32. */
 mm_status mm_rmsnorm_f32(int64_t rows, int64_t cols, float eps, const float* x, float* y,
                          void* stream);
+
+/*
+ * The join of a decoder block's sub-layers (section "MoE preliminaries and
+ * three design factors": each layer is attention plus the FFN on the
+ * residual stream): sum = x + r (FP32, elementwise) and, when norm is not
+ * NULL, norm = RMSNorm(sum) with eps (> 0) and unit gain, the next
+ * sub-layer's input.  All device FP32 [rows][cols]; outputs must not alias
+ * inputs.  Errors: MM_ERR_NULL / MM_ERR_ALIGN, MM_ERR_SHAPE.
+ */
+mm_status mm_add_rmsnorm_f32(int64_t rows, int64_t cols, float eps, const float* x, const float* r,
+                             float* sum, float* norm, void* stream);
 
 /*
  * Test-only twins of the INT4 gate/up and down calls that also write the

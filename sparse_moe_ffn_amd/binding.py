@@ -40,6 +40,7 @@ EXPORTS = (
     "mm_expert_backward_f32", "mm_router_backward_f32", "mm_set_profile_events",
     "mm_moe_decode", "mm_moe_decode_supported", "mm_moe_decode_noalloc",
     "mm_expert_gateup_pair_f32_dbg", "mm_expert_down_pair_f32", "mm_expert_down_pair_f32_dbg",
+    "mm_add_rmsnorm_f32", "mm_kv_cache_bytes",
 )
 
 
@@ -99,6 +100,8 @@ _SIGS = {
     "mm_shared_expert": ([_DESC, _I64, _VP, _VP, Weight, Weight, _VP, _VP, _SZ, _VP], ctypes.c_int),
     "mm_combine": ([_DESC, _I64, _VP, _VP, _VP, _VP, _VP, _VP], ctypes.c_int),
     "mm_rmsnorm_f32": ([_I64, _I64, _F, _VP, _VP, _VP], ctypes.c_int),
+    "mm_add_rmsnorm_f32": ([_I64, _I64, _F, _VP, _VP, _VP, _VP, _VP], ctypes.c_int),
+    "mm_kv_cache_bytes": ([_I64, _I32, _I32, _I64, _I32], _SZ),
     "mm_linear_w4a8": ([_I64, _I64, _I64, _VP, _VP, Weight, _VP, _VP], ctypes.c_int),
     "mm_attn_workspace_bytes": ([_I64, _I32, _I64], _SZ),
     "mm_kv_append_i8": ([_I64, _I32, _I32, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
@@ -417,3 +420,15 @@ def router_backward_f32(ds, T, x, w_router, bias, topk_idx, f, inv, dy, lambda_z
 def rmsnorm_f32(rows, cols, eps, x, y, stream=None):
     _check(load().mm_rmsnorm_f32(rows, cols, eps, _ptr(x), _ptr(y), _stream(stream)),
            "mm_rmsnorm_f32")
+
+
+def add_rmsnorm_f32(rows, cols, eps, x, r, out_sum, out_norm=None, stream=None):
+    _check(load().mm_add_rmsnorm_f32(rows, cols, eps, _ptr(x), _ptr(r), _ptr(out_sum),
+                                     _ptr(out_norm), _stream(stream)), "mm_add_rmsnorm_f32")
+
+
+MM_KV_CODES, MM_KV_SCALES = 0, 1
+
+
+def kv_cache_bytes(B, n_kv, d_h, max_T, which) -> int:
+    return int(load().mm_kv_cache_bytes(B, n_kv, d_h, max_T, which))

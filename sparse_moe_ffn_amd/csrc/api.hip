@@ -1210,4 +1210,29 @@ mm_status mm_rmsnorm_f32(int64_t rows, int64_t cols, float eps, const float* x, 
   return hip_status(mm::launch_rmsnorm(rows, cols, eps, x, y, S(stream)), "mm_rmsnorm_f32");
 }
 
+mm_status mm_add_rmsnorm_f32(int64_t rows, int64_t cols, float eps, const float* x, const float* r,
+                             float* sum, float* norm, void* stream) {
+  if (rows < 0 || cols <= 0) return fail(MM_ERR_SHAPE, "bad shape");
+  if (norm && !(eps > 0.0f)) return fail(MM_ERR_SHAPE, "eps must be positive");
+  if (rows == 0) return MM_OK;
+  MM_REQUIRE(x);
+  MM_REQUIRE(r);
+  MM_REQUIRE(sum);
+  MM_OPTIONAL(norm);
+  if (sum == x || sum == r || (norm && (norm == x || norm == r || norm == sum)))
+    return fail(MM_ERR_SHAPE, "outputs must not alias the inputs or each other");
+  return hip_status(mm::launch_add_rmsnorm(rows, cols, eps, x, r, sum, norm, S(stream)),
+                    "mm_add_rmsnorm_f32");
+}
+
+size_t mm_kv_cache_bytes(int64_t B, int32_t n_kv, int32_t d_h, int64_t max_T, int32_t which) {
+  if (B < 0 || n_kv < 1 || d_h < 1 || max_T < 0) return 0;
+  const size_t vectors = (size_t)B * (size_t)n_kv * (size_t)max_T;
+  switch (which) {
+    case MM_KV_CODES: return vectors * (size_t)d_h;  // one byte per value
+    case MM_KV_SCALES: return vectors * sizeof(float);
+    default: return 0;
+  }
+}
+
 }  // extern "C"

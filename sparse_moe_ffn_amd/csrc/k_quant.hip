@@ -250,6 +250,33 @@ __global__ __launch_bounds__(256) void k_rmsnorm(int64_t rows, int64_t cols, flo
   for (int64_t c = lane; c < cols; c += kWave) y[r * cols + c] = xr[c] * inv;
 }
 
+// Residual add and (optionally) the RMSNorm of the sum, one wave per row:
+// sum = x + r (FP32), norm = sum / sqrt(mean(sum^2) + eps) with the sum of
+// squares accumulated as k_rmsnorm does.  The join of a decoder block's
+// sub-layers (the residual stream and the next sub-layer's normalised input).
+__global__ __launch_bounds__(256) void k_add_rmsnorm(int64_t rows, int64_t cols, float eps,
+                                                     const float* __restrict__ x,
+                                                     const float* __restrict__ r,
+                                                     float* __restrict__ sum,
+                                                     float* __restrict__ norm) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float* xr = x + row * cols;
+  const float* rr = r + row * cols;
+  float* sr = sum + row * cols;
+  float ss = 0.0f;
+  for (int64_t c = lane; c < cols; c += kWave) {
+    const float v = xr[c] + rr[c];
+    sr[c] = v;
+    ss = fmaf(v, v, ss);
+  }
+  if (norm == nullptr) return;
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)cols + eps);
+  for (int64_t c = lane; c < cols; c += kWave) norm[row * cols + c] = (xr[c] + rr[c]) * inv;
+}
+
 inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
 
 }  // namespace
@@ -311,6 +338,13 @@ hipError_t launch_act_quant_i8_pair(int64_t rows0, int64_t cols0, const float* x
 
 hipError_t launch_convert_bf16(int64_t n, const float* x, uint16_t* y, hipStream_t st) {
   hipLaunchKernelGGL(k_convert_bf16, dim3(blocks_for(n, 256)), dim3(256), 0, st, n, x, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_add_rmsnorm(int64_t rows, int64_t cols, float eps, const float* x,
+                              const float* r, float* sum, float* norm, hipStream_t st) {
+  hipLaunchKernelGGL(k_add_rmsnorm, dim3(blocks_for(rows, 4)), dim3(256), 0, st, rows, cols, eps,
+                     x, r, sum, norm);
   return hipGetLastError();
 }
 

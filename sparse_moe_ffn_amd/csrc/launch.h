@@ -34,6 +34,9 @@ hipError_t launch_act_quant_i8_pair(int64_t rows0, int64_t cols0, const float* x
 hipError_t launch_convert_bf16(int64_t n, const float* x, uint16_t* y, hipStream_t st);
 hipError_t launch_rmsnorm(int64_t rows, int64_t cols, float eps, const float* x, float* y,
                           hipStream_t st);
+// sum = x + r; norm (may be null) = RMSNorm(sum) with eps, unit gain.
+hipError_t launch_add_rmsnorm(int64_t rows, int64_t cols, float eps, const float* x,
+                              const float* r, float* sum, float* norm, hipStream_t st);
 
 // Router (k_router.hip)
 // xq / sx non-null: also the per-token INT8 quantisation of x (in the same

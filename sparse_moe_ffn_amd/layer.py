@@ -274,3 +274,91 @@ class MoELayer:
                 self.shared(x, T)
         self.combine(T)
         return self.y
+
+
+class DecoderBlock:
+    """One MobileMoE decoder block for decode steps (one new token per
+    sequence): the MoE-FFN layer with its neighbours ([P1] "MoE preliminaries
+    and three design factors": each layer is grouped-query attention plus the
+    FFN on the residual stream; "Quantisation-aware training": every linear
+    layer in W4A8; eq. (5): the KV cache in 8 bits).
+
+        a  = RMSNorm(x)
+        q, k, v = W4A8 projections of a        (n_h, n_kv heads of 64)
+        append k, v at pos[b] of the INT8 KV caches
+        o  = GQA decode attention of q over positions 0 .. lens[b] - 1
+        h  = x + W4A8(o) ;  a2 = RMSNorm(h)
+        y  = h + MoE-FFN(a2)
+
+    Positional encoding (RoPE) is the caller's: q and k are used as the
+    projections give them.  Every step runs in the library's kernels through
+    the C ABI; torch holds the buffers."""
+
+    def __init__(self, moe: MoELayer, n_h: int, n_kv: int, wq, wk, wv, wo, batch: int, max_T: int,
+                 eps: float = 1e-5):
+        if moe.wfmt != "int4g32" or moe.desc.out_dtype != B.MM_OUT_F32:
+            raise ValueError("the decoder block runs the INT4 layer with FP32 output")
+        d, dev = moe.d, moe.device
+        self.moe, self.n_h, self.n_kv, self.B, self.max_T, self.eps = moe, n_h, n_kv, batch, max_T, eps
+        self.d, self.dh = d, 64
+        qd, kd = n_h * 64, n_kv * 64
+        if wq.shape != (qd, d) or wk.shape != (kd, d) or wv.shape != (kd, d) or wo.shape != (d, qd):
+            raise ValueError("projection shapes do not match n_h, n_kv and d")
+        self.wq, self.wk = prepare_weight(wq, "int4g32", dev), prepare_weight(wk, "int4g32", dev)
+        self.wv, self.wo = prepare_weight(wv, "int4g32", dev), prepare_weight(wo, "int4g32", dev)
+        f32, i8 = torch.float32, torch.int8
+        self.a = _empty((batch, d), f32, dev)
+        self.aq, self.asc = _empty((batch, d), i8, dev), _empty((batch,), f32, dev)
+        self.q = _empty((batch, qd), f32, dev)
+        self.k, self.v = _empty((batch, kd), f32, dev), _empty((batch, kd), f32, dev)
+        self.o = _empty((batch, qd), f32, dev)
+        self.oq, self.osc = _empty((batch, qd), i8, dev), _empty((batch,), f32, dev)
+        self.attn = _empty((batch, d), f32, dev)
+        self.h, self.a2, self.y = (_empty((batch, d), f32, dev) for _ in range(3))
+        # caches [B][n_kv][max_T][64] codes and [B][n_kv][max_T] scales
+        cb = B.kv_cache_bytes(batch, n_kv, 64, max_T, B.MM_KV_CODES)
+        sb = B.kv_cache_bytes(batch, n_kv, 64, max_T, B.MM_KV_SCALES) // 4
+        self.kc = torch.zeros((cb,), dtype=i8, device=dev)
+        self.vc = torch.zeros((cb,), dtype=i8, device=dev)
+        self.ks = torch.zeros((sb,), dtype=f32, device=dev)
+        self.vs = torch.zeros((sb,), dtype=f32, device=dev)
+        self.ws, self.ws_bytes, self._ws_len = None, 0, 0
+
+    def load_context(self, kq: np.ndarray, vq: np.ndarray, ks: np.ndarray, vs: np.ndarray):
+        """Copies an existing cache (codes [B, n_kv, max_T, 64] int8, scales
+        [B, n_kv, max_T] FP32) to the device."""
+        for dst, src in ((self.kc, kq), (self.vc, vq), (self.ks, ks), (self.vs, vs)):
+            dst.copy_(_dev(src, self.moe.device).reshape(-1))
+
+    def _attn_ws(self, max_len: int):
+        if max_len > self._ws_len:
+            nb = max(B.attn_workspace_bytes(self.B, self.n_kv, max_len), 256)
+            self.ws = torch.empty((nb,), dtype=torch.uint8, device=self.moe.device)
+            self.ws_bytes, self._ws_len = nb, max_len
+
+    def decode(self, x: torch.Tensor, pos: torch.Tensor, lens: torch.Tensor, max_len: int) -> torch.Tensor:
+        """One decode step: x [B, d] FP32; pos [B] int32 (cache slot of the new
+        token; outside 0 .. max_T - 1 skips the append), lens [B] int32
+        (positions attended after the append, 0 .. max_len), max_len
+        <= max_T.  Returns the block output y [B, d]."""
+        Bn, d = self.B, self.d
+        qd, kd = self.n_h * 64, self.n_kv * 64
+        if tuple(x.shape) != (Bn, d) or max_len < 1 or max_len > self.max_T:
+            raise ValueError("x must be [B, d] and 1 <= max_len <= max_T")
+        self._attn_ws(max_len)
+        B.rmsnorm_f32(Bn, d, self.eps, x, self.a)
+        B.act_quant_i8(Bn, d, self.a, self.aq, self.asc)
+        B.linear_w4a8(Bn, d, qd, self.aq, self.asc, self.wq.c(), self.q)
+        B.linear_w4a8(Bn, d, kd, self.aq, self.asc, self.wk.c(), self.k)
+        B.linear_w4a8(Bn, d, kd, self.aq, self.asc, self.wv.c(), self.v)
+        B.kv_append_i8(Bn, self.n_kv, 64, self.max_T, pos, self.k, self.v, self.kc, self.vc,
+                       self.ks, self.vs)
+        B.attn_decode_i8(Bn, self.n_h, self.n_kv, 64, self.max_T, max_len, lens, self.q, self.kc,
+                         self.vc, self.ks, self.vs, self.o, self.ws, self.ws_bytes)
+        B.act_quant_i8(Bn, qd, self.o, self.oq, self.osc)
+        B.linear_w4a8(Bn, qd, d, self.oq, self.osc, self.wo.c(), self.attn)
+        B.add_rmsnorm_f32(Bn, d, self.eps, x, self.attn, self.h, self.a2)
+        m = self.moe.forward_decode(self.a2) if self.moe.decode_supported(Bn) else \
+            self.moe.forward_fused(self.a2)
+        B.add_rmsnorm_f32(Bn, d, self.eps, self.h, m, self.y, None)
+        return self.y

@@ -21,6 +21,8 @@ from typing import Dict, Optional, Tuple
 import numpy as np
 
 TENSOR_ROUTER, TENSOR_GATEUP, TENSOR_DOWN, TENSOR_SGATEUP, TENSOR_SDOWN, TENSOR_ZIPF = range(6)
+TENSOR_WQ, TENSOR_WK, TENSOR_WV, TENSOR_WO, TENSOR_KV = range(6, 11)
+HEAD_DIM, KV_HEADS = 64, 4
 
 
 @dataclass(frozen=True)
@@ -117,6 +119,44 @@ def layer_weights(w: Workload, layer: int = 0) -> LayerWeights:
         ws_d = _normal(weight_seed(w, layer, TENSOR_SDOWN), (w.d, w.hs), sd)
     bias = zipf_bias(w, layer) if w.bias == "zipf" else None
     return LayerWeights(wr, bias, w_gu, w_d, ws_gu, ws_d)
+
+
+@dataclass
+class AttnWeights:
+    n_h: int                       # query heads (d / 64)
+    n_kv: int                      # key/value heads
+    wq: np.ndarray                 # [n_h * 64, d]
+    wk: np.ndarray                 # [n_kv * 64, d]
+    wv: np.ndarray                 # [n_kv * 64, d]
+    wo: np.ndarray                 # [d, n_h * 64]
+
+
+def attn_weights(w: Workload, layer: int = 0) -> AttnWeights:
+    """The attention projections of the decoder block around the layer: GQA
+    with KV_HEADS heads of HEAD_DIM and d / HEAD_DIM query heads
+    (section "MoE preliminaries and three design factors"; "Mid-training":
+    n_kv = 4, d_h = 64), FP32 ~ N(0, std^2) from per-tensor seeds."""
+    n_h, sd = w.d // HEAD_DIM, w.weight_std
+    qd, kd = n_h * HEAD_DIM, KV_HEADS * HEAD_DIM
+    return AttnWeights(n_h, KV_HEADS,
+                       _normal(weight_seed(w, layer, TENSOR_WQ), (qd, w.d), sd),
+                       _normal(weight_seed(w, layer, TENSOR_WK), (kd, w.d), sd),
+                       _normal(weight_seed(w, layer, TENSOR_WV), (kd, w.d), sd),
+                       _normal(weight_seed(w, layer, TENSOR_WO), (w.d, qd), sd))
+
+
+def kv_context(w: Workload, B: int, max_T: int, layer: int = 0):
+    """Earlier context already in an INT8 KV cache: codes uniform in
+    [-127, 127] and per-vector scales uniform in [0.5, 1.5] / 127, as
+    (k_codes, v_codes [B, n_kv, max_T, 64] int8, k_scales, v_scales
+    [B, n_kv, max_T] FP32)."""
+    g = np.random.Generator(np.random.PCG64(weight_seed(w, layer, TENSOR_KV) + 7919 * B + max_T))
+    shp = (B, KV_HEADS, max_T, HEAD_DIM)
+    kq = g.integers(-127, 128, shp, dtype=np.int8)
+    vq = g.integers(-127, 128, shp, dtype=np.int8)
+    ks = (g.uniform(0.5, 1.5, shp[:3]) / 127).astype(np.float32)
+    vs = (g.uniform(0.5, 1.5, shp[:3]) / 127).astype(np.float32)
+    return kq, vq, ks, vs
 
 
 def tokens(w: Workload, step: int = 0, T: Optional[int] = None) -> np.ndarray:

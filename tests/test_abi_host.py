@@ -350,3 +350,42 @@ def test_profile_events_checks(lib):
     assert lib.mm_set_profile_events(FAKE, None) == B.MM_ERR_NULL
     assert lib.mm_set_profile_events(None, FAKE) == B.MM_ERR_NULL
     assert lib.mm_set_profile_events(None, None) == B.MM_OK
+
+
+def test_add_rmsnorm_checks(lib):
+    """Residual add + RMSNorm: shape, eps, NULL and aliasing checks on the host."""
+    f = lib.mm_add_rmsnorm_f32
+    assert f(0, 768, 1e-5, None, None, None, None, None) == B.MM_OK
+    assert f(2, 0, 1e-5, FAKE, FAKE, FAKE, FAKE, None) == B.MM_ERR_SHAPE
+    assert f(-1, 768, 1e-5, FAKE, FAKE, FAKE, FAKE, None) == B.MM_ERR_SHAPE
+    assert f(2, 768, 0.0, FAKE, FAKE, FAKE + 4096, FAKE + 8192, None) == B.MM_ERR_SHAPE
+    assert f(2, 768, 1e-5, None, FAKE, FAKE + 4096, None, None) == B.MM_ERR_NULL
+    assert f(2, 768, 1e-5, FAKE, None, FAKE + 4096, None, None) == B.MM_ERR_NULL
+    assert f(2, 768, 1e-5, FAKE, FAKE + 4096, None, None, None) == B.MM_ERR_NULL
+    assert f(2, 768, 1e-5, FAKE, FAKE + 4096, FAKE, None, None) == B.MM_ERR_SHAPE        # sum == x
+    assert f(2, 768, 1e-5, FAKE, FAKE + 4096, FAKE + 8192, FAKE + 8192, None) == B.MM_ERR_SHAPE
+
+
+def test_kv_cache_bytes_match_eq5():
+    """The library's INT8 KV cache for MobileMoE-S/M/L (20/26/32 layers, 4 KV
+    heads of 64) at the 8K mid-training context: its code bytes for K and V
+    over all layers equal eq. (5)'s KV-cache term with b_kv = 8, and its
+    per-vector FP32 scales add one sixteenth of that.  With the printed total
+    parameter counts in INT4 (eq. (5)'s weight term) each model's memory
+    function stays under the page's DRAM budget of about 5 GB."""
+    import json
+    g = {e["key"]: e["value"] for e in
+         json.load(open(os.path.join(ROOT, "tests", "golden", "mobilemoe_printed_shapes.json")))["entries"]}
+    T, n_kv, d_h, b_kv, b_w = (g["mid_training_context"], g["kv_heads"], g["head_dim"], g["kv_bits"],
+                               g["weight_bits"])
+    for key, n_l in (("S", 20), ("M", 26), ("L", 32)):
+        term = b_kv * 2 * T * n_l * n_kv * d_h // 8                 # eq. (5), bytes
+        codes = B.kv_cache_bytes(1, n_kv, d_h, T, B.MM_KV_CODES)    # one layer, one of K / V
+        scales = B.kv_cache_bytes(1, n_kv, d_h, T, B.MM_KV_SCALES)
+        assert 2 * n_l * codes == term
+        assert 2 * n_l * scales * 16 == term
+        assert B.kv_cache_bytes(8, n_kv, d_h, T, B.MM_KV_CODES) == 8 * codes
+        mem = b_w / 8 * g[f"total_params_{key}"] + term
+        assert mem < g["dram_budget_bytes"], (key, mem)
+    assert B.kv_cache_bytes(1, 0, 64, T, B.MM_KV_CODES) == 0
+    assert B.kv_cache_bytes(1, 4, 64, T, 7) == 0
