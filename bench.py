@@ -81,10 +81,14 @@ def layer_work(w, T, counts=None):
 
 
 # Kernel chosen by the library for the routed expert products (mirrors the
-# dispatch in csrc/api.hip and csrc/k_mfma.hip: weight-streaming up to 512
-# routed rows when the reduction length fits, matrix cores from 256 rows when
-# K % 128 == 0, with two row tiles per wave once that still gives 4096 waves;
+# dispatch in csrc/api.hip and csrc/k_mfma.hip: weight-streaming up to 32
+# routed rows (8 shared rows) when the reduction length fits, matrix cores
+# beyond when K % 128 == 0, with two row tiles per wave once that still gives
+# 4096 waves;
 # BF16 weights always on the bf16 matrix cores).
+GEMV_MAX_ROUTED, GEMV_MAX_DENSE = 32, 8  # csrc/launch.h kGemvMaxRowsRouted / kGemvMaxRowsDense
+
+
 def kernel_of(w, T, gateup: bool):
     """(kernel name as rocprofv3 lists it, path) of the routed gate/up or down product."""
     rows, K = T * w.k, (w.d if gateup else w.h)
@@ -97,9 +101,9 @@ def kernel_of(w, T, gateup: bool):
         return f"k_bf16w<2, {gu}, false>", "matrix-core"
     if w.wfmt != "int4g32":
         return ("k_gateup_fp<false>" if gateup else "k_down_fp<false>"), "row-tile"
-    if rows <= 512 and K % 64 == 0 and K <= 2560:
+    if rows <= GEMV_MAX_ROUTED and K % 64 == 0 and K <= 2560:
         return f"k_gemv_i4<4, {gu}, false, false>", "weight-streaming"
-    if rows >= 256 and K % 128 == 0:
+    if rows > GEMV_MAX_ROUTED and K % 128 == 0:
         nsplit = w.h // 32 if gateup else w.d // 64
         mt = 2 if ((rows + 63) // 64 + min(w.E, rows)) * nsplit >= 4096 else 1
         return f"k_w4a8w<{mt}, {gu}, false, false>", "matrix-core"
@@ -113,7 +117,7 @@ def pair_kernel_of(w, T):
     if w.wfmt != "int4g32" or not w.hs or w.d % 128:
         return None
     rows = T * w.k
-    if rows <= 512 or rows < 256 or T <= 64:
+    if rows <= GEMV_MAX_ROUTED or T <= GEMV_MAX_DENSE:
         return None
     r2 = ((rows + 63) // 64 + min(w.E, rows)) * (w.h // 32) >= 4096
     d2 = ((T + 63) // 64) * (w.hs // 32) >= 4096
@@ -122,12 +126,12 @@ def pair_kernel_of(w, T):
 
 def pair_gemv_kernel_of(w, T):
     """rocprofv3 name of the merged weight-streaming gate/up kernel
-    mm_moe_forward launches for decode batches (routed rows <= 512, shared
-    rows <= 64, reduction fits), or None."""
+    mm_moe_forward launches for decode batches (routed rows <= 32, shared
+    rows <= 8, reduction fits), or None."""
     if w.wfmt != "int4g32" or not w.hs:
         return None
     rows, K = T * w.k, w.d
-    if rows <= 512 and T <= 64 and K % 64 == 0 and K <= 2560:
+    if rows <= GEMV_MAX_ROUTED and T <= GEMV_MAX_DENSE and K % 64 == 0 and K <= 2560:
         return "k_gemv_i4_pair<4, true, false>"
     return None
 
@@ -468,11 +472,12 @@ def main():
             gu_bytes = n_distinct * 2 * w.h * w.d * wb_r + 2 * w.hs * w.d * wb_r
             ka = gu_bytes / (stage_us * 1e-6) / 1e9
             kind, path = kernel_of(w, T, True)
-            roof["kernel"] = {"stage": "gate/up (routed + shared)", "kernel": pair_gemv_kernel_of(w, T) or kind,
+            kind = pair_gemv_kernel_of(w, T) or pair_kernel_of(w, T) or kind
+            roof["kernel"] = {"stage": "gate/up (routed + shared)", "kernel": kind,
                               "launch_us": round(stage_us, 3), "achieved": round(ka, 2),
                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ka / HBM_PEAK_GBS, 5),
                               "algorithmic_bytes_per_launch": int(gu_bytes),
-                              "traffic": stored_traffic(w.name, pair_gemv_kernel_of(w, T) or kind, key=T),
+                              "traffic": stored_traffic(w.name, kind, key=T),
                               "timing": "HIP events around the stage inside eager steps"}
     else:
         peak = INT8_MFMA_PEAK_TOPS if w.wfmt == "int4g32" else (

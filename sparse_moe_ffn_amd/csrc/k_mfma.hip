@@ -293,15 +293,20 @@ __global__ __launch_bounds__(64) void k_w4a8w(W4A8Prob P) {
 // XCD gets its share of both: its first per1 slots take shared tiles, the
 // rest routed tiles.  Workgroups start in slot order, so the shared tiles
 // (as long as or, for down with h_s = 4h, four times as long as a routed
-// tile) go first and the short routed ones fill in behind them.
-template <int kMT0, int kMT1, bool kGateUp>
+// tile) go first and the short routed ones fill in behind them.  kNT1: the
+// shared problem's 32-column tiles per wave (down with few tokens: 1, so
+// that twice as many waves share its long reduction).
+template <int kMT0, int kMT1, bool kGateUp, int kNT1 = 2>
 __global__ __launch_bounds__(64) void k_w4a8w_pair(W4A8Prob P0, W4A8Prob P1, int per1) {
   const int b = (int)blockIdx.x, x = b % kXcd, i = b / kXcd;
   if (i < per1)
-    w4a8w_tile<kMT1, 2, kGateUp, false, true, true>(P1, x, i, per1);
+    w4a8w_tile<kMT1, kNT1, kGateUp, false, true, true>(P1, x, i, per1);
   else
     w4a8w_tile<kMT0, 2, kGateUp, false, false, true>(P0, x, i - per1, 0);
 }
+
+// The shared down takes one 32-column tile per wave up to this many tokens.
+constexpr int64_t kNarrowSharedDownRows = 256;
 
 // Two row tiles per wave once that still gives at least 4 waves per SIMD
 // (256 CUs x 4 SIMDs): half the weight traffic per MFMA, fewer waves.
@@ -356,13 +361,27 @@ hipError_t launch_prob(const W4A8Prob& P, hipStream_t st) {
 // Routed problem R and dense problem D in one launch; each keeps the row
 // tiles it would get on its own.
 template <bool kGateUp>
-hipError_t launch_pair(const W4A8Prob& R, const W4A8Prob& D, hipStream_t st) {
+hipError_t launch_pair(const W4A8Prob& R, const W4A8Prob& D0, hipStream_t st) {
   const dim3 block(64);
+  // down of few tokens: the shared down's tiles would be few waves each
+  // running the long h_s reduction; one 32-column tile per wave doubles them
+  const bool narrow = !kGateUp && D0.a.rows <= kNarrowSharedDownRows;
+  W4A8Prob D = D0;
+  if (narrow) D.nsplit = D0.N / 32;
   const bool r2 = two_row_tiles(R.a, R.nsplit), d2 = two_row_tiles(D.a, D.nsplit);
   const int64_t n0 = n_tiles(R.a, r2 ? 64 : 32, R.nsplit);
   const int64_t n1 = n_tiles(D.a, d2 ? 64 : 32, D.nsplit);
   const int per1 = (int)(grid_of(n1) / kXcd);
   const dim3 grid(grid_of(n0) + grid_of(n1));
+  if constexpr (!kGateUp) {
+    if (narrow) {
+      if (r2)
+        hipLaunchKernelGGL((k_w4a8w_pair<2, 1, false, 1>), grid, block, 0, st, R, D, per1);
+      else
+        hipLaunchKernelGGL((k_w4a8w_pair<1, 1, false, 1>), grid, block, 0, st, R, D, per1);
+      return hipGetLastError();
+    }
+  }
   if (r2 && d2)
     hipLaunchKernelGGL((k_w4a8w_pair<2, 2, kGateUp>), grid, block, 0, st, R, D, per1);
   else if (r2)

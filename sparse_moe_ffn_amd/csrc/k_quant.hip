@@ -131,6 +131,44 @@ __device__ __forceinline__ void quant_row_v2(int64_t r, int64_t cols, const floa
     }
 }
 
+// Same quantiser with 16-byte loads: lane l holds the float4 columns
+// 4 j .. 4 j + 3, j = l + 64 i (cols % 4 == 0, cols <= 256 * kMaxF4); its four
+// codes are one 4-byte store in either layout (they share a quantisation
+// group).  Every load of the row is issued before the first use.
+template <int kMaxF4>
+__device__ __forceinline__ void quant_row_v4(int64_t r, int64_t cols, const float* __restrict__ x,
+                                             int8_t* __restrict__ q, float* __restrict__ s,
+                                             int64_t gm_rows) {
+  const int lane = threadIdx.x & 63;
+  const int n4 = (int)(cols / 4);
+  const float4* xr = reinterpret_cast<const float4*>(x + r * cols);
+  float4 v[kMaxF4];
+#pragma unroll
+  for (int i = 0; i < kMaxF4; ++i)
+    if (lane + 64 * i < n4) v[i] = xr[lane + 64 * i];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kMaxF4; ++i)
+    if (lane + 64 * i < n4)
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+  amax = max64(amax);
+  const float sr = (2.0f * amax) / 255.0f, yr = quant_recip(sr);
+  if (lane == 0) s[r] = sr;
+#pragma unroll
+  for (int i = 0; i < kMaxF4; ++i) {
+    const int j = lane + 64 * i;
+    if (j >= n4) continue;
+    uint32_t word = 0;
+    if (sr != 0.0f) {
+      word = (uint32_t)(uint8_t)quant_i8(v[i].x, sr, yr) |
+             (uint32_t)(uint8_t)quant_i8(v[i].y, sr, yr) << 8 |
+             (uint32_t)(uint8_t)quant_i8(v[i].z, sr, yr) << 16 |
+             (uint32_t)(uint8_t)quant_i8(v[i].w, sr, yr) << 24;
+    }
+    *reinterpret_cast<uint32_t*>(q + act_offset(r, 4 * j, cols, gm_rows)) = word;
+  }
+}
+
 // Same quantiser writing f16 paired codes (common.h): lane l holds columns
 // 4 j .. 4 j + 3, j = l + 64 i, read as float4; those are columns 0..3 (j
 // even) or 4..7 (j odd) of an 8-column block, which land in slots 0, 4, 1, 5
@@ -211,10 +249,10 @@ __global__ __launch_bounds__(256) void k_act_quant_i8_pair(QuantRows A, QuantRow
   const int wave = threadIdx.x >> 6;
   if ((int)blockIdx.x < nb0) {
     const int64_t r = (int64_t)blockIdx.x * 4 + wave;
-    if (r < A.rows) quant_row_v2<kMaxV>(r, A.cols, A.x, A.q, A.s, A.gm_rows);
+    if (r < A.rows) quant_row_v4<kMaxV / 2>(r, A.cols, A.x, A.q, A.s, A.gm_rows);
   } else {
     const int64_t r = (int64_t)(blockIdx.x - nb0) * 4 + wave;
-    if (r < B.rows) quant_row_v2<kMaxV>(r, B.cols, B.x, B.q, B.s, B.gm_rows);
+    if (r < B.rows) quant_row_v4<kMaxV / 2>(r, B.cols, B.x, B.q, B.s, B.gm_rows);
   }
 }
 

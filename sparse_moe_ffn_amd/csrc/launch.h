@@ -116,12 +116,17 @@ hipError_t launch_down_i4_gemv(const ExpertArgs& a, const int8_t* hq, const floa
                                const uint8_t* wq, const float* ws, float* f, int32_t* isum,
                                hipStream_t st);
 // Weight-streaming forms are used up to this many rows (routed: all experts
-// together; dense: the tokens).
-constexpr int64_t kGemvMaxRowsRouted = 512;
-constexpr int64_t kGemvMaxRowsDense = 64;
+// together; dense: the tokens): decode batches up to 8 tokens of top-4.
+// Beyond that the one-wave matrix-core tiles are faster even with most of
+// their 32 rows padding (S decode stack: B = 16 -11 %, 32 -21 %, 64 -35 %;
+// L layer at B = 64 -60 %): the weight-streaming kernels' dot products grow
+// with the rows of a tile, and an expert with more than four rows has its
+// weights read once per four.
+constexpr int64_t kGemvMaxRowsRouted = 32;
+constexpr int64_t kGemvMaxRowsDense = 8;
 // The matrix-core forms are used from this many rows on, when the reduction
 // dimension is a multiple of 128.
-constexpr int64_t kMfmaMinRows = 256;
+constexpr int64_t kMfmaMinRows = kGemvMaxRowsRouted + 1;
 // Routed and shared products of one kind in a single launch: matrix-core
 // and weight-streaming forms.  The matrix-core pair reads its INT8
 // activations (x_q [T][d] for gate/up; the hidden rows [Tk][h], [T][hs] for

@@ -119,8 +119,9 @@ def test_act_quant_halfway_bitexact(cols):
 
 # ------------------------------------------------------------ dense W4A8 linear
 @pytest.mark.parametrize("rows,K,N", [
-    (1, 768, 256), (7, 768, 768), (64, 1280, 256),   # weight-streaming (decode rows)
-    (65, 1024, 1024), (300, 1280, 1280), (2048, 768, 768), (130, 3072, 640),  # matrix cores
+    (1, 768, 256), (7, 768, 768), (8, 1280, 256),    # weight-streaming (decode rows)
+    (9, 768, 256), (64, 1280, 256),                  # matrix cores from 9 rows
+    (65, 1024, 1024), (300, 1280, 1280), (2048, 768, 768), (130, 3072, 640),
     (3, 3072, 128),                                    # row-tile kernel (K beyond the streaming form)
 ])
 def test_linear_w4a8_bitexact(rows, K, N):
@@ -745,13 +746,14 @@ def _sorted_reference(layer, w, lw, x):
     return hq, hs, f, igu, idn, a
 
 
-# The cases reach each kernel family: weight-streaming (up to 512 routed rows),
+# The cases reach each kernel family: weight-streaming (up to 32 routed rows),
 # matrix-core (more rows, K % 128 == 0) and row-tile (the rest: K % 128 != 0,
 # or K beyond the weight-streaming limit of 2560).
 STAGE_CASES = [
     ("s_prefill", 200, {}),                              # matrix-core
-    ("m_prefill", 70, {}),                               # weight-streaming
-    ("l_prefill", 45, {}),                               # weight-streaming, skewed routing
+    ("m_prefill", 70, {}),                               # matrix-core, few rows per expert
+    ("m_prefill", 8, {}),                                # weight-streaming
+    ("l_prefill", 8, {}),                                # weight-streaming, skewed routing (several tiles per expert)
     ("s_prefill", 3, {}),                                # weight-streaming, decode-sized
     ("s_prefill", 150, {"d": 704, "h": 320, "hs": 640}),  # row-tile (K % 128 != 0)
     ("s_prefill", 30, {"d": 2688, "hs": 0}),              # gate/up row-tile (K > 2560)
@@ -908,7 +910,8 @@ CASES = [
     ("s_prefill", 16, {"E": 1, "k": 1, "hs": 0}),
     ("s_prefill", 8, {}),                                 # decode batch
     ("l_prefill", 1, {}),                                 # decode, largest shared expert
-    ("m_prefill", 64, {}),                                # largest weight-streaming shared batch
+    ("m_prefill", 8, {}),                                 # largest weight-streaming shared batch
+    ("m_prefill", 9, {}),                                 # ... and the first on the matrix cores
     ("s_prefill", 150, {"d": 704, "h": 320, "hs": 640}),  # row-tile kernels
 ]
 
@@ -976,9 +979,10 @@ def test_rmsnorm():
 # (weight-streaming pair, matrix-core pair), the mixed case that falls back to
 # separate launches, the other weight formats and the no-shared layer.
 FUSED_CASES = [
-    ("s_prefill", 1, {}), ("s_prefill", 8, {}), ("s_prefill", 64, {}),   # weight-streaming pair
+    ("s_prefill", 1, {}), ("s_prefill", 8, {}),                          # weight-streaming pair
+    ("s_prefill", 9, {}), ("s_prefill", 64, {}),                         # matrix-core pair, decode batches
     ("l_prefill", 1, {}), ("m_prefill", 2, {}), ("s_prefill", 3, {}),     # one-workgroup front and past it
-    ("s_prefill", 100, {}),                                                # mixed: separate launches
+    ("s_prefill", 16, {"k": 2}), ("s_prefill", 5, {"E": 64, "k": 8}),    # mixed: separate launches
     ("s_prefill", 256, {}), ("s_prefill", 700, {}),                      # matrix-core pair
     ("s_prefill", 120, {"hs": 0}),
     ("m_prefill", 200, {}), ("l_prefill", 130, {}),
