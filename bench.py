@@ -121,7 +121,11 @@ def pair_kernel_of(w, T):
         return None
     r2 = ((rows + 63) // 64 + min(w.E, rows)) * (w.h // 32) >= 4096
     d2 = ((T + 63) // 64) * (w.hs // 32) >= 4096
-    return f"k_w4a8w_pair<{2 if r2 else 1}, {2 if d2 else 1}, true>"
+    # two column pairs per wave once the one-pair waves would reach 4096
+    waves = ((rows + 31) // 32 + min(w.E, rows)) * (w.h // 32) + ((T + 31) // 32) * (w.hs // 32)
+    if not r2 and not d2 and waves >= 4096 and w.h % 64 == 0 and w.hs % 64 == 0:
+        return "k_w4a8w_pair<1, 1, true, 4, 4>"
+    return f"k_w4a8w_pair<{2 if r2 else 1}, {2 if d2 else 1}, true, 2, 2>"
 
 
 def pair_gemv_kernel_of(w, T):

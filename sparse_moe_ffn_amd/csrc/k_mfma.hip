@@ -37,6 +37,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kXcd = 8;
+constexpr int kRingWide = 3;  // register-ring depth of the four-column-tile waves
 
 __device__ __forceinline__ v4i unpack16(uint2 w) {
   uint32_t q0, q1, q2, q3;
@@ -233,8 +234,9 @@ __device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int x, int i, int 
   // Register ring of kD single-group slots: slot i % kD holds group i,
   // loaded kD - 1 groups before its products (the last groups re-load group
   // G - 1: valid addresses, results unused).  Every load is a scalar base
-  // plus a 32-bit lane offset.  G % kD == 0.
-  constexpr int kD = 4;
+  // plus a 32-bit lane offset.  Four column tiles per wave keep three slots
+  // (registers for three waves per SIMD).
+  constexpr int kD = kNT >= 4 ? kRingWide : 4;
   WSlot<kMT, kNT> sl[kD];
   auto load = [&](WSlot<kMT, kNT>& st, int g) {
 #pragma unroll
@@ -256,7 +258,7 @@ __device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int x, int i, int 
 #pragma unroll
     for (int i = 0; i < kD; ++i) {
       load(sl[(i + kD - 1) % kD], min(g + i + kD - 1, G - 1));
-      wcompute1<kMT, kNT, kCapture>(acc, sl[i], g + i, lane, rb, cap);
+      if (G % kD == 0 || g + i < G) wcompute1<kMT, kNT, kCapture>(acc, sl[i], g + i, lane, rb, cap);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -296,14 +298,18 @@ __global__ __launch_bounds__(64) void k_w4a8w(W4A8Prob P) {
 // tile) go first and the short routed ones fill in behind them.  kNT1: the
 // shared problem's 32-column tiles per wave (down with few tokens: 1, so
 // that twice as many waves share its long reduction).
-template <int kMT0, int kMT1, bool kGateUp, int kNT1 = 2>
+template <int kMT0, int kMT1, bool kGateUp, int kNT1 = 2, int kNT0 = 2>
 __global__ __launch_bounds__(64) void k_w4a8w_pair(W4A8Prob P0, W4A8Prob P1, int per1) {
   const int b = (int)blockIdx.x, x = b % kXcd, i = b / kXcd;
   if (i < per1)
     w4a8w_tile<kMT1, kNT1, kGateUp, false, true, true>(P1, x, i, per1);
   else
-    w4a8w_tile<kMT0, 2, kGateUp, false, false, true>(P0, x, i - per1, 0);
+    w4a8w_tile<kMT0, kNT0, kGateUp, false, false, true>(P0, x, i - per1, 0);
 }
+
+// The merged gate/up takes two column pairs per wave, and the merged down
+// four column tiles per routed wave, from this many two-tile waves on.
+constexpr int64_t kWideGateUpWaves = 4096;
 
 // The shared down takes one 32-column tile per wave up to this many tokens.
 constexpr int64_t kNarrowSharedDownRows = 256;
@@ -373,7 +379,37 @@ hipError_t launch_pair(const W4A8Prob& R, const W4A8Prob& D0, hipStream_t st) {
   const int64_t n1 = n_tiles(D.a, d2 ? 64 : 32, D.nsplit);
   const int per1 = (int)(grid_of(n1) / kXcd);
   const dim3 grid(grid_of(n0) + grid_of(n1));
+  if constexpr (kGateUp) {
+    // two (gate, up) column pairs per wave when the one-pair form would have
+    // more waves than the chip holds at once: each activation fragment feeds
+    // four products instead of two, and the launch is closer to one wave
+    // per slot (S prefill: 44.5 against 46.1 us; with fewer tiles, as in
+    // decode batches, the one-pair form is faster)
+    if (!r2 && !d2 && n0 + n1 >= kWideGateUpWaves && R.a.h % 64 == 0 && D.a.h % 64 == 0) {
+      // (half the column splits: still one row tile per wave)
+      W4A8Prob R2 = R, D2 = D;
+      R2.nsplit = R.a.h / 64;
+      D2.nsplit = D.a.h / 64;
+      const int64_t m0 = n_tiles(R2.a, 32, R2.nsplit), m1 = n_tiles(D2.a, 32, D2.nsplit);
+      const int q1 = (int)(grid_of(m1) / kXcd);
+      hipLaunchKernelGGL((k_w4a8w_pair<1, 1, true, 4, 4>), dim3(grid_of(m0) + grid_of(m1)), block, 0,
+                         st, R2, D2, q1);
+      return hipGetLastError();
+    }
+  }
   if constexpr (!kGateUp) {
+    // the routed down with four 32-column tiles per wave on a large launch:
+    // its reduction is short (h), so each wave's first loads weigh on it
+    // (S prefill: 23.1 against 24.1 us; the shared down, with its long h_s
+    // reduction, keeps two: with four, 27.4 us)
+    if (!narrow && !r2 && !d2 && n0 + n1 >= kWideGateUpWaves && R.N % 128 == 0) {
+      W4A8Prob R2 = R;
+      R2.nsplit = R.N / 128;
+      const int64_t m0 = n_tiles(R2.a, 32, R2.nsplit);
+      hipLaunchKernelGGL((k_w4a8w_pair<1, 1, false, 2, 4>), dim3(grid_of(m0) + grid_of(n1)), block, 0,
+                         st, R2, D, per1);
+      return hipGetLastError();
+    }
     if (narrow) {
       if (r2)
         hipLaunchKernelGGL((k_w4a8w_pair<2, 1, false, 1>), grid, block, 0, st, R, D, per1);

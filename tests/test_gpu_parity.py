@@ -984,6 +984,7 @@ FUSED_CASES = [
     ("l_prefill", 1, {}), ("m_prefill", 2, {}), ("s_prefill", 3, {}),     # one-workgroup front and past it
     ("s_prefill", 16, {"k": 2}), ("s_prefill", 5, {"E": 64, "k": 8}),    # mixed: separate launches
     ("s_prefill", 256, {}), ("s_prefill", 700, {}),                      # matrix-core pair
+    ("s_prefill", 1900, {}),                                               # ... wide waves (two column pairs / four tiles)
     ("s_prefill", 120, {"hs": 0}),
     ("m_prefill", 200, {}), ("l_prefill", 130, {}),
     ("s_prefill", 150, {"d": 704, "h": 320, "hs": 640}),                  # row-tile kernels
