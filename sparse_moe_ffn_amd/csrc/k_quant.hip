@@ -169,6 +169,56 @@ __device__ __forceinline__ void quant_row_v4(int64_t r, int64_t cols, const floa
   }
 }
 
+// The same quantiser for two short rows per wave (cols % 4 == 0, cols <=
+// 128 * kMaxH): lanes 0..31 take row r0, lanes 32..63 row r0 + 1 (if it is
+// below `rows`), half-lane l the float4 columns l + 32 i.  Halves the waves
+// of a launch of short rows, so all of them are resident at once.
+template <int kMaxH>
+__device__ __forceinline__ void quant_rows2_v4(int64_t r0, int64_t rows, int64_t cols,
+                                               const float* __restrict__ x, int8_t* __restrict__ q,
+                                               float* __restrict__ s, int64_t gm_rows) {
+  const int lane = threadIdx.x & 63, hl = lane & 31;
+  const int64_t r = r0 + (lane >> 5);
+  const bool live = r < rows;
+  const int n4 = (int)(cols / 4);
+  const float4* xr = reinterpret_cast<const float4*>(x + (live ? r : r0) * cols);
+  float4 v[kMaxH];
+#pragma unroll
+  for (int i = 0; i < kMaxH; ++i)
+    if (live && hl + 32 * i < n4) v[i] = xr[hl + 32 * i];
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kMaxH; ++i)
+    if (live && hl + 32 * i < n4)
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+  // maximum over each 32-lane half: within the 16-lane rows, then the half's two rows
+  m = fmaxf(m, dpp<kDppXor1>(m));
+  m = fmaxf(m, dpp<kDppXor2>(m));
+  m = fmaxf(m, dpp<kDppHalfMirror>(m));
+  m = fmaxf(m, dpp<kDppMirror>(m));
+  const float m0 = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0)),
+                         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 16)));
+  const float m1 = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 32)),
+                         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 48)));
+  const float amax = lane < 32 ? m0 : m1;
+  const float sr = (2.0f * amax) / 255.0f, yr = quant_recip(sr);
+  if (!live) return;
+  if (hl == 0) s[r] = sr;
+#pragma unroll
+  for (int i = 0; i < kMaxH; ++i) {
+    const int j = hl + 32 * i;
+    if (j >= n4) continue;
+    uint32_t word = 0;
+    if (sr != 0.0f) {
+      word = (uint32_t)(uint8_t)quant_i8(v[i].x, sr, yr) |
+             (uint32_t)(uint8_t)quant_i8(v[i].y, sr, yr) << 8 |
+             (uint32_t)(uint8_t)quant_i8(v[i].z, sr, yr) << 16 |
+             (uint32_t)(uint8_t)quant_i8(v[i].w, sr, yr) << 24;
+    }
+    *reinterpret_cast<uint32_t*>(q + act_offset(r, 4 * j, cols, gm_rows)) = word;
+  }
+}
+
 // Same quantiser writing f16 paired codes (common.h): lane l holds columns
 // 4 j .. 4 j + 3, j = l + 64 i, read as float4; those are columns 0..3 (j
 // even) or 4..7 (j odd) of an 8-column block, which land in slots 0, 4, 1, 5
@@ -236,6 +286,8 @@ __global__ __launch_bounds__(256) void k_act_quant_f16p(int64_t rows, int64_t co
 // Two row sets in one launch: blocks [0, nb0) cover set 0, the rest set 1
 // (the launcher puts the set with the longer rows first, so that its waves,
 // the longest, start first and the short ones fill in behind them).
+constexpr int kMaxH2 = 5;  // two rows per wave up to 640 columns
+
 struct QuantRows {
   int64_t rows, cols;
   const float* x;
@@ -244,12 +296,16 @@ struct QuantRows {
   int64_t gm_rows;
 };
 
-template <int kMaxV>
+// kRows2: set B (the shorter rows) two rows per wave.
+template <int kMaxV, bool kRows2>
 __global__ __launch_bounds__(256) void k_act_quant_i8_pair(QuantRows A, QuantRows B, int nb0) {
   const int wave = threadIdx.x >> 6;
   if ((int)blockIdx.x < nb0) {
     const int64_t r = (int64_t)blockIdx.x * 4 + wave;
     if (r < A.rows) quant_row_v4<kMaxV / 2>(r, A.cols, A.x, A.q, A.s, A.gm_rows);
+  } else if constexpr (kRows2) {
+    const int64_t r = ((int64_t)(blockIdx.x - nb0) * 4 + wave) * 2;
+    if (r < B.rows) quant_rows2_v4<kMaxH2>(r, B.rows, B.cols, B.x, B.q, B.s, B.gm_rows);
   } else {
     const int64_t r = (int64_t)(blockIdx.x - nb0) * 4 + wave;
     if (r < B.rows) quant_row_v4<kMaxV / 2>(r, B.cols, B.x, B.q, B.s, B.gm_rows);
@@ -366,11 +422,15 @@ hipError_t launch_act_quant_i8_pair(int64_t rows0, int64_t cols0, const float* x
   QuantRows A{rows0, cols0, x0, q0, s0, act_gm_rows(layout, rows0)};
   QuantRows B{rows1, cols1, x1, q1, s1, act_gm_rows(layout, rows1)};
   if (B.cols > A.cols) std::swap(A, B);
-  const int nbA = (int)blocks_for(A.rows, 4), nbB = (int)blocks_for(B.rows, 4);
+  const int nbA = (int)blocks_for(A.rows, 4);
+  const bool rows2 = layout != kActF16Paired && B.cols <= 128 * kMaxH2;
+  const int nbB = (int)blocks_for(rows2 ? (B.rows + 1) / 2 : B.rows, 4);
   if (layout == kActF16Paired)
     hipLaunchKernelGGL(k_act_quant_f16p_pair<12>, dim3(nbA + nbB), dim3(256), 0, st, A, B, nbA);
+  else if (rows2)
+    hipLaunchKernelGGL((k_act_quant_i8_pair<24, true>), dim3(nbA + nbB), dim3(256), 0, st, A, B, nbA);
   else
-    hipLaunchKernelGGL(k_act_quant_i8_pair<24>, dim3(nbA + nbB), dim3(256), 0, st, A, B, nbA);
+    hipLaunchKernelGGL((k_act_quant_i8_pair<24, false>), dim3(nbA + nbB), dim3(256), 0, st, A, B, nbA);
   return hipGetLastError();
 }
 
