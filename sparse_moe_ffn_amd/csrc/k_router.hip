@@ -98,9 +98,20 @@ __global__ __launch_bounds__(256) void k_router(int64_t T, int d, int E, int k,
     // wave w quantises token w (every wave holds all kTok rows), while the
     // first expert rows are in flight
     if constexpr (kQuant) {
+      // one copy of the quantiser on the selected row (four inlined copies
+      // kept 185 VGPRs live: two waves per SIMD instead of four)
+      const int wq = __builtin_amdgcn_readfirstlane(wave);
+      if (wq < nt) {
+        float sel[kNX];
 #pragma unroll
-      for (int q = 0; q < kTok; ++q)
-        if (q == wave && q < nt) quant_row_regs(xv[q], lane, t0 + q, d, xq, sx, gm_rows);
+        for (int c = 0; c < kNX; ++c) {
+          float v = xv[0][c];
+#pragma unroll
+          for (int q = 1; q < kTok; ++q) v = wq == q ? xv[q][c] : v;
+          sel[c] = v;
+        }
+        quant_row_regs(sel, lane, t0 + wq, d, xq, sx, gm_rows);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
