@@ -49,7 +49,7 @@ def parse():
                          "a second stream; auto: decode where it applies, else fused (measured "
                          "fastest on every workload)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
-    ap.add_argument("--op", choices=("layer", "attn_decode", "linear", "train_step"), default="layer",
+    ap.add_argument("--op", choices=("layer", "attn_decode", "linear", "train_step", "block"), default="layer",
                     help="layer: the MoE-FFN layer (default); attn_decode: GQA decode attention "
                          "over an INT8 KV cache (--batch sequences, --context positions, --heads "
                          "query heads, 4 key/value heads); linear: the dense W4A8 projection "
@@ -210,6 +210,8 @@ def main():
         return bench_linear(args, dev)
     if args.op == "train_step":
         return bench_train(args, dev)
+    if args.op == "block":
+        return bench_block(args, dev)
     w = wl.WORKLOADS[args.workload]
     if args.batch is not None:
         w = w.with_(T=args.batch)
@@ -673,6 +675,113 @@ def bench_attn(args, dev):
                                                "gqa_decode_attention_kernels.md", ATTN_SOURCES),
                      "kernel": "k_attn_split + k_attn_merge (one mm_attn_decode_i8 call)",
                      "algorithmic_bytes_per_launch": nbytes, "launch_us": round(ms * 1e3, 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out_line), flush=True)
+
+
+def bench_block(args, dev):
+    """One decode step of a MobileMoE-S decoder block (RMSNorm, W4A8 q/k/v,
+    INT8 KV append, GQA decode attention over `context` positions, W4A8 o,
+    residual add + RMSNorm, the MoE-FFN layer, residual add) for a batch of
+    sequences: tokens per second, and the step's algorithmic HBM bytes
+    (projection weights, the KV cache read, the selected experts', shared
+    expert's and router's weights, token rows) per second.  Distinct blocks
+    (weights and caches) rotated past the 256 MB MALL; every step writes the
+    new token at the cache's last position (the same work every step)."""
+    import numpy as np
+    import torch
+    from sparse_moe_ffn_amd import workloads as wl
+    from sparse_moe_ffn_amd.layer import DecoderBlock, MoELayer
+    Bn, T = args.batch or 8, args.context
+    w = wl.WORKLOADS["s_decode"].with_(T=Bn, layers=1)
+    per = (w.E * 3 * w.d * w.h + 3 * w.d * w.hs) * 0.625 + Bn * 4 * T * 136
+    n_inst = int(max(2, math.ceil(1.6 * MALL_BYTES / per)))  # a step touches about 3/4 of a block
+    blocks = []
+    for i in range(n_inst):
+        lw = wl.layer_weights(w, layer=i)
+        aw = wl.attn_weights(w, layer=i)
+        moe = MoELayer.from_workload(w, lw, device=dev)
+        blk = DecoderBlock(moe, aw.n_h, aw.n_kv, aw.wq, aw.wk, aw.wv, aw.wo, Bn, T)
+        blk.load_context(*wl.kv_context(w, Bn, T, layer=i))
+        blocks.append(blk)
+    x = torch.from_numpy(wl.tokens(w, step=0)).to(dev)
+    pos = torch.full((Bn,), T - 1, dtype=torch.int32, device=dev)
+    lens = torch.full((Bn,), T, dtype=torch.int32, device=dev)
+    for blk in blocks:  # buffers and workspaces exist before the graphs are recorded
+        blk.decode(x, pos, lens, T)
+    torch.cuda.synchronize()
+    distinct = [len(np.unique(blk.moe.idx.cpu().numpy())) for blk in blocks]
+
+    def issue(i):
+        blocks[i % n_inst].decode(x, pos, lens, T)
+
+    ms = _time_graphs(issue, args.warmup, args.steps)
+    d, h, hs, qd, kd = w.d, w.h, w.hs, 12 * 64, 4 * 64
+    proj = (2 * qd * d + 2 * kd * d) * 0.625
+    kv = Bn * 4 * T * 136
+    moe_b = float(np.mean(distinct)) * 3 * d * h * 0.625 + 3 * d * hs * 0.625 + 4 * w.E * d
+    rows = 5 * Bn * d * 4
+    nbytes = proj + kv + moe_b + rows
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        blk = blocks[0]
+        lw, aw = wl.layer_weights(w, layer=0), wl.attn_weights(w, layer=0)
+        kq, vq, ks, vs = wl.kv_context(w, Bn, T, layer=0)
+        q4 = [oracle.quant_w4g32(m) for m in (aw.wq, aw.wk, aw.wv, aw.wo)]
+        xh = x.cpu().numpy()
+        f32 = np.float32
+
+        def ora_step(n):
+            a = oracle.rmsnorm(xh[:n], 1e-5).astype(f32)
+            aq, sa = oracle.quant_act_i8(a)
+            q, k, v = (oracle.linear_w4a8(aq, sa, *q4[j]).astype(f32) for j in range(3))
+            kqq, kss = oracle.quant_act_i8(k.reshape(-1, 64))
+            vqq, vss = oracle.quant_act_i8(v.reshape(-1, 64))
+            kc, vc, ksc, vsc = kq[:n].copy(), vq[:n].copy(), ks[:n].copy(), vs[:n].copy()
+            kc[:, :, T - 1] = kqq.reshape(n, 4, 64)
+            vc[:, :, T - 1] = vqq.reshape(n, 4, 64)
+            ksc[:, :, T - 1] = kss.reshape(n, 4)
+            vsc[:, :, T - 1] = vss.reshape(n, 4)
+            o = oracle.attn_decode(q.reshape(n, 12, 64), kc, vc, ksc, vsc, T).reshape(n, -1).astype(f32)
+            oq, so = oracle.quant_act_i8(o)
+            hh = xh[:n] + oracle.linear_w4a8(oq, so, *q4[3]).astype(f32)
+            a2 = oracle.rmsnorm(hh, 1e-5).astype(f32)
+            r = oracle.forward(a2, lw.wr, lw.bias, lw.w_gu, lw.w_d, lw.ws_gu, lw.ws_d, k=w.k,
+                               wfmt="int4g32", nthreads=1)
+            return hh + r.y.astype(f32)
+
+        ora_step(1)  # the oracle's weight quantisation is per call; time the slope
+        t1 = time.time()
+        ora_step(1)
+        d1 = time.time() - t1
+        n = min(Bn, 8)
+        t1 = time.time()
+        ora_step(n)
+        dn = time.time() - t1
+        per_tok = (dn - d1) / (n - 1) if n > 1 and dn > d1 else dn / n
+        cpu = {"value": round(1.0 / per_tok, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"the composed oracle block (the oracle's RMSNorm, INT8 quantiser, W4A8 "
+                         f"linear, decode attention over {T} positions and layer forward) for 1 "
+                         f"and {n} sequences, one thread; rate = token-count slope ({dn:.1f}s)"}
+    out_line = {
+        "metric": "decoder-block decode step (MobileMoE-S block): tokens per second",
+        "value": round(Bn / (ms * 1e-3), 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": "s_decoder_block", "sequences": Bn, "context": T, "d_model": d,
+                   "query_heads": 12, "kv_heads": 4, "head_dim": 64, "experts": w.E, "top_k": w.k,
+                   "hidden": h, "shared_hidden": hs, "blocks_rotated": n_inst,
+                   "parallelism": "single GPU",
+                   "path": "DecoderBlock.decode (RMSNorm, 3 + 1 W4A8 projections, KV append, "
+                           "mm_attn_decode_i8, mm_add_rmsnorm_f32 x 2, the MoE layer)"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 5), "traffic": None,
+                     "scope": "whole step", "algorithmic_bytes_per_step": int(nbytes),
+                     "bytes": {"projections": int(proj), "kv_cache": int(kv), "moe_layer": int(moe_b),
+                               "token_rows": int(rows)}},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out_line), flush=True)
