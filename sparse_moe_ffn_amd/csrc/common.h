@@ -50,9 +50,12 @@ enum : int {
   kDppMirror = 0x140        // lane i of each 16 <- lane 15-i
 };
 
+// Every control above reads a lane of the same row, so no source lane is out
+// of range; bound_ctrl set lets the compiler fold the move into the VALU
+// instruction that uses it (v_add_f32_dpp, v_max_f32_dpp).
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, true));
 }
 
 // Sum of the 64 lanes as a balanced pairwise tree over lane indices: pairs at
@@ -287,6 +290,15 @@ __device__ __forceinline__ int8_t quant_i8(float v, float s, float y) {
   if (!(fabsf(t - r) < 0.5f - 0x1p-12f)) r = rintf(v / s);
   r = fminf(fmaxf(r, -128.0f), 127.0f);
   return (int8_t)(int)r;
+}
+
+// Branch-free INT8 code of v with y = quant_recip(s): quant_i8's fast case;
+// slow becomes true where quant_i8 would take its exact division instead.
+__device__ __forceinline__ int quant_code_fast(float v, float y, bool& slow) {
+  const float t = v * y;
+  const float r = rintf(t);
+  slow |= !(fabsf(t - r) < 0.5f - 0x1p-12f);
+  return (int)fminf(fmaxf(r, -128.0f), 127.0f);
 }
 
 }  // namespace mm

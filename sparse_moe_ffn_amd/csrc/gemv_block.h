@@ -178,15 +178,6 @@ __device__ __forceinline__ float quant_row_lds(const float* __restrict__ x, int 
   return quant_regs_lds<kNQ>(v, K, dst, lane);
 }
 
-// Branch-free INT8 code of v with y = quant_recip(s): quant_i8's fast case;
-// slow becomes true where quant_i8 would take its exact division instead.
-__device__ __forceinline__ int quant_code_fast(float v, float y, bool& slow) {
-  const float t = v * y;
-  const float r = rintf(t);
-  slow |= !(fabsf(t - r) < 0.5f - 0x1p-12f);
-  return (int)fminf(fmaxf(r, -128.0f), 127.0f);
-}
-
 // The row quantiser over the whole workgroup: rows r < n (n <= 4) of src
 // (workgroup memory, floats, row stride K, K % 128 == 0) into INT8 rows of
 // dst (row stride K) and their scales into scale[r]; wave w takes the
@@ -531,7 +522,7 @@ __device__ __forceinline__ void gemv_block(const GemvProb& P, int blk,
         dot16x2(wv[i][m], x, q0, q1);
         const int send = half ? q0 : q1;
         const int keep = half ? q1 : q0;
-        const int full = keep + __builtin_amdgcn_mov_dpp(send, kDppXor1, 0xF, 0xF, false);
+        const int full = keep + __builtin_amdgcn_mov_dpp(send, kDppXor1, 0xF, 0xF, true);
         s_is[((m * kR + r) * G + g) * 32 + row] = full;
       }
     }

@@ -38,6 +38,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kXcd = 8;
 constexpr int kRingWide = 3;  // register-ring depth of the four-column-tile waves
+constexpr int kRingDeep = 8;  // register-ring depth of the small-launch waves
 
 __device__ __forceinline__ v4i unpack16(uint2 w) {
   uint32_t q0, q1, q2, q3;
@@ -146,7 +147,8 @@ struct W4A8Prob {
 // are group-major (act_offset in common.h), so a tile's 32 rows of one group
 // are read from one contiguous kilobyte when the rows are consecutive.
 // K % 128 == 0.  Called by one whole wave.
-template <int kMT, int kNT, bool kGateUp, bool kCapture, bool kDense, bool kGM = false>
+template <int kMT, int kNT, bool kGateUp, bool kCapture, bool kDense, bool kGM = false,
+          bool kDeep = false>
 __device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int x, int i, int per_dense) {
   static_assert(!kGateUp || kNT % 2 == 0, "gate/up tiles come in (gate, up) pairs");
   constexpr int kP = kNT / 2;  // gate/up: column pairs per wave
@@ -236,8 +238,10 @@ __device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int x, int i, int 
   // G - 1: valid addresses, results unused).  Every load is a scalar base
   // plus a 32-bit lane offset.  Four column tiles or two row tiles per wave
   // keep three slots (registers for three waves per SIMD instead of two:
-  // M prefill 459 -> 436 us, L 609 -> 583 us per step).
-  constexpr int kD = (kNT >= 4 || kMT >= 2) ? kRingWide : 4;
+  // M prefill 459 -> 436 us, L 609 -> 583 us per step).  kDeep (launches of
+  // fewer waves than the chip has SIMDs, as in decode batches): eight slots,
+  // so that each wave keeps seven groups of weights in flight.
+  constexpr int kD = kDeep ? kRingDeep : (kNT >= 4 || kMT >= 2) ? kRingWide : 4;
   WSlot<kMT, kNT> sl[kD];
   auto load = [&](WSlot<kMT, kNT>& st, int g) {
 #pragma unroll
@@ -252,7 +256,7 @@ __device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int x, int i, int 
   // find slot 0 oldest, as it is on every later iteration)
 #pragma unroll
   for (int i = 0; i < kD - 1; ++i) {
-    load(sl[i], i);
+    load(sl[i], min(i, G - 1));
     __builtin_amdgcn_sched_barrier(0);
   }
   for (int g = 0; g < G; g += kD) {
@@ -299,14 +303,19 @@ __global__ __launch_bounds__(64) void k_w4a8w(W4A8Prob P) {
 // tile) go first and the short routed ones fill in behind them.  kNT1: the
 // shared problem's 32-column tiles per wave (down with few tokens: 1, so
 // that twice as many waves share its long reduction).
-template <int kMT0, int kMT1, bool kGateUp, int kNT1 = 2, int kNT0 = 2>
+template <int kMT0, int kMT1, bool kGateUp, int kNT1 = 2, int kNT0 = 2, bool kDeep = false>
 __global__ __launch_bounds__(64) void k_w4a8w_pair(W4A8Prob P0, W4A8Prob P1, int per1) {
   const int b = (int)blockIdx.x, x = b % kXcd, i = b / kXcd;
   if (i < per1)
-    w4a8w_tile<kMT1, kNT1, kGateUp, false, true, true>(P1, x, i, per1);
+    w4a8w_tile<kMT1, kNT1, kGateUp, false, true, true, kDeep>(P1, x, i, per1);
   else
-    w4a8w_tile<kMT0, kNT0, kGateUp, false, false, true>(P0, x, i - per1, 0);
+    w4a8w_tile<kMT0, kNT0, kGateUp, false, false, true, kDeep>(P0, x, i - per1, 0);
 }
+
+// Launches of at most this many waves (decode batches) take the deep
+// register ring: the chip then holds every wave at once with spare
+// registers, and the weight stream, not the products, sets the pace.
+constexpr int64_t kDeepRingWaves = 2048;
 
 // The merged gate/up takes two column pairs per wave, and the merged down
 // four column tiles per routed wave, from this many two-tile waves on.
@@ -414,6 +423,8 @@ hipError_t launch_pair(const W4A8Prob& R, const W4A8Prob& D0, hipStream_t st) {
     if (narrow) {
       if (r2)
         hipLaunchKernelGGL((k_w4a8w_pair<2, 1, false, 1>), grid, block, 0, st, R, D, per1);
+      else if (n0 + n1 <= kDeepRingWaves)
+        hipLaunchKernelGGL((k_w4a8w_pair<1, 1, false, 1, 2, true>), grid, block, 0, st, R, D, per1);
       else
         hipLaunchKernelGGL((k_w4a8w_pair<1, 1, false, 1>), grid, block, 0, st, R, D, per1);
       return hipGetLastError();
@@ -425,6 +436,8 @@ hipError_t launch_pair(const W4A8Prob& R, const W4A8Prob& D0, hipStream_t st) {
     hipLaunchKernelGGL((k_w4a8w_pair<2, 1, kGateUp>), grid, block, 0, st, R, D, per1);
   else if (d2)
     hipLaunchKernelGGL((k_w4a8w_pair<1, 2, kGateUp>), grid, block, 0, st, R, D, per1);
+  else if (n0 + n1 <= kDeepRingWaves)
+    hipLaunchKernelGGL((k_w4a8w_pair<1, 1, kGateUp, 2, 2, true>), grid, block, 0, st, R, D, per1);
   else
     hipLaunchKernelGGL((k_w4a8w_pair<1, 1, kGateUp>), grid, block, 0, st, R, D, per1);
   return hipGetLastError();

@@ -49,6 +49,25 @@ __global__ __launch_bounds__(kBlockSlots) void k_route_count(int64_t Tk, int E,
 // counting kernel runs.
 enum { kCounts = 0, kSingle = 1, kHist = 2 };
 
+// Sum of the first `lim` of the 16 byte counts in wd (all 16 when lim >= 16,
+// none when lim <= 0).  lim is the same on every lane of the wave.
+__device__ __forceinline__ int hist_piece_sum(const uint32_t (&wd)[4], int64_t lim) {
+  if (lim <= 0) return 0;
+  int sum = 0;
+  if (lim >= 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sum = (int)__builtin_amdgcn_udot4(wd[i], 0x01010101u, (uint32_t)sum, false);
+    return sum;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t l = lim - 4 * i;  // bytes of word i below the limit
+    const uint32_t m = l >= 4 ? 0xFFFFFFFFu : l <= 0 ? 0u : (1u << (8 * (int)l)) - 1u;
+    sum = (int)__builtin_amdgcn_udot4(wd[i] & m, 0x01010101u, (uint32_t)sum, false);
+  }
+  return sum;
+}
+
 template <int kMode>
 __global__ __launch_bounds__(kBlockSlots) void k_route_scatter(
     int64_t Tk, int E, int64_t nblk, const int32_t* __restrict__ idx,
@@ -60,7 +79,7 @@ __global__ __launch_bounds__(kBlockSlots) void k_route_scatter(
   __shared__ int part_total[4][64];
   __shared__ int base[64];    // offsets[e] + count of e in earlier blocks
   __shared__ int wcnt[4][64];  // count of e in each wave of this block
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t blk = blockIdx.x;
   // this thread's slot id, read first so that its latency overlaps the counts
   const int64_t slot = blk * kBlockSlots + tid;
@@ -78,19 +97,29 @@ __global__ __launch_bounds__(kBlockSlots) void k_route_scatter(
   } else if constexpr (kMode == kHist) {
     // expert `lane`, quarter `wv` of the router workgroups, 16 bytes a load
     // (hstride % 64 == 0; bytes past nrb are not counted)
+    // The loads of a batch of kHistBatch 16-byte pieces are all issued
+    // before any is summed, so a lane pays one memory round trip per batch
+    // instead of one per piece.  A piece's block indices are the same for
+    // every lane (only the expert row differs), so whether a piece lies
+    // wholly below a limit is a wave-uniform test; only a piece that
+    // straddles one is masked byte by byte.
+    constexpr int kHistBatch = 8;
     int before = 0, total = 0;
     if (lane < E) {
       const int64_t q = hstride / 4, b0 = wv * q, bend = blk * rpb;  // router blocks before this block
+      const int64_t npiece = q / 16;
       const uint4* row = reinterpret_cast<const uint4*>(hist + (int64_t)lane * hstride + b0);
-      for (int64_t c = 0; c < q / 16; ++c) {
-        const uint4 v = row[c];
-        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+      for (int64_t c0 = 0; c0 < npiece; c0 += kHistBatch) {
+        uint4 v[kHistBatch];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int64_t b = b0 + 16 * c + i;
-          const int n = (int)((wd[i >> 2] >> (8 * (i & 3))) & 0xFFu);
-          if (b < nrb) total += n;
-          if (b < bend) before += n;
+        for (int j = 0; j < kHistBatch; ++j)
+          v[j] = c0 + j < npiece ? row[c0 + j] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int j = 0; j < kHistBatch; ++j) {
+          const int64_t pb = b0 + 16 * (c0 + j);  // block index of the piece's first byte
+          const uint32_t wd[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+          total += hist_piece_sum(wd, nrb - pb);
+          before += hist_piece_sum(wd, bend - pb);
         }
       }
     }

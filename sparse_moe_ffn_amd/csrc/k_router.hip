@@ -71,7 +71,9 @@ __global__ __launch_bounds__(256) void k_router(int64_t T, int d, int E, int k,
   __shared__ float s_part[4][16 * kTok][kRowStride];
   __shared__ float s_logit[kTok][64];
   __shared__ int s_hist[64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is made wave-uniform (a scalar), so the expert loop
+  // branches on scalars and each expert row is read from a scalar base
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (hist != nullptr && threadIdx.x < 64) s_hist[threadIdx.x] = 0;
   const int64_t t0 = (int64_t)blockIdx.x * kTok;
   const int nt = (int)min((int64_t)kTok, T - t0);
@@ -122,7 +124,9 @@ __global__ __launch_bounds__(256) void k_router(int64_t T, int d, int E, int k,
 #pragma unroll
           for (int c = 0; c < kNX; ++c) p = __builtin_fmaf(xv[q][c], wv[i % kRing][c], p);
           p = quad_sum(p);
-          if ((lane & 3) == 0) s_part[wave][i * kTok + q][lane >> 2] = p;
+          // the four lanes of a quad store the same sum to the same word
+          // (no lane mask around the store)
+          s_part[wave][i * kTok + q][lane >> 2] = p;
         }
       }
       if (i + kRing < 16) load_row(i + kRing, wv[i % kRing]);

@@ -993,6 +993,7 @@ FUSED_CASES = [
     ("s_prefill", 4, {}),                                                  # token rows staged before the tile lookup
     ("s_prefill", 1500, {"E": 16, "k": 2}),                                # count sort from router histograms, k = 2
     ("s_prefill", 2300, {"E": 1, "k": 1}),                                 # ... one expert, k = 1
+    ("s_prefill", 700, {"E": 64, "k": 8}),                                 # ... k = 8: block limits inside a 16-byte piece
     ("l_decode", 1, {}), ("m_decode", 1, {}),                              # one token: one-workgroup front, widths 1280 / 1024
     ("s_prefill", 1, {"E": 64, "k": 8}), ("s_prefill", 1, {"d": 256, "h": 128, "hs": 512}),
 ]
