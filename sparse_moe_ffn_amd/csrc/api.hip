@@ -816,6 +816,10 @@ mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
     dn_mfma_pair = !qin && shared && !dv && dm && !use_gemv(ar, h, false) && quant_pair;
   }
   const int xq_layout = gu_mfma_pair ? mm::kActGroupMajor : mm::kActRowMajor;
+  // the matrix-core down pair with FP32 output and no fused RMSNorm: the
+  // combine runs in the shared down's epilogue (no ys, no combine launch)
+  const bool cmb_in_down = dn_mfma_pair && y_norm == nullptr && desc->out_dtype == MM_OUT_F32 &&
+                           mm::down_cmb_fits(ar, as);
 
   // router + top-k (+ per-token INT8 of x), then the count sort; for a few
   // tokens all of it in one workgroup
@@ -877,6 +881,11 @@ mm_status mm_moe_forward(const mm_layer_desc* desc, int64_t T, const float* x,
     } else if (shared && dv) {
       MM_TRY(hip_status(mm::launch_down_i4_gemv_pair(ar, as, q_r, s_r, q_s, s_s, dq, w_down.scales,
                                                      sdq, ws_down.scales, f, ys, st), where));
+    } else if (dn_mfma_pair && cmb_in_down) {
+      MM_TRY(hip_status(mm::launch_down_i4_mfma_cmb(ar, as, q_r, s_r, q_s, s_s, dq, w_down.scales, sdq,
+                                                    ws_down.scales, f, inv, topk_w,
+                                                    static_cast<float*>(y), st), where));
+      return MM_OK;
     } else if (dn_mfma_pair) {
       MM_TRY(hip_status(mm::launch_down_i4_mfma_pair(ar, as, q_r, s_r, q_s, s_s, dq, w_down.scales,
                                                      sdq, ws_down.scales, f, ys, st), where));

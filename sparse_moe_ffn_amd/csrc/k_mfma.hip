@@ -132,6 +132,23 @@ struct W4A8Prob {
   int32_t* isum;
 };
 
+// The weighted combine done in the shared down's epilogue (down problems
+// with the shared expert's rows, one per token): instead of writing ys, the
+// tile writes y[t][c] = fma(w[t][k-1], f[inv[t*k+k-1]][c], ... fma(w[t][0],
+// f[inv[t*k]][c], 0)) + ys[t][c], the combine kernel's arithmetic in its
+// order (positions outside [0, Tk) add nothing), with ys[t][c] the value
+// the shared down would have stored.  The routed outputs f must be complete
+// (an earlier launch).
+struct CombineArgs {
+  const float* f;      // [Tk][N] routed outputs, expert-sorted
+  const int32_t* inv;  // [Tk] position of slot t*k+j in f
+  const float* w;      // [Tk] gate weights
+  float* y;            // [T][N]
+  int64_t Tk;
+  int k;               // 1..kMaxCmbK
+};
+constexpr int kMaxCmbK = 8;
+
 // Workgroup b runs on XCD b % 8 as that XCD's slot b / 8.  Each XCD works
 // through a contiguous range of logical tile ids (the same expert's weights
 // stay in its L2): slot i of XCD x takes logical id x * per + i, with per the
@@ -140,6 +157,62 @@ struct W4A8Prob {
 // for the worst case) and the spare slots exit; the empty tail is thereby
 // spread over the XCDs instead of idling the last ones.
 //
+// The combine in the shared down's epilogue (CombineArgs), for k <= kK:
+// the tile's positions and gate weights go to workgroup memory, then the
+// rows are taken kRB at a time, every gather of those rows issued before
+// the sums.
+template <int kNT, int kK>
+__device__ __forceinline__ void combine_epilogue(const v16f (&acc)[kNT], float srow,
+                                                 const int (&cpos)[kK / 2],
+                                                 const float (&cwt)[kK / 2], const CombineArgs& C,
+                                                 int p0, int n, int col0, int N, int lane) {
+  constexpr int kRB = 32 / (kK * kNT);  // rows per batch: 32 gathers in flight per lane
+  static_assert(kRB >= 1 && 16 % kRB == 0, "rows per batch");
+  __shared__ int s_pos[32][kK];
+  __shared__ float s_w[32][kK];
+#pragma unroll
+  for (int q = 0; q < kK / 2; ++q) {
+    const int jj = (lane >> 5) * (kK / 2) + q;
+    s_pos[lane & 31][jj] = cpos[q];
+    s_w[lane & 31][jj] = cwt[q];
+  }
+  __syncthreads();  // one wave per workgroup: its stores are visible to its own loads
+  const int c = lane & 31;
+#pragma unroll
+  for (int r0 = 0; r0 < 16; r0 += kRB) {
+    float v[kRB][kK][kNT], wj[kRB][kK], sc[kRB];
+    int pj[kRB][kK], rl[kRB];
+#pragma unroll
+    for (int u = 0; u < kRB; ++u) {
+      const int r = r0 + u;
+      rl[u] = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      sc[u] = __shfl(srow, rl[u]);  // every lane takes part (before any divergence)
+#pragma unroll
+      for (int jj = 0; jj < kK; ++jj) {
+        const int p = s_pos[rl[u]][jj];
+        // slots past k and positions outside [0, Tk) add nothing; they read
+        // row 0 (a valid address) and are never used
+        pj[u][jj] = (jj < C.k && rl[u] < n && p >= 0 && (int64_t)p < C.Tk) ? p : -1;
+        wj[u][jj] = s_w[rl[u]][jj];
+        const int pr = pj[u][jj] >= 0 ? pj[u][jj] : 0;
+#pragma unroll
+        for (int j = 0; j < kNT; ++j) v[u][jj][j] = C.f[(int64_t)pr * N + col0 + j * 32 + c];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kRB; ++u) {
+#pragma unroll
+      for (int j = 0; j < kNT; ++j) {
+        float a = 0.0f;
+#pragma unroll
+        for (int jj = 0; jj < kK; ++jj)
+          if (pj[u][jj] >= 0) a = fmaf(wj[u][jj], v[u][jj][j], a);
+        if (rl[u] < n) C.y[(int64_t)(p0 + rl[u]) * N + col0 + j * 32 + c] = a + acc[j][r0 + u] * sc[u];
+      }
+    }
+  }
+}
+
 // One tile (kMT row tiles x kNT column tiles) of problem P for XCD x, slot
 // i; logical id = mt * nsplit + split.  kDense: rows are the tokens in order
 // (shared expert), per_dense its slots per XCD; otherwise routed
@@ -148,8 +221,12 @@ struct W4A8Prob {
 // are read from one contiguous kilobyte when the rows are consecutive.
 // K % 128 == 0.  Called by one whole wave.
 template <int kMT, int kNT, bool kGateUp, bool kCapture, bool kDense, bool kGM = false,
-          bool kDeep = false>
-__device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int x, int i, int per_dense) {
+          bool kDeep = false, int kCmbK = 0>
+__device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int x, int i, int per_dense,
+                                           const CombineArgs* cmb = nullptr) {
+  // kCmbK > 0: the combine in the epilogue for k <= kCmbK (shared down only)
+  constexpr bool kCmb = kCmbK > 0;
+  static_assert(!kCmb || (kDense && !kGateUp && kMT == 1), "combine: shared down, one row tile");
   static_assert(!kGateUp || kNT % 2 == 0, "gate/up tiles come in (gate, up) pairs");
   constexpr int kP = kNT / 2;  // gate/up: column pairs per wave
   constexpr int kBM = 32 * kMT;
@@ -233,6 +310,24 @@ __device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int x, int i, int 
 #pragma unroll
     for (int j = 0; j < kNT; ++j) acc[m][j] = v16f{};
 
+  // Combine: the positions and gate weights of the tile's 32 tokens are
+  // requested now, so they arrive under the products; lane l holds slots
+  // (l >> 5) kCmbK / 2 .. + kCmbK / 2 - 1 of row l & 31.
+  constexpr int kCmbPer = kCmb ? kCmbK / 2 : 1;
+  int cpos[kCmbPer];
+  float cwt[kCmbPer];
+  if constexpr (kCmb) {
+    const int rr = (lane & 31) < n ? (lane & 31) : 0;
+    const int64_t t = p0 + rr;
+#pragma unroll
+    for (int q = 0; q < kCmbPer; ++q) {
+      const int jj = (lane >> 5) * kCmbPer + q;
+      const int jc = jj < cmb->k ? jj : 0;
+      cpos[q] = cmb->inv[t * cmb->k + jc];
+      cwt[q] = cmb->w[t * cmb->k + jc];
+    }
+  }
+
   // Register ring of kD single-group slots: slot i % kD holds group i,
   // loaded kD - 1 groups before its products (the last groups re-load group
   // G - 1: valid addresses, results unused).  Every load is a scalar base
@@ -281,12 +376,13 @@ __device__ __forceinline__ void w4a8w_tile(const W4A8Prob& P, int x, int i, int 
         for (int p = 0; p < kP; ++p)
           out[(int64_t)(p0 + row) * h + col0 + p * 32 + (lane & 31)] =
               silu(acc[m][p][r] * s) * (acc[m][kP + p][r] * s);
-      } else {
+      } else if constexpr (!kCmb) {
 #pragma unroll
         for (int j = 0; j < kNT; ++j)
           out[(int64_t)(p0 + row) * N + col0 + j * 32 + (lane & 31)] = acc[m][j][r] * s;
       }
     }
+  if constexpr (kCmb) combine_epilogue<kNT, kCmbK>(acc[0], srow[0], cpos, cwt, *cmb, p0, n, col0, N, lane);
 }
 
 template <int kMT, bool kGateUp, bool kCapture, bool kDense>
@@ -310,6 +406,14 @@ __global__ __launch_bounds__(64) void k_w4a8w_pair(W4A8Prob P0, W4A8Prob P1, int
     w4a8w_tile<kMT1, kNT1, kGateUp, false, true, true, kDeep>(P1, x, i, per1);
   else
     w4a8w_tile<kMT0, kNT0, kGateUp, false, false, true, kDeep>(P0, x, i - per1, 0);
+}
+
+// The shared down with the combine in its epilogue (CombineArgs), launched
+// after the routed down: one row tile and kNT column tiles per wave.
+template <int kNT, int kK>
+__global__ __launch_bounds__(64) void k_w4a8w_shared_cmb(W4A8Prob P, CombineArgs C, int per) {
+  const int b = (int)blockIdx.x;
+  w4a8w_tile<1, kNT, false, false, true, true, false, kK>(P, b % kXcd, b / kXcd, per, &C);
 }
 
 // Launches of at most this many waves (decode batches) take the deep
@@ -443,7 +547,65 @@ hipError_t launch_pair(const W4A8Prob& R, const W4A8Prob& D0, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Routed down, then the shared down with the combine in its epilogue
+// (y written, no ys).  The routed launch keeps the tile forms of the merged
+// launch; the shared launch takes two 32-column tiles per wave.  Used from
+// kCmbMinTokens tokens on: there the combine launch it replaces (which
+// reads every routed and shared output row once more) costs more than the
+// second launch and the gathers in the epilogue (M prefill: routed down
+// 69 + shared down with the combine 70 us, against 108 us for the merged
+// down and 39 us for the combine; S prefill, 2048 tokens: 17 + 18 against
+// 23 + 8 us).
+constexpr int64_t kCmbMinTokens = 4096;
+
+hipError_t launch_down_cmb(const W4A8Prob& R, const W4A8Prob& D0, const CombineArgs& C,
+                           hipStream_t st) {
+  const dim3 block(64);
+  const bool r2 = two_row_tiles(R.a, R.nsplit);
+  const int64_t n0 = n_tiles(R.a, r2 ? 64 : 32, R.nsplit);
+  if (!r2 && n0 >= kWideGateUpWaves && R.N % 128 == 0) {
+    W4A8Prob R2 = R;
+    R2.nsplit = R.N / 128;
+    hipLaunchKernelGGL((k_w4a8w_pair<1, 1, false, 2, 4>), dim3(grid_of(n_tiles(R2.a, 32, R2.nsplit))),
+                       block, 0, st, R2, D0, 0);
+  } else if (r2) {
+    hipLaunchKernelGGL((k_w4a8w_pair<2, 1, false>), dim3(grid_of(n0)), block, 0, st, R, D0, 0);
+  } else if (n0 <= kDeepRingWaves) {
+    hipLaunchKernelGGL((k_w4a8w_pair<1, 1, false, 2, 2, true>), dim3(grid_of(n0)), block, 0, st, R, D0,
+                       0);
+  } else {
+    hipLaunchKernelGGL((k_w4a8w_pair<1, 1, false>), dim3(grid_of(n0)), block, 0, st, R, D0, 0);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  W4A8Prob D = D0;
+  D.nsplit = D0.N / 64;
+  const unsigned g1 = grid_of(n_tiles(D.a, 32, D.nsplit));
+  const int per = (int)(g1 / kXcd);
+  if (C.k <= 4)
+    hipLaunchKernelGGL((k_w4a8w_shared_cmb<2, 4>), dim3(g1), block, 0, st, D, C, per);
+  else
+    hipLaunchKernelGGL((k_w4a8w_shared_cmb<2, 8>), dim3(g1), block, 0, st, D, C, per);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+bool down_cmb_fits(const ExpertArgs& ar, const ExpertArgs& as) {
+  return ar.k >= 1 && ar.k <= kMaxCmbK && as.rows == ar.T && ar.d % 64 == 0 &&
+         ar.T >= kCmbMinTokens;
+}
+
+hipError_t launch_down_i4_mfma_cmb(const ExpertArgs& ar, const ExpertArgs& as, const int8_t* hq_r,
+                                   const float* hs_r, const int8_t* hq_s, const float* hs_s,
+                                   const uint8_t* wq_r, const float* ws_r, const uint8_t* wq_s,
+                                   const float* ws_s, float* f, const int32_t* inv_perm,
+                                   const float* topk_w, float* y, hipStream_t st) {
+  if (!down_cmb_fits(ar, as)) return hipErrorInvalidValue;
+  const CombineArgs C{f, inv_perm, topk_w, y, ar.rows, ar.k};
+  return launch_down_cmb(down_prob(ar, hq_r, hs_r, wq_r, ws_r, f, nullptr),
+                         down_prob(as, hq_s, hs_s, wq_s, ws_s, nullptr, nullptr), C, st);
+}
 
 hipError_t launch_gateup_i4_mfma(const ExpertArgs& a, const int8_t* xq, const float* sx,
                                  const uint8_t* wq, const float* ws, float* a_buf, int32_t* isum,

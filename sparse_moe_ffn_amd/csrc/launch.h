@@ -141,6 +141,18 @@ hipError_t launch_down_i4_mfma_pair(const ExpertArgs& ar, const ExpertArgs& as,
                                     const float* hs_s, const uint8_t* wq_r, const float* ws_r,
                                     const uint8_t* wq_s, const float* ws_s, float* f, float* ys,
                                     hipStream_t st);
+// The same two products with the weighted combine in the shared down's
+// epilogue (y [T][d] written, no ys): the routed down first, then the shared
+// down, whose tiles gather each token's routed outputs through inv_perm and
+// add them, weighted by topk_w, in the combine's order.  down_cmb_fits: k <= 8,
+// d % 64 == 0, one shared row per token, and enough tokens (4096) that this
+// form is the faster one.
+bool down_cmb_fits(const ExpertArgs& ar, const ExpertArgs& as);
+hipError_t launch_down_i4_mfma_cmb(const ExpertArgs& ar, const ExpertArgs& as, const int8_t* hq_r,
+                                   const float* hs_r, const int8_t* hq_s, const float* hs_s,
+                                   const uint8_t* wq_r, const float* ws_r, const uint8_t* wq_s,
+                                   const float* ws_s, float* f, const int32_t* inv_perm,
+                                   const float* topk_w, float* y, hipStream_t st);
 hipError_t launch_gateup_i4_gemv_pair(const ExpertArgs& ar, const ExpertArgs& as,
                                       const int8_t* xq, const float* sx, const uint8_t* wq_r,
                                       const float* ws_r, const uint8_t* wq_s, const float* ws_s,
