@@ -417,19 +417,24 @@ __device__ __forceinline__ void gemv_block(const GemvProb& P, int blk,
     }
   }
 
-  // scales of the workgroup's blocks: G * 32 contiguous floats per block
-  // (fused: the first kScR per thread are loaded now, with the weights)
+  // scales of the workgroup's blocks: G * 32 contiguous floats per block;
+  // the first kScR per thread are loaded now, with the weights, so that
+  // their latency does not add to the activations' (the rest, if any,
+  // later)
   const float* se = wsc + (int64_t)e * (wrows / 32) * G * 32;
   const int nsc = kM * G * 32;
   constexpr int kScR = (kGateUp || kDense) ? 10 : 3;  // routed down: h <= 768 in the preload
   float scr[kScR];
-  if constexpr (kFused) {
 #pragma unroll
-    for (int i = 0; i < kScR; ++i) {
-      const int j = tid + kWaves * 64 * i;
-      if (j < nsc) scr[i] = se[(int64_t)rbm[j / (G * 32)] * G * 32 + j % (G * 32)];
-    }
+  for (int i = 0; i < kScR; ++i) {
+    const int j = tid + kWaves * 64 * i;
+    if (j < nsc) scr[i] = se[(int64_t)rbm[j / (G * 32)] * G * 32 + j % (G * 32)];
   }
+  // Routed gate/up whose token rows are not pre-staged: every thread finds
+  // the source token of the rows it stages itself and loads them at once
+  // (no barrier between the permutation and the activation loads); the
+  // first thread of each row also takes the row's scale.
+  const bool direct = !kQIn && !pre && !kQX;
   if constexpr (kQX && kDense) quant_x();
   hook();
   if constexpr (kQIn && kFused) {
@@ -460,6 +465,23 @@ __device__ __forceinline__ void gemv_block(const GemvProb& P, int blk,
       const float sr = quant_row_lds(P.actf + (int64_t)(p0 + r) * K, K, dst, lane);
       if (lane == 0) s_as[r] = sr;
     }
+  } else if (direct) {
+    for (int i = tid; i < kR * c16; i += blockDim.x) {
+      const int r = i / c16, c = i % c16;
+      int4 v = make_int4(0, 0, 0, 0);
+      if (r < n) {
+        int src = p0 + r;
+        if (kGateUp && !kDense) {
+          src = a.T == 1 ? 0 : a.perm[p0 + r] / a.k;
+          if ((unsigned)src >= (unsigned)a.T) src = 0;  // stays in bounds for a corrupt perm
+        }
+        v = reinterpret_cast<const int4*>(act + (int64_t)src * K)[c];
+        if (c == 0) s_as[r] = act_scale[src];
+      } else if (c == 0) {
+        s_as[r] = 0.0f;
+      }
+      s_act[i] = v;
+    }
   } else if (tid < kR) {
     const int r = tid;
     int src = -1;
@@ -475,30 +497,14 @@ __device__ __forceinline__ void gemv_block(const GemvProb& P, int blk,
     s_src[r] = src;
     s_as[r] = s;
   }
-  if constexpr (kFused) {
 #pragma unroll
-    for (int i = 0; i < kScR; ++i) {
-      const int j = tid + kWaves * 64 * i;
-      if (j < nsc) s_sc[j] = scr[i];
-    }
-    for (int j = tid + kWaves * 64 * kScR; j < nsc; j += kWaves * 64)
-      s_sc[j] = se[(int64_t)rbm[j / (G * 32)] * G * 32 + j % (G * 32)];
-  } else {
-    for (int i = tid; i < kM * G * 32; i += blockDim.x) {
-      const int m = i / (G * 32), j = i % (G * 32);
-      s_sc[i] = se[(int64_t)rbm[m] * G * 32 + j];
-    }
+  for (int i = 0; i < kScR; ++i) {
+    const int j = tid + kWaves * 64 * i;
+    if (j < nsc) s_sc[j] = scr[i];
   }
-  __syncthreads();  // s_src ready (in-kernel quantisation: activations staged)
-  if (!kQIn && !pre && !kQX) {
-    for (int i = tid; i < kR * c16; i += blockDim.x) {
-      const int r = i / c16, c = i % c16;
-      int4 v = make_int4(0, 0, 0, 0);
-      if (r < n) v = reinterpret_cast<const int4*>(act + (int64_t)s_src[r] * K)[c];
-      s_act[i] = v;
-    }
-    __syncthreads();  // activations and scales staged
-  }
+  for (int j = tid + kWaves * 64 * kScR; j < nsc; j += kWaves * 64)
+    s_sc[j] = se[(int64_t)rbm[j / (G * 32)] * G * 32 + j % (G * 32)];
+  __syncthreads();  // scales, activations (or, in-kernel quantisation, the codes) staged
 
   // Lane geometry inside a pair: lanes 0..31 hold group 2gp, 32..63 group
   // 2gp+1; within a group, lane l (= lane % 32) holds rows 2*(l / 2) and
