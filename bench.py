@@ -124,8 +124,10 @@ def pair_kernel_of(w, T):
     # two column pairs per wave once the one-pair waves would reach 4096
     waves = ((rows + 31) // 32 + min(w.E, rows)) * (w.h // 32) + ((T + 31) // 32) * (w.hs // 32)
     if not r2 and not d2 and waves >= 4096 and w.h % 64 == 0 and w.hs % 64 == 0:
-        return "k_w4a8w_pair<1, 1, true, 4, 4>"
-    return f"k_w4a8w_pair<{2 if r2 else 1}, {2 if d2 else 1}, true, 2, 2>"
+        return "k_w4a8w_pair<1, 1, true, 4, 4, false>"
+    # launches of at most 2048 one-pair waves keep the deep register ring
+    deep = not r2 and not d2 and waves <= 2048
+    return f"k_w4a8w_pair<{2 if r2 else 1}, {2 if d2 else 1}, true, 2, 2, {'true' if deep else 'false'}>"
 
 
 def pair_gemv_kernel_of(w, T):
