@@ -350,7 +350,10 @@ mm_status mm_combine(const mm_layer_desc* desc, int64_t T, const float* f,
  * design factors"), the seven calls above in order with the same arithmetic
  * and bit-identical results, issued as fewer launches on one stream.  The
  * router pass also quantises x (INT4 weights), and the routed and shared
- * products of each kind share one launch, as do their hidden-row quantisers.
+ * products of each kind share one launch, as do their hidden-row quantisers;
+ * from 4096 tokens (matrix-core products, FP32 y, no y_norm) the shared down
+ * runs after the routed down and does the weighted combine itself, in the
+ * combine's order (no separate combine launch).
  *   x                  device FP32 [T][d]
  *   w_router, bias     as mm_router_topk (bias may be NULL)
  *   w_gateup, w_down   routed experts, as mm_expert_gateup_swiglu / mm_expert_down
