@@ -995,7 +995,8 @@ FUSED_CASES = [
     ("s_prefill", 2300, {"E": 1, "k": 1}),                                 # ... one expert, k = 1
     ("s_prefill", 700, {"E": 64, "k": 8}),                                 # ... k = 8: block limits inside a 16-byte piece
     ("s_prefill", 4099, {}), ("s_prefill", 4100, {"E": 16, "k": 8}),       # combine in the shared down's epilogue (ragged, k = 8)
-    ("m_prefill", 4100, {}),                                               # gate/up on the f16 matrix cores (two row tiles per wave)
+    ("m_prefill", 4100, {}),                                               # two row tiles per wave, combine in the shared down (ragged)
+    ("s_prefill", 4200, {"E": 1, "k": 1}), ("s_prefill", 4096, {"E": 8, "k": 2}),  # ... with k = 1 and k = 2 (unused slots)
     ("l_decode", 1, {}), ("m_decode", 1, {}),                              # one token: one-workgroup front, widths 1280 / 1024
     ("s_prefill", 1, {"E": 64, "k": 8}), ("s_prefill", 1, {"d": 256, "h": 128, "hs": 512}),
 ]
